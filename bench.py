@@ -1,0 +1,363 @@
+#!/usr/bin/env python3
+"""Benchmark of the Gated DeltaNet chunked forward on one MI355X.
+
+One step = one gdn_chunk_fwd call over one batch of the workload's synthetic
+inputs (decay cumsum, UT transform, WY pair, the sequential chunk walk or the
+chunk-group fold / prefix / replay, and the outputs), with inputs, outputs
+and workspace resident in HBM before the timed region starts.
+
+Prints ONE JSON line.  `value` is tokens/s (B*T per step).  `roofline` is for
+the kernel that takes the most time per step, timed live with HIP events on
+the stream the library launches on (torch's current stream), against the
+bytes that kernel must move at minimum; `path_roofline` relates the whole
+step to the method's own algorithmic bytes and FLOPs.  `cpu_baseline` times
+the fp64 oracle on this host's cores over a bounded sample of the workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12            # bytes/s, MI355X HBM3E
+BF16_PEAK = 2.5e15           # dense bf16 MFMA FLOP/s
+METRIC = "GDN fwd tokens/sec (all heads) at T=4096/262144; MFMA util % vs gfx950 peak"
+
+
+def algorithmic(w, o_bytes=4):
+    """The method's own FLOPs and HBM bytes per step (inputs read once, o and
+    h_T written once; the long path adds the fold's re-read of k, v, g, beta,
+    the pairs and the incoming states)."""
+    C, dk, dv = w.chunk, w.dk, w.dv
+    tok = w.B * w.T
+    s = 2 if w.dtype == "bf16" else 4
+    per_qk = 2 * C * dk
+    per_v = (C - 1) * (dk + dv) + (C + 1) * dv + 6 * dk * dv + C * C / 3
+    flops = tok * (w.Hqk * per_qk + w.Hv * per_v)
+    nbytes = tok * (2 * w.Hqk * dk * s + w.Hv * dv * s + 8 * w.Hv + w.Hv * dv * o_bytes)
+    nbytes += w.B * w.Hv * dk * dv * 4 * (2 if w.h0_std > 0 else 1)
+    J = max(w.n_groups, 1)
+    if J > 1:
+        flops += tok * w.Hv * 4 * dk * (dk + dv)
+        flops += w.B * w.Hv * J * 2 * dk * dk * dv
+        nbytes += tok * (w.Hqk * dk * s + w.Hv * dv * s + 8 * w.Hv)
+        nbytes += w.B * w.Hv * J * (dk * dk + dk * dv) * 4 * 2 + w.B * w.Hv * J * dk * dv * 4 * 2
+    return flops, nbytes
+
+
+def stage_bytes(w, o_bytes=4):
+    """Minimum HBM bytes each kernel must move in this design (its inputs read
+    once, its outputs written once)."""
+    C, dk, dv = w.chunk, w.dk, w.dv
+    tok = w.B * w.T
+    s = 2 if w.dtype == "bf16" else 4
+    N = w.T // C
+    J = max(w.n_groups, 1)
+    BHv = w.B * w.Hv
+    k_b = tok * w.Hqk * dk * s
+    q_b = k_b
+    v_b = tok * w.Hv * dv * s
+    gb_b = 8 * tok * w.Hv
+    G_b = 4 * tok * w.Hv
+    W_b = 4 * tok * w.Hv * dk
+    U_b = 4 * tok * w.Hv * dv
+    Hs_b = 4 * BHv * N * dk * dv
+    Vn_b = 4 * tok * w.Hv * dv
+    st = 4 * BHv * dk * dv
+    h0_b = st if w.h0_std > 0 else 0
+    pairs = 4 * BHv * J * (dk * dk + dk * dv)
+    hin = 4 * BHv * J * dk * dv
+    out = {
+        "prep": k_b + v_b + gb_b + G_b + W_b + U_b,
+        "out": q_b + k_b + G_b + Hs_b + Vn_b + tok * w.Hv * dv * o_bytes,
+    }
+    if J == 1:
+        out["walk"] = W_b + U_b + G_b + k_b + h0_b + Hs_b + Vn_b + st
+    else:
+        out["fold"] = W_b + U_b + G_b + k_b + pairs
+        out["prefix"] = pairs + h0_b + hin + st
+        out["walk"] = W_b + U_b + G_b + k_b + hin + Hs_b + Vn_b
+    return out
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "linear_attention_rnn_gdn_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".h", ".hip")):
+            h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel sources; else None."""
+    p = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        d = json.load(open(p))
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    e = d.get("workloads", {}).get(workload, {}).get(kernel)
+    return None if e is None else e.get("bytes_per_launch")
+
+
+def _stage_of(kernel_name):
+    """Map a demangled kernel name to its stage."""
+    n = kernel_name
+    if "prep_kernel" in n:
+        return "prep"
+    if "prefix_kernel" in n:
+        return "prefix"
+    if "out_kernel" in n:
+        return "out"
+    if "walk_kernel" in n:
+        # walk_kernel<C, TI, MODE, S, KIND>: KIND 1 = fold (demangled or mangled name)
+        if "walk_kernel<" in n:
+            kind = n.split("walk_kernel<", 1)[1].split(">", 1)[0].split(",")[-1].strip()
+        else:
+            import re
+            kind = re.findall(r"Li(\d+)E", n.split("walk_kernel", 1)[1])[-1]
+        return "fold" if kind == "1" else "walk"
+    if "copy" in n.lower():
+        return "copy"
+    return None
+
+
+def _pmc_rows(d, counter):
+    import csv
+    import glob
+
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection*.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r.get("Counter_Name") == counter:
+                rows.append((int(r.get("Dispatch_Id", 0) or 0), r.get("Kernel_Name", ""),
+                             float(r["Counter_Value"])))
+    rows.sort()
+    return [(name, val) for _, name, val in rows]
+
+
+def summarize_pmc(fetch_dir, write_dir, workload, copy_bytes):
+    """Per-launch HBM bytes per kernel from two rocprofv3 --pmc runs of
+    `bench.py --profile-run` (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch),
+    each scaled by what the counter reads for the calibration copy of
+    `copy_bytes` bytes.  Writes profiles/hbm_traffic.json."""
+    out = {}
+    scale = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        per = {}
+        for name, val in _pmc_rows(d, counter):
+            st = _stage_of(name)
+            if st:
+                per.setdefault(st, []).append(val * 1024.0)
+        # the calibration copies are the first three copy kernels of the run
+        copy = sorted(per.get("copy", [])[:3])
+        if len(copy) < 3:
+            raise SystemExit(f"no calibration copy kernels found for {counter} in {d}")
+        med = copy[1]
+        scale[counter] = copy_bytes / med
+        for st, vals in per.items():
+            if st != "copy":
+                out.setdefault(st, {})[counter] = sum(vals) / len(vals) * scale[counter]
+    p = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        d = json.load(open(p))
+    except (OSError, ValueError):
+        d = {}
+    if d.get("kernel_source_sha") != kernel_source_sha():
+        d = {"workloads": {}}
+    d["kernel_source_sha"] = kernel_source_sha()
+    d["note"] = ("bytes_per_launch = mean FETCH_SIZE + WRITE_SIZE per dispatch (KiB x 1024), each "
+                 "scaled by copy_bytes / (what that counter reads for one torch copy of copy_bytes)")
+    d["scale"] = scale
+    d["workloads"][workload] = {st: {"fetch_bytes": v.get("FETCH_SIZE"),
+                                     "write_bytes": v.get("WRITE_SIZE"),
+                                     "bytes_per_launch": (v.get("FETCH_SIZE") or 0)
+                                     + (v.get("WRITE_SIZE") or 0)}
+                                for st, v in out.items()}
+    json.dump(d, open(p, "w"), indent=1)
+    print(json.dumps(d, indent=1))
+
+
+def cpu_baseline(w, x, budget_s=15.0):
+    """Time the fp64 oracle (as it stands) on this host over a bounded sample:
+    the first T_s tokens of every head of the workload."""
+    import oracle
+
+    nthreads = oracle.default_threads()
+    cpu = {kk: (None if vv is None else vv) for kk, vv in x.items()}
+
+    def run(T_s):
+        sub = {kk: (vv[:, :T_s].cpu() if kk not in ("h0",) else (None if vv is None else vv.cpu()))
+               for kk, vv in cpu.items()}
+        t0 = time.perf_counter()
+        oracle.fwd(**sub, nthreads=nthreads)
+        return time.perf_counter() - t0
+
+    T_s = min(w.T, 256)
+    dt = run(T_s)
+    est_full = dt * w.T / T_s
+    if est_full <= 2 * budget_s:
+        T_s = w.T
+    else:
+        T_s = max(256, min(w.T, int(T_s * budget_s / max(dt, 1e-6)) // 256 * 256))
+    dt = run(T_s)
+    return {"value": w.B * T_s / dt, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"first {T_s} of {w.T} tokens x batch {w.B}, all {w.Hv} value heads, "
+                      f"all {w.dv} state columns; fp64 per-token rule in C, {nthreads} threads; "
+                      f"{dt:.2f} s"}
+
+
+def time_steps(fn, steps, warmup):
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen3next_8b_layer")
+    ap.add_argument("--secondary", default="long_256k",
+                    help="second workload timed for context ('' to skip)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-run", action="store_true",
+                    help="counter-collection run: calibration copies, then the workload's steps")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/hbm_traffic.json from two --pmc runs of --profile-run")
+    args = ap.parse_args()
+    copy_bytes = 1 << 30
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload, copy_bytes)
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import linear_attention_rnn_gdn_amd as gdn
+    from workloads import WORKLOADS, make_inputs
+
+    stage_bits = {"prep": gdn.STAGE_PREP, "fold": gdn.STAGE_FOLD, "prefix": gdn.STAGE_PREFIX,
+                  "walk": gdn.STAGE_WALK, "out": gdn.STAGE_OUT}
+
+    def setup(w):
+        x = make_inputs(w, device="cuda")
+        shape = gdn.make_shape(w.B, w.T, w.Hqk, w.Hv, w.dk, w.dv, w.chunk, w.n_groups,
+                               x["k"].dtype, torch.float32)
+        ws = torch.empty(gdn.workspace_size(shape), dtype=torch.uint8, device="cuda")
+        o = torch.empty((w.B, w.T, w.Hv, w.dv), dtype=torch.float32, device="cuda")
+        hT = torch.empty((w.B, w.Hv, w.dk, w.dv), dtype=torch.float32, device="cuda")
+
+        def step(stages=None):
+            gdn.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"], chunk=w.chunk,
+                          n_groups=w.n_groups, workspace=ws, out=o, final_state=hT, stages=stages)
+        return x, step
+
+    w = WORKLOADS[args.workload]
+    if args.profile_run:
+        a = torch.empty(copy_bytes // 4, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        a.fill_(1.0)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+    x, step = setup(w)
+    ms = time_steps(step, args.steps, args.warmup)
+    if args.profile_run:
+        print(json.dumps({"profile_run": w.name, "ms_per_step": ms}), flush=True)
+        return
+
+    # per-kernel times: the same step issued stage by stage, events between
+    names = [n for n in ("prep", "fold", "prefix", "walk", "out")
+             if (w.n_groups > 1 or n not in ("fold", "prefix"))]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+    acc = {n: 0.0 for n in names}
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        ev[0].record()
+        for i, n in enumerate(names):
+            step(stage_bits[n])
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        for i, n in enumerate(names):
+            acc[n] += ev[i].elapsed_time(ev[i + 1])
+    stage_ms = {n: acc[n] / args.steps for n in names}
+
+    flops, nbytes = algorithmic(w)
+    sb = stage_bytes(w)
+    dom = max(stage_ms, key=stage_ms.get)
+    dom_s = stage_ms[dom] * 1e-3
+    achieved = sb[dom] / dom_s
+    traffic = measured_traffic(w.name, dom)
+    roof = {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK, "traffic": traffic, "kernel": dom,
+            "bytes_per_launch": sb[dom], "avg_launch_ms": stage_ms[dom]}
+    t = ms * 1e-3
+    path = {"flops": flops, "bytes": nbytes, "hbm_frac": nbytes / t / HBM_PEAK,
+            "mfma_frac": flops / t / BF16_PEAK}
+    line = {
+        "metric": METRIC,
+        "value": w.tokens / t,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "H_qk": w.Hqk, "H_v": w.Hv,
+                   "d_k": w.dk, "d_v": w.dv, "chunk": w.chunk, "n_groups": w.n_groups,
+                   "o_dtype": "f32", "parallelism": "single GPU"},
+        "mfma_util_pct": 100.0 * flops / t / BF16_PEAK,
+        "roofline": roof,
+        "path_roofline": path,
+        "stages_ms": stage_ms,
+    }
+    if args.secondary and args.secondary != w.name:
+        del x, step
+        torch.cuda.empty_cache()
+        w2 = WORKLOADS[args.secondary]
+        x2, step2 = setup(w2)
+        ms2 = time_steps(step2, max(2, args.steps // 4), 1)
+        f2, b2 = algorithmic(w2)
+        line["secondary"] = {"workload": w2.name, "value": w2.tokens / (ms2 * 1e-3),
+                             "unit": "tokens/s", "ms_per_step": ms2,
+                             "mfma_util_pct": 100.0 * f2 / (ms2 * 1e-3) / BF16_PEAK,
+                             "hbm_frac": b2 / (ms2 * 1e-3) / HBM_PEAK}
+        del x2, step2
+        torch.cuda.empty_cache()
+        x = make_inputs(w, device="cuda")
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, x)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,169 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) Gated DeltaNet chunked forward.
+ *
+ * The operation.  Per value head, with state S (d_k x d_v) and tokens t:
+ *     S_t = exp(g_t) (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,
+ *     o_t = S_t^T q_t.
+ * It is evaluated chunk by chunk (C tokens per chunk) with the gated UT/WY
+ * transform T = (I+S)^-1 and the affine inter-chunk step
+ *     h' = (exp(g_last) I - k_g^T w) h + k_g^T u = A h + B
+ * ("Shard the GatedDeltaNet sequence under ici_context_parallelism", PR
+ * description; "GatedDeltaNet does not support ici_context_parallelism",
+ * section "The recurrence is affine, so it can be parallelized"), with T
+ * formed by the blockwise doubling ladder X - X S_l X ("Fuse the Gated Delta
+ * Net inter-chunk scan into a Pallas TPU kernel", section "Changes").  Long
+ * sequences are split into chunk-groups, each folded into one (A, B) pair,
+ * composed by (A2,B2) o (A1,B1) = (A2 A1, A2 B1 + B2), prefixed exclusively
+ * and replayed from the incoming state (issue page, same section; PR page,
+ * code-review suggestion for the incoming-state routine).
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor arguments are DEVICE pointers owned by the caller; the
+ *    library never allocates, frees or synchronises.  Work is enqueued on
+ *    the caller's HIP stream (`hip_stream`, a hipStream_t; NULL = the null
+ *    stream) and the call returns without waiting.
+ *  - Tensors are dense, row-major, with the layouts stated per argument.
+ *    Every pointer must be 16-byte aligned.
+ *  - Errors are returned, never aborted on.  Arguments are checked before
+ *    anything is launched; on any status other than GDN_OK returned by the
+ *    argument checks no output has been touched.  GDN_ERR_HIP means a
+ *    launch failed after earlier launches of the same call were queued.
+ *  - Calls on different streams do not interact; two calls that share an
+ *    output or workspace buffer must be ordered by the caller.
+ *  - Supported sizes: d_k = d_v = 128; chunk 64 or 128 for bf16 inputs,
+ *    chunk 64 for fp32 inputs; T a multiple of chunk.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GDN_OK = 0,
+  GDN_ERR_NULL = -1,      /* a required pointer is NULL                         */
+  GDN_ERR_SHAPE = -2,     /* unsupported or inconsistent sizes                  */
+  GDN_ERR_DTYPE = -3,     /* unsupported dtype code                             */
+  GDN_ERR_ALIGN = -4,     /* a pointer is not 16-byte aligned                   */
+  GDN_ERR_WORKSPACE = -5, /* workspace smaller than gdn_workspace_size()        */
+  GDN_ERR_HIP = -6        /* a kernel launch failed                             */
+} gdn_status;
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+/* Problem description.
+ *   B        batch
+ *   T        tokens per sequence (multiple of chunk)
+ *   H_qk     query/key heads; H_v value heads, H_v % H_qk == 0.  Value head
+ *            h reads query/key head h / (H_v / H_qk) (contiguous groups).
+ *   d_k, d_v head dims (128, 128)
+ *   chunk    tokens per chunk C (64 or 128)
+ *   n_groups 0 or 1: one sequential walk over all T/C chunks per head.
+ *            > 1: split the T/C chunks of each head into n_groups equal
+ *            chunk-groups (n_groups must divide T/C): fold each group into
+ *            one (A, B) pair, exclusive prefix, replay every group from its
+ *            incoming state.  Same result up to rounding.
+ *   dtype    gdn_dtype of q, k, v
+ *   o_dtype  gdn_dtype of o                                                  */
+typedef struct {
+  int32_t B, T, H_qk, H_v, d_k, d_v, chunk, n_groups;
+  int32_t dtype, o_dtype;
+} gdn_shape;
+
+/* Human-readable name of a status code (static string). */
+const char *gdn_status_str(gdn_status s);
+
+/* Host-only check of a problem description; launches nothing. */
+gdn_status gdn_validate(const gdn_shape *shape);
+
+/* Bytes of device workspace gdn_chunk_fwd / gdn_chunk_fold need for `shape`
+ * (written to *bytes).  The workspace holds per-chunk intermediates (decay
+ * cumsums, W, U, chunk-start states, corrected values) and, with groups, the
+ * (A, B) pairs and incoming states.  It carries nothing between calls. */
+gdn_status gdn_workspace_size(const gdn_shape *shape, size_t *bytes);
+
+/* The whole chunked forward.
+ *   q, k  [B, T, H_qk, d_k]  dtype          v [B, T, H_v, d_v] dtype
+ *   g     [B, T, H_v] fp32 per-token log decay (g <= 0 expected, not required)
+ *   beta  [B, T, H_v] fp32
+ *   h0    [B, H_v, d_k, d_v] fp32 initial state, NULL = zero
+ *   o     [B, T, H_v, d_v] o_dtype           (written)
+ *   h_T   [B, H_v, d_k, d_v] fp32 final state, NULL = not wanted (written)
+ *   ws    device workspace of at least gdn_workspace_size() bytes
+ * No scale is applied to q; a caller folds any scale into q. */
+gdn_status gdn_chunk_fwd(const gdn_shape *shape, const void *q, const void *k, const void *v,
+                         const float *g, const float *beta, const float *h0, void *o,
+                         float *h_T, void *ws, size_t ws_bytes, void *hip_stream);
+
+/* The same computation issued one stage at a time, for timing each kernel.
+ * `stages` is a mask of GDN_STAGE_* bits; only the selected stages are
+ * launched.  The stages communicate through `ws`, so issuing every stage in
+ * increasing bit order on one stream with one workspace (one call per bit,
+ * or several bits at once) equals one gdn_chunk_fwd call.  Arguments and
+ * checks are those of gdn_chunk_fwd.
+ *   PREP    intra-chunk transform (decay cumsum, UT inverse, W, U)
+ *   FOLD    per-group affine pairs            (n_groups > 1 only)
+ *   PREFIX  exclusive prefix over the groups  (n_groups > 1 only; writes h_T)
+ *   WALK    sequential chunk walk: the whole sequence (writes h_T), or every
+ *           group from its incoming state (n_groups > 1)
+ *   OUT     chunk outputs o                                                  */
+#define GDN_STAGE_PREP 1
+#define GDN_STAGE_FOLD 2
+#define GDN_STAGE_PREFIX 4
+#define GDN_STAGE_WALK 8
+#define GDN_STAGE_OUT 16
+#define GDN_STAGE_ALL 31
+gdn_status gdn_chunk_fwd_stages(const gdn_shape *shape, int32_t stages, const void *q,
+                                const void *k, const void *v, const float *g, const float *beta,
+                                const float *h0, void *o, float *h_T, void *ws, size_t ws_bytes,
+                                void *hip_stream);
+
+/* Per-group affine pairs of the chunk-group split (shape->n_groups >= 1
+ * groups of equal length; 0 is taken as 1).  For group j of value head h:
+ *   A[b,h,j] = product over the group's tokens t (latest on the left) of
+ *              exp(g_t)(I - beta_t k_t k_t^T)            [d_k, d_k] fp32
+ *   Bm[b,h,j] = the state the group reaches from a zero state  [d_k, d_v] fp32
+ * so that the group maps an incoming state h to A h + Bm.
+ *   A  [B, H_v, n_groups, d_k, d_k]     Bm [B, H_v, n_groups, d_k, d_v]
+ * q is not read; o is not produced. */
+gdn_status gdn_chunk_fold(const gdn_shape *shape, const void *k, const void *v, const float *g,
+                          const float *beta, float *A, float *Bm, void *ws, size_t ws_bytes,
+                          void *hip_stream);
+
+/* Exclusive prefix of affine pairs applied to an initial state, per
+ * (batch*head) row bh:
+ *   h_in[bh,0] = h_init[bh];  h_in[bh,j+1] = A[bh,j] h_in[bh,j] + Bm[bh,j];
+ *   h_final[bh] = A[bh,n-1] h_in[bh,n-1] + Bm[bh,n-1].
+ *   A [batch_heads, n, d_k, d_k] fp32, Bm [batch_heads, n, d_k, d_v] fp32,
+ *   h_init [batch_heads, d_k, d_v] fp32 or NULL (= zero),
+ *   h_in [batch_heads, n, d_k, d_v] fp32 or NULL, h_final [batch_heads, d_k, d_v]
+ *   fp32 or NULL (at least one of them non-NULL).
+ * flags bit 0 (GDN_PREFIX_SPLIT_BF16): form the products from hi/lo bf16
+ * halves on the bf16 matrix cores (about 1e-5 relative) instead of fp32
+ * matrix-core products. */
+#define GDN_PREFIX_SPLIT_BF16 1
+gdn_status gdn_compose_prefix(int32_t batch_heads, int32_t n, int32_t d_k, int32_t d_v,
+                              const float *A, const float *Bm, const float *h_init,
+                              float *h_in, float *h_final, int32_t flags, void *hip_stream);
+
+/* The intra-chunk transform alone (decay cumsum, gated strict-lower
+ * beta K K^T, UT inversion by the doubling ladder, WY formation), for every
+ * chunk of every value head.  N = T / chunk.
+ *   G  [B, H_v, N, C] fp32     G[r] = sum_{s<=r} g_s within the chunk
+ *   Tm [B, H_v, N, C, C] fp32  (I+S)^-1, S_ri = beta_r e^{G_r-G_i} k_r.k_i (i<r);
+ *                              NULL = not wanted
+ *   W  [B, H_v, N, C, d_k] fp32   W = T diag(beta e^G) K
+ *   U  [B, H_v, N, C, d_v] fp32   U = T diag(beta) V
+ * shape->n_groups and o_dtype are ignored. */
+gdn_status gdn_chunk_transform(const gdn_shape *shape, const void *k, const void *v,
+                               const float *g, const float *beta, float *G, float *Tm, float *W,
+                               float *U, void *hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GDN_H */

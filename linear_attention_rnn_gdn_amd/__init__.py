@@ -1,0 +1,231 @@
+"""MI355X-native Gated DeltaNet chunked forward.
+
+A thin Python binding over ``libgdn.so`` (C ABI declared in include/gdn.h).
+Every step of the computation runs in the library's HIP kernels; this module
+only checks tensors, allocates outputs and workspace with torch and passes
+device pointers plus torch's current HIP stream.  There is no fallback: if the
+library is not built, every call raises.
+
+Functions (same names as the C entry points, without the ``gdn_`` prefix):
+  chunk_fwd(q, k, v, g, beta, h0=None, chunk=128, n_groups=0, ...) -> (o, h_T)
+  chunk_fold(k, v, g, beta, n_groups, chunk=128)                 -> (A, Bm)
+  compose_prefix(A, Bm, h_init=None, split_bf16=False)          -> (h_in, h_final)
+  chunk_transform(k, v, g, beta, chunk=128, want_T=False)       -> (G, T, W, U)
+  workspace_size(...), validate(...)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+
+F32, BF16 = 0, 1
+PREFIX_SPLIT_BF16 = 1
+STATUS = {0: "ok", -1: "null pointer", -2: "unsupported or inconsistent sizes",
+          -3: "unsupported dtype", -4: "misaligned pointer", -5: "workspace too small",
+          -6: "kernel launch failed"}
+
+
+class GdnShape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("B", "T", "H_qk", "H_v", "d_k", "d_v", "chunk", "n_groups", "dtype", "o_dtype")]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {STATUS.get(status, status)} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+SYMBOLS = ("gdn_status_str", "gdn_validate", "gdn_workspace_size", "gdn_chunk_fwd",
+           "gdn_chunk_fwd_stages", "gdn_chunk_fold", "gdn_compose_prefix", "gdn_chunk_transform")
+STAGE_PREP, STAGE_FOLD, STAGE_PREFIX, STAGE_WALK, STAGE_OUT, STAGE_ALL = 1, 2, 4, 8, 16, 31
+
+
+def lib():
+    """Load libgdn.so (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                               "(there is no fallback path)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        SP = ctypes.POINTER(GdnShape)
+        L.gdn_status_str.argtypes = [I]
+        L.gdn_status_str.restype = ctypes.c_char_p
+        L.gdn_validate.argtypes = [SP]
+        L.gdn_validate.restype = I
+        L.gdn_workspace_size.argtypes = [SP, ctypes.POINTER(SZ)]
+        L.gdn_workspace_size.restype = I
+        L.gdn_chunk_fwd.argtypes = [SP] + [P] * 9 + [SZ, P]
+        L.gdn_chunk_fwd.restype = I
+        L.gdn_chunk_fwd_stages.argtypes = [SP, I] + [P] * 9 + [SZ, P]
+        L.gdn_chunk_fwd_stages.restype = I
+        L.gdn_chunk_fold.argtypes = [SP] + [P] * 7 + [SZ, P]
+        L.gdn_chunk_fold.restype = I
+        L.gdn_compose_prefix.argtypes = [I, I, I, I] + [P] * 5 + [I, P]
+        L.gdn_compose_prefix.restype = I
+        L.gdn_chunk_transform.argtypes = [SP] + [P] * 8 + [P]
+        L.gdn_chunk_transform.restype = I
+        _lib = L
+    return _lib
+
+
+def _check(st: int, where: str):
+    if st != 0:
+        raise GdnError(st, where)
+
+
+def _dt(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return F32
+    if t == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t}")
+
+
+def make_shape(B, T, H_qk, H_v, d_k=128, d_v=128, chunk=128, n_groups=0,
+               dtype=torch.bfloat16, o_dtype=torch.float32) -> GdnShape:
+    return GdnShape(B, T, H_qk, H_v, d_k, d_v, chunk, n_groups, _dt(dtype), _dt(o_dtype))
+
+
+def validate(shape: GdnShape) -> int:
+    """Host-only check; returns the status code (0 = supported)."""
+    return int(lib().gdn_validate(ctypes.byref(shape)))
+
+
+def workspace_size(shape: GdnShape) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().gdn_workspace_size(ctypes.byref(shape), ctypes.byref(n)), "gdn_workspace_size")
+    return int(n.value)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, name, dtype=None, shape=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _inputs(q, k, v, g, beta):
+    B, T, Hqk, dk = k.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    dev = k.device
+    if q is not None:
+        _need(q, "q", k.dtype, (B, T, Hqk, dk), dev)
+    _need(k, "k", None, None, dev)
+    _need(v, "v", k.dtype, (B, T, Hv, dv), dev)
+    _need(g, "g", torch.float32, (B, T, Hv), dev)
+    _need(beta, "beta", torch.float32, (B, T, Hv), dev)
+    return B, T, Hqk, Hv, dk, dv, dev
+
+
+def chunk_fwd(q, k, v, g, beta, h0=None, chunk=128, n_groups=0, o_dtype=torch.float32,
+              output_final_state=True, workspace=None, out=None, final_state=None, stream=None,
+              stages=None):
+    """Gated DeltaNet chunked forward (gdn_chunk_fwd; gdn_chunk_fwd_stages when
+    ``stages`` is a mask of STAGE_* bits).
+
+    q, k [B,T,H_qk,d_k]; v [B,T,H_v,d_v] (bf16 or fp32); g, beta [B,T,H_v] fp32;
+    h0 [B,H_v,d_k,d_v] fp32 or None.  Returns (o [B,T,H_v,d_v] o_dtype, h_T or None)."""
+    B, T, Hqk, Hv, dk, dv, dev = _inputs(q, k, v, g, beta)
+    shape = make_shape(B, T, Hqk, Hv, dk, dv, chunk, n_groups, k.dtype, o_dtype)
+    if h0 is not None:
+        _need(h0, "h0", torch.float32, (B, Hv, dk, dv), dev)
+    need = workspace_size(shape)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    o = out if out is not None else torch.empty((B, T, Hv, dv), dtype=o_dtype, device=dev)
+    _need(o, "o", o_dtype, (B, T, Hv, dv), dev)
+    hT = None
+    if output_final_state:
+        hT = final_state if final_state is not None else torch.empty((B, Hv, dk, dv),
+                                                                    dtype=torch.float32, device=dev)
+        _need(hT, "h_T", torch.float32, (B, Hv, dk, dv), dev)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(o), _ptr(hT),
+            _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream(stream))
+    if stages is None:
+        _check(lib().gdn_chunk_fwd(ctypes.byref(shape), *args), "gdn_chunk_fwd")
+    else:
+        _check(lib().gdn_chunk_fwd_stages(ctypes.byref(shape), int(stages), *args),
+               "gdn_chunk_fwd_stages")
+    return o, hT
+
+
+def chunk_fold(k, v, g, beta, n_groups, chunk=128, workspace=None, stream=None):
+    """Per-group affine pairs (gdn_chunk_fold): A [B,H_v,G,d_k,d_k], Bm [B,H_v,G,d_k,d_v]."""
+    B, T, Hqk, Hv, dk, dv, dev = _inputs(None, k, v, g, beta)
+    shape = make_shape(B, T, Hqk, Hv, dk, dv, chunk, n_groups, k.dtype, torch.float32)
+    Gn = max(int(n_groups), 1)
+    need = workspace_size(shape)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    A = torch.empty((B, Hv, Gn, dk, dk), dtype=torch.float32, device=dev)
+    Bm = torch.empty((B, Hv, Gn, dk, dv), dtype=torch.float32, device=dev)
+    st = lib().gdn_chunk_fold(ctypes.byref(shape), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A),
+                              _ptr(Bm), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
+                              _stream(stream))
+    _check(st, "gdn_chunk_fold")
+    return A, Bm
+
+
+def compose_prefix(A, Bm, h_init=None, split_bf16=False, want_h_in=True, stream=None):
+    """Exclusive prefix of affine pairs (gdn_compose_prefix).
+    A [BH,n,d_k,d_k], Bm [BH,n,d_k,d_v] fp32; h_init [BH,d_k,d_v] or None.
+    Returns (h_in [BH,n,d_k,d_v] or None, h_final [BH,d_k,d_v])."""
+    BH, n, dk, _ = A.shape
+    dv = Bm.shape[3]
+    dev = A.device
+    _need(A, "A", torch.float32, None, dev)
+    _need(Bm, "Bm", torch.float32, (BH, n, dk, dv), dev)
+    if h_init is not None:
+        _need(h_init, "h_init", torch.float32, (BH, dk, dv), dev)
+    h_in = torch.empty((BH, n, dk, dv), dtype=torch.float32, device=dev) if want_h_in else None
+    h_fin = torch.empty((BH, dk, dv), dtype=torch.float32, device=dev)
+    st = lib().gdn_compose_prefix(BH, n, dk, dv, _ptr(A), _ptr(Bm), _ptr(h_init), _ptr(h_in),
+                                  _ptr(h_fin), PREFIX_SPLIT_BF16 if split_bf16 else 0,
+                                  _stream(stream))
+    _check(st, "gdn_compose_prefix")
+    return h_in, h_fin
+
+
+def chunk_transform(k, v, g, beta, chunk=128, want_T=False, stream=None):
+    """Intra-chunk transform (gdn_chunk_transform): G [B,H_v,N,C], T [B,H_v,N,C,C] or None,
+    W [B,H_v,N,C,d_k], U [B,H_v,N,C,d_v], all fp32."""
+    B, T, Hqk, Hv, dk, dv, dev = _inputs(None, k, v, g, beta)
+    shape = make_shape(B, T, Hqk, Hv, dk, dv, chunk, 0, k.dtype, torch.float32)
+    _check(validate(shape), "gdn_chunk_transform")
+    N = T // chunk
+    f = dict(dtype=torch.float32, device=dev)
+    G = torch.empty((B, Hv, N, chunk), **f)
+    Tm = torch.empty((B, Hv, N, chunk, chunk), **f) if want_T else None
+    W = torch.empty((B, Hv, N, chunk, dk), **f)
+    U = torch.empty((B, Hv, N, chunk, dv), **f)
+    st = lib().gdn_chunk_transform(ctypes.byref(shape), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                   _ptr(G), _ptr(Tm), _ptr(W), _ptr(U), _stream(stream))
+    _check(st, "gdn_chunk_transform")
+    return G, Tm, W, U

@@ -1,0 +1,302 @@
+// gdn_api.hip -- C ABI of the GDN chunked forward (declared in include/gdn.h).
+//
+// Host side only: argument checks, workspace carving and kernel launches on
+// the caller's stream.  No allocation, no synchronisation, no global state.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "gdn.h"
+#include "gdn_kernels.h"
+
+using namespace gdn;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+  size_t G, W, U, Hs, Vn, A, Bp, Hin, total;
+};
+
+int groups_of(const gdn_shape &s) { return s.n_groups > 1 ? s.n_groups : 1; }
+
+Layout layout(const gdn_shape &s) {
+  const size_t BH = (size_t)s.B * s.H_v, C = s.chunk, N = s.T / s.chunk;
+  const size_t J = groups_of(s);
+  Layout L{};
+  size_t off = 0;
+  L.G = off;  off += align_up(BH * N * C * 4);
+  L.W = off;  off += align_up(BH * N * C * D * 4);
+  L.U = off;  off += align_up(BH * N * C * D * 4);
+  L.Hs = off; off += align_up(BH * N * D * D * 4);
+  L.Vn = off; off += align_up(BH * N * C * D * 4);
+  if (J > 1) {
+    L.A = off;   off += align_up(BH * J * D * D * 4);
+    L.Bp = off;  off += align_up(BH * J * D * D * 4);
+    L.Hin = off; off += align_up(BH * J * D * D * 4);
+  }
+  L.total = off;
+  return L;
+}
+
+bool misaligned(const void *p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u); }
+
+gdn_status check_launch() {
+  return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+#define GDN_TRY(x)                       \
+  do {                                   \
+    gdn_status st_ = (x);                \
+    if (st_ != GDN_OK) return st_;       \
+  } while (0)
+
+// copies h0 (or zero) to h_T for an empty sequence
+__global__ void copy_state_kernel(const float *src, float *dst, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    dst[i] = src ? src[i] : 0.f;
+}
+
+FwdArgs base_args(const gdn_shape &s) {
+  FwdArgs a{};
+  a.B = s.B; a.T = s.T; a.Hqk = s.H_qk; a.Hv = s.H_v; a.N = s.T / s.chunk;
+  a.jobs = 1; a.cpj = a.N;
+  return a;
+}
+
+template <int C, typename TI, int MODE>
+gdn_status launch_prep(const FwdArgs &a, hipStream_t st) {
+  hipLaunchKernelGGL((prep_kernel<C, TI, MODE>), dim3(a.N, a.Hv, a.B), dim3(NT), 0, st, a);
+  return check_launch();
+}
+
+constexpr int kSlice = 32;
+
+template <int C, typename TI, int MODE, int KIND>
+gdn_status launch_walk(const FwdArgs &a, hipStream_t st) {
+  const int width = KIND == FOLD ? 2 * D : D;
+  hipLaunchKernelGGL((walk_kernel<C, TI, MODE, kSlice, KIND>), dim3(width / kSlice, a.Hv, a.B * a.jobs),
+                     dim3(NT), 0, st, a);
+  return check_launch();
+}
+
+template <int C, typename TI, int MODE, typename TO>
+gdn_status launch_out(const FwdArgs &a, hipStream_t st) {
+  hipLaunchKernelGGL((out_kernel<C, TI, MODE, kSlice, TO>), dim3(D / kSlice, a.N, a.B * a.Hv), dim3(NT), 0,
+                     st, a);
+  return check_launch();
+}
+
+gdn_status launch_prefix(int BH, int n, const float *A, const float *Bm, const float *h_init, float *h_in,
+                         float *h_final, bool split, hipStream_t st) {
+  PrefixArgs p{n, A, Bm, h_init, h_in, h_final};
+  if (split)
+    hipLaunchKernelGGL((prefix_kernel<kSlice, P_SPLIT_AB>), dim3(D / kSlice, BH), dim3(NT), 0, st, p);
+  else
+    hipLaunchKernelGGL((prefix_kernel<kSlice, P_F32>), dim3(D / kSlice, BH), dim3(NT), 0, st, p);
+  return check_launch();
+}
+
+template <int C, typename TI, int MODE>
+gdn_status run_fwd(const gdn_shape &s, int stages, const void *q, const void *k, const void *v, const float *g,
+                   const float *beta, const float *h0, void *o, float *h_T, char *ws, hipStream_t st) {
+  const Layout L = layout(s);
+  FwdArgs a = base_args(s);
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.o = o;
+  a.G = reinterpret_cast<float *>(ws + L.G);
+  a.W = reinterpret_cast<float *>(ws + L.W);
+  a.U = reinterpret_cast<float *>(ws + L.U);
+  a.Hs = reinterpret_cast<float *>(ws + L.Hs);
+  a.Vn = reinterpret_cast<float *>(ws + L.Vn);
+  if (stages & GDN_STAGE_PREP) GDN_TRY((launch_prep<C, TI, MODE>(a, st)));
+  const int J = groups_of(s);
+  if (J == 1) {
+    a.init = h0; a.init_per_job = 0; a.fin = h_T;
+    if (stages & GDN_STAGE_WALK) GDN_TRY((launch_walk<C, TI, MODE, WALK>(a, st)));
+  } else {
+    FwdArgs f = a;
+    f.jobs = J; f.cpj = a.N / J;
+    f.pairA = reinterpret_cast<float *>(ws + L.A);
+    f.pairB = reinterpret_cast<float *>(ws + L.Bp);
+    if (stages & GDN_STAGE_FOLD) GDN_TRY((launch_walk<C, TI, MODE, FOLD>(f, st)));
+    float *h_in = reinterpret_cast<float *>(ws + L.Hin);
+    if (stages & GDN_STAGE_PREFIX)
+      GDN_TRY(launch_prefix(s.B * s.H_v, J, f.pairA, f.pairB, h0, h_in, h_T, MODE == MODE_BF16, st));
+    FwdArgs r = a;
+    r.jobs = J; r.cpj = a.N / J;
+    r.init = h_in; r.init_per_job = 1; r.fin = nullptr;
+    if (stages & GDN_STAGE_WALK) GDN_TRY((launch_walk<C, TI, MODE, WALK>(r, st)));
+  }
+  if (!(stages & GDN_STAGE_OUT)) return GDN_OK;
+  if (s.o_dtype == GDN_F32) return launch_out<C, TI, MODE, float>(a, st);
+  return launch_out<C, TI, MODE, __bf16>(a, st);
+}
+
+template <int C, typename TI, int MODE>
+gdn_status run_fold(const gdn_shape &s, const void *k, const void *v, const float *g, const float *beta,
+                    float *A, float *Bm, char *ws, hipStream_t st) {
+  const Layout L = layout(s);
+  FwdArgs a = base_args(s);
+  a.k = k; a.v = v; a.g = g; a.beta = beta;
+  a.G = reinterpret_cast<float *>(ws + L.G);
+  a.W = reinterpret_cast<float *>(ws + L.W);
+  a.U = reinterpret_cast<float *>(ws + L.U);
+  GDN_TRY((launch_prep<C, TI, MODE>(a, st)));
+  const int J = groups_of(s);
+  a.jobs = J; a.cpj = a.N / J; a.pairA = A; a.pairB = Bm;
+  return launch_walk<C, TI, MODE, FOLD>(a, st);
+}
+
+template <int C, typename TI, int MODE>
+gdn_status run_transform(const gdn_shape &s, const void *k, const void *v, const float *g, const float *beta,
+                         float *G, float *Tm, float *W, float *U, hipStream_t st) {
+  FwdArgs a = base_args(s);
+  a.k = k; a.v = v; a.g = g; a.beta = beta; a.G = G; a.Tm = Tm; a.W = W; a.U = U;
+  return launch_prep<C, TI, MODE>(a, st);
+}
+
+struct FwdCall {
+  const gdn_shape &s; int stages; const void *q, *k, *v; const float *g, *beta, *h0; void *o; float *h_T;
+  char *w; hipStream_t st;
+  template <int C, typename TI, int MODE> gdn_status run() {
+    return run_fwd<C, TI, MODE>(s, stages, q, k, v, g, beta, h0, o, h_T, w, st);
+  }
+};
+struct FoldCall {
+  const gdn_shape &s; const void *k, *v; const float *g, *beta; float *A, *Bm; char *w; hipStream_t st;
+  template <int C, typename TI, int MODE> gdn_status run() {
+    return run_fold<C, TI, MODE>(s, k, v, g, beta, A, Bm, w, st);
+  }
+};
+struct TransformCall {
+  const gdn_shape &s; const void *k, *v; const float *g, *beta; float *G, *Tm, *W, *U; hipStream_t st;
+  template <int C, typename TI, int MODE> gdn_status run() {
+    return run_transform<C, TI, MODE>(s, k, v, g, beta, G, Tm, W, U, st);
+  }
+};
+
+// (dtype, chunk) -> instantiation
+template <typename F>
+gdn_status dispatch(const gdn_shape &s, F &&f) {
+  if (s.dtype == GDN_BF16 && s.chunk == 128) return f.template run<128, __bf16, MODE_BF16>();
+  if (s.dtype == GDN_BF16 && s.chunk == 64) return f.template run<64, __bf16, MODE_BF16>();
+  if (s.dtype == GDN_F32 && s.chunk == 64) return f.template run<64, float, MODE_F32>();
+  return GDN_ERR_SHAPE;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *gdn_status_str(gdn_status s) {
+  switch (s) {
+    case GDN_OK: return "ok";
+    case GDN_ERR_NULL: return "a required pointer is NULL";
+    case GDN_ERR_SHAPE: return "unsupported or inconsistent sizes";
+    case GDN_ERR_DTYPE: return "unsupported dtype";
+    case GDN_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case GDN_ERR_WORKSPACE: return "workspace too small";
+    case GDN_ERR_HIP: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+gdn_status gdn_validate(const gdn_shape *s) {
+  if (!s) return GDN_ERR_NULL;
+  if (s->dtype != GDN_F32 && s->dtype != GDN_BF16) return GDN_ERR_DTYPE;
+  if (s->o_dtype != GDN_F32 && s->o_dtype != GDN_BF16) return GDN_ERR_DTYPE;
+  if (s->B < 1 || s->T < 0 || s->H_qk < 1 || s->H_v < 1 || s->H_v % s->H_qk) return GDN_ERR_SHAPE;
+  if (s->d_k != D || s->d_v != D) return GDN_ERR_SHAPE;
+  if (s->chunk != 64 && s->chunk != 128) return GDN_ERR_SHAPE;
+  if (s->dtype == GDN_F32 && s->chunk != 64) return GDN_ERR_SHAPE;
+  if (s->T % s->chunk) return GDN_ERR_SHAPE;
+  if (s->n_groups < 0) return GDN_ERR_SHAPE;
+  const int N = s->T / s->chunk;
+  if (N > 65535 || (int64_t)s->B * s->H_v > 65535) return GDN_ERR_SHAPE;
+  if (s->n_groups > 1 && N > 0) {
+    if (N % s->n_groups) return GDN_ERR_SHAPE;
+    if ((int64_t)s->B * s->n_groups > 65535) return GDN_ERR_SHAPE;
+  }
+  return GDN_OK;
+}
+
+gdn_status gdn_workspace_size(const gdn_shape *s, size_t *bytes) {
+  if (!bytes) return GDN_ERR_NULL;
+  GDN_TRY(gdn_validate(s));
+  *bytes = layout(*s).total;
+  return GDN_OK;
+}
+
+gdn_status gdn_chunk_fwd(const gdn_shape *s, const void *q, const void *k, const void *v, const float *g,
+                         const float *beta, const float *h0, void *o, float *h_T, void *ws, size_t ws_bytes,
+                         void *hip_stream) {
+  return gdn_chunk_fwd_stages(s, GDN_STAGE_ALL, q, k, v, g, beta, h0, o, h_T, ws, ws_bytes, hip_stream);
+}
+
+gdn_status gdn_chunk_fwd_stages(const gdn_shape *s, int32_t stages, const void *q, const void *k, const void *v,
+                                const float *g, const float *beta, const float *h0, void *o, float *h_T,
+                                void *ws, size_t ws_bytes, void *hip_stream) {
+  GDN_TRY(gdn_validate(s));
+  if (stages & ~GDN_STAGE_ALL) return GDN_ERR_SHAPE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+  if (s->T == 0) {
+    if (misaligned(h0) || misaligned(h_T)) return GDN_ERR_ALIGN;
+    if (!h_T || !(stages & (GDN_STAGE_WALK | GDN_STAGE_PREFIX))) return GDN_OK;
+    const size_t n = (size_t)s->B * s->H_v * D * D;
+    hipLaunchKernelGGL(copy_state_kernel, dim3(256), dim3(256), 0, st, h0, h_T, n);
+    return check_launch();
+  }
+  if (!q || !k || !v || !g || !beta || !o || !ws) return GDN_ERR_NULL;
+  for (const void *p : {(const void *)q, (const void *)k, (const void *)v, (const void *)g,
+                        (const void *)beta, (const void *)h0, (const void *)o, (const void *)h_T,
+                        (const void *)ws})
+    if (misaligned(p)) return GDN_ERR_ALIGN;
+  if (ws_bytes < layout(*s).total) return GDN_ERR_WORKSPACE;
+  char *w = reinterpret_cast<char *>(ws);
+  FwdCall f{*s, stages, q, k, v, g, beta, h0, o, h_T, w, st};
+  return dispatch(*s, f);
+}
+
+gdn_status gdn_chunk_fold(const gdn_shape *s, const void *k, const void *v, const float *g, const float *beta,
+                          float *A, float *Bm, void *ws, size_t ws_bytes, void *hip_stream) {
+  GDN_TRY(gdn_validate(s));
+  if (s->T == 0) return GDN_ERR_SHAPE;
+  if (!k || !v || !g || !beta || !A || !Bm || !ws) return GDN_ERR_NULL;
+  for (const void *p : {(const void *)k, (const void *)v, (const void *)g, (const void *)beta, (const void *)A,
+                        (const void *)Bm, (const void *)ws})
+    if (misaligned(p)) return GDN_ERR_ALIGN;
+  if (ws_bytes < layout(*s).total) return GDN_ERR_WORKSPACE;
+  char *w = reinterpret_cast<char *>(ws);
+  hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+  FoldCall f{*s, k, v, g, beta, A, Bm, w, st};
+  return dispatch(*s, f);
+}
+
+gdn_status gdn_compose_prefix(int32_t batch_heads, int32_t n, int32_t d_k, int32_t d_v, const float *A,
+                              const float *Bm, const float *h_init, float *h_in, float *h_final, int32_t flags,
+                              void *hip_stream) {
+  if (batch_heads < 1 || batch_heads > 65535 || n < 1 || d_k != D || d_v != D) return GDN_ERR_SHAPE;
+  if (!A || !Bm || (!h_in && !h_final)) return GDN_ERR_NULL;
+  for (const void *p : {(const void *)A, (const void *)Bm, (const void *)h_init, (const void *)h_in,
+                        (const void *)h_final})
+    if (misaligned(p)) return GDN_ERR_ALIGN;
+  return launch_prefix(batch_heads, n, A, Bm, h_init, h_in, h_final, (flags & GDN_PREFIX_SPLIT_BF16) != 0,
+                       reinterpret_cast<hipStream_t>(hip_stream));
+}
+
+gdn_status gdn_chunk_transform(const gdn_shape *s, const void *k, const void *v, const float *g,
+                               const float *beta, float *G, float *Tm, float *W, float *U, void *hip_stream) {
+  GDN_TRY(gdn_validate(s));
+  if (s->T == 0) return GDN_OK;
+  if (!k || !v || !g || !beta || !G || !W || !U) return GDN_ERR_NULL;
+  for (const void *p : {(const void *)k, (const void *)v, (const void *)g, (const void *)beta, (const void *)G,
+                        (const void *)Tm, (const void *)W, (const void *)U})
+    if (misaligned(p)) return GDN_ERR_ALIGN;
+  hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+  TransformCall f{*s, k, v, g, beta, G, Tm, W, U, st};
+  return dispatch(*s, f);
+}
+
+}  // extern "C"

@@ -1,0 +1,88 @@
+// gdn_mfma.h -- gfx950 matrix-core building blocks for the GDN kernels.
+//
+// Every product in the kernels is built from one 16x16 output tile per wave
+// and a contraction (k) loop in blocks of 32.  Operands are staged in LDS; for
+// a k-block each lane fetches 8 consecutive k-values of one row of A and of
+// one column of B:
+//     lane l:  A row  = l % 16,  k = 8*(l/16) + j   (j = 0..7)
+//              B col  = l % 16,  k = 8*(l/16) + j
+//     result:  lane l holds D[4*(l/16) + i][l % 16], i = 0..3
+// This is the operand layout of v_mfma_f32_16x16x32_bf16.  The fp32 matrix
+// core instruction v_mfma_f32_16x16x4_f32 takes one k-value per lane group;
+// feeding it j = 0..7 in turn covers the same 32 k-values (the k order of a
+// sum is free as long as A and B agree), so both precisions share one
+// fetch layout and one result layout.
+//
+// Precision policies for one product (chosen per product, see the kernels):
+//   P_BF16      both operands rounded to bf16 (exact when they are bf16 data)
+//   P_SPLIT_A   A = a_hi + a_lo (two bf16), B bf16: 2 bf16 MFMAs
+//   P_SPLIT_B   A bf16, B split: 2 bf16 MFMAs
+//   P_SPLIT_AB  both split, a_lo*b_lo dropped: 3 bf16 MFMAs (~fp32 accuracy)
+//   P_F32       fp32 matrix-core products (exact fp32 multiply)
+#pragma once
+#include <hip/hip_runtime.h>
+
+namespace gdn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+enum : int { P_BF16 = 0, P_SPLIT_A = 1, P_SPLIT_B = 2, P_SPLIT_AB = 3, P_F32 = 4 };
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+template <int P>
+__device__ __forceinline__ void mma_k32(f32x4 &c, const float (&a)[8], const float (&b)[8]) {
+  if constexpr (P == P_F32) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], c, 0, 0, 0);
+  } else {
+    bf16x8 ah, bh;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      ah[j] = (__bf16)a[j];
+      bh[j] = (__bf16)b[j];
+    }
+    // small terms first
+    if constexpr (P == P_SPLIT_A || P == P_SPLIT_AB) {
+      bf16x8 al;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) al[j] = (__bf16)(a[j] - (float)ah[j]);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, c, 0, 0, 0);
+    }
+    if constexpr (P == P_SPLIT_B || P == P_SPLIT_AB) {
+      bf16x8 bl;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) bl[j] = (__bf16)(b[j] - (float)bh[j]);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, c, 0, 0, 0);
+    }
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, c, 0, 0, 0);
+  }
+}
+
+// 8 consecutive LDS elements -> float[8]  (p 16-byte aligned)
+__device__ __forceinline__ void ld8(const float *p, float (&x)[8]) {
+  const float4 u = *reinterpret_cast<const float4 *>(p);
+  const float4 w = *reinterpret_cast<const float4 *>(p + 4);
+  x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
+  x[4] = w.x; x[5] = w.y; x[6] = w.z; x[7] = w.w;
+}
+__device__ __forceinline__ void ld8(const __bf16 *p, float (&x)[8]) {
+  const bf16x8 u = *reinterpret_cast<const bf16x8 *>(p);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = (float)u[j];
+}
+// 8 LDS elements with a stride
+template <typename T>
+__device__ __forceinline__ void ld8s(const T *p, int stride, float (&x)[8]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = (float)p[j * stride];
+}
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }
+
+}  // namespace gdn

@@ -1,0 +1,300 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Tolerances: max-abs error <= 1e-4 * RMS for fp32 inputs and <= 2e-2 * RMS for
+bf16 inputs, on o and on h_T.  Each tensor is gated against the RMS of the
+oracle's own tensor and also against RMS(o) (the two readings of "RMS(o)"
+for h_T); both must pass.  Intermediate steps (decay cumsum, UT inverse, W,
+U, fold pairs, prefix) are checked against the oracle's fp64 values of the
+same quantities.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import WORKLOADS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+@pytest.fixture(scope="module")
+def gdn():
+    import linear_attention_rnn_gdn_amd as g
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    g.lib()
+    return g
+
+
+def _rms(x):
+    return float(np.sqrt(np.mean(np.asarray(x, np.float64) ** 2)))
+
+
+def _err(got, ref):
+    return float(np.abs(np.asarray(got, np.float64) - ref).max())
+
+
+def _check(name, got, ref, tol, rms_o):
+    e = _err(got, ref)
+    lim = tol * min(_rms(ref), rms_o)
+    print(f"  {name}: max-abs {e:.3e}  limit {lim:.3e}  (rel to RMS {e / max(_rms(ref), 1e-30):.2e})",
+          flush=True)
+    assert e <= lim, f"{name}: max-abs error {e:.3e} > {lim:.3e}"
+
+
+def _cpu(x):
+    return None if x is None else x.detach().cpu()
+
+
+def _run_and_compare(gdn, w, x, heads=None, cols=None, o_dtype=torch.float32, n_groups=None):
+    ng = w.n_groups if n_groups is None else n_groups
+    o, hT = gdn.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"], chunk=w.chunk,
+                          n_groups=ng, o_dtype=o_dtype)
+    torch.cuda.synchronize()
+    hl, hh = heads if heads else (0, w.Hv)
+    cl, ch = cols if cols else (0, w.dv)
+    if heads or cols:
+        hq_lo = hl // (w.Hv // w.Hqk)
+        hq_hi = (hh - 1) // (w.Hv // w.Hqk) + 1
+        rep = w.Hv // w.Hqk
+        # the oracle sees only the needed heads: re-index value heads from 0
+        sub = dict(
+            q=_cpu(x["q"][:, :, hq_lo:hq_hi]), k=_cpu(x["k"][:, :, hq_lo:hq_hi]),
+            v=_cpu(x["v"][:, :, hq_lo * rep:hq_hi * rep]),
+            g=_cpu(x["g"][:, :, hq_lo * rep:hq_hi * rep]),
+            beta=_cpu(x["beta"][:, :, hq_lo * rep:hq_hi * rep]),
+            h0=_cpu(x["h0"][:, hq_lo * rep:hq_hi * rep]) if x["h0"] is not None else None)
+        o_ref, h_ref = oracle.fwd(**sub, heads=(hl - hq_lo * rep, hh - hq_lo * rep), cols=(cl, ch))
+    else:
+        o_ref, h_ref = oracle.fwd(**{kk: _cpu(vv) for kk, vv in x.items()})
+    o_got = o[:, :, hl:hh, cl:ch].float().cpu().numpy()
+    h_got = hT[:, hl:hh, :, cl:ch].cpu().numpy()
+    return o_got, h_got, o_ref, h_ref
+
+
+# ---------------------------------------------------------------------------
+# rows a1-a4: decay cumsum, UT inverse, W, U
+
+
+@pytest.mark.parametrize("dtype,C", [("bf16", 128), ("bf16", 64), ("f32", 64)])
+def test_chunk_transform_matches_oracle(gdn, dtype, C):
+    w = WORKLOADS["tiny"].replace(T=4 * C, Hqk=1, Hv=2, chunk=C, dtype=dtype)
+    x = make_inputs(w, device="cuda", seed=7)
+    G, Tm, W, U = gdn.chunk_transform(x["k"], x["v"], x["g"], x["beta"], chunk=C, want_T=True)
+    torch.cuda.synchronize()
+    ch = oracle.chunked
+    k = x["k"].float().cpu().numpy()
+    v = x["v"].float().cpu().numpy()
+    g = x["g"].cpu().numpy()
+    beta = x["beta"].cpu().numpy()
+    tol = 1e-5 if dtype == "f32" else 2e-4
+    for hv in range(2):
+        for n in range(4):
+            s = slice(n * C, (n + 1) * C)
+            Gr = ch.decay_cumsum(g[0, s, hv])
+            S = ch.gated_strict_kkt(k[0, s, 0], beta[0, s, hv], Gr)
+            Tr = ch.ut_inverse(S)
+            Wr, Ur, _ = ch.wy(Tr, k[0, s, 0], v[0, s, hv], beta[0, s, hv], Gr)
+            assert _err(G[0, hv, n].cpu().numpy(), Gr) <= 1e-5 * max(1, np.abs(Gr).max())
+            assert _err(Tm[0, hv, n].cpu().numpy(), Tr) <= tol * max(1, np.abs(Tr).max())
+            assert _err(W[0, hv, n].cpu().numpy(), Wr) <= tol * max(_rms(Wr), 1e-3) * 10
+            assert _err(U[0, hv, n].cpu().numpy(), Ur) <= tol * max(_rms(Ur), 1e-3) * 10
+            # (I + S) T = I on the GPU's T
+            res = (np.eye(C) + S) @ Tm[0, hv, n].cpu().numpy().astype(np.float64) - np.eye(C)
+            assert np.abs(res).max() <= tol * 10
+
+
+def test_ut_inverse_all_ones_gram(gdn):
+    # unit keys all equal, beta = 1, g = 0: S = strict-lower ones, T = I - subdiagonal
+    C = 128
+    w = WORKLOADS["tiny"].replace(T=C, Hqk=1, Hv=1, chunk=C, dtype="bf16")
+    x = make_inputs(w, device="cuda", seed=1)
+    e = torch.zeros(128, device="cuda")
+    e[3] = 1.0
+    x["k"][:] = e.to(torch.bfloat16)
+    x["beta"][:] = 1.0
+    x["g"][:] = 0.0
+    _, Tm, _, _ = gdn.chunk_transform(x["k"], x["v"], x["g"], x["beta"], chunk=C, want_T=True)
+    ref = np.eye(C) - np.eye(C, k=-1)
+    assert _err(Tm[0, 0, 0].cpu().numpy(), ref) <= 1e-5
+
+
+# ---------------------------------------------------------------------------
+# rows a5-a6 end to end, single walk
+
+
+@pytest.mark.parametrize("name", ["tiny", "qwen3next_8b_layer"])
+def test_forward_full_size(gdn, name):
+    w = WORKLOADS[name]
+    x = make_inputs(w, device="cuda")
+    o, h, o_ref, h_ref = _run_and_compare(gdn, w, x)
+    ro = _rms(o_ref)
+    _check("o", o, o_ref, TOL[w.dtype], ro)
+    _check("h_T", h, h_ref, TOL[w.dtype], ro)
+
+
+def test_forward_dense_layer_full_size(gdn):
+    w = WORKLOADS["dense_d4096_layer"]
+    x = make_inputs(w, device="cuda")
+    o, h, o_ref, h_ref = _run_and_compare(gdn, w, x)
+    ro = _rms(o_ref)
+    _check("o", o, o_ref, TOL[w.dtype], ro)
+    _check("h_T", h, h_ref, TOL[w.dtype], ro)
+
+
+@pytest.mark.parametrize("dtype,C,T,Hqk,Hv,h0", [
+    ("bf16", 64, 640, 2, 4, 0.02),
+    ("bf16", 128, 128, 1, 1, 0.0),        # a single chunk
+    ("f32", 64, 64 * 7, 1, 3, 0.5),        # odd chunk count, strong h0
+    ("bf16", 128, 128 * 9, 3, 6, 0.1),
+])
+def test_forward_small_shapes(gdn, dtype, C, T, Hqk, Hv, h0):
+    w = WORKLOADS["tiny"].replace(T=T, Hqk=Hqk, Hv=Hv, chunk=C, dtype=dtype, h0_std=h0, B=2)
+    x = make_inputs(w, device="cuda", seed=T + Hv)
+    o, h, o_ref, h_ref = _run_and_compare(gdn, w, x)
+    ro = _rms(o_ref)
+    _check("o", o, o_ref, TOL[dtype], ro)
+    _check("h_T", h, h_ref, TOL[dtype], ro)
+
+
+def test_bf16_output(gdn):
+    # a bf16 o carries its own rounding (half an ulp of |o|) on top of the
+    # computation error
+    w = WORKLOADS["tiny"].replace(T=1024, Hqk=2, Hv=4, chunk=128, dtype="bf16", h0_std=0.02)
+    x = make_inputs(w, device="cuda", seed=3)
+    o, h, o_ref, h_ref = _run_and_compare(gdn, w, x, o_dtype=torch.bfloat16)
+    ro = _rms(o_ref)
+    bound = 2e-2 * ro + np.abs(o_ref) * 2.0 ** -8
+    assert (np.abs(o - o_ref) <= bound).all()
+    _check("h_T", h, h_ref, 2e-2, ro)
+
+
+def test_empty_sequence_returns_initial_state(gdn):
+    w = WORKLOADS["tiny"].replace(T=0, dtype="bf16", chunk=128, h0_std=0.3)
+    x = make_inputs(w, device="cuda", seed=5)
+    o, hT = gdn.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"], chunk=128)
+    torch.cuda.synchronize()
+    assert o.numel() == 0
+    assert torch.equal(hT, x["h0"])
+    o, hT = gdn.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], None, chunk=128)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(hT) == 0
+
+
+def test_gqa_equals_broadcast_mha_on_gpu(gdn):
+    w = WORKLOADS["tiny"].replace(T=512, Hqk=2, Hv=4, chunk=128, dtype="bf16", h0_std=0.02)
+    x = make_inputs(w, device="cuda", seed=9)
+    o1, h1 = gdn.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"], chunk=128)
+    q2 = x["q"].repeat_interleave(2, dim=2).contiguous()
+    k2 = x["k"].repeat_interleave(2, dim=2).contiguous()
+    o2, h2 = gdn.chunk_fwd(q2, k2, x["v"], x["g"], x["beta"], x["h0"], chunk=128)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
+
+
+def test_run_to_run_bitwise_determinism(gdn):
+    w = WORKLOADS["qwen3next_8b_layer"]
+    x = make_inputs(w, device="cuda")
+    a = gdn.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"], chunk=128)
+    b = gdn.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"], chunk=128)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+# ---------------------------------------------------------------------------
+# rows a7-a9: fold, exclusive prefix, replay
+
+
+@pytest.mark.parametrize("dtype,C", [("bf16", 128), ("f32", 64)])
+def test_fold_matches_oracle(gdn, dtype, C):
+    w = WORKLOADS["tiny"].replace(T=C * 8, Hqk=1, Hv=2, chunk=C, dtype=dtype)
+    x = make_inputs(w, device="cuda", seed=11, g_const=-0.01)   # weak decay: A far from 0
+    A, Bm = gdn.chunk_fold(x["k"], x["v"], x["g"], x["beta"], n_groups=4, chunk=C)
+    torch.cuda.synchronize()
+    Ar, Br = oracle.fold(_cpu(x["k"]), _cpu(x["v"]), _cpu(x["g"]), _cpu(x["beta"]), n_groups=4)
+    # A decays towards zero with most entries tiny, so errors are scaled by
+    # the largest entry.  bf16 path: the walk's W x state product takes bf16
+    # operands (relative 2^-9 each) over 2 chunks per group -> 1e-2 of max.
+    # fp32 path: fp32 products, 1e-4 of max.
+    tol = 1e-2 if dtype == "bf16" else 1e-4
+    assert _err(A.cpu().numpy(), Ar) <= tol * np.abs(Ar).max()
+    assert _err(Bm.cpu().numpy(), Br) <= tol * np.abs(Br).max()
+
+
+@pytest.mark.parametrize("split", [False, True])
+def test_compose_prefix_matches_oracle(gdn, split):
+    BH, n = 3, 9
+    gen = torch.Generator().manual_seed(12)
+    A = (torch.randn(BH, n, 128, 128, generator=gen) * (0.9 / 128 ** 0.5)).float()
+    Bm = torch.randn(BH, n, 128, 128, generator=gen).float()
+    h0 = torch.randn(BH, 128, 128, generator=gen).float()
+    h_in, h_fin = gdn.compose_prefix(A.cuda(), Bm.cuda(), h0.cuda(), split_bf16=split)
+    torch.cuda.synchronize()
+    r_in, r_fin = oracle.prefix(A.numpy(), Bm.numpy(), h0.numpy())
+    # fp32 products: 128-term dots at unit roundoff 6e-8 carried over 9
+    # contracting steps stay within ~1e-5 of RMS; hi/lo bf16 splitting drops
+    # terms of relative size 2^-16 -> 1e-4.
+    tol = 1e-4 if split else 2e-5
+    assert _err(h_in.cpu().numpy(), r_in) <= tol * _rms(r_in)
+    assert _err(h_fin.cpu().numpy(), r_fin) <= tol * _rms(r_fin)
+
+
+@pytest.mark.parametrize("ng", [2, 4, 16])
+def test_group_count_invariance(gdn, ng):
+    w = WORKLOADS["qwen3next_8b_layer"].replace(T=2048)
+    x = make_inputs(w, device="cuda", seed=13)
+    o, h, o_ref, h_ref = _run_and_compare(gdn, w, x, n_groups=ng)
+    ro = _rms(o_ref)
+    _check("o", o, o_ref, 2e-2, ro)
+    _check("h_T", h, h_ref, 2e-2, ro)
+
+
+def test_groups_weak_decay_compose_matters(gdn):
+    # g = 0 and small beta keep each group's affine map far from zero, so the
+    # incoming states really carry information across groups
+    w = WORKLOADS["tiny"].replace(T=2048, Hqk=2, Hv=2, chunk=128, dtype="bf16", h0_std=0.02, B=1)
+    x = make_inputs(w, device="cuda", seed=14, g_const=0.0, beta_scale=0.1)
+    o, h, o_ref, h_ref = _run_and_compare(gdn, w, x, n_groups=8)
+    ro = _rms(o_ref)
+    _check("o", o, o_ref, 2e-2, ro)
+    _check("h_T", h, h_ref, 2e-2, ro)
+    # negative control: groups replayed from a zero state miss by far
+    L = 256
+    bad = []
+    for j in range(8):
+        s = slice(j * L, (j + 1) * L)
+        oj, _ = gdn.chunk_fwd(x["q"][:, s].contiguous(), x["k"][:, s].contiguous(),
+                              x["v"][:, s].contiguous(), x["g"][:, s].contiguous(),
+                              x["beta"][:, s].contiguous(), None, chunk=128)
+        bad.append(oj)
+    bad = torch.cat(bad, dim=1).float().cpu().numpy()
+    assert _err(bad, o_ref) > 10 * 2e-2 * ro
+
+
+def test_long_sequence_reduced(gdn):
+    # the long-sequence workload's shape and group structure at 1/16 of its length
+    w = WORKLOADS["long_256k"].replace(T=16384, n_groups=16)
+    x = make_inputs(w, device="cuda")
+    o, h, o_ref, h_ref = _run_and_compare(gdn, w, x)
+    ro = _rms(o_ref)
+    _check("o", o, o_ref, 2e-2, ro)
+    _check("h_T", h, h_ref, 2e-2, ro)
+
+
+@pytest.mark.parametrize("name", ["long_256k", "million_1m"])
+def test_long_sequence_full_size_sampled(gdn, name):
+    # full length, in the benchmark's launch configuration; the oracle walks
+    # the whole sequence for a sample of one value head and 16 state columns
+    w = WORKLOADS[name]
+    x = make_inputs(w, device="cuda")
+    hv = 5
+    o, h, o_ref, h_ref = _run_and_compare(gdn, w, x, heads=(hv, hv + 1), cols=(32, 48))
+    ro = _rms(o_ref)
+    _check("o", o, o_ref, 2e-2, ro)
+    _check("h_T", h, h_ref, 2e-2, ro)
+    # the same workload as one sequential walk agrees with the grouped result
+    del o, h
+    torch.cuda.empty_cache()
