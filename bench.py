@@ -65,7 +65,7 @@ def stage_bytes(w, o_bytes=4):
     v_b = tok * w.Hv * dv * s
     gb_b = 8 * tok * w.Hv
     G_b = 4 * tok * w.Hv
-    W_b = 4 * tok * w.Hv * dk
+    W_b = s * tok * w.Hv * dk
     U_b = 4 * tok * w.Hv * dv
     Hs_b = 4 * BHv * N * dk * dv
     Vn_b = 4 * tok * w.Hv * dv
@@ -73,16 +73,17 @@ def stage_bytes(w, o_bytes=4):
     h0_b = st if w.h0_std > 0 else 0
     pairs = 4 * BHv * J * (dk * dk + dk * dv)
     hin = 4 * BHv * J * dk * dv
+    Kt_b = W_b                      # K^T per chunk and value head, input dtype
     out = {
-        "prep": k_b + v_b + gb_b + G_b + W_b + U_b,
+        "prep": k_b + v_b + gb_b + G_b + W_b + Kt_b + U_b,
         "out": q_b + k_b + G_b + Hs_b + Vn_b + tok * w.Hv * dv * o_bytes,
     }
     if J == 1:
-        out["walk"] = W_b + U_b + G_b + k_b + h0_b + Hs_b + Vn_b + st
+        out["walk"] = W_b + U_b + G_b + Kt_b + h0_b + Hs_b + Vn_b + st
     else:
-        out["fold"] = W_b + U_b + G_b + k_b + pairs
+        out["fold"] = W_b + U_b + G_b + Kt_b + pairs
         out["prefix"] = pairs + h0_b + hin + st
-        out["walk"] = W_b + U_b + G_b + k_b + hin + Hs_b + Vn_b
+        out["walk"] = W_b + U_b + G_b + Kt_b + hin + Hs_b + Vn_b
     return out
 
 

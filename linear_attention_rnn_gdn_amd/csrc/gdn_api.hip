@@ -17,7 +17,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t G, W, U, Hs, Vn, A, Bp, Hin, total;
+  size_t G, W, Kt, U, Hs, Vn, A, Bp, Hin, total;
 };
 
 int groups_of(const gdn_shape &s) { return s.n_groups > 1 ? s.n_groups : 1; }
@@ -25,10 +25,12 @@ int groups_of(const gdn_shape &s) { return s.n_groups > 1 ? s.n_groups : 1; }
 Layout layout(const gdn_shape &s) {
   const size_t BH = (size_t)s.B * s.H_v, C = s.chunk, N = s.T / s.chunk;
   const size_t J = groups_of(s);
+  const size_t in_bytes = s.dtype == GDN_BF16 ? 2 : 4;
   Layout L{};
   size_t off = 0;
   L.G = off;  off += align_up(BH * N * C * 4);
-  L.W = off;  off += align_up(BH * N * C * D * 4);
+  L.W = off;  off += align_up(BH * N * C * D * in_bytes);
+  L.Kt = off; off += align_up(BH * N * C * D * in_bytes);
   L.U = off;  off += align_up(BH * N * C * D * 4);
   L.Hs = off; off += align_up(BH * N * D * D * 4);
   L.Vn = off; off += align_up(BH * N * C * D * 4);
@@ -66,9 +68,9 @@ FwdArgs base_args(const gdn_shape &s) {
   return a;
 }
 
-template <int C, typename TI, int MODE>
+template <int C, typename TI, int MODE, bool FWD = true>
 gdn_status launch_prep(const FwdArgs &a, hipStream_t st) {
-  hipLaunchKernelGGL((prep_kernel<C, TI, MODE>), dim3(a.N, a.Hv, a.B), dim3(NT), 0, st, a);
+  hipLaunchKernelGGL((prep_kernel<C, TI, MODE, FWD>), dim3(a.N, a.Hv, a.B), dim3(NT), 0, st, a);
   return check_launch();
 }
 
@@ -77,25 +79,26 @@ constexpr int kSlice = 32;
 template <int C, typename TI, int MODE, int KIND>
 gdn_status launch_walk(const FwdArgs &a, hipStream_t st) {
   const int width = KIND == FOLD ? 2 * D : D;
-  hipLaunchKernelGGL((walk_kernel<C, TI, MODE, kSlice, KIND>), dim3(width / kSlice, a.Hv, a.B * a.jobs),
-                     dim3(NT), 0, st, a);
+  const long blocks = (long)(width / kSlice) * a.B * a.Hv * a.jobs;
+  hipLaunchKernelGGL((walk_kernel<C, TI, MODE, kSlice, KIND>), dim3((unsigned)blocks), dim3(WALK_NT), 0, st, a);
   return check_launch();
 }
 
 template <int C, typename TI, int MODE, typename TO>
 gdn_status launch_out(const FwdArgs &a, hipStream_t st) {
-  hipLaunchKernelGGL((out_kernel<C, TI, MODE, kSlice, TO>), dim3(D / kSlice, a.N, a.B * a.Hv), dim3(NT), 0,
-                     st, a);
+  const long blocks = (long)(D / kSlice) * a.N * a.B * a.Hv;
+  hipLaunchKernelGGL((out_kernel<C, TI, MODE, kSlice, TO>), dim3((unsigned)blocks), dim3(NT), 0, st, a);
   return check_launch();
 }
 
 gdn_status launch_prefix(int BH, int n, const float *A, const float *Bm, const float *h_init, float *h_in,
                          float *h_final, bool split, hipStream_t st) {
-  PrefixArgs p{n, A, Bm, h_init, h_in, h_final};
+  PrefixArgs p{BH, n, A, Bm, h_init, h_in, h_final};
+  const unsigned blocks = (unsigned)(D / kSlice) * BH;
   if (split)
-    hipLaunchKernelGGL((prefix_kernel<kSlice, P_SPLIT_AB>), dim3(D / kSlice, BH), dim3(NT), 0, st, p);
+    hipLaunchKernelGGL((prefix_kernel<kSlice, P_SPLIT_AB>), dim3(blocks), dim3(NT), 0, st, p);
   else
-    hipLaunchKernelGGL((prefix_kernel<kSlice, P_F32>), dim3(D / kSlice, BH), dim3(NT), 0, st, p);
+    hipLaunchKernelGGL((prefix_kernel<kSlice, P_F32>), dim3(blocks), dim3(NT), 0, st, p);
   return check_launch();
 }
 
@@ -106,7 +109,8 @@ gdn_status run_fwd(const gdn_shape &s, int stages, const void *q, const void *k,
   FwdArgs a = base_args(s);
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.o = o;
   a.G = reinterpret_cast<float *>(ws + L.G);
-  a.W = reinterpret_cast<float *>(ws + L.W);
+  a.W = ws + L.W;
+  a.Kt = ws + L.Kt;
   a.U = reinterpret_cast<float *>(ws + L.U);
   a.Hs = reinterpret_cast<float *>(ws + L.Hs);
   a.Vn = reinterpret_cast<float *>(ws + L.Vn);
@@ -141,7 +145,8 @@ gdn_status run_fold(const gdn_shape &s, const void *k, const void *v, const floa
   FwdArgs a = base_args(s);
   a.k = k; a.v = v; a.g = g; a.beta = beta;
   a.G = reinterpret_cast<float *>(ws + L.G);
-  a.W = reinterpret_cast<float *>(ws + L.W);
+  a.W = ws + L.W;
+  a.Kt = ws + L.Kt;
   a.U = reinterpret_cast<float *>(ws + L.U);
   GDN_TRY((launch_prep<C, TI, MODE>(a, st)));
   const int J = groups_of(s);
@@ -154,7 +159,7 @@ gdn_status run_transform(const gdn_shape &s, const void *k, const void *v, const
                          float *G, float *Tm, float *W, float *U, hipStream_t st) {
   FwdArgs a = base_args(s);
   a.k = k; a.v = v; a.g = g; a.beta = beta; a.G = G; a.Tm = Tm; a.W = W; a.U = U;
-  return launch_prep<C, TI, MODE>(a, st);
+  return launch_prep<C, TI, MODE, false>(a, st);
 }
 
 struct FwdCall {

@@ -15,19 +15,43 @@
 // are the reading under which the affine step equals the per-token rule.
 //
 // Kernels (all 256 threads = 4 waves of 64):
-//   prep_kernel    one workgroup per (chunk, value head, batch): G, S, T, W, U
-//   walk_kernel    one workgroup per (column slice, value head, batch*job):
-//                  the sequential chunk walk with the state slice resident in
+//   prep_kernel    one workgroup per (chunk, value head, batch): G, S, T, W, U,
+//                  and K^T for the walk
+//   walk_kernel    one workgroup per (column slice, value head, batch, job):
+//                  the sequential chunk walk.  Each wave keeps its part of the
+//                  fp32 state in registers; W and K^T operand fragments come
+//                  straight from global memory one chunk ahead; only a bf16
+//                  copy of the state and the corrected values V' pass through
 //                  LDS.  Modes: WALK (state = h, writes chunk-start states and
 //                  V') and FOLD (state = the augmented [A | B] of a group,
 //                  started from [I | 0]; writes the group's pair).
 //   prefix_kernel  one workgroup per (column slice, bh): exclusive prefix of
 //                  the groups' affine pairs.
-//   out_kernel     one workgroup per (column slice, chunk, bh): the output.
+//   out_kernel     one workgroup per (column slice, chunk, bh): the output,
+//                  with P^T kept in registers between its two products.
 //
-// Workspace tensors (fp32):  G [BH,N,C]  W [BH,N,C,D]  U [BH,N,C,D]
-//   Hs [BH,N,D,D] chunk-start states   Vn [BH,N,C,D] corrected values V'.
+// Workspace tensors (cb = bh*N + n indexes a chunk of a value head).  The
+// tensors that pass from one kernel to the next are stored fragment-major: in
+// the order in which the consumer's lanes read them, so that each 16-byte
+// per-lane load or store of a wave covers 1 KB of consecutive bytes.
+// (Row-major tiles read in matrix-core operand layout put consecutive lanes
+// on different rows, and each such instruction breaks into dozens of memory
+// requests.)  Lane l = lr + 16 g (lr = l % 16, g = l / 16).
+//   G   [cb][C] fp32 decay cumsum
+//   Wf  [cb][C/16][D/32][64][8]  W[16m + lr][32kb + 8g + j], input dtype
+//   Ktf [cb][D/16][C/32][64][8]  K[32kb + 8g + j][16m + lr], input dtype
+//   Uf  [cb][C/16][D/16][64][4]  U[16m + 4g + i][16nd + lr], fp32
+//   Hsf [cb][D/S][D/16][S/16][64][4]  chunk-start state h[16m + 4g + i][c0 + 16ni + lr]
+//   Vnf [cb][D/S][C/16][S/16][64][4]  corrected values V'[16m + 4g + i][c0 + 16ni + lr]
+// (S = column-slice width, c0 = S * slice.)  Decays are evaluated as exp2 of
+// log2-scaled cumsums (one v_exp_f32 each).
+//
+// Workgroups are numbered 1-D.  The hardware places workgroup i on XCD i % 8;
+// xcd_unit() hands all column slices of one (head, chunk or job) to one XCD
+// so they share that XCD's L2 for the operands they all read.
 #pragma once
+#include <type_traits>
+
 #include "gdn_mfma.h"
 
 namespace gdn {
@@ -46,16 +70,34 @@ template <int MODE> struct Prec {
   static constexpr int ladder = MODE == MODE_F32 ? P_F32 : P_SPLIT_AB;
   static constexpr int wy = MODE == MODE_F32 ? P_F32 : P_SPLIT_A;       // T' (fp32) x K/V (data)
   static constexpr int wh = MODE == MODE_F32 ? P_F32 : P_BF16;          // W x h
-  static constexpr int kv = MODE == MODE_F32 ? P_F32 : P_SPLIT_B;       // K^T x V'
-  static constexpr int qh = MODE == MODE_F32 ? P_F32 : P_SPLIT_B;       // Q x h
-  static constexpr int pv = MODE == MODE_F32 ? P_F32 : P_SPLIT_AB;      // P x V'
+  static constexpr int kv = MODE == MODE_F32 ? P_F32 : P_SPLIT_B;       // K^T (data) x V'
+  static constexpr int hq = MODE == MODE_F32 ? P_F32 : P_SPLIT_A;       // h^T x Q^T (data)
+  static constexpr int pv = MODE == MODE_F32 ? P_F32 : P_SPLIT_AB;      // V'^T x P^T
 };
+
+// 1-D workgroup index -> (unit, part) with the `parts` workgroups of a unit on
+// one XCD (falls back to unit-major order when units is not a multiple of 8).
+__device__ __forceinline__ void xcd_unit(int L, int parts, int units, int &unit, int &part) {
+  if ((units & 7) == 0) {
+    const int x = L & 7, i = L >> 3;
+    unit = (i / parts) * 8 + x;
+    part = i % parts;
+  } else {
+    unit = L / parts;
+    part = L % parts;
+  }
+}
+
+constexpr float LOG2E = 1.4426950408889634f;
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 struct FwdArgs {
   int B, T, Hqk, Hv, N;           // N = T / C chunks per sequence
   const void *q, *k, *v;
   const float *g, *beta;
-  float *G, *W, *U, *Tm;          // prep outputs (Tm optional)
+  float *G, *U, *Tm;              // prep outputs (Tm optional); U is U^T on the forward path
+  void *W;                        // prep output, input dtype (fp32 for the transform hook)
+  void *Kt;                       // prep output / walk input: K^T per chunk, input dtype
   float *Hs, *Vn;                 // walk outputs (optional) / out inputs
   const float *init;              // walk: initial states (h0 [BH,D,D] or h_in [BH,J,D,D]) or null
   int init_per_job;               // init indexed by job (replay) instead of bh only
@@ -67,21 +109,52 @@ struct FwdArgs {
 
 // Copy C rows of D elements (row stride `gstride` elements in global memory)
 // into LDS rows of leading dimension `ld`, 16 bytes per thread access.
+// All loads are issued before the first LDS store so their latencies overlap.
 template <typename TI, int ROWS>
 __device__ __forceinline__ void load_rows(TI *dst, int ld, const TI *src, size_t gstride) {
   constexpr int VE = 16 / sizeof(TI);
   constexpr int PER_ROW = D / VE;
-  for (int idx = threadIdx.x; idx < ROWS * PER_ROW; idx += NT) {
-    const int r = idx / PER_ROW, cv = idx % PER_ROW;
-    const uint4 val = *reinterpret_cast<const uint4 *>(src + (size_t)r * gstride + cv * VE);
-    *reinterpret_cast<uint4 *>(dst + r * ld + cv * VE) = val;
+  constexpr int NV = ROWS * PER_ROW / NT;
+  static_assert(ROWS * PER_ROW % NT == 0, "tile must split evenly over the workgroup");
+  uint4 v[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int idx = threadIdx.x + i * NT, r = idx / PER_ROW, cv = idx % PER_ROW;
+    v[i] = *reinterpret_cast<const uint4 *>(src + (size_t)r * gstride + cv * VE);
+  }
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int idx = threadIdx.x + i * NT, r = idx / PER_ROW, cv = idx % PER_ROW;
+    *reinterpret_cast<uint4 *>(dst + r * ld + cv * VE) = v[i];
+  }
+}
+
+// Copy ROWS rows of COLS floats (global row stride gld) into LDS (row stride ld).
+template <int ROWS, int COLS>
+__device__ __forceinline__ void load_rows_f32(float *dst, int ld, const float *src, int gld) {
+  constexpr int PER_ROW = COLS / 4;
+  constexpr int NV = ROWS * PER_ROW / NT;
+  static_assert(ROWS * PER_ROW % NT == 0, "tile must split evenly over the workgroup");
+  float4 v[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int idx = threadIdx.x + i * NT, r = idx / PER_ROW, c4 = (idx % PER_ROW) * 4;
+    v[i] = *reinterpret_cast<const float4 *>(src + (size_t)r * gld + c4);
+  }
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int idx = threadIdx.x + i * NT, r = idx / PER_ROW, c4 = (idx % PER_ROW) * 4;
+    *reinterpret_cast<float4 *>(dst + r * ld + c4) = v[i];
   }
 }
 
 // ----------------------------------------------------------------------------
 // prep: decay cumsum, S, T (ladder), W, U for one chunk of one value head.
-template <int C, typename TI, int MODE>
+// FWD: the forward path's layouts (W in the input dtype, U^T, K^T written);
+// otherwise the transform hook's (W and U fp32 row-major, no K^T).
+template <int C, typename TI, int MODE, bool FWD>
 __global__ __launch_bounds__(NT) void prep_kernel(FwdArgs a) {
+  using WT = typename std::conditional<FWD, TI, float>::type;
   using PR = Prec<MODE>;
   constexpr int LDI = D + LdPad<TI>::v;   // input tile leading dim
   constexpr int LDS_ = C + 4;             // S / T leading dim
@@ -89,13 +162,13 @@ __global__ __launch_bounds__(NT) void prep_kernel(FwdArgs a) {
   __shared__ __align__(16) TI sIn[C * LDI];
   __shared__ __align__(16) float sS[C * LDS_];
   __shared__ __align__(16) float sM[(C / 2) * LDM_MAX];   // ladder scratch: nb * b * (b+4) <= C/2*(C/2+4)
-  __shared__ float sG[C], sBeta[C], sScale[C];
+  __shared__ float sG[C], sG2[C], sBeta[C], sScale[C];
   __shared__ float sWt[2];
 
   const int n = blockIdx.x, hv = blockIdx.y, b = blockIdx.z;
   const int hq = hv / (a.Hv / a.Hqk);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lr = lane & 15, lk = (lane >> 4) * 8, lq = (lane >> 4) * 4;
+  const int lr = lane & 15, g = lane >> 4, lk = g * 8, lq = g * 4;
   const size_t bh = (size_t)b * a.Hv + hv;
   const size_t t0 = (size_t)n * C;
 
@@ -113,41 +186,78 @@ __global__ __launch_bounds__(NT) void prep_kernel(FwdArgs a) {
       if (lane >= off) x += y;
     }
     if (lane == 63 && wave < 2) sWt[wave] = x;
-    __syncthreads();
+    lds_barrier();
     if (wave == 1) x += sWt[0];
     if (tid < C) {
       sG[tid] = x;
+      sG2[tid] = x * LOG2E;
       sBeta[tid] = bx;
-      sScale[tid] = bx * expf(x);
+      sScale[tid] = bx * exp2_fast(x * LOG2E);
     }
   }
   // (2) K chunk -> LDS
   const TI *kin = reinterpret_cast<const TI *>(a.k) + (((size_t)b * a.T + t0) * a.Hqk + hq) * D;
   load_rows<TI, C>(sIn, LDI, kin, (size_t)a.Hqk * D);
-  __syncthreads();
-
-  // (3) S = strict-lower( beta_r e^{G_r - G_i} K K^T ); upper tiles zero
-  constexpr int TC = C / 16;
-  for (int tt = wave; tt < TC * TC; tt += 4) {
-    const int mi = tt / TC, ni = tt % TC;
-    f32x4 acc = zero4();
-    if (ni <= mi) {
+  lds_barrier();
+  if constexpr (FWD) {
+    // K^T fragments of this chunk for the walk: one 16-byte vector per lane
+    // and (d tile, k-block), gathered down a column of the K tile
+    constexpr int VE = 16 / sizeof(TI);
+    TI *Ktg = reinterpret_cast<TI *>(a.Kt) + (bh * a.N + n) * D * C;
 #pragma unroll
-      for (int kb = 0; kb < D / 32; ++kb) {
-        float a8[8], b8[8];
-        ld8(sIn + (16 * mi + lr) * LDI + 32 * kb + lk, a8);
-        ld8(sIn + (16 * ni + lr) * LDI + 32 * kb + lk, b8);
-        mma_k32<PR::exact>(acc, a8, b8);
-      }
-    }
-    const int c = 16 * ni + lr;
+    for (int i = 0; i < D * C / 8 / NT; ++i) {
+      const int f = tid + i * NT;           // fragment-vector index: (m, kb, lane)
+      const int l = f & 63, mk = f >> 6, m = mk / (C / 32), kb = mk % (C / 32);
+      const int d = 16 * m + (l & 15), r0 = 32 * kb + 8 * (l >> 4);
+      TI tmp[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * mi + lq + i;
-      sS[r * LDS_ + c] = (c < r) ? sBeta[r] * expf(sG[r] - sG[c]) * acc[i] : 0.f;
+      for (int j = 0; j < 8; ++j) tmp[j] = sIn[(r0 + j) * LDI + d];
+#pragma unroll
+      for (int v = 0; v < 8 / VE; ++v)
+        *reinterpret_cast<uint4 *>(Ktg + (size_t)f * 8 + v * VE) = *reinterpret_cast<const uint4 *>(tmp + v * VE);
     }
   }
-  __syncthreads();
+  // (3) S = strict-lower( beta_r e^{G_r - G_i} K K^T ); upper tiles zero.
+  //     Wave w owns row tiles {w, TC-1-w} (balanced triangle); each k-block's
+  //     column fragment feeds both of them.
+  constexpr int TC = C / 16;
+  constexpr int RU = TC / 4;   // row tiles per wave
+  {
+    using PK = PolicyKinds<PR::exact>;
+    int mrow[RU];
+#pragma unroll
+    for (int u = 0; u < RU; ++u) mrow[u] = u == 0 ? wave : TC - 1 - wave;
+    f32x4 acc[RU][TC];
+#pragma unroll
+    for (int u = 0; u < RU; ++u)
+#pragma unroll
+      for (int ni = 0; ni < TC; ++ni) acc[u][ni] = zero4();
+#pragma unroll
+    for (int kb = 0; kb < D / 32; ++kb) {
+      Frag<PK::a> af[RU];
+#pragma unroll
+      for (int u = 0; u < RU; ++u) af[u] = lds_frag<PK::a>(sIn + (16 * mrow[u] + lr) * LDI + 32 * kb + lk);
+#pragma unroll
+      for (int ni = 0; ni < TC; ++ni) {
+        const auto bf = lds_frag<PK::b>(sIn + (16 * ni + lr) * LDI + 32 * kb + lk);
+#pragma unroll
+        for (int u = 0; u < RU; ++u)
+          if (ni <= mrow[u]) mma(acc[u][ni], af[u], bf);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < RU; ++u)
+#pragma unroll
+      for (int ni = 0; ni < TC; ++ni) {
+        const int c = 16 * ni + lr;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * mrow[u] + lq + i;
+          sS[r * LDS_ + c] = (c < r) ? sBeta[r] * exp2_fast(sG2[r] - sG2[c]) * acc[u][ni][i] : 0.f;
+        }
+      }
+  }
+  lds_barrier();
 
   // (4) exact inverses of the 16x16 diagonal blocks (forward substitution,
   //     one thread per block column)
@@ -164,13 +274,13 @@ __global__ __launch_bounds__(NT) void prep_kernel(FwdArgs a) {
         x[r] = v;
       }
     }
-    __syncthreads();
+    lds_barrier();
     if (tid < C) {
       float *Sb = sS + (16 * blk) * LDS_ + 16 * blk;
 #pragma unroll
       for (int r = 0; r < 16; ++r) Sb[r * LDS_ + j] = x[r];
     }
-    __syncthreads();
+    lds_barrier();
   }
 
   // (5) doubling ladder: for each 2b diagonal block [[P,0],[L,Q]] the new
@@ -198,7 +308,7 @@ __global__ __launch_bounds__(NT) void prep_kernel(FwdArgs a) {
       *reinterpret_cast<float4 *>(M + (16 * ni + lr) * ldm + 16 * mi + lq) =
           float4{acc[0], acc[1], acc[2], acc[3]};
     }
-    __syncthreads();
+    lds_barrier();
     // L <- -X_Q M1
     for (int tt = wave; tt < nb * tb * tb; tt += 4) {
       const int blk = tt / (tb * tb), ti = tt % (tb * tb), mi = ti / tb, ni = ti % tb;
@@ -220,7 +330,7 @@ __global__ __launch_bounds__(NT) void prep_kernel(FwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) sS[(s + bs + 16 * mi + lq + i) * LDS_ + s + 16 * ni + lr] = -acc[i];
     }
-    __syncthreads();
+    lds_barrier();
   }
 
   const size_t cb = bh * a.N + n;  // chunk index into the workspace
@@ -230,152 +340,298 @@ __global__ __launch_bounds__(NT) void prep_kernel(FwdArgs a) {
   }
   if (tid < C) a.G[cb * C + tid] = sG[tid];
 
-  // (6) W = (T diag(beta e^G)) K ;  (7) U = (T diag(beta)) V
+  // (6) W = (T diag(beta e^G)) K, computed transposed (W^T = K^T T'^T) so
+  //     that each lane ends with 4 consecutive columns of one row of W.
+  // (7) U = (T diag(beta)) V, computed as is, so that each lane ends with 4
+  //     consecutive rows of one column of U (= 4 consecutive entries of U^T).
+  // Wave w owns row tiles {w, TC-1-w}; T is lower triangular, so row tile m
+  // needs k < 16(m+1).  The T fragments of k-blocks past the diagonal read
+  // T's zero upper triangle and their products are skipped.
   constexpr int TD = D / 16;
+  constexpr int KT = PolicyKinds<PR::wy>::a;   // T' fragments (split)
+  constexpr int KX = PolicyKinds<PR::wy>::b;   // K / V fragments (exact data)
+  int mrow[RU];
+#pragma unroll
+  for (int u = 0; u < RU; ++u) mrow[u] = u == 0 ? wave : TC - 1 - wave;
   for (int pass = 0; pass < 2; ++pass) {
     if (pass == 1) {
-      __syncthreads();
+      lds_barrier();
       const TI *vin = reinterpret_cast<const TI *>(a.v) + (((size_t)b * a.T + t0) * a.Hv + hv) * D;
       load_rows<TI, C>(sIn, LDI, vin, (size_t)a.Hv * D);
-      __syncthreads();
+      lds_barrier();
     }
     const float *scale = pass == 0 ? sScale : sBeta;
-    float *out = (pass == 0 ? a.W : a.U) + cb * C * D;
-    for (int tt = wave; tt < TC * TD; tt += 4) {
-      const int mi = tt / TD, ni = tt % TD;
-      f32x4 acc = zero4();
-      for (int kb = 0; kb * 32 < 16 * (mi + 1); ++kb) {
-        float a8[8], b8[8];
-        const int k0 = 32 * kb + lk;
-        ld8(sS + (16 * mi + lr) * LDS_ + k0, a8);
+    f32x4 acc[RU][TD];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) a8[j] *= scale[k0 + j];
-        ld8s(sIn + k0 * LDI + 16 * ni + lr, LDI, b8);
-        mma_k32<PR::wy>(acc, a8, b8);
+    for (int u = 0; u < RU; ++u)
+#pragma unroll
+      for (int md = 0; md < TD; ++md) acc[u][md] = zero4();
+#pragma unroll
+    for (int kb = 0; kb < C / 32; ++kb) {
+      const int k0 = 32 * kb + lk;
+      Frag<KT> tf[RU];
+      bool live[RU];
+#pragma unroll
+      for (int u = 0; u < RU; ++u) {
+        live[u] = 32 * kb < 16 * (mrow[u] + 1);
+        float x[8];
+        ld8(sS + (16 * mrow[u] + lr) * LDS_ + k0, x);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] *= scale[k0 + j];
+        tf[u] = make_frag<KT>(x);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) out[(size_t)(16 * mi + lq + i) * D + 16 * ni + lr] = acc[i];
+      for (int md = 0; md < TD; ++md) {
+        float x[8];
+        ld8s(sIn + k0 * LDI + 16 * md + lr, LDI, x);   // column 16md+lr of K (or V), rows k0..k0+7
+        const auto xf = make_frag<KX>(x);
+#pragma unroll
+        for (int u = 0; u < RU; ++u) {
+          if (!live[u]) continue;
+          if (pass == 0) mma(acc[u][md], xf, tf[u]);   // W^T tile (d, r)
+          else mma(acc[u][md], tf[u], xf);             // U tile (r, d)
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < RU; ++u) {
+#pragma unroll
+      for (int md = 0; md < TD; ++md) {
+        if (pass == 0 && FWD) {
+          // lane holds W[r][16md + 4g + i], r = 16 mrow + lr: in the walk's
+          // fragment (mrow, kb = md/2) these are lane lr + 16 (2 (md%2) + g/2),
+          // elements 4 (g%2) + i
+          const int kb = md >> 1, gg = 2 * (md & 1) + (g >> 1);
+          WT *dst = reinterpret_cast<WT *>(a.W) +
+                    ((cb * (C / 16) + mrow[u]) * (D / 32) + kb) * 512 + (lr + 16 * gg) * 8 + 4 * (g & 1);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dst[i] = from_f32<WT>(acc[u][md][i]);
+        } else if (pass == 0) {
+          WT *dst = reinterpret_cast<WT *>(a.W) + (cb * C + 16 * mrow[u] + lr) * D + 16 * md + lq;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dst[i] = from_f32<WT>(acc[u][md][i]);
+        } else if constexpr (FWD) {
+          // lane holds U[16 mrow + 4g + i][16md + lr]: the walk's fragment (mrow, md)
+          *reinterpret_cast<float4 *>(a.U + ((cb * (C / 16) + mrow[u]) * TD + md) * 256 + lane * 4) =
+              float4{acc[u][md][0], acc[u][md][1], acc[u][md][2], acc[u][md][3]};
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            a.U[(cb * C + 16 * mrow[u] + lq + i) * D + 16 * md + lr] = acc[u][md][i];
+        }
+      }
     }
   }
 }
 
 // ----------------------------------------------------------------------------
 // walk / fold: the sequential chunk loop for one column slice of the state.
-template <int C, typename TI, int MODE, int S, int KIND>
-__global__ __launch_bounds__(NT) void walk_kernel(FwdArgs a) {
-  using PR = Prec<MODE>;
-  constexpr int LDW = D + LdPad<TI>::v;   // W tile [C][LDW]
-  constexpr int LDK = C + LdPad<TI>::v;   // K^T tile [D][LDK]
-  constexpr int RSZ = (C * LDW > D * LDK) ? C * LDW : D * LDK;
-  constexpr int LDH = D + 4;              // state slice, transposed [S][LDH]
-  constexpr int LDV = C + 4;              // scaled V' slice, transposed [S][LDV]
-  __shared__ __align__(16) TI sR[RSZ];
-  __shared__ __align__(16) float sH[S * LDH];
-  __shared__ __align__(16) float sV[S * LDV];
-  __shared__ float sD[C];
+//
+// 8 waves (512 threads; two per SIMD so one can issue while the other waits).
+// Wave w owns one row tile of V' (C x S) and one row tile of the state
+// (D x S), with the column tiles shared out as below.  Its share of the fp32
+// state stays in registers for the whole walk.  Per chunk:
+//   V' = U - W h        A = W rows (fragments loaded from global, one chunk
+//                       ahead), B = bf16 copy of h in LDS
+//   h  = e^{G_last} h + K^T (d o V')   A = K^T rows (global, one chunk
+//                       ahead), B = d o V' in LDS, already split into the
+//                       operand form (hi/lo bf16) by its producer;
+//                       d_r = e^{G_last - G_r}
+// with two barriers per chunk.
+constexpr int WALK_NT = 512;
 
-  const int slice = blockIdx.x, hv = blockIdx.y;
-  const int b = blockIdx.z / a.jobs, job = blockIdx.z % a.jobs;
-  const int hq = hv / (a.Hv / a.Hqk);
+template <int C, typename TI, int MODE, int S, int KIND>
+__global__ __launch_bounds__(WALK_NT) void walk_kernel(FwdArgs a) {
+  using PR = Prec<MODE>;
+  using PKw = PolicyKinds<PR::wh>;
+  using PKk = PolicyKinds<PR::kv>;
+  static_assert(PKw::a == (sizeof(TI) == 2 ? F_BF16 : F_F32) && PKk::a == PKw::a,
+                "W and K^T fragments are read as stored");
+  constexpr bool F32 = PKk::b == F_F32;
+  using HB = typename std::conditional<PKw::b == F_F32, float, __bf16>::type;   // state copy for W h
+  constexpr int NW = WALK_NT / 64;
+  constexpr int NS = (KIND == FOLD ? 2 * D : D) / S;
+  constexpr int TN = S / 16;          // column tiles of the slice
+  constexpr int TRV = C / 16;         // V' row tiles
+  constexpr int CPW = TN * TRV / NW;  // V' column tiles per wave
+  constexpr int CPH = TN * (D / 16) / NW;   // state column tiles per wave
+  constexpr int KBW = D / 32, KBK = C / 32;
+  constexpr int LDHB = D + (sizeof(HB) == 2 ? 8 : 4);   // sHb [S][LDHB]
+  constexpr int LDV = C + (F32 ? 4 : 8);                 // sV  [S][LDV] (x2 when split)
+  static_assert(CPW >= 1 && CPH >= 1 && TN % CPW == 0 && TN % CPH == 0, "tiling");
+  __shared__ __align__(16) HB sHb[S * LDHB];
+  __shared__ __align__(16) typename std::conditional<F32, float, __bf16>::type sV[(F32 ? 1 : 2) * S * LDV];
+
+  int unit, slice;
+  xcd_unit(blockIdx.x, NS, a.B * a.Hv * a.jobs, unit, slice);
+  const int job = unit % a.jobs;
+  const size_t bh = (size_t)(unit / a.jobs);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lk = (lane >> 4) * 8, lq = (lane >> 4) * 4;
-  const size_t bh = (size_t)b * a.Hv + hv;
   const int c0 = slice * S;   // first column of the slice (augmented [A|B] in FOLD)
+  const bool has_u = KIND == WALK || c0 >= D;
+  const int uc0 = KIND == WALK ? c0 : c0 - D;
+  // this wave's tiles
+  const int mv = wave % TRV, nv0 = (wave / TRV) * CPW;             // V' row tile, first column tile
+  const int mh = wave % (D / 16), nh0 = (wave / (D / 16)) * CPH;   // state row tile, first column tile
 
-  // initial state slice
-  for (int idx = tid; idx < D * S; idx += NT) {
-    const int kr = idx / S, c = idx % S, col = c0 + c;
-    float x = 0.f;
-    if (KIND == FOLD) {
-      x = (col < D && kr == col) ? 1.f : 0.f;
-    } else if (a.init) {
-      const float *src = a.init_per_job ? a.init + (bh * a.jobs + job) * D * D : a.init + bh * D * D;
-      x = src[(size_t)kr * D + col];
+  // state: tiles (mh, nh0 + t): rows 16 mh + lq + i, column 16 (nh0 + t) + lr
+  f32x4 h[CPH];
+#pragma unroll
+  for (int t = 0; t < CPH; ++t) {
+    const int col = c0 + 16 * (nh0 + t) + lr;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int kr = 16 * mh + lq + i;
+      float x = 0.f;
+      if (KIND == FOLD) {
+        x = (col < D && kr == col) ? 1.f : 0.f;
+      } else if (a.init) {
+        const float *src = a.init_per_job ? a.init + (bh * a.jobs + job) * D * D : a.init + bh * D * D;
+        x = src[(size_t)kr * D + col];
+      }
+      h[t][i] = x;
     }
-    sH[c * LDH + kr] = x;
   }
+  auto put_state_copy = [&]() {
+#pragma unroll
+    for (int t = 0; t < CPH; ++t) {
+      HB *dst = sHb + (16 * (nh0 + t) + lr) * LDHB + 16 * mh + lq;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[i] = from_f32<HB>(h[t][i]);
+    }
+  };
 
-  for (int cc = 0; cc < a.cpj; ++cc) {
+  struct Ops {
+    Frag<PKw::a> wf[KBW];
+    Frag<PKk::a> kf[KBK];
+    float4 u[CPW];
+    float4 g;
+    float glast;
+  };
+  auto fetch = [&](Ops &op, int n) {
+    const size_t cb = bh * a.N + n;
+    const TI *Wg = reinterpret_cast<const TI *>(a.W) + cb * C * D + (size_t)mv * KBW * 512 + lane * 8;
+    const TI *Kg = reinterpret_cast<const TI *>(a.Kt) + cb * D * C + (size_t)mh * KBK * 512 + lane * 8;
+#pragma unroll
+    for (int kb = 0; kb < KBW; ++kb) {
+      if constexpr (sizeof(TI) == 2) {
+        op.wf[kb].hi = *reinterpret_cast<const bf16x8 *>(Wg + kb * 512);
+      } else {
+        const float4 x0 = *reinterpret_cast<const float4 *>(Wg + kb * 512);
+        const float4 x1 = *reinterpret_cast<const float4 *>(Wg + kb * 512 + 4);
+        float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        op.wf[kb] = make_frag<PKw::a>(x);
+      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < KBK; ++kb) {
+      if constexpr (sizeof(TI) == 2) {
+        op.kf[kb].hi = *reinterpret_cast<const bf16x8 *>(Kg + kb * 512);
+      } else {
+        const float4 x0 = *reinterpret_cast<const float4 *>(Kg + kb * 512);
+        const float4 x1 = *reinterpret_cast<const float4 *>(Kg + kb * 512 + 4);
+        float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        op.kf[kb] = make_frag<PKk::a>(x);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < CPW; ++t)
+      op.u[t] = has_u ? *reinterpret_cast<const float4 *>(
+                            a.U + ((cb * TRV + mv) * (D / 16) + uc0 / 16 + nv0 + t) * 256 + lane * 4)
+                      : float4{0.f, 0.f, 0.f, 0.f};
+    op.g = *reinterpret_cast<const float4 *>(a.G + cb * C + 16 * mv + lq);
+    op.glast = a.G[cb * C + C - 1 + vgpr_zero()];
+  };
+
+  Ops ops[2];
+  fetch(ops[0], job * a.cpj);
+  put_state_copy();
+  lds_barrier();
+
+  auto step = [&](Ops &cur, Ops &nxt, int cc) {
     const int n = job * a.cpj + cc;
     const size_t cb = bh * a.N + n;
-    const float glog = a.G[cb * C + C - 1];
-    if (tid < C) sD[tid] = expf(glog - a.G[cb * C + tid]);
-    // W_n -> sR (as TI)
-    {
-      const float *Wg = a.W + cb * C * D;
-      for (int idx = tid; idx < C * D / 4; idx += NT) {
-        const int r = idx / (D / 4), c4 = (idx % (D / 4)) * 4;
-        const float4 w = *reinterpret_cast<const float4 *>(Wg + (size_t)r * D + c4);
-        TI *dst = sR + r * LDW + c4;
-        dst[0] = from_f32<TI>(w.x); dst[1] = from_f32<TI>(w.y);
-        dst[2] = from_f32<TI>(w.z); dst[3] = from_f32<TI>(w.w);
-      }
-    }
-    __syncthreads();   // sH (previous update / init) and sR visible
+    if (cc + 1 < a.cpj) fetch(nxt, n + 1);
+
+    // chunk-start state for the output stage, fragment-major
     if (KIND == WALK && a.Hs) {
-      float *Hg = a.Hs + cb * D * D;
-      for (int idx = tid; idx < D * S; idx += NT) {
-        const int kr = idx / S, c = idx % S;
-        Hg[(size_t)kr * D + c0 + c] = sH[c * LDH + kr];
-      }
-    }
-    // V' = U - W h  (tiles of C x S)
-    for (int tt = wave; tt < (C / 16) * (S / 16); tt += 4) {
-      const int mi = tt / (S / 16), ni = tt % (S / 16);
-      f32x4 acc = zero4();
 #pragma unroll
-      for (int kb = 0; kb < D / 32; ++kb) {
-        float a8[8], b8[8];
-        ld8(sR + (16 * mi + lr) * LDW + 32 * kb + lk, a8);
-        ld8(sH + (16 * ni + lr) * LDH + 32 * kb + lk, b8);
-        mma_k32<PR::wh>(acc, a8, b8);
-      }
-      const int c = 16 * ni + lr, col = c0 + c;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * mi + lq + i;
-        float u = 0.f;
-        if (KIND == WALK) u = a.U[(cb * C + r) * D + col];
-        else if (col >= D) u = a.U[(cb * C + r) * D + col - D];
-        const float vp = u - acc[i];
-        if (KIND == WALK && a.Vn) a.Vn[(cb * C + r) * D + col] = vp;
-        sV[c * LDV + r] = vp * sD[r];
-      }
+      for (int t = 0; t < CPH; ++t)
+        *reinterpret_cast<float4 *>(a.Hs + (((cb * NS + slice) * (D / 16) + mh) * TN + nh0 + t) * 256 + lane * 4) =
+            float4{h[t][0], h[t][1], h[t][2], h[t][3]};
     }
-    __syncthreads();   // done with W; sV complete
-    // K_n^T -> sR  ([D][LDK])
+    // V' = U - W h, then d o V' into LDS in the update's operand form
+    const float gl2 = cur.glast * LOG2E;
     {
-      const TI *kin = reinterpret_cast<const TI *>(a.k) + (((size_t)b * a.T + (size_t)n * C) * a.Hqk + hq) * D;
-      constexpr int VE = 16 / sizeof(TI);
-      for (int idx = tid; idx < C * D / VE; idx += NT) {
-        const int r = idx / (D / VE), cv = (idx % (D / VE)) * VE;
-        TI tmp[VE];
-        *reinterpret_cast<uint4 *>(tmp) = *reinterpret_cast<const uint4 *>(kin + (size_t)r * a.Hqk * D + cv);
+      f32x4 acc[CPW];
 #pragma unroll
-        for (int j = 0; j < VE; ++j) sR[(cv + j) * LDK + r] = tmp[j];
+      for (int t = 0; t < CPW; ++t) acc[t] = zero4();
+#pragma unroll
+      for (int kb = 0; kb < KBW; ++kb) {
+#pragma unroll
+        for (int t = 0; t < CPW; ++t)
+          mma(acc[t], cur.wf[kb], lds_frag<PKw::b>(sHb + (16 * (nv0 + t) + lr) * LDHB + 32 * kb + lk));
+      }
+      const int r0 = 16 * mv + lq;
+      const float d0 = exp2_fast(gl2 - cur.g.x * LOG2E), d1 = exp2_fast(gl2 - cur.g.y * LOG2E);
+      const float d2 = exp2_fast(gl2 - cur.g.z * LOG2E), d3 = exp2_fast(gl2 - cur.g.w * LOG2E);
+#pragma unroll
+      for (int t = 0; t < CPW; ++t) {
+        const int c = 16 * (nv0 + t) + lr;
+        const float4 uu = cur.u[t];
+        const float4 vp = {uu.x - acc[t][0], uu.y - acc[t][1], uu.z - acc[t][2], uu.w - acc[t][3]};
+        if (KIND == WALK && a.Vn)
+          *reinterpret_cast<float4 *>(a.Vn + (((cb * NS + slice) * TRV + mv) * TN + nv0 + t) * 256 + lane * 4) = vp;
+        const float s4[4] = {vp.x * d0, vp.y * d1, vp.z * d2, vp.w * d3};
+        if constexpr (F32) {
+          *reinterpret_cast<float4 *>(sV + c * LDV + r0) = float4{s4[0], s4[1], s4[2], s4[3]};
+        } else {
+          __bf16 hi[4], lo[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            hi[i] = (__bf16)s4[i];
+            lo[i] = (__bf16)(s4[i] - (float)hi[i]);
+          }
+          *reinterpret_cast<uint2 *>(sV + c * LDV + r0) = *reinterpret_cast<const uint2 *>(hi);
+          *reinterpret_cast<uint2 *>(sV + S * LDV + c * LDV + r0) = *reinterpret_cast<const uint2 *>(lo);
+        }
       }
     }
-    __syncthreads();
-    // h <- e^{G_last} h + K^T (diag(e^{G_last-G}) V')   (tiles of D x S)
-    const float gl = expf(glog);
-    for (int tt = wave; tt < (D / 16) * (S / 16); tt += 4) {
-      const int mi = tt / (S / 16), ni = tt % (S / 16);
-      f32x4 acc = zero4();
+    lds_barrier();
+    // h <- e^{G_last} h + K^T (d o V')
+    {
+      const float gl = exp2_fast(gl2);
+      f32x4 acc[CPH];
 #pragma unroll
-      for (int kb = 0; kb < C / 32; ++kb) {
-        float a8[8], b8[8];
-        ld8(sR + (16 * mi + lr) * LDK + 32 * kb + lk, a8);
-        ld8(sV + (16 * ni + lr) * LDV + 32 * kb + lk, b8);
-        mma_k32<PR::kv>(acc, a8, b8);
-      }
-      const int c = 16 * ni + lr;
+      for (int t = 0; t < CPH; ++t) acc[t] = zero4();
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float *h = sH + c * LDH + 16 * mi + lq + i;
-        *h = gl * *h + acc[i];
+      for (int kb = 0; kb < KBK; ++kb) {
+#pragma unroll
+        for (int t = 0; t < CPH; ++t) {
+          const int off = (16 * (nh0 + t) + lr) * LDV + 32 * kb + lk;
+          Frag<PKk::b> bf;
+          if constexpr (F32) {
+            bf = lds_frag<PKk::b>(sV + off);
+          } else {
+            bf.hi = *reinterpret_cast<const bf16x8 *>(sV + off);
+            bf.lo = *reinterpret_cast<const bf16x8 *>(sV + S * LDV + off);
+          }
+          mma(acc[t], cur.kf[kb], bf);
+        }
       }
+#pragma unroll
+      for (int t = 0; t < CPH; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) h[t][i] = gl * h[t][i] + acc[t][i];
     }
-    __syncthreads();
+    put_state_copy();
+    lds_barrier();
+  };
+  // two chunks per trip so the operand sets alternate without copies
+  for (int cc = 0; cc < a.cpj; cc += 2) {
+    step(ops[0], ops[1], cc);
+    if (cc + 1 < a.cpj) step(ops[1], ops[0], cc + 1);
   }
 
   // final state slice
@@ -388,17 +644,18 @@ __global__ __launch_bounds__(NT) void walk_kernel(FwdArgs a) {
     dst = a.fin + bh * D * D;
   }
   if (dst) {
-    for (int idx = tid; idx < D * S; idx += NT) {
-      const int kr = idx / S, c = idx % S;
-      dst[(size_t)kr * D + dcol + c] = sH[c * LDH + kr];
-    }
+#pragma unroll
+    for (int t = 0; t < CPH; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        dst[(size_t)(16 * mh + lq + i) * D + dcol + 16 * (nh0 + t) + lr] = h[t][i];
   }
 }
 
 // ----------------------------------------------------------------------------
 // exclusive prefix of affine pairs, one column slice of the state.
 struct PrefixArgs {
-  int n;
+  int BH, n;
   const float *A, *Bm, *h_init;
   float *h_in, *h_final;
 };
@@ -408,8 +665,9 @@ __global__ __launch_bounds__(NT) void prefix_kernel(PrefixArgs a) {
   constexpr int LDA = D + 4, LDH = D + 4;
   __shared__ __align__(16) float sA[D * LDA];
   __shared__ __align__(16) float sH[S * LDH];
-  const int slice = blockIdx.x;
-  const size_t bh = blockIdx.y;
+  int unit, slice;
+  xcd_unit(blockIdx.x, D / S, a.BH, unit, slice);
+  const size_t bh = (size_t)unit;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lk = (lane >> 4) * 8, lq = (lane >> 4) * 4;
   const int c0 = slice * S;
@@ -424,7 +682,7 @@ __global__ __launch_bounds__(NT) void prefix_kernel(PrefixArgs a) {
       const int r = idx / (D / 4), c4 = (idx % (D / 4)) * 4;
       *reinterpret_cast<float4 *>(sA + r * LDA + c4) = *reinterpret_cast<const float4 *>(Ag + (size_t)r * D + c4);
     }
-    __syncthreads();
+    lds_barrier();
     if (a.h_in) {
       float *Hg = a.h_in + pj * D * D;
       for (int idx = tid; idx < D * S; idx += NT) {
@@ -432,21 +690,26 @@ __global__ __launch_bounds__(NT) void prefix_kernel(PrefixArgs a) {
         Hg[(size_t)kr * D + c0 + c] = sH[c * LDH + kr];
       }
     }
-    f32x4 acc[(D / 16) * (S / 16) / 4];
+    // all of this wave's tiles share column tile wave % (S/16)
+    constexpr int NTU = (D / 16) * (S / 16) / 4;
+    static_assert(4 % (S / 16) == 0, "tiling");
+    using PK = PolicyKinds<PREC>;
+    f32x4 acc[NTU];
 #pragma unroll
-    for (int u = 0; u < (D / 16) * (S / 16) / 4; ++u) {
-      const int tt = wave + 4 * u;
-      const int mi = tt / (S / 16), ni = tt % (S / 16);
-      acc[u] = zero4();
+    for (int u = 0; u < NTU; ++u) acc[u] = zero4();
+    {
+      const int ni = wave % (S / 16);
 #pragma unroll
       for (int kb = 0; kb < D / 32; ++kb) {
-        float a8[8], b8[8];
-        ld8(sA + (16 * mi + lr) * LDA + 32 * kb + lk, a8);
-        ld8(sH + (16 * ni + lr) * LDH + 32 * kb + lk, b8);
-        mma_k32<PREC>(acc[u], a8, b8);
+        const auto bf = lds_frag<PK::b>(sH + (16 * ni + lr) * LDH + 32 * kb + lk);
+#pragma unroll
+        for (int u = 0; u < NTU; ++u) {
+          const int mi = (wave + 4 * u) / (S / 16);
+          mma(acc[u], lds_frag<PK::a>(sA + (16 * mi + lr) * LDA + 32 * kb + lk), bf);
+        }
       }
     }
-    __syncthreads();
+    lds_barrier();
     const float *Bg = a.Bm + pj * D * D;
 #pragma unroll
     for (int u = 0; u < (D / 16) * (S / 16) / 4; ++u) {
@@ -459,7 +722,7 @@ __global__ __launch_bounds__(NT) void prefix_kernel(PrefixArgs a) {
         sH[c * LDH + m] = acc[u][i] + Bg[(size_t)m * D + c0 + c];
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
   if (a.h_final) {
     for (int idx = tid; idx < D * S; idx += NT) {
@@ -470,25 +733,38 @@ __global__ __launch_bounds__(NT) void prefix_kernel(PrefixArgs a) {
 }
 
 // ----------------------------------------------------------------------------
-// output for one column slice of one chunk.
+// output for one column slice of one chunk, computed transposed:
+//   O^T = h^T (diag(e^G) Q)^T + V'^T P^T,   P^T = (K Q^T) o Gamma^T o [i <= r].
+// Each wave owns query-row tiles (w and R-1-w, balancing the triangle).  P^T
+// tiles stay in the matrix-core result registers and feed V'^T P^T directly
+// as B operands: a result tile holds rows 4g..4g+3 of 16 for lane group g, so
+// two stacked tiles give lane group g the k-values {4g..4g+3, 16+4g..16+4g+3},
+// and the A operand is fetched with the same k order.
 template <int C, typename TI, int MODE, int S, typename TO>
-__global__ __launch_bounds__(NT) void out_kernel(FwdArgs a) {
+__global__ __launch_bounds__(NT, 2) void out_kernel(FwdArgs a) {
   using PR = Prec<MODE>;
-  constexpr int LDI = D + LdPad<TI>::v;
-  constexpr int LDP = C + 4;
-  constexpr int LDH = D + 4;
-  constexpr int LDV = C + 4;
-  constexpr int KB = C * LDI * (int)sizeof(TI), HVB = S * (LDH + LDV) * 4;
-  __shared__ __align__(16) TI sQ[C * LDI];
-  __shared__ __align__(16) char sKraw[KB > HVB ? KB : HVB];   // K tile, then the h / V' slices
-  __shared__ __align__(16) float sP[C * LDP];
-  __shared__ float sG[C], sE[C];
-  TI *sK = reinterpret_cast<TI *>(sKraw);
-  float *sH = reinterpret_cast<float *>(sKraw);   // reused after P is formed
-  float *sV = sH + S * LDH;
+  using PKq = PolicyKinds<PR::exact>;   // K x Q^T
+  using PKh = PolicyKinds<PR::hq>;      // h^T x Q^T
+  using PKv = PolicyKinds<PR::pv>;      // V'^T x P^T
+  static_assert(PKq::b == PKh::b, "one query fragment serves both products");
+  constexpr int VE = 16 / sizeof(TI);
+  constexpr int LDK = D + LdPad<TI>::v;   // K tile [C][LDK]
+  constexpr int LDH = D + 4;              // h^T slice [S][LDH]
+  constexpr int LDV = C + 4;              // V'^T slice [S][LDV]
+  constexpr int R = C / 16;               // query-row tiles
+  constexpr int RU = R / 4;               // row tiles per wave
+  constexpr int NS = D / S;
+  constexpr int CT = S / 16;              // column tiles of the slice
+  static_assert(R % 4 == 0, "row tiles must split over 4 waves");
+  __shared__ __align__(16) TI sK[C * LDK];
+  __shared__ __align__(16) float sH[S * LDH];
+  __shared__ __align__(16) float sV[S * LDV];
+  __shared__ float sG[C];
 
-  const int slice = blockIdx.x, n = blockIdx.y;
-  const size_t bh = blockIdx.z;
+  int unit, slice;
+  xcd_unit(blockIdx.x, NS, a.N * a.B * a.Hv, unit, slice);
+  const size_t bh = (size_t)(unit / a.N);
+  const int n = unit % a.N;
   const int b = (int)(bh / a.Hv), hv = (int)(bh % a.Hv);
   const int hq = hv / (a.Hv / a.Hqk);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -497,74 +773,111 @@ __global__ __launch_bounds__(NT) void out_kernel(FwdArgs a) {
   const size_t t0 = (size_t)n * C;
   const int c0 = slice * S;
 
-  if (tid < C) {
-    const float x = a.G[cb * C + tid];
-    sG[tid] = x;
-    sE[tid] = expf(x);
+  const size_t koff = (((size_t)b * a.T + t0) * a.Hqk + hq) * D;
+  load_rows<TI, C>(sK, LDK, reinterpret_cast<const TI *>(a.k) + koff, (size_t)a.Hqk * D);
+  // chunk-start state and V' of this slice (fragment-major, contiguous),
+  // scattered into transposed LDS tiles sH[c][d], sV[c][r]
+  {
+    constexpr int NH = (D / 16) * CT * 64 / NT, NV = (C / 16) * CT * 64 / NT;
+    const float *Hg = a.Hs + (cb * NS + slice) * (size_t)(D * S);
+    const float *Vg = a.Vn + (cb * NS + slice) * (size_t)(C * S);
+    float4 hv4[NH], vv4[NV];
+#pragma unroll
+    for (int i = 0; i < NH; ++i) hv4[i] = *reinterpret_cast<const float4 *>(Hg + (size_t)(tid + i * NT) * 4);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) vv4[i] = *reinterpret_cast<const float4 *>(Vg + (size_t)(tid + i * NT) * 4);
+#pragma unroll
+    for (int i = 0; i < NH; ++i) {
+      const int f = tid + i * NT, l = f & 63, t = f >> 6, m = t / CT, ni = t % CT;
+      *reinterpret_cast<float4 *>(sH + (16 * ni + (l & 15)) * LDH + 16 * m + 4 * (l >> 4)) = hv4[i];
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int f = tid + i * NT, l = f & 63, t = f >> 6, m = t / CT, ni = t % CT;
+      *reinterpret_cast<float4 *>(sV + (16 * ni + (l & 15)) * LDV + 16 * m + 4 * (l >> 4)) = vv4[i];
+    }
   }
-  const size_t qoff = (((size_t)b * a.T + t0) * a.Hqk + hq) * D;
-  load_rows<TI, C>(sQ, LDI, reinterpret_cast<const TI *>(a.q) + qoff, (size_t)a.Hqk * D);
-  load_rows<TI, C>(sK, LDI, reinterpret_cast<const TI *>(a.k) + qoff, (size_t)a.Hqk * D);
-  __syncthreads();
+  if (tid < C) sG[tid] = a.G[cb * C + tid] * LOG2E;   // log2-scaled
+  lds_barrier();
 
-  // P = (Q K^T) o Gamma o [i <= r]
-  constexpr int TC = C / 16;
-  for (int tt = wave; tt < TC * TC; tt += 4) {
-    const int mi = tt / TC, ni = tt % TC;
-    f32x4 acc = zero4();
-    if (ni <= mi) {
+  TO *og = reinterpret_cast<TO *>(a.o);
+#pragma unroll 1
+  for (int u = 0; u < RU; ++u) {
+    const int rt = u == 0 ? wave : R - 1 - wave;
+    const int r = 16 * rt + lr;   // this lane's query row (result column)
+    // query fragments of this row tile (B operand: n = row, k = feature)
+    Frag<PKq::b> qf[D / 32];
+    {
+      const TI *qrow = reinterpret_cast<const TI *>(a.q) + (((size_t)b * a.T + t0 + r) * a.Hqk + hq) * D;
 #pragma unroll
       for (int kb = 0; kb < D / 32; ++kb) {
-        float a8[8], b8[8];
-        ld8(sQ + (16 * mi + lr) * LDI + 32 * kb + lk, a8);
-        ld8(sK + (16 * ni + lr) * LDI + 32 * kb + lk, b8);
-        mma_k32<PR::exact>(acc, a8, b8);
+        TI tmp[8];
+#pragma unroll
+        for (int v = 0; v < 8 / VE; ++v)
+          *reinterpret_cast<uint4 *>(tmp + v * VE) = *reinterpret_cast<const uint4 *>(qrow + 32 * kb + lk + v * VE);
+        float x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = to_f32(tmp[j]);
+        qf[kb] = make_frag<PKq::b>(x);
       }
     }
-    const int c = 16 * ni + lr;
+    const float Gr = sG[r];
+    f32x4 acc1[CT], acc2[CT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * mi + lq + i;
-      sP[r * LDP + c] = (c <= r) ? acc[i] * expf(sG[r] - sG[c]) : 0.f;
-    }
-  }
-  __syncthreads();
-  // chunk-start state slice and V' slice, both transposed
-  {
-    const float *Hg = a.Hs + cb * D * D;
-    const float *Vg = a.Vn + cb * C * D;
-    for (int idx = tid; idx < D * S; idx += NT) {
-      const int kr = idx / S, c = idx % S;
-      sH[c * LDH + kr] = Hg[(size_t)kr * D + c0 + c];
-    }
-    for (int idx = tid; idx < C * S; idx += NT) {
-      const int r = idx / S, c = idx % S;
-      sV[c * LDV + r] = Vg[(size_t)r * D + c0 + c];
-    }
-  }
-  __syncthreads();
-  TO *og = reinterpret_cast<TO *>(a.o);
-  for (int tt = wave; tt < TC * (S / 16); tt += 4) {
-    const int mi = tt / (S / 16), ni = tt % (S / 16);
-    f32x4 acc1 = zero4(), acc2 = zero4();
+    for (int ct = 0; ct < CT; ++ct) acc1[ct] = acc2[ct] = zero4();
+    // h^T Q^T for every column tile of the slice
 #pragma unroll
     for (int kb = 0; kb < D / 32; ++kb) {
-      float a8[8], b8[8];
-      ld8(sQ + (16 * mi + lr) * LDI + 32 * kb + lk, a8);
-      ld8(sH + (16 * ni + lr) * LDH + 32 * kb + lk, b8);
-      mma_k32<PR::qh>(acc1, a8, b8);
-    }
-    for (int kb = 0; kb * 32 < 16 * (mi + 1); ++kb) {
-      float a8[8], b8[8];
-      ld8(sP + (16 * mi + lr) * LDP + 32 * kb + lk, a8);
-      ld8(sV + (16 * ni + lr) * LDV + 32 * kb + lk, b8);
-      mma_k32<PR::pv>(acc2, a8, b8);
-    }
-    const int c = 16 * ni + lr;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * mi + lq + i;
-      og[(((size_t)b * a.T + t0 + r) * a.Hv + hv) * D + c0 + c] = from_f32<TO>(sE[r] * acc1[i] + acc2[i]);
+      for (int ct = 0; ct < CT; ++ct)
+        mma(acc1[ct], lds_frag<PKh::a>(sH + (16 * ct + lr) * LDH + 32 * kb + lk), qf[kb]);
+    }
+    // key blocks of 32: P^T tiles (2kp, 2kp+1) are formed and consumed at
+    // once.  A result tile gives lane group g keys {4g..4g+3} (first tile)
+    // and {16+4g..16+4g+3} (second tile) of the block; the V'^T fragment is
+    // read with the same key order.
+#pragma unroll
+    for (int kp = 0; kp < R / 2; ++kp) {
+      if (2 * kp <= rt) {
+        f32x4 p0 = zero4(), p1 = zero4();
+        const bool two = 2 * kp + 1 <= rt;
+#pragma unroll
+        for (int kb = 0; kb < D / 32; ++kb) {
+          mma(p0, lds_frag<PKq::a>(sK + (32 * kp + lr) * LDK + 32 * kb + lk), qf[kb]);
+          if (two) mma(p1, lds_frag<PKq::a>(sK + (32 * kp + 16 + lr) * LDK + 32 * kb + lk), qf[kb]);
+        }
+        float b8[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int k0 = 32 * kp + lq + i, k1 = k0 + 16;
+          b8[i] = k0 <= r ? p0[i] * exp2_fast(Gr - sG[k0]) : 0.f;
+          b8[4 + i] = (two && k1 <= r) ? p1[i] * exp2_fast(Gr - sG[k1]) : 0.f;
+        }
+        const auto bf = make_frag<PKv::b>(b8);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          float a8[8];
+          const float *vrow = sV + (16 * ct + lr) * LDV + 32 * kp + lq;
+          const float4 v0 = *reinterpret_cast<const float4 *>(vrow);
+          const float4 v1 = *reinterpret_cast<const float4 *>(vrow + 16);
+          a8[0] = v0.x; a8[1] = v0.y; a8[2] = v0.z; a8[3] = v0.w;
+          a8[4] = v1.x; a8[5] = v1.y; a8[6] = v1.z; a8[7] = v1.w;
+          mma(acc2[ct], make_frag<PKv::a>(a8), bf);
+        }
+      }
+    }
+    const float er = exp2_fast(Gr);
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      // lane holds O^T[c = 16ct + 4g + i][r]
+      TO *dst = og + (((size_t)b * a.T + t0 + r) * a.Hv + hv) * D + c0 + 16 * ct + lq;
+      if constexpr (sizeof(TO) == 4) {
+        *reinterpret_cast<float4 *>(dst) = float4{er * acc1[ct][0] + acc2[ct][0], er * acc1[ct][1] + acc2[ct][1],
+                                                  er * acc1[ct][2] + acc2[ct][2], er * acc1[ct][3] + acc2[ct][3]};
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[i] = from_f32<TO>(er * acc1[ct][i] + acc2[ct][i]);
+      }
     }
   }
 }

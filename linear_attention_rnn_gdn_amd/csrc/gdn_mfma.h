@@ -29,6 +29,26 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 enum : int { P_BF16 = 0, P_SPLIT_A = 1, P_SPLIT_B = 2, P_SPLIT_AB = 3, P_F32 = 4 };
 
+// A zero the compiler cannot see through, held in a VGPR.  Added to the
+// address of a wave-uniform load it keeps the load on the vector memory path:
+// a scalar (SMEM) load shares the lgkm counter with LDS and can return out of
+// order, so while one is in flight every LDS wait becomes lgkmcnt(0) and
+// stalls for the full memory latency.
+__device__ __forceinline__ int vgpr_zero() {
+  int z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+  return z;
+}
+
+// Workgroup barrier for LDS traffic only.  __syncthreads() is a workgroup
+// memory fence as well and drains every outstanding global load and store
+// (s_waitcnt vmcnt(0)) at each barrier, which would serialise the prefetch of
+// the next chunk with the compute of this one.  Here only the LDS counter is
+// drained; global data never passes between waves of a workgroup.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 template <int P>
@@ -60,6 +80,55 @@ __device__ __forceinline__ void mma_k32(f32x4 &c, const float (&a)[8], const flo
   }
 }
 
+// Operand fragments: an operand is converted (or split) once and can then
+// feed several MFMAs.  Kinds: F_BF16 (rounded to bf16), F_SPLIT (hi + lo
+// bf16), F_F32 (kept fp32 for the fp32 matrix-core instruction).
+enum : int { F_BF16 = 0, F_SPLIT = 1, F_F32 = 2 };
+template <int K> struct Frag;
+template <> struct Frag<F_BF16> { bf16x8 hi; };
+template <> struct Frag<F_SPLIT> { bf16x8 hi, lo; };
+template <> struct Frag<F_F32> { float v[8]; };
+
+// operand kinds of each product policy: A side, B side
+template <int P> struct PolicyKinds;
+template <> struct PolicyKinds<P_BF16> { static constexpr int a = F_BF16, b = F_BF16; };
+template <> struct PolicyKinds<P_SPLIT_A> { static constexpr int a = F_SPLIT, b = F_BF16; };
+template <> struct PolicyKinds<P_SPLIT_B> { static constexpr int a = F_BF16, b = F_SPLIT; };
+template <> struct PolicyKinds<P_SPLIT_AB> { static constexpr int a = F_SPLIT, b = F_SPLIT; };
+template <> struct PolicyKinds<P_F32> { static constexpr int a = F_F32, b = F_F32; };
+
+template <int K>
+__device__ __forceinline__ Frag<K> make_frag(const float (&x)[8]) {
+  Frag<K> f;
+  if constexpr (K == F_F32) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f.v[j] = x[j];
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f.hi[j] = (__bf16)x[j];
+    if constexpr (K == F_SPLIT) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) f.lo[j] = (__bf16)(x[j] - (float)f.hi[j]);
+    }
+  }
+  return f;
+}
+
+// c += A B for one k-block, with the instruction count the operand kinds need
+// (lo x lo products are dropped; small terms are accumulated first).
+template <int KA, int KB>
+__device__ __forceinline__ void mma(f32x4 &c, const Frag<KA> &a, const Frag<KB> &b) {
+  if constexpr (KA == F_F32 || KB == F_F32) {
+    static_assert(KA == F_F32 && KB == F_F32, "fp32 operands pair with fp32 operands");
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[j], b.v[j], c, 0, 0, 0);
+  } else {
+    if constexpr (KA == F_SPLIT) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.hi, c, 0, 0, 0);
+    if constexpr (KB == F_SPLIT) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.lo, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, c, 0, 0, 0);
+  }
+}
+
 // 8 consecutive LDS elements -> float[8]  (p 16-byte aligned)
 __device__ __forceinline__ void ld8(const float *p, float (&x)[8]) {
   const float4 u = *reinterpret_cast<const float4 *>(p);
@@ -77,6 +146,27 @@ template <typename T>
 __device__ __forceinline__ void ld8s(const T *p, int stride, float (&x)[8]) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) x[j] = (float)p[j * stride];
+}
+
+// LDS -> operand fragment.  Exact bf16 data become a bf16 fragment with one
+// 16-byte read and no conversion.
+template <int K>
+__device__ __forceinline__ Frag<K> lds_frag(const float *p) {
+  float x[8];
+  ld8(p, x);
+  return make_frag<K>(x);
+}
+template <int K>
+__device__ __forceinline__ Frag<K> lds_frag(const __bf16 *p) {
+  if constexpr (K == F_BF16) {
+    Frag<K> f;
+    f.hi = *reinterpret_cast<const bf16x8 *>(p);
+    return f;
+  } else {
+    float x[8];
+    ld8(p, x);
+    return make_frag<K>(x);
+  }
 }
 
 __device__ __forceinline__ float to_f32(float x) { return x; }
