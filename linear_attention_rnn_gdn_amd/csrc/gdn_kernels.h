@@ -150,20 +150,150 @@ __device__ __forceinline__ void load_rows_f32(float *dst, int ld, const float *s
 
 // ----------------------------------------------------------------------------
 // prep: decay cumsum, S, T (ladder), W, U for one chunk of one value head.
-// FWD: the forward path's layouts (W in the input dtype, U^T, K^T written);
-// otherwise the transform hook's (W and U fp32 row-major, no K^T).
+// FWD: the forward path's layouts (W in the input dtype, fragment-major W,
+// K^T and U); otherwise the transform hook's (W and U fp32 row-major).
+//
+// LDS (about 78 KB at C = 128, so two workgroups share a compute unit):
+//   sX  one C x D input tile at a time: K row-major (for S), the ladder's
+//       scratch, then K^T and V^T (for W and U)
+//   sT  S, then T, in packed lower-triangular form (Tri)
+// Each thread loads one 8-row block of K (and later of V) into registers
+// once; the row-major copy feeds S, and the same registers are transposed in
+// place for the K^T copy, so K is read from memory once.
+
+// Packed lower-triangular C x C matrix: row tile m (16 rows) keeps its first
+// len(m) = 32 (m/2 + 1) columns -- its part of the lower triangle rounded up
+// to whole k-blocks of 32, zero-filled above the diagonal -- with rows padded
+// by 4 floats against bank conflicts.
+template <int C> struct Tri {
+  static constexpr int size = 512 * ((C / 32) * (C / 32 + 1)) + 64 * (C / 16);
+  __device__ static int len(int m) { return 32 * (m / 2 + 1); }
+  __device__ static int base(int m) {
+    const int h = m >> 1;
+    return 512 * ((m & 1) ? (h + 1) * (h + 1) : h * (h + 1)) + 64 * m;
+  }
+  __device__ static int at(int r, int c) {
+    const int m = r >> 4;
+    return base(m) + (r & 15) * (len(m) + 4) + c;
+  }
+};
+
+// Transposed input tile X^T [D][C] in LDS, unpadded.  The 16-byte blocks of
+// row d are XOR-swizzled by (d ^ d/8): the transposing stores (rows 8 apart)
+// and the operand reads (16 consecutive rows) then both spread over all banks.
+template <int C, typename TI> struct XT {
+  static constexpr int VE = 16 / (int)sizeof(TI);   // elements per 16-byte block
+  static constexpr int NB = C / VE;                  // blocks per row
+  __device__ static int at(int d, int k) {           // k a multiple of VE
+    return d * C + (((k / VE) ^ ((d ^ (d >> 3)) & (NB - 1))) * VE);
+  }
+};
+
+// One thread's block of the input tile: rows 8 rb .. 8 rb + 7, columns
+// VE cb .. VE cb + VE - 1, as 8 row vectors of 16 bytes.
+template <int C, typename TI> struct TileBlock {
+  static constexpr int VE = 16 / (int)sizeof(TI);
+  static constexpr int NCB = D / VE, NBLK = (C / 8) * NCB;
+  static constexpr int PER = (NBLK + NT - 1) / NT;   // blocks per thread
+  uint4 v[PER][8];
+  __device__ void load(const TI *src, size_t gstride) {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int blk = threadIdx.x + p * NT, rb = blk / NCB, cb = blk % NCB;
+      if (blk < NBLK) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          v[p][j] = *reinterpret_cast<const uint4 *>(src + (size_t)(8 * rb + j) * gstride + VE * cb);
+      }
+    }
+  }
+  // row-major copy [C][ld]
+  __device__ void put_rows(TI *dst, int ld) const {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int blk = threadIdx.x + p * NT, rb = blk / NCB, cb = blk % NCB;
+      if (blk < NBLK) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) *reinterpret_cast<uint4 *>(dst + (8 * rb + j) * ld + VE * cb) = v[p][j];
+      }
+    }
+  }
+  // transposed copy X^T (XT layout): column VE cb + e becomes row d, and the
+  // block's 8 rows its 8 consecutive k-values
+  __device__ void put_transposed(TI *dst) const {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int blk = threadIdx.x + p * NT, rb = blk / NCB, cb = blk % NCB;
+      if (blk >= NBLK) continue;
+      if constexpr (sizeof(TI) == 2) {
+        // 8 x 8 transpose of 16-bit values: output dword q of column e packs
+        // rows 2q (low half) and 2q + 1 (high half)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          uint32_t w[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t lo = (&v[p][2 * q].x)[e >> 1], hi = (&v[p][2 * q + 1].x)[e >> 1];
+            w[q] = (e & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+          }
+          *reinterpret_cast<uint4 *>(dst + XT<C, TI>::at(8 * cb + e, 8 * rb)) = uint4{w[0], w[1], w[2], w[3]};
+        }
+      } else {
+        // 8 x 4 of 32-bit values: column e = two 16-byte halves of 4 rows
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const uint4 x = {(&v[p][4 * hh].x)[e], (&v[p][4 * hh + 1].x)[e], (&v[p][4 * hh + 2].x)[e],
+                             (&v[p][4 * hh + 3].x)[e]};
+            *reinterpret_cast<uint4 *>(dst + XT<C, TI>::at(4 * cb + e, 8 * rb + 4 * hh)) = x;
+          }
+        }
+      }
+    }
+  }
+};
+
+// operand fragment of X^T: row d, k-values k0 .. k0 + 7
+template <int K, int C, typename TI>
+__device__ __forceinline__ Frag<K> xt_frag(const TI *sxt, int d, int k0) {
+  if constexpr (sizeof(TI) == 2) {
+    const bf16x8 u = *reinterpret_cast<const bf16x8 *>(sxt + XT<C, TI>::at(d, k0));
+    if constexpr (K == F_BF16) {
+      Frag<K> f;
+      f.hi = u;
+      return f;
+    } else {
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = (float)u[j];
+      return make_frag<K>(x);
+    }
+  } else {
+    const float4 u0 = *reinterpret_cast<const float4 *>(sxt + XT<C, TI>::at(d, k0));
+    const float4 u1 = *reinterpret_cast<const float4 *>(sxt + XT<C, TI>::at(d, k0 + 4));
+    float x[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+    return make_frag<K>(x);
+  }
+}
+
 template <int C, typename TI, int MODE, bool FWD>
-__global__ __launch_bounds__(NT) void prep_kernel(FwdArgs a) {
+__global__ __launch_bounds__(NT, 2) void prep_kernel(FwdArgs a) {
   using WT = typename std::conditional<FWD, TI, float>::type;
   using PR = Prec<MODE>;
-  constexpr int LDI = D + LdPad<TI>::v;   // input tile leading dim
-  constexpr int LDS_ = C + 4;             // S / T leading dim
-  constexpr int LDM_MAX = C / 2 + 4;
-  __shared__ __align__(16) TI sIn[C * LDI];
-  __shared__ __align__(16) float sS[C * LDS_];
-  __shared__ __align__(16) float sM[(C / 2) * LDM_MAX];   // ladder scratch: nb * b * (b+4) <= C/2*(C/2+4)
-  __shared__ float sG[C], sG2[C], sBeta[C], sScale[C];
+  using TRI = Tri<C>;
+  constexpr int LDI = D + LdPad<TI>::v;   // row-major input tile leading dim
+  constexpr int XBYTES_ROWS = C * LDI * (int)sizeof(TI);
+  constexpr int XBYTES_T = D * C * (int)sizeof(TI);
+  constexpr int XBYTES_M = (C / 2) * (C / 2 + 4) * 4;   // ladder scratch: nb * b * (b+4) <= C/2*(C/2+4)
+  constexpr int XBYTES = XBYTES_ROWS > XBYTES_T ? (XBYTES_ROWS > XBYTES_M ? XBYTES_ROWS : XBYTES_M)
+                                                : (XBYTES_T > XBYTES_M ? XBYTES_T : XBYTES_M);
+  __shared__ __align__(16) char sXraw[XBYTES];
+  __shared__ __align__(16) float sT[TRI::size];
+  __shared__ __align__(16) float sG[C], sG2[C], sBeta[C], sScale[C];
   __shared__ float sWt[2];
+  TI *sX = reinterpret_cast<TI *>(sXraw);
+  float *sM = reinterpret_cast<float *>(sXraw);
 
   const int n = blockIdx.x, hv = blockIdx.y, b = blockIdx.z;
   const int hq = hv / (a.Hv / a.Hqk);
@@ -171,6 +301,11 @@ __global__ __launch_bounds__(NT) void prep_kernel(FwdArgs a) {
   const int lr = lane & 15, g = lane >> 4, lk = g * 8, lq = g * 4;
   const size_t bh = (size_t)b * a.Hv + hv;
   const size_t t0 = (size_t)n * C;
+  const size_t cb = bh * a.N + n;  // chunk index into the workspace
+
+  // K block of this thread -> registers (kept for the transposed copy)
+  TileBlock<C, TI> kt, vt;
+  kt.load(reinterpret_cast<const TI *>(a.k) + (((size_t)b * a.T + t0) * a.Hqk + hq) * D, (size_t)a.Hqk * D);
 
   // (1) decay cumsum over the chunk (inclusive), beta
   {
@@ -195,38 +330,20 @@ __global__ __launch_bounds__(NT) void prep_kernel(FwdArgs a) {
       sScale[tid] = bx * exp2_fast(x * LOG2E);
     }
   }
-  // (2) K chunk -> LDS
-  const TI *kin = reinterpret_cast<const TI *>(a.k) + (((size_t)b * a.T + t0) * a.Hqk + hq) * D;
-  load_rows<TI, C>(sIn, LDI, kin, (size_t)a.Hqk * D);
+  // (2) K row-major -> LDS
+  kt.put_rows(sX, LDI);
   lds_barrier();
-  if constexpr (FWD) {
-    // K^T fragments of this chunk for the walk: one 16-byte vector per lane
-    // and (d tile, k-block), gathered down a column of the K tile
-    constexpr int VE = 16 / sizeof(TI);
-    TI *Ktg = reinterpret_cast<TI *>(a.Kt) + (bh * a.N + n) * D * C;
-#pragma unroll
-    for (int i = 0; i < D * C / 8 / NT; ++i) {
-      const int f = tid + i * NT;           // fragment-vector index: (m, kb, lane)
-      const int l = f & 63, mk = f >> 6, m = mk / (C / 32), kb = mk % (C / 32);
-      const int d = 16 * m + (l & 15), r0 = 32 * kb + 8 * (l >> 4);
-      TI tmp[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) tmp[j] = sIn[(r0 + j) * LDI + d];
-#pragma unroll
-      for (int v = 0; v < 8 / VE; ++v)
-        *reinterpret_cast<uint4 *>(Ktg + (size_t)f * 8 + v * VE) = *reinterpret_cast<const uint4 *>(tmp + v * VE);
-    }
-  }
-  // (3) S = strict-lower( beta_r e^{G_r - G_i} K K^T ); upper tiles zero.
+
+  // (3) S = strict-lower( beta_r e^{G_r - G_i} K K^T ) into packed sT.
   //     Wave w owns row tiles {w, TC-1-w} (balanced triangle); each k-block's
   //     column fragment feeds both of them.
   constexpr int TC = C / 16;
   constexpr int RU = TC / 4;   // row tiles per wave
+  int mrow[RU];
+#pragma unroll
+  for (int u = 0; u < RU; ++u) mrow[u] = u == 0 ? wave : TC - 1 - wave;
   {
     using PK = PolicyKinds<PR::exact>;
-    int mrow[RU];
-#pragma unroll
-    for (int u = 0; u < RU; ++u) mrow[u] = u == 0 ? wave : TC - 1 - wave;
     f32x4 acc[RU][TC];
 #pragma unroll
     for (int u = 0; u < RU; ++u)
@@ -236,27 +353,33 @@ __global__ __launch_bounds__(NT) void prep_kernel(FwdArgs a) {
     for (int kb = 0; kb < D / 32; ++kb) {
       Frag<PK::a> af[RU];
 #pragma unroll
-      for (int u = 0; u < RU; ++u) af[u] = lds_frag<PK::a>(sIn + (16 * mrow[u] + lr) * LDI + 32 * kb + lk);
+      for (int u = 0; u < RU; ++u) af[u] = lds_frag<PK::a>(sX + (16 * mrow[u] + lr) * LDI + 32 * kb + lk);
 #pragma unroll
       for (int ni = 0; ni < TC; ++ni) {
-        const auto bf = lds_frag<PK::b>(sIn + (16 * ni + lr) * LDI + 32 * kb + lk);
+        const auto bf = lds_frag<PK::b>(sX + (16 * ni + lr) * LDI + 32 * kb + lk);
 #pragma unroll
         for (int u = 0; u < RU; ++u)
           if (ni <= mrow[u]) mma(acc[u][ni], af[u], bf);
       }
     }
 #pragma unroll
-    for (int u = 0; u < RU; ++u)
+    for (int u = 0; u < RU; ++u) {
+      const int m = mrow[u], L = TRI::len(m);
 #pragma unroll
       for (int ni = 0; ni < TC; ++ni) {
         const int c = 16 * ni + lr;
+        if (16 * ni < L) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * mrow[u] + lq + i;
-          sS[r * LDS_ + c] = (c < r) ? sBeta[r] * exp2_fast(sG2[r] - sG2[c]) * acc[u][ni][i] : 0.f;
+          for (int i = 0; i < 4; ++i) {
+            const int r = 16 * m + lq + i;
+            sT[TRI::at(r, c)] = (c < r) ? sBeta[r] * exp2_fast(sG2[r] - sG2[c]) * acc[u][ni][i] : 0.f;
+          }
         }
       }
+    }
   }
+  // V block -> registers; its latency hides behind the inversion
+  vt.load(reinterpret_cast<const TI *>(a.v) + (((size_t)b * a.T + t0) * a.Hv + hv) * D, (size_t)a.Hv * D);
   lds_barrier();
 
   // (4) exact inverses of the 16x16 diagonal blocks (forward substitution,
@@ -265,26 +388,26 @@ __global__ __launch_bounds__(NT) void prep_kernel(FwdArgs a) {
     float x[16];
     const int blk = tid >> 4, j = tid & 15;
     if (tid < C) {
-      const float *Sb = sS + (16 * blk) * LDS_ + 16 * blk;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
+        const float *Srow = sT + TRI::at(16 * blk + r, 16 * blk);
         float v = (r == j) ? 1.f : 0.f;
 #pragma unroll
-        for (int i = 0; i < r; ++i) v -= Sb[r * LDS_ + i] * x[i];
+        for (int i = 0; i < r; ++i) v -= Srow[i] * x[i];
         x[r] = v;
       }
     }
     lds_barrier();
     if (tid < C) {
-      float *Sb = sS + (16 * blk) * LDS_ + 16 * blk;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) Sb[r * LDS_ + j] = x[r];
+      for (int r = 0; r < 16; ++r) sT[TRI::at(16 * blk + r, 16 * blk + j)] = x[r];
     }
     lds_barrier();
   }
 
   // (5) doubling ladder: for each 2b diagonal block [[P,0],[L,Q]] the new
   //     lower-left block is -X_Q L X_P (X_P, X_Q the current inverses).
+  //     The row-major K tile is dead; its space holds the scratch sM.
   for (int bs = 16; bs < C; bs *= 2) {
     const int nb = C / (2 * bs), tb = bs / 16, ldm = bs + 4;
     // M1 = L X_P  (stored transposed in sM)
@@ -296,8 +419,9 @@ __global__ __launch_bounds__(NT) void prep_kernel(FwdArgs a) {
         float a8[8], b8[8];
         const int k0 = 32 * kb + lk;
         if (k0 < bs) {
-          ld8(sS + (s + bs + 16 * mi + lr) * LDS_ + s + k0, a8);
-          ld8s(sS + (s + k0) * LDS_ + s + 16 * ni + lr, LDS_, b8);
+          ld8(sT + TRI::at(s + bs + 16 * mi + lr, s + k0), a8);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) b8[j] = sT[TRI::at(s + k0 + j, s + 16 * ni + lr)];
         } else {
 #pragma unroll
           for (int j = 0; j < 8; ++j) a8[j] = b8[j] = 0.f;
@@ -319,7 +443,7 @@ __global__ __launch_bounds__(NT) void prep_kernel(FwdArgs a) {
         float a8[8], b8[8];
         const int k0 = 32 * kb + lk;
         if (k0 < bs) {
-          ld8(sS + (s + bs + 16 * mi + lr) * LDS_ + s + bs + k0, a8);
+          ld8(sT + TRI::at(s + bs + 16 * mi + lr, s + bs + k0), a8);
           ld8(M + (16 * ni + lr) * ldm + k0, b8);
         } else {
 #pragma unroll
@@ -328,17 +452,39 @@ __global__ __launch_bounds__(NT) void prep_kernel(FwdArgs a) {
         mma_k32<PR::ladder>(acc, a8, b8);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sS[(s + bs + 16 * mi + lq + i) * LDS_ + s + 16 * ni + lr] = -acc[i];
+      for (int i = 0; i < 4; ++i) sT[TRI::at(s + bs + 16 * mi + lq + i, s + 16 * ni + lr)] = -acc[i];
     }
     lds_barrier();
   }
 
-  const size_t cb = bh * a.N + n;  // chunk index into the workspace
   if (a.Tm) {
     float *Tg = a.Tm + cb * C * C;
-    for (int idx = tid; idx < C * C; idx += NT) Tg[idx] = sS[(idx / C) * LDS_ + idx % C];
+    for (int idx = tid; idx < C * C; idx += NT) {
+      const int r = idx / C, c = idx % C;
+      Tg[idx] = c < TRI::len(r >> 4) ? sT[TRI::at(r, c)] : 0.f;
+    }
   }
   if (tid < C) a.G[cb * C + tid] = sG[tid];
+
+  // K^T -> LDS from the registers
+  kt.put_transposed(sX);
+  lds_barrier();
+  if constexpr (FWD) {
+    // K^T fragments for the walk, fragment-major: (d tile m, k-block kb, lane)
+    // holds K[32 kb + 8 g + j][16 m + lr]; one contiguous 1 KB per wave store
+    TI *Ktg = reinterpret_cast<TI *>(a.Kt) + cb * D * C;
+#pragma unroll
+    for (int i = 0; i < D * C / 8 / NT; ++i) {
+      const int f = tid + i * NT;
+      const int l = f & 63, mk = f >> 6, m = mk / (C / 32), kb = mk % (C / 32);
+      const int d = 16 * m + (l & 15), r0 = 32 * kb + 8 * (l >> 4);
+      constexpr int VE = 16 / sizeof(TI);
+#pragma unroll
+      for (int v = 0; v < 8 / VE; ++v)
+        *reinterpret_cast<uint4 *>(Ktg + (size_t)f * 8 + v * VE) =
+            *reinterpret_cast<const uint4 *>(sX + XT<C, TI>::at(d, r0 + v * VE));
+    }
+  }
 
   // (6) W = (T diag(beta e^G)) K, computed transposed (W^T = K^T T'^T) so
   //     that each lane ends with 4 consecutive columns of one row of W.
@@ -346,18 +492,14 @@ __global__ __launch_bounds__(NT) void prep_kernel(FwdArgs a) {
   //     consecutive rows of one column of U (= 4 consecutive entries of U^T).
   // Wave w owns row tiles {w, TC-1-w}; T is lower triangular, so row tile m
   // needs k < 16(m+1).  The T fragments of k-blocks past the diagonal read
-  // T's zero upper triangle and their products are skipped.
+  // T's zero-filled or neighbouring entries and their products are skipped.
   constexpr int TD = D / 16;
   constexpr int KT = PolicyKinds<PR::wy>::a;   // T' fragments (split)
   constexpr int KX = PolicyKinds<PR::wy>::b;   // K / V fragments (exact data)
-  int mrow[RU];
-#pragma unroll
-  for (int u = 0; u < RU; ++u) mrow[u] = u == 0 ? wave : TC - 1 - wave;
   for (int pass = 0; pass < 2; ++pass) {
     if (pass == 1) {
       lds_barrier();
-      const TI *vin = reinterpret_cast<const TI *>(a.v) + (((size_t)b * a.T + t0) * a.Hv + hv) * D;
-      load_rows<TI, C>(sIn, LDI, vin, (size_t)a.Hv * D);
+      vt.put_transposed(sX);
       lds_barrier();
     }
     const float *scale = pass == 0 ? sScale : sBeta;
@@ -374,17 +516,16 @@ __global__ __launch_bounds__(NT) void prep_kernel(FwdArgs a) {
 #pragma unroll
       for (int u = 0; u < RU; ++u) {
         live[u] = 32 * kb < 16 * (mrow[u] + 1);
-        float x[8];
-        ld8(sS + (16 * mrow[u] + lr) * LDS_ + k0, x);
+        float x[8], sc[8];
+        ld8(sT + TRI::at(16 * mrow[u] + lr, k0), x);
+        ld8(scale + k0, sc);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] *= scale[k0 + j];
+        for (int j = 0; j < 8; ++j) x[j] *= sc[j];
         tf[u] = make_frag<KT>(x);
       }
 #pragma unroll
       for (int md = 0; md < TD; ++md) {
-        float x[8];
-        ld8s(sIn + k0 * LDI + 16 * md + lr, LDI, x);   // column 16md+lr of K (or V), rows k0..k0+7
-        const auto xf = make_frag<KX>(x);
+        const auto xf = xt_frag<KX, C, TI>(sX, 16 * md + lr, k0);   // X^T row 16md+lr = column of K (or V)
 #pragma unroll
         for (int u = 0; u < RU; ++u) {
           if (!live[u]) continue;
