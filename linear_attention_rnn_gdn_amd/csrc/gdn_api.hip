@@ -79,8 +79,17 @@ constexpr int kSlice = 32;
 template <int C, typename TI, int MODE, int KIND>
 gdn_status launch_walk(const FwdArgs &a, hipStream_t st) {
   const int width = KIND == FOLD ? 2 * D : D;
-  const long blocks = (long)(width / kSlice) * a.B * a.Hv * a.jobs;
-  hipLaunchKernelGGL((walk_kernel<C, TI, MODE, kSlice, KIND>), dim3((unsigned)blocks), dim3(WALK_NT), 0, st, a);
+  // one wave per 16-column slice.  Enough units to give every compute unit
+  // two workgroups: 8 slices per workgroup sharing their operands through
+  // LDS.  Fewer (a short walk, latency-bound): one slice per workgroup, so
+  // the walk spreads over the chip's compute units.
+  const long units = (long)a.B * a.Hv * a.jobs;
+  if (units * (width / 128) >= 512) {
+    hipLaunchKernelGGL((walk_shared_kernel<C, TI, MODE, KIND, 8>), dim3((unsigned)(units * (width / 128))), dim3(512), 0,
+                       st, a);
+  } else {
+    hipLaunchKernelGGL((walk_ring_kernel<C, TI, MODE, KIND>), dim3((unsigned)(units * (width / 16))), dim3(64), 0, st, a);
+  }
   return check_launch();
 }
 

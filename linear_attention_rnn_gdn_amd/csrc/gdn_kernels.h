@@ -14,20 +14,22 @@
 // "Changes").  w, u, k_g and S are not defined on those pages; the forms above
 // are the reading under which the affine step equals the per-token rule.
 //
-// Kernels (all 256 threads = 4 waves of 64):
-//   prep_kernel    one workgroup per (chunk, value head, batch): G, S, T, W, U,
-//                  and K^T for the walk
-//   walk_kernel    one workgroup per (column slice, value head, batch, job):
-//                  the sequential chunk walk.  Each wave keeps its part of the
-//                  fp32 state in registers; W and K^T operand fragments come
-//                  straight from global memory one chunk ahead; only a bf16
-//                  copy of the state and the corrected values V' pass through
-//                  LDS.  Modes: WALK (state = h, writes chunk-start states and
-//                  V') and FOLD (state = the augmented [A | B] of a group,
+// Kernels:
+//   prep_kernel    one workgroup (4 waves) per (chunk, value head, batch):
+//                  G, S, T, W, U, and K^T for the walk
+//   walk_ring_kernel / walk_shared_kernel
+//                  the sequential chunk walk, one wave per 16-column slice of
+//                  the state, which stays in matrix-core result registers and
+//                  feeds the next product directly.  The ring form (one wave
+//                  per workgroup) streams W and K^T through registers, for
+//                  walks too few to fill the chip; the shared form (8 waves
+//                  per workgroup) copies them once per workgroup into LDS.
+//                  Modes: WALK (state = h, writes chunk-start states and V')
+//                  and FOLD (state = the augmented [A | B] of a group,
 //                  started from [I | 0]; writes the group's pair).
 //   prefix_kernel  one workgroup per (column slice, bh): exclusive prefix of
 //                  the groups' affine pairs.
-//   out_kernel     one workgroup per (column slice, chunk, bh): the output,
+//   out_kernel     one workgroup per (32-column slice, chunk, bh): the output,
 //                  with P^T kept in registers between its two products.
 //
 // Workspace tensors (cb = bh*N + n indexes a chunk of a value head).  The
@@ -36,15 +38,17 @@
 // per-lane load or store of a wave covers 1 KB of consecutive bytes.
 // (Row-major tiles read in matrix-core operand layout put consecutive lanes
 // on different rows, and each such instruction breaks into dozens of memory
-// requests.)  Lane l = lr + 16 g (lr = l % 16, g = l / 16).
+// requests.)  Lane l = lr + 16 g (lr = l % 16, g = l / 16); a fragment's 8
+// k-values for lane group g are kk(g, j) = 4g + j (j < 4), 16 + 4g + j - 4
+// (j >= 4) within its block of 32 (the order of two stacked result tiles).
 //   G   [cb][C] fp32 decay cumsum
-//   Wf  [cb][C/16][D/32][64][8]  W[16m + lr][32kb + 8g + j], input dtype
-//   Ktf [cb][D/16][C/32][64][8]  K[32kb + 8g + j][16m + lr], input dtype
+//   Wf  [cb][C/16][D/32][64][8]  W[16m + lr][32kb + kk(g, j)], input dtype
+//   Ktf [cb][D/16][C/32][64][8]  K[32kb + kk(g, j)][16m + lr], input dtype
 //   Uf  [cb][C/16][D/16][64][4]  U[16m + 4g + i][16nd + lr], fp32
-//   Hsf [cb][D/S][D/16][S/16][64][4]  chunk-start state h[16m + 4g + i][c0 + 16ni + lr]
-//   Vnf [cb][D/S][C/16][S/16][64][4]  corrected values V'[16m + 4g + i][c0 + 16ni + lr]
-// (S = column-slice width, c0 = S * slice.)  Decays are evaluated as exp2 of
-// log2-scaled cumsums (one v_exp_f32 each).
+//   Hsf [cb][D/16][D/16][64][4]  chunk-start state h[16m + 4g + i][16s + lr]
+//   Vnf [cb][D/16][C/16][64][4]  corrected values V'[16m + 4g + i][16s + lr]
+// (s = the 16-column slice.)  Decays are evaluated as exp2 of log2-scaled
+// cumsums (one v_exp_f32 each).
 //
 // Workgroups are numbered 1-D.  The hardware places workgroup i on XCD i % 8;
 // xcd_unit() hands all column slices of one (head, chunk or job) to one XCD
@@ -471,18 +475,27 @@ __global__ __launch_bounds__(NT, 2) void prep_kernel(FwdArgs a) {
   lds_barrier();
   if constexpr (FWD) {
     // K^T fragments for the walk, fragment-major: (d tile m, k-block kb, lane)
-    // holds K[32 kb + 8 g + j][16 m + lr]; one contiguous 1 KB per wave store
+    // holds K[r][16 m + lr] for the 8 tokens r = 32 kb + {4g..4g+3,
+    // 16+4g..16+4g+3} (the k order of the walk's register-chained operand);
+    // one contiguous 1 KB per wave store
     TI *Ktg = reinterpret_cast<TI *>(a.Kt) + cb * D * C;
+    constexpr int VE = 16 / sizeof(TI);
 #pragma unroll
     for (int i = 0; i < D * C / 8 / NT; ++i) {
       const int f = tid + i * NT;
       const int l = f & 63, mk = f >> 6, m = mk / (C / 32), kb = mk % (C / 32);
-      const int d = 16 * m + (l & 15), r0 = 32 * kb + 8 * (l >> 4);
-      constexpr int VE = 16 / sizeof(TI);
+      const int d = 16 * m + (l & 15);
+      TI tmp[8];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int k = 32 * kb + 16 * hh + 4 * (l >> 4);   // 4 consecutive tokens
+        const TI *src = sX + XT<C, TI>::at(d, k - k % VE) + k % VE;
+        if constexpr (sizeof(TI) == 2) *reinterpret_cast<uint2 *>(tmp + 4 * hh) = *reinterpret_cast<const uint2 *>(src);
+        else *reinterpret_cast<uint4 *>(tmp + 4 * hh) = *reinterpret_cast<const uint4 *>(src);
+      }
 #pragma unroll
       for (int v = 0; v < 8 / VE; ++v)
-        *reinterpret_cast<uint4 *>(Ktg + (size_t)f * 8 + v * VE) =
-            *reinterpret_cast<const uint4 *>(sX + XT<C, TI>::at(d, r0 + v * VE));
+        *reinterpret_cast<uint4 *>(Ktg + (size_t)f * 8 + v * VE) = *reinterpret_cast<const uint4 *>(tmp + v * VE);
     }
   }
 
@@ -539,14 +552,22 @@ __global__ __launch_bounds__(NT, 2) void prep_kernel(FwdArgs a) {
 #pragma unroll
       for (int md = 0; md < TD; ++md) {
         if (pass == 0 && FWD) {
-          // lane holds W[r][16md + 4g + i], r = 16 mrow + lr: in the walk's
-          // fragment (mrow, kb = md/2) these are lane lr + 16 (2 (md%2) + g/2),
-          // elements 4 (g%2) + i
-          const int kb = md >> 1, gg = 2 * (md & 1) + (g >> 1);
-          WT *dst = reinterpret_cast<WT *>(a.W) +
-                    ((cb * (C / 16) + mrow[u]) * (D / 32) + kb) * 512 + (lr + 16 * gg) * 8 + 4 * (g & 1);
+          // lane holds W[r][16md + 4g + i], r = 16 mrow + lr.  The walk's
+          // fragment (mrow, kb) gives lane (lr, g) the k-values 32 kb +
+          // {4g..4g+3, 16+4g..16+4g+3}: tiles md = 2kb and 2kb+1 of this
+          // lane, stored together as one 16-byte vector.
+          if (md & 1) continue;
+          WT tmp[8];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) dst[i] = from_f32<WT>(acc[u][md][i]);
+          for (int i = 0; i < 4; ++i) {
+            tmp[i] = from_f32<WT>(acc[u][md][i]);
+            tmp[4 + i] = from_f32<WT>(acc[u][md + 1][i]);
+          }
+          WT *dst = reinterpret_cast<WT *>(a.W) + ((cb * (C / 16) + mrow[u]) * (D / 32) + (md >> 1)) * 512 + lane * 8;
+          constexpr int VE = 16 / sizeof(WT);
+#pragma unroll
+          for (int v = 0; v < 8 / VE; ++v)
+            *reinterpret_cast<uint4 *>(dst + v * VE) = *reinterpret_cast<const uint4 *>(tmp + v * VE);
         } else if (pass == 0) {
           WT *dst = reinterpret_cast<WT *>(a.W) + (cb * C + 16 * mrow[u] + lr) * D + 16 * md + lq;
 #pragma unroll
@@ -566,64 +587,75 @@ __global__ __launch_bounds__(NT, 2) void prep_kernel(FwdArgs a) {
 }
 
 // ----------------------------------------------------------------------------
-// walk / fold: the sequential chunk loop for one column slice of the state.
+// walk / fold, throughput form: the sequential chunk loop.  Each wave owns a
+// 16-column slice of the state; a workgroup of WPG waves covers WPG adjacent
+// slices and shares the chunk's W and K^T operand fragments through LDS.
 //
-// 8 waves (512 threads; two per SIMD so one can issue while the other waits).
-// Wave w owns one row tile of V' (C x S) and one row tile of the state
-// (D x S), with the column tiles shared out as below.  Its share of the fp32
-// state stays in registers for the whole walk.  Per chunk:
-//   V' = U - W h        A = W rows (fragments loaded from global, one chunk
-//                       ahead), B = bf16 copy of h in LDS
-//   h  = e^{G_last} h + K^T (d o V')   A = K^T rows (global, one chunk
-//                       ahead), B = d o V' in LDS, already split into the
-//                       operand form (hi/lo bf16) by its producer;
-//                       d_r = e^{G_last - G_r}
-// with two barriers per chunk.
-constexpr int WALK_NT = 512;
+// The wave keeps its D x 16 slice of the fp32 state in matrix-core result
+// registers (D/16 tiles of 16 x 16).  Per chunk:
+//   V' = U - W h                        B operand: the state tiles
+//   h  = e^{G_last} h + K^T (d o V')    B operand: the V' result tiles,
+//                                       d_r = e^{G_last - G_r}
+// A result tile gives lane group g rows 4g..4g+3 of its 16 rows, so two
+// stacked tiles give lane group g the k-values {4g..4g+3, 16+4g..16+4g+3} of
+// a block of 32: prep stores W and K^T with the k-values of each fragment in
+// that order, and neither h nor V' leaves the registers between products.
+//
+// W and K^T fragments (the A operands; 64 KB per chunk at C = 128) and the
+// decay cumsum G are copied from memory straight into LDS (global_load_lds,
+// no registers), one chunk ahead into the other of two buffers, the copies
+// split over the waves; one barrier per chunk.  U arrives in registers one
+// chunk ahead.
+// Modes: WALK (state = h; writes chunk-start states and V') and FOLD
+// (state = the augmented [A | B] of a group, started from [I | 0]; writes
+// the group's pair).
+template <int C, typename TI> struct WalkOps {
+  static constexpr int MV = C / 16, MH = D / 16;              // V' and state row tiles
+  static constexpr int KBW = D / 32, KBK = C / 32;            // k-blocks of the two products
+  static constexpr int FW = MV * KBW, FK = MH * KBK, F = FW + FK;   // fragments per chunk
+  static constexpr int BPF = 8 * (int)sizeof(TI) / 16;       // 1 KB blocks per fragment
+  static constexpr int NBLK = F * BPF;                        // 1 KB blocks per chunk
+  static constexpr int GOFF = NBLK * 1024;                    // G (C floats) after the fragments
+  static constexpr int ELEMS = (GOFF + 4 * C) / (int)sizeof(TI); // LDS buffer elements
+};
 
-template <int C, typename TI, int MODE, int S, int KIND>
-__global__ __launch_bounds__(WALK_NT) void walk_kernel(FwdArgs a) {
+template <int C, typename TI, int MODE, int KIND, int WPG>
+__global__ __launch_bounds__(64 * WPG) void walk_shared_kernel(FwdArgs a) {
   using PR = Prec<MODE>;
   using PKw = PolicyKinds<PR::wh>;
   using PKk = PolicyKinds<PR::kv>;
-  static_assert(PKw::a == (sizeof(TI) == 2 ? F_BF16 : F_F32) && PKk::a == PKw::a,
-                "W and K^T fragments are read as stored");
-  constexpr bool F32 = PKk::b == F_F32;
-  using HB = typename std::conditional<PKw::b == F_F32, float, __bf16>::type;   // state copy for W h
-  constexpr int NW = WALK_NT / 64;
-  constexpr int NS = (KIND == FOLD ? 2 * D : D) / S;
-  constexpr int TN = S / 16;          // column tiles of the slice
-  constexpr int TRV = C / 16;         // V' row tiles
-  constexpr int CPW = TN * TRV / NW;  // V' column tiles per wave
-  constexpr int CPH = TN * (D / 16) / NW;   // state column tiles per wave
-  constexpr int KBW = D / 32, KBK = C / 32;
-  constexpr int LDHB = D + (sizeof(HB) == 2 ? 8 : 4);   // sHb [S][LDHB]
-  constexpr int LDV = C + (F32 ? 4 : 8);                 // sV  [S][LDV] (x2 when split)
-  static_assert(CPW >= 1 && CPH >= 1 && TN % CPW == 0 && TN % CPH == 0, "tiling");
-  __shared__ __align__(16) HB sHb[S * LDHB];
-  __shared__ __align__(16) typename std::conditional<F32, float, __bf16>::type sV[(F32 ? 1 : 2) * S * LDV];
+  using OPS = WalkOps<C, TI>;
+  constexpr bool F32 = sizeof(TI) == 4;
+  static_assert(PKw::a == (F32 ? F_F32 : F_BF16) && PKk::a == PKw::a, "W and K^T fragments are used as stored");
+  using AF = Frag<PKw::a>;
+  constexpr int NS = (KIND == FOLD ? 2 * D : D) / 16;   // slices per unit
+  constexpr int NG = NS / WPG;                           // workgroups per unit
+  constexpr int MV = OPS::MV, MH = OPS::MH, KBW = OPS::KBW, KBK = OPS::KBK;
+  constexpr int FW = OPS::FW, BPF = OPS::BPF, NBLK = OPS::NBLK;
+  static_assert(NS % WPG == 0 && NBLK % WPG == 0, "work split");
+  __shared__ __align__(16) TI bufA[OPS::ELEMS];
+  __shared__ __align__(16) TI bufB[OPS::ELEMS];
 
-  int unit, slice;
-  xcd_unit(blockIdx.x, NS, a.B * a.Hv * a.jobs, unit, slice);
+  int unit, grp;
+  xcd_unit(blockIdx.x, NG, a.B * a.Hv * a.jobs, unit, grp);
   const int job = unit % a.jobs;
   const size_t bh = (size_t)(unit / a.jobs);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lr = lane & 15, lk = (lane >> 4) * 8, lq = (lane >> 4) * 4;
-  const int c0 = slice * S;   // first column of the slice (augmented [A|B] in FOLD)
+  const int lr = lane & 15, g = lane >> 4;
+  const int slice = grp * WPG + wave;
+  const int c0 = slice * 16;   // first column (of the augmented [A|B] in FOLD)
   const bool has_u = KIND == WALK || c0 >= D;
-  const int uc0 = KIND == WALK ? c0 : c0 - D;
-  // this wave's tiles
-  const int mv = wave % TRV, nv0 = (wave / TRV) * CPW;             // V' row tile, first column tile
-  const int mh = wave % (D / 16), nh0 = (wave / (D / 16)) * CPH;   // state row tile, first column tile
+  const int us = KIND == WALK ? slice : slice - D / 16;   // U column tile
+  const size_t cb0 = bh * a.N + (size_t)job * a.cpj;
 
-  // state: tiles (mh, nh0 + t): rows 16 mh + lq + i, column 16 (nh0 + t) + lr
-  f32x4 h[CPH];
+  // state tiles: h[m] holds rows 16m + 4g + i, column c0 + lr
+  f32x4 h[MH];
 #pragma unroll
-  for (int t = 0; t < CPH; ++t) {
-    const int col = c0 + 16 * (nh0 + t) + lr;
+  for (int m = 0; m < MH; ++m) {
+    const int col = c0 + lr;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int kr = 16 * mh + lq + i;
+      const int kr = 16 * m + 4 * g + i;
       float x = 0.f;
       if (KIND == FOLD) {
         x = (col < D && kr == col) ? 1.f : 0.f;
@@ -631,148 +663,160 @@ __global__ __launch_bounds__(WALK_NT) void walk_kernel(FwdArgs a) {
         const float *src = a.init_per_job ? a.init + (bh * a.jobs + job) * D * D : a.init + bh * D * D;
         x = src[(size_t)kr * D + col];
       }
-      h[t][i] = x;
+      h[m][i] = x;
     }
   }
-  auto put_state_copy = [&]() {
+
+  // copy the chunk's operand fragments into an LDS buffer: block j (1 KB) is
+  // half j % BPF of fragment j / BPF; wave w copies blocks w, w + WPG, ...
+  // (addresses: a wave-uniform base plus a 32-bit lane offset)
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const unsigned loff = lane * 16 * BPF;
+  auto stage = [&](TI *buf, size_t cb) {
+    const char *wbase = reinterpret_cast<const char *>(a.W) + cb * C * D * sizeof(TI);
+    const char *kbase = reinterpret_cast<const char *>(a.Kt) + cb * D * C * sizeof(TI);
 #pragma unroll
-    for (int t = 0; t < CPH; ++t) {
-      HB *dst = sHb + (16 * (nh0 + t) + lr) * LDHB + 16 * mh + lq;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dst[i] = from_f32<HB>(h[t][i]);
+    for (int jj = 0; jj < NBLK / WPG; ++jj) {
+      const int j = jj * WPG + wv, p = j / BPF, hh = j % BPF;
+      const char *src = (p < FW ? wbase + p * 1024 * BPF : kbase + (p - FW) * 1024 * BPF) + hh * 16;
+      __builtin_amdgcn_global_load_lds((const void *)(src + loff),
+                                       (__attribute__((address_space(3))) void *)(reinterpret_cast<char *>(buf) + j * 1024),
+                                       16, 0, 0);
     }
+    if (wv == WPG - 1 && lane < C / 4)
+      __builtin_amdgcn_global_load_lds((const void *)(a.G + cb * C + lane * 4),
+                                       (__attribute__((address_space(3))) void *)(reinterpret_cast<char *>(buf) + OPS::GOFF),
+                                       16, 0, 0);
+    // keep the copies ahead of everything that follows in program order
+    asm volatile("" ::: "memory");
+  };
+  auto frag = [&](const TI *buf, int p) -> AF {
+    AF f;
+    const char *base = reinterpret_cast<const char *>(buf) + p * BPF * 1024 + lane * 16;
+    if constexpr (F32) {
+      const float4 x0 = *reinterpret_cast<const float4 *>(base);
+      const float4 x1 = *reinterpret_cast<const float4 *>(base + 1024);
+      f.v[0] = x0.x; f.v[1] = x0.y; f.v[2] = x0.z; f.v[3] = x0.w;
+      f.v[4] = x1.x; f.v[5] = x1.y; f.v[6] = x1.z; f.v[7] = x1.w;
+    } else {
+      f.hi = *reinterpret_cast<const bf16x8 *>(base);
+    }
+    return f;
+  };
+  // this wave's copies and loads done, then every wave's
+  auto chunk_barrier = [&]() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    __builtin_amdgcn_s_barrier();
   };
 
-  struct Ops {
-    Frag<PKw::a> wf[KBW];
-    Frag<PKk::a> kf[KBK];
-    float4 u[CPW];
-    float4 g;
-    float glast;
+  struct UG {
+    float4 u[MV];
   };
-  auto fetch = [&](Ops &op, int n) {
-    const size_t cb = bh * a.N + n;
-    const TI *Wg = reinterpret_cast<const TI *>(a.W) + cb * C * D + (size_t)mv * KBW * 512 + lane * 8;
-    const TI *Kg = reinterpret_cast<const TI *>(a.Kt) + cb * D * C + (size_t)mh * KBK * 512 + lane * 8;
+  auto fetch_u = [&](size_t cb, UG &x) {
+#pragma unroll
+    for (int m = 0; m < MV; ++m)
+      x.u[m] = has_u ? *reinterpret_cast<const float4 *>(a.U + ((cb * MV + m) * (D / 16) + us) * 256 + lane * 4)
+                     : float4{0.f, 0.f, 0.f, 0.f};
+  };
+
+  UG ug[2];
+  stage(bufA, cb0);
+  fetch_u(cb0, ug[0]);
+  chunk_barrier();
+
+  auto step = [&](const TI *cur, TI *nxt, UG &cu, UG &nu, int cc) {
+    const size_t cb = cb0 + cc;
+    const bool more = cc + 1 < a.cpj;
+    // everything for the next chunk; waited for at the chunk's end only
+    fetch_u(more ? cb + 1 : cb, nu);
+    if (more) stage(nxt, cb + 1);
+    const float *Gs = reinterpret_cast<const float *>(reinterpret_cast<const char *>(cur) + OPS::GOFF);
+    const float gl2 = Gs[C - 1] * LOG2E;
+    float dcy[MV][4];
+#pragma unroll
+    for (int m = 0; m < MV; ++m) {
+      const float4 gq = *reinterpret_cast<const float4 *>(Gs + 16 * m + 4 * g);
+      dcy[m][0] = exp2_fast(gl2 - gq.x * LOG2E);
+      dcy[m][1] = exp2_fast(gl2 - gq.y * LOG2E);
+      dcy[m][2] = exp2_fast(gl2 - gq.z * LOG2E);
+      dcy[m][3] = exp2_fast(gl2 - gq.w * LOG2E);
+    }
+    // V' = U - W h
+    Frag<PKw::b> hb[KBW];
 #pragma unroll
     for (int kb = 0; kb < KBW; ++kb) {
-      if constexpr (sizeof(TI) == 2) {
-        op.wf[kb].hi = *reinterpret_cast<const bf16x8 *>(Wg + kb * 512);
-      } else {
-        const float4 x0 = *reinterpret_cast<const float4 *>(Wg + kb * 512);
-        const float4 x1 = *reinterpret_cast<const float4 *>(Wg + kb * 512 + 4);
-        float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-        op.wf[kb] = make_frag<PKw::a>(x);
-      }
+      const float x[8] = {h[2 * kb][0], h[2 * kb][1], h[2 * kb][2], h[2 * kb][3],
+                          h[2 * kb + 1][0], h[2 * kb + 1][1], h[2 * kb + 1][2], h[2 * kb + 1][3]};
+      hb[kb] = make_frag<PKw::b>(x);
     }
+    f32x4 acc[MV];
 #pragma unroll
-    for (int kb = 0; kb < KBK; ++kb) {
-      if constexpr (sizeof(TI) == 2) {
-        op.kf[kb].hi = *reinterpret_cast<const bf16x8 *>(Kg + kb * 512);
-      } else {
-        const float4 x0 = *reinterpret_cast<const float4 *>(Kg + kb * 512);
-        const float4 x1 = *reinterpret_cast<const float4 *>(Kg + kb * 512 + 4);
-        float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-        op.kf[kb] = make_frag<PKk::a>(x);
+    for (int m = 0; m < MV; ++m) acc[m] = zero4();
+    // fragments are read a group (one output tile's k-blocks) ahead
+    AF fa[2][KBW];
+#pragma unroll
+    for (int kb = 0; kb < KBW; ++kb) fa[0][kb] = frag(cur, kb);
+#pragma unroll
+    for (int m = 0; m < MV; ++m) {
+      if (m + 1 < MV) {
+#pragma unroll
+        for (int kb = 0; kb < KBW; ++kb) fa[(m + 1) & 1][kb] = frag(cur, (m + 1) * KBW + kb);
       }
-    }
 #pragma unroll
-    for (int t = 0; t < CPW; ++t)
-      op.u[t] = has_u ? *reinterpret_cast<const float4 *>(
-                            a.U + ((cb * TRV + mv) * (D / 16) + uc0 / 16 + nv0 + t) * 256 + lane * 4)
-                      : float4{0.f, 0.f, 0.f, 0.f};
-    op.g = *reinterpret_cast<const float4 *>(a.G + cb * C + 16 * mv + lq);
-    op.glast = a.G[cb * C + C - 1 + vgpr_zero()];
-  };
-
-  Ops ops[2];
-  fetch(ops[0], job * a.cpj);
-  put_state_copy();
-  lds_barrier();
-
-  auto step = [&](Ops &cur, Ops &nxt, int cc) {
-    const int n = job * a.cpj + cc;
-    const size_t cb = bh * a.N + n;
-    if (cc + 1 < a.cpj) fetch(nxt, n + 1);
-
-    // chunk-start state for the output stage, fragment-major
+      for (int kb = 0; kb < KBW; ++kb) mma(acc[m], fa[m & 1][kb], hb[kb]);
+    }
+    // chunk-start state for the output stage (stores issued after the loads
+    // this chunk still waits for)
     if (KIND == WALK && a.Hs) {
 #pragma unroll
-      for (int t = 0; t < CPH; ++t)
-        *reinterpret_cast<float4 *>(a.Hs + (((cb * NS + slice) * (D / 16) + mh) * TN + nh0 + t) * 256 + lane * 4) =
-            float4{h[t][0], h[t][1], h[t][2], h[t][3]};
+      for (int m = 0; m < MH; ++m)
+        *reinterpret_cast<float4 *>(a.Hs + ((cb * (D / 16) + slice) * MH + m) * 256 + lane * 4) =
+            float4{h[m][0], h[m][1], h[m][2], h[m][3]};
     }
-    // V' = U - W h, then d o V' into LDS in the update's operand form
-    const float gl2 = cur.glast * LOG2E;
+    Frag<PKk::b> vb[KBK];
     {
-      f32x4 acc[CPW];
+      float s[MV][4];
 #pragma unroll
-      for (int t = 0; t < CPW; ++t) acc[t] = zero4();
-#pragma unroll
-      for (int kb = 0; kb < KBW; ++kb) {
-#pragma unroll
-        for (int t = 0; t < CPW; ++t)
-          mma(acc[t], cur.wf[kb], lds_frag<PKw::b>(sHb + (16 * (nv0 + t) + lr) * LDHB + 32 * kb + lk));
-      }
-      const int r0 = 16 * mv + lq;
-      const float d0 = exp2_fast(gl2 - cur.g.x * LOG2E), d1 = exp2_fast(gl2 - cur.g.y * LOG2E);
-      const float d2 = exp2_fast(gl2 - cur.g.z * LOG2E), d3 = exp2_fast(gl2 - cur.g.w * LOG2E);
-#pragma unroll
-      for (int t = 0; t < CPW; ++t) {
-        const int c = 16 * (nv0 + t) + lr;
-        const float4 uu = cur.u[t];
-        const float4 vp = {uu.x - acc[t][0], uu.y - acc[t][1], uu.z - acc[t][2], uu.w - acc[t][3]};
+      for (int m = 0; m < MV; ++m) {
+        const float4 uu = cu.u[m];
+        const float4 vp = {uu.x - acc[m][0], uu.y - acc[m][1], uu.z - acc[m][2], uu.w - acc[m][3]};
         if (KIND == WALK && a.Vn)
-          *reinterpret_cast<float4 *>(a.Vn + (((cb * NS + slice) * TRV + mv) * TN + nv0 + t) * 256 + lane * 4) = vp;
-        const float s4[4] = {vp.x * d0, vp.y * d1, vp.z * d2, vp.w * d3};
-        if constexpr (F32) {
-          *reinterpret_cast<float4 *>(sV + c * LDV + r0) = float4{s4[0], s4[1], s4[2], s4[3]};
-        } else {
-          __bf16 hi[4], lo[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            hi[i] = (__bf16)s4[i];
-            lo[i] = (__bf16)(s4[i] - (float)hi[i]);
-          }
-          *reinterpret_cast<uint2 *>(sV + c * LDV + r0) = *reinterpret_cast<const uint2 *>(hi);
-          *reinterpret_cast<uint2 *>(sV + S * LDV + c * LDV + r0) = *reinterpret_cast<const uint2 *>(lo);
-        }
+          *reinterpret_cast<float4 *>(a.Vn + ((cb * (D / 16) + slice) * MV + m) * 256 + lane * 4) = vp;
+        s[m][0] = vp.x * dcy[m][0];
+        s[m][1] = vp.y * dcy[m][1];
+        s[m][2] = vp.z * dcy[m][2];
+        s[m][3] = vp.w * dcy[m][3];
       }
-    }
-    lds_barrier();
-    // h <- e^{G_last} h + K^T (d o V')
-    {
-      const float gl = exp2_fast(gl2);
-      f32x4 acc[CPH];
-#pragma unroll
-      for (int t = 0; t < CPH; ++t) acc[t] = zero4();
 #pragma unroll
       for (int kb = 0; kb < KBK; ++kb) {
-#pragma unroll
-        for (int t = 0; t < CPH; ++t) {
-          const int off = (16 * (nh0 + t) + lr) * LDV + 32 * kb + lk;
-          Frag<PKk::b> bf;
-          if constexpr (F32) {
-            bf = lds_frag<PKk::b>(sV + off);
-          } else {
-            bf.hi = *reinterpret_cast<const bf16x8 *>(sV + off);
-            bf.lo = *reinterpret_cast<const bf16x8 *>(sV + S * LDV + off);
-          }
-          mma(acc[t], cur.kf[kb], bf);
-        }
+        const float x[8] = {s[2 * kb][0], s[2 * kb][1], s[2 * kb][2], s[2 * kb][3],
+                            s[2 * kb + 1][0], s[2 * kb + 1][1], s[2 * kb + 1][2], s[2 * kb + 1][3]};
+        vb[kb] = make_frag<PKk::b>(x);
       }
-#pragma unroll
-      for (int t = 0; t < CPH; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) h[t][i] = gl * h[t][i] + acc[t][i];
     }
-    put_state_copy();
-    lds_barrier();
+    // h <- e^{G_last} h + K^T (d o V')
+    const float gl = exp2_fast(gl2);
+    AF fk[2][KBK];
+#pragma unroll
+    for (int kb = 0; kb < KBK; ++kb) fk[0][kb] = frag(cur, FW + kb);
+#pragma unroll
+    for (int m = 0; m < MH; ++m) {
+      if (m + 1 < MH) {
+#pragma unroll
+        for (int kb = 0; kb < KBK; ++kb) fk[(m + 1) & 1][kb] = frag(cur, FW + (m + 1) * KBK + kb);
+      }
+      f32x4 acc2 = zero4();
+#pragma unroll
+      for (int kb = 0; kb < KBK; ++kb) mma(acc2, fk[m & 1][kb], vb[kb]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) h[m][i] = gl * h[m][i] + acc2[i];
+    }
+    chunk_barrier();
   };
-  // two chunks per trip so the operand sets alternate without copies
+  // two chunks per trip: the LDS buffers and U/G sets alternate statically
   for (int cc = 0; cc < a.cpj; cc += 2) {
-    step(ops[0], ops[1], cc);
-    if (cc + 1 < a.cpj) step(ops[1], ops[0], cc + 1);
+    step(bufA, bufB, ug[0], ug[1], cc);
+    if (cc + 1 < a.cpj) step(bufB, bufA, ug[1], ug[0], cc + 1);
   }
 
   // final state slice
@@ -786,10 +830,192 @@ __global__ __launch_bounds__(WALK_NT) void walk_kernel(FwdArgs a) {
   }
   if (dst) {
 #pragma unroll
-    for (int t = 0; t < CPH; ++t)
+    for (int m = 0; m < MH; ++m)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        dst[(size_t)(16 * mh + lq + i) * D + dcol + 16 * (nh0 + t) + lr] = h[t][i];
+      for (int i = 0; i < 4; ++i) dst[(size_t)(16 * m + 4 * g + i) * D + dcol + lr] = h[m][i];
+  }
+}
+
+// ----------------------------------------------------------------------------
+// walk / fold, latency form: one workgroup of one wave per 16-column slice of
+// the state (no LDS, no barriers), for walks too few to fill the chip.
+//
+// The state, V' and their register chaining are those of walk_shared_kernel
+// below.  W and K^T fragments stream from memory, in the order they are used,
+// through a ring of RING register slots (a slot is refilled as soon as its
+// fragment has been consumed); U and G arrive one chunk ahead.
+template <int C, typename TI, int MODE, int KIND>
+__global__ __launch_bounds__(64) void walk_ring_kernel(FwdArgs a) {
+  using PR = Prec<MODE>;
+  using PKw = PolicyKinds<PR::wh>;
+  using PKk = PolicyKinds<PR::kv>;
+  constexpr bool F32 = sizeof(TI) == 4;
+  static_assert(PKw::a == (F32 ? F_F32 : F_BF16) && PKk::a == PKw::a, "W and K^T fragments are used as stored");
+  using AF = Frag<PKw::a>;
+  constexpr int NS = (KIND == FOLD ? 2 * D : D) / 16;   // slices
+  constexpr int MV = C / 16, MH = D / 16;                // V' and state row tiles
+  constexpr int KBW = D / 32, KBK = C / 32;              // k-blocks of the two products
+  constexpr int FW = MV * KBW, FK = MH * KBK, F = FW + FK;   // fragments per chunk
+  constexpr int RING = F32 ? 16 : 32;
+  static_assert(F % RING == 0, "ring slots must repeat every chunk");
+
+  int unit, slice;
+  xcd_unit(blockIdx.x, NS, a.B * a.Hv * a.jobs, unit, slice);
+  const int job = unit % a.jobs;
+  const size_t bh = (size_t)(unit / a.jobs);
+  const int lane = threadIdx.x, lr = lane & 15, g = lane >> 4;
+  const int c0 = slice * 16;   // first column (of the augmented [A|B] in FOLD)
+  const bool has_u = KIND == WALK || c0 >= D;
+  const int us = KIND == WALK ? slice : slice - D / 16;   // U column tile
+  const size_t cb0 = bh * a.N + (size_t)job * a.cpj;
+
+  // state tiles: h[m] holds rows 16m + 4g + i, column c0 + lr
+  f32x4 h[MH];
+#pragma unroll
+  for (int m = 0; m < MH; ++m) {
+    const int col = c0 + lr;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int kr = 16 * m + 4 * g + i;
+      float x = 0.f;
+      if (KIND == FOLD) {
+        x = (col < D && kr == col) ? 1.f : 0.f;
+      } else if (a.init) {
+        const float *src = a.init_per_job ? a.init + (bh * a.jobs + job) * D * D : a.init + bh * D * D;
+        x = src[(size_t)kr * D + col];
+      }
+      h[m][i] = x;
+    }
+  }
+
+  const TI *Wb = reinterpret_cast<const TI *>(a.W) + lane * 8;
+  const TI *Kb = reinterpret_cast<const TI *>(a.Kt) + lane * 8;
+  auto load = [&](size_t cb, int p) -> AF {
+    const TI *src = p < FW ? Wb + cb * C * D + (size_t)p * 512 : Kb + cb * D * C + (size_t)(p - FW) * 512;
+    AF f;
+    if constexpr (F32) {
+      const float4 x0 = *reinterpret_cast<const float4 *>(src);
+      const float4 x1 = *reinterpret_cast<const float4 *>(src + 4);
+      f.v[0] = x0.x; f.v[1] = x0.y; f.v[2] = x0.z; f.v[3] = x0.w;
+      f.v[4] = x1.x; f.v[5] = x1.y; f.v[6] = x1.z; f.v[7] = x1.w;
+    } else {
+      f.hi = *reinterpret_cast<const bf16x8 *>(src);
+    }
+    return f;
+  };
+  struct UG {
+    float4 u[MV], g[MV];
+    float glast;
+  };
+  auto fetch_ug = [&](size_t cb, UG &x) {
+#pragma unroll
+    for (int m = 0; m < MV; ++m) {
+      x.u[m] = has_u ? *reinterpret_cast<const float4 *>(a.U + ((cb * MV + m) * (D / 16) + us) * 256 + lane * 4)
+                     : float4{0.f, 0.f, 0.f, 0.f};
+      x.g[m] = *reinterpret_cast<const float4 *>(a.G + cb * C + 16 * m + 4 * g);
+    }
+    x.glast = a.G[cb * C + C - 1 + vgpr_zero()];
+  };
+
+  AF ring[RING];
+#pragma unroll
+  for (int p = 0; p < RING; ++p) ring[p] = load(cb0, p);
+  UG ug[2];
+  fetch_ug(cb0, ug[0]);
+
+  auto step = [&](UG &cur, UG &nxt, int cc) {
+    const size_t cb = cb0 + cc;
+    // the next chunk's operands (the current chunk again on the last step,
+    // so that every load is unconditional; those values are not used)
+    const size_t cbn = cc + 1 < a.cpj ? cb + 1 : cb;
+    fetch_ug(cbn, nxt);
+    const float gl2 = cur.glast * LOG2E;
+    float dcy[MV][4];
+#pragma unroll
+    for (int m = 0; m < MV; ++m) {
+      dcy[m][0] = exp2_fast(gl2 - cur.g[m].x * LOG2E);
+      dcy[m][1] = exp2_fast(gl2 - cur.g[m].y * LOG2E);
+      dcy[m][2] = exp2_fast(gl2 - cur.g[m].z * LOG2E);
+      dcy[m][3] = exp2_fast(gl2 - cur.g[m].w * LOG2E);
+    }
+    if (KIND == WALK && a.Hs) {
+#pragma unroll
+      for (int m = 0; m < MH; ++m)
+        *reinterpret_cast<float4 *>(a.Hs + ((cb * (D / 16) + slice) * MH + m) * 256 + lane * 4) =
+            float4{h[m][0], h[m][1], h[m][2], h[m][3]};
+    }
+    // V' = U - W h
+    Frag<PKw::b> hb[KBW];
+#pragma unroll
+    for (int kb = 0; kb < KBW; ++kb) {
+      const float x[8] = {h[2 * kb][0], h[2 * kb][1], h[2 * kb][2], h[2 * kb][3],
+                          h[2 * kb + 1][0], h[2 * kb + 1][1], h[2 * kb + 1][2], h[2 * kb + 1][3]};
+      hb[kb] = make_frag<PKw::b>(x);
+    }
+    f32x4 acc[MV];
+#pragma unroll
+    for (int m = 0; m < MV; ++m) acc[m] = zero4();
+#pragma unroll
+    for (int p = 0; p < FW; ++p) {
+      mma(acc[p / KBW], ring[p % RING], hb[p % KBW]);
+      ring[p % RING] = p + RING < F ? load(cb, p + RING) : load(cbn, p + RING - F);
+    }
+    Frag<PKk::b> vb[KBK];
+    {
+      float s[MV][4];
+#pragma unroll
+      for (int m = 0; m < MV; ++m) {
+        const float4 uu = cur.u[m];
+        const float4 vp = {uu.x - acc[m][0], uu.y - acc[m][1], uu.z - acc[m][2], uu.w - acc[m][3]};
+        if (KIND == WALK && a.Vn)
+          *reinterpret_cast<float4 *>(a.Vn + ((cb * (D / 16) + slice) * MV + m) * 256 + lane * 4) = vp;
+        s[m][0] = vp.x * dcy[m][0];
+        s[m][1] = vp.y * dcy[m][1];
+        s[m][2] = vp.z * dcy[m][2];
+        s[m][3] = vp.w * dcy[m][3];
+      }
+#pragma unroll
+      for (int kb = 0; kb < KBK; ++kb) {
+        const float x[8] = {s[2 * kb][0], s[2 * kb][1], s[2 * kb][2], s[2 * kb][3],
+                            s[2 * kb + 1][0], s[2 * kb + 1][1], s[2 * kb + 1][2], s[2 * kb + 1][3]};
+        vb[kb] = make_frag<PKk::b>(x);
+      }
+    }
+    // h <- e^{G_last} h + K^T (d o V')
+    const float gl = exp2_fast(gl2);
+#pragma unroll
+    for (int m = 0; m < MH; ++m) {
+      f32x4 acc2 = zero4();
+#pragma unroll
+      for (int kb = 0; kb < KBK; ++kb) {
+        const int p = FW + m * KBK + kb;
+        mma(acc2, ring[p % RING], vb[kb]);
+        ring[p % RING] = p + RING < F ? load(cb, p + RING) : load(cbn, p + RING - F);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) h[m][i] = gl * h[m][i] + acc2[i];
+    }
+  };
+  // two chunks per trip so the U/G sets alternate without copies
+  for (int cc = 0; cc < a.cpj; cc += 2) {
+    step(ug[0], ug[1], cc);
+    if (cc + 1 < a.cpj) step(ug[1], ug[0], cc + 1);
+  }
+
+  // final state slice
+  float *dst = nullptr;
+  int dcol = c0;
+  if (KIND == FOLD) {
+    if (c0 < D) dst = a.pairA + (bh * a.jobs + job) * D * D;
+    else { dst = a.pairB + (bh * a.jobs + job) * D * D; dcol = c0 - D; }
+  } else if (a.fin) {
+    dst = a.fin + bh * D * D;
+  }
+  if (dst) {
+#pragma unroll
+    for (int m = 0; m < MH; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[(size_t)(16 * m + 4 * g + i) * D + dcol + lr] = h[m][i];
   }
 }
 
@@ -929,12 +1155,12 @@ __global__ __launch_bounds__(NT, 2) void out_kernel(FwdArgs a) {
     for (int i = 0; i < NV; ++i) vv4[i] = *reinterpret_cast<const float4 *>(Vg + (size_t)(tid + i * NT) * 4);
 #pragma unroll
     for (int i = 0; i < NH; ++i) {
-      const int f = tid + i * NT, l = f & 63, t = f >> 6, m = t / CT, ni = t % CT;
+      const int f = tid + i * NT, l = f & 63, t = f >> 6, ni = t / (D / 16), m = t % (D / 16);
       *reinterpret_cast<float4 *>(sH + (16 * ni + (l & 15)) * LDH + 16 * m + 4 * (l >> 4)) = hv4[i];
     }
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const int f = tid + i * NT, l = f & 63, t = f >> 6, m = t / CT, ni = t % CT;
+      const int f = tid + i * NT, l = f & 63, t = f >> 6, ni = t / (C / 16), m = t % (C / 16);
       *reinterpret_cast<float4 *>(sV + (16 * ni + (l & 15)) * LDV + 16 * m + 4 * (l >> 4)) = vv4[i];
     }
   }
