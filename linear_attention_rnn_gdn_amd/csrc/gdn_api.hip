@@ -65,12 +65,22 @@ FwdArgs base_args(const gdn_shape &s) {
   FwdArgs a{};
   a.B = s.B; a.T = s.T; a.Hqk = s.H_qk; a.Hv = s.H_v; a.N = s.T / s.chunk;
   a.jobs = 1; a.cpj = a.N;
+  a.n0 = 0; a.nn = a.N;
   return a;
+}
+
+// compute units of the current device (256 on MI355X)
+int num_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n < 8)
+    return 256;
+  return n;
 }
 
 template <int C, typename TI, int MODE, bool FWD = true>
 gdn_status launch_prep(const FwdArgs &a, hipStream_t st) {
-  hipLaunchKernelGGL((prep_kernel<C, TI, MODE, FWD>), dim3(a.N, a.Hv, a.B), dim3(NT), 0, st, a);
+  hipLaunchKernelGGL((prep_kernel<C, TI, MODE, FWD>), dim3(a.nn, a.Hv, a.B), dim3(NT), 0, st, a);
   return check_launch();
 }
 
@@ -95,8 +105,8 @@ gdn_status launch_walk(const FwdArgs &a, hipStream_t st) {
 
 template <int C, typename TI, int MODE, typename TO>
 gdn_status launch_out(const FwdArgs &a, hipStream_t st) {
-  const long blocks = (long)(D / kSlice) * a.N * a.B * a.Hv;
-  hipLaunchKernelGGL((out_kernel<C, TI, MODE, kSlice, TO>), dim3((unsigned)blocks), dim3(NT), 0, st, a);
+  const long items = (long)(D / kSlice) * a.nn * a.B * a.Hv;
+  hipLaunchKernelGGL((out_kernel<C, TI, MODE, kSlice, TO>), dim3((unsigned)items), dim3(NT), 0, st, a);
   return check_launch();
 }
 
@@ -123,8 +133,8 @@ gdn_status run_fwd(const gdn_shape &s, int stages, const void *q, const void *k,
   a.U = reinterpret_cast<float *>(ws + L.U);
   a.Hs = reinterpret_cast<float *>(ws + L.Hs);
   a.Vn = reinterpret_cast<float *>(ws + L.Vn);
-  if (stages & GDN_STAGE_PREP) GDN_TRY((launch_prep<C, TI, MODE>(a, st)));
   const int J = groups_of(s);
+  if (stages & GDN_STAGE_PREP) GDN_TRY((launch_prep<C, TI, MODE>(a, st)));
   if (J == 1) {
     a.init = h0; a.init_per_job = 0; a.fin = h_T;
     if (stages & GDN_STAGE_WALK) GDN_TRY((launch_walk<C, TI, MODE, WALK>(a, st)));

@@ -77,6 +77,8 @@ template <int MODE> struct Prec {
   static constexpr int kv = MODE == MODE_F32 ? P_F32 : P_SPLIT_B;       // K^T (data) x V'
   static constexpr int hq = MODE == MODE_F32 ? P_F32 : P_SPLIT_A;       // h^T x Q^T (data)
   static constexpr int pv = MODE == MODE_F32 ? P_F32 : P_SPLIT_AB;      // V'^T x P^T
+  // h and V' are handed to the output stage as hi/lo bf16 planes
+  static constexpr bool split_store = MODE == MODE_BF16;
 };
 
 // 1-D workgroup index -> (unit, part) with the `parts` workgroups of a unit on
@@ -89,6 +91,35 @@ __device__ __forceinline__ void xcd_unit(int L, int parts, int units, int &unit,
   } else {
     unit = L / parts;
     part = L % parts;
+  }
+}
+
+// Store a wave's column of result tiles (rows 16m + 4g + i, column lr) for the
+// output stage, at `dst` (this chunk's and slice's part of the tensor).  Split
+// form (bf16 products): per pair of tiles (2p, 2p+1) the operand fragment the
+// output stage reads -- 8 values per lane in the order {tile 2p rows 4g..4g+3,
+// tile 2p+1 rows 4g..4g+3} -- as a bf16 high plane and a bf16 low plane (the
+// rounding remainder), 1 KB each.  fp32 form: one 1 KB block per tile.
+template <bool SPLIT, int NTILE>
+__device__ __forceinline__ void store_result_tiles(float *dst, const f32x4 (&t)[NTILE], int lane) {
+  if constexpr (SPLIT) {
+    char *d = reinterpret_cast<char *>(dst);
+#pragma unroll
+    for (int p = 0; p < NTILE / 2; ++p) {
+      bf16x8 hi, lo;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float x = t[2 * p + j / 4][j % 4];
+        hi[j] = (__bf16)x;
+        lo[j] = (__bf16)(x - (float)hi[j]);
+      }
+      *reinterpret_cast<bf16x8 *>(d + (2 * p) * 1024 + lane * 16) = hi;
+      *reinterpret_cast<bf16x8 *>(d + (2 * p + 1) * 1024 + lane * 16) = lo;
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < NTILE; ++m)
+      *reinterpret_cast<float4 *>(dst + (m * 64 + lane) * 4) = float4{t[m][0], t[m][1], t[m][2], t[m][3]};
   }
 }
 
@@ -108,6 +139,7 @@ struct FwdArgs {
   float *fin;                     // walk: final state per bh (h_T) when jobs == 1, or null
   float *pairA, *pairB;           // fold outputs [BH,J,D,D]
   int jobs, cpj;                  // walk/fold: jobs per bh, chunks per job
+  int n0, nn;                     // chunk range [n0, n0 + nn) of this launch (prep, out, single walk)
   void *o;                        // out output
 };
 
@@ -299,7 +331,7 @@ __global__ __launch_bounds__(NT, 2) void prep_kernel(FwdArgs a) {
   TI *sX = reinterpret_cast<TI *>(sXraw);
   float *sM = reinterpret_cast<float *>(sXraw);
 
-  const int n = blockIdx.x, hv = blockIdx.y, b = blockIdx.z;
+  const int n = a.n0 + blockIdx.x, hv = blockIdx.y, b = blockIdx.z;
   const int hq = hv / (a.Hv / a.Hqk);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, g = lane >> 4, lk = g * 8, lq = g * 4;
@@ -646,7 +678,7 @@ __global__ __launch_bounds__(64 * WPG) void walk_shared_kernel(FwdArgs a) {
   const int c0 = slice * 16;   // first column (of the augmented [A|B] in FOLD)
   const bool has_u = KIND == WALK || c0 >= D;
   const int us = KIND == WALK ? slice : slice - D / 16;   // U column tile
-  const size_t cb0 = bh * a.N + (size_t)job * a.cpj;
+  const size_t cb0 = bh * a.N + a.n0 + (size_t)job * a.cpj;
 
   // state tiles: h[m] holds rows 16m + 4g + i, column c0 + lr
   f32x4 h[MH];
@@ -767,26 +799,19 @@ __global__ __launch_bounds__(64 * WPG) void walk_shared_kernel(FwdArgs a) {
     }
     // chunk-start state for the output stage (stores issued after the loads
     // this chunk still waits for)
-    if (KIND == WALK && a.Hs) {
-#pragma unroll
-      for (int m = 0; m < MH; ++m)
-        *reinterpret_cast<float4 *>(a.Hs + ((cb * (D / 16) + slice) * MH + m) * 256 + lane * 4) =
-            float4{h[m][0], h[m][1], h[m][2], h[m][3]};
-    }
+    if (KIND == WALK && a.Hs) store_result_tiles<PR::split_store>(a.Hs + (cb * (D / 16) + slice) * MH * 256, h, lane);
     Frag<PKk::b> vb[KBK];
     {
       float s[MV][4];
+      f32x4 vps[MV];
 #pragma unroll
       for (int m = 0; m < MV; ++m) {
         const float4 uu = cu.u[m];
-        const float4 vp = {uu.x - acc[m][0], uu.y - acc[m][1], uu.z - acc[m][2], uu.w - acc[m][3]};
-        if (KIND == WALK && a.Vn)
-          *reinterpret_cast<float4 *>(a.Vn + ((cb * (D / 16) + slice) * MV + m) * 256 + lane * 4) = vp;
-        s[m][0] = vp.x * dcy[m][0];
-        s[m][1] = vp.y * dcy[m][1];
-        s[m][2] = vp.z * dcy[m][2];
-        s[m][3] = vp.w * dcy[m][3];
+        vps[m] = f32x4{uu.x - acc[m][0], uu.y - acc[m][1], uu.z - acc[m][2], uu.w - acc[m][3]};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[m][i] = vps[m][i] * dcy[m][i];
       }
+      if (KIND == WALK && a.Vn) store_result_tiles<PR::split_store>(a.Vn + (cb * (D / 16) + slice) * MV * 256, vps, lane);
 #pragma unroll
       for (int kb = 0; kb < KBK; ++kb) {
         const float x[8] = {s[2 * kb][0], s[2 * kb][1], s[2 * kb][2], s[2 * kb][3],
@@ -867,7 +892,7 @@ __global__ __launch_bounds__(64) void walk_ring_kernel(FwdArgs a) {
   const int c0 = slice * 16;   // first column (of the augmented [A|B] in FOLD)
   const bool has_u = KIND == WALK || c0 >= D;
   const int us = KIND == WALK ? slice : slice - D / 16;   // U column tile
-  const size_t cb0 = bh * a.N + (size_t)job * a.cpj;
+  const size_t cb0 = bh * a.N + a.n0 + (size_t)job * a.cpj;
 
   // state tiles: h[m] holds rows 16m + 4g + i, column c0 + lr
   f32x4 h[MH];
@@ -938,12 +963,7 @@ __global__ __launch_bounds__(64) void walk_ring_kernel(FwdArgs a) {
       dcy[m][2] = exp2_fast(gl2 - cur.g[m].z * LOG2E);
       dcy[m][3] = exp2_fast(gl2 - cur.g[m].w * LOG2E);
     }
-    if (KIND == WALK && a.Hs) {
-#pragma unroll
-      for (int m = 0; m < MH; ++m)
-        *reinterpret_cast<float4 *>(a.Hs + ((cb * (D / 16) + slice) * MH + m) * 256 + lane * 4) =
-            float4{h[m][0], h[m][1], h[m][2], h[m][3]};
-    }
+    if (KIND == WALK && a.Hs) store_result_tiles<PR::split_store>(a.Hs + (cb * (D / 16) + slice) * MH * 256, h, lane);
     // V' = U - W h
     Frag<PKw::b> hb[KBW];
 #pragma unroll
@@ -963,17 +983,15 @@ __global__ __launch_bounds__(64) void walk_ring_kernel(FwdArgs a) {
     Frag<PKk::b> vb[KBK];
     {
       float s[MV][4];
+      f32x4 vps[MV];
 #pragma unroll
       for (int m = 0; m < MV; ++m) {
         const float4 uu = cur.u[m];
-        const float4 vp = {uu.x - acc[m][0], uu.y - acc[m][1], uu.z - acc[m][2], uu.w - acc[m][3]};
-        if (KIND == WALK && a.Vn)
-          *reinterpret_cast<float4 *>(a.Vn + ((cb * (D / 16) + slice) * MV + m) * 256 + lane * 4) = vp;
-        s[m][0] = vp.x * dcy[m][0];
-        s[m][1] = vp.y * dcy[m][1];
-        s[m][2] = vp.z * dcy[m][2];
-        s[m][3] = vp.w * dcy[m][3];
+        vps[m] = f32x4{uu.x - acc[m][0], uu.y - acc[m][1], uu.z - acc[m][2], uu.w - acc[m][3]};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[m][i] = vps[m][i] * dcy[m][i];
       }
+      if (KIND == WALK && a.Vn) store_result_tiles<PR::split_store>(a.Vn + (cb * (D / 16) + slice) * MV * 256, vps, lane);
 #pragma unroll
       for (int kb = 0; kb < KBK; ++kb) {
         const float x[8] = {s[2 * kb][0], s[2 * kb][1], s[2 * kb][2], s[2 * kb][3],
@@ -1100,153 +1118,285 @@ __global__ __launch_bounds__(NT) void prefix_kernel(PrefixArgs a) {
 }
 
 // ----------------------------------------------------------------------------
-// output for one column slice of one chunk, computed transposed:
+// output for one 32-column slice of one chunk, computed transposed:
 //   O^T = h^T (diag(e^G) Q)^T + V'^T P^T,   P^T = (K Q^T) o Gamma^T o [i <= r].
+// Persistent: each workgroup (4 waves) walks a strided list of (slice,
+// chunk, head) items.  The next item's K tile, chunk-start state slice,
+// corrected-value slice and G are copied straight into the other of two LDS
+// buffers (global_load_lds) and its queries into registers while the current
+// item is computed; one barrier per item.
+// All contractions use the k order of two stacked result tiles (lane group g
+// holds k = 4g..4g+3 and 16+4g..16+4g+3 of each block of 32), the order in
+// which the walk stored h and V': their fragments are read as stored.
 // Each wave owns query-row tiles (w and R-1-w, balancing the triangle).  P^T
-// tiles stay in the matrix-core result registers and feed V'^T P^T directly
-// as B operands: a result tile holds rows 4g..4g+3 of 16 for lane group g, so
-// two stacked tiles give lane group g the k-values {4g..4g+3, 16+4g..16+4g+3},
-// and the A operand is fetched with the same k order.
+// tiles stay in result registers and feed V'^T P^T directly as B operands.
+template <int C, typename TI> struct OutBuf {
+  static constexpr int RP = D * (int)sizeof(TI) / 16;   // 16-byte pieces per K row
+  static constexpr int KB = C * RP * 16;                // K tile bytes (swizzled rows)
+  static constexpr int HB = D * 32 * 4;                 // state slice: 2 walk slices x D/16 tiles
+  static constexpr int VB = C * 32 * 4;                 // V' slice
+  static constexpr int HOFF = KB, VOFF = KB + HB, GOFF = KB + HB + VB;
+  static constexpr int BYTES = GOFF + 4 * C;
+  static constexpr int NBLK = (KB + HB + VB) / 1024;    // 1 KB copies (G aside)
+  // K[r][piece c] lives at piece position c ^ (r mod 16) of row r, so the 16
+  // rows of an operand read hit 16 different bank groups
+  __device__ static int kpos(int r, int c) { return r * RP + (c ^ (r & 15)); }
+};
+
 template <int C, typename TI, int MODE, int S, typename TO>
 __global__ __launch_bounds__(NT, 2) void out_kernel(FwdArgs a) {
+  static_assert(S == 32, "two 16-column walk slices per item");
   using PR = Prec<MODE>;
   using PKq = PolicyKinds<PR::exact>;   // K x Q^T
   using PKh = PolicyKinds<PR::hq>;      // h^T x Q^T
   using PKv = PolicyKinds<PR::pv>;      // V'^T x P^T
   static_assert(PKq::b == PKh::b, "one query fragment serves both products");
-  constexpr int VE = 16 / sizeof(TI);
-  constexpr int LDK = D + LdPad<TI>::v;   // K tile [C][LDK]
-  constexpr int LDH = D + 4;              // h^T slice [S][LDH]
-  constexpr int LDV = C + 4;              // V'^T slice [S][LDV]
+  using OB = OutBuf<C, TI>;
+  constexpr bool F32 = sizeof(TI) == 4;
   constexpr int R = C / 16;               // query-row tiles
   constexpr int RU = R / 4;               // row tiles per wave
   constexpr int NS = D / S;
-  constexpr int CT = S / 16;              // column tiles of the slice
-  static_assert(R % 4 == 0, "row tiles must split over 4 waves");
-  __shared__ __align__(16) TI sK[C * LDK];
-  __shared__ __align__(16) float sH[S * LDH];
-  __shared__ __align__(16) float sV[S * LDV];
-  __shared__ float sG[C];
+  constexpr int MH = D / 16, MV = C / 16;
+  static_assert(R % 4 == 0 && OB::NBLK % 4 == 0, "work split");
+  __shared__ __align__(16) char buf[OB::BYTES];
 
-  int unit, slice;
-  xcd_unit(blockIdx.x, NS, a.N * a.B * a.Hv, unit, slice);
-  const size_t bh = (size_t)(unit / a.N);
-  const int n = unit % a.N;
-  const int b = (int)(bh / a.Hv), hv = (int)(bh % a.Hv);
-  const int hq = hv / (a.Hv / a.Hqk);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lr = lane & 15, lk = (lane >> 4) * 8, lq = (lane >> 4) * 4;
-  const size_t cb = bh * a.N + n;
-  const size_t t0 = (size_t)n * C;
-  const int c0 = slice * S;
+  const int lr = lane & 15, g = lane >> 4, lq = g * 4;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int rp = wv;   // row tiles rp and R-1-rp
+  const int units = a.nn * a.B * a.Hv, items = units * NS;
 
-  const size_t koff = (((size_t)b * a.T + t0) * a.Hqk + hq) * D;
-  load_rows<TI, C>(sK, LDK, reinterpret_cast<const TI *>(a.k) + koff, (size_t)a.Hqk * D);
-  // chunk-start state and V' of this slice (fragment-major, contiguous),
-  // scattered into transposed LDS tiles sH[c][d], sV[c][r]
-  {
-    constexpr int NH = (D / 16) * CT * 64 / NT, NV = (C / 16) * CT * 64 / NT;
-    const float *Hg = a.Hs + (cb * NS + slice) * (size_t)(D * S);
-    const float *Vg = a.Vn + (cb * NS + slice) * (size_t)(C * S);
-    float4 hv4[NH], vv4[NV];
+  struct Item {
+    size_t bh, cb;
+    int b, hv, hq, n, slice;
+  };
+  auto item_of = [&](int it) {
+    Item x;
+    int unit;
+    xcd_unit(it, NS, units, unit, x.slice);
+    x.bh = (size_t)(unit / a.nn);
+    x.n = a.n0 + unit % a.nn;
+    x.b = (int)(x.bh / a.Hv);
+    x.hv = (int)(x.bh % a.Hv);
+    x.hq = x.hv / (a.Hv / a.Hqk);
+    x.cb = x.bh * a.N + x.n;
+    return x;
+  };
+  // copy one item's operands into an LDS buffer; wave w takes every 4th block
+  auto stage = [&](char *buf, const Item &x) {
+    const char *kg = reinterpret_cast<const char *>(a.k) +
+                     ((((size_t)x.b * a.T + (size_t)x.n * C) * a.Hqk + x.hq) * D) * sizeof(TI);
+    const size_t krow = (size_t)a.Hqk * D * sizeof(TI);   // bytes between tokens
+    const char *hg = reinterpret_cast<const char *>(a.Hs + (x.cb * NS + x.slice) * (size_t)(D * S));
+    const char *vg = reinterpret_cast<const char *>(a.Vn + (x.cb * NS + x.slice) * (size_t)(C * S));
+    using LDSP = __attribute__((address_space(3))) void *;
+    // K: block j holds pieces p = 64 j + lane of the swizzled tile
 #pragma unroll
-    for (int i = 0; i < NH; ++i) hv4[i] = *reinterpret_cast<const float4 *>(Hg + (size_t)(tid + i * NT) * 4);
-#pragma unroll
-    for (int i = 0; i < NV; ++i) vv4[i] = *reinterpret_cast<const float4 *>(Vg + (size_t)(tid + i * NT) * 4);
-#pragma unroll
-    for (int i = 0; i < NH; ++i) {
-      const int f = tid + i * NT, l = f & 63, t = f >> 6, ni = t / (D / 16), m = t % (D / 16);
-      *reinterpret_cast<float4 *>(sH + (16 * ni + (l & 15)) * LDH + 16 * m + 4 * (l >> 4)) = hv4[i];
+    for (int jj = 0; jj < OB::KB / 4096; ++jj) {
+      const int j = jj * 4 + wv;
+      const int p = j * 64 + lane, r = p / OB::RP, c = (p % OB::RP) ^ (r & 15);
+      __builtin_amdgcn_global_load_lds((const void *)(kg + r * krow + c * 16), (LDSP)(buf + j * 1024), 16, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int f = tid + i * NT, l = f & 63, t = f >> 6, ni = t / (C / 16), m = t % (C / 16);
-      *reinterpret_cast<float4 *>(sV + (16 * ni + (l & 15)) * LDV + 16 * m + 4 * (l >> 4)) = vv4[i];
+    for (int jj = 0; jj < OB::HB / 4096; ++jj) {
+      const int j = jj * 4 + wv;
+      __builtin_amdgcn_global_load_lds((const void *)(hg + j * 1024 + lane * 16), (LDSP)(buf + OB::HOFF + j * 1024),
+                                       16, 0, 0);
     }
-  }
-  if (tid < C) sG[tid] = a.G[cb * C + tid] * LOG2E;   // log2-scaled
-  lds_barrier();
-
-  TO *og = reinterpret_cast<TO *>(a.o);
-#pragma unroll 1
-  for (int u = 0; u < RU; ++u) {
-    const int rt = u == 0 ? wave : R - 1 - wave;
-    const int r = 16 * rt + lr;   // this lane's query row (result column)
-    // query fragments of this row tile (B operand: n = row, k = feature)
-    Frag<PKq::b> qf[D / 32];
-    {
-      const TI *qrow = reinterpret_cast<const TI *>(a.q) + (((size_t)b * a.T + t0 + r) * a.Hqk + hq) * D;
+#pragma unroll
+    for (int jj = 0; jj < OB::VB / 4096; ++jj) {
+      const int j = jj * 4 + wv;
+      __builtin_amdgcn_global_load_lds((const void *)(vg + j * 1024 + lane * 16), (LDSP)(buf + OB::VOFF + j * 1024),
+                                       16, 0, 0);
+    }
+    if (wv == 3 && lane < C / 4)
+      __builtin_amdgcn_global_load_lds((const void *)(a.G + x.cb * C + lane * 4),
+                                       (__attribute__((address_space(3))) void *)(buf + OB::GOFF), 16, 0, 0);
+    asm volatile("" ::: "memory");
+  };
+  // query fragments of this wave's row tiles, k order kk(g, j)
+  struct Qf {
+    Frag<PKq::b> f[RU][D / 32];
+  };
+  auto load_q = [&](const Item &x, Qf &q) {
+#pragma unroll
+    for (int u = 0; u < RU; ++u) {
+      const int rt = u == 0 ? rp : R - 1 - rp;
+      const TI *qrow = reinterpret_cast<const TI *>(a.q) +
+                       (((size_t)x.b * a.T + (size_t)x.n * C + 16 * rt + lr) * a.Hqk + x.hq) * D;
 #pragma unroll
       for (int kb = 0; kb < D / 32; ++kb) {
-        TI tmp[8];
-#pragma unroll
-        for (int v = 0; v < 8 / VE; ++v)
-          *reinterpret_cast<uint4 *>(tmp + v * VE) = *reinterpret_cast<const uint4 *>(qrow + 32 * kb + lk + v * VE);
-        float x[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = to_f32(tmp[j]);
-        qf[kb] = make_frag<PKq::b>(x);
-      }
-    }
-    const float Gr = sG[r];
-    f32x4 acc1[CT], acc2[CT];
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) acc1[ct] = acc2[ct] = zero4();
-    // h^T Q^T for every column tile of the slice
-#pragma unroll
-    for (int kb = 0; kb < D / 32; ++kb) {
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
-        mma(acc1[ct], lds_frag<PKh::a>(sH + (16 * ct + lr) * LDH + 32 * kb + lk), qf[kb]);
-    }
-    // key blocks of 32: P^T tiles (2kp, 2kp+1) are formed and consumed at
-    // once.  A result tile gives lane group g keys {4g..4g+3} (first tile)
-    // and {16+4g..16+4g+3} (second tile) of the block; the V'^T fragment is
-    // read with the same key order.
-#pragma unroll
-    for (int kp = 0; kp < R / 2; ++kp) {
-      if (2 * kp <= rt) {
-        f32x4 p0 = zero4(), p1 = zero4();
-        const bool two = 2 * kp + 1 <= rt;
-#pragma unroll
-        for (int kb = 0; kb < D / 32; ++kb) {
-          mma(p0, lds_frag<PKq::a>(sK + (32 * kp + lr) * LDK + 32 * kb + lk), qf[kb]);
-          if (two) mma(p1, lds_frag<PKq::a>(sK + (32 * kp + 16 + lr) * LDK + 32 * kb + lk), qf[kb]);
+        TI t[8];
+        if constexpr (F32) {
+          *reinterpret_cast<float4 *>(t) = *reinterpret_cast<const float4 *>(qrow + 32 * kb + 4 * g);
+          *reinterpret_cast<float4 *>(t + 4) = *reinterpret_cast<const float4 *>(qrow + 32 * kb + 16 + 4 * g);
+        } else {
+          *reinterpret_cast<uint2 *>(t) = *reinterpret_cast<const uint2 *>(qrow + 32 * kb + 4 * g);
+          *reinterpret_cast<uint2 *>(t + 4) = *reinterpret_cast<const uint2 *>(qrow + 32 * kb + 16 + 4 * g);
         }
-        float b8[8];
+        if constexpr (PKq::b == F_BF16) {
+          q.f[u][kb].hi = *reinterpret_cast<const bf16x8 *>(t);
+        } else {
+          float x8[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int k0 = 32 * kp + lq + i, k1 = k0 + 16;
-          b8[i] = k0 <= r ? p0[i] * exp2_fast(Gr - sG[k0]) : 0.f;
-          b8[4 + i] = (two && k1 <= r) ? p1[i] * exp2_fast(Gr - sG[k1]) : 0.f;
-        }
-        const auto bf = make_frag<PKv::b>(b8);
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-          float a8[8];
-          const float *vrow = sV + (16 * ct + lr) * LDV + 32 * kp + lq;
-          const float4 v0 = *reinterpret_cast<const float4 *>(vrow);
-          const float4 v1 = *reinterpret_cast<const float4 *>(vrow + 16);
-          a8[0] = v0.x; a8[1] = v0.y; a8[2] = v0.z; a8[3] = v0.w;
-          a8[4] = v1.x; a8[5] = v1.y; a8[6] = v1.z; a8[7] = v1.w;
-          mma(acc2[ct], make_frag<PKv::a>(a8), bf);
+          for (int j = 0; j < 8; ++j) x8[j] = to_f32(t[j]);
+          q.f[u][kb] = make_frag<PKq::b>(x8);
         }
       }
     }
-    const float er = exp2_fast(Gr);
+  };
+  auto chunk_barrier = [&]() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    __builtin_amdgcn_s_barrier();
+  };
+
+  auto compute = [&](const char *buf, const Item &x, const Qf &q) {
+    const float *Gs = reinterpret_cast<const float *>(buf + OB::GOFF);
+    const float *Hs = reinterpret_cast<const float *>(buf + OB::HOFF);
+    const float *Vs = reinterpret_cast<const float *>(buf + OB::VOFF);
+    TO *og = reinterpret_cast<TO *>(a.o);
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      // lane holds O^T[c = 16ct + 4g + i][r]
-      TO *dst = og + (((size_t)b * a.T + t0 + r) * a.Hv + hv) * D + c0 + 16 * ct + lq;
-      if constexpr (sizeof(TO) == 4) {
-        *reinterpret_cast<float4 *>(dst) = float4{er * acc1[ct][0] + acc2[ct][0], er * acc1[ct][1] + acc2[ct][1],
-                                                  er * acc1[ct][2] + acc2[ct][2], er * acc1[ct][3] + acc2[ct][3]};
-      } else {
+    for (int u = 0; u < RU; ++u) {
+      const int rt = u == 0 ? rp : R - 1 - rp;
+      const int r = 16 * rt + lr;   // this lane's query row (result column)
+      const float Gr = Gs[r] * LOG2E;
+      f32x4 acc1[2], acc2[2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dst[i] = from_f32<TO>(er * acc1[ct][i] + acc2[ct][i]);
+      for (int ct = 0; ct < 2; ++ct) acc1[ct] = acc2[ct] = zero4();
+      // h^T Q^T: A = h^T rows c, k = state rows 32kb + kk(g, j): tiles 2kb, 2kb+1
+      // (all fragments read before the first product: one LDS wait)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        if constexpr (PR::split_store) {
+          // stored as hi/lo planes: the operand fragments as they are
+          static_assert(PKh::a == F_SPLIT, "split planes feed a split operand");
+          Frag<F_SPLIT> hf[D / 32];
+          const char *hb = reinterpret_cast<const char *>(Hs) + ct * MH * 1024 + lane * 16;
+#pragma unroll
+          for (int kb = 0; kb < D / 32; ++kb) {
+            hf[kb].hi = *reinterpret_cast<const bf16x8 *>(hb + (2 * kb) * 1024);
+            hf[kb].lo = *reinterpret_cast<const bf16x8 *>(hb + (2 * kb + 1) * 1024);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int kb = 0; kb < D / 32; ++kb) mma(acc1[ct], hf[kb], q.f[u][kb]);
+        } else {
+          float4 hv[D / 16];
+#pragma unroll
+          for (int m = 0; m < D / 16; ++m) hv[m] = *reinterpret_cast<const float4 *>(Hs + ((ct * MH + m) * 64 + lane) * 4);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int kb = 0; kb < D / 32; ++kb) {
+            const float4 h0 = hv[2 * kb], h1 = hv[2 * kb + 1];
+            const float x8[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+            mma(acc1[ct], make_frag<PKh::a>(x8), q.f[u][kb]);
+          }
+        }
+      }
+      // key blocks of 32: P^T tiles (2kp, 2kp+1) formed and consumed at once.
+      // Each block's LDS operands (K fragments, V' fragments, G) are read
+      // together ahead of its products: one LDS wait per block.
+#pragma unroll
+      for (int kp = 0; kp < R / 2; ++kp) {
+        if (2 * kp <= rt) {
+          const bool two = 2 * kp + 1 <= rt;
+          Frag<PKq::a> kf[2][D / 32];
+#pragma unroll
+          for (int kb = 0; kb < D / 32; ++kb) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              const int kr = 32 * kp + 16 * t + lr;   // key row
+              if constexpr (!F32 && PKq::a == F_BF16) {
+                const TI *kt = reinterpret_cast<const TI *>(buf);
+                const int k = 32 * kb + 4 * g;
+                const uint2 w0 = *reinterpret_cast<const uint2 *>(kt + OB::kpos(kr, k / 8) * 8 + k % 8);
+                const uint2 w1 = *reinterpret_cast<const uint2 *>(kt + OB::kpos(kr, (k + 16) / 8) * 8 + k % 8);
+                kf[t][kb].hi = __builtin_bit_cast(bf16x8, uint4{w0.x, w0.y, w1.x, w1.y});
+              } else {
+                float x8[8];
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                  const int k = 32 * kb + 16 * hh + 4 * g;   // 4 consecutive features
+                  const int c = k * (int)sizeof(TI) / 16, off = (k * (int)sizeof(TI)) % 16 / (int)sizeof(TI);
+                  const TI *src = reinterpret_cast<const TI *>(buf) + OB::kpos(kr, c) * (16 / (int)sizeof(TI)) + off;
+                  if constexpr (F32) {
+                    const float4 v4 = *reinterpret_cast<const float4 *>(src);
+                    x8[4 * hh] = v4.x; x8[4 * hh + 1] = v4.y; x8[4 * hh + 2] = v4.z; x8[4 * hh + 3] = v4.w;
+                  } else {
+                    const uint2 v2 = *reinterpret_cast<const uint2 *>(src);
+                    const __bf16 *e = reinterpret_cast<const __bf16 *>(&v2);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) x8[4 * hh + j] = (float)e[j];
+                  }
+                }
+                kf[t][kb] = make_frag<PKq::a>(x8);
+              }
+            }
+          }
+          // V'^T fragments of the key block: (hi, lo) planes or two fp32 tiles
+          float4 v0[2], v1[2];
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) {
+            v0[ct] = *reinterpret_cast<const float4 *>(Vs + ((ct * MV + 2 * kp) * 64 + lane) * 4);
+            v1[ct] = *reinterpret_cast<const float4 *>(Vs + ((ct * MV + 2 * kp + 1) * 64 + lane) * 4);
+          }
+          const float4 gk0 = *reinterpret_cast<const float4 *>(Gs + 32 * kp + lq);
+          const float4 gk1 = *reinterpret_cast<const float4 *>(Gs + 32 * kp + 16 + lq);
+          __builtin_amdgcn_sched_barrier(0);
+          f32x4 p0 = zero4(), p1 = zero4();
+#pragma unroll
+          for (int kb = 0; kb < D / 32; ++kb) {
+            mma(p0, kf[0][kb], q.f[u][kb]);
+            if (two) mma(p1, kf[1][kb], q.f[u][kb]);
+          }
+          const float g0[4] = {gk0.x, gk0.y, gk0.z, gk0.w}, g1[4] = {gk1.x, gk1.y, gk1.z, gk1.w};
+          float b8[8];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int k0i = 32 * kp + lq + i, k1i = k0i + 16;
+            b8[i] = k0i <= r ? p0[i] * exp2_fast(Gr - g0[i] * LOG2E) : 0.f;
+            b8[4 + i] = (two && k1i <= r) ? p1[i] * exp2_fast(Gr - g1[i] * LOG2E) : 0.f;
+          }
+          const auto bf = make_frag<PKv::b>(b8);
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) {
+            if constexpr (PR::split_store) {
+              static_assert(PKv::a == F_SPLIT, "split planes feed a split operand");
+              Frag<F_SPLIT> vf;
+              vf.hi = __builtin_bit_cast(bf16x8, v0[ct]);
+              vf.lo = __builtin_bit_cast(bf16x8, v1[ct]);
+              mma(acc2[ct], vf, bf);
+            } else {
+              const float a8[8] = {v0[ct].x, v0[ct].y, v0[ct].z, v0[ct].w, v1[ct].x, v1[ct].y, v1[ct].z, v1[ct].w};
+              mma(acc2[ct], make_frag<PKv::a>(a8), bf);
+            }
+          }
+        }
+      }
+      const float er = exp2_fast(Gr);
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        // lane holds O^T[c = 16ct + 4g + i][r]
+        TO *dst = og + (((size_t)x.b * a.T + (size_t)x.n * C + r) * a.Hv + x.hv) * D + x.slice * S + 16 * ct + lq;
+        if constexpr (sizeof(TO) == 4) {
+          *reinterpret_cast<float4 *>(dst) = float4{er * acc1[ct][0] + acc2[ct][0], er * acc1[ct][1] + acc2[ct][1],
+                                                    er * acc1[ct][2] + acc2[ct][2], er * acc1[ct][3] + acc2[ct][3]};
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dst[i] = from_f32<TO>(er * acc1[ct][i] + acc2[ct][i]);
+        }
       }
     }
-  }
+  };
+
+  // one item per workgroup; two workgroups share a compute unit, so one
+  // copies while the other computes
+  const Item x = item_of(blockIdx.x);
+  Qf q;
+  stage(buf, x);
+  load_q(x, q);
+  chunk_barrier();
+  compute(buf, x, q);
 }
 
 }  // namespace gdn
