@@ -1250,6 +1250,17 @@ __global__ __launch_bounds__(NT, 2) void out_kernel(FwdArgs a) {
     __builtin_amdgcn_s_barrier();
   };
 
+  // this lane's byte offsets of its K fragment halves within a 16-row key
+  // tile: row lr, piece c = (32kb + 16hh + 4g) * size / 16 stored at c ^ lr
+  int koff[D / 32][2];
+#pragma unroll
+  for (int kb = 0; kb < D / 32; ++kb)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int k = 32 * kb + 16 * hh + 4 * g;
+      const int c = k * (int)sizeof(TI) / 16, off = (k * (int)sizeof(TI)) % 16;
+      koff[kb][hh] = lr * OB::RP * 16 + ((c ^ lr) * 16) + off;
+    }
   auto compute = [&](const char *buf, const Item &x, const Qf &q) {
     const float *Gs = reinterpret_cast<const float *>(buf + OB::GOFF);
     const float *Hs = reinterpret_cast<const float *>(buf + OB::HOFF);
@@ -1302,28 +1313,23 @@ __global__ __launch_bounds__(NT, 2) void out_kernel(FwdArgs a) {
           const bool two = 2 * kp + 1 <= rt;
           Frag<PKq::a> kf[2][D / 32];
 #pragma unroll
-          for (int kb = 0; kb < D / 32; ++kb) {
+          for (int t = 0; t < 2; ++t) {
+            const char *tile = buf + (32 * kp + 16 * t) * OB::RP * 16;   // key rows 32kp + 16t ..
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-              const int kr = 32 * kp + 16 * t + lr;   // key row
+            for (int kb = 0; kb < D / 32; ++kb) {
               if constexpr (!F32 && PKq::a == F_BF16) {
-                const TI *kt = reinterpret_cast<const TI *>(buf);
-                const int k = 32 * kb + 4 * g;
-                const uint2 w0 = *reinterpret_cast<const uint2 *>(kt + OB::kpos(kr, k / 8) * 8 + k % 8);
-                const uint2 w1 = *reinterpret_cast<const uint2 *>(kt + OB::kpos(kr, (k + 16) / 8) * 8 + k % 8);
+                const uint2 w0 = *reinterpret_cast<const uint2 *>(tile + koff[kb][0]);
+                const uint2 w1 = *reinterpret_cast<const uint2 *>(tile + koff[kb][1]);
                 kf[t][kb].hi = __builtin_bit_cast(bf16x8, uint4{w0.x, w0.y, w1.x, w1.y});
               } else {
                 float x8[8];
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
-                  const int k = 32 * kb + 16 * hh + 4 * g;   // 4 consecutive features
-                  const int c = k * (int)sizeof(TI) / 16, off = (k * (int)sizeof(TI)) % 16 / (int)sizeof(TI);
-                  const TI *src = reinterpret_cast<const TI *>(buf) + OB::kpos(kr, c) * (16 / (int)sizeof(TI)) + off;
                   if constexpr (F32) {
-                    const float4 v4 = *reinterpret_cast<const float4 *>(src);
+                    const float4 v4 = *reinterpret_cast<const float4 *>(tile + koff[kb][hh]);
                     x8[4 * hh] = v4.x; x8[4 * hh + 1] = v4.y; x8[4 * hh + 2] = v4.z; x8[4 * hh + 3] = v4.w;
                   } else {
-                    const uint2 v2 = *reinterpret_cast<const uint2 *>(src);
+                    const uint2 v2 = *reinterpret_cast<const uint2 *>(tile + koff[kb][hh]);
                     const __bf16 *e = reinterpret_cast<const __bf16 *>(&v2);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) x8[4 * hh + j] = (float)e[j];
@@ -1351,11 +1357,20 @@ __global__ __launch_bounds__(NT, 2) void out_kernel(FwdArgs a) {
           }
           const float g0[4] = {gk0.x, gk0.y, gk0.z, gk0.w}, g1[4] = {gk1.x, gk1.y, gk1.z, gk1.w};
           float b8[8];
+          if (2 * kp + 1 < rt) {
+            // both key tiles wholly before this query tile: no mask
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int k0i = 32 * kp + lq + i, k1i = k0i + 16;
-            b8[i] = k0i <= r ? p0[i] * exp2_fast(Gr - g0[i] * LOG2E) : 0.f;
-            b8[4 + i] = (two && k1i <= r) ? p1[i] * exp2_fast(Gr - g1[i] * LOG2E) : 0.f;
+            for (int i = 0; i < 4; ++i) {
+              b8[i] = p0[i] * exp2_fast(Gr - g0[i] * LOG2E);
+              b8[4 + i] = p1[i] * exp2_fast(Gr - g1[i] * LOG2E);
+            }
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int k0i = 32 * kp + lq + i, k1i = k0i + 16;
+              b8[i] = k0i <= r ? p0[i] * exp2_fast(Gr - g0[i] * LOG2E) : 0.f;
+              b8[4 + i] = (two && k1i <= r) ? p1[i] * exp2_fast(Gr - g1[i] * LOG2E) : 0.f;
+            }
           }
           const auto bf = make_frag<PKv::b>(b8);
 #pragma unroll
