@@ -119,13 +119,15 @@ def _stage_of(kernel_name):
         return "prefix"
     if "out_kernel" in n:
         return "out"
-    if "walk_kernel" in n:
-        # walk_kernel<C, TI, MODE, S, KIND>: KIND 1 = fold (demangled or mangled name)
-        if "walk_kernel<" in n:
-            kind = n.split("walk_kernel<", 1)[1].split(">", 1)[0].split(",")[-1].strip()
+    if "walk_ring_kernel" in n or "walk_shared_kernel" in n:
+        # walk_*_kernel<C, TI, MODE, KIND[, WPG]>: KIND 1 = fold (demangled or
+        # mangled name; TI is not an integer argument in the mangled form)
+        import re
+        tail = n.split("_kernel", 1)[1]
+        if tail.startswith("<"):
+            kind = tail[1:].split(">", 1)[0].split(",")[3].strip()
         else:
-            import re
-            kind = re.findall(r"Li(\d+)E", n.split("walk_kernel", 1)[1])[-1]
+            kind = re.findall(r"Li(\d+)E", tail)[2]
         return "fold" if kind == "1" else "walk"
     if "copy" in n.lower():
         return "copy"
@@ -210,11 +212,16 @@ def cpu_baseline(w, x, budget_s=15.0):
         T_s = w.T
     else:
         T_s = max(256, min(w.T, int(T_s * budget_s / max(dt, 1e-6)) // 256 * 256))
-    dt = run(T_s)
+    # repeat short samples until about 5 s of CPU work for a steady figure
+    reps, total = 0, 0.0
+    while reps == 0 or (total < 5.0 and reps < 50):
+        total += run(T_s)
+        reps += 1
+    dt = total / reps
     return {"value": w.B * T_s / dt, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
             "sample": f"first {T_s} of {w.T} tokens x batch {w.B}, all {w.Hv} value heads, "
                       f"all {w.dv} state columns; fp64 per-token rule in C, {nthreads} threads; "
-                      f"{dt:.2f} s"}
+                      f"mean of {reps} runs, {dt:.2f} s each"}
 
 
 def time_steps(fn, steps, warmup):
@@ -292,21 +299,22 @@ def main():
         print(json.dumps({"profile_run": w.name, "ms_per_step": ms}), flush=True)
         return
 
-    # per-kernel times: the same step issued stage by stage, events between
+    # per-kernel times: the same steps issued stage by stage on the same
+    # stream with events between the stages, all steps queued back to back
+    # (so no interval holds host launch latency); the first step is dropped
     names = [n for n in ("prep", "fold", "prefix", "walk", "out")
              if (w.n_groups > 1 or n not in ("fold", "prefix"))]
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-    acc = {n: 0.0 for n in names}
+    nst = args.steps + 1
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(nst)]
     torch.cuda.synchronize()
-    for _ in range(args.steps):
-        ev[0].record()
+    for k in range(nst):
+        ev[k][0].record()
         for i, n in enumerate(names):
             step(stage_bits[n])
-            ev[i + 1].record()
-        torch.cuda.synchronize()
-        for i, n in enumerate(names):
-            acc[n] += ev[i].elapsed_time(ev[i + 1])
-    stage_ms = {n: acc[n] / args.steps for n in names}
+            ev[k][i + 1].record()
+    torch.cuda.synchronize()
+    stage_ms = {n: sum(ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(1, nst)) / args.steps
+                for i, n in enumerate(names)}
 
     flops, nbytes = algorithmic(w)
     sb = stage_bytes(w)

@@ -204,6 +204,28 @@ def test_run_to_run_bitwise_determinism(gdn):
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
+@pytest.mark.parametrize("C,N,ng", [(64, 16, 0), (128, 32, 0), (128, 16, 4)])
+def test_stages_one_by_one_equal_one_call(gdn, C, N, ng):
+    # gdn_chunk_fwd_stages issued one stage per call on one stream (the
+    # per-kernel timing path of bench.py) must equal one gdn_chunk_fwd call
+    # bit for bit: the stages communicate only through the workspace
+    w = WORKLOADS["tiny"].replace(T=C * N, Hqk=2, Hv=4, chunk=C, dtype="bf16", h0_std=0.05)
+    x = make_inputs(w, device="cuda", seed=N + ng)
+    args = (x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"])
+    o1, h1 = gdn.chunk_fwd(*args, chunk=C, n_groups=ng)
+    shape = gdn.make_shape(w.B, w.T, w.Hqk, w.Hv, 128, 128, C, ng, x["k"].dtype, torch.float32)
+    ws = torch.empty(gdn.workspace_size(shape), dtype=torch.uint8, device="cuda")
+    o2, h2 = torch.empty_like(o1), torch.empty_like(h1)
+    stages = [gdn.STAGE_PREP] + ([gdn.STAGE_FOLD, gdn.STAGE_PREFIX] if ng > 1 else []) + \
+        [gdn.STAGE_WALK, gdn.STAGE_OUT]
+    for st in stages:
+        gdn.chunk_fwd(*args, chunk=C, n_groups=ng, workspace=ws, out=o2, final_state=h2, stages=st)
+    o3, h3 = gdn.chunk_fwd(*args, chunk=C, n_groups=ng, output_final_state=False)
+    torch.cuda.synchronize()
+    assert h3 is None
+    assert torch.equal(o1, o2) and torch.equal(h1, h2) and torch.equal(o1, o3)
+
+
 # ---------------------------------------------------------------------------
 # rows a7-a9: fold, exclusive prefix, replay
 
