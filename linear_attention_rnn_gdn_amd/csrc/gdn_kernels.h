@@ -193,9 +193,10 @@ __device__ __forceinline__ void load_rows_f32(float *dst, int ld, const float *s
 //   sX  one C x D input tile at a time: K row-major (for S), the ladder's
 //       scratch, then K^T and V^T (for W and U)
 //   sT  S, then T, in packed lower-triangular form (Tri)
-// Each thread loads one 8-row block of K (and later of V) into registers
-// once; the row-major copy feeds S, and the same registers are transposed in
-// place for the K^T copy, so K is read from memory once.
+// Each thread loads one 8-row block of K and of V into registers at the
+// start; the row-major copy of K feeds S, and the same registers are
+// transposed in place for the K^T and V^T copies, so K and V are read from
+// memory once.
 
 // Packed lower-triangular C x C matrix: row tile m (16 rows) keeps its first
 // len(m) = 32 (m/2 + 1) columns -- its part of the lower triangle rounded up
@@ -313,6 +314,98 @@ __device__ __forceinline__ Frag<K> xt_frag(const TI *sxt, int d, int k0) {
   }
 }
 
+// One level (block size BS) of the doubling ladder of step (5) below, fully
+// unrolled: for each 2BS diagonal block [[P,0],[L,Q]] of the packed T, the
+// lower-left block becomes -X_Q L X_P.  Tiles are shared out over the 4
+// waves; each tile's operands are read from LDS in one batch before its
+// products.  sM holds M1 = L X_P transposed (nb blocks of BS x (BS+4)).
+template <int C, int BS, int PL>
+__device__ __forceinline__ void ladder_level(float *sT, float *sM, int wave, int lane) {
+  using TRI = Tri<C>;
+  constexpr int NB = C / (2 * BS), TB = BS / 16, NTILE = NB * TB * TB, PER = (NTILE + 3) / 4;
+  constexpr int LDM = BS + 4, KBM = (BS + 31) / 32;
+  constexpr int GRP = PER < 2 ? PER : 2;   // tiles per batch of reads
+  const int lr = lane & 15, lk = (lane >> 4) * 8, lq = (lane >> 4) * 4;
+  // M1 = L X_P (stored transposed in sM)
+#pragma unroll
+  for (int u0 = 0; u0 < PER; u0 += GRP) {
+    float a8[GRP][KBM][8], b8[GRP][KBM][8];
+    int tl[GRP];
+#pragma unroll
+    for (int v = 0; v < GRP; ++v) {
+      const int tt = wave + 4 * (u0 + v);
+      tl[v] = tt;
+      const int blk = tt / (TB * TB), ti = tt % (TB * TB), mi = ti / TB, ni = ti % TB;
+      const int s = blk * 2 * BS, kb0 = (16 * ni) / 32;
+#pragma unroll
+      for (int kb = 0; kb < KBM; ++kb) {
+        const int k0 = 32 * kb + lk;
+        if (tt < NTILE && kb >= kb0 && k0 < BS) {
+          ld8(sT + TRI::at(s + BS + 16 * mi + lr, s + k0), a8[v][kb]);
+          // column s + 16 ni + lr of X_P, rows s + k0 .. + 7 (one row tile)
+          const float *col = sT + TRI::at(s + k0, s + 16 * ni + lr);
+          const int str = TRI::len((s + k0) >> 4) + 4;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) b8[v][kb][j] = col[j * str];
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) a8[v][kb][j] = b8[v][kb][j] = 0.f;
+        }
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < GRP; ++v) {
+      const int tt = tl[v];
+      if (tt >= NTILE) continue;
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int kb = 0; kb < KBM; ++kb) mma_k32<PL>(acc, a8[v][kb], b8[v][kb]);
+      const int blk = tt / (TB * TB), ti = tt % (TB * TB), mi = ti / TB, ni = ti % TB;
+      float *M = sM + blk * BS * LDM;
+      *reinterpret_cast<float4 *>(M + (16 * ni + lr) * LDM + 16 * mi + lq) = float4{acc[0], acc[1], acc[2], acc[3]};
+    }
+  }
+  lds_barrier();
+  // L <- -X_Q M1
+#pragma unroll
+  for (int u0 = 0; u0 < PER; u0 += GRP) {
+    float a8[GRP][KBM][8], b8[GRP][KBM][8];
+    int tl[GRP];
+#pragma unroll
+    for (int v = 0; v < GRP; ++v) {
+      const int tt = wave + 4 * (u0 + v);
+      tl[v] = tt;
+      const int blk = tt / (TB * TB), ti = tt % (TB * TB), mi = ti / TB, ni = ti % TB;
+      const int s = blk * 2 * BS;
+      const float *M = sM + blk * BS * LDM;
+#pragma unroll
+      for (int kb = 0; kb < KBM; ++kb) {
+        const int k0 = 32 * kb + lk;
+        if (tt < NTILE && kb * 32 < 16 * (mi + 1) && k0 < BS) {
+          ld8(sT + TRI::at(s + BS + 16 * mi + lr, s + BS + k0), a8[v][kb]);
+          ld8(M + (16 * ni + lr) * LDM + k0, b8[v][kb]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) a8[v][kb][j] = b8[v][kb][j] = 0.f;
+        }
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < GRP; ++v) {
+      const int tt = tl[v];
+      if (tt >= NTILE) continue;
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int kb = 0; kb < KBM; ++kb) mma_k32<PL>(acc, a8[v][kb], b8[v][kb]);
+      const int blk = tt / (TB * TB), ti = tt % (TB * TB), mi = ti / TB, ni = ti % TB;
+      const int s = blk * 2 * BS;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sT[TRI::at(s + BS + 16 * mi + lq + i, s + 16 * ni + lr)] = -acc[i];
+    }
+  }
+  lds_barrier();
+}
+
 template <int C, typename TI, int MODE, bool FWD>
 __global__ __launch_bounds__(NT, 2) void prep_kernel(FwdArgs a) {
   using WT = typename std::conditional<FWD, TI, float>::type;
@@ -342,6 +435,7 @@ __global__ __launch_bounds__(NT, 2) void prep_kernel(FwdArgs a) {
   // K block of this thread -> registers (kept for the transposed copy)
   TileBlock<C, TI> kt, vt;
   kt.load(reinterpret_cast<const TI *>(a.k) + (((size_t)b * a.T + t0) * a.Hqk + hq) * D, (size_t)a.Hqk * D);
+  vt.load(reinterpret_cast<const TI *>(a.v) + (((size_t)b * a.T + t0) * a.Hv + hv) * D, (size_t)a.Hv * D);
 
   // (1) decay cumsum over the chunk (inclusive), beta
   {
@@ -414,8 +508,6 @@ __global__ __launch_bounds__(NT, 2) void prep_kernel(FwdArgs a) {
       }
     }
   }
-  // V block -> registers; its latency hides behind the inversion
-  vt.load(reinterpret_cast<const TI *>(a.v) + (((size_t)b * a.T + t0) * a.Hv + hv) * D, (size_t)a.Hv * D);
   lds_barrier();
 
   // (4) exact inverses of the 16x16 diagonal blocks (forward substitution,
@@ -444,54 +536,10 @@ __global__ __launch_bounds__(NT, 2) void prep_kernel(FwdArgs a) {
   // (5) doubling ladder: for each 2b diagonal block [[P,0],[L,Q]] the new
   //     lower-left block is -X_Q L X_P (X_P, X_Q the current inverses).
   //     The row-major K tile is dead; its space holds the scratch sM.
-  for (int bs = 16; bs < C; bs *= 2) {
-    const int nb = C / (2 * bs), tb = bs / 16, ldm = bs + 4;
-    // M1 = L X_P  (stored transposed in sM)
-    for (int tt = wave; tt < nb * tb * tb; tt += 4) {
-      const int blk = tt / (tb * tb), ti = tt % (tb * tb), mi = ti / tb, ni = ti % tb;
-      const int s = blk * 2 * bs;
-      f32x4 acc = zero4();
-      for (int kb = (16 * ni) / 32; kb * 32 < bs; ++kb) {
-        float a8[8], b8[8];
-        const int k0 = 32 * kb + lk;
-        if (k0 < bs) {
-          ld8(sT + TRI::at(s + bs + 16 * mi + lr, s + k0), a8);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) b8[j] = sT[TRI::at(s + k0 + j, s + 16 * ni + lr)];
-        } else {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) a8[j] = b8[j] = 0.f;
-        }
-        mma_k32<PR::ladder>(acc, a8, b8);
-      }
-      float *M = sM + blk * bs * ldm;
-      *reinterpret_cast<float4 *>(M + (16 * ni + lr) * ldm + 16 * mi + lq) =
-          float4{acc[0], acc[1], acc[2], acc[3]};
-    }
-    lds_barrier();
-    // L <- -X_Q M1
-    for (int tt = wave; tt < nb * tb * tb; tt += 4) {
-      const int blk = tt / (tb * tb), ti = tt % (tb * tb), mi = ti / tb, ni = ti % tb;
-      const int s = blk * 2 * bs;
-      const float *M = sM + blk * bs * ldm;
-      f32x4 acc = zero4();
-      for (int kb = 0; kb * 32 < 16 * (mi + 1); ++kb) {
-        float a8[8], b8[8];
-        const int k0 = 32 * kb + lk;
-        if (k0 < bs) {
-          ld8(sT + TRI::at(s + bs + 16 * mi + lr, s + bs + k0), a8);
-          ld8(M + (16 * ni + lr) * ldm + k0, b8);
-        } else {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) a8[j] = b8[j] = 0.f;
-        }
-        mma_k32<PR::ladder>(acc, a8, b8);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sT[TRI::at(s + bs + 16 * mi + lq + i, s + 16 * ni + lr)] = -acc[i];
-    }
-    lds_barrier();
-  }
+  ladder_level<C, 16, PR::ladder>(sT, sM, wave, lane);
+  ladder_level<C, 32, PR::ladder>(sT, sM, wave, lane);
+  if constexpr (C > 64) ladder_level<C, 64, PR::ladder>(sT, sM, wave, lane);
+  static_assert(C == 64 || C == 128, "ladder levels for C = 64 and 128");
 
   if (a.Tm) {
     float *Tg = a.Tm + cb * C * C;
@@ -1038,82 +1086,104 @@ __global__ __launch_bounds__(64) void walk_ring_kernel(FwdArgs a) {
 }
 
 // ----------------------------------------------------------------------------
-// exclusive prefix of affine pairs, one column slice of the state.
+// exclusive prefix of affine pairs: h_in[0] = h_init, h_in[j+1] = A_j h_in[j]
+// + B_j, h_final = A_{n-1} h_in[n-1] + B_{n-1}.  One wave per 16-column slice
+// of the state (the recurrence is column-separable), with the slice in
+// matrix-core result registers for all n steps, as in the walk.  A_j (row-
+// major fp32) is the A operand: per lane two 16-byte runs of a row, in the
+// k order of two stacked result tiles, so the state tiles are the B operand
+// as they stand.  A's fragments stream through a ring of register slots in
+// the order they are used; B_j arrives one step ahead.
 struct PrefixArgs {
   int BH, n;
   const float *A, *Bm, *h_init;
   float *h_in, *h_final;
 };
 
-template <int S, int PREC>
-__global__ __launch_bounds__(NT) void prefix_kernel(PrefixArgs a) {
-  constexpr int LDA = D + 4, LDH = D + 4;
-  __shared__ __align__(16) float sA[D * LDA];
-  __shared__ __align__(16) float sH[S * LDH];
+template <int PREC>
+__global__ __launch_bounds__(64) void prefix_kernel(PrefixArgs a) {
+  using PK = PolicyKinds<PREC>;
+  constexpr int MH = D / 16, KB = D / 32;
+  constexpr int F = MH * KB;      // A fragments per step
+  constexpr int RING = 16;        // slots (two 16-byte runs each)
+  static_assert(F % RING == 0, "ring slots must repeat every step");
   int unit, slice;
-  xcd_unit(blockIdx.x, D / S, a.BH, unit, slice);
+  xcd_unit(blockIdx.x, D / 16, a.BH, unit, slice);
   const size_t bh = (size_t)unit;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lr = lane & 15, lk = (lane >> 4) * 8, lq = (lane >> 4) * 4;
-  const int c0 = slice * S;
-  for (int idx = tid; idx < D * S; idx += NT) {
-    const int kr = idx / S, c = idx % S;
-    sH[c * LDH + kr] = a.h_init ? a.h_init[(bh * D + kr) * D + c0 + c] : 0.f;
-  }
-  for (int j = 0; j < a.n; ++j) {
-    const size_t pj = bh * a.n + j;
-    const float *Ag = a.A + pj * D * D;
-    for (int idx = tid; idx < D * D / 4; idx += NT) {
-      const int r = idx / (D / 4), c4 = (idx % (D / 4)) * 4;
-      *reinterpret_cast<float4 *>(sA + r * LDA + c4) = *reinterpret_cast<const float4 *>(Ag + (size_t)r * D + c4);
-    }
-    lds_barrier();
+  const int lane = threadIdx.x, lr = lane & 15, g = lane >> 4;
+  const int c0 = slice * 16;
+
+  f32x4 h[MH];
+#pragma unroll
+  for (int m = 0; m < MH; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      h[m][i] = a.h_init ? a.h_init[(bh * D + 16 * m + 4 * g + i) * D + c0 + lr] : 0.f;
+
+  // fragment p = (row tile m, k-block kb) of A_j: row 16m + lr, columns
+  // 32kb + 4g .. +3 and 32kb + 16 + 4g .. +3
+  struct Run2 {
+    float4 x0, x1;
+  };
+  auto load = [&](size_t j, int p) -> Run2 {
+    const float *row = a.A + ((bh * a.n + j) * D + 16 * (p / KB) + lr) * D + 32 * (p % KB) + 4 * g;
+    return Run2{*reinterpret_cast<const float4 *>(row), *reinterpret_cast<const float4 *>(row + 16)};
+  };
+  auto load_b = [&](size_t j, f32x4 (&bq)[MH]) {
+    const float *B = a.Bm + (bh * a.n + j) * D * D + c0 + lr;
+#pragma unroll
+    for (int m = 0; m < MH; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bq[m][i] = B[(size_t)(16 * m + 4 * g + i) * D];
+  };
+  Run2 ring[RING];
+#pragma unroll
+  for (int p = 0; p < RING; ++p) ring[p] = load(0, p);
+  f32x4 bq[2][MH];
+  load_b(0, bq[0]);
+
+  auto step = [&](f32x4 (&bc)[MH], f32x4 (&bn)[MH], int j) {
+    const size_t jn = j + 1 < a.n ? j + 1 : j;   // last step: loads repeat (unused)
+    load_b(jn, bn);
     if (a.h_in) {
-      float *Hg = a.h_in + pj * D * D;
-      for (int idx = tid; idx < D * S; idx += NT) {
-        const int kr = idx / S, c = idx % S;
-        Hg[(size_t)kr * D + c0 + c] = sH[c * LDH + kr];
-      }
+      float *dst = a.h_in + ((bh * a.n + j) * D) * D + c0 + lr;
+#pragma unroll
+      for (int m = 0; m < MH; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[(size_t)(16 * m + 4 * g + i) * D] = h[m][i];
     }
-    // all of this wave's tiles share column tile wave % (S/16)
-    constexpr int NTU = (D / 16) * (S / 16) / 4;
-    static_assert(4 % (S / 16) == 0, "tiling");
-    using PK = PolicyKinds<PREC>;
-    f32x4 acc[NTU];
+    Frag<PK::b> hb[KB];
 #pragma unroll
-    for (int u = 0; u < NTU; ++u) acc[u] = zero4();
-    {
-      const int ni = wave % (S / 16);
-#pragma unroll
-      for (int kb = 0; kb < D / 32; ++kb) {
-        const auto bf = lds_frag<PK::b>(sH + (16 * ni + lr) * LDH + 32 * kb + lk);
-#pragma unroll
-        for (int u = 0; u < NTU; ++u) {
-          const int mi = (wave + 4 * u) / (S / 16);
-          mma(acc[u], lds_frag<PK::a>(sA + (16 * mi + lr) * LDA + 32 * kb + lk), bf);
-        }
-      }
+    for (int kb = 0; kb < KB; ++kb) {
+      const float x[8] = {h[2 * kb][0], h[2 * kb][1], h[2 * kb][2], h[2 * kb][3],
+                          h[2 * kb + 1][0], h[2 * kb + 1][1], h[2 * kb + 1][2], h[2 * kb + 1][3]};
+      hb[kb] = make_frag<PK::b>(x);
     }
-    lds_barrier();
-    const float *Bg = a.Bm + pj * D * D;
 #pragma unroll
-    for (int u = 0; u < (D / 16) * (S / 16) / 4; ++u) {
-      const int tt = wave + 4 * u;
-      const int mi = tt / (S / 16), ni = tt % (S / 16);
-      const int c = 16 * ni + lr;
+    for (int m = 0; m < MH; ++m) {
+      f32x4 acc = zero4();
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = 16 * mi + lq + i;
-        sH[c * LDH + m] = acc[u][i] + Bg[(size_t)m * D + c0 + c];
+      for (int kb = 0; kb < KB; ++kb) {
+        const int p = m * KB + kb;
+        const Run2 r = ring[p % RING];
+        const float x[8] = {r.x0.x, r.x0.y, r.x0.z, r.x0.w, r.x1.x, r.x1.y, r.x1.z, r.x1.w};
+        ring[p % RING] = p + RING < F ? load(j, p + RING) : load(jn, p + RING - F);
+        mma(acc, make_frag<PK::a>(x), hb[kb]);
       }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) h[m][i] = acc[i] + bc[m][i];
     }
-    lds_barrier();
+  };
+  // two steps per trip so the B sets alternate without copies
+  for (int j = 0; j < a.n; j += 2) {
+    step(bq[0], bq[1], j);
+    if (j + 1 < a.n) step(bq[1], bq[0], j + 1);
   }
   if (a.h_final) {
-    for (int idx = tid; idx < D * S; idx += NT) {
-      const int kr = idx / S, c = idx % S;
-      a.h_final[(bh * D + kr) * D + c0 + c] = sH[c * LDH + kr];
-    }
+#pragma unroll
+    for (int m = 0; m < MH; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a.h_final[(bh * D + 16 * m + 4 * g + i) * D + c0 + lr] = h[m][i];
   }
 }
 
