@@ -91,14 +91,16 @@ gdn_status launch_walk(const FwdArgs &a, hipStream_t st) {
   const int width = KIND == FOLD ? 2 * D : D;
   // one wave per 16-column slice.  Enough units to give every compute unit
   // two workgroups: 8 slices per workgroup sharing their operands through
-  // LDS.  Fewer (a short walk, latency-bound): one slice per workgroup, so
-  // the walk spreads over the chip's compute units.
+  // LDS.  Fewer (a short walk, latency-bound): one slice per workgroup of 2
+  // or 4 waves that split its rows, so the walk spreads over the chip.
   const long units = (long)a.B * a.Hv * a.jobs;
   if (units * (width / 128) >= 512) {
     hipLaunchKernelGGL((walk_shared_kernel<C, TI, MODE, KIND, 8>), dim3((unsigned)(units * (width / 128))), dim3(512), 0,
                        st, a);
   } else {
-    hipLaunchKernelGGL((walk_ring_kernel<C, TI, MODE, KIND>), dim3((unsigned)(units * (width / 16))), dim3(64), 0, st, a);
+    constexpr int NWS = C >= 128 ? 4 : 2;   // waves per slice: whole k-blocks of V' rows each
+    hipLaunchKernelGGL((walk_ring_kernel<C, TI, MODE, KIND, NWS>), dim3((unsigned)(units * (width / 16))), dim3(64 * NWS), 0,
+                       st, a);
   }
   return check_launch();
 }

@@ -910,46 +910,62 @@ __global__ __launch_bounds__(64 * WPG) void walk_shared_kernel(FwdArgs a) {
 }
 
 // ----------------------------------------------------------------------------
-// walk / fold, latency form: one workgroup of one wave per 16-column slice of
-// the state (no LDS, no barriers), for walks too few to fill the chip.
-//
-// The state, V' and their register chaining are those of walk_shared_kernel
-// below.  W and K^T fragments stream from memory, in the order they are used,
-// through a ring of RING register slots (a slot is refilled as soon as its
-// fragment has been consumed); U and G arrive one chunk ahead.
-template <int C, typename TI, int MODE, int KIND>
-__global__ __launch_bounds__(64) void walk_ring_kernel(FwdArgs a) {
+// walk / fold, latency form: one workgroup of NWS waves per 16-column slice
+// of the state, for walks too few to fill the chip.  The state, V' and their
+// register chaining are those of walk_shared_kernel above; here the slice's
+// rows are split between the waves: wave w holds state rows 128w/NWS.. and
+// corrected-value rows Cw/NWS.., and streams only the W and K^T fragments of
+// its own rows (1/NWS of a chunk's, through a ring of register slots,
+// refilled as soon as consumed: one or more chunks ahead).  The B operands --
+// the bf16 state for V' = U - W h, the split d o V' for the state update --
+// pass between the waves through LDS, two barriers per chunk.  U and G arrive
+// one chunk ahead.
+template <int C, typename TI, int MODE, int KIND, int NWS>
+__global__ __launch_bounds__(64 * NWS) void walk_ring_kernel(FwdArgs a) {
   using PR = Prec<MODE>;
   using PKw = PolicyKinds<PR::wh>;
   using PKk = PolicyKinds<PR::kv>;
   constexpr bool F32 = sizeof(TI) == 4;
   static_assert(PKw::a == (F32 ? F_F32 : F_BF16) && PKk::a == PKw::a, "W and K^T fragments are used as stored");
   using AF = Frag<PKw::a>;
+  using HF = Frag<PKw::b>;   // state operand (for W h)
+  using VF = Frag<PKk::b>;   // d o V' operand (for K^T (d o V'))
   constexpr int NS = (KIND == FOLD ? 2 * D : D) / 16;   // slices
   constexpr int MV = C / 16, MH = D / 16;                // V' and state row tiles
   constexpr int KBW = D / 32, KBK = C / 32;              // k-blocks of the two products
-  constexpr int FW = MV * KBW, FK = MH * KBK, F = FW + FK;   // fragments per chunk
-  constexpr int RING = F32 ? 16 : 32;
-  static_assert(F % RING == 0, "ring slots must repeat every chunk");
+  constexpr int MVW = MV / NWS, MHW = MH / NWS;          // row tiles per wave
+  constexpr int KBWW = KBW / NWS, KBKW = KBK / NWS;      // k-blocks held by each wave
+  static_assert(MVW % 2 == 0 && MHW % 2 == 0, "each wave holds whole k-blocks");
+  constexpr int FW = MV * KBW;                           // W fragments per chunk (K^T follow)
+  constexpr int FWW = MVW * KBW, FKW = MHW * KBK, FPW = FWW + FKW;   // per wave per chunk
+  // ring slots: up to 32 (bf16) / 16 (fp32) fragments, at most one chunk's
+  // (a ring of two chunks, slot parity = chunk parity, measured no faster)
+  constexpr int SLOTS = F32 ? 16 : 32;
+  constexpr int RING = SLOTS < FPW ? SLOTS : FPW;
+  static_assert(FPW % RING == 0 && KBKW >= 1, "ring slots must repeat every chunk");
+  __shared__ __align__(16) HF xh[NWS][KBWW][64];
+  __shared__ __align__(16) VF xv[NWS][KBKW][64];
 
   int unit, slice;
   xcd_unit(blockIdx.x, NS, a.B * a.Hv * a.jobs, unit, slice);
   const int job = unit % a.jobs;
   const size_t bh = (size_t)(unit / a.jobs);
-  const int lane = threadIdx.x, lr = lane & 15, g = lane >> 4;
+  const int lane = threadIdx.x & 63, lr = lane & 15, g = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c0 = slice * 16;   // first column (of the augmented [A|B] in FOLD)
   const bool has_u = KIND == WALK || c0 >= D;
   const int us = KIND == WALK ? slice : slice - D / 16;   // U column tile
   const size_t cb0 = bh * a.N + a.n0 + (size_t)job * a.cpj;
+  const int mv0 = w * MVW, mh0 = w * MHW;                 // this wave's first V' / state tile
 
-  // state tiles: h[m] holds rows 16m + 4g + i, column c0 + lr
-  f32x4 h[MH];
+  // state tiles of this wave: h[t] holds rows 16(mh0+t) + 4g + i, column c0 + lr
+  f32x4 h[MHW];
 #pragma unroll
-  for (int m = 0; m < MH; ++m) {
+  for (int t = 0; t < MHW; ++t) {
     const int col = c0 + lr;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int kr = 16 * m + 4 * g + i;
+      const int kr = 16 * (mh0 + t) + 4 * g + i;
       float x = 0.f;
       if (KIND == FOLD) {
         x = (col < D && kr == col) ? 1.f : 0.f;
@@ -957,14 +973,17 @@ __global__ __launch_bounds__(64) void walk_ring_kernel(FwdArgs a) {
         const float *src = a.init_per_job ? a.init + (bh * a.jobs + job) * D * D : a.init + bh * D * D;
         x = src[(size_t)kr * D + col];
       }
-      h[m][i] = x;
+      h[t][i] = x;
     }
   }
 
+  // this wave's fragment sequence per chunk: W (its V' row tiles, all
+  // k-blocks), then K^T (its state row tiles, all k-blocks)
   const TI *Wb = reinterpret_cast<const TI *>(a.W) + lane * 8;
   const TI *Kb = reinterpret_cast<const TI *>(a.Kt) + lane * 8;
-  auto load = [&](size_t cb, int p) -> AF {
-    const TI *src = p < FW ? Wb + cb * C * D + (size_t)p * 512 : Kb + cb * D * C + (size_t)(p - FW) * 512;
+  auto load = [&](size_t cb, int q) -> AF {
+    const TI *src = q < FWW ? Wb + cb * C * D + (size_t)(mv0 * KBW + q) * 512
+                            : Kb + cb * D * C + (size_t)(mh0 * KBK + q - FWW) * 512;
     AF f;
     if constexpr (F32) {
       const float4 x0 = *reinterpret_cast<const float4 *>(src);
@@ -977,98 +996,123 @@ __global__ __launch_bounds__(64) void walk_ring_kernel(FwdArgs a) {
     return f;
   };
   struct UG {
-    float4 u[MV], g[MV];
+    float4 u[MVW], g[MVW];
     float glast;
   };
   auto fetch_ug = [&](size_t cb, UG &x) {
 #pragma unroll
-    for (int m = 0; m < MV; ++m) {
-      x.u[m] = has_u ? *reinterpret_cast<const float4 *>(a.U + ((cb * MV + m) * (D / 16) + us) * 256 + lane * 4)
+    for (int m = 0; m < MVW; ++m) {
+      x.u[m] = has_u ? *reinterpret_cast<const float4 *>(a.U + ((cb * MV + mv0 + m) * (D / 16) + us) * 256 + lane * 4)
                      : float4{0.f, 0.f, 0.f, 0.f};
-      x.g[m] = *reinterpret_cast<const float4 *>(a.G + cb * C + 16 * m + 4 * g);
+      x.g[m] = *reinterpret_cast<const float4 *>(a.G + cb * C + 16 * (mv0 + m) + 4 * g);
     }
     x.glast = a.G[cb * C + C - 1 + vgpr_zero()];
+  };
+  auto state_frag = [&](int kbl) -> HF {   // own state k-block kbl (tiles 2kbl, 2kbl+1)
+    const float x[8] = {h[2 * kbl][0], h[2 * kbl][1], h[2 * kbl][2], h[2 * kbl][3],
+                        h[2 * kbl + 1][0], h[2 * kbl + 1][1], h[2 * kbl + 1][2], h[2 * kbl + 1][3]};
+    return make_frag<PKw::b>(x);
   };
 
   AF ring[RING];
 #pragma unroll
-  for (int p = 0; p < RING; ++p) ring[p] = load(cb0, p);
+  for (int q = 0; q < RING; ++q) {
+    const size_t c = cb0 + q / FPW;
+    ring[q] = load(c < cb0 + a.cpj - 1 ? c : cb0 + a.cpj - 1, q % FPW);
+  }
   UG ug[2];
   fetch_ug(cb0, ug[0]);
+  // the state operand of the first chunk
+#pragma unroll
+  for (int kbl = 0; kbl < KBWW; ++kbl) xh[w][kbl][lane] = state_frag(kbl);
+  lds_barrier();
 
-  auto step = [&](UG &cur, UG &nxt, int cc) {
+  const size_t cblast = cb0 + a.cpj - 1;
+  // fragment q of chunk cb sits in slot (P FPW + q) % RING (P = chunk parity);
+  // once consumed, the slot takes the fragment RING positions later in the
+  // sequence (past the last chunk: the last chunk again, unused)
+  auto refill = [&](int P, size_t cb, int q) {
+    const int nq = q + RING;
+    const size_t c = cb + nq / FPW;
+    ring[(P * FPW + q) % RING] = load(c < cblast ? c : cblast, nq % FPW);
+  };
+  auto step = [&](UG &cur, UG &nxt, int cc, auto Pc) {
+    constexpr int P = decltype(Pc)::value;
     const size_t cb = cb0 + cc;
-    // the next chunk's operands (the current chunk again on the last step,
-    // so that every load is unconditional; those values are not used)
-    const size_t cbn = cc + 1 < a.cpj ? cb + 1 : cb;
+    const size_t cbn = cc + 1 < a.cpj ? cb + 1 : cb;   // last chunk: repeat loads (unused)
     fetch_ug(cbn, nxt);
     const float gl2 = cur.glast * LOG2E;
-    float dcy[MV][4];
+    float dcy[MVW][4];
 #pragma unroll
-    for (int m = 0; m < MV; ++m) {
+    for (int m = 0; m < MVW; ++m) {
       dcy[m][0] = exp2_fast(gl2 - cur.g[m].x * LOG2E);
       dcy[m][1] = exp2_fast(gl2 - cur.g[m].y * LOG2E);
       dcy[m][2] = exp2_fast(gl2 - cur.g[m].z * LOG2E);
       dcy[m][3] = exp2_fast(gl2 - cur.g[m].w * LOG2E);
     }
-    if (KIND == WALK && a.Hs) store_result_tiles<PR::split_store>(a.Hs + (cb * (D / 16) + slice) * MH * 256, h, lane);
-    // V' = U - W h
-    Frag<PKw::b> hb[KBW];
+    if (KIND == WALK && a.Hs)
+      store_result_tiles<PR::split_store>(a.Hs + (cb * (D / 16) + slice) * MH * 256 + mh0 * 256, h, lane);
+    // V' = U - W h over all state k-blocks: own from registers, partner's from LDS
+    // every k-block from LDS, the wave's own included (static indices)
+    HF hb[KBW];
 #pragma unroll
-    for (int kb = 0; kb < KBW; ++kb) {
-      const float x[8] = {h[2 * kb][0], h[2 * kb][1], h[2 * kb][2], h[2 * kb][3],
-                          h[2 * kb + 1][0], h[2 * kb + 1][1], h[2 * kb + 1][2], h[2 * kb + 1][3]};
-      hb[kb] = make_frag<PKw::b>(x);
+    for (int kb = 0; kb < KBW; ++kb) hb[kb] = xh[kb / KBWW][kb % KBWW][lane];
+    f32x4 acc[MVW];
+#pragma unroll
+    for (int m = 0; m < MVW; ++m) acc[m] = zero4();
+#pragma unroll
+    for (int q = 0; q < FWW; ++q) {
+      mma(acc[q / KBW], ring[(P * FPW + q) % RING], hb[q % KBW]);
+      refill(P, cb, q);
     }
-    f32x4 acc[MV];
-#pragma unroll
-    for (int m = 0; m < MV; ++m) acc[m] = zero4();
-#pragma unroll
-    for (int p = 0; p < FW; ++p) {
-      mma(acc[p / KBW], ring[p % RING], hb[p % KBW]);
-      ring[p % RING] = p + RING < F ? load(cb, p + RING) : load(cbn, p + RING - F);
-    }
-    Frag<PKk::b> vb[KBK];
+    VF vb[KBK];
     {
-      float s[MV][4];
-      f32x4 vps[MV];
+      float s[MVW][4];
+      f32x4 vps[MVW];
 #pragma unroll
-      for (int m = 0; m < MV; ++m) {
+      for (int m = 0; m < MVW; ++m) {
         const float4 uu = cur.u[m];
         vps[m] = f32x4{uu.x - acc[m][0], uu.y - acc[m][1], uu.z - acc[m][2], uu.w - acc[m][3]};
 #pragma unroll
         for (int i = 0; i < 4; ++i) s[m][i] = vps[m][i] * dcy[m][i];
       }
-      if (KIND == WALK && a.Vn) store_result_tiles<PR::split_store>(a.Vn + (cb * (D / 16) + slice) * MV * 256, vps, lane);
+      if (KIND == WALK && a.Vn)
+        store_result_tiles<PR::split_store>(a.Vn + (cb * (D / 16) + slice) * MV * 256 + mv0 * 256, vps, lane);
 #pragma unroll
-      for (int kb = 0; kb < KBK; ++kb) {
-        const float x[8] = {s[2 * kb][0], s[2 * kb][1], s[2 * kb][2], s[2 * kb][3],
-                            s[2 * kb + 1][0], s[2 * kb + 1][1], s[2 * kb + 1][2], s[2 * kb + 1][3]};
-        vb[kb] = make_frag<PKk::b>(x);
+      for (int kbl = 0; kbl < KBKW; ++kbl) {
+        const float x[8] = {s[2 * kbl][0], s[2 * kbl][1], s[2 * kbl][2], s[2 * kbl][3],
+                            s[2 * kbl + 1][0], s[2 * kbl + 1][1], s[2 * kbl + 1][2], s[2 * kbl + 1][3]};
+        xv[w][kbl][lane] = make_frag<PKk::b>(x);
       }
+      lds_barrier();
+#pragma unroll
+      for (int kb = 0; kb < KBK; ++kb) vb[kb] = xv[kb / KBKW][kb % KBKW][lane];
     }
-    // h <- e^{G_last} h + K^T (d o V')
+    // h <- e^{G_last} h + K^T (d o V') for this wave's state rows
     const float gl = exp2_fast(gl2);
 #pragma unroll
-    for (int m = 0; m < MH; ++m) {
+    for (int t = 0; t < MHW; ++t) {
       f32x4 acc2 = zero4();
 #pragma unroll
       for (int kb = 0; kb < KBK; ++kb) {
-        const int p = FW + m * KBK + kb;
-        mma(acc2, ring[p % RING], vb[kb]);
-        ring[p % RING] = p + RING < F ? load(cb, p + RING) : load(cbn, p + RING - F);
+        const int q = FWW + t * KBK + kb;
+        mma(acc2, ring[(P * FPW + q) % RING], vb[kb]);
+        refill(P, cb, q);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) h[m][i] = gl * h[m][i] + acc2[i];
+      for (int i = 0; i < 4; ++i) h[t][i] = gl * h[t][i] + acc2[i];
     }
+#pragma unroll
+    for (int kbl = 0; kbl < KBWW; ++kbl) xh[w][kbl][lane] = state_frag(kbl);
+    lds_barrier();
   };
   // two chunks per trip so the U/G sets alternate without copies
   for (int cc = 0; cc < a.cpj; cc += 2) {
-    step(ug[0], ug[1], cc);
-    if (cc + 1 < a.cpj) step(ug[1], ug[0], cc + 1);
+    step(ug[0], ug[1], cc, std::integral_constant<int, 0>{});
+    if (cc + 1 < a.cpj) step(ug[1], ug[0], cc + 1, std::integral_constant<int, 1>{});
   }
 
-  // final state slice
+  // final state rows of this wave
   float *dst = nullptr;
   int dcol = c0;
   if (KIND == FOLD) {
@@ -1079,9 +1123,9 @@ __global__ __launch_bounds__(64) void walk_ring_kernel(FwdArgs a) {
   }
   if (dst) {
 #pragma unroll
-    for (int m = 0; m < MH; ++m)
+    for (int t = 0; t < MHW; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dst[(size_t)(16 * m + 4 * g + i) * D + dcol + lr] = h[m][i];
+      for (int i = 0; i < 4; ++i) dst[(size_t)(16 * (mh0 + t) + 4 * g + i) * D + dcol + lr] = h[t][i];
   }
 }
 

@@ -274,6 +274,19 @@ def test_group_count_invariance(gdn, ng):
     _check("h_T", h, h_ref, 2e-2, ro)
 
 
+@pytest.mark.parametrize("ng", [64, 72])
+def test_many_groups_of_one_chunk(gdn, ng):
+    # one chunk per group: the fold, a 64- or 72-step prefix and the replay
+    # carry the whole sequence; weak decay so that every group's pair
+    # reaches the output
+    w = WORKLOADS["tiny"].replace(T=64 * ng, Hqk=1, Hv=2, chunk=64, dtype="bf16", h0_std=0.05)
+    x = make_inputs(w, device="cuda", seed=ng, g_const=-0.01, beta_scale=0.1)
+    o, h, o_ref, h_ref = _run_and_compare(gdn, w, x, n_groups=ng)
+    ro = _rms(o_ref)
+    _check("o", o, o_ref, 2e-2, ro)
+    _check("h_T", h, h_ref, 2e-2, ro)
+
+
 def test_groups_weak_decay_compose_matters(gdn):
     # g = 0 and small beta keep each group's affine map far from zero, so the
     # incoming states really carry information across groups
