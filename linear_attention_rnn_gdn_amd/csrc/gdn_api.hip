@@ -84,7 +84,6 @@ gdn_status launch_prep(const FwdArgs &a, hipStream_t st) {
   return check_launch();
 }
 
-constexpr int kSlice = 32;
 
 template <int C, typename TI, int MODE, int KIND>
 gdn_status launch_walk(const FwdArgs &a, hipStream_t st) {
@@ -107,8 +106,8 @@ gdn_status launch_walk(const FwdArgs &a, hipStream_t st) {
 
 template <int C, typename TI, int MODE, typename TO>
 gdn_status launch_out(const FwdArgs &a, hipStream_t st) {
-  const long items = (long)(D / kSlice) * a.nn * a.B * a.Hv;
-  hipLaunchKernelGGL((out_kernel<C, TI, MODE, kSlice, TO>), dim3((unsigned)items), dim3(NT), 0, st, a);
+  const long units = (long)a.nn * a.B * a.Hv;   // one workgroup per (chunk, head)
+  hipLaunchKernelGGL((out_kernel<C, TI, MODE, TO>), dim3((unsigned)units), dim3(NT), 0, st, a);
   return check_launch();
 }
 

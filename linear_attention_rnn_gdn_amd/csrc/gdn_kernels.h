@@ -1232,300 +1232,287 @@ __global__ __launch_bounds__(64) void prefix_kernel(PrefixArgs a) {
 }
 
 // ----------------------------------------------------------------------------
-// output for one 32-column slice of one chunk, computed transposed:
+// output, one 4-wave workgroup per (chunk, value head), computed transposed:
 //   O^T = h^T (diag(e^G) Q)^T + V'^T P^T,   P^T = (K Q^T) o Gamma^T o [i <= r].
-// Persistent: each workgroup (4 waves) walks a strided list of (slice,
-// chunk, head) items.  The next item's K tile, chunk-start state slice,
-// corrected-value slice and G are copied straight into the other of two LDS
-// buffers (global_load_lds) and its queries into registers while the current
-// item is computed; one barrier per item.
-// All contractions use the k order of two stacked result tiles (lane group g
-// holds k = 4g..4g+3 and 16+4g..16+4g+3 of each block of 32), the order in
-// which the walk stored h and V': their fragments are read as stored.
-// Each wave owns query-row tiles (w and R-1-w, balancing the triangle).  P^T
-// tiles stay in result registers and feed V'^T P^T directly as B operands.
-template <int C, typename TI> struct OutBuf {
+// Phase A forms P^T once per chunk: wave w takes query-row tiles {w, R-1-w}
+// (balancing the triangle), reads K from LDS (copied in with
+// global_load_lds, row pieces XOR-swizzled against bank conflicts) and its
+// queries from memory, masks, decays and splits each tile pair and leaves it
+// in LDS as the B-operand fragment of (query tile, key block of 32).
+// Phase B: wave w owns state columns 32w .. 32w+31 for every query row; its
+// h^T and V'^T fragments (stored by the walk in this order) are loaded once
+// into registers, the queries stream from memory one tile ahead, and P^T
+// comes from LDS.  All contractions use the k order of two stacked result
+// tiles (lane group g holds k = 4g..4g+3 and 16+4g..16+4g+3 of each 32).
+template <int C, typename TI> struct OutLds {
   static constexpr int RP = D * (int)sizeof(TI) / 16;   // 16-byte pieces per K row
-  static constexpr int KB = C * RP * 16;                // K tile bytes (swizzled rows)
-  static constexpr int HB = D * 32 * 4;                 // state slice: 2 walk slices x D/16 tiles
-  static constexpr int VB = C * 32 * 4;                 // V' slice
-  static constexpr int HOFF = KB, VOFF = KB + HB, GOFF = KB + HB + VB;
-  static constexpr int BYTES = GOFF + 4 * C;
-  static constexpr int NBLK = (KB + HB + VB) / 1024;    // 1 KB copies (G aside)
-  // K[r][piece c] lives at piece position c ^ (r mod 16) of row r, so the 16
-  // rows of an operand read hit 16 different bank groups
+  static constexpr int KB = C * RP * 16;                // K tile bytes
+  static constexpr int R = C / 16;                      // query-row tiles
+  // (query tile rt, key block kp <= rt/2) pairs before tile rt
+  __host__ __device__ static constexpr int pbase(int rt) {
+    return (rt & 1) ? (rt / 2 + 1) * (rt / 2 + 1) : (rt / 2) * (rt / 2 + 1);
+  }
+  static constexpr int NPAIR = pbase(R);
+  static constexpr int POFF = KB, GOFF = POFF + NPAIR * 2048, BYTES = GOFF + 4 * C;
+  // K[r][piece c] lives at piece position c ^ (r mod 16) of row r
   __device__ static int kpos(int r, int c) { return r * RP + (c ^ (r & 15)); }
 };
 
-template <int C, typename TI, int MODE, int S, typename TO>
+template <int C, typename TI, int MODE, typename TO>
 __global__ __launch_bounds__(NT, 2) void out_kernel(FwdArgs a) {
-  static_assert(S == 32, "two 16-column walk slices per item");
   using PR = Prec<MODE>;
   using PKq = PolicyKinds<PR::exact>;   // K x Q^T
   using PKh = PolicyKinds<PR::hq>;      // h^T x Q^T
   using PKv = PolicyKinds<PR::pv>;      // V'^T x P^T
   static_assert(PKq::b == PKh::b, "one query fragment serves both products");
-  using OB = OutBuf<C, TI>;
+  using OL = OutLds<C, TI>;
   constexpr bool F32 = sizeof(TI) == 4;
-  constexpr int R = C / 16;               // query-row tiles
-  constexpr int RU = R / 4;               // row tiles per wave
-  constexpr int NS = D / S;
-  constexpr int MH = D / 16, MV = C / 16;
-  static_assert(R % 4 == 0 && OB::NBLK % 4 == 0, "work split");
-  __shared__ __align__(16) char buf[OB::BYTES];
+  constexpr int R = C / 16;              // query-row tiles
+  constexpr int RU = R >= 8 ? 2 : 1;     // phase-A row tiles per wave
+  constexpr int MH = D / 16, MV = C / 16, KBD = D / 32, KBC = C / 32;
+  static_assert(R == 4 * RU, "phase A: R/4 row tiles per wave");
+  static_assert(!PR::split_store || (PKh::a == F_SPLIT && PKv::a == F_SPLIT), "split planes feed split operands");
+  __shared__ __align__(16) char lds[OL::BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, g = lane >> 4, lq = g * 4;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  const int rp = wv;   // row tiles rp and R-1-rp
-  const int units = a.nn * a.B * a.Hv, items = units * NS;
+  const int unit = blockIdx.x;
+  const size_t bh = (size_t)(unit / a.nn);
+  const int n = a.n0 + unit % a.nn;
+  const int b = (int)(bh / a.Hv), hv = (int)(bh % a.Hv);
+  const int hq = hv / (a.Hv / a.Hqk);
+  const size_t cb = bh * a.N + n;
+  const size_t tok0 = (size_t)b * a.T + (size_t)n * C;   // first token of the chunk
+  const float *Gs = reinterpret_cast<const float *>(lds + OL::GOFF);
 
-  struct Item {
-    size_t bh, cb;
-    int b, hv, hq, n, slice;
-  };
-  auto item_of = [&](int it) {
-    Item x;
-    int unit;
-    xcd_unit(it, NS, units, unit, x.slice);
-    x.bh = (size_t)(unit / a.nn);
-    x.n = a.n0 + unit % a.nn;
-    x.b = (int)(x.bh / a.Hv);
-    x.hv = (int)(x.bh % a.Hv);
-    x.hq = x.hv / (a.Hv / a.Hqk);
-    x.cb = x.bh * a.N + x.n;
-    return x;
-  };
-  // copy one item's operands into an LDS buffer; wave w takes every 4th block
-  auto stage = [&](char *buf, const Item &x) {
-    const char *kg = reinterpret_cast<const char *>(a.k) +
-                     ((((size_t)x.b * a.T + (size_t)x.n * C) * a.Hqk + x.hq) * D) * sizeof(TI);
+  // K tile and G into LDS
+  {
+    const char *kg = reinterpret_cast<const char *>(a.k) + ((tok0 * a.Hqk + hq) * D) * sizeof(TI);
     const size_t krow = (size_t)a.Hqk * D * sizeof(TI);   // bytes between tokens
-    const char *hg = reinterpret_cast<const char *>(a.Hs + (x.cb * NS + x.slice) * (size_t)(D * S));
-    const char *vg = reinterpret_cast<const char *>(a.Vn + (x.cb * NS + x.slice) * (size_t)(C * S));
     using LDSP = __attribute__((address_space(3))) void *;
-    // K: block j holds pieces p = 64 j + lane of the swizzled tile
 #pragma unroll
-    for (int jj = 0; jj < OB::KB / 4096; ++jj) {
-      const int j = jj * 4 + wv;
-      const int p = j * 64 + lane, r = p / OB::RP, c = (p % OB::RP) ^ (r & 15);
-      __builtin_amdgcn_global_load_lds((const void *)(kg + r * krow + c * 16), (LDSP)(buf + j * 1024), 16, 0, 0);
-    }
-#pragma unroll
-    for (int jj = 0; jj < OB::HB / 4096; ++jj) {
-      const int j = jj * 4 + wv;
-      __builtin_amdgcn_global_load_lds((const void *)(hg + j * 1024 + lane * 16), (LDSP)(buf + OB::HOFF + j * 1024),
-                                       16, 0, 0);
-    }
-#pragma unroll
-    for (int jj = 0; jj < OB::VB / 4096; ++jj) {
-      const int j = jj * 4 + wv;
-      __builtin_amdgcn_global_load_lds((const void *)(vg + j * 1024 + lane * 16), (LDSP)(buf + OB::VOFF + j * 1024),
-                                       16, 0, 0);
+    for (int jj = 0; jj < OL::KB / 4096; ++jj) {
+      const int j = jj * 4 + wv;   // 1 KB block: pieces 64 j + lane of the swizzled tile
+      const int p = j * 64 + lane, r = p / OL::RP, c = (p % OL::RP) ^ (r & 15);
+      __builtin_amdgcn_global_load_lds((const void *)(kg + r * krow + c * 16), (LDSP)(lds + j * 1024), 16, 0, 0);
     }
     if (wv == 3 && lane < C / 4)
-      __builtin_amdgcn_global_load_lds((const void *)(a.G + x.cb * C + lane * 4),
-                                       (__attribute__((address_space(3))) void *)(buf + OB::GOFF), 16, 0, 0);
-    asm volatile("" ::: "memory");
-  };
-  // query fragments of this wave's row tiles, k order kk(g, j)
-  struct Qf {
-    Frag<PKq::b> f[RU][D / 32];
-  };
-  auto load_q = [&](const Item &x, Qf &q) {
+      __builtin_amdgcn_global_load_lds((const void *)(a.G + cb * C + lane * 4), (LDSP)(lds + OL::GOFF), 16, 0, 0);
+  }
+  // query fragments of one row tile, k order kk(g, j)
+  using QF = Frag<PKq::b>;
+  auto load_q = [&](int rt, QF (&q)[KBD]) {
+    const TI *qrow = reinterpret_cast<const TI *>(a.q) + ((tok0 + 16 * rt + lr) * a.Hqk + hq) * D;
 #pragma unroll
-    for (int u = 0; u < RU; ++u) {
-      const int rt = u == 0 ? rp : R - 1 - rp;
-      const TI *qrow = reinterpret_cast<const TI *>(a.q) +
-                       (((size_t)x.b * a.T + (size_t)x.n * C + 16 * rt + lr) * a.Hqk + x.hq) * D;
+    for (int kb = 0; kb < KBD; ++kb) {
+      TI t[8];
+      if constexpr (F32) {
+        *reinterpret_cast<float4 *>(t) = *reinterpret_cast<const float4 *>(qrow + 32 * kb + 4 * g);
+        *reinterpret_cast<float4 *>(t + 4) = *reinterpret_cast<const float4 *>(qrow + 32 * kb + 16 + 4 * g);
+      } else {
+        *reinterpret_cast<uint2 *>(t) = *reinterpret_cast<const uint2 *>(qrow + 32 * kb + 4 * g);
+        *reinterpret_cast<uint2 *>(t + 4) = *reinterpret_cast<const uint2 *>(qrow + 32 * kb + 16 + 4 * g);
+      }
+      if constexpr (PKq::b == F_BF16) {
+        q[kb].hi = *reinterpret_cast<const bf16x8 *>(t);
+      } else {
+        float x8[8];
 #pragma unroll
-      for (int kb = 0; kb < D / 32; ++kb) {
-        TI t[8];
-        if constexpr (F32) {
-          *reinterpret_cast<float4 *>(t) = *reinterpret_cast<const float4 *>(qrow + 32 * kb + 4 * g);
-          *reinterpret_cast<float4 *>(t + 4) = *reinterpret_cast<const float4 *>(qrow + 32 * kb + 16 + 4 * g);
-        } else {
-          *reinterpret_cast<uint2 *>(t) = *reinterpret_cast<const uint2 *>(qrow + 32 * kb + 4 * g);
-          *reinterpret_cast<uint2 *>(t + 4) = *reinterpret_cast<const uint2 *>(qrow + 32 * kb + 16 + 4 * g);
-        }
-        if constexpr (PKq::b == F_BF16) {
-          q.f[u][kb].hi = *reinterpret_cast<const bf16x8 *>(t);
-        } else {
-          float x8[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) x8[j] = to_f32(t[j]);
-          q.f[u][kb] = make_frag<PKq::b>(x8);
-        }
+        for (int j = 0; j < 8; ++j) x8[j] = to_f32(t[j]);
+        q[kb] = make_frag<PKq::b>(x8);
       }
     }
   };
-  auto chunk_barrier = [&]() {
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-    __builtin_amdgcn_s_barrier();
-  };
+  QF qa[RU][KBD];
+#pragma unroll
+  for (int u = 0; u < RU; ++u) load_q(u == 0 ? wv : R - 1 - wv, qa[u]);
+  // phase-B operands of this wave's columns: h^T (2 column tiles x KBD) and
+  // V'^T (2 x KBC) fragments, as stored by the walk; issued last, they arrive
+  // during phase A (two 16-byte loads per fragment)
+  constexpr int NLATE = 2 * (2 * KBD + 2 * KBC);
+  static_assert(NLATE <= 63, "memory counter range");
+  Frag<PKh::a> hf[2][KBD];
+  Frag<PKv::a> vf[2][KBC];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const int s = 2 * wv + ct;   // walk slice
+    const float *hs = a.Hs + (cb * (D / 16) + s) * MH * 256;
+    const float *vs = a.Vn + (cb * (D / 16) + s) * MV * 256;
+#pragma unroll
+    for (int kb = 0; kb < KBD; ++kb) {
+      if constexpr (PR::split_store) {
+        hf[ct][kb].hi = *reinterpret_cast<const bf16x8 *>(hs + ((2 * kb) * 64 + lane) * 4);
+        hf[ct][kb].lo = *reinterpret_cast<const bf16x8 *>(hs + ((2 * kb + 1) * 64 + lane) * 4);
+      } else {
+        const float4 x0 = *reinterpret_cast<const float4 *>(hs + ((2 * kb) * 64 + lane) * 4);
+        const float4 x1 = *reinterpret_cast<const float4 *>(hs + ((2 * kb + 1) * 64 + lane) * 4);
+        const float x8[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        hf[ct][kb] = make_frag<PKh::a>(x8);
+      }
+    }
+#pragma unroll
+    for (int kp = 0; kp < KBC; ++kp) {
+      if constexpr (PR::split_store) {
+        vf[ct][kp].hi = *reinterpret_cast<const bf16x8 *>(vs + ((2 * kp) * 64 + lane) * 4);
+        vf[ct][kp].lo = *reinterpret_cast<const bf16x8 *>(vs + ((2 * kp + 1) * 64 + lane) * 4);
+      } else {
+        const float4 x0 = *reinterpret_cast<const float4 *>(vs + ((2 * kp) * 64 + lane) * 4);
+        const float4 x1 = *reinterpret_cast<const float4 *>(vs + ((2 * kp + 1) * 64 + lane) * 4);
+        const float x8[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        vf[ct][kp] = make_frag<PKv::a>(x8);
+      }
+    }
+  }
+  // the K tile and G copies (issued first) done in every wave; the phase-B
+  // loads may still be in flight
+  __builtin_amdgcn_s_waitcnt((NLATE & 15) | ((NLATE >> 4) << 14) | (0x7 << 4) | (0xF << 8));   // vmcnt(NLATE)
+  __builtin_amdgcn_s_barrier();
 
   // this lane's byte offsets of its K fragment halves within a 16-row key
   // tile: row lr, piece c = (32kb + 16hh + 4g) * size / 16 stored at c ^ lr
-  int koff[D / 32][2];
+  int koff[KBD][2];
 #pragma unroll
-  for (int kb = 0; kb < D / 32; ++kb)
+  for (int kb = 0; kb < KBD; ++kb)
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       const int k = 32 * kb + 16 * hh + 4 * g;
       const int c = k * (int)sizeof(TI) / 16, off = (k * (int)sizeof(TI)) % 16;
-      koff[kb][hh] = lr * OB::RP * 16 + ((c ^ lr) * 16) + off;
+      koff[kb][hh] = lr * OL::RP * 16 + ((c ^ lr) * 16) + off;
     }
-  auto compute = [&](const char *buf, const Item &x, const Qf &q) {
-    const float *Gs = reinterpret_cast<const float *>(buf + OB::GOFF);
-    const float *Hs = reinterpret_cast<const float *>(buf + OB::HOFF);
-    const float *Vs = reinterpret_cast<const float *>(buf + OB::VOFF);
-    TO *og = reinterpret_cast<TO *>(a.o);
+
+  // ---- phase A: P^T fragments into LDS ----
 #pragma unroll
-    for (int u = 0; u < RU; ++u) {
-      const int rt = u == 0 ? rp : R - 1 - rp;
-      const int r = 16 * rt + lr;   // this lane's query row (result column)
-      const float Gr = Gs[r] * LOG2E;
-      f32x4 acc1[2], acc2[2];
+  for (int u = 0; u < RU; ++u) {
+    const int rt = u == 0 ? wv : R - 1 - wv;
+    const int r = 16 * rt + lr;   // this lane's query row (result column)
+    const float Gr = Gs[r] * LOG2E;
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) acc1[ct] = acc2[ct] = zero4();
-      // h^T Q^T: A = h^T rows c, k = state rows 32kb + kk(g, j): tiles 2kb, 2kb+1
-      // (all fragments read before the first product: one LDS wait)
+    for (int kp = 0; kp < R / 2; ++kp) {
+      if (2 * kp > rt) continue;
+      const bool two = 2 * kp + 1 <= rt;
+      Frag<PKq::a> kf[2][KBD];
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        if constexpr (PR::split_store) {
-          // stored as hi/lo planes: the operand fragments as they are
-          static_assert(PKh::a == F_SPLIT, "split planes feed a split operand");
-          Frag<F_SPLIT> hf[D / 32];
-          const char *hb = reinterpret_cast<const char *>(Hs) + ct * MH * 1024 + lane * 16;
+      for (int t = 0; t < 2; ++t) {
+        const char *tile = lds + (32 * kp + 16 * t) * OL::RP * 16;   // key rows 32kp + 16t ..
 #pragma unroll
-          for (int kb = 0; kb < D / 32; ++kb) {
-            hf[kb].hi = *reinterpret_cast<const bf16x8 *>(hb + (2 * kb) * 1024);
-            hf[kb].lo = *reinterpret_cast<const bf16x8 *>(hb + (2 * kb + 1) * 1024);
-          }
-          __builtin_amdgcn_sched_barrier(0);
+        for (int kb = 0; kb < KBD; ++kb) {
+          if constexpr (!F32 && PKq::a == F_BF16) {
+            const uint2 w0 = *reinterpret_cast<const uint2 *>(tile + koff[kb][0]);
+            const uint2 w1 = *reinterpret_cast<const uint2 *>(tile + koff[kb][1]);
+            kf[t][kb].hi = __builtin_bit_cast(bf16x8, uint4{w0.x, w0.y, w1.x, w1.y});
+          } else {
+            float x8[8];
 #pragma unroll
-          for (int kb = 0; kb < D / 32; ++kb) mma(acc1[ct], hf[kb], q.f[u][kb]);
-        } else {
-          float4 hv[D / 16];
-#pragma unroll
-          for (int m = 0; m < D / 16; ++m) hv[m] = *reinterpret_cast<const float4 *>(Hs + ((ct * MH + m) * 64 + lane) * 4);
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int kb = 0; kb < D / 32; ++kb) {
-            const float4 h0 = hv[2 * kb], h1 = hv[2 * kb + 1];
-            const float x8[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
-            mma(acc1[ct], make_frag<PKh::a>(x8), q.f[u][kb]);
-          }
-        }
-      }
-      // key blocks of 32: P^T tiles (2kp, 2kp+1) formed and consumed at once.
-      // Each block's LDS operands (K fragments, V' fragments, G) are read
-      // together ahead of its products: one LDS wait per block.
-#pragma unroll
-      for (int kp = 0; kp < R / 2; ++kp) {
-        if (2 * kp <= rt) {
-          const bool two = 2 * kp + 1 <= rt;
-          Frag<PKq::a> kf[2][D / 32];
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const char *tile = buf + (32 * kp + 16 * t) * OB::RP * 16;   // key rows 32kp + 16t ..
-#pragma unroll
-            for (int kb = 0; kb < D / 32; ++kb) {
-              if constexpr (!F32 && PKq::a == F_BF16) {
-                const uint2 w0 = *reinterpret_cast<const uint2 *>(tile + koff[kb][0]);
-                const uint2 w1 = *reinterpret_cast<const uint2 *>(tile + koff[kb][1]);
-                kf[t][kb].hi = __builtin_bit_cast(bf16x8, uint4{w0.x, w0.y, w1.x, w1.y});
+            for (int hh = 0; hh < 2; ++hh) {
+              if constexpr (F32) {
+                const float4 v4 = *reinterpret_cast<const float4 *>(tile + koff[kb][hh]);
+                x8[4 * hh] = v4.x; x8[4 * hh + 1] = v4.y; x8[4 * hh + 2] = v4.z; x8[4 * hh + 3] = v4.w;
               } else {
-                float x8[8];
+                const uint2 v2 = *reinterpret_cast<const uint2 *>(tile + koff[kb][hh]);
+                const __bf16 *e = reinterpret_cast<const __bf16 *>(&v2);
 #pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                  if constexpr (F32) {
-                    const float4 v4 = *reinterpret_cast<const float4 *>(tile + koff[kb][hh]);
-                    x8[4 * hh] = v4.x; x8[4 * hh + 1] = v4.y; x8[4 * hh + 2] = v4.z; x8[4 * hh + 3] = v4.w;
-                  } else {
-                    const uint2 v2 = *reinterpret_cast<const uint2 *>(tile + koff[kb][hh]);
-                    const __bf16 *e = reinterpret_cast<const __bf16 *>(&v2);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) x8[4 * hh + j] = (float)e[j];
-                  }
-                }
-                kf[t][kb] = make_frag<PKq::a>(x8);
+                for (int j = 0; j < 4; ++j) x8[4 * hh + j] = (float)e[j];
               }
             }
-          }
-          // V'^T fragments of the key block: (hi, lo) planes or two fp32 tiles
-          float4 v0[2], v1[2];
-#pragma unroll
-          for (int ct = 0; ct < 2; ++ct) {
-            v0[ct] = *reinterpret_cast<const float4 *>(Vs + ((ct * MV + 2 * kp) * 64 + lane) * 4);
-            v1[ct] = *reinterpret_cast<const float4 *>(Vs + ((ct * MV + 2 * kp + 1) * 64 + lane) * 4);
-          }
-          const float4 gk0 = *reinterpret_cast<const float4 *>(Gs + 32 * kp + lq);
-          const float4 gk1 = *reinterpret_cast<const float4 *>(Gs + 32 * kp + 16 + lq);
-          __builtin_amdgcn_sched_barrier(0);
-          f32x4 p0 = zero4(), p1 = zero4();
-#pragma unroll
-          for (int kb = 0; kb < D / 32; ++kb) {
-            mma(p0, kf[0][kb], q.f[u][kb]);
-            if (two) mma(p1, kf[1][kb], q.f[u][kb]);
-          }
-          const float g0[4] = {gk0.x, gk0.y, gk0.z, gk0.w}, g1[4] = {gk1.x, gk1.y, gk1.z, gk1.w};
-          float b8[8];
-          if (2 * kp + 1 < rt) {
-            // both key tiles wholly before this query tile: no mask
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              b8[i] = p0[i] * exp2_fast(Gr - g0[i] * LOG2E);
-              b8[4 + i] = p1[i] * exp2_fast(Gr - g1[i] * LOG2E);
-            }
-          } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int k0i = 32 * kp + lq + i, k1i = k0i + 16;
-              b8[i] = k0i <= r ? p0[i] * exp2_fast(Gr - g0[i] * LOG2E) : 0.f;
-              b8[4 + i] = (two && k1i <= r) ? p1[i] * exp2_fast(Gr - g1[i] * LOG2E) : 0.f;
-            }
-          }
-          const auto bf = make_frag<PKv::b>(b8);
-#pragma unroll
-          for (int ct = 0; ct < 2; ++ct) {
-            if constexpr (PR::split_store) {
-              static_assert(PKv::a == F_SPLIT, "split planes feed a split operand");
-              Frag<F_SPLIT> vf;
-              vf.hi = __builtin_bit_cast(bf16x8, v0[ct]);
-              vf.lo = __builtin_bit_cast(bf16x8, v1[ct]);
-              mma(acc2[ct], vf, bf);
-            } else {
-              const float a8[8] = {v0[ct].x, v0[ct].y, v0[ct].z, v0[ct].w, v1[ct].x, v1[ct].y, v1[ct].z, v1[ct].w};
-              mma(acc2[ct], make_frag<PKv::a>(a8), bf);
-            }
+            kf[t][kb] = make_frag<PKq::a>(x8);
           }
         }
       }
-      const float er = exp2_fast(Gr);
+      const float4 gk0 = *reinterpret_cast<const float4 *>(Gs + 32 * kp + lq);
+      const float4 gk1 = *reinterpret_cast<const float4 *>(Gs + 32 * kp + 16 + lq);
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4 p0 = zero4(), p1 = zero4();
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        // lane holds O^T[c = 16ct + 4g + i][r]
-        TO *dst = og + (((size_t)x.b * a.T + (size_t)x.n * C + r) * a.Hv + x.hv) * D + x.slice * S + 16 * ct + lq;
-        if constexpr (sizeof(TO) == 4) {
-          *reinterpret_cast<float4 *>(dst) = float4{er * acc1[ct][0] + acc2[ct][0], er * acc1[ct][1] + acc2[ct][1],
-                                                    er * acc1[ct][2] + acc2[ct][2], er * acc1[ct][3] + acc2[ct][3]};
-        } else {
+      for (int kb = 0; kb < KBD; ++kb) {
+        mma(p0, kf[0][kb], qa[u][kb]);
+        if (two) mma(p1, kf[1][kb], qa[u][kb]);
+      }
+      const float g0[4] = {gk0.x, gk0.y, gk0.z, gk0.w}, g1[4] = {gk1.x, gk1.y, gk1.z, gk1.w};
+      float b8[8];
+      if (2 * kp + 1 < rt) {
+        // both key tiles wholly before this query tile: no mask
 #pragma unroll
-          for (int i = 0; i < 4; ++i) dst[i] = from_f32<TO>(er * acc1[ct][i] + acc2[ct][i]);
+        for (int i = 0; i < 4; ++i) {
+          b8[i] = p0[i] * exp2_fast(Gr - g0[i] * LOG2E);
+          b8[4 + i] = p1[i] * exp2_fast(Gr - g1[i] * LOG2E);
         }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int k0i = 32 * kp + lq + i, k1i = k0i + 16;
+          b8[i] = k0i <= r ? p0[i] * exp2_fast(Gr - g0[i] * LOG2E) : 0.f;
+          b8[4 + i] = (two && k1i <= r) ? p1[i] * exp2_fast(Gr - g1[i] * LOG2E) : 0.f;
+        }
+      }
+      // the B-operand fragment (hi, lo planes; or 8 fp32 in two halves)
+      char *pf = lds + OL::POFF + (OL::pbase(rt) + kp) * 2048 + lane * 16;
+      const auto bf = make_frag<PKv::b>(b8);
+      if constexpr (PKv::b == F_SPLIT) {
+        *reinterpret_cast<bf16x8 *>(pf) = bf.hi;
+        *reinterpret_cast<bf16x8 *>(pf + 1024) = bf.lo;
+      } else {
+        *reinterpret_cast<float4 *>(pf) = float4{bf.v[0], bf.v[1], bf.v[2], bf.v[3]};
+        *reinterpret_cast<float4 *>(pf + 1024) = float4{bf.v[4], bf.v[5], bf.v[6], bf.v[7]};
+      }
+    }
+  }
+  lds_barrier();
+
+  // ---- phase B: this wave's 32 columns for every query tile ----
+  TO *og = reinterpret_cast<TO *>(a.o);
+  QF qb[2][KBD];
+  load_q(0, qb[0]);
+  auto tile_out = [&](int rt, const QF (&q)[KBD]) {
+    const int r = 16 * rt + lr;
+    f32x4 acc1[2], acc2[2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) acc1[ct] = acc2[ct] = zero4();
+#pragma unroll
+    for (int kb = 0; kb < KBD; ++kb)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) mma(acc1[ct], hf[ct][kb], q[kb]);
+#pragma unroll
+    for (int kp = 0; kp < KBC; ++kp) {
+      if (2 * kp > rt) continue;
+      const char *pf = lds + OL::POFF + (OL::pbase(rt) + kp) * 2048 + lane * 16;
+      Frag<PKv::b> bf;
+      if constexpr (PKv::b == F_SPLIT) {
+        bf.hi = *reinterpret_cast<const bf16x8 *>(pf);
+        bf.lo = *reinterpret_cast<const bf16x8 *>(pf + 1024);
+      } else {
+        const float4 x0 = *reinterpret_cast<const float4 *>(pf), x1 = *reinterpret_cast<const float4 *>(pf + 1024);
+        bf.v[0] = x0.x; bf.v[1] = x0.y; bf.v[2] = x0.z; bf.v[3] = x0.w;
+        bf.v[4] = x1.x; bf.v[5] = x1.y; bf.v[6] = x1.z; bf.v[7] = x1.w;
+      }
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) mma(acc2[ct], vf[ct][kp], bf);
+    }
+    const float er = exp2_fast(Gs[r] * LOG2E);
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      // lane holds O^T[c = 32w + 16ct + 4g + i][r]
+      TO *dst = og + ((tok0 + r) * a.Hv + hv) * D + 32 * wv + 16 * ct + lq;
+      if constexpr (sizeof(TO) == 4) {
+        *reinterpret_cast<float4 *>(dst) = float4{er * acc1[ct][0] + acc2[ct][0], er * acc1[ct][1] + acc2[ct][1],
+                                                  er * acc1[ct][2] + acc2[ct][2], er * acc1[ct][3] + acc2[ct][3]};
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[i] = from_f32<TO>(er * acc1[ct][i] + acc2[ct][i]);
       }
     }
   };
-
-  // one item per workgroup; two workgroups share a compute unit, so one
-  // copies while the other computes
-  const Item x = item_of(blockIdx.x);
-  Qf q;
-  stage(buf, x);
-  load_q(x, q);
-  chunk_barrier();
-  compute(buf, x, q);
+  // query tiles two at a time, the next tile's queries in flight (unrolled,
+  // so that each wait covers exactly the loads it needs)
+#pragma unroll
+  for (int rt = 0; rt < R; rt += 2) {
+    load_q(rt + 1, qb[1]);
+    __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the tile
+    tile_out(rt, qb[0]);
+    if (rt + 2 < R) load_q(rt + 2, qb[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    tile_out(rt + 1, qb[1]);
+  }
 }
 
 }  // namespace gdn
