@@ -71,7 +71,7 @@ template <> struct LdPad<float> { static constexpr int v = 4; };
 constexpr int MODE_BF16 = 0, MODE_F32 = 1;
 template <int MODE> struct Prec {
   static constexpr int exact = MODE == MODE_F32 ? P_F32 : P_BF16;       // bf16 data x bf16 data
-  static constexpr int ladder = MODE == MODE_F32 ? P_F32 : P_SPLIT_AB;
+  static constexpr int ladder = P_F32;                                    // fp32 x fp32, no operand splitting
   static constexpr int wy = MODE == MODE_F32 ? P_F32 : P_SPLIT_A;       // T' (fp32) x K/V (data)
   static constexpr int wh = MODE == MODE_F32 ? P_F32 : P_BF16;          // W x h
   static constexpr int kv = MODE == MODE_F32 ? P_F32 : P_SPLIT_B;       // K^T (data) x V'
@@ -426,7 +426,8 @@ __global__ __launch_bounds__(NT, 2) void prep_kernel(FwdArgs a) {
 
   const int n = a.n0 + blockIdx.x, hv = blockIdx.y, b = blockIdx.z;
   const int hq = hv / (a.Hv / a.Hqk);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // (the wave index as a scalar: tests on a wave's row tiles are uniform branches)
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, g = lane >> 4, lk = g * 8, lq = g * 4;
   const size_t bh = (size_t)b * a.Hv + hv;
   const size_t t0 = (size_t)n * C;
