@@ -213,6 +213,8 @@ template <int C> struct Tri {
     const int m = r >> 4;
     return base(m) + (r & 15) * (len(m) + 4) + c;
   }
+  // row rr (0..15) of row tile m, column c; m usually wave-uniform
+  __device__ static int at_t(int m, int rr, int c) { return base(m) + rr * (len(m) + 4) + c; }
 };
 
 // Transposed input tile X^T [D][C] in LDS, unpadded.  The 16-byte blocks of
@@ -221,9 +223,11 @@ template <int C> struct Tri {
 template <int C, typename TI> struct XT {
   static constexpr int VE = 16 / (int)sizeof(TI);   // elements per 16-byte block
   static constexpr int NB = C / VE;                  // blocks per row
+  __device__ static int swz(int d) { return (d ^ (d >> 3)) & (NB - 1); }
   __device__ static int at(int d, int k) {           // k a multiple of VE
-    return d * C + (((k / VE) ^ ((d ^ (d >> 3)) & (NB - 1))) * VE);
+    return d * C + (((k / VE) ^ swz(d)) * VE);
   }
+  __device__ static int at(int d, int k, int sw) { return d * C + (((k / VE) ^ sw) * VE); }
 };
 
 // One thread's block of the input tile: rows 8 rb .. 8 rb + 7, columns
@@ -293,9 +297,9 @@ template <int C, typename TI> struct TileBlock {
 
 // operand fragment of X^T: row d, k-values k0 .. k0 + 7
 template <int K, int C, typename TI>
-__device__ __forceinline__ Frag<K> xt_frag(const TI *sxt, int d, int k0) {
+__device__ __forceinline__ Frag<K> xt_frag(const TI *sxt, int d, int k0, int sw) {
   if constexpr (sizeof(TI) == 2) {
-    const bf16x8 u = *reinterpret_cast<const bf16x8 *>(sxt + XT<C, TI>::at(d, k0));
+    const bf16x8 u = *reinterpret_cast<const bf16x8 *>(sxt + XT<C, TI>::at(d, k0, sw));
     if constexpr (K == F_BF16) {
       Frag<K> f;
       f.hi = u;
@@ -307,8 +311,8 @@ __device__ __forceinline__ Frag<K> xt_frag(const TI *sxt, int d, int k0) {
       return make_frag<K>(x);
     }
   } else {
-    const float4 u0 = *reinterpret_cast<const float4 *>(sxt + XT<C, TI>::at(d, k0));
-    const float4 u1 = *reinterpret_cast<const float4 *>(sxt + XT<C, TI>::at(d, k0 + 4));
+    const float4 u0 = *reinterpret_cast<const float4 *>(sxt + XT<C, TI>::at(d, k0, sw));
+    const float4 u1 = *reinterpret_cast<const float4 *>(sxt + XT<C, TI>::at(d, k0 + 4, sw));
     float x[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
     return make_frag<K>(x);
   }
@@ -341,10 +345,11 @@ __device__ __forceinline__ void ladder_level(float *sT, float *sM, int wave, int
       for (int kb = 0; kb < KBM; ++kb) {
         const int k0 = 32 * kb + lk;
         if (tt < NTILE && kb >= kb0 && k0 < BS) {
-          ld8(sT + TRI::at(s + BS + 16 * mi + lr, s + k0), a8[v][kb]);
+          ld8(sT + TRI::at_t((s + BS) / 16 + mi, lr, s + k0), a8[v][kb]);
           // column s + 16 ni + lr of X_P, rows s + k0 .. + 7 (one row tile)
-          const float *col = sT + TRI::at(s + k0, s + 16 * ni + lr);
-          const int str = TRI::len((s + k0) >> 4) + 4;
+          const int mk = (s + 32 * kb) / 16 + (lane >> 5);
+          const float *col = sT + TRI::at_t(mk, lk & 15, s + 16 * ni + lr);
+          const int str = TRI::len(mk) + 4;
 #pragma unroll
           for (int j = 0; j < 8; ++j) b8[v][kb][j] = col[j * str];
         } else {
@@ -382,7 +387,7 @@ __device__ __forceinline__ void ladder_level(float *sT, float *sM, int wave, int
       for (int kb = 0; kb < KBM; ++kb) {
         const int k0 = 32 * kb + lk;
         if (tt < NTILE && kb * 32 < 16 * (mi + 1) && k0 < BS) {
-          ld8(sT + TRI::at(s + BS + 16 * mi + lr, s + BS + k0), a8[v][kb]);
+          ld8(sT + TRI::at_t((s + BS) / 16 + mi, lr, s + BS + k0), a8[v][kb]);
           ld8(M + (16 * ni + lr) * LDM + k0, b8[v][kb]);
         } else {
 #pragma unroll
@@ -398,9 +403,11 @@ __device__ __forceinline__ void ladder_level(float *sT, float *sM, int wave, int
 #pragma unroll
       for (int kb = 0; kb < KBM; ++kb) mma_k32<PL>(acc, a8[v][kb], b8[v][kb]);
       const int blk = tt / (TB * TB), ti = tt % (TB * TB), mi = ti / TB, ni = ti % TB;
-      const int s = blk * 2 * BS;
+      const int s = blk * 2 * BS, mr = (s + BS) / 16 + mi;
+      float *rp = sT + TRI::at_t(mr, lq, s + 16 * ni + lr);
+      const int rstr = TRI::len(mr) + 4;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sT[TRI::at(s + BS + 16 * mi + lq + i, s + 16 * ni + lr)] = -acc[i];
+      for (int i = 0; i < 4; ++i) rp[i * rstr] = -acc[i];
     }
   }
   lds_barrier();
@@ -495,15 +502,22 @@ __global__ __launch_bounds__(NT, 2) void prep_kernel(FwdArgs a) {
     }
 #pragma unroll
     for (int u = 0; u < RU; ++u) {
+      // per-row terms once (this lane's rows r = 16m + lq + i), then per column
       const int m = mrow[u], L = TRI::len(m);
+      const float4 br = *reinterpret_cast<const float4 *>(sBeta + 16 * m + lq);
+      const float4 gr = *reinterpret_cast<const float4 *>(sG2 + 16 * m + lq);
+      const float brv[4] = {br.x, br.y, br.z, br.w}, grv[4] = {gr.x, gr.y, gr.z, gr.w};
+      float *rowp = sT + TRI::at(16 * m + lq, lr);   // row 16m + lq, column lr
+      const int rstr = L + 4;                         // row stride of this row tile
 #pragma unroll
       for (int ni = 0; ni < TC; ++ni) {
-        const int c = 16 * ni + lr;
         if (16 * ni < L) {
+          const int c = 16 * ni + lr;
+          const float gc = sG2[c];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = 16 * m + lq + i;
-            sT[TRI::at(r, c)] = (c < r) ? sBeta[r] * exp2_fast(sG2[r] - sG2[c]) * acc[u][ni][i] : 0.f;
+            rowp[i * rstr + 16 * ni] = (c < r) ? brv[i] * exp2_fast(grv[i] - gc) * acc[u][ni][i] : 0.f;
           }
         }
       }
@@ -588,6 +602,10 @@ __global__ __launch_bounds__(NT, 2) void prep_kernel(FwdArgs a) {
   // needs k < 16(m+1).  The T fragments of k-blocks past the diagonal read
   // T's zero-filled or neighbouring entries and their products are skipped.
   constexpr int TD = D / 16;
+  // swizzle term of this lane's X^T rows 16md + lr
+  int xsw[TD];
+#pragma unroll
+  for (int md = 0; md < TD; ++md) xsw[md] = XT<C, TI>::swz(16 * md + lr);
   constexpr int KT = PolicyKinds<PR::wy>::a;   // T' fragments (split)
   constexpr int KX = PolicyKinds<PR::wy>::b;   // K / V fragments (exact data)
   for (int pass = 0; pass < 2; ++pass) {
@@ -619,7 +637,7 @@ __global__ __launch_bounds__(NT, 2) void prep_kernel(FwdArgs a) {
       }
 #pragma unroll
       for (int md = 0; md < TD; ++md) {
-        const auto xf = xt_frag<KX, C, TI>(sX, 16 * md + lr, k0);   // X^T row 16md+lr = column of K (or V)
+        const auto xf = xt_frag<KX, C, TI>(sX, 16 * md + lr, k0, xsw[md]);   // X^T row 16md+lr = column of K (or V)
 #pragma unroll
         for (int u = 0; u < RU; ++u) {
           if (!live[u]) continue;
