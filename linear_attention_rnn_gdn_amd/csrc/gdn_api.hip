@@ -32,7 +32,7 @@ Layout layout(const gdn_shape &s) {
   L.W = off;  off += align_up(BH * N * C * D * in_bytes);
   L.Kt = off; off += align_up(BH * N * C * D * in_bytes);
   L.U = off;  off += align_up(BH * N * C * D * 4);
-  L.Hs = off; off += align_up(BH * N * D * D * 4);
+  L.Hs = off; off += align_up(BH * N * D * D * 4);   // fp32, or bf16 hi + lo planes
   L.Vn = off; off += align_up(BH * N * C * D * 4);
   if (J > 1) {
     L.A = off;   off += align_up(BH * J * D * D * 4);

@@ -47,7 +47,9 @@
 //   Uf  [cb][C/16][D/16][64][4]  U[16m + 4g + i][16nd + lr], fp32
 //   Hsf [cb][D/16][D/16][64][4]  chunk-start state h[16m + 4g + i][16s + lr]
 //   Vnf [cb][D/16][C/16][64][4]  corrected values V'[16m + 4g + i][16s + lr]
-// (s = the 16-column slice.)  Decays are evaluated as exp2 of log2-scaled
+// (s = the 16-column slice.)  Hsf and Vnf are fp32 for fp32 inputs.  For bf16
+// inputs they hold operand fragments -- element j of lane l from tile 2p + j/4,
+// row 4g + j%4 -- as a bf16 high and a bf16 low plane, [cb][D/16][rows/32][2][64][8].  Decays are evaluated as exp2 of log2-scaled
 // cumsums (one v_exp_f32 each).
 //
 // Workgroups are numbered 1-D.  The hardware places workgroup i on XCD i % 8;
@@ -67,6 +69,9 @@ constexpr int WALK = 0, FOLD = 1;
 template <typename TI> struct LdPad { static constexpr int v = 8; };
 template <> struct LdPad<float> { static constexpr int v = 4; };
 
+// Forms of a tensor handed from the walk to the output stage.
+enum : int { ST_F32 = 0, ST_SPLIT = 1, ST_BF16 = 2 };
+
 // Product precision per input precision: MODE_BF16 (bf16 q/k/v) or MODE_F32.
 constexpr int MODE_BF16 = 0, MODE_F32 = 1;
 template <int MODE> struct Prec {
@@ -77,8 +82,13 @@ template <int MODE> struct Prec {
   static constexpr int kv = MODE == MODE_F32 ? P_F32 : P_SPLIT_B;       // K^T (data) x V'
   static constexpr int hq = MODE == MODE_F32 ? P_F32 : P_SPLIT_A;       // h^T x Q^T (data)
   static constexpr int pv = MODE == MODE_F32 ? P_F32 : P_SPLIT_AB;      // V'^T x P^T
-  // h and V' are handed to the output stage as hi/lo bf16 planes
-  static constexpr bool split_store = MODE == MODE_BF16;
+  // How h and V' are handed to the output stage (the walk keeps its state in
+  // fp32; only these copies are rounded).  For bf16 inputs both go as hi/lo
+  // bf16 planes: one bf16 rounding of V' (several times larger than the output
+  // it feeds: the masked intra-chunk product cancels) costs about 2% of RMS(o)
+  // at the max, one of h about 1%.
+  static constexpr int h_store = MODE == MODE_F32 ? ST_F32 : ST_SPLIT;
+  static constexpr int v_store = MODE == MODE_F32 ? ST_F32 : ST_SPLIT;
 };
 
 // 1-D workgroup index -> (unit, part) with the `parts` workgroups of a unit on
@@ -95,14 +105,20 @@ __device__ __forceinline__ void xcd_unit(int L, int parts, int units, int &unit,
 }
 
 // Store a wave's column of result tiles (rows 16m + 4g + i, column lr) for the
-// output stage, at `dst` (this chunk's and slice's part of the tensor).  Split
-// form (bf16 products): per pair of tiles (2p, 2p+1) the operand fragment the
-// output stage reads -- 8 values per lane in the order {tile 2p rows 4g..4g+3,
-// tile 2p+1 rows 4g..4g+3} -- as a bf16 high plane and a bf16 low plane (the
-// rounding remainder), 1 KB each.  fp32 form: one 1 KB block per tile.
-template <bool SPLIT, int NTILE>
+// output stage, at `dst` (this chunk's and slice's part of the tensor).  bf16
+// forms: per pair of tiles (2p, 2p+1) the operand fragment the output stage
+// reads -- 8 values per lane in the order {tile 2p rows 4g..4g+3, tile 2p+1
+// rows 4g..4g+3} -- rounded to bf16 (1 KB per pair), or as a bf16 high plane
+// and a bf16 low plane (the rounding remainder; 1 KB each).  fp32 form: one
+// 1 KB block per tile.
+template <int ST> struct Store {
+  static constexpr int tile_floats = ST == ST_BF16 ? 128 : 256;   // per 16x16 tile
+  static constexpr int loads = ST == ST_BF16 ? 1 : 2;             // 16-byte loads per fragment
+  static constexpr int frag = ST == ST_F32 ? F_F32 : ST == ST_SPLIT ? F_SPLIT : F_BF16;
+};
+template <int ST, int NTILE>
 __device__ __forceinline__ void store_result_tiles(float *dst, const f32x4 (&t)[NTILE], int lane) {
-  if constexpr (SPLIT) {
+  if constexpr (ST != ST_F32) {
     char *d = reinterpret_cast<char *>(dst);
 #pragma unroll
     for (int p = 0; p < NTILE / 2; ++p) {
@@ -113,13 +129,17 @@ __device__ __forceinline__ void store_result_tiles(float *dst, const f32x4 (&t)[
         hi[j] = (__bf16)x;
         lo[j] = (__bf16)(x - (float)hi[j]);
       }
-      *reinterpret_cast<bf16x8 *>(d + (2 * p) * 1024 + lane * 16) = hi;
-      *reinterpret_cast<bf16x8 *>(d + (2 * p + 1) * 1024 + lane * 16) = lo;
+      if constexpr (ST == ST_BF16) {
+        st16_stream(d + p * 1024 + lane * 16, hi);
+      } else {
+        st16_stream(d + (2 * p) * 1024 + lane * 16, hi);
+        st16_stream(d + (2 * p + 1) * 1024 + lane * 16, lo);
+      }
     }
   } else {
 #pragma unroll
     for (int m = 0; m < NTILE; ++m)
-      *reinterpret_cast<float4 *>(dst + (m * 64 + lane) * 4) = float4{t[m][0], t[m][1], t[m][2], t[m][3]};
+      st16_stream(dst + (m * 64 + lane) * 4, t[m]);
   }
 }
 
@@ -589,8 +609,7 @@ __global__ __launch_bounds__(NT, 2) void prep_kernel(FwdArgs a) {
         else *reinterpret_cast<uint4 *>(tmp + 4 * hh) = *reinterpret_cast<const uint4 *>(src);
       }
 #pragma unroll
-      for (int v = 0; v < 8 / VE; ++v)
-        *reinterpret_cast<uint4 *>(Ktg + (size_t)f * 8 + v * VE) = *reinterpret_cast<const uint4 *>(tmp + v * VE);
+      for (int v = 0; v < 8 / VE; ++v) st16_stream(Ktg + (size_t)f * 8 + v * VE, *reinterpret_cast<const uint4 *>(tmp + v * VE));
     }
   }
 
@@ -665,16 +684,14 @@ __global__ __launch_bounds__(NT, 2) void prep_kernel(FwdArgs a) {
           WT *dst = reinterpret_cast<WT *>(a.W) + ((cb * (C / 16) + mrow[u]) * (D / 32) + (md >> 1)) * 512 + lane * 8;
           constexpr int VE = 16 / sizeof(WT);
 #pragma unroll
-          for (int v = 0; v < 8 / VE; ++v)
-            *reinterpret_cast<uint4 *>(dst + v * VE) = *reinterpret_cast<const uint4 *>(tmp + v * VE);
+          for (int v = 0; v < 8 / VE; ++v) st16_stream(dst + v * VE, *reinterpret_cast<const uint4 *>(tmp + v * VE));
         } else if (pass == 0) {
           WT *dst = reinterpret_cast<WT *>(a.W) + (cb * C + 16 * mrow[u] + lr) * D + 16 * md + lq;
 #pragma unroll
           for (int i = 0; i < 4; ++i) dst[i] = from_f32<WT>(acc[u][md][i]);
         } else if constexpr (FWD) {
           // lane holds U[16 mrow + 4g + i][16md + lr]: the walk's fragment (mrow, md)
-          *reinterpret_cast<float4 *>(a.U + ((cb * (C / 16) + mrow[u]) * TD + md) * 256 + lane * 4) =
-              float4{acc[u][md][0], acc[u][md][1], acc[u][md][2], acc[u][md][3]};
+          st16_stream(a.U + ((cb * (C / 16) + mrow[u]) * TD + md) * 256 + lane * 4, acc[u][md]);
         } else {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
@@ -866,7 +883,8 @@ __global__ __launch_bounds__(64 * WPG) void walk_shared_kernel(FwdArgs a) {
     }
     // chunk-start state for the output stage (stores issued after the loads
     // this chunk still waits for)
-    if (KIND == WALK && a.Hs) store_result_tiles<PR::split_store>(a.Hs + (cb * (D / 16) + slice) * MH * 256, h, lane);
+    if (KIND == WALK && a.Hs)
+      store_result_tiles<PR::h_store>(a.Hs + (cb * (D / 16) + slice) * MH * Store<PR::h_store>::tile_floats, h, lane);
     Frag<PKk::b> vb[KBK];
     {
       float s[MV][4];
@@ -878,7 +896,8 @@ __global__ __launch_bounds__(64 * WPG) void walk_shared_kernel(FwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) s[m][i] = vps[m][i] * dcy[m][i];
       }
-      if (KIND == WALK && a.Vn) store_result_tiles<PR::split_store>(a.Vn + (cb * (D / 16) + slice) * MV * 256, vps, lane);
+      if (KIND == WALK && a.Vn)
+        store_result_tiles<PR::v_store>(a.Vn + (cb * (D / 16) + slice) * MV * Store<PR::v_store>::tile_floats, vps, lane);
 #pragma unroll
       for (int kb = 0; kb < KBK; ++kb) {
         const float x[8] = {s[2 * kb][0], s[2 * kb][1], s[2 * kb][2], s[2 * kb][3],
@@ -1069,8 +1088,6 @@ __global__ __launch_bounds__(64 * NWS) void walk_ring_kernel(FwdArgs a) {
       dcy[m][2] = exp2_fast(gl2 - cur.g[m].z * LOG2E);
       dcy[m][3] = exp2_fast(gl2 - cur.g[m].w * LOG2E);
     }
-    if (KIND == WALK && a.Hs)
-      store_result_tiles<PR::split_store>(a.Hs + (cb * (D / 16) + slice) * MH * 256 + mh0 * 256, h, lane);
     // V' = U - W h over all state k-blocks: own from registers, partner's from LDS
     // every k-block from LDS, the wave's own included (static indices)
     HF hb[KBW];
@@ -1085,9 +1102,9 @@ __global__ __launch_bounds__(64 * NWS) void walk_ring_kernel(FwdArgs a) {
       refill(P, cb, q);
     }
     VF vb[KBK];
+    f32x4 vps[MVW];
     {
       float s[MVW][4];
-      f32x4 vps[MVW];
 #pragma unroll
       for (int m = 0; m < MVW; ++m) {
         const float4 uu = cur.u[m];
@@ -1095,8 +1112,6 @@ __global__ __launch_bounds__(64 * NWS) void walk_ring_kernel(FwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) s[m][i] = vps[m][i] * dcy[m][i];
       }
-      if (KIND == WALK && a.Vn)
-        store_result_tiles<PR::split_store>(a.Vn + (cb * (D / 16) + slice) * MV * 256 + mv0 * 256, vps, lane);
 #pragma unroll
       for (int kbl = 0; kbl < KBKW; ++kbl) {
         const float x[8] = {s[2 * kbl][0], s[2 * kbl][1], s[2 * kbl][2], s[2 * kbl][3],
@@ -1109,18 +1124,28 @@ __global__ __launch_bounds__(64 * NWS) void walk_ring_kernel(FwdArgs a) {
     }
     // h <- e^{G_last} h + K^T (d o V') for this wave's state rows
     const float gl = exp2_fast(gl2);
+    f32x4 acc2[MHW];
 #pragma unroll
     for (int t = 0; t < MHW; ++t) {
-      f32x4 acc2 = zero4();
+      acc2[t] = zero4();
 #pragma unroll
       for (int kb = 0; kb < KBK; ++kb) {
         const int q = FWW + t * KBK + kb;
-        mma(acc2, ring[(P * FPW + q) % RING], vb[kb]);
+        mma(acc2[t], ring[(P * FPW + q) % RING], vb[kb]);
         refill(P, cb, q);
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) h[t][i] = gl * h[t][i] + acc2[i];
     }
+    // The chunk-start state and V' go out after the chunk's last loads: the
+    // memory counter drains in issue order, so a store issued ahead of a load
+    // would hold up every wait for that load.
+    if (KIND == WALK && a.Hs)
+      store_result_tiles<PR::h_store>(a.Hs + ((cb * (D / 16) + slice) * MH + mh0) * Store<PR::h_store>::tile_floats, h, lane);
+    if (KIND == WALK && a.Vn)
+      store_result_tiles<PR::v_store>(a.Vn + ((cb * (D / 16) + slice) * MV + mv0) * Store<PR::v_store>::tile_floats, vps, lane);
+#pragma unroll
+    for (int t = 0; t < MHW; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) h[t][i] = gl * h[t][i] + acc2[t][i];
 #pragma unroll
     for (int kbl = 0; kbl < KBWW; ++kbl) xh[w][kbl][lane] = state_frag(kbl);
     lds_barrier();
@@ -1290,7 +1315,9 @@ __global__ __launch_bounds__(NT, 2) void out_kernel(FwdArgs a) {
   constexpr int RU = R >= 8 ? 2 : 1;     // phase-A row tiles per wave
   constexpr int MH = D / 16, MV = C / 16, KBD = D / 32, KBC = C / 32;
   static_assert(R == 4 * RU, "phase A: R/4 row tiles per wave");
-  static_assert(!PR::split_store || (PKh::a == F_SPLIT && PKv::a == F_SPLIT), "split planes feed split operands");
+  using SH = Store<PR::h_store>;
+  using SV = Store<PR::v_store>;
+  static_assert(PKh::a == SH::frag && PKv::a == SV::frag, "stored copies are used as stored");
   __shared__ __align__(16) char lds[OL::BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1348,19 +1375,21 @@ __global__ __launch_bounds__(NT, 2) void out_kernel(FwdArgs a) {
   for (int u = 0; u < RU; ++u) load_q(u == 0 ? wv : R - 1 - wv, qa[u]);
   // phase-B operands of this wave's columns: h^T (2 column tiles x KBD) and
   // V'^T (2 x KBC) fragments, as stored by the walk; issued last, they arrive
-  // during phase A (two 16-byte loads per fragment)
-  constexpr int NLATE = 2 * (2 * KBD + 2 * KBC);
+  // during phase A (one 16-byte load per bf16 fragment, two per split or fp32 one)
+  constexpr int NLATE = SH::loads * 2 * KBD + SV::loads * 2 * KBC;
   static_assert(NLATE <= 63, "memory counter range");
   Frag<PKh::a> hf[2][KBD];
   Frag<PKv::a> vf[2][KBC];
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) {
     const int s = 2 * wv + ct;   // walk slice
-    const float *hs = a.Hs + (cb * (D / 16) + s) * MH * 256;
-    const float *vs = a.Vn + (cb * (D / 16) + s) * MV * 256;
+    const float *hs = a.Hs + (cb * (D / 16) + s) * MH * SH::tile_floats;
+    const float *vs = a.Vn + (cb * (D / 16) + s) * MV * SV::tile_floats;
 #pragma unroll
     for (int kb = 0; kb < KBD; ++kb) {
-      if constexpr (PR::split_store) {
+      if constexpr (PR::h_store == ST_BF16) {
+        hf[ct][kb].hi = *reinterpret_cast<const bf16x8 *>(hs + (kb * 64 + lane) * 4);
+      } else if constexpr (PR::h_store == ST_SPLIT) {
         hf[ct][kb].hi = *reinterpret_cast<const bf16x8 *>(hs + ((2 * kb) * 64 + lane) * 4);
         hf[ct][kb].lo = *reinterpret_cast<const bf16x8 *>(hs + ((2 * kb + 1) * 64 + lane) * 4);
       } else {
@@ -1372,7 +1401,9 @@ __global__ __launch_bounds__(NT, 2) void out_kernel(FwdArgs a) {
     }
 #pragma unroll
     for (int kp = 0; kp < KBC; ++kp) {
-      if constexpr (PR::split_store) {
+      if constexpr (PR::v_store == ST_BF16) {
+        vf[ct][kp].hi = *reinterpret_cast<const bf16x8 *>(vs + (kp * 64 + lane) * 4);
+      } else if constexpr (PR::v_store == ST_SPLIT) {
         vf[ct][kp].hi = *reinterpret_cast<const bf16x8 *>(vs + ((2 * kp) * 64 + lane) * 4);
         vf[ct][kp].lo = *reinterpret_cast<const bf16x8 *>(vs + ((2 * kp + 1) * 64 + lane) * 4);
       } else {
@@ -1512,13 +1543,11 @@ __global__ __launch_bounds__(NT, 2) void out_kernel(FwdArgs a) {
     for (int ct = 0; ct < 2; ++ct) {
       // lane holds O^T[c = 32w + 16ct + 4g + i][r]
       TO *dst = og + ((tok0 + r) * a.Hv + hv) * D + 32 * wv + 16 * ct + lq;
-      if constexpr (sizeof(TO) == 4) {
-        *reinterpret_cast<float4 *>(dst) = float4{er * acc1[ct][0] + acc2[ct][0], er * acc1[ct][1] + acc2[ct][1],
-                                                  er * acc1[ct][2] + acc2[ct][2], er * acc1[ct][3] + acc2[ct][3]};
-      } else {
+      TO ov[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dst[i] = from_f32<TO>(er * acc1[ct][i] + acc2[ct][i]);
-      }
+      for (int i = 0; i < 4; ++i) ov[i] = from_f32<TO>(er * acc1[ct][i] + acc2[ct][i]);
+      if constexpr (sizeof(TO) == 4) st16_stream(dst, ov);
+      else st8_stream(dst, ov);
     }
   };
   // query tiles two at a time, the next tile's queries in flight (unrolled,

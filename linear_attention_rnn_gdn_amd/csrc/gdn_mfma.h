@@ -51,6 +51,24 @@ __device__ __forceinline__ void lds_barrier() {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// Global stores with the nontemporal hint, for tensors that one launch writes
+// once and a later launch reads.  With plain stores their dirty lines sit in
+// L2 next to the operands the writing kernel keeps re-reading (and each
+// store's completion, which every later wait on the memory counter includes,
+// takes longer); streamed, the sequential walk runs about a quarter faster.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+template <typename T>
+__device__ __forceinline__ void st16_stream(void *p, const T &v) {
+  static_assert(sizeof(T) == 16, "16-byte store");
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4 *>(p));
+}
+template <typename T>
+__device__ __forceinline__ void st8_stream(void *p, const T &v) {
+  static_assert(sizeof(T) == 8, "8-byte store");
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x2, v), reinterpret_cast<u32x2 *>(p));
+}
+
 template <int P>
 __device__ __forceinline__ void mma_k32(f32x4 &c, const float (&a)[8], const float (&b)[8]) {
   if constexpr (P == P_F32) {
