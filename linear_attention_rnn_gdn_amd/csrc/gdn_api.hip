@@ -80,7 +80,8 @@ int num_cus() {
 
 template <int C, typename TI, int MODE, bool FWD = true>
 gdn_status launch_prep(const FwdArgs &a, hipStream_t st) {
-  hipLaunchKernelGGL((prep_kernel<C, TI, MODE, FWD>), dim3(a.nn, a.Hv, a.B), dim3(NT), 0, st, a);
+  const long units = (long)a.nn * a.B * a.Hv;   // one workgroup per (chunk, head)
+  hipLaunchKernelGGL((prep_kernel<C, TI, MODE, FWD>), dim3((unsigned)units), dim3(NT), 0, st, a);
   return check_launch();
 }
 
@@ -240,6 +241,9 @@ gdn_status gdn_validate(const gdn_shape *s) {
   if (s->n_groups < 0) return GDN_ERR_SHAPE;
   const int N = s->T / s->chunk;
   if (N > 65535 || (int64_t)s->B * s->H_v > 65535) return GDN_ERR_SHAPE;
+  // one workgroup per (chunk, head) in a 1-D grid; the walk's grid is
+  // (batch row, head, group or slice) x 16 at most
+  if ((int64_t)N * s->B * s->H_v > (1 << 30)) return GDN_ERR_SHAPE;
   if (s->n_groups > 1 && N > 0) {
     if (N % s->n_groups) return GDN_ERR_SHAPE;
     if ((int64_t)s->B * s->n_groups > 65535) return GDN_ERR_SHAPE;

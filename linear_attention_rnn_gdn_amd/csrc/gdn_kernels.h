@@ -163,6 +163,22 @@ struct FwdArgs {
   void *o;                        // out output
 };
 
+// 1-D workgroup index of the per-chunk kernels (prep, out) -> (chunk n,
+// batch row b, value head hv), heads fastest.  The workgroups resident at one
+// time then cover every head of a few chunks: together they read whole token
+// rows of q, k and v (one head's part of a row is only a few hundred bytes)
+// and write whole rows of o.  The value heads that share a qk head land on one
+// XCD next to each other and share its L2 for that head's q and k.
+__device__ __forceinline__ void chunk_head_unit(int L, const FwdArgs &a, int &n, int &b, int &hv) {
+  const int grp = a.Hv / a.Hqk;
+  int unit, part;
+  xcd_unit(L, grp, a.nn * a.B * a.Hqk, unit, part);
+  const int hq = unit % a.Hqk, rest = unit / a.Hqk;
+  b = rest % a.B;
+  n = a.n0 + rest / a.B;
+  hv = hq * grp + part;
+}
+
 // Copy C rows of D elements (row stride `gstride` elements in global memory)
 // into LDS rows of leading dimension `ld`, 16 bytes per thread access.
 // All loads are issued before the first LDS store so their latencies overlap.
@@ -451,7 +467,8 @@ __global__ __launch_bounds__(NT, 2) void prep_kernel(FwdArgs a) {
   TI *sX = reinterpret_cast<TI *>(sXraw);
   float *sM = reinterpret_cast<float *>(sXraw);
 
-  const int n = a.n0 + blockIdx.x, hv = blockIdx.y, b = blockIdx.z;
+  int n, b, hv;
+  chunk_head_unit(blockIdx.x, a, n, b, hv);
   const int hq = hv / (a.Hv / a.Hqk);
   // (the wave index as a scalar: tests on a wave's row tiles are uniform branches)
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1323,10 +1340,9 @@ __global__ __launch_bounds__(NT, 2) void out_kernel(FwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, g = lane >> 4, lq = g * 4;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  const int unit = blockIdx.x;
-  const size_t bh = (size_t)(unit / a.nn);
-  const int n = a.n0 + unit % a.nn;
-  const int b = (int)(bh / a.Hv), hv = (int)(bh % a.Hv);
+  int n, b, hv;
+  chunk_head_unit(blockIdx.x, a, n, b, hv);
+  const size_t bh = (size_t)b * a.Hv + hv;
   const int hq = hv / (a.Hv / a.Hqk);
   const size_t cb = bh * a.N + n;
   const size_t tok0 = (size_t)b * a.T + (size_t)n * C;   // first token of the chunk
@@ -1508,13 +1524,26 @@ __global__ __launch_bounds__(NT, 2) void out_kernel(FwdArgs a) {
     }
   }
   lds_barrier();
+  // the query fragments, over the K tile (read by no one from here on): the
+  // waves' phase-A tiles cover every query tile once, and phase B reads them
+  // back from LDS instead of fetching each tile again in every wave
+  static_assert(R * KBD * 64 * sizeof(QF) <= (size_t)OL::KB, "query fragments fit the K tile");
+  QF *qs = reinterpret_cast<QF *>(lds);   // [R][KBD][64]
+#pragma unroll
+  for (int u = 0; u < RU; ++u) {
+    const int rt = u == 0 ? wv : R - 1 - wv;
+#pragma unroll
+    for (int kb = 0; kb < KBD; ++kb) qs[(rt * KBD + kb) * 64 + lane] = qa[u][kb];
+  }
+  lds_barrier();
 
   // ---- phase B: this wave's 32 columns for every query tile ----
   TO *og = reinterpret_cast<TO *>(a.o);
-  QF qb[2][KBD];
-  load_q(0, qb[0]);
-  auto tile_out = [&](int rt, const QF (&q)[KBD]) {
+  auto tile_out = [&](int rt) {
     const int r = 16 * rt + lr;
+    QF q[KBD];
+#pragma unroll
+    for (int kb = 0; kb < KBD; ++kb) q[kb] = qs[(rt * KBD + kb) * 64 + lane];
     f32x4 acc1[2], acc2[2];
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) acc1[ct] = acc2[ct] = zero4();
@@ -1550,17 +1579,8 @@ __global__ __launch_bounds__(NT, 2) void out_kernel(FwdArgs a) {
       else st8_stream(dst, ov);
     }
   };
-  // query tiles two at a time, the next tile's queries in flight (unrolled,
-  // so that each wait covers exactly the loads it needs)
 #pragma unroll
-  for (int rt = 0; rt < R; rt += 2) {
-    load_q(rt + 1, qb[1]);
-    __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the tile
-    tile_out(rt, qb[0]);
-    if (rt + 2 < R) load_q(rt + 2, qb[0]);
-    __builtin_amdgcn_sched_barrier(0);
-    tile_out(rt + 1, qb[1]);
-  }
+  for (int rt = 0; rt < R; ++rt) tile_out(rt);
 }
 
 }  // namespace gdn
