@@ -81,7 +81,7 @@ int num_cus() {
 template <int C, typename TI, int MODE, bool FWD = true>
 gdn_status launch_prep(const FwdArgs &a, hipStream_t st) {
   const long units = (long)a.nn * a.B * a.Hv;   // one workgroup per (chunk, head)
-  hipLaunchKernelGGL((prep_kernel<C, TI, MODE, FWD>), dim3((unsigned)units), dim3(NT), 0, st, a);
+  hipLaunchKernelGGL((prep_kernel<C, TI, MODE, FWD>), dim3((unsigned)units), dim3(PNT), 0, st, a);
   return check_launch();
 }
 

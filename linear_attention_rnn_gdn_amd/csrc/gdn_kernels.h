@@ -15,7 +15,7 @@
 // are the reading under which the affine step equals the per-token rule.
 //
 // Kernels:
-//   prep_kernel    one workgroup (4 waves) per (chunk, value head, batch):
+//   prep_kernel    one workgroup (8 waves) per (chunk, value head, batch):
 //                  G, S, T, W, U, and K^T for the walk
 //   walk_ring_kernel / walk_shared_kernel
 //                  the sequential chunk walk, one wave per 16-column slice of
@@ -179,47 +179,6 @@ __device__ __forceinline__ void chunk_head_unit(int L, const FwdArgs &a, int &n,
   hv = hq * grp + part;
 }
 
-// Copy C rows of D elements (row stride `gstride` elements in global memory)
-// into LDS rows of leading dimension `ld`, 16 bytes per thread access.
-// All loads are issued before the first LDS store so their latencies overlap.
-template <typename TI, int ROWS>
-__device__ __forceinline__ void load_rows(TI *dst, int ld, const TI *src, size_t gstride) {
-  constexpr int VE = 16 / sizeof(TI);
-  constexpr int PER_ROW = D / VE;
-  constexpr int NV = ROWS * PER_ROW / NT;
-  static_assert(ROWS * PER_ROW % NT == 0, "tile must split evenly over the workgroup");
-  uint4 v[NV];
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int idx = threadIdx.x + i * NT, r = idx / PER_ROW, cv = idx % PER_ROW;
-    v[i] = *reinterpret_cast<const uint4 *>(src + (size_t)r * gstride + cv * VE);
-  }
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int idx = threadIdx.x + i * NT, r = idx / PER_ROW, cv = idx % PER_ROW;
-    *reinterpret_cast<uint4 *>(dst + r * ld + cv * VE) = v[i];
-  }
-}
-
-// Copy ROWS rows of COLS floats (global row stride gld) into LDS (row stride ld).
-template <int ROWS, int COLS>
-__device__ __forceinline__ void load_rows_f32(float *dst, int ld, const float *src, int gld) {
-  constexpr int PER_ROW = COLS / 4;
-  constexpr int NV = ROWS * PER_ROW / NT;
-  static_assert(ROWS * PER_ROW % NT == 0, "tile must split evenly over the workgroup");
-  float4 v[NV];
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int idx = threadIdx.x + i * NT, r = idx / PER_ROW, c4 = (idx % PER_ROW) * 4;
-    v[i] = *reinterpret_cast<const float4 *>(src + (size_t)r * gld + c4);
-  }
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int idx = threadIdx.x + i * NT, r = idx / PER_ROW, c4 = (idx % PER_ROW) * 4;
-    *reinterpret_cast<float4 *>(dst + r * ld + c4) = v[i];
-  }
-}
-
 // ----------------------------------------------------------------------------
 // prep: decay cumsum, S, T (ladder), W, U for one chunk of one value head.
 // FWD: the forward path's layouts (W in the input dtype, fragment-major W,
@@ -268,15 +227,15 @@ template <int C, typename TI> struct XT {
 
 // One thread's block of the input tile: rows 8 rb .. 8 rb + 7, columns
 // VE cb .. VE cb + VE - 1, as 8 row vectors of 16 bytes.
-template <int C, typename TI> struct TileBlock {
+template <int C, typename TI, int NTH> struct TileBlock {   // NTH threads share the tile; tix = 0..NTH-1
   static constexpr int VE = 16 / (int)sizeof(TI);
   static constexpr int NCB = D / VE, NBLK = (C / 8) * NCB;
-  static constexpr int PER = (NBLK + NT - 1) / NT;   // blocks per thread
+  static constexpr int PER = (NBLK + NTH - 1) / NTH;   // blocks per thread
   uint4 v[PER][8];
-  __device__ void load(const TI *src, size_t gstride) {
+  __device__ void load(int tix, const TI *src, size_t gstride) {
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
-      const int blk = threadIdx.x + p * NT, rb = blk / NCB, cb = blk % NCB;
+      const int blk = tix + p * NTH, rb = blk / NCB, cb = blk % NCB;
       if (blk < NBLK) {
 #pragma unroll
         for (int j = 0; j < 8; ++j)
@@ -285,10 +244,10 @@ template <int C, typename TI> struct TileBlock {
     }
   }
   // row-major copy [C][ld]
-  __device__ void put_rows(TI *dst, int ld) const {
+  __device__ void put_rows(int tix, TI *dst, int ld) const {
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
-      const int blk = threadIdx.x + p * NT, rb = blk / NCB, cb = blk % NCB;
+      const int blk = tix + p * NTH, rb = blk / NCB, cb = blk % NCB;
       if (blk < NBLK) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) *reinterpret_cast<uint4 *>(dst + (8 * rb + j) * ld + VE * cb) = v[p][j];
@@ -296,36 +255,51 @@ template <int C, typename TI> struct TileBlock {
     }
   }
   // transposed copy X^T (XT layout): column VE cb + e becomes row d, and the
-  // block's 8 rows its 8 consecutive k-values
-  __device__ void put_transposed(TI *dst) const {
+  // block's 8 rows its 8 consecutive k-values.  transpose() forms the 16-byte
+  // pieces in registers, put_transposed() stores them: a thread that keeps
+  // its block for a later copy holds it in one form only.
+  using Words = uint4[PER][8];
+  __device__ void transpose(Words &w) const {
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
-      const int blk = threadIdx.x + p * NT, rb = blk / NCB, cb = blk % NCB;
-      if (blk >= NBLK) continue;
       if constexpr (sizeof(TI) == 2) {
         // 8 x 8 transpose of 16-bit values: output dword q of column e packs
         // rows 2q (low half) and 2q + 1 (high half)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          uint32_t w[4];
+          uint32_t x[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const uint32_t lo = (&v[p][2 * q].x)[e >> 1], hi = (&v[p][2 * q + 1].x)[e >> 1];
-            w[q] = (e & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+            x[q] = (e & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
           }
-          *reinterpret_cast<uint4 *>(dst + XT<C, TI>::at(8 * cb + e, 8 * rb)) = uint4{w[0], w[1], w[2], w[3]};
+          w[p][e] = uint4{x[0], x[1], x[2], x[3]};
         }
       } else {
         // 8 x 4 of 32-bit values: column e = two 16-byte halves of 4 rows
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
+        for (int e = 0; e < 4; ++e)
 #pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const uint4 x = {(&v[p][4 * hh].x)[e], (&v[p][4 * hh + 1].x)[e], (&v[p][4 * hh + 2].x)[e],
-                             (&v[p][4 * hh + 3].x)[e]};
-            *reinterpret_cast<uint4 *>(dst + XT<C, TI>::at(4 * cb + e, 8 * rb + 4 * hh)) = x;
-          }
-        }
+          for (int hh = 0; hh < 2; ++hh)
+            w[p][2 * e + hh] = uint4{(&v[p][4 * hh].x)[e], (&v[p][4 * hh + 1].x)[e], (&v[p][4 * hh + 2].x)[e],
+                                     (&v[p][4 * hh + 3].x)[e]};
+      }
+    }
+  }
+  __device__ static void put_transposed(int tix, TI *dst, const Words &w) {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int blk = tix + p * NTH, rb = blk / NCB, cb = blk % NCB;
+      if (blk >= NBLK) continue;
+      if constexpr (sizeof(TI) == 2) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) *reinterpret_cast<uint4 *>(dst + XT<C, TI>::at(8 * cb + e, 8 * rb)) = w[p][e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh)
+            *reinterpret_cast<uint4 *>(dst + XT<C, TI>::at(4 * cb + e, 8 * rb + 4 * hh)) = w[p][2 * e + hh];
       }
     }
   }
@@ -356,15 +330,15 @@ __device__ __forceinline__ Frag<K> xt_frag(const TI *sxt, int d, int k0, int sw)
 
 // One level (block size BS) of the doubling ladder of step (5) below, fully
 // unrolled: for each 2BS diagonal block [[P,0],[L,Q]] of the packed T, the
-// lower-left block becomes -X_Q L X_P.  Tiles are shared out over the 4
+// lower-left block becomes -X_Q L X_P.  Tiles are shared out over the PW
 // waves; each tile's operands are read from LDS in one batch before its
 // products.  sM holds M1 = L X_P transposed (nb blocks of BS x (BS+4)).
-template <int C, int BS, int PL>
+template <int C, int BS, int PL, int PW>
 __device__ __forceinline__ void ladder_level(float *sT, float *sM, int wave, int lane) {
   using TRI = Tri<C>;
-  constexpr int NB = C / (2 * BS), TB = BS / 16, NTILE = NB * TB * TB, PER = (NTILE + 3) / 4;
+  constexpr int NB = C / (2 * BS), TB = BS / 16, NTILE = NB * TB * TB, PER = (NTILE + PW - 1) / PW;
   constexpr int LDM = BS + 4, KBM = (BS + 31) / 32;
-  constexpr int GRP = PER < 2 ? PER : 2;   // tiles per batch of reads
+  constexpr int GRP = (PER < 2 || PW > 4) ? 1 : 2;   // tiles per batch of reads (registers allowing)
   const int lr = lane & 15, lk = (lane >> 4) * 8, lq = (lane >> 4) * 4;
   // M1 = L X_P (stored transposed in sM)
 #pragma unroll
@@ -373,7 +347,7 @@ __device__ __forceinline__ void ladder_level(float *sT, float *sM, int wave, int
     int tl[GRP];
 #pragma unroll
     for (int v = 0; v < GRP; ++v) {
-      const int tt = wave + 4 * (u0 + v);
+      const int tt = wave + PW * (u0 + v);
       tl[v] = tt;
       const int blk = tt / (TB * TB), ti = tt % (TB * TB), mi = ti / TB, ni = ti % TB;
       const int s = blk * 2 * BS, kb0 = (16 * ni) / 32;
@@ -414,7 +388,7 @@ __device__ __forceinline__ void ladder_level(float *sT, float *sM, int wave, int
     int tl[GRP];
 #pragma unroll
     for (int v = 0; v < GRP; ++v) {
-      const int tt = wave + 4 * (u0 + v);
+      const int tt = wave + PW * (u0 + v);
       tl[v] = tt;
       const int blk = tt / (TB * TB), ti = tt % (TB * TB), mi = ti / TB, ni = ti % TB;
       const int s = blk * 2 * BS;
@@ -449,8 +423,10 @@ __device__ __forceinline__ void ladder_level(float *sT, float *sM, int wave, int
   lds_barrier();
 }
 
+constexpr int PW = 8, PNT = 64 * PW;   // prep: waves, threads per workgroup
+
 template <int C, typename TI, int MODE, bool FWD>
-__global__ __launch_bounds__(NT, 2) void prep_kernel(FwdArgs a) {
+__global__ __launch_bounds__(PNT, 4) void prep_kernel(FwdArgs a) {   // two workgroups per CU
   using WT = typename std::conditional<FWD, TI, float>::type;
   using PR = Prec<MODE>;
   using TRI = Tri<C>;
@@ -477,10 +453,16 @@ __global__ __launch_bounds__(NT, 2) void prep_kernel(FwdArgs a) {
   const size_t t0 = (size_t)n * C;
   const size_t cb = bh * a.N + n;  // chunk index into the workspace
 
-  // K block of this thread -> registers (kept for the transposed copy)
-  TileBlock<C, TI> kt, vt;
-  kt.load(reinterpret_cast<const TI *>(a.k) + (((size_t)b * a.T + t0) * a.Hqk + hq) * D, (size_t)a.Hqk * D);
-  vt.load(reinterpret_cast<const TI *>(a.v) + (((size_t)b * a.T + t0) * a.Hv + hv) * D, (size_t)a.Hv * D);
+  // The first half of the workgroup holds the K tile in registers, the second
+  // half the V tile, one 8-row block per thread (kept for the transposed
+  // copies, so K and V are read from memory once).
+  const bool vhalf = wave >= PW / 2;
+  const int tix = tid & (PNT / 2 - 1);
+  TileBlock<C, TI, PNT / 2> xt;
+  if (!vhalf)
+    xt.load(tix, reinterpret_cast<const TI *>(a.k) + (((size_t)b * a.T + t0) * a.Hqk + hq) * D, (size_t)a.Hqk * D);
+  else
+    xt.load(tix, reinterpret_cast<const TI *>(a.v) + (((size_t)b * a.T + t0) * a.Hv + hv) * D, (size_t)a.Hv * D);
 
   // (1) decay cumsum over the chunk (inclusive), beta
   {
@@ -505,36 +487,47 @@ __global__ __launch_bounds__(NT, 2) void prep_kernel(FwdArgs a) {
       sScale[tid] = bx * exp2_fast(x * LOG2E);
     }
   }
-  // (2) K row-major -> LDS
-  kt.put_rows(sX, LDI);
+  // (2) K row-major -> LDS; from here on each thread keeps its block in
+  // transposed form only
+  if (!vhalf) xt.put_rows(tix, sX, LDI);
+  typename TileBlock<C, TI, PNT / 2>::Words xw;
+  xt.transpose(xw);
   lds_barrier();
 
-  // (3) S = strict-lower( beta_r e^{G_r - G_i} K K^T ) into packed sT.
-  //     Wave w owns row tiles {w, TC-1-w} (balanced triangle); each k-block's
-  //     column fragment feeds both of them.
+  // Work split for the products of (3), (6), (7): row tiles are taken in
+  // pairs {j, TC-1-j} (equal shares of the triangle), group j = wave % NGR,
+  // and the WPG waves of a group split the pair's column tiles.
   constexpr int TC = C / 16;
-  constexpr int RU = TC / 4;   // row tiles per wave
-  int mrow[RU];
-#pragma unroll
-  for (int u = 0; u < RU; ++u) mrow[u] = u == 0 ? wave : TC - 1 - wave;
+  constexpr int NGR = TC / 2, WPG = PW / NGR;
+  static_assert(PW % NGR == 0 && TC % WPG == 0, "whole column shares");
+  constexpr int RU = 2;   // row tiles per wave
+  const int grp = wave % NGR, sub = wave / NGR;
+  const int mrow[RU] = {grp, TC - 1 - grp};
+
+  // (3) S = strict-lower( beta_r e^{G_r - G_i} K K^T ) into packed sT.  A
+  //     wave takes the column tiles ni = sub + WPG c of its two row tiles;
+  //     each k-block's column fragment feeds both.
   {
     using PK = PolicyKinds<PR::exact>;
-    f32x4 acc[RU][TC];
+    constexpr int NC = TC / WPG;
+    f32x4 acc[RU][NC];
 #pragma unroll
     for (int u = 0; u < RU; ++u)
 #pragma unroll
-      for (int ni = 0; ni < TC; ++ni) acc[u][ni] = zero4();
+      for (int c = 0; c < NC; ++c) acc[u][c] = zero4();
 #pragma unroll
     for (int kb = 0; kb < D / 32; ++kb) {
       Frag<PK::a> af[RU];
 #pragma unroll
       for (int u = 0; u < RU; ++u) af[u] = lds_frag<PK::a>(sX + (16 * mrow[u] + lr) * LDI + 32 * kb + lk);
 #pragma unroll
-      for (int ni = 0; ni < TC; ++ni) {
+      for (int c = 0; c < NC; ++c) {
+        const int ni = sub + WPG * c;
+        if (ni > mrow[1]) continue;
         const auto bf = lds_frag<PK::b>(sX + (16 * ni + lr) * LDI + 32 * kb + lk);
 #pragma unroll
         for (int u = 0; u < RU; ++u)
-          if (ni <= mrow[u]) mma(acc[u][ni], af[u], bf);
+          if (ni <= mrow[u]) mma(acc[u][c], af[u], bf);
       }
     }
 #pragma unroll
@@ -547,14 +540,15 @@ __global__ __launch_bounds__(NT, 2) void prep_kernel(FwdArgs a) {
       float *rowp = sT + TRI::at(16 * m + lq, lr);   // row 16m + lq, column lr
       const int rstr = L + 4;                         // row stride of this row tile
 #pragma unroll
-      for (int ni = 0; ni < TC; ++ni) {
-        if (16 * ni < L) {
+      for (int cc = 0; cc < NC; ++cc) {
+        const int ni = sub + WPG * cc;
+        if (16 * ni < L) {   // the row tile's stored columns (zeros past the diagonal)
           const int c = 16 * ni + lr;
           const float gc = sG2[c];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = 16 * m + lq + i;
-            rowp[i * rstr + 16 * ni] = (c < r) ? brv[i] * exp2_fast(grv[i] - gc) * acc[u][ni][i] : 0.f;
+            rowp[i * rstr + 16 * ni] = (c < r) ? brv[i] * exp2_fast(grv[i] - gc) * acc[u][cc][i] : 0.f;
           }
         }
       }
@@ -588,14 +582,14 @@ __global__ __launch_bounds__(NT, 2) void prep_kernel(FwdArgs a) {
   // (5) doubling ladder: for each 2b diagonal block [[P,0],[L,Q]] the new
   //     lower-left block is -X_Q L X_P (X_P, X_Q the current inverses).
   //     The row-major K tile is dead; its space holds the scratch sM.
-  ladder_level<C, 16, PR::ladder>(sT, sM, wave, lane);
-  ladder_level<C, 32, PR::ladder>(sT, sM, wave, lane);
-  if constexpr (C > 64) ladder_level<C, 64, PR::ladder>(sT, sM, wave, lane);
+  ladder_level<C, 16, PR::ladder, PW>(sT, sM, wave, lane);
+  ladder_level<C, 32, PR::ladder, PW>(sT, sM, wave, lane);
+  if constexpr (C > 64) ladder_level<C, 64, PR::ladder, PW>(sT, sM, wave, lane);
   static_assert(C == 64 || C == 128, "ladder levels for C = 64 and 128");
 
   if (a.Tm) {
     float *Tg = a.Tm + cb * C * C;
-    for (int idx = tid; idx < C * C; idx += NT) {
+    for (int idx = tid; idx < C * C; idx += PNT) {
       const int r = idx / C, c = idx % C;
       Tg[idx] = c < TRI::len(r >> 4) ? sT[TRI::at(r, c)] : 0.f;
     }
@@ -603,7 +597,7 @@ __global__ __launch_bounds__(NT, 2) void prep_kernel(FwdArgs a) {
   if (tid < C) a.G[cb * C + tid] = sG[tid];
 
   // K^T -> LDS from the registers
-  kt.put_transposed(sX);
+  if (!vhalf) TileBlock<C, TI, PNT / 2>::put_transposed(tix, sX, xw);
   lds_barrier();
   if constexpr (FWD) {
     // K^T fragments for the walk, fragment-major: (d tile m, k-block kb, lane)
@@ -613,8 +607,8 @@ __global__ __launch_bounds__(NT, 2) void prep_kernel(FwdArgs a) {
     TI *Ktg = reinterpret_cast<TI *>(a.Kt) + cb * D * C;
     constexpr int VE = 16 / sizeof(TI);
 #pragma unroll
-    for (int i = 0; i < D * C / 8 / NT; ++i) {
-      const int f = tid + i * NT;
+    for (int i = 0; i < D * C / 8 / PNT; ++i) {
+      const int f = tid + i * PNT;
       const int l = f & 63, mk = f >> 6, m = mk / (C / 32), kb = mk % (C / 32);
       const int d = 16 * m + (l & 15);
       TI tmp[8];
@@ -634,58 +628,59 @@ __global__ __launch_bounds__(NT, 2) void prep_kernel(FwdArgs a) {
   //     that each lane ends with 4 consecutive columns of one row of W.
   // (7) U = (T diag(beta)) V, computed as is, so that each lane ends with 4
   //     consecutive rows of one column of U (= 4 consecutive entries of U^T).
-  // Wave w owns row tiles {w, TC-1-w}; T is lower triangular, so row tile m
-  // needs k < 16(m+1).  The T fragments of k-blocks past the diagonal read
-  // T's zero-filled or neighbouring entries and their products are skipped.
-  constexpr int TD = D / 16;
+  // A wave takes its two row tiles and d tiles md0 .. md0 + TDW - 1; T is
+  // lower triangular, so row tile m needs k < 16(m+1).  The T fragments of
+  // k-blocks past the diagonal read T's zero-filled or neighbouring entries
+  // and their products are skipped.
+  constexpr int TD = D / 16, TDW = TD / WPG;
+  static_assert(TD % WPG == 0 && TDW % 2 == 0, "W fragments pair d tiles");
+  const int md0 = sub * TDW;
   // swizzle term of this lane's X^T rows 16md + lr
-  int xsw[TD];
+  int xsw[TDW];
 #pragma unroll
-  for (int md = 0; md < TD; ++md) xsw[md] = XT<C, TI>::swz(16 * md + lr);
+  for (int mdl = 0; mdl < TDW; ++mdl) xsw[mdl] = XT<C, TI>::swz(16 * (md0 + mdl) + lr);
   constexpr int KT = PolicyKinds<PR::wy>::a;   // T' fragments (split)
   constexpr int KX = PolicyKinds<PR::wy>::b;   // K / V fragments (exact data)
   for (int pass = 0; pass < 2; ++pass) {
     if (pass == 1) {
       lds_barrier();
-      vt.put_transposed(sX);
+      if (vhalf) TileBlock<C, TI, PNT / 2>::put_transposed(tix, sX, xw);
       lds_barrier();
     }
     const float *scale = pass == 0 ? sScale : sBeta;
-    f32x4 acc[RU][TD];
-#pragma unroll
-    for (int u = 0; u < RU; ++u)
-#pragma unroll
-      for (int md = 0; md < TD; ++md) acc[u][md] = zero4();
-#pragma unroll
-    for (int kb = 0; kb < C / 32; ++kb) {
-      const int k0 = 32 * kb + lk;
-      Frag<KT> tf[RU];
-      bool live[RU];
-#pragma unroll
-      for (int u = 0; u < RU; ++u) {
-        live[u] = 32 * kb < 16 * (mrow[u] + 1);
-        float x[8], sc[8];
-        ld8(sT + TRI::at(16 * mrow[u] + lr, k0), x);
-        ld8(scale + k0, sc);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] *= sc[j];
-        tf[u] = make_frag<KT>(x);
-      }
-#pragma unroll
-      for (int md = 0; md < TD; ++md) {
-        const auto xf = xt_frag<KX, C, TI>(sX, 16 * md + lr, k0, xsw[md]);   // X^T row 16md+lr = column of K (or V)
-#pragma unroll
-        for (int u = 0; u < RU; ++u) {
-          if (!live[u]) continue;
-          if (pass == 0) mma(acc[u][md], xf, tf[u]);   // W^T tile (d, r)
-          else mma(acc[u][md], tf[u], xf);             // U tile (r, d)
-        }
-      }
-    }
+    // one row tile at a time (registers: the other half of the workgroup
+    // still holds its V block)
 #pragma unroll
     for (int u = 0; u < RU; ++u) {
+      f32x4 acc[TDW];
 #pragma unroll
-      for (int md = 0; md < TD; ++md) {
+      for (int md = 0; md < TDW; ++md) acc[md] = zero4();
+      // (k-blocks not unrolled: unrolled, their operand loads are hoisted
+      // ahead and the registers run out)
+#pragma unroll 1
+      for (int kb = 0; kb < C / 32; ++kb) {
+        if (32 * kb >= 16 * (mrow[u] + 1)) break;   // T is zero from here
+        const int k0 = 32 * kb + lk;
+        Frag<KT> tf;
+        {
+          float x[8], sc[8];
+          ld8(sT + TRI::at(16 * mrow[u] + lr, k0), x);
+          ld8(scale + k0, sc);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) x[j] *= sc[j];
+          tf = make_frag<KT>(x);
+        }
+#pragma unroll
+        for (int mdl = 0; mdl < TDW; ++mdl) {
+          // X^T row 16md+lr = column of K (or V)
+          const auto xf = xt_frag<KX, C, TI>(sX, 16 * (md0 + mdl) + lr, k0, xsw[mdl]);
+          if (pass == 0) mma(acc[mdl], xf, tf);   // W^T tile (d, r)
+          else mma(acc[mdl], tf, xf);             // U tile (r, d)
+        }
+      }
+#pragma unroll
+      for (int mdl = 0; mdl < TDW; ++mdl) {
+        const int md = md0 + mdl;
         if (pass == 0 && FWD) {
           // lane holds W[r][16md + 4g + i], r = 16 mrow + lr.  The walk's
           // fragment (mrow, kb) gives lane (lr, g) the k-values 32 kb +
@@ -695,8 +690,8 @@ __global__ __launch_bounds__(NT, 2) void prep_kernel(FwdArgs a) {
           WT tmp[8];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            tmp[i] = from_f32<WT>(acc[u][md][i]);
-            tmp[4 + i] = from_f32<WT>(acc[u][md + 1][i]);
+            tmp[i] = from_f32<WT>(acc[mdl][i]);
+            tmp[4 + i] = from_f32<WT>(acc[mdl + 1][i]);
           }
           WT *dst = reinterpret_cast<WT *>(a.W) + ((cb * (C / 16) + mrow[u]) * (D / 32) + (md >> 1)) * 512 + lane * 8;
           constexpr int VE = 16 / sizeof(WT);
@@ -705,14 +700,14 @@ __global__ __launch_bounds__(NT, 2) void prep_kernel(FwdArgs a) {
         } else if (pass == 0) {
           WT *dst = reinterpret_cast<WT *>(a.W) + (cb * C + 16 * mrow[u] + lr) * D + 16 * md + lq;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) dst[i] = from_f32<WT>(acc[u][md][i]);
+          for (int i = 0; i < 4; ++i) dst[i] = from_f32<WT>(acc[mdl][i]);
         } else if constexpr (FWD) {
           // lane holds U[16 mrow + 4g + i][16md + lr]: the walk's fragment (mrow, md)
-          st16_stream(a.U + ((cb * (C / 16) + mrow[u]) * TD + md) * 256 + lane * 4, acc[u][md]);
+          st16_stream(a.U + ((cb * (C / 16) + mrow[u]) * TD + md) * 256 + lane * 4, acc[mdl]);
         } else {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            a.U[(cb * C + 16 * mrow[u] + lq + i) * D + 16 * md + lr] = acc[u][md][i];
+            a.U[(cb * C + 16 * mrow[u] + lq + i) * D + 16 * md + lr] = acc[mdl][i];
         }
       }
     }
