@@ -271,7 +271,8 @@ template <int C, typename TI, int NTH> struct TileBlock {   // NTH threads share
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const uint32_t lo = (&v[p][2 * q].x)[e >> 1], hi = (&v[p][2 * q + 1].x)[e >> 1];
-            x[q] = (e & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+            // one byte permute: bytes {0,1} (even e) or {2,3} (odd e) of lo, then of hi
+            x[q] = __builtin_amdgcn_perm(hi, lo, (e & 1) ? 0x07060302u : 0x05040100u);
           }
           w[p][e] = uint4{x[0], x[1], x[2], x[3]};
         }
@@ -604,23 +605,27 @@ __global__ __launch_bounds__(PNT, 4) void prep_kernel(FwdArgs a) {   // two work
     // holds K[r][16 m + lr] for the 8 tokens r = 32 kb + {4g..4g+3,
     // 16+4g..16+4g+3} (the k order of the walk's register-chained operand);
     // one contiguous 1 KB per wave store
-    TI *Ktg = reinterpret_cast<TI *>(a.Kt) + cb * D * C;
+    // fragment f = wave + PW i (i-th store of this wave): d tile m = f / KBC,
+    // k-block kb = f % KBC
+    constexpr int KBC = C / 32, NF = D * C / 8 / 64;   // fragments (1 KB each)
+    static_assert(NF % PW == 0, "whole fragments per wave");
+    TI *Ktg = reinterpret_cast<TI *>(a.Kt) + cb * D * C + lane * 8;
     constexpr int VE = 16 / sizeof(TI);
 #pragma unroll
-    for (int i = 0; i < D * C / 8 / PNT; ++i) {
-      const int f = tid + i * PNT;
-      const int l = f & 63, mk = f >> 6, m = mk / (C / 32), kb = mk % (C / 32);
-      const int d = 16 * m + (l & 15);
+    for (int i = 0; i < NF / PW; ++i) {
+      const int f = wave + PW * i, m = f / KBC, kb = f % KBC;
+      const int d = 16 * m + lr;
+      const int sw = XT<C, TI>::swz(d);
       TI tmp[8];
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        const int k = 32 * kb + 16 * hh + 4 * (l >> 4);   // 4 consecutive tokens
-        const TI *src = sX + XT<C, TI>::at(d, k - k % VE) + k % VE;
+        const int k = 32 * kb + 16 * hh + 4 * g;   // 4 consecutive tokens
+        const TI *src = sX + XT<C, TI>::at(d, k - k % VE, sw) + k % VE;
         if constexpr (sizeof(TI) == 2) *reinterpret_cast<uint2 *>(tmp + 4 * hh) = *reinterpret_cast<const uint2 *>(src);
         else *reinterpret_cast<uint4 *>(tmp + 4 * hh) = *reinterpret_cast<const uint4 *>(src);
       }
 #pragma unroll
-      for (int v = 0; v < 8 / VE; ++v) st16_stream(Ktg + (size_t)f * 8 + v * VE, *reinterpret_cast<const uint4 *>(tmp + v * VE));
+      for (int v = 0; v < 8 / VE; ++v) st16_stream(Ktg + f * 512 + v * VE, *reinterpret_cast<const uint4 *>(tmp + v * VE));
     }
   }
 
