@@ -625,7 +625,7 @@ __global__ __launch_bounds__(PNT, 4) void prep_kernel(FwdArgs a) {   // two work
         else *reinterpret_cast<uint4 *>(tmp + 4 * hh) = *reinterpret_cast<const uint4 *>(src);
       }
 #pragma unroll
-      for (int v = 0; v < 8 / VE; ++v) st16_stream(Ktg + f * 512 + v * VE, *reinterpret_cast<const uint4 *>(tmp + v * VE));
+      for (int v = 0; v < 8 / VE; ++v) st16(Ktg + f * 512 + v * VE, *reinterpret_cast<const uint4 *>(tmp + v * VE));
     }
   }
 
@@ -701,14 +701,14 @@ __global__ __launch_bounds__(PNT, 4) void prep_kernel(FwdArgs a) {   // two work
           WT *dst = reinterpret_cast<WT *>(a.W) + ((cb * (C / 16) + mrow[u]) * (D / 32) + (md >> 1)) * 512 + lane * 8;
           constexpr int VE = 16 / sizeof(WT);
 #pragma unroll
-          for (int v = 0; v < 8 / VE; ++v) st16_stream(dst + v * VE, *reinterpret_cast<const uint4 *>(tmp + v * VE));
+          for (int v = 0; v < 8 / VE; ++v) st16(dst + v * VE, *reinterpret_cast<const uint4 *>(tmp + v * VE));
         } else if (pass == 0) {
           WT *dst = reinterpret_cast<WT *>(a.W) + (cb * C + 16 * mrow[u] + lr) * D + 16 * md + lq;
 #pragma unroll
           for (int i = 0; i < 4; ++i) dst[i] = from_f32<WT>(acc[mdl][i]);
         } else if constexpr (FWD) {
           // lane holds U[16 mrow + 4g + i][16md + lr]: the walk's fragment (mrow, md)
-          st16_stream(a.U + ((cb * (C / 16) + mrow[u]) * TD + md) * 256 + lane * 4, acc[mdl]);
+          st16(a.U + ((cb * (C / 16) + mrow[u]) * TD + md) * 256 + lane * 4, acc[mdl]);
         } else {
 #pragma unroll
           for (int i = 0; i < 4; ++i)

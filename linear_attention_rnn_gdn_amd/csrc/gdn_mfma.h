@@ -52,12 +52,21 @@ __device__ __forceinline__ void lds_barrier() {
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 // Global stores with the nontemporal hint, for tensors that one launch writes
-// once and a later launch reads.  With plain stores their dirty lines sit in
-// L2 next to the operands the writing kernel keeps re-reading (and each
-// store's completion, which every later wait on the memory counter includes,
-// takes longer); streamed, the sequential walk runs about a quarter faster.
+// once and a later launch reads: the walk's copies of h and V' for the output
+// stage, and o.  With plain stores the walk's dirty lines sit in L2 next to
+// the operands it keeps re-reading (and each store's completion, which every
+// later wait on the memory counter includes, takes longer); streamed, the
+// walk runs about a quarter faster.  Prep's outputs are the exception: the
+// walk that follows reads them at once, and with plain stores they are still
+// in the memory-side cache then (measured over whole steps: the walk runs in
+// two thirds of the time).
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+template <typename T>
+__device__ __forceinline__ void st16(void *p, const T &v) {
+  static_assert(sizeof(T) == 16, "16-byte store");
+  *reinterpret_cast<u32x4 *>(p) = __builtin_bit_cast(u32x4, v);
+}
 template <typename T>
 __device__ __forceinline__ void st16_stream(void *p, const T &v) {
   static_assert(sizeof(T) == 16, "16-byte store");
