@@ -224,9 +224,23 @@ def cpu_baseline(w, x, budget_s=15.0):
                       f"mean of {reps} runs, {dt:.2f} s each"}
 
 
+def ramp_clocks(fn, seconds=0.5):
+    """Untimed steps for `seconds` of wall time before the warm-up proper: a
+    short burst of kernels leaves the GPU below its working clocks, and the
+    first few hundred microseconds of work run measurably slower."""
+    import torch
+
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
+
+
 def time_steps(fn, steps, warmup):
     import torch
 
+    ramp_clocks(fn)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -243,8 +257,8 @@ def time_steps(fn, steps, warmup):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="qwen3next_8b_layer")
     ap.add_argument("--secondary", default="long_256k",
                     help="second workload timed for context ('' to skip)")
