@@ -76,7 +76,7 @@ enum : int { ST_F32 = 0, ST_SPLIT = 1, ST_BF16 = 2 };
 constexpr int MODE_BF16 = 0, MODE_F32 = 1;
 template <int MODE> struct Prec {
   static constexpr int exact = MODE == MODE_F32 ? P_F32 : P_BF16;       // bf16 data x bf16 data
-  static constexpr int ladder = P_F32;                                    // fp32 x fp32, no operand splitting
+  static constexpr int ladder = MODE == MODE_F32 ? P_F32 : P_SPLIT_AB;  // fp32 x fp32 (bf16 inputs: as hi/lo bf16 pairs)
   static constexpr int wy = MODE == MODE_F32 ? P_F32 : P_SPLIT_A;       // T' (fp32) x K/V (data)
   static constexpr int wh = MODE == MODE_F32 ? P_F32 : P_BF16;          // W x h
   static constexpr int kv = MODE == MODE_F32 ? P_F32 : P_SPLIT_B;       // K^T (data) x V'
