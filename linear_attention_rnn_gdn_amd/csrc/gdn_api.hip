@@ -115,11 +115,12 @@ gdn_status launch_out(const FwdArgs &a, hipStream_t st) {
 gdn_status launch_prefix(int BH, int n, const float *A, const float *Bm, const float *h_init, float *h_in,
                          float *h_final, bool split, hipStream_t st) {
   PrefixArgs p{BH, n, A, Bm, h_init, h_in, h_final};
-  const unsigned blocks = (unsigned)(D / 16) * BH;   // one wave per 16-column slice
+  const unsigned blocks = (unsigned)(D / 16) * BH;   // one workgroup per 16-column slice
+  constexpr int NWS = 4;                              // waves per slice, 32 state rows each
   if (split)
-    hipLaunchKernelGGL((prefix_kernel<P_SPLIT_AB>), dim3(blocks), dim3(64), 0, st, p);
+    hipLaunchKernelGGL((prefix_kernel<P_SPLIT_AB, NWS>), dim3(blocks), dim3(64 * NWS), 0, st, p);
   else
-    hipLaunchKernelGGL((prefix_kernel<P_F32>), dim3(blocks), dim3(64), 0, st, p);
+    hipLaunchKernelGGL((prefix_kernel<P_F32, NWS>), dim3(blocks), dim3(64 * NWS), 0, st, p);
   return check_launch();
 }
 

@@ -1192,103 +1192,110 @@ __global__ __launch_bounds__(64 * NWS) void walk_ring_kernel(FwdArgs a) {
 
 // ----------------------------------------------------------------------------
 // exclusive prefix of affine pairs: h_in[0] = h_init, h_in[j+1] = A_j h_in[j]
-// + B_j, h_final = A_{n-1} h_in[n-1] + B_{n-1}.  One wave per 16-column slice
-// of the state (the recurrence is column-separable), with the slice in
-// matrix-core result registers for all n steps, as in the walk.  A_j (row-
-// major fp32) is the A operand: per lane two 16-byte runs of a row, in the
-// k order of two stacked result tiles, so the state tiles are the B operand
-// as they stand.  A's fragments stream through a ring of register slots in
-// the order they are used; B_j arrives one step ahead.
+// + B_j, h_final = A_{n-1} h_in[n-1] + B_{n-1}.  One workgroup per 16-column
+// slice of the state (the recurrence is column-separable); its NWS waves
+// split the slice's rows, each holding its rows in matrix-core result
+// registers for all n steps, as in the walk.  A_j (row-major fp32) is the A
+// operand: per lane two 16-byte runs of a row, in the k order of two stacked
+// result tiles, so a wave's two state tiles are one k-block of the B operand
+// as they stand; the waves pass their k-blocks through LDS (double-buffered:
+// one barrier per step).  Each wave streams only its rows of A_j, one step
+// ahead; B_j also arrives one step ahead.
 struct PrefixArgs {
   int BH, n;
   const float *A, *Bm, *h_init;
   float *h_in, *h_final;
 };
 
-template <int PREC>
-__global__ __launch_bounds__(64) void prefix_kernel(PrefixArgs a) {
+template <int PREC, int NWS>
+__global__ __launch_bounds__(64 * NWS) void prefix_kernel(PrefixArgs a) {
   using PK = PolicyKinds<PREC>;
+  using HF = Frag<PK::b>;
   constexpr int MH = D / 16, KB = D / 32;
-  constexpr int F = MH * KB;      // A fragments per step
-  constexpr int RING = 16;        // slots (two 16-byte runs each)
-  static_assert(F % RING == 0, "ring slots must repeat every step");
+  constexpr int MHW = MH / NWS;   // state row tiles per wave
+  static_assert(MHW == 2, "each wave holds one k-block of the state");
+  constexpr int F = MHW * KB;     // A fragments per wave and step (= ring slots)
+  __shared__ __align__(16) HF xh[2][KB][64];
   int unit, slice;
   xcd_unit(blockIdx.x, D / 16, a.BH, unit, slice);
   const size_t bh = (size_t)unit;
-  const int lane = threadIdx.x, lr = lane & 15, g = lane >> 4;
-  const int c0 = slice * 16;
+  const int lane = threadIdx.x & 63, lr = lane & 15, g = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c0 = slice * 16, m0 = w * MHW;
 
-  f32x4 h[MH];
+  f32x4 h[MHW];
 #pragma unroll
-  for (int m = 0; m < MH; ++m)
+  for (int t = 0; t < MHW; ++t)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      h[m][i] = a.h_init ? a.h_init[(bh * D + 16 * m + 4 * g + i) * D + c0 + lr] : 0.f;
+      h[t][i] = a.h_init ? a.h_init[(bh * D + 16 * (m0 + t) + 4 * g + i) * D + c0 + lr] : 0.f;
 
-  // fragment p = (row tile m, k-block kb) of A_j: row 16m + lr, columns
-  // 32kb + 4g .. +3 and 32kb + 16 + 4g .. +3
+  // fragment p = (own row tile t, k-block kb) of A_j: row 16(m0+t) + lr,
+  // columns 32kb + 4g .. +3 and 32kb + 16 + 4g .. +3
   struct Run2 {
     float4 x0, x1;
   };
   auto load = [&](size_t j, int p) -> Run2 {
-    const float *row = a.A + ((bh * a.n + j) * D + 16 * (p / KB) + lr) * D + 32 * (p % KB) + 4 * g;
+    const float *row = a.A + ((bh * a.n + j) * D + 16 * (m0 + p / KB) + lr) * D + 32 * (p % KB) + 4 * g;
     return Run2{*reinterpret_cast<const float4 *>(row), *reinterpret_cast<const float4 *>(row + 16)};
   };
-  auto load_b = [&](size_t j, f32x4 (&bq)[MH]) {
+  auto load_b = [&](size_t j, f32x4 (&bq)[MHW]) {
     const float *B = a.Bm + (bh * a.n + j) * D * D + c0 + lr;
 #pragma unroll
-    for (int m = 0; m < MH; ++m)
+    for (int t = 0; t < MHW; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) bq[m][i] = B[(size_t)(16 * m + 4 * g + i) * D];
+      for (int i = 0; i < 4; ++i) bq[t][i] = B[(size_t)(16 * (m0 + t) + 4 * g + i) * D];
   };
-  Run2 ring[RING];
+  Run2 ring[F];
 #pragma unroll
-  for (int p = 0; p < RING; ++p) ring[p] = load(0, p);
-  f32x4 bq[2][MH];
+  for (int p = 0; p < F; ++p) ring[p] = load(0, p);
+  f32x4 bq[2][MHW];
   load_b(0, bq[0]);
 
-  auto step = [&](f32x4 (&bc)[MH], f32x4 (&bn)[MH], int j) {
+  auto step = [&](f32x4 (&bc)[MHW], f32x4 (&bn)[MHW], int j, auto Pc) {
+    constexpr int P = decltype(Pc)::value;   // step parity: LDS buffer
     const size_t jn = j + 1 < a.n ? j + 1 : j;   // last step: loads repeat (unused)
     load_b(jn, bn);
+    {
+      const float x[8] = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
+      xh[P][w][lane] = make_frag<PK::b>(x);
+    }
     if (a.h_in) {
       float *dst = a.h_in + ((bh * a.n + j) * D) * D + c0 + lr;
 #pragma unroll
-      for (int m = 0; m < MH; ++m)
+      for (int t = 0; t < MHW; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dst[(size_t)(16 * m + 4 * g + i) * D] = h[m][i];
+        for (int i = 0; i < 4; ++i) dst[(size_t)(16 * (m0 + t) + 4 * g + i) * D] = h[t][i];
     }
-    Frag<PK::b> hb[KB];
+    lds_barrier();
+    HF hb[KB];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      const float x[8] = {h[2 * kb][0], h[2 * kb][1], h[2 * kb][2], h[2 * kb][3],
-                          h[2 * kb + 1][0], h[2 * kb + 1][1], h[2 * kb + 1][2], h[2 * kb + 1][3]};
-      hb[kb] = make_frag<PK::b>(x);
-    }
+    for (int kb = 0; kb < KB; ++kb) hb[kb] = xh[P][kb][lane];
 #pragma unroll
-    for (int m = 0; m < MH; ++m) {
+    for (int t = 0; t < MHW; ++t) {
       f32x4 acc = zero4();
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const int p = m * KB + kb;
-        const Run2 r = ring[p % RING];
+        const int p = t * KB + kb;
+        const Run2 r = ring[p];
         const float x[8] = {r.x0.x, r.x0.y, r.x0.z, r.x0.w, r.x1.x, r.x1.y, r.x1.z, r.x1.w};
-        ring[p % RING] = p + RING < F ? load(j, p + RING) : load(jn, p + RING - F);
+        ring[p] = load(jn, p);
         mma(acc, make_frag<PK::a>(x), hb[kb]);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) h[m][i] = acc[i] + bc[m][i];
+      for (int i = 0; i < 4; ++i) h[t][i] = acc[i] + bc[t][i];
     }
   };
-  // two steps per trip so the B sets alternate without copies
+  // two steps per trip: the B sets and the LDS buffers alternate
   for (int j = 0; j < a.n; j += 2) {
-    step(bq[0], bq[1], j);
-    if (j + 1 < a.n) step(bq[1], bq[0], j + 1);
+    step(bq[0], bq[1], j, std::integral_constant<int, 0>{});
+    if (j + 1 < a.n) step(bq[1], bq[0], j + 1, std::integral_constant<int, 1>{});
   }
   if (a.h_final) {
 #pragma unroll
-    for (int m = 0; m < MH; ++m)
+    for (int t = 0; t < MHW; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a.h_final[(bh * D + 16 * m + 4 * g + i) * D + c0 + lr] = h[m][i];
+      for (int i = 0; i < 4; ++i) a.h_final[(bh * D + 16 * (m0 + t) + 4 * g + i) * D + c0 + lr] = h[t][i];
   }
 }
 
