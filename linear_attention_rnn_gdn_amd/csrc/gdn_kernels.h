@@ -1214,7 +1214,8 @@ __global__ __launch_bounds__(64 * NWS) void prefix_kernel(PrefixArgs a) {
   constexpr int MH = D / 16, KB = D / 32;
   constexpr int MHW = MH / NWS;   // state row tiles per wave
   static_assert(MHW == 2, "each wave holds one k-block of the state");
-  constexpr int F = MHW * KB;     // A fragments per wave and step (= ring slots)
+  constexpr int F = MHW * KB;     // A fragments per wave and step
+  constexpr int RING = 2 * F;     // two steps in flight: slot P F + p, P the step parity
   __shared__ __align__(16) HF xh[2][KB][64];
   int unit, slice;
   xcd_unit(blockIdx.x, D / 16, a.BH, unit, slice);
@@ -1246,15 +1247,16 @@ __global__ __launch_bounds__(64 * NWS) void prefix_kernel(PrefixArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) bq[t][i] = B[(size_t)(16 * (m0 + t) + 4 * g + i) * D];
   };
-  Run2 ring[F];
+  Run2 ring[RING];
 #pragma unroll
-  for (int p = 0; p < F; ++p) ring[p] = load(0, p);
+  for (int p = 0; p < RING; ++p) ring[p] = load(p < F || a.n < 2 ? 0 : 1, p % F);
   f32x4 bq[2][MHW];
   load_b(0, bq[0]);
 
   auto step = [&](f32x4 (&bc)[MHW], f32x4 (&bn)[MHW], int j, auto Pc) {
     constexpr int P = decltype(Pc)::value;   // step parity: LDS buffer
     const size_t jn = j + 1 < a.n ? j + 1 : j;   // last step: loads repeat (unused)
+    const size_t jr = j + 2 < a.n ? j + 2 : jn;   // ring refill: two steps ahead
     load_b(jn, bn);
     {
       const float x[8] = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
@@ -1277,9 +1279,9 @@ __global__ __launch_bounds__(64 * NWS) void prefix_kernel(PrefixArgs a) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         const int p = t * KB + kb;
-        const Run2 r = ring[p];
+        const Run2 r = ring[P * F + p];
         const float x[8] = {r.x0.x, r.x0.y, r.x0.z, r.x0.w, r.x1.x, r.x1.y, r.x1.z, r.x1.w};
-        ring[p] = load(jn, p);
+        ring[P * F + p] = load(jr, p);
         mma(acc, make_frag<PK::a>(x), hb[kb]);
       }
 #pragma unroll
