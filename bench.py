@@ -293,9 +293,10 @@ def main():
         o = torch.empty((w.B, w.T, w.Hv, w.dv), dtype=torch.float32, device="cuda")
         hT = torch.empty((w.B, w.Hv, w.dk, w.dv), dtype=torch.float32, device="cuda")
 
-        def step(stages=None):
+        def step(stages=None, events=None):
             gdn.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"], chunk=w.chunk,
-                          n_groups=w.n_groups, workspace=ws, out=o, final_state=hT, stages=stages)
+                          n_groups=w.n_groups, workspace=ws, out=o, final_state=hT, stages=stages,
+                          events=events)
         return x, step
 
     w = WORKLOADS[args.workload]
@@ -313,22 +314,26 @@ def main():
         print(json.dumps({"profile_run": w.name, "ms_per_step": ms}), flush=True)
         return
 
-    # per-kernel times: the same steps issued stage by stage on the same
-    # stream with events between the stages, all steps queued back to back
-    # (so no interval holds host launch latency); the first step is dropped
+    # per-kernel times: the same steps again, each kernel launched with a pair
+    # of HIP events that record its own start and end on the launch stream
+    # (gdn_chunk_fwd_timed), all steps queued back to back; the first dropped
     names = [n for n in ("prep", "fold", "prefix", "walk", "out")
              if (w.n_groups > 1 or n not in ("fold", "prefix"))]
+    bit = {n: stage_bits[n].bit_length() - 1 for n in names}
     nst = args.steps + 1
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(nst)]
+    ev = [[[None] * 5, [None] * 5] for _ in range(nst)]
+    for k in range(nst):
+        for n in names:
+            for side in (0, 1):
+                e = torch.cuda.Event(enable_timing=True)
+                e.record()   # creates the event
+                ev[k][side][bit[n]] = e
     torch.cuda.synchronize()
     for k in range(nst):
-        ev[k][0].record()
-        for i, n in enumerate(names):
-            step(stage_bits[n])
-            ev[k][i + 1].record()
+        step(events=(ev[k][0], ev[k][1]))
     torch.cuda.synchronize()
-    stage_ms = {n: sum(ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(1, nst)) / args.steps
-                for i, n in enumerate(names)}
+    stage_ms = {n: sum(ev[k][0][bit[n]].elapsed_time(ev[k][1][bit[n]]) for k in range(1, nst)) / args.steps
+                for n in names}
 
     flops, nbytes = algorithmic(w)
     sb = stage_bytes(w)

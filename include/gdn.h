@@ -122,6 +122,19 @@ gdn_status gdn_chunk_fwd_stages(const gdn_shape *shape, int32_t stages, const vo
                                 const float *h0, void *o, float *h_T, void *ws, size_t ws_bytes,
                                 void *hip_stream);
 
+/* gdn_chunk_fwd_stages that also times each launched stage's kernel: the
+ * kernel of stage bit b (GDN_STAGE_* == 1 << b, b = 0..4) records its own
+ * start into ev_start[b] and its end into ev_stop[b] (hipExtLaunchKernel), so
+ * hipEventElapsedTime(ev_start[b], ev_stop[b]) is the kernel's duration with
+ * no event packet between kernels.  The events are hipEvent_t handles the
+ * caller created (with timing) and owns; ev_start or ev_stop may be null, and
+ * so may any entry (that stage is then not timed).  Other arguments, checks
+ * and results as gdn_chunk_fwd_stages.  Measurement aid for benchmarks.      */
+gdn_status gdn_chunk_fwd_timed(const gdn_shape *shape, int32_t stages, const void *q,
+                               const void *k, const void *v, const float *g, const float *beta,
+                               const float *h0, void *o, float *h_T, void *ws, size_t ws_bytes,
+                               void *hip_stream, void *const *ev_start, void *const *ev_stop);
+
 /* Per-group affine pairs of the chunk-group split (shape->n_groups >= 1
  * groups of equal length; 0 is taken as 1).  For group j of value head h:
  *   A[b,h,j] = product over the group's tokens t (latest on the left) of

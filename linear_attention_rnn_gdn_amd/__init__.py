@@ -44,7 +44,8 @@ class GdnError(RuntimeError):
 _lib = None
 
 SYMBOLS = ("gdn_status_str", "gdn_validate", "gdn_workspace_size", "gdn_chunk_fwd",
-           "gdn_chunk_fwd_stages", "gdn_chunk_fold", "gdn_compose_prefix", "gdn_chunk_transform")
+           "gdn_chunk_fwd_stages", "gdn_chunk_fwd_timed", "gdn_chunk_fold", "gdn_compose_prefix",
+           "gdn_chunk_transform")
 STAGE_PREP, STAGE_FOLD, STAGE_PREFIX, STAGE_WALK, STAGE_OUT, STAGE_ALL = 1, 2, 4, 8, 16, 31
 
 
@@ -68,6 +69,8 @@ def lib():
         L.gdn_chunk_fwd.restype = I
         L.gdn_chunk_fwd_stages.argtypes = [SP, I] + [P] * 9 + [SZ, P]
         L.gdn_chunk_fwd_stages.restype = I
+        L.gdn_chunk_fwd_timed.argtypes = [SP, I] + [P] * 9 + [SZ, P, P, P]
+        L.gdn_chunk_fwd_timed.restype = I
         L.gdn_chunk_fold.argtypes = [SP] + [P] * 7 + [SZ, P]
         L.gdn_chunk_fold.restype = I
         L.gdn_compose_prefix.argtypes = [I, I, I, I] + [P] * 5 + [I, P]
@@ -146,9 +149,11 @@ def _inputs(q, k, v, g, beta):
 
 def chunk_fwd(q, k, v, g, beta, h0=None, chunk=128, n_groups=0, o_dtype=torch.float32,
               output_final_state=True, workspace=None, out=None, final_state=None, stream=None,
-              stages=None):
+              stages=None, events=None):
     """Gated DeltaNet chunked forward (gdn_chunk_fwd; gdn_chunk_fwd_stages when
-    ``stages`` is a mask of STAGE_* bits).
+    ``stages`` is a mask of STAGE_* bits; gdn_chunk_fwd_timed when ``events`` =
+    (starts, stops) gives, per stage bit b = 0..4, timing torch.cuda.Event
+    objects (already recorded once, so that they exist) or None).
 
     q, k [B,T,H_qk,d_k]; v [B,T,H_v,d_v] (bf16 or fp32); g, beta [B,T,H_v] fp32;
     h0 [B,H_v,d_k,d_v] fp32 or None.  Returns (o [B,T,H_v,d_v] o_dtype, h_T or None)."""
@@ -168,7 +173,12 @@ def chunk_fwd(q, k, v, g, beta, h0=None, chunk=128, n_groups=0, o_dtype=torch.fl
         _need(hT, "h_T", torch.float32, (B, Hv, dk, dv), dev)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(o), _ptr(hT),
             _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream(stream))
-    if stages is None:
+    if events is not None:
+        arr = [(ctypes.c_void_p * 5)(*[e.cuda_event if e is not None else None for e in evs])
+               for evs in events]
+        _check(lib().gdn_chunk_fwd_timed(ctypes.byref(shape), int(STAGE_ALL if stages is None else stages),
+                                         *args, arr[0], arr[1]), "gdn_chunk_fwd_timed")
+    elif stages is None:
         _check(lib().gdn_chunk_fwd(ctypes.byref(shape), *args), "gdn_chunk_fwd")
     else:
         _check(lib().gdn_chunk_fwd_stages(ctypes.byref(shape), int(stages), *args),

@@ -2,6 +2,7 @@
 //
 // Host side only: argument checks, workspace carving and kernel launches on
 // the caller's stream.  No allocation, no synchronisation, no global state.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -78,16 +79,31 @@ int num_cus() {
   return n;
 }
 
+// Where a kernel goes: the stream, and optionally two timing events that
+// record the kernel's own start and end (hipExtLaunchKernel; no event packets
+// between kernels).
+struct Lx {
+  hipStream_t st;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+};
+template <typename K, typename... Args>
+void launch(K kernel, dim3 grid, dim3 block, const Lx &x, Args... args) {
+  if (x.e0 || x.e1)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, x.st, x.e0, x.e1, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, x.st, args...);
+}
+
 template <int C, typename TI, int MODE, bool FWD = true>
-gdn_status launch_prep(const FwdArgs &a, hipStream_t st) {
+gdn_status launch_prep(const FwdArgs &a, const Lx &x) {
   const long units = (long)a.nn * a.B * a.Hv;   // one workgroup per (chunk, head)
-  hipLaunchKernelGGL((prep_kernel<C, TI, MODE, FWD>), dim3((unsigned)units), dim3(PNT), 0, st, a);
+  launch(prep_kernel<C, TI, MODE, FWD>, dim3((unsigned)units), dim3(PNT), x, a);
   return check_launch();
 }
 
 
 template <int C, typename TI, int MODE, int KIND>
-gdn_status launch_walk(const FwdArgs &a, hipStream_t st) {
+gdn_status launch_walk(const FwdArgs &a, const Lx &x) {
   const int width = KIND == FOLD ? 2 * D : D;
   // one wave per 16-column slice.  Enough units to give every compute unit
   // two workgroups: 8 slices per workgroup sharing their operands through
@@ -95,38 +111,44 @@ gdn_status launch_walk(const FwdArgs &a, hipStream_t st) {
   // or 4 waves that split its rows, so the walk spreads over the chip.
   const long units = (long)a.B * a.Hv * a.jobs;
   if (units * (width / 128) >= 512) {
-    hipLaunchKernelGGL((walk_shared_kernel<C, TI, MODE, KIND, 8>), dim3((unsigned)(units * (width / 128))), dim3(512), 0,
-                       st, a);
+    launch(walk_shared_kernel<C, TI, MODE, KIND, 8>, dim3((unsigned)(units * (width / 128))), dim3(512), x, a);
   } else {
     constexpr int NWS = C >= 128 ? 4 : 2;   // waves per slice: whole k-blocks of V' rows each
-    hipLaunchKernelGGL((walk_ring_kernel<C, TI, MODE, KIND, NWS>), dim3((unsigned)(units * (width / 16))), dim3(64 * NWS), 0,
-                       st, a);
+    launch(walk_ring_kernel<C, TI, MODE, KIND, NWS>, dim3((unsigned)(units * (width / 16))), dim3(64 * NWS), x, a);
   }
   return check_launch();
 }
 
 template <int C, typename TI, int MODE, typename TO>
-gdn_status launch_out(const FwdArgs &a, hipStream_t st) {
+gdn_status launch_out(const FwdArgs &a, const Lx &x) {
   const long units = (long)a.nn * a.B * a.Hv;   // one workgroup per (chunk, head)
-  hipLaunchKernelGGL((out_kernel<C, TI, MODE, TO>), dim3((unsigned)units), dim3(NT), 0, st, a);
+  launch(out_kernel<C, TI, MODE, TO>, dim3((unsigned)units), dim3(NT), x, a);
   return check_launch();
 }
 
 gdn_status launch_prefix(int BH, int n, const float *A, const float *Bm, const float *h_init, float *h_in,
-                         float *h_final, bool split, hipStream_t st) {
+                         float *h_final, bool split, const Lx &x) {
   PrefixArgs p{BH, n, A, Bm, h_init, h_in, h_final};
   const unsigned blocks = (unsigned)(D / 16) * BH;   // one workgroup per 16-column slice
   constexpr int NWS = 4;                              // waves per slice, 32 state rows each
   if (split)
-    hipLaunchKernelGGL((prefix_kernel<P_SPLIT_AB, NWS>), dim3(blocks), dim3(64 * NWS), 0, st, p);
+    launch(prefix_kernel<P_SPLIT_AB, NWS>, dim3(blocks), dim3(64 * NWS), x, p);
   else
-    hipLaunchKernelGGL((prefix_kernel<P_F32, NWS>), dim3(blocks), dim3(64 * NWS), 0, st, p);
+    launch(prefix_kernel<P_F32, NWS>, dim3(blocks), dim3(64 * NWS), x, p);
   return check_launch();
 }
 
 template <int C, typename TI, int MODE>
 gdn_status run_fwd(const gdn_shape &s, int stages, const void *q, const void *k, const void *v, const float *g,
-                   const float *beta, const float *h0, void *o, float *h_T, char *ws, hipStream_t st) {
+                   const float *beta, const float *h0, void *o, float *h_T, char *ws, hipStream_t st,
+                   void *const *ev0 = nullptr, void *const *ev1 = nullptr) {
+  // stage bit b (GDN_STAGE_* = 1 << b) launches with events ev0[b], ev1[b]
+  auto lx = [&](int b) {
+    Lx x{st};
+    if (ev0) x.e0 = reinterpret_cast<hipEvent_t>(ev0[b]);
+    if (ev1) x.e1 = reinterpret_cast<hipEvent_t>(ev1[b]);
+    return x;
+  };
   const Layout L = layout(s);
   FwdArgs a = base_args(s);
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.o = o;
@@ -137,27 +159,27 @@ gdn_status run_fwd(const gdn_shape &s, int stages, const void *q, const void *k,
   a.Hs = reinterpret_cast<float *>(ws + L.Hs);
   a.Vn = reinterpret_cast<float *>(ws + L.Vn);
   const int J = groups_of(s);
-  if (stages & GDN_STAGE_PREP) GDN_TRY((launch_prep<C, TI, MODE>(a, st)));
+  if (stages & GDN_STAGE_PREP) GDN_TRY((launch_prep<C, TI, MODE>(a, lx(0))));
   if (J == 1) {
     a.init = h0; a.init_per_job = 0; a.fin = h_T;
-    if (stages & GDN_STAGE_WALK) GDN_TRY((launch_walk<C, TI, MODE, WALK>(a, st)));
+    if (stages & GDN_STAGE_WALK) GDN_TRY((launch_walk<C, TI, MODE, WALK>(a, lx(3))));
   } else {
     FwdArgs f = a;
     f.jobs = J; f.cpj = a.N / J;
     f.pairA = reinterpret_cast<float *>(ws + L.A);
     f.pairB = reinterpret_cast<float *>(ws + L.Bp);
-    if (stages & GDN_STAGE_FOLD) GDN_TRY((launch_walk<C, TI, MODE, FOLD>(f, st)));
+    if (stages & GDN_STAGE_FOLD) GDN_TRY((launch_walk<C, TI, MODE, FOLD>(f, lx(1))));
     float *h_in = reinterpret_cast<float *>(ws + L.Hin);
     if (stages & GDN_STAGE_PREFIX)
-      GDN_TRY(launch_prefix(s.B * s.H_v, J, f.pairA, f.pairB, h0, h_in, h_T, MODE == MODE_BF16, st));
+      GDN_TRY(launch_prefix(s.B * s.H_v, J, f.pairA, f.pairB, h0, h_in, h_T, MODE == MODE_BF16, lx(2)));
     FwdArgs r = a;
     r.jobs = J; r.cpj = a.N / J;
     r.init = h_in; r.init_per_job = 1; r.fin = nullptr;
-    if (stages & GDN_STAGE_WALK) GDN_TRY((launch_walk<C, TI, MODE, WALK>(r, st)));
+    if (stages & GDN_STAGE_WALK) GDN_TRY((launch_walk<C, TI, MODE, WALK>(r, lx(3))));
   }
   if (!(stages & GDN_STAGE_OUT)) return GDN_OK;
-  if (s.o_dtype == GDN_F32) return launch_out<C, TI, MODE, float>(a, st);
-  return launch_out<C, TI, MODE, __bf16>(a, st);
+  if (s.o_dtype == GDN_F32) return launch_out<C, TI, MODE, float>(a, lx(4));
+  return launch_out<C, TI, MODE, __bf16>(a, lx(4));
 }
 
 template <int C, typename TI, int MODE>
@@ -170,10 +192,10 @@ gdn_status run_fold(const gdn_shape &s, const void *k, const void *v, const floa
   a.W = ws + L.W;
   a.Kt = ws + L.Kt;
   a.U = reinterpret_cast<float *>(ws + L.U);
-  GDN_TRY((launch_prep<C, TI, MODE>(a, st)));
+  GDN_TRY((launch_prep<C, TI, MODE>(a, Lx{st})));
   const int J = groups_of(s);
   a.jobs = J; a.cpj = a.N / J; a.pairA = A; a.pairB = Bm;
-  return launch_walk<C, TI, MODE, FOLD>(a, st);
+  return launch_walk<C, TI, MODE, FOLD>(a, Lx{st});
 }
 
 template <int C, typename TI, int MODE>
@@ -181,14 +203,14 @@ gdn_status run_transform(const gdn_shape &s, const void *k, const void *v, const
                          float *G, float *Tm, float *W, float *U, hipStream_t st) {
   FwdArgs a = base_args(s);
   a.k = k; a.v = v; a.g = g; a.beta = beta; a.G = G; a.Tm = Tm; a.W = W; a.U = U;
-  return launch_prep<C, TI, MODE, false>(a, st);
+  return launch_prep<C, TI, MODE, false>(a, Lx{st});
 }
 
 struct FwdCall {
   const gdn_shape &s; int stages; const void *q, *k, *v; const float *g, *beta, *h0; void *o; float *h_T;
-  char *w; hipStream_t st;
+  char *w; hipStream_t st; void *const *ev0 = nullptr, *const *ev1 = nullptr;
   template <int C, typename TI, int MODE> gdn_status run() {
-    return run_fwd<C, TI, MODE>(s, stages, q, k, v, g, beta, h0, o, h_T, w, st);
+    return run_fwd<C, TI, MODE>(s, stages, q, k, v, g, beta, h0, o, h_T, w, st, ev0, ev1);
   }
 };
 struct FoldCall {
@@ -268,6 +290,13 @@ gdn_status gdn_chunk_fwd(const gdn_shape *s, const void *q, const void *k, const
 gdn_status gdn_chunk_fwd_stages(const gdn_shape *s, int32_t stages, const void *q, const void *k, const void *v,
                                 const float *g, const float *beta, const float *h0, void *o, float *h_T,
                                 void *ws, size_t ws_bytes, void *hip_stream) {
+  return gdn_chunk_fwd_timed(s, stages, q, k, v, g, beta, h0, o, h_T, ws, ws_bytes, hip_stream, nullptr, nullptr);
+}
+
+gdn_status gdn_chunk_fwd_timed(const gdn_shape *s, int32_t stages, const void *q, const void *k, const void *v,
+                               const float *g, const float *beta, const float *h0, void *o, float *h_T,
+                               void *ws, size_t ws_bytes, void *hip_stream, void *const *ev_start,
+                               void *const *ev_stop) {
   GDN_TRY(gdn_validate(s));
   if (stages & ~GDN_STAGE_ALL) return GDN_ERR_SHAPE;
   hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
@@ -285,7 +314,7 @@ gdn_status gdn_chunk_fwd_stages(const gdn_shape *s, int32_t stages, const void *
     if (misaligned(p)) return GDN_ERR_ALIGN;
   if (ws_bytes < layout(*s).total) return GDN_ERR_WORKSPACE;
   char *w = reinterpret_cast<char *>(ws);
-  FwdCall f{*s, stages, q, k, v, g, beta, h0, o, h_T, w, st};
+  FwdCall f{*s, stages, q, k, v, g, beta, h0, o, h_T, w, st, ev_start, ev_stop};
   return dispatch(*s, f);
 }
 
@@ -313,7 +342,7 @@ gdn_status gdn_compose_prefix(int32_t batch_heads, int32_t n, int32_t d_k, int32
                         (const void *)h_final})
     if (misaligned(p)) return GDN_ERR_ALIGN;
   return launch_prefix(batch_heads, n, A, Bm, h_init, h_in, h_final, (flags & GDN_PREFIX_SPLIT_BF16) != 0,
-                       reinterpret_cast<hipStream_t>(hip_stream));
+                       Lx{reinterpret_cast<hipStream_t>(hip_stream)});
 }
 
 gdn_status gdn_chunk_transform(const gdn_shape *s, const void *k, const void *v, const float *g,

@@ -226,6 +226,30 @@ def test_stages_one_by_one_equal_one_call(gdn, C, N, ng):
     assert torch.equal(o1, o2) and torch.equal(h1, h2) and torch.equal(o1, o3)
 
 
+@pytest.mark.parametrize("ng", [0, 4])
+def test_timed_call_equals_plain_call(gdn, ng):
+    # gdn_chunk_fwd_timed (bench.py's per-kernel timing) computes what
+    # gdn_chunk_fwd does, bit for bit, and every timed stage's events bound a
+    # positive duration; untimed stages (null entries) are still launched
+    w = WORKLOADS["tiny"].replace(T=128 * 16, Hqk=2, Hv=4, chunk=128, dtype="bf16", h0_std=0.05)
+    x = make_inputs(w, device="cuda", seed=7 + ng)
+    args = (x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"])
+    o1, h1 = gdn.chunk_fwd(*args, chunk=128, n_groups=ng)
+    bits = [0, 3, 4] if ng <= 1 else [0, 1, 2, 3, 4]
+    starts, stops = [None] * 5, [None] * 5
+    for b in bits[:-1]:   # the last stage launched untimed
+        for lst in (starts, stops):
+            e = torch.cuda.Event(enable_timing=True)
+            e.record()
+            lst[b] = e
+    torch.cuda.synchronize()
+    o2, h2 = gdn.chunk_fwd(*args, chunk=128, n_groups=ng, events=(starts, stops))
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
+    for b in bits[:-1]:
+        assert starts[b].elapsed_time(stops[b]) > 0
+
+
 # ---------------------------------------------------------------------------
 # rows a7-a9: fold, exclusive prefix, replay
 
