@@ -160,6 +160,44 @@ def test_forward_small_shapes(gdn, dtype, C, T, Hqk, Hv, h0):
     _check("h_T", h, h_ref, TOL[dtype], ro)
 
 
+@pytest.mark.parametrize("case", ["beta0", "overwrite", "strong_decay", "resets", "large_scale"])
+@pytest.mark.parametrize("C", [64, 128])
+def test_degenerate_inputs(gdn, case, C):
+    # the rule's special cases, against the fp64 oracle at the bf16 bar:
+    #   beta0         beta = 0: no writes, the state only decays (o = e^G Q h0)
+    #   overwrite     g = 0, beta = 1, one-hot keys repeating within a chunk:
+    #                 each write replaces the row of its key (S has unit entries)
+    #   strong_decay  g = -20 per token: e^G underflows to 0 inside a chunk
+    #   resets        usual g, with g = -60 every 37th token (state wiped)
+    #   large_scale   v and h0 scaled by 1e3 (o and h_T scale with them)
+    w = WORKLOADS["tiny"].replace(T=C * 6, Hqk=1, Hv=2, chunk=C, dtype="bf16", h0_std=0.5)
+    x = make_inputs(w, device="cuda", seed=11 + C)
+    T = w.T
+    if case == "beta0":
+        x["beta"] = torch.zeros_like(x["beta"])
+    elif case == "overwrite":
+        x["g"] = torch.zeros_like(x["g"])
+        x["beta"] = torch.ones_like(x["beta"])
+        idx = (torch.arange(T, device="cuda") * 5) % 24           # 24 distinct keys
+        k = torch.zeros_like(x["k"])
+        k[0, torch.arange(T, device="cuda"), :, idx] = 1.0
+        x["k"] = k
+    elif case == "strong_decay":
+        x["g"] = torch.full_like(x["g"], -20.0)
+    elif case == "resets":
+        g = x["g"].clone()
+        g[:, ::37] = -60.0
+        x["g"] = g
+    elif case == "large_scale":
+        x["v"] = (x["v"].float() * 1e3).to(torch.bfloat16)
+        x["h0"] = x["h0"] * 1e3
+    o, h, o_ref, h_ref = _run_and_compare(gdn, w, x)
+    assert np.isfinite(o).all() and np.isfinite(h).all()
+    ro = _rms(o_ref)
+    _check("o", o, o_ref, TOL["bf16"], ro)
+    _check("h_T", h, h_ref, TOL["bf16"], ro)
+
+
 def test_bf16_output(gdn):
     # a bf16 o carries its own rounding (half an ulp of |o|) on top of the
     # computation error
