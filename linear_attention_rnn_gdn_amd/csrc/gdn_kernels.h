@@ -332,94 +332,77 @@ __device__ __forceinline__ Frag<K> xt_frag(const TI *sxt, int d, int k0, int sw)
 // One level (block size BS) of the doubling ladder of step (5) below, fully
 // unrolled: for each 2BS diagonal block [[P,0],[L,Q]] of the packed T, the
 // lower-left block becomes -X_Q L X_P.  Tiles are shared out over the PW
-// waves; each tile's operands are read from LDS in one batch before its
-// products.  sM holds M1 = L X_P transposed (nb blocks of BS x (BS+4)).
+// waves; k-blocks that the triangular factors make zero are skipped, not
+// multiplied as zeros.  sM holds M1 = L X_P transposed (nb blocks of
+// BS x (BS+4)).
 template <int C, int BS, int PL, int PW>
 __device__ __forceinline__ void ladder_level(float *sT, float *sM, int wave, int lane) {
   using TRI = Tri<C>;
   constexpr int NB = C / (2 * BS), TB = BS / 16, NTILE = NB * TB * TB, PER = (NTILE + PW - 1) / PW;
   constexpr int LDM = BS + 4, KBM = (BS + 31) / 32;
-  constexpr int GRP = (PER < 2 || PW > 4) ? 1 : 2;   // tiles per batch of reads (registers allowing)
   const int lr = lane & 15, lk = (lane >> 4) * 8, lq = (lane >> 4) * 4;
-  // M1 = L X_P (stored transposed in sM)
+  // k-values past a 16-wide block (lane groups 2 and 3) enter as zeros
+  const bool kin = BS >= 32 || lk < BS;
+  // M1 = L X_P (stored transposed in sM).  X_P is lower triangular: the
+  // k-blocks above column tile ni's diagonal are skipped (a uniform branch).
 #pragma unroll
-  for (int u0 = 0; u0 < PER; u0 += GRP) {
-    float a8[GRP][KBM][8], b8[GRP][KBM][8];
-    int tl[GRP];
+  for (int u = 0; u < PER; ++u) {
+    const int tt = wave + PW * u;
+    if (tt >= NTILE) break;
+    const int blk = tt / (TB * TB), ti = tt % (TB * TB), mi = ti / TB, ni = ti % TB;
+    const int s = blk * 2 * BS, kb0 = (16 * ni) / 32;
+    f32x4 acc = zero4();
 #pragma unroll
-    for (int v = 0; v < GRP; ++v) {
-      const int tt = wave + PW * (u0 + v);
-      tl[v] = tt;
-      const int blk = tt / (TB * TB), ti = tt % (TB * TB), mi = ti / TB, ni = ti % TB;
-      const int s = blk * 2 * BS, kb0 = (16 * ni) / 32;
+    for (int kb = 0; kb < KBM; ++kb) {
+      if (kb < kb0) continue;
+      const int k0 = 32 * kb + lk;
+      float a8[8], b8[8];
+      if (kin) {
+        ld8(sT + TRI::at_t((s + BS) / 16 + mi, lr, s + k0), a8);
+        // column s + 16 ni + lr of X_P, rows s + k0 .. + 7 (one row tile)
+        const int mk = (s + 32 * kb) / 16 + (lane >> 5);
+        const float *col = sT + TRI::at_t(mk, lk & 15, s + 16 * ni + lr);
+        const int str = TRI::len(mk) + 4;
 #pragma unroll
-      for (int kb = 0; kb < KBM; ++kb) {
-        const int k0 = 32 * kb + lk;
-        if (tt < NTILE && kb >= kb0 && k0 < BS) {
-          ld8(sT + TRI::at_t((s + BS) / 16 + mi, lr, s + k0), a8[v][kb]);
-          // column s + 16 ni + lr of X_P, rows s + k0 .. + 7 (one row tile)
-          const int mk = (s + 32 * kb) / 16 + (lane >> 5);
-          const float *col = sT + TRI::at_t(mk, lk & 15, s + 16 * ni + lr);
-          const int str = TRI::len(mk) + 4;
+        for (int jj = 0; jj < 8; ++jj) b8[jj] = col[jj * str];
+      } else {
 #pragma unroll
-          for (int j = 0; j < 8; ++j) b8[v][kb][j] = col[j * str];
-        } else {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) a8[v][kb][j] = b8[v][kb][j] = 0.f;
-        }
+        for (int jj = 0; jj < 8; ++jj) a8[jj] = b8[jj] = 0.f;
       }
+      mma_k32<PL>(acc, a8, b8);
     }
-#pragma unroll
-    for (int v = 0; v < GRP; ++v) {
-      const int tt = tl[v];
-      if (tt >= NTILE) continue;
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int kb = 0; kb < KBM; ++kb) mma_k32<PL>(acc, a8[v][kb], b8[v][kb]);
-      const int blk = tt / (TB * TB), ti = tt % (TB * TB), mi = ti / TB, ni = ti % TB;
-      float *M = sM + blk * BS * LDM;
-      *reinterpret_cast<float4 *>(M + (16 * ni + lr) * LDM + 16 * mi + lq) = float4{acc[0], acc[1], acc[2], acc[3]};
-    }
+    float *M = sM + blk * BS * LDM;
+    *reinterpret_cast<float4 *>(M + (16 * ni + lr) * LDM + 16 * mi + lq) = float4{acc[0], acc[1], acc[2], acc[3]};
   }
   lds_barrier();
-  // L <- -X_Q M1
+  // L <- -X_Q M1.  X_Q is lower triangular: row tile mi needs k < 16(mi+1).
 #pragma unroll
-  for (int u0 = 0; u0 < PER; u0 += GRP) {
-    float a8[GRP][KBM][8], b8[GRP][KBM][8];
-    int tl[GRP];
+  for (int u = 0; u < PER; ++u) {
+    const int tt = wave + PW * u;
+    if (tt >= NTILE) break;
+    const int blk = tt / (TB * TB), ti = tt % (TB * TB), mi = ti / TB, ni = ti % TB;
+    const int s = blk * 2 * BS;
+    const float *M = sM + blk * BS * LDM;
+    f32x4 acc = zero4();
 #pragma unroll
-    for (int v = 0; v < GRP; ++v) {
-      const int tt = wave + PW * (u0 + v);
-      tl[v] = tt;
-      const int blk = tt / (TB * TB), ti = tt % (TB * TB), mi = ti / TB, ni = ti % TB;
-      const int s = blk * 2 * BS;
-      const float *M = sM + blk * BS * LDM;
+    for (int kb = 0; kb < KBM; ++kb) {
+      if (kb * 32 >= 16 * (mi + 1)) continue;
+      const int k0 = 32 * kb + lk;
+      float a8[8], b8[8];
+      if (kin) {
+        ld8(sT + TRI::at_t((s + BS) / 16 + mi, lr, s + BS + k0), a8);
+        ld8(M + (16 * ni + lr) * LDM + k0, b8);
+      } else {
 #pragma unroll
-      for (int kb = 0; kb < KBM; ++kb) {
-        const int k0 = 32 * kb + lk;
-        if (tt < NTILE && kb * 32 < 16 * (mi + 1) && k0 < BS) {
-          ld8(sT + TRI::at_t((s + BS) / 16 + mi, lr, s + BS + k0), a8[v][kb]);
-          ld8(M + (16 * ni + lr) * LDM + k0, b8[v][kb]);
-        } else {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) a8[v][kb][j] = b8[v][kb][j] = 0.f;
-        }
+        for (int jj = 0; jj < 8; ++jj) a8[jj] = b8[jj] = 0.f;
       }
+      mma_k32<PL>(acc, a8, b8);
     }
+    const int mr = (s + BS) / 16 + mi;
+    float *rp = sT + TRI::at_t(mr, lq, s + 16 * ni + lr);
+    const int rstr = TRI::len(mr) + 4;
 #pragma unroll
-    for (int v = 0; v < GRP; ++v) {
-      const int tt = tl[v];
-      if (tt >= NTILE) continue;
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int kb = 0; kb < KBM; ++kb) mma_k32<PL>(acc, a8[v][kb], b8[v][kb]);
-      const int blk = tt / (TB * TB), ti = tt % (TB * TB), mi = ti / TB, ni = ti % TB;
-      const int s = blk * 2 * BS, mr = (s + BS) / 16 + mi;
-      float *rp = sT + TRI::at_t(mr, lq, s + 16 * ni + lr);
-      const int rstr = TRI::len(mr) + 4;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) rp[i * rstr] = -acc[i];
-    }
+    for (int i = 0; i < 4; ++i) rp[i * rstr] = -acc[i];
   }
   lds_barrier();
 }
