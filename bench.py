@@ -73,7 +73,7 @@ def stage_bytes(w, o_bytes=4):
     h0_b = st if w.h0_std > 0 else 0
     pairs = 4 * BHv * J * (dk * dk + dk * dv)
     hin = 4 * BHv * J * dk * dv
-    Kt_b = W_b                      # K^T per chunk and value head, input dtype
+    Kt_b = k_b                      # K^T per chunk and query/key head, input dtype
     out = {
         "prep": k_b + v_b + gb_b + G_b + W_b + Kt_b + U_b,
         "out": q_b + k_b + G_b + Hs_b + Vn_b + tok * w.Hv * dv * o_bytes,

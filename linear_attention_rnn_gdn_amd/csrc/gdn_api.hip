@@ -31,7 +31,7 @@ Layout layout(const gdn_shape &s) {
   size_t off = 0;
   L.G = off;  off += align_up(BH * N * C * 4);
   L.W = off;  off += align_up(BH * N * C * D * in_bytes);
-  L.Kt = off; off += align_up(BH * N * C * D * in_bytes);
+  L.Kt = off; off += align_up((size_t)s.B * s.H_qk * N * C * D * in_bytes);   // per key head
   L.U = off;  off += align_up(BH * N * C * D * 4);
   L.Hs = off; off += align_up(BH * N * D * D * 4);   // fp32, or bf16 hi + lo planes
   L.Vn = off; off += align_up(BH * N * C * D * 4);

@@ -43,7 +43,9 @@
 // (j >= 4) within its block of 32 (the order of two stacked result tiles).
 //   G   [cb][C] fp32 decay cumsum
 //   Wf  [cb][C/16][D/32][64][8]  W[16m + lr][32kb + kk(g, j)], input dtype
-//   Ktf [cb][D/16][C/32][64][8]  K[32kb + kk(g, j)][16m + lr], input dtype
+//   Ktf [cq][D/16][C/32][64][8]  K[32kb + kk(g, j)][16m + lr], input dtype,
+//       once per query/key head (cq = (b*H_qk + hq)*N + n): the value heads
+//       that share a key head share its K^T
 //   Uf  [cb][C/16][D/16][64][4]  U[16m + 4g + i][16nd + lr], fp32
 //   Hsf [cb][D/16][D/16][64][4]  chunk-start state h[16m + 4g + i][16s + lr]
 //   Vnf [cb][D/16][C/16][64][4]  corrected values V'[16m + 4g + i][16s + lr]
@@ -162,6 +164,13 @@ struct FwdArgs {
   int n0, nn;                     // chunk range [n0, n0 + nn) of this launch (prep, out, single walk)
   void *o;                        // out output
 };
+
+// Offset from a value head's chunk index cb = bh*N + n to the chunk index of
+// its query/key head, cq = (b*H_qk + hq)*N + n (K^T is stored per key head).
+__device__ __forceinline__ long long kt_offset(const FwdArgs &a, size_t bh) {
+  const size_t b = bh / a.Hv, hv = bh % a.Hv, hq = hv / (a.Hv / a.Hqk);
+  return ((long long)(b * a.Hqk + hq) - (long long)bh) * a.N;
+}
 
 // 1-D workgroup index of the per-chunk kernels (prep, out) -> (chunk n,
 // batch row b, value head hv), heads fastest.  The workgroups resident at one
@@ -583,7 +592,8 @@ __global__ __launch_bounds__(PNT, 4) void prep_kernel(FwdArgs a) {   // two work
   // K^T -> LDS from the registers
   if (!vhalf) TileBlock<C, TI, PNT / 2>::put_transposed(tix, sX, xw);
   lds_barrier();
-  if constexpr (FWD) {
+  // (written by the first value head of each key head only)
+  if (FWD && hv % (a.Hv / a.Hqk) == 0) {
     // K^T fragments for the walk, fragment-major: (d tile m, k-block kb, lane)
     // holds K[r][16 m + lr] for the 8 tokens r = 32 kb + {4g..4g+3,
     // 16+4g..16+4g+3} (the k order of the walk's register-chained operand);
@@ -592,7 +602,7 @@ __global__ __launch_bounds__(PNT, 4) void prep_kernel(FwdArgs a) {   // two work
     // k-block kb = f % KBC
     constexpr int KBC = C / 32, NF = D * C / 8 / 64;   // fragments (1 KB each)
     static_assert(NF % PW == 0, "whole fragments per wave");
-    TI *Ktg = reinterpret_cast<TI *>(a.Kt) + cb * D * C + lane * 8;
+    TI *Ktg = reinterpret_cast<TI *>(a.Kt) + (cb + kt_offset(a, bh)) * D * C + lane * 8;
     constexpr int VE = 16 / sizeof(TI);
 #pragma unroll
     for (int i = 0; i < NF / PW; ++i) {
@@ -763,6 +773,7 @@ __global__ __launch_bounds__(64 * WPG) void walk_shared_kernel(FwdArgs a) {
   const bool has_u = KIND == WALK || c0 >= D;
   const int us = KIND == WALK ? slice : slice - D / 16;   // U column tile
   const size_t cb0 = bh * a.N + a.n0 + (size_t)job * a.cpj;
+  const long long ktoff = kt_offset(a, bh);
 
   // state tiles: h[m] holds rows 16m + 4g + i, column c0 + lr
   f32x4 h[MH];
@@ -790,7 +801,7 @@ __global__ __launch_bounds__(64 * WPG) void walk_shared_kernel(FwdArgs a) {
   const unsigned loff = lane * 16 * BPF;
   auto stage = [&](TI *buf, size_t cb) {
     const char *wbase = reinterpret_cast<const char *>(a.W) + cb * C * D * sizeof(TI);
-    const char *kbase = reinterpret_cast<const char *>(a.Kt) + cb * D * C * sizeof(TI);
+    const char *kbase = reinterpret_cast<const char *>(a.Kt) + (cb + ktoff) * D * C * sizeof(TI);
 #pragma unroll
     for (int jj = 0; jj < NBLK / WPG; ++jj) {
       const int j = jj * WPG + wv, p = j / BPF, hh = j % BPF;
@@ -995,6 +1006,7 @@ __global__ __launch_bounds__(64 * NWS) void walk_ring_kernel(FwdArgs a) {
   const int us = KIND == WALK ? slice : slice - D / 16;   // U column tile
   const size_t cb0 = bh * a.N + a.n0 + (size_t)job * a.cpj;
   const int mv0 = w * MVW, mh0 = w * MHW;                 // this wave's first V' / state tile
+  const long long ktoff = kt_offset(a, bh);
 
   // state tiles of this wave: h[t] holds rows 16(mh0+t) + 4g + i, column c0 + lr
   f32x4 h[MHW];
@@ -1021,7 +1033,7 @@ __global__ __launch_bounds__(64 * NWS) void walk_ring_kernel(FwdArgs a) {
   const TI *Kb = reinterpret_cast<const TI *>(a.Kt) + lane * 8;
   auto load = [&](size_t cb, int q) -> AF {
     const TI *src = q < FWW ? Wb + cb * C * D + (size_t)(mv0 * KBW + q) * 512
-                            : Kb + cb * D * C + (size_t)(mh0 * KBK + q - FWW) * 512;
+                            : Kb + (cb + ktoff) * D * C + (size_t)(mh0 * KBK + q - FWW) * 512;
     AF f;
     if constexpr (F32) {
       const float4 x0 = *reinterpret_cast<const float4 *>(src);

@@ -381,6 +381,19 @@ def test_long_sequence_reduced(gdn):
     _check("h_T", h, h_ref, 2e-2, ro)
 
 
+@pytest.mark.parametrize("C", [64, 128])
+def test_forward_throughput_form(gdn, C):
+    # 512 walks (B * H_v): the single walk takes its throughput form (eight
+    # slices per workgroup sharing W and K^T through LDS) instead of the
+    # latency form the shorter walks above take
+    w = WORKLOADS["tiny"].replace(T=3 * C, Hqk=16, Hv=32, chunk=C, dtype="bf16", h0_std=0.02, B=16)
+    x = make_inputs(w, device="cuda", seed=C + 3)
+    o, h, o_ref, h_ref = _run_and_compare(gdn, w, x)
+    ro = _rms(o_ref)
+    _check("o", o, o_ref, 2e-2, ro)
+    _check("h_T", h, h_ref, 2e-2, ro)
+
+
 @pytest.mark.parametrize("name", ["long_256k", "million_1m"])
 def test_long_sequence_full_size_sampled(gdn, name):
     # full length, in the benchmark's launch configuration; the oracle walks
