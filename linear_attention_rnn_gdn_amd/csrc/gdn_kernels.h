@@ -124,13 +124,12 @@ __device__ __forceinline__ void store_result_tiles(float *dst, const f32x4 (&t)[
     char *d = reinterpret_cast<char *>(dst);
 #pragma unroll
     for (int p = 0; p < NTILE / 2; ++p) {
-      bf16x8 hi, lo;
+      float x[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float x = t[2 * p + j / 4][j % 4];
-        hi[j] = (__bf16)x;
-        lo[j] = (__bf16)(x - (float)hi[j]);
-      }
+      for (int j = 0; j < 8; ++j) x[j] = t[2 * p + j / 4][j % 4];
+      bf16x8 hi, lo;
+      if constexpr (ST == ST_BF16) hi = to_bf16x8(x);
+      else to_bf16x8_split(x, hi, lo);
       if constexpr (ST == ST_BF16) {
         st16_stream(d + p * 1024 + lane * 16, hi);
       } else {
@@ -602,7 +601,8 @@ __global__ __launch_bounds__(PNT, 4) void prep_kernel(FwdArgs a) {   // two work
     // k-block kb = f % KBC
     constexpr int KBC = C / 32, NF = D * C / 8 / 64;   // fragments (1 KB each)
     static_assert(NF % PW == 0, "whole fragments per wave");
-    TI *Ktg = reinterpret_cast<TI *>(a.Kt) + (cb + kt_offset(a, bh)) * D * C + lane * 8;
+    const size_t cq = ((size_t)b * a.Hqk + hq) * a.N + n;   // chunk of the key head
+    TI *Ktg = reinterpret_cast<TI *>(a.Kt) + cq * D * C + lane * 8;
     constexpr int VE = 16 / sizeof(TI);
 #pragma unroll
     for (int i = 0; i < NF / PW; ++i) {
@@ -639,12 +639,11 @@ __global__ __launch_bounds__(PNT, 4) void prep_kernel(FwdArgs a) {   // two work
   for (int mdl = 0; mdl < TDW; ++mdl) xsw[mdl] = XT<C, TI>::swz(16 * (md0 + mdl) + lr);
   constexpr int KT = PolicyKinds<PR::wy>::a;   // T' fragments (split)
   constexpr int KX = PolicyKinds<PR::wy>::b;   // K / V fragments (exact data)
-  for (int pass = 0; pass < 2; ++pass) {
-    if (pass == 1) {
-      lds_barrier();
-      if (vhalf) TileBlock<C, TI, PNT / 2>::put_transposed(tix, sX, xw);
-      lds_barrier();
-    }
+  // (one body per pass, the pass a compile-time constant: a runtime choice of
+  // the operand order inside the k loop merges the two MFMA sequences'
+  // accumulators through register copies on every iteration)
+  auto wu_pass = [&](auto pass_c) {
+    constexpr int pass = decltype(pass_c)::value;
     const float *scale = pass == 0 ? sScale : sBeta;
     // one row tile at a time (registers: the other half of the workgroup
     // still holds its V block)
@@ -672,14 +671,14 @@ __global__ __launch_bounds__(PNT, 4) void prep_kernel(FwdArgs a) {   // two work
         for (int mdl = 0; mdl < TDW; ++mdl) {
           // X^T row 16md+lr = column of K (or V)
           const auto xf = xt_frag<KX, C, TI>(sX, 16 * (md0 + mdl) + lr, k0, xsw[mdl]);
-          if (pass == 0) mma(acc[mdl], xf, tf);   // W^T tile (d, r)
-          else mma(acc[mdl], tf, xf);             // U tile (r, d)
+          if constexpr (pass == 0) mma(acc[mdl], xf, tf);   // W^T tile (d, r)
+          else mma(acc[mdl], tf, xf);                       // U tile (r, d)
         }
       }
 #pragma unroll
       for (int mdl = 0; mdl < TDW; ++mdl) {
         const int md = md0 + mdl;
-        if (pass == 0 && FWD) {
+        if constexpr (pass == 0 && FWD) {
           // lane holds W[r][16md + 4g + i], r = 16 mrow + lr.  The walk's
           // fragment (mrow, kb) gives lane (lr, g) the k-values 32 kb +
           // {4g..4g+3, 16+4g..16+4g+3}: tiles md = 2kb and 2kb+1 of this
@@ -695,7 +694,7 @@ __global__ __launch_bounds__(PNT, 4) void prep_kernel(FwdArgs a) {   // two work
           constexpr int VE = 16 / sizeof(WT);
 #pragma unroll
           for (int v = 0; v < 8 / VE; ++v) st16(dst + v * VE, *reinterpret_cast<const uint4 *>(tmp + v * VE));
-        } else if (pass == 0) {
+        } else if constexpr (pass == 0) {
           WT *dst = reinterpret_cast<WT *>(a.W) + (cb * C + 16 * mrow[u] + lr) * D + 16 * md + lq;
 #pragma unroll
           for (int i = 0; i < 4; ++i) dst[i] = from_f32<WT>(acc[mdl][i]);
@@ -709,7 +708,12 @@ __global__ __launch_bounds__(PNT, 4) void prep_kernel(FwdArgs a) {   // two work
         }
       }
     }
-  }
+  };
+  wu_pass(std::integral_constant<int, 0>{});
+  lds_barrier();
+  if (vhalf) TileBlock<C, TI, PNT / 2>::put_transposed(tix, sX, xw);
+  lds_barrier();
+  wu_pass(std::integral_constant<int, 1>{});
 }
 
 // ----------------------------------------------------------------------------

@@ -78,31 +78,48 @@ __device__ __forceinline__ void st8_stream(void *p, const T &v) {
   __builtin_nontemporal_store(__builtin_bit_cast(u32x2, v), reinterpret_cast<u32x2 *>(p));
 }
 
+// Round 8 fp32 values to bf16 (round to nearest even), two per packed
+// convert.  to_bf16x8_split also returns the rounding remainders x - hi,
+// rounded the same way (exact differences in fp32); the widened high halves
+// come from the packed words by a shift (element 2p) and a mask (element
+// 2p + 1), so a value costs about two instructions less than converting it
+// alone and widening it back.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ unsigned pk_bf16(float x0, float x1) {
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{x0, x1}, bf16x2));
+}
+__device__ __forceinline__ bf16x8 to_bf16x8(const float (&x)[8]) {
+  const uint4 u{pk_bf16(x[0], x[1]), pk_bf16(x[2], x[3]), pk_bf16(x[4], x[5]), pk_bf16(x[6], x[7])};
+  return __builtin_bit_cast(bf16x8, u);
+}
+__device__ __forceinline__ void to_bf16x8_split(const float (&x)[8], bf16x8 &hi, bf16x8 &lo) {
+  unsigned h[4], l[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    h[p] = pk_bf16(x[2 * p], x[2 * p + 1]);
+    const float h0 = __builtin_bit_cast(float, h[p] << 16);
+    const float h1 = __builtin_bit_cast(float, h[p] & 0xffff0000u);
+    l[p] = pk_bf16(x[2 * p] - h0, x[2 * p + 1] - h1);
+  }
+  hi = __builtin_bit_cast(bf16x8, uint4{h[0], h[1], h[2], h[3]});
+  lo = __builtin_bit_cast(bf16x8, uint4{l[0], l[1], l[2], l[3]});
+}
+
 template <int P>
 __device__ __forceinline__ void mma_k32(f32x4 &c, const float (&a)[8], const float (&b)[8]) {
   if constexpr (P == P_F32) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], c, 0, 0, 0);
   } else {
-    bf16x8 ah, bh;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      ah[j] = (__bf16)a[j];
-      bh[j] = (__bf16)b[j];
-    }
+    bf16x8 ah, bh, al, bl;
+    if constexpr (P == P_SPLIT_A || P == P_SPLIT_AB) to_bf16x8_split(a, ah, al);
+    else ah = to_bf16x8(a);
+    if constexpr (P == P_SPLIT_B || P == P_SPLIT_AB) to_bf16x8_split(b, bh, bl);
+    else bh = to_bf16x8(b);
     // small terms first
-    if constexpr (P == P_SPLIT_A || P == P_SPLIT_AB) {
-      bf16x8 al;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) al[j] = (__bf16)(a[j] - (float)ah[j]);
-      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, c, 0, 0, 0);
-    }
-    if constexpr (P == P_SPLIT_B || P == P_SPLIT_AB) {
-      bf16x8 bl;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) bl[j] = (__bf16)(b[j] - (float)bh[j]);
-      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, c, 0, 0, 0);
-    }
+    if constexpr (P == P_SPLIT_A || P == P_SPLIT_AB) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, c, 0, 0, 0);
+    if constexpr (P == P_SPLIT_B || P == P_SPLIT_AB) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, c, 0, 0, 0);
     c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, c, 0, 0, 0);
   }
 }
@@ -130,13 +147,10 @@ __device__ __forceinline__ Frag<K> make_frag(const float (&x)[8]) {
   if constexpr (K == F_F32) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) f.v[j] = x[j];
+  } else if constexpr (K == F_SPLIT) {
+    to_bf16x8_split(x, f.hi, f.lo);
   } else {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) f.hi[j] = (__bf16)x[j];
-    if constexpr (K == F_SPLIT) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) f.lo[j] = (__bf16)(x[j] - (float)f.hi[j]);
-    }
+    f.hi = to_bf16x8(x);
   }
   return f;
 }
