@@ -82,8 +82,9 @@ gdn_status gdn_validate(const gdn_shape *shape);
 
 /* Bytes of device workspace gdn_chunk_fwd / gdn_chunk_fold need for `shape`
  * (written to *bytes).  The workspace holds per-chunk intermediates (decay
- * cumsums, W, U, chunk-start states, corrected values) and, with groups, the
- * (A, B) pairs and incoming states.  It carries nothing between calls. */
+ * cumsums, W, U, chunk-start states, corrected values per value head; K^T
+ * per query/key head) and, with groups, the (A, B) pairs and incoming
+ * states.  It carries nothing between calls. */
 gdn_status gdn_workspace_size(const gdn_shape *shape, size_t *bytes);
 
 /* The whole chunked forward.
