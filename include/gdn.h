@@ -31,7 +31,10 @@
  *  - Calls on different streams do not interact; two calls that share an
  *    output or workspace buffer must be ordered by the caller.
  *  - Supported sizes: d_k = d_v = 128; chunk 64 or 128 for bf16 inputs,
- *    chunk 64 for fp32 inputs; T a multiple of chunk.
+ *    chunk 64 for fp32 inputs; any T >= 0.  A partial last chunk (T not a
+ *    multiple of chunk) is padded with identity steps (k = v = 0, g = 0,
+ *    beta = 0), which leave the state and the real tokens' outputs exactly
+ *    as the unpadded rule gives them; nothing past T is read or written.
  */
 #ifndef GDN_H
 #define GDN_H
@@ -57,14 +60,14 @@ typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
 
 /* Problem description.
  *   B        batch
- *   T        tokens per sequence (multiple of chunk)
+ *   T        tokens per sequence; N = ceil(T / chunk) chunks
  *   H_qk     query/key heads; H_v value heads, H_v % H_qk == 0.  Value head
  *            h reads query/key head h / (H_v / H_qk) (contiguous groups).
  *   d_k, d_v head dims (128, 128)
  *   chunk    tokens per chunk C (64 or 128)
- *   n_groups 0 or 1: one sequential walk over all T/C chunks per head.
- *            > 1: split the T/C chunks of each head into n_groups equal
- *            chunk-groups (n_groups must divide T/C): fold each group into
+ *   n_groups 0 or 1: one sequential walk over all N chunks per head.
+ *            > 1: split the N chunks of each head into n_groups equal
+ *            chunk-groups (n_groups must divide N): fold each group into
  *            one (A, B) pair, exclusive prefix, replay every group from its
  *            incoming state.  Same result up to rounding.
  *   dtype    gdn_dtype of q, k, v
@@ -166,7 +169,9 @@ gdn_status gdn_compose_prefix(int32_t batch_heads, int32_t n, int32_t d_k, int32
 
 /* The intra-chunk transform alone (decay cumsum, gated strict-lower
  * beta K K^T, UT inversion by the doubling ladder, WY formation), for every
- * chunk of every value head.  N = T / chunk.
+ * chunk of every value head.  N = ceil(T / chunk); the rows of a partial
+ * last chunk past T are its identity padding (G repeats the last real
+ * cumsum, T has unit rows, W and U zero rows).
  *   G  [B, H_v, N, C] fp32     G[r] = sum_{s<=r} g_s within the chunk
  *   Tm [B, H_v, N, C, C] fp32  (I+S)^-1, S_ri = beta_r e^{G_r-G_i} k_r.k_i (i<r);
  *                              NULL = not wanted

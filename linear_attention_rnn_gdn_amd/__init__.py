@@ -229,7 +229,7 @@ def chunk_transform(k, v, g, beta, chunk=128, want_T=False, stream=None):
     B, T, Hqk, Hv, dk, dv, dev = _inputs(None, k, v, g, beta)
     shape = make_shape(B, T, Hqk, Hv, dk, dv, chunk, 0, k.dtype, torch.float32)
     _check(validate(shape), "gdn_chunk_transform")
-    N = T // chunk
+    N = -(-T // chunk)   # a partial last chunk is padded with identity steps
     f = dict(dtype=torch.float32, device=dev)
     G = torch.empty((B, Hv, N, chunk), **f)
     Tm = torch.empty((B, Hv, N, chunk, chunk), **f) if want_T else None

@@ -23,8 +23,11 @@ struct Layout {
 
 int groups_of(const gdn_shape &s) { return s.n_groups > 1 ? s.n_groups : 1; }
 
+// chunks per sequence; a partial last chunk is padded with identity steps
+int chunks_of(const gdn_shape &s) { return (int)(((int64_t)s.T + s.chunk - 1) / s.chunk); }
+
 Layout layout(const gdn_shape &s) {
-  const size_t BH = (size_t)s.B * s.H_v, C = s.chunk, N = s.T / s.chunk;
+  const size_t BH = (size_t)s.B * s.H_v, C = s.chunk, N = chunks_of(s);
   const size_t J = groups_of(s);
   const size_t in_bytes = s.dtype == GDN_BF16 ? 2 : 4;
   Layout L{};
@@ -64,7 +67,7 @@ __global__ void copy_state_kernel(const float *src, float *dst, size_t n) {
 
 FwdArgs base_args(const gdn_shape &s) {
   FwdArgs a{};
-  a.B = s.B; a.T = s.T; a.Hqk = s.H_qk; a.Hv = s.H_v; a.N = s.T / s.chunk;
+  a.B = s.B; a.T = s.T; a.Hqk = s.H_qk; a.Hv = s.H_v; a.N = chunks_of(s);
   a.jobs = 1; a.cpj = a.N;
   a.n0 = 0; a.nn = a.N;
   return a;
@@ -97,7 +100,10 @@ void launch(K kernel, dim3 grid, dim3 block, const Lx &x, Args... args) {
 template <int C, typename TI, int MODE, bool FWD = true>
 gdn_status launch_prep(const FwdArgs &a, const Lx &x) {
   const long units = (long)a.nn * a.B * a.Hv;   // one workgroup per (chunk, head)
-  launch(prep_kernel<C, TI, MODE, FWD>, dim3((unsigned)units), dim3(PNT), x, a);
+  if (a.T % C)
+    launch(prep_kernel<C, TI, MODE, FWD, true>, dim3((unsigned)units), dim3(PNT), x, a);
+  else
+    launch(prep_kernel<C, TI, MODE, FWD, false>, dim3((unsigned)units), dim3(PNT), x, a);
   return check_launch();
 }
 
@@ -122,7 +128,10 @@ gdn_status launch_walk(const FwdArgs &a, const Lx &x) {
 template <int C, typename TI, int MODE, typename TO>
 gdn_status launch_out(const FwdArgs &a, const Lx &x) {
   const long units = (long)a.nn * a.B * a.Hv;   // one workgroup per (chunk, head)
-  launch(out_kernel<C, TI, MODE, TO>, dim3((unsigned)units), dim3(NT), x, a);
+  if (a.T % C)
+    launch(out_kernel<C, TI, MODE, TO, true>, dim3((unsigned)units), dim3(NT), x, a);
+  else
+    launch(out_kernel<C, TI, MODE, TO, false>, dim3((unsigned)units), dim3(NT), x, a);
   return check_launch();
 }
 
@@ -260,10 +269,10 @@ gdn_status gdn_validate(const gdn_shape *s) {
   if (s->d_k != D || s->d_v != D) return GDN_ERR_SHAPE;
   if (s->chunk != 64 && s->chunk != 128) return GDN_ERR_SHAPE;
   if (s->dtype == GDN_F32 && s->chunk != 64) return GDN_ERR_SHAPE;
-  if (s->T % s->chunk) return GDN_ERR_SHAPE;
   if (s->n_groups < 0) return GDN_ERR_SHAPE;
-  const int N = s->T / s->chunk;
-  if (N > 65535 || (int64_t)s->B * s->H_v > 65535) return GDN_ERR_SHAPE;
+  const int64_t N64 = ((int64_t)s->T + s->chunk - 1) / s->chunk;
+  if (N64 > 65535 || (int64_t)s->B * s->H_v > 65535) return GDN_ERR_SHAPE;
+  const int N = (int)N64;
   // one workgroup per (chunk, head) in a 1-D grid; the walk's grid is
   // (batch row, head, group or slice) x 16 at most
   if ((int64_t)N * s->B * s->H_v > (1 << 30)) return GDN_ERR_SHAPE;

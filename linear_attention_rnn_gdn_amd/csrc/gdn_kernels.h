@@ -240,14 +240,16 @@ template <int C, typename TI, int NTH> struct TileBlock {   // NTH threads share
   static constexpr int NCB = D / VE, NBLK = (C / 8) * NCB;
   static constexpr int PER = (NBLK + NTH - 1) / NTH;   // blocks per thread
   uint4 v[PER][8];
-  __device__ void load(int tix, const TI *src, size_t gstride) {
+  // rows at or past `rows` (the padding of a partial last chunk) are zero
+  __device__ void load(int tix, const TI *src, size_t gstride, int rows) {
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
       const int blk = tix + p * NTH, rb = blk / NCB, cb = blk % NCB;
       if (blk < NBLK) {
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-          v[p][j] = *reinterpret_cast<const uint4 *>(src + (size_t)(8 * rb + j) * gstride + VE * cb);
+          v[p][j] = 8 * rb + j < rows ? *reinterpret_cast<const uint4 *>(src + (size_t)(8 * rb + j) * gstride + VE * cb)
+                                      : uint4{0u, 0u, 0u, 0u};
       }
     }
   }
@@ -417,7 +419,9 @@ __device__ __forceinline__ void ladder_level(float *sT, float *sM, int wave, int
 
 constexpr int PW = 8, PNT = 64 * PW;   // prep: waves, threads per workgroup
 
-template <int C, typename TI, int MODE, bool FWD>
+// RAG: T is not a multiple of C (the last chunk is partial); otherwise every
+// chunk is whole and the row masks below fold away.
+template <int C, typename TI, int MODE, bool FWD, bool RAG>
 __global__ __launch_bounds__(PNT, 4) void prep_kernel(FwdArgs a) {   // two workgroups per CU
   using WT = typename std::conditional<FWD, TI, float>::type;
   using PR = Prec<MODE>;
@@ -444,6 +448,12 @@ __global__ __launch_bounds__(PNT, 4) void prep_kernel(FwdArgs a) {   // two work
   const size_t bh = (size_t)b * a.Hv + hv;
   const size_t t0 = (size_t)n * C;
   const size_t cb = bh * a.N + n;  // chunk index into the workspace
+  // tokens of this chunk; a partial last chunk is padded with identity steps
+  // (k = v = 0, g = 0, beta = 0): their rows of S are zero, their rows of T
+  // unit rows, their W, U (and so V') rows exactly zero, and G carries the
+  // last real token's cumsum, so the walk and the outputs of the real tokens
+  // are those of the unpadded sequence
+  const int rows = RAG ? (int)(a.T - t0 < (size_t)C ? a.T - t0 : (size_t)C) : C;
 
   // The first half of the workgroup holds the K tile in registers, the second
   // half the V tile, one 8-row block per thread (kept for the transposed
@@ -452,14 +462,14 @@ __global__ __launch_bounds__(PNT, 4) void prep_kernel(FwdArgs a) {   // two work
   const int tix = tid & (PNT / 2 - 1);
   TileBlock<C, TI, PNT / 2> xt;
   if (!vhalf)
-    xt.load(tix, reinterpret_cast<const TI *>(a.k) + (((size_t)b * a.T + t0) * a.Hqk + hq) * D, (size_t)a.Hqk * D);
+    xt.load(tix, reinterpret_cast<const TI *>(a.k) + (((size_t)b * a.T + t0) * a.Hqk + hq) * D, (size_t)a.Hqk * D, rows);
   else
-    xt.load(tix, reinterpret_cast<const TI *>(a.v) + (((size_t)b * a.T + t0) * a.Hv + hv) * D, (size_t)a.Hv * D);
+    xt.load(tix, reinterpret_cast<const TI *>(a.v) + (((size_t)b * a.T + t0) * a.Hv + hv) * D, (size_t)a.Hv * D, rows);
 
   // (1) decay cumsum over the chunk (inclusive), beta
   {
     float x = 0.f, bx = 0.f;
-    if (tid < C) {
+    if (tid < rows) {
       const size_t si = ((size_t)b * a.T + t0 + tid) * a.Hv + hv;
       x = a.g[si];
       bx = a.beta[si];
@@ -1327,7 +1337,7 @@ template <int C, typename TI> struct OutLds {
   __device__ static int kpos(int r, int c) { return r * RP + (c ^ (r & 15)); }
 };
 
-template <int C, typename TI, int MODE, typename TO>
+template <int C, typename TI, int MODE, typename TO, bool RAG>   // RAG as for prep_kernel
 __global__ __launch_bounds__(NT, 2) void out_kernel(FwdArgs a) {
   using PR = Prec<MODE>;
   using PKq = PolicyKinds<PR::exact>;   // K x Q^T
@@ -1354,6 +1364,10 @@ __global__ __launch_bounds__(NT, 2) void out_kernel(FwdArgs a) {
   const int hq = hv / (a.Hv / a.Hqk);
   const size_t cb = bh * a.N + n;
   const size_t tok0 = (size_t)b * a.T + (size_t)n * C;   // first token of the chunk
+  // real tokens of the chunk (a partial last chunk: rows past it read the
+  // last real token's q and k, finite values that meet zero V' rows, and
+  // write no output)
+  const int rows = RAG ? (int)(a.T - (size_t)n * C < (size_t)C ? a.T - (size_t)n * C : (size_t)C) : C;
   const float *Gs = reinterpret_cast<const float *>(lds + OL::GOFF);
 
   // K tile and G into LDS
@@ -1365,7 +1379,7 @@ __global__ __launch_bounds__(NT, 2) void out_kernel(FwdArgs a) {
     for (int jj = 0; jj < OL::KB / 4096; ++jj) {
       const int j = jj * 4 + wv;   // 1 KB block: pieces 64 j + lane of the swizzled tile
       const int p = j * 64 + lane, r = p / OL::RP, c = (p % OL::RP) ^ (r & 15);
-      __builtin_amdgcn_global_load_lds((const void *)(kg + r * krow + c * 16), (LDSP)(lds + j * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void *)(kg + (r < rows ? r : rows - 1) * krow + c * 16), (LDSP)(lds + j * 1024), 16, 0, 0);
     }
     if (wv == 3 && lane < C / 4)
       __builtin_amdgcn_global_load_lds((const void *)(a.G + cb * C + lane * 4), (LDSP)(lds + OL::GOFF), 16, 0, 0);
@@ -1373,7 +1387,8 @@ __global__ __launch_bounds__(NT, 2) void out_kernel(FwdArgs a) {
   // query fragments of one row tile, k order kk(g, j)
   using QF = Frag<PKq::b>;
   auto load_q = [&](int rt, QF (&q)[KBD]) {
-    const TI *qrow = reinterpret_cast<const TI *>(a.q) + ((tok0 + 16 * rt + lr) * a.Hqk + hq) * D;
+    const int qr = 16 * rt + lr < rows ? 16 * rt + lr : rows - 1;
+    const TI *qrow = reinterpret_cast<const TI *>(a.q) + ((tok0 + qr) * a.Hqk + hq) * D;
 #pragma unroll
     for (int kb = 0; kb < KBD; ++kb) {
       TI t[8];
@@ -1583,8 +1598,10 @@ __global__ __launch_bounds__(NT, 2) void out_kernel(FwdArgs a) {
       TO ov[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) ov[i] = from_f32<TO>(er * acc1[ct][i] + acc2[ct][i]);
-      if constexpr (sizeof(TO) == 4) st16_stream(dst, ov);
-      else st8_stream(dst, ov);
+      if (r < rows) {
+        if constexpr (sizeof(TO) == 4) st16_stream(dst, ov);
+        else st8_stream(dst, ov);
+      }
     }
   };
 #pragma unroll

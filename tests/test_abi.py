@@ -64,7 +64,9 @@ def _shape(gdn, **kw):
     (dict(n_groups=32), 0),
     (dict(n_groups=3), -2),            # does not divide the 32 chunks
     (dict(n_groups=-1), -2),
-    (dict(T=4100), -2),                # ragged tail
+    (dict(T=4100), 0),                 # ragged tail: the last chunk padded with identity steps
+    (dict(T=4100, n_groups=33), 0),    # 33 chunks
+    (dict(T=4100, n_groups=32), -2),   # does not divide the 33 chunks
     (dict(chunk=96), -2),
     (dict(d_k=64), -2),
     (dict(d_v=256), -2),
@@ -119,7 +121,7 @@ def test_entry_points_reject_bad_arguments_without_launching(gdn):
     # workspace too small
     assert L.gdn_chunk_fwd(ctypes.byref(s), ok, ok, ok, ok, ok, null, ok, null, ok, ws - 1, null) == -5
     # bad shape
-    bad = _shape(gdn, T=4100)
+    bad = _shape(gdn, chunk=96)
     assert L.gdn_chunk_fwd(ctypes.byref(bad), ok, ok, ok, ok, ok, null, ok, null, ok, ws, null) == -2
     # fold / transform / prefix
     assert L.gdn_chunk_fold(ctypes.byref(s), ok, ok, ok, ok, null, ok, ok, ws, null) == -1

@@ -381,13 +381,30 @@ def test_long_sequence_reduced(gdn):
     _check("h_T", h, h_ref, 2e-2, ro)
 
 
+@pytest.mark.parametrize("dtype,C,T,Hqk,Hv,h0,ng", [
+    ("f32", 64, 64 * 5 + 17, 1, 3, 0.3, 0),       # fp32, partial last chunk
+    ("bf16", 128, 128 * 9 + 1, 2, 4, 0.1, 0),     # a one-token last chunk
+    ("bf16", 64, 63, 1, 2, 0.05, 0),              # shorter than one chunk
+    ("bf16", 128, 4000, 2, 4, 0.02, 4),           # chunk-groups, the last one ragged
+])
+def test_forward_ragged_tail(gdn, dtype, C, T, Hqk, Hv, h0, ng):
+    # T not a multiple of the chunk: the last chunk is padded with identity
+    # steps inside the library; o and h_T must be those of the unpadded rule
+    w = WORKLOADS["tiny"].replace(T=T, Hqk=Hqk, Hv=Hv, chunk=C, dtype=dtype, h0_std=h0, B=2)
+    x = make_inputs(w, device="cuda", seed=T + C)
+    o, h, o_ref, h_ref = _run_and_compare(gdn, w, x, n_groups=ng)
+    ro = _rms(o_ref)
+    _check("o", o, o_ref, TOL[dtype], ro)
+    _check("h_T", h, h_ref, TOL[dtype], ro)
+
+
 @pytest.mark.parametrize("C", [64, 128])
 def test_forward_throughput_form(gdn, C):
     # 512 walks (B * H_v): the single walk takes its throughput form (eight
     # slices per workgroup sharing W and K^T through LDS) instead of the
     # latency form the shorter walks above take
-    w = WORKLOADS["tiny"].replace(T=3 * C, Hqk=16, Hv=32, chunk=C, dtype="bf16", h0_std=0.02, B=16)
-    x = make_inputs(w, device="cuda", seed=C + 3)
+    w = WORKLOADS["tiny"].replace(T=3 * C - 5, Hqk=16, Hv=32, chunk=C, dtype="bf16", h0_std=0.02, B=16)
+    x = make_inputs(w, device="cuda", seed=C + 3)   # (with a partial last chunk)
     o, h, o_ref, h_ref = _run_and_compare(gdn, w, x)
     ro = _rms(o_ref)
     _check("o", o, o_ref, 2e-2, ro)
