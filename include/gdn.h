@@ -139,6 +139,27 @@ gdn_status gdn_chunk_fwd_timed(const gdn_shape *shape, int32_t stages, const voi
                                const float *h0, void *o, float *h_T, void *ws, size_t ws_bytes,
                                void *hip_stream, void *const *ev_start, void *const *ev_stop);
 
+/* The chunked forward over packed variable-length sequences.  shape->B
+ * sequences are concatenated along one row of shape->T tokens: sequence s
+ * holds tokens [cu_seqlens[s], cu_seqlens[s+1]), each with its own initial
+ * and final state and no state passing between sequences.  Each sequence is
+ * cut into chunks of its own, its last one partial (padded with identity
+ * steps as above).  shape->n_groups must be 0 or 1 (one walk per sequence).
+ *   cu_seqlens [B + 1] int32 DEVICE array: 0 = cu[0] <= cu[1] <= ... <=
+ *              cu[B] = T.  Offsets outside [0, T] are clamped; for offsets
+ *              that are not such a partition the results are unspecified,
+ *              but nothing outside the tensors and the workspace is touched.
+ *   q, k  [1, T, H_qk, d_k]   v, o [1, T, H_v, d_v]   g, beta [1, T, H_v]
+ *   h0, h_T [B, H_v, d_k, d_v] fp32 (h0 NULL = zero; h_T NULL = not wanted)
+ *   ws    at least gdn_workspace_size_varlen() bytes.
+ * Work is planned on the device (no host copy of cu_seqlens is needed); other
+ * conventions as gdn_chunk_fwd. */
+gdn_status gdn_workspace_size_varlen(const gdn_shape *shape, size_t *bytes);
+gdn_status gdn_chunk_fwd_varlen(const gdn_shape *shape, const int32_t *cu_seqlens, const void *q,
+                                const void *k, const void *v, const float *g, const float *beta,
+                                const float *h0, void *o, float *h_T, void *ws, size_t ws_bytes,
+                                void *hip_stream);
+
 /* Per-group affine pairs of the chunk-group split (shape->n_groups >= 1
  * groups of equal length; 0 is taken as 1).  For group j of value head h:
  *   A[b,h,j] = product over the group's tokens t (latest on the left) of

@@ -43,7 +43,8 @@ class GdnError(RuntimeError):
 
 _lib = None
 
-SYMBOLS = ("gdn_status_str", "gdn_validate", "gdn_workspace_size", "gdn_chunk_fwd",
+SYMBOLS = ("gdn_status_str", "gdn_validate", "gdn_workspace_size", "gdn_workspace_size_varlen",
+           "gdn_chunk_fwd", "gdn_chunk_fwd_varlen",
            "gdn_chunk_fwd_stages", "gdn_chunk_fwd_timed", "gdn_chunk_fold", "gdn_compose_prefix",
            "gdn_chunk_transform")
 STAGE_PREP, STAGE_FOLD, STAGE_PREFIX, STAGE_WALK, STAGE_OUT, STAGE_ALL = 1, 2, 4, 8, 16, 31
@@ -65,6 +66,10 @@ def lib():
         L.gdn_validate.restype = I
         L.gdn_workspace_size.argtypes = [SP, ctypes.POINTER(SZ)]
         L.gdn_workspace_size.restype = I
+        L.gdn_workspace_size_varlen.argtypes = [SP, ctypes.POINTER(SZ)]
+        L.gdn_workspace_size_varlen.restype = I
+        L.gdn_chunk_fwd_varlen.argtypes = [SP] + [P] * 10 + [SZ, P]
+        L.gdn_chunk_fwd_varlen.restype = I
         L.gdn_chunk_fwd.argtypes = [SP] + [P] * 9 + [SZ, P]
         L.gdn_chunk_fwd.restype = I
         L.gdn_chunk_fwd_stages.argtypes = [SP, I] + [P] * 9 + [SZ, P]
@@ -183,6 +188,45 @@ def chunk_fwd(q, k, v, g, beta, h0=None, chunk=128, n_groups=0, o_dtype=torch.fl
     else:
         _check(lib().gdn_chunk_fwd_stages(ctypes.byref(shape), int(stages), *args),
                "gdn_chunk_fwd_stages")
+    return o, hT
+
+
+def workspace_size_varlen(shape: GdnShape) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().gdn_workspace_size_varlen(ctypes.byref(shape), ctypes.byref(n)), "gdn_workspace_size_varlen")
+    return int(n.value)
+
+
+def chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, h0=None, chunk=128, o_dtype=torch.float32,
+                     output_final_state=True, workspace=None, out=None, final_state=None, stream=None):
+    """Chunked forward over packed variable-length sequences
+    (gdn_chunk_fwd_varlen).  q, k [1,T,H_qk,d_k]; v [1,T,H_v,d_v]; g, beta
+    [1,T,H_v]; cu_seqlens int32 [n+1] on the device (sequence s = tokens
+    cu[s]..cu[s+1]); h0 [n,H_v,d_k,d_v] or None.  Returns (o, h_T [n,...] or None)."""
+    B, T, Hqk, Hv, dk, dv, dev = _inputs(q, k, v, g, beta)
+    if B != 1:
+        raise ValueError("packed sequences: the batch dimension of q, k, v, g, beta must be 1")
+    _need(cu_seqlens, "cu_seqlens", torch.int32, None, dev)
+    nseq = cu_seqlens.numel() - 1
+    if nseq < 1:
+        raise ValueError("cu_seqlens must hold at least two offsets")
+    shape = make_shape(nseq, T, Hqk, Hv, dk, dv, chunk, 0, k.dtype, o_dtype)
+    if h0 is not None:
+        _need(h0, "h0", torch.float32, (nseq, Hv, dk, dv), dev)
+    need = workspace_size_varlen(shape)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    o = out if out is not None else torch.empty((1, T, Hv, dv), dtype=o_dtype, device=dev)
+    _need(o, "o", o_dtype, (1, T, Hv, dv), dev)
+    hT = None
+    if output_final_state:
+        hT = final_state if final_state is not None else torch.empty((nseq, Hv, dk, dv),
+                                                                    dtype=torch.float32, device=dev)
+        _need(hT, "h_T", torch.float32, (nseq, Hv, dk, dv), dev)
+    _check(lib().gdn_chunk_fwd_varlen(ctypes.byref(shape), _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v),
+                                      _ptr(g), _ptr(beta), _ptr(h0), _ptr(o), _ptr(hT), _ptr(workspace),
+                                      ctypes.c_size_t(workspace.numel()), _stream(stream)),
+           "gdn_chunk_fwd_varlen")
     return o, hT
 
 

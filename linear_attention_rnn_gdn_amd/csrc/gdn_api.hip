@@ -18,7 +18,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t G, W, Kt, U, Hs, Vn, A, Bp, Hin, total;
+  size_t G, W, Kt, U, Hs, Vn, A, Bp, Hin, Ct, Jt, Nt, total;
 };
 
 int groups_of(const gdn_shape &s) { return s.n_groups > 1 ? s.n_groups : 1; }
@@ -26,15 +26,21 @@ int groups_of(const gdn_shape &s) { return s.n_groups > 1 ? s.n_groups : 1; }
 // chunks per sequence; a partial last chunk is padded with identity steps
 int chunks_of(const gdn_shape &s) { return (int)(((int64_t)s.T + s.chunk - 1) / s.chunk); }
 
-Layout layout(const gdn_shape &s) {
-  const size_t BH = (size_t)s.B * s.H_v, C = s.chunk, N = chunks_of(s);
+// Packed variable-length sequences: s.B sequences share one row of T tokens;
+// their chunks, at most T / C + s.B of them, are numbered across sequences.
+int varlen_nmax(const gdn_shape &s) { return (int)((int64_t)s.T / s.chunk + s.B); }
+
+// Workspace of `rows` sequence rows of N chunks each (plus, for `nseq` packed
+// sequences, their chunk tables).
+Layout layout_n(const gdn_shape &s, size_t rows, size_t N, size_t nseq) {
+  const size_t BH = rows * s.H_v, C = s.chunk;
   const size_t J = groups_of(s);
   const size_t in_bytes = s.dtype == GDN_BF16 ? 2 : 4;
   Layout L{};
   size_t off = 0;
   L.G = off;  off += align_up(BH * N * C * 4);
   L.W = off;  off += align_up(BH * N * C * D * in_bytes);
-  L.Kt = off; off += align_up((size_t)s.B * s.H_qk * N * C * D * in_bytes);   // per key head
+  L.Kt = off; off += align_up(rows * s.H_qk * N * C * D * in_bytes);   // per key head
   L.U = off;  off += align_up(BH * N * C * D * 4);
   L.Hs = off; off += align_up(BH * N * D * D * 4);   // fp32, or bf16 hi + lo planes
   L.Vn = off; off += align_up(BH * N * C * D * 4);
@@ -43,9 +49,16 @@ Layout layout(const gdn_shape &s) {
     L.Bp = off;  off += align_up(BH * J * D * D * 4);
     L.Hin = off; off += align_up(BH * J * D * D * 4);
   }
+  if (nseq) {
+    L.Ct = off; off += align_up(N * sizeof(int2));
+    L.Jt = off; off += align_up(nseq * sizeof(int2));
+    L.Nt = off; off += align_up(sizeof(int));
+  }
   L.total = off;
   return L;
 }
+Layout layout(const gdn_shape &s) { return layout_n(s, s.B, chunks_of(s), 0); }
+Layout layout_varlen(const gdn_shape &s) { return layout_n(s, 1, varlen_nmax(s), s.B); }
 
 bool misaligned(const void *p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u); }
 
@@ -97,10 +110,12 @@ void launch(K kernel, dim3 grid, dim3 block, const Lx &x, Args... args) {
     hipLaunchKernelGGL(kernel, grid, block, 0, x.st, args...);
 }
 
+// rag: some chunk is partial (the last one when T % C != 0, or any chunk of
+// packed sequences): the row-masked instantiation
 template <int C, typename TI, int MODE, bool FWD = true>
-gdn_status launch_prep(const FwdArgs &a, const Lx &x) {
+gdn_status launch_prep(const FwdArgs &a, const Lx &x, bool rag = false) {
   const long units = (long)a.nn * a.B * a.Hv;   // one workgroup per (chunk, head)
-  if (a.T % C)
+  if (rag || a.T % C)
     launch(prep_kernel<C, TI, MODE, FWD, true>, dim3((unsigned)units), dim3(PNT), x, a);
   else
     launch(prep_kernel<C, TI, MODE, FWD, false>, dim3((unsigned)units), dim3(PNT), x, a);
@@ -126,9 +141,9 @@ gdn_status launch_walk(const FwdArgs &a, const Lx &x) {
 }
 
 template <int C, typename TI, int MODE, typename TO>
-gdn_status launch_out(const FwdArgs &a, const Lx &x) {
+gdn_status launch_out(const FwdArgs &a, const Lx &x, bool rag = false) {
   const long units = (long)a.nn * a.B * a.Hv;   // one workgroup per (chunk, head)
-  if (a.T % C)
+  if (rag || a.T % C)
     launch(out_kernel<C, TI, MODE, TO, true>, dim3((unsigned)units), dim3(NT), x, a);
   else
     launch(out_kernel<C, TI, MODE, TO, false>, dim3((unsigned)units), dim3(NT), x, a);
@@ -191,6 +206,42 @@ gdn_status run_fwd(const gdn_shape &s, int stages, const void *q, const void *k,
   return launch_out<C, TI, MODE, __bf16>(a, lx(4));
 }
 
+// Packed variable-length sequences: the chunk tables, then prep and out over
+// the numbered chunks (every one possibly partial) and one walk per
+// (sequence, value head).
+template <int C, typename TI, int MODE>
+gdn_status run_fwd_varlen(const gdn_shape &s, const int *cu, const void *q, const void *k, const void *v,
+                          const float *g, const float *beta, const float *h0, void *o, float *h_T, char *ws,
+                          hipStream_t st) {
+  const Layout L = layout_varlen(s);
+  const int nmax = varlen_nmax(s);
+  int2 *ctab = reinterpret_cast<int2 *>(ws + L.Ct);
+  int2 *jtab = reinterpret_cast<int2 *>(ws + L.Jt);
+  int *ntot = reinterpret_cast<int *>(ws + L.Nt);
+  hipLaunchKernelGGL(varlen_tables_kernel, dim3(1), dim3(256), 0, st, cu, s.B, s.T, C, nmax, ctab, jtab, ntot);
+  GDN_TRY(check_launch());
+  FwdArgs a{};
+  a.B = 1; a.T = s.T; a.Hqk = s.H_qk; a.Hv = s.H_v; a.N = nmax;
+  a.jobs = 1; a.cpj = 0; a.n0 = 0; a.nn = nmax;
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.o = o;
+  a.G = reinterpret_cast<float *>(ws + L.G);
+  a.W = ws + L.W;
+  a.Kt = ws + L.Kt;
+  a.U = reinterpret_cast<float *>(ws + L.U);
+  a.Hs = reinterpret_cast<float *>(ws + L.Hs);
+  a.Vn = reinterpret_cast<float *>(ws + L.Vn);
+  a.ctab = ctab; a.ntot = ntot;
+  GDN_TRY((launch_prep<C, TI, MODE>(a, Lx{st}, true)));
+  FwdArgs w = a;
+  w.B = s.B; w.jtab = jtab; w.init = h0; w.init_per_job = 0; w.fin = h_T;
+  if (s.o_dtype == GDN_F32) {
+    GDN_TRY((launch_walk<C, TI, MODE, WALK>(w, Lx{st})));
+    return launch_out<C, TI, MODE, float>(a, Lx{st}, true);
+  }
+  GDN_TRY((launch_walk<C, TI, MODE, WALK>(w, Lx{st})));
+  return launch_out<C, TI, MODE, __bf16>(a, Lx{st}, true);
+}
+
 template <int C, typename TI, int MODE>
 gdn_status run_fold(const gdn_shape &s, const void *k, const void *v, const float *g, const float *beta,
                     float *A, float *Bm, char *ws, hipStream_t st) {
@@ -220,6 +271,13 @@ struct FwdCall {
   char *w; hipStream_t st; void *const *ev0 = nullptr, *const *ev1 = nullptr;
   template <int C, typename TI, int MODE> gdn_status run() {
     return run_fwd<C, TI, MODE>(s, stages, q, k, v, g, beta, h0, o, h_T, w, st, ev0, ev1);
+  }
+};
+struct VarlenCall {
+  const gdn_shape &s; const int *cu; const void *q, *k, *v; const float *g, *beta, *h0; void *o; float *h_T;
+  char *w; hipStream_t st;
+  template <int C, typename TI, int MODE> gdn_status run() {
+    return run_fwd_varlen<C, TI, MODE>(s, cu, q, k, v, g, beta, h0, o, h_T, w, st);
   }
 };
 struct FoldCall {
@@ -324,6 +382,41 @@ gdn_status gdn_chunk_fwd_timed(const gdn_shape *s, int32_t stages, const void *q
   if (ws_bytes < layout(*s).total) return GDN_ERR_WORKSPACE;
   char *w = reinterpret_cast<char *>(ws);
   FwdCall f{*s, stages, q, k, v, g, beta, h0, o, h_T, w, st, ev_start, ev_stop};
+  return dispatch(*s, f);
+}
+
+// host checks of a packed-sequences problem (s->B sequences, s->T tokens)
+gdn_status validate_varlen(const gdn_shape *s) {
+  GDN_TRY(gdn_validate(s));
+  if (s->n_groups > 1) return GDN_ERR_SHAPE;
+  if ((int64_t)varlen_nmax(*s) * s->H_v > (1 << 30)) return GDN_ERR_SHAPE;
+  return GDN_OK;
+}
+
+gdn_status gdn_workspace_size_varlen(const gdn_shape *s, size_t *bytes) {
+  if (!bytes) return GDN_ERR_NULL;
+  GDN_TRY(validate_varlen(s));
+  *bytes = layout_varlen(*s).total;
+  return GDN_OK;
+}
+
+gdn_status gdn_chunk_fwd_varlen(const gdn_shape *s, const int32_t *cu_seqlens, const void *q, const void *k,
+                                const void *v, const float *g, const float *beta, const float *h0, void *o,
+                                float *h_T, void *ws, size_t ws_bytes, void *hip_stream) {
+  GDN_TRY(validate_varlen(s));
+  hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+  if (misaligned(h0) || misaligned(h_T)) return GDN_ERR_ALIGN;
+  if (s->T == 0) {   // every sequence empty: h_T = h0
+    if (!h_T) return GDN_OK;
+    hipLaunchKernelGGL(copy_state_kernel, dim3(256), dim3(256), 0, st, h0, h_T, (size_t)s->B * s->H_v * D * D);
+    return check_launch();
+  }
+  if (!cu_seqlens || !q || !k || !v || !g || !beta || !o || !ws) return GDN_ERR_NULL;
+  for (const void *p : {(const void *)cu_seqlens, (const void *)q, (const void *)k, (const void *)v,
+                        (const void *)g, (const void *)beta, (const void *)o, (const void *)ws})
+    if (misaligned(p)) return GDN_ERR_ALIGN;
+  if (ws_bytes < layout_varlen(*s).total) return GDN_ERR_WORKSPACE;
+  VarlenCall f{*s, cu_seqlens, q, k, v, g, beta, h0, o, h_T, reinterpret_cast<char *>(ws), st};
   return dispatch(*s, f);
 }
 

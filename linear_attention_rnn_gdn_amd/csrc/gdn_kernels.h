@@ -162,10 +162,22 @@ struct FwdArgs {
   int jobs, cpj;                  // walk/fold: jobs per bh, chunks per job
   int n0, nn;                     // chunk range [n0, n0 + nn) of this launch (prep, out, single walk)
   void *o;                        // out output
+  // packed variable-length sequences (null otherwise): per chunk (first
+  // token, tokens), per sequence (first chunk, chunks), number of chunks
+  const int2 *ctab, *jtab;
+  const int *ntot;
 };
 
 // Offset from a value head's chunk index cb = bh*N + n to the chunk index of
 // its query/key head, cq = (b*H_qk + hq)*N + n (K^T is stored per key head).
+// A wave-uniform 64-bit value moved to scalar registers (so that address
+// arithmetic derived from it stays on the scalar unit).
+__device__ __forceinline__ unsigned long long uniform64(unsigned long long x) {
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)x);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(x >> 32));
+  return ((unsigned long long)hi << 32) | lo;
+}
+
 __device__ __forceinline__ long long kt_offset(const FwdArgs &a, size_t bh) {
   const size_t b = bh / a.Hv, hv = bh % a.Hv, hq = hv / (a.Hv / a.Hqk);
   return ((long long)(b * a.Hqk + hq) - (long long)bh) * a.N;
@@ -446,14 +458,18 @@ __global__ __launch_bounds__(PNT, 4) void prep_kernel(FwdArgs a) {   // two work
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, g = lane >> 4, lk = g * 8, lq = g * 4;
   const size_t bh = (size_t)b * a.Hv + hv;
-  const size_t t0 = (size_t)n * C;
+  // packed sequences (launched with the RAG instantiation only): chunk n of
+  // the table (past the last one: nothing to do)
+  const bool packed = RAG && a.ctab;
+  if (packed && n >= *a.ntot) return;
+  const size_t t0 = packed ? (size_t)a.ctab[n].x : (size_t)n * C;
   const size_t cb = bh * a.N + n;  // chunk index into the workspace
   // tokens of this chunk; a partial last chunk is padded with identity steps
   // (k = v = 0, g = 0, beta = 0): their rows of S are zero, their rows of T
   // unit rows, their W, U (and so V') rows exactly zero, and G carries the
   // last real token's cumsum, so the walk and the outputs of the real tokens
   // are those of the unpadded sequence
-  const int rows = RAG ? (int)(a.T - t0 < (size_t)C ? a.T - t0 : (size_t)C) : C;
+  const int rows = !RAG ? C : packed ? a.ctab[n].y : (int)(a.T - t0 < (size_t)C ? a.T - t0 : (size_t)C);
 
   // The first half of the workgroup holds the K tile in registers, the second
   // half the V tile, one 8-row block per thread (kept for the transposed
@@ -786,8 +802,24 @@ __global__ __launch_bounds__(64 * WPG) void walk_shared_kernel(FwdArgs a) {
   const int c0 = slice * 16;   // first column (of the augmented [A|B] in FOLD)
   const bool has_u = KIND == WALK || c0 >= D;
   const int us = KIND == WALK ? slice : slice - D / 16;   // U column tile
-  const size_t cb0 = bh * a.N + a.n0 + (size_t)job * a.cpj;
-  const long long ktoff = kt_offset(a, bh);
+  // this walk's chunks: the job's share of the head's, or (packed sequences)
+  // the sequence's, in the workspace row of its value head
+  size_t cb0;
+  int cpj;
+  long long ktoff;
+  if (a.jtab) {
+    const int2 jt = a.jtab[bh / a.Hv];
+    // (wave-uniform: scalar loop bounds)
+    cb0 = (bh % a.Hv) * a.N + __builtin_amdgcn_readfirstlane(jt.x);
+    cpj = __builtin_amdgcn_readfirstlane(jt.y);
+    ktoff = kt_offset(a, bh % a.Hv);
+  } else {
+    cb0 = bh * a.N + a.n0 + (size_t)job * a.cpj;
+    cpj = a.cpj;
+    ktoff = kt_offset(a, bh);
+  }
+  cb0 = uniform64(cb0);
+  ktoff = (long long)uniform64((unsigned long long)ktoff);
 
   // state tiles: h[m] holds rows 16m + 4g + i, column c0 + lr
   f32x4 h[MH];
@@ -806,6 +838,30 @@ __global__ __launch_bounds__(64 * WPG) void walk_shared_kernel(FwdArgs a) {
       }
       h[m][i] = x;
     }
+  }
+
+  // final state slice (the pair of a group in FOLD)
+  auto store_final = [&]() {
+    float *dst = nullptr;
+    int dcol = c0;
+    if (KIND == FOLD) {
+      if (c0 < D) dst = a.pairA + (bh * a.jobs + job) * D * D;
+      else { dst = a.pairB + (bh * a.jobs + job) * D * D; dcol = c0 - D; }
+    } else if (a.fin) {
+      dst = a.fin + bh * D * D;
+    }
+    if (dst) {
+#pragma unroll
+      for (int m = 0; m < MH; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[(size_t)(16 * m + 4 * g + i) * D + dcol + lr] = h[m][i];
+    }
+  };
+  // an empty sequence (packed sequences): the final state is the initial one,
+  // and no chunk operand is touched
+  if (cpj == 0) {
+    store_final();
+    return;
   }
 
   // copy the chunk's operand fragments into an LDS buffer: block j (1 KB) is
@@ -867,7 +923,7 @@ __global__ __launch_bounds__(64 * WPG) void walk_shared_kernel(FwdArgs a) {
 
   auto step = [&](const TI *cur, TI *nxt, UG &cu, UG &nu, int cc) {
     const size_t cb = cb0 + cc;
-    const bool more = cc + 1 < a.cpj;
+    const bool more = cc + 1 < cpj;
     // everything for the next chunk; waited for at the chunk's end only
     fetch_u(more ? cb + 1 : cb, nu);
     if (more) stage(nxt, cb + 1);
@@ -950,26 +1006,12 @@ __global__ __launch_bounds__(64 * WPG) void walk_shared_kernel(FwdArgs a) {
     chunk_barrier();
   };
   // two chunks per trip: the LDS buffers and U/G sets alternate statically
-  for (int cc = 0; cc < a.cpj; cc += 2) {
+  for (int cc = 0; cc < cpj; cc += 2) {
     step(bufA, bufB, ug[0], ug[1], cc);
-    if (cc + 1 < a.cpj) step(bufB, bufA, ug[1], ug[0], cc + 1);
+    if (cc + 1 < cpj) step(bufB, bufA, ug[1], ug[0], cc + 1);
   }
 
-  // final state slice
-  float *dst = nullptr;
-  int dcol = c0;
-  if (KIND == FOLD) {
-    if (c0 < D) dst = a.pairA + (bh * a.jobs + job) * D * D;
-    else { dst = a.pairB + (bh * a.jobs + job) * D * D; dcol = c0 - D; }
-  } else if (a.fin) {
-    dst = a.fin + bh * D * D;
-  }
-  if (dst) {
-#pragma unroll
-    for (int m = 0; m < MH; ++m)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dst[(size_t)(16 * m + 4 * g + i) * D + dcol + lr] = h[m][i];
-  }
+  store_final();
 }
 
 // ----------------------------------------------------------------------------
@@ -1018,9 +1060,24 @@ __global__ __launch_bounds__(64 * NWS) void walk_ring_kernel(FwdArgs a) {
   const int c0 = slice * 16;   // first column (of the augmented [A|B] in FOLD)
   const bool has_u = KIND == WALK || c0 >= D;
   const int us = KIND == WALK ? slice : slice - D / 16;   // U column tile
-  const size_t cb0 = bh * a.N + a.n0 + (size_t)job * a.cpj;
   const int mv0 = w * MVW, mh0 = w * MHW;                 // this wave's first V' / state tile
-  const long long ktoff = kt_offset(a, bh);
+  // this walk's chunks, as in walk_shared_kernel
+  size_t cb0;
+  int cpj;
+  long long ktoff;
+  if (a.jtab) {
+    const int2 jt = a.jtab[bh / a.Hv];
+    // (wave-uniform: scalar loop bounds)
+    cb0 = (bh % a.Hv) * a.N + __builtin_amdgcn_readfirstlane(jt.x);
+    cpj = __builtin_amdgcn_readfirstlane(jt.y);
+    ktoff = kt_offset(a, bh % a.Hv);
+  } else {
+    cb0 = bh * a.N + a.n0 + (size_t)job * a.cpj;
+    cpj = a.cpj;
+    ktoff = kt_offset(a, bh);
+  }
+  cb0 = uniform64(cb0);
+  ktoff = (long long)uniform64((unsigned long long)ktoff);
 
   // state tiles of this wave: h[t] holds rows 16(mh0+t) + 4g + i, column c0 + lr
   f32x4 h[MHW];
@@ -1039,6 +1096,30 @@ __global__ __launch_bounds__(64 * NWS) void walk_ring_kernel(FwdArgs a) {
       }
       h[t][i] = x;
     }
+  }
+
+  // final state rows of this wave (the pair of a group in FOLD)
+  auto store_final = [&]() {
+    float *dst = nullptr;
+    int dcol = c0;
+    if (KIND == FOLD) {
+      if (c0 < D) dst = a.pairA + (bh * a.jobs + job) * D * D;
+      else { dst = a.pairB + (bh * a.jobs + job) * D * D; dcol = c0 - D; }
+    } else if (a.fin) {
+      dst = a.fin + bh * D * D;
+    }
+    if (dst) {
+#pragma unroll
+      for (int t = 0; t < MHW; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[(size_t)(16 * (mh0 + t) + 4 * g + i) * D + dcol + lr] = h[t][i];
+    }
+  };
+  // an empty sequence (packed sequences): the final state is the initial one,
+  // and no chunk operand is touched
+  if (cpj == 0) {
+    store_final();
+    return;
   }
 
   // this wave's fragment sequence per chunk: W (its V' row tiles, all
@@ -1082,7 +1163,7 @@ __global__ __launch_bounds__(64 * NWS) void walk_ring_kernel(FwdArgs a) {
 #pragma unroll
   for (int q = 0; q < RING; ++q) {
     const size_t c = cb0 + q / FPW;
-    ring[q] = load(c < cb0 + a.cpj - 1 ? c : cb0 + a.cpj - 1, q % FPW);
+    ring[q] = load(c < cb0 + cpj - 1 ? c : cb0 + cpj - 1, q % FPW);
   }
   UG ug[2];
   fetch_ug(cb0, ug[0]);
@@ -1091,7 +1172,7 @@ __global__ __launch_bounds__(64 * NWS) void walk_ring_kernel(FwdArgs a) {
   for (int kbl = 0; kbl < KBWW; ++kbl) xh[w][kbl][lane] = state_frag(kbl);
   lds_barrier();
 
-  const size_t cblast = cb0 + a.cpj - 1;
+  const size_t cblast = cb0 + cpj - 1;
   // fragment q of chunk cb sits in slot (P FPW + q) % RING (P = chunk parity);
   // once consumed, the slot takes the fragment RING positions later in the
   // sequence (past the last chunk: the last chunk again, unused)
@@ -1103,7 +1184,7 @@ __global__ __launch_bounds__(64 * NWS) void walk_ring_kernel(FwdArgs a) {
   auto step = [&](UG &cur, UG &nxt, int cc, auto Pc) {
     constexpr int P = decltype(Pc)::value;
     const size_t cb = cb0 + cc;
-    const size_t cbn = cc + 1 < a.cpj ? cb + 1 : cb;   // last chunk: repeat loads (unused)
+    const size_t cbn = cc + 1 < cpj ? cb + 1 : cb;   // last chunk: repeat loads (unused)
     fetch_ug(cbn, nxt);
     const float gl2 = cur.glast * LOG2E;
     float dcy[MVW][4];
@@ -1177,26 +1258,12 @@ __global__ __launch_bounds__(64 * NWS) void walk_ring_kernel(FwdArgs a) {
     lds_barrier();
   };
   // two chunks per trip so the U/G sets alternate without copies
-  for (int cc = 0; cc < a.cpj; cc += 2) {
+  for (int cc = 0; cc < cpj; cc += 2) {
     step(ug[0], ug[1], cc, std::integral_constant<int, 0>{});
-    if (cc + 1 < a.cpj) step(ug[1], ug[0], cc + 1, std::integral_constant<int, 1>{});
+    if (cc + 1 < cpj) step(ug[1], ug[0], cc + 1, std::integral_constant<int, 1>{});
   }
 
-  // final state rows of this wave
-  float *dst = nullptr;
-  int dcol = c0;
-  if (KIND == FOLD) {
-    if (c0 < D) dst = a.pairA + (bh * a.jobs + job) * D * D;
-    else { dst = a.pairB + (bh * a.jobs + job) * D * D; dcol = c0 - D; }
-  } else if (a.fin) {
-    dst = a.fin + bh * D * D;
-  }
-  if (dst) {
-#pragma unroll
-    for (int t = 0; t < MHW; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dst[(size_t)(16 * (mh0 + t) + 4 * g + i) * D + dcol + lr] = h[t][i];
-  }
+  store_final();
 }
 
 // ----------------------------------------------------------------------------
@@ -1363,11 +1430,13 @@ __global__ __launch_bounds__(NT, 2) void out_kernel(FwdArgs a) {
   const size_t bh = (size_t)b * a.Hv + hv;
   const int hq = hv / (a.Hv / a.Hqk);
   const size_t cb = bh * a.N + n;
-  const size_t tok0 = (size_t)b * a.T + (size_t)n * C;   // first token of the chunk
+  const bool packed = RAG && a.ctab;   // packed sequences (RAG instantiation only)
+  if (packed && n >= *a.ntot) return;   // past the last chunk
+  const size_t tok0 = packed ? (size_t)a.ctab[n].x : (size_t)b * a.T + (size_t)n * C;   // first token of the chunk
   // real tokens of the chunk (a partial last chunk: rows past it read the
   // last real token's q and k, finite values that meet zero V' rows, and
   // write no output)
-  const int rows = RAG ? (int)(a.T - (size_t)n * C < (size_t)C ? a.T - (size_t)n * C : (size_t)C) : C;
+  const int rows = !RAG ? C : packed ? a.ctab[n].y : (int)(a.T - (size_t)n * C < (size_t)C ? a.T - (size_t)n * C : (size_t)C);
   const float *Gs = reinterpret_cast<const float *>(lds + OL::GOFF);
 
   // K tile and G into LDS
@@ -1606,6 +1675,60 @@ __global__ __launch_bounds__(NT, 2) void out_kernel(FwdArgs a) {
   };
 #pragma unroll
   for (int rt = 0; rt < R; ++rt) tile_out(rt);
+}
+
+// ----------------------------------------------------------------------------
+// packed variable-length sequences: the chunk tables.  Sequence s covers
+// tokens [cu[s], cu[s+1]) of the packed tensors (offsets clamped into
+// [0, T], a sequence ending no earlier than it starts) and is cut into
+// ceil(len / C) chunks, the last one partial.  One workgroup of 256 threads;
+// thread t takes a contiguous block of sequences.  Writes, with nmax the
+// table capacity (T / C + nseq, enough for any valid cu):
+//   jtab[s] = (first chunk, chunks)      ctab[c] = (first token, tokens)
+//   *ntot   = number of chunks
+// Entries that would pass nmax (only for offsets that are not a valid
+// partition of [0, T]) are dropped, so no access leaves the tables.
+__global__ __launch_bounds__(256) void varlen_tables_kernel(const int *cu, int nseq, int T, int C, int nmax,
+                                                            int2 *ctab, int2 *jtab, int *ntot) {
+  __shared__ int part[256];
+  const int t = threadIdx.x, per = (nseq + 255) / 256;
+  const int s0 = t * per < nseq ? t * per : nseq, s1 = s0 + per < nseq ? s0 + per : nseq;
+  auto seg = [&](int s, int &st, int &en) {
+    st = cu[s] < 0 ? 0 : cu[s] > T ? T : cu[s];
+    en = cu[s + 1] < st ? st : cu[s + 1] > T ? T : cu[s + 1];
+  };
+  int mine = 0;
+  for (int s = s0; s < s1; ++s) {
+    int st, en;
+    seg(s, st, en);
+    mine += (en - st + C - 1) / C;
+  }
+  part[t] = mine;
+  __syncthreads();
+  if (t == 0) {
+    int run = 0;
+    for (int i = 0; i < 256; ++i) {
+      const int x = part[i];
+      part[i] = run;
+      run += x;
+    }
+    *ntot = run < nmax ? run : nmax;
+  }
+  __syncthreads();
+  int c = part[t];
+  for (int s = s0; s < s1; ++s) {
+    int st, en;
+    seg(s, st, en);
+    const int nch = (en - st + C - 1) / C;
+    const int first = c < nmax ? c : nmax;
+    const int room = nmax - first;
+    jtab[s] = int2{first, nch < room ? nch : room};
+    for (int j = 0; j < nch && c + j < nmax; ++j) {
+      const int a0 = st + j * C;
+      ctab[c + j] = int2{a0, en - a0 < C ? en - a0 : C};
+    }
+    c += nch;
+  }
 }
 
 }  // namespace gdn

@@ -131,3 +131,21 @@ def test_entry_points_reject_bad_arguments_without_launching(gdn):
     assert L.gdn_compose_prefix(0, 8, 128, 128, ok, ok, null, ok, null, 0, null) == -2
     assert L.gdn_compose_prefix(4, 8, 128, 128, odd, ok, null, ok, null, 0, null) == -4
     assert L.gdn_validate(None) == -1
+
+
+def test_varlen_checks_without_launching(gdn):
+    # packed sequences: one walk per sequence (no chunk-groups); NULL offsets
+    # are rejected before anything is launched
+    L = gdn.lib()
+    s = _shape(gdn, B=8, T=1000)
+    ws = gdn.workspace_size_varlen(s)
+    assert ws > 0
+    assert gdn.workspace_size_varlen(_shape(gdn, B=8, T=1000, n_groups=1)) == ws
+    with pytest.raises(gdn.GdnError):
+        gdn.workspace_size_varlen(_shape(gdn, B=8, T=1000, n_groups=4))
+    ok = _fake(1 << 20)
+    null = None
+    assert L.gdn_chunk_fwd_varlen(ctypes.byref(s), null, ok, ok, ok, ok, ok, null, ok, null, ok, ws, null) == -1
+    assert L.gdn_chunk_fwd_varlen(ctypes.byref(s), ok, ok, ok, ok, ok, ok, null, ok, null, ok, ws - 1, null) == -5
+    assert L.gdn_chunk_fwd_varlen(ctypes.byref(s), _fake((1 << 20) + 4), ok, ok, ok, ok, ok, null, ok, null, ok,
+                                  ws, null) == -4

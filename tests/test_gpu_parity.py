@@ -398,6 +398,73 @@ def test_forward_ragged_tail(gdn, dtype, C, T, Hqk, Hv, h0, ng):
     _check("h_T", h, h_ref, TOL[dtype], ro)
 
 
+def _packed(gdn, dtype, C, lens, Hqk, Hv, h0_std, seed):
+    # one packed row of the given sequence lengths, with per-sequence h0
+    T = int(sum(lens))
+    w = WORKLOADS["tiny"].replace(T=max(T, 1), Hqk=Hqk, Hv=Hv, chunk=C, dtype=dtype, h0_std=0.0, B=1)
+    x = make_inputs(w, device="cuda", seed=seed)
+    x = {kk: (vv[:, :T].contiguous() if vv is not None and kk != "h0" else vv) for kk, vv in x.items()}
+    gen = torch.Generator().manual_seed(seed + 1)
+    h0 = (torch.randn((len(lens), Hv, 128, 128), generator=gen) * h0_std).to("cuda")
+    cu = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32, device="cuda")
+    return x, h0, cu
+
+
+@pytest.mark.parametrize("dtype,C", [("bf16", 64), ("bf16", 128), ("f32", 64)])
+def test_varlen_equals_separate_calls(gdn, dtype, C):
+    # packed sequences (gdn_chunk_fwd_varlen) equal one gdn_chunk_fwd call per
+    # sequence, bit for bit (same kernels, same arithmetic), including empty
+    # and one-token sequences; and each matches the oracle
+    lens = [0, 1, C - 1, C, C + 1, 3 * C + 7, 0, 2 * C]
+    x, h0, cu = _packed(gdn, dtype, C, lens, 2, 4, 0.05, seed=C + len(dtype))
+    o, hT = gdn.chunk_fwd_varlen(x["q"], x["k"], x["v"], x["g"], x["beta"], cu, h0, chunk=C)
+    torch.cuda.synchronize()
+    a = 0
+    for s_, n in enumerate(lens):
+        if n == 0:
+            assert torch.equal(hT[s_], h0[s_])
+            continue
+        sl = slice(a, a + n)
+        args = [x[kk][:, sl].contiguous() for kk in ("q", "k", "v", "g", "beta")]
+        o1, h1 = gdn.chunk_fwd(*args, h0[s_:s_ + 1].contiguous(), chunk=C)
+        torch.cuda.synchronize()
+        assert torch.equal(o[:, sl], o1) and torch.equal(hT[s_:s_ + 1], h1), f"sequence {s_} (length {n})"
+        o_ref, h_ref = oracle.fwd(*[t.cpu() for t in args], h0[s_:s_ + 1].cpu())
+        ro = _rms(o_ref)
+        _check(f"o[{s_}]", o1.float().cpu().numpy(), o_ref, TOL[dtype], ro)
+        _check(f"h_T[{s_}]", h1.cpu().numpy(), h_ref, TOL[dtype], ro)
+        a += n
+
+
+def test_varlen_throughput_form(gdn):
+    # 16 sequences x 32 value heads = 512 walks: the throughput form of the
+    # walk and the separate output stage, against the oracle per sequence
+    rng = np.random.default_rng(5)
+    lens = [int(n) for n in rng.integers(1, 400, size=16)]
+    x, h0, cu = _packed(gdn, "bf16", 128, lens, 16, 32, 0.02, seed=17)
+    o, hT = gdn.chunk_fwd_varlen(x["q"], x["k"], x["v"], x["g"], x["beta"], cu, h0, chunk=128)
+    torch.cuda.synchronize()
+    a = 0
+    for s_, n in enumerate(lens):
+        sl = slice(a, a + n)
+        o_ref, h_ref = oracle.fwd(*[x[kk][:, sl].cpu() for kk in ("q", "k", "v", "g", "beta")], h0[s_:s_ + 1].cpu())
+        ro = _rms(o_ref)
+        _check(f"o[{s_}]", o[:, sl].float().cpu().numpy(), o_ref, 2e-2, ro)
+        _check(f"h_T[{s_}]", hT[s_:s_ + 1].cpu().numpy(), h_ref, 2e-2, ro)
+        a += n
+
+
+def test_varlen_all_empty(gdn):
+    # every sequence empty: h_T = h0 (and nothing else is touched)
+    x, h0, cu = _packed(gdn, "bf16", 128, [0, 0, 0], 1, 2, 0.1, seed=3)
+    q = torch.zeros((1, 0, 1, 128), dtype=torch.bfloat16, device="cuda")
+    v = torch.zeros((1, 0, 2, 128), dtype=torch.bfloat16, device="cuda")
+    gb = torch.zeros((1, 0, 2), dtype=torch.float32, device="cuda")
+    o, hT = gdn.chunk_fwd_varlen(q, q, v, gb, gb, cu, h0, chunk=128)
+    torch.cuda.synchronize()
+    assert o.numel() == 0 and torch.equal(hT, h0)
+
+
 @pytest.mark.parametrize("C", [64, 128])
 def test_forward_throughput_form(gdn, C):
     # 512 walks (B * H_v): the single walk takes its throughput form (eight
