@@ -263,6 +263,8 @@ def main():
     ap.add_argument("--secondary", default="long_256k",
                     help="second workload timed for context ('' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--packed", default="packed_8b_mix",
+                    help="packed variable-length workload reported beside the headline ('' = none)")
     ap.add_argument("--profile-run", action="store_true",
                     help="counter-collection run: calibration copies, then the workload's steps")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -380,6 +382,28 @@ def main():
                              "mfma_util_pct": 100.0 * f2 / (ms2 * 1e-3) / BF16_PEAK,
                              "hbm_frac": b2 / (ms2 * 1e-3) / HBM_PEAK}
         del x2, step2
+        torch.cuda.empty_cache()
+        x = make_inputs(w, device="cuda")
+    if args.packed:
+        # packed variable-length sequences (gdn_chunk_fwd_varlen), inputs and
+        # workspace resident; reported beside the headline, not as `value`
+        from workloads import make_packed_inputs
+        del x
+        torch.cuda.empty_cache()
+        wp, xp, cu = make_packed_inputs(args.packed, device="cuda")
+        shp = gdn.make_shape(len(cu) - 1, wp.T, wp.Hqk, wp.Hv, 128, 128, wp.chunk, 0, xp["k"].dtype,
+                             torch.float32)
+        wsp = torch.empty(gdn.workspace_size_varlen(shp), dtype=torch.uint8, device="cuda")
+        op = torch.empty((1, wp.T, wp.Hv, 128), dtype=torch.float32, device="cuda")
+        hp = torch.empty_like(xp["h0"])
+
+        def step_p(stages=None, events=None):
+            gdn.chunk_fwd_varlen(xp["q"], xp["k"], xp["v"], xp["g"], xp["beta"], cu, xp["h0"],
+                                 chunk=wp.chunk, workspace=wsp, out=op, final_state=hp)
+        msp = time_steps(step_p, max(5, args.steps // 4), 2)
+        line["packed"] = {"workload": args.packed, "sequences": len(cu) - 1, "tokens": wp.T,
+                          "value": wp.T / (msp * 1e-3), "unit": "tokens/s", "ms_per_step": msp}
+        del xp, op, hp, wsp
         torch.cuda.empty_cache()
         x = make_inputs(w, device="cuda")
     if not args.no_cpu_baseline:

@@ -133,3 +133,33 @@ def make_inputs(w: Workload, device="cpu", seed=None, t_block: int = 65536,
     if beta_scale is not None:
         beta.mul_(float(beta_scale))
     return dict(q=q, k=k, v=v, g=g, beta=beta, h0=h0)
+
+
+# Packed variable-length sequences: n_seq sequences, lengths drawn uniformly
+# from [1, max_len] with their own seeded generator, concatenated along one
+# row (B = 1) and drawn as one workload of their total length; one h0 per
+# sequence, N(0, h0_std^2).
+PACKED = {
+    "packed_8b_mix": dict(n_seq=16, max_len=8192, Hqk=16, Hv=32, chunk=128, dtype="bf16",
+                          h0_std=0.02, seed=2000,
+                          desc="16 packed sequences of 1..8192 tokens, Qwen3-Next-8B-shaped "
+                               "heads (16 qk / 32 v), chunk 128, bf16, h0~N(0,0.02) each"),
+}
+
+
+@torch.no_grad()
+def make_packed_inputs(name: str, device="cpu"):
+    """Inputs of a packed workload: the tensors of make_inputs over the total
+    length (B = 1), cu_seqlens (int32) and per-sequence h0."""
+    p = PACKED[name]
+    gen = torch.Generator().manual_seed(p["seed"])
+    lens = torch.randint(1, p["max_len"] + 1, (p["n_seq"],), generator=gen)
+    cu = torch.zeros(p["n_seq"] + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(lens, 0).to(torch.int32)
+    T = int(cu[-1])
+    w = Workload(name, 1, T, p["Hqk"], p["Hv"], 128, 128, p["chunk"], 1, p["dtype"], 0.0, p["desc"])
+    x = make_inputs(w, device=device, seed=p["seed"] + 1)
+    h0 = torch.randn((p["n_seq"], p["Hv"], 128, 128), generator=gen) * p["h0_std"]
+    x["h0"] = h0.to(device)
+    return w, x, cu.to(device)
+
