@@ -57,7 +57,7 @@ def stage_bytes(w, o_bytes=4):
     C, dk, dv = w.chunk, w.dk, w.dv
     tok = w.B * w.T
     s = 2 if w.dtype == "bf16" else 4
-    N = w.T // C
+    N = -(-w.T // C)   # chunks (a partial last chunk counts whole)
     J = max(w.n_groups, 1)
     BHv = w.B * w.Hv
     k_b = tok * w.Hqk * dk * s

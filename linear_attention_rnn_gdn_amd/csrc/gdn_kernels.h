@@ -148,7 +148,7 @@ constexpr float LOG2E = 1.4426950408889634f;
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 struct FwdArgs {
-  int B, T, Hqk, Hv, N;           // N = T / C chunks per sequence
+  int B, T, Hqk, Hv, N;           // N = ceil(T / C) chunks per sequence row (packed: the table capacity)
   const void *q, *k, *v;
   const float *g, *beta;
   float *G, *U, *Tm;              // prep outputs (Tm optional); U is U^T on the forward path
