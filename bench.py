@@ -275,7 +275,7 @@ def main():
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload, copy_bytes)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
