@@ -652,13 +652,21 @@ __global__ __launch_bounds__(PNT, 4) void prep_kernel(FwdArgs a) {   // two work
   //     that each lane ends with 4 consecutive columns of one row of W.
   // (7) U = (T diag(beta)) V, computed as is, so that each lane ends with 4
   //     consecutive rows of one column of U (= 4 consecutive entries of U^T).
-  // A wave takes its two row tiles and d tiles md0 .. md0 + TDW - 1; T is
-  // lower triangular, so row tile m needs k < 16(m+1).  The T fragments of
+  // A wave takes row tiles of its pair and d tiles md0 .. md0 + TDW - 1 (see
+  // below); T is lower triangular, so row tile m needs k < 16(m+1).  The T fragments of
   // k-blocks past the diagonal read T's zero-filled or neighbouring entries
   // and their products are skipped.
-  constexpr int TD = D / 16, TDW = TD / WPG;
+  // At C = 128 (two waves per row-tile pair) each wave takes one row tile of
+  // the pair, mrow[sub], for all d tiles: every T' fragment is then split
+  // once per pass instead of once per wave of the pair (the split is most of
+  // this phase's vector-ALU work, which bounds the kernel; the longer matrix
+  // chain of the pair's larger tile costs less: 1 us less per launch at the
+  // 4096-token layer).  At C = 64 (four waves per pair) the d tiles are split.
+  constexpr bool ONE = C == 128;
+  constexpr int TD = D / 16, TDW = ONE ? TD : TD / WPG;
   static_assert(TD % WPG == 0 && TDW % 2 == 0, "W fragments pair d tiles");
-  const int md0 = sub * TDW;
+  static_assert(!ONE || WPG == RU, "one row tile of the pair per wave");
+  const int md0 = ONE ? 0 : sub * TDW;
   // swizzle term of this lane's X^T rows 16md + lr
   int xsw[TDW];
 #pragma unroll
@@ -675,6 +683,7 @@ __global__ __launch_bounds__(PNT, 4) void prep_kernel(FwdArgs a) {   // two work
     // still holds its V block)
 #pragma unroll
     for (int u = 0; u < RU; ++u) {
+      if (ONE && u != sub) continue;
       f32x4 acc[TDW];
 #pragma unroll
       for (int md = 0; md < TDW; ++md) acc[md] = zero4();
