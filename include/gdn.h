@@ -153,7 +153,8 @@ gdn_status gdn_chunk_fwd_timed(const gdn_shape *shape, int32_t stages, const voi
  *   h0, h_T [B, H_v, d_k, d_v] fp32 (h0 NULL = zero; h_T NULL = not wanted)
  *   ws    at least gdn_workspace_size_varlen() bytes.
  * Work is planned on the device (no host copy of cu_seqlens is needed); other
- * conventions as gdn_chunk_fwd. */
+ * conventions as gdn_chunk_fwd, except the sequence count: B * H_v may reach
+ * 2^26 (the padded-batch entry points keep B * H_v <= 65535). */
 gdn_status gdn_workspace_size_varlen(const gdn_shape *shape, size_t *bytes);
 gdn_status gdn_chunk_fwd_varlen(const gdn_shape *shape, const int32_t *cu_seqlens, const void *q,
                                 const void *k, const void *v, const float *g, const float *beta,

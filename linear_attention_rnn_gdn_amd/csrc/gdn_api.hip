@@ -319,7 +319,11 @@ const char *gdn_status_str(gdn_status s) {
   return "unknown status";
 }
 
-gdn_status gdn_validate(const gdn_shape *s) {
+}  // extern "C"
+
+namespace {
+// checks shared by the padded-batch and packed-sequence entry points
+gdn_status validate_common(const gdn_shape *s) {
   if (!s) return GDN_ERR_NULL;
   if (s->dtype != GDN_F32 && s->dtype != GDN_BF16) return GDN_ERR_DTYPE;
   if (s->o_dtype != GDN_F32 && s->o_dtype != GDN_BF16) return GDN_ERR_DTYPE;
@@ -328,6 +332,14 @@ gdn_status gdn_validate(const gdn_shape *s) {
   if (s->chunk != 64 && s->chunk != 128) return GDN_ERR_SHAPE;
   if (s->dtype == GDN_F32 && s->chunk != 64) return GDN_ERR_SHAPE;
   if (s->n_groups < 0) return GDN_ERR_SHAPE;
+  return GDN_OK;
+}
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_validate(const gdn_shape *s) {
+  GDN_TRY(validate_common(s));
   const int64_t N64 = ((int64_t)s->T + s->chunk - 1) / s->chunk;
   if (N64 > 65535 || (int64_t)s->B * s->H_v > 65535) return GDN_ERR_SHAPE;
   const int N = (int)N64;
@@ -385,13 +397,22 @@ gdn_status gdn_chunk_fwd_timed(const gdn_shape *s, int32_t stages, const void *q
   return dispatch(*s, f);
 }
 
-// host checks of a packed-sequences problem (s->B sequences, s->T tokens)
+}  // extern "C"
+
+namespace {
+// host checks of a packed-sequences problem (s->B sequences, s->T tokens):
+// the chunk table bounds the (chunk, head) grids, the walk grid has 8
+// workgroups per (sequence, value head) at most (16 for a fold, not offered)
 gdn_status validate_varlen(const gdn_shape *s) {
-  GDN_TRY(gdn_validate(s));
+  GDN_TRY(validate_common(s));
   if (s->n_groups > 1) return GDN_ERR_SHAPE;
   if ((int64_t)varlen_nmax(*s) * s->H_v > (1 << 30)) return GDN_ERR_SHAPE;
+  if ((int64_t)s->B * s->H_v > (1 << 26)) return GDN_ERR_SHAPE;
   return GDN_OK;
 }
+}  // namespace
+
+extern "C" {
 
 gdn_status gdn_workspace_size_varlen(const gdn_shape *s, size_t *bytes) {
   if (!bytes) return GDN_ERR_NULL;

@@ -149,3 +149,10 @@ def test_varlen_checks_without_launching(gdn):
     assert L.gdn_chunk_fwd_varlen(ctypes.byref(s), ok, ok, ok, ok, ok, ok, null, ok, null, ok, ws - 1, null) == -5
     assert L.gdn_chunk_fwd_varlen(ctypes.byref(s), _fake((1 << 20) + 4), ok, ok, ok, ok, ok, null, ok, null, ok,
                                   ws, null) == -4
+
+
+def test_varlen_allows_many_sequences(gdn):
+    # packed sequences are bounded by their grids only: 4096 sequences x 32
+    # value heads are accepted (the padded-batch entry point keeps B*H_v <= 65535)
+    assert gdn.workspace_size_varlen(_shape(gdn, B=4096, T=40000)) > 0
+    assert gdn.validate(_shape(gdn, B=4096, T=40000)) == -2

@@ -454,6 +454,24 @@ def test_varlen_throughput_form(gdn):
         a += n
 
 
+def test_varlen_many_short_sequences(gdn):
+    # 2100 sequences of 1..20 tokens x 32 value heads (67,200 walks, more
+    # than a padded batch allows): a sample of sequences against the oracle
+    rng = np.random.default_rng(9)
+    lens = [int(n) for n in rng.integers(1, 21, size=2100)]
+    x, h0, cu = _packed(gdn, "bf16", 128, lens, 16, 32, 0.02, seed=23)
+    o, hT = gdn.chunk_fwd_varlen(x["q"], x["k"], x["v"], x["g"], x["beta"], cu, h0, chunk=128)
+    torch.cuda.synchronize()
+    starts = np.concatenate([[0], np.cumsum(lens)])
+    for s_ in list(range(0, 2100, 97)) + [2099]:
+        sl = slice(int(starts[s_]), int(starts[s_ + 1]))
+        o_ref, h_ref = oracle.fwd(*[x[kk][:, sl].cpu() for kk in ("q", "k", "v", "g", "beta")],
+                                  h0[s_:s_ + 1].cpu())
+        ro = _rms(o_ref)
+        _check(f"o[{s_}]", o[:, sl].float().cpu().numpy(), o_ref, 2e-2, ro)
+        _check(f"h_T[{s_}]", hT[s_:s_ + 1].cpu().numpy(), h_ref, 2e-2, ro)
+
+
 def test_varlen_all_empty(gdn):
     # every sequence empty: h_T = h0 (and nothing else is touched)
     x, h0, cu = _packed(gdn, "bf16", 128, [0, 0, 0], 1, 2, 0.1, seed=3)
