@@ -816,7 +816,7 @@ __global__ __launch_bounds__(64 * WPG) void walk_shared_kernel(FwdArgs a) {
   size_t cb0;
   int cpj;
   long long ktoff;
-  if (a.jtab) {
+  if (KIND != FOLD && a.jtab) {   // (packed sequences walk, never fold)
     const int2 jt = a.jtab[bh / a.Hv];
     // (wave-uniform: scalar loop bounds)
     cb0 = (bh % a.Hv) * a.N + __builtin_amdgcn_readfirstlane(jt.x);
@@ -868,7 +868,7 @@ __global__ __launch_bounds__(64 * WPG) void walk_shared_kernel(FwdArgs a) {
   };
   // an empty sequence (packed sequences): the final state is the initial one,
   // and no chunk operand is touched
-  if (cpj == 0) {
+  if (KIND != FOLD && cpj == 0) {
     store_final();
     return;
   }
@@ -1074,7 +1074,7 @@ __global__ __launch_bounds__(64 * NWS) void walk_ring_kernel(FwdArgs a) {
   size_t cb0;
   int cpj;
   long long ktoff;
-  if (a.jtab) {
+  if (KIND != FOLD && a.jtab) {   // (packed sequences walk, never fold)
     const int2 jt = a.jtab[bh / a.Hv];
     // (wave-uniform: scalar loop bounds)
     cb0 = (bh % a.Hv) * a.N + __builtin_amdgcn_readfirstlane(jt.x);
@@ -1126,7 +1126,7 @@ __global__ __launch_bounds__(64 * NWS) void walk_ring_kernel(FwdArgs a) {
   };
   // an empty sequence (packed sequences): the final state is the initial one,
   // and no chunk operand is touched
-  if (cpj == 0) {
+  if (KIND != FOLD && cpj == 0) {
     store_final();
     return;
   }
