@@ -201,11 +201,14 @@ def chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, h0=None, chunk=128, o_dtype=t
                      output_final_state=True, workspace=None, out=None, final_state=None, stream=None):
     """Chunked forward over packed variable-length sequences
     (gdn_chunk_fwd_varlen).  q, k [1,T,H_qk,d_k]; v [1,T,H_v,d_v]; g, beta
-    [1,T,H_v]; cu_seqlens int32 [n+1] on the device (sequence s = tokens
-    cu[s]..cu[s+1]); h0 [n,H_v,d_k,d_v] or None.  Returns (o, h_T [n,...] or None)."""
+    [1,T,H_v]; cu_seqlens int32 [n+1] on the device, or a Python sequence of
+    the n+1 offsets (sequence s = tokens cu[s]..cu[s+1]); h0 [n,H_v,d_k,d_v]
+    or None.  Returns (o, h_T [n,...] or None)."""
     B, T, Hqk, Hv, dk, dv, dev = _inputs(q, k, v, g, beta)
     if B != 1:
         raise ValueError("packed sequences: the batch dimension of q, k, v, g, beta must be 1")
+    if not isinstance(cu_seqlens, torch.Tensor):   # a sequence of offsets
+        cu_seqlens = torch.tensor(list(cu_seqlens), dtype=torch.int32, device=dev)
     _need(cu_seqlens, "cu_seqlens", torch.int32, None, dev)
     nseq = cu_seqlens.numel() - 1
     if nseq < 1:

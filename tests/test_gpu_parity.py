@@ -479,8 +479,9 @@ def test_varlen_all_empty(gdn):
     v = torch.zeros((1, 0, 2, 128), dtype=torch.bfloat16, device="cuda")
     gb = torch.zeros((1, 0, 2), dtype=torch.float32, device="cuda")
     o, hT = gdn.chunk_fwd_varlen(q, q, v, gb, gb, cu, h0, chunk=128)
+    o2, hT2 = gdn.chunk_fwd_varlen(q, q, v, gb, gb, [0, 0, 0, 0], h0, chunk=128)   # offsets as a list
     torch.cuda.synchronize()
-    assert o.numel() == 0 and torch.equal(hT, h0)
+    assert o.numel() == 0 and torch.equal(hT, h0) and torch.equal(hT2, h0)
 
 
 @pytest.mark.parametrize("C", [64, 128])
