@@ -242,12 +242,13 @@ def test_run_to_run_bitwise_determinism(gdn):
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
-@pytest.mark.parametrize("C,N,ng", [(64, 16, 0), (128, 32, 0), (128, 16, 4)])
-def test_stages_one_by_one_equal_one_call(gdn, C, N, ng):
+@pytest.mark.parametrize("C,N,ng,tail", [(64, 16, 0, 0), (128, 32, 0, 0), (128, 16, 4, 0), (128, 16, 4, 37)])
+def test_stages_one_by_one_equal_one_call(gdn, C, N, ng, tail):
     # gdn_chunk_fwd_stages issued one stage per call on one stream (the
     # per-kernel timing path of bench.py) must equal one gdn_chunk_fwd call
-    # bit for bit: the stages communicate only through the workspace
-    w = WORKLOADS["tiny"].replace(T=C * N, Hqk=2, Hv=4, chunk=C, dtype="bf16", h0_std=0.05)
+    # bit for bit: the stages communicate only through the workspace (also
+    # with a partial last chunk: `tail` tokens short)
+    w = WORKLOADS["tiny"].replace(T=C * N - tail, Hqk=2, Hv=4, chunk=C, dtype="bf16", h0_std=0.05)
     x = make_inputs(w, device="cuda", seed=N + ng)
     args = (x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"])
     o1, h1 = gdn.chunk_fwd(*args, chunk=C, n_groups=ng)
@@ -470,6 +471,19 @@ def test_varlen_many_short_sequences(gdn):
         ro = _rms(o_ref)
         _check(f"o[{s_}]", o[:, sl].float().cpu().numpy(), o_ref, 2e-2, ro)
         _check(f"h_T[{s_}]", hT[s_:s_ + 1].cpu().numpy(), h_ref, 2e-2, ro)
+
+
+def test_varlen_bf16_output(gdn):
+    # packed sequences with a bf16 o: the fp32-o call's values rounded once
+    # (the output stage rounds its fp32 result), bit for bit
+    lens = [70, 1, 300, 128]
+    x, h0, cu = _packed(gdn, "bf16", 128, lens, 2, 4, 0.05, seed=31)
+    args = (x["q"], x["k"], x["v"], x["g"], x["beta"], cu, h0)
+    o32, h32 = gdn.chunk_fwd_varlen(*args, chunk=128)
+    o16, h16 = gdn.chunk_fwd_varlen(*args, chunk=128, o_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert o16.dtype == torch.bfloat16
+    assert torch.equal(o16, o32.to(torch.bfloat16)) and torch.equal(h16, h32)
 
 
 def test_varlen_all_empty(gdn):
