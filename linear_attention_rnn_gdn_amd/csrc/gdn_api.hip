@@ -131,10 +131,14 @@ gdn_status launch_walk(const FwdArgs &a, const Lx &x) {
   // LDS.  Fewer (a short walk, latency-bound): one slice per workgroup of 2
   // or 4 waves that split its rows, so the walk spreads over the chip.
   const long units = (long)a.B * a.Hv * a.jobs;
+  constexpr int NWS = C >= 128 ? 4 : 2;   // waves per slice: whole k-blocks of V' rows each
   if (units * (width / 128) >= 512) {
     launch(walk_shared_kernel<C, TI, MODE, KIND, 8>, dim3((unsigned)(units * (width / 128))), dim3(512), x, a);
+  } else if (KIND == WALK && a.Hs && a.Vn && units > 32 && units <= 64) {
+    // two latency-form slices per compute unit would each stream the same
+    // operands: one workgroup of two slices shares a copy in LDS instead
+    launch(walk_pair_kernel<C, TI, MODE, NWS>, dim3((unsigned)(units * (D / 32))), dim3(128 * NWS), x, a);
   } else {
-    constexpr int NWS = C >= 128 ? 4 : 2;   // waves per slice: whole k-blocks of V' rows each
     launch(walk_ring_kernel<C, TI, MODE, KIND, NWS>, dim3((unsigned)(units * (width / 16))), dim3(64 * NWS), x, a);
   }
   return check_launch();

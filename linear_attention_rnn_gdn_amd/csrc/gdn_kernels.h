@@ -1276,6 +1276,251 @@ __global__ __launch_bounds__(64 * NWS) void walk_ring_kernel(FwdArgs a) {
 }
 
 // ----------------------------------------------------------------------------
+// walk, paired form: two 16-column slices of one head per workgroup, each
+// split over NWS waves by rows as in walk_ring_kernel, for walks too many to
+// give each slice a compute unit of its own and too few for the throughput
+// form (33..64 walks of 8 slices: one workgroup per compute unit).  The two
+// slices need the same W and K^T fragments: they are copied into LDS once
+// per chunk (global_load_lds, double-buffered, one chunk ahead) instead of
+// being streamed by every wave, which halves what each compute unit moves
+// per chunk against two latency-form workgroups.  State and d o V' operands
+// pass between a slice's waves through LDS, as in the latency form.  WALK
+// mode only, with h and V' for the output stage always written.
+template <int C, typename TI, int MODE, int NWS>
+__global__ __launch_bounds__(128 * NWS) void walk_pair_kernel(FwdArgs a) {
+  using PR = Prec<MODE>;
+  using PKw = PolicyKinds<PR::wh>;
+  using PKk = PolicyKinds<PR::kv>;
+  using OPS = WalkOps<C, TI>;
+  constexpr bool F32 = sizeof(TI) == 4;
+  static_assert(PKw::a == (F32 ? F_F32 : F_BF16) && PKk::a == PKw::a, "W and K^T fragments are used as stored");
+  using AF = Frag<PKw::a>;
+  using HF = Frag<PKw::b>;   // state operand (for W h)
+  using VF = Frag<PKk::b>;   // d o V' operand (for K^T (d o V'))
+  constexpr int NSL = 2, WPG = NSL * NWS;               // slices per workgroup, waves
+  constexpr int MV = OPS::MV, MH = OPS::MH, KBW = OPS::KBW, KBK = OPS::KBK;
+  constexpr int FW = OPS::FW, BPF = OPS::BPF, NBLK = OPS::NBLK;
+  constexpr int MVW = MV / NWS, MHW = MH / NWS;         // row tiles per wave
+  constexpr int KBWW = KBW / NWS, KBKW = KBK / NWS;     // k-blocks written by each wave
+  static_assert(MVW % 2 == 0 && MHW % 2 == 0 && KBWW >= 1 && KBKW >= 1, "each wave holds whole k-blocks");
+  static_assert(NBLK % WPG == 0, "copies shared out evenly");
+  __shared__ __align__(16) TI bufA[OPS::ELEMS];
+  __shared__ __align__(16) TI bufB[OPS::ELEMS];
+  __shared__ __align__(16) HF xh[NSL][KBW][64];
+  __shared__ __align__(16) VF xv[NSL][KBK][64];
+
+  int unit, pair;
+  xcd_unit(blockIdx.x, D / 16 / NSL, a.B * a.Hv * a.jobs, unit, pair);
+  const int job = unit % a.jobs;
+  const size_t bh = (size_t)(unit / a.jobs);
+  const int lane = threadIdx.x & 63, lr = lane & 15, g = lane >> 4;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int sl = wid / NWS, w = wid % NWS;              // slice of the pair, row part
+  const int slice = pair * NSL + sl, c0 = slice * 16;
+  const int mv0 = w * MVW, mh0 = w * MHW;               // this wave's first V' / state tile
+  size_t cb0;
+  int cpj;
+  long long ktoff;
+  if (a.jtab) {   // packed sequences
+    const int2 jt = a.jtab[bh / a.Hv];
+    cb0 = (bh % a.Hv) * a.N + __builtin_amdgcn_readfirstlane(jt.x);
+    cpj = __builtin_amdgcn_readfirstlane(jt.y);
+    ktoff = kt_offset(a, bh % a.Hv);
+  } else {
+    cb0 = bh * a.N + a.n0 + (size_t)job * a.cpj;
+    cpj = a.cpj;
+    ktoff = kt_offset(a, bh);
+  }
+  cb0 = uniform64(cb0);
+  ktoff = (long long)uniform64((unsigned long long)ktoff);
+
+  // state tiles of this wave: h[t] holds rows 16(mh0+t) + 4g + i, column c0 + lr
+  f32x4 h[MHW];
+#pragma unroll
+  for (int t = 0; t < MHW; ++t) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int kr = 16 * (mh0 + t) + 4 * g + i;
+      float x = 0.f;
+      if (a.init) {
+        const float *src = a.init_per_job ? a.init + (bh * a.jobs + job) * D * D : a.init + bh * D * D;
+        x = src[(size_t)kr * D + c0 + lr];
+      }
+      h[t][i] = x;
+    }
+  }
+  auto store_final = [&]() {
+    if (a.fin) {
+#pragma unroll
+      for (int t = 0; t < MHW; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a.fin[bh * D * D + (size_t)(16 * (mh0 + t) + 4 * g + i) * D + c0 + lr] = h[t][i];
+    }
+  };
+  if (cpj == 0) {   // an empty packed sequence
+    store_final();
+    return;
+  }
+
+  // the chunk's W and K^T fragments into an LDS buffer (block j: half
+  // j % BPF of fragment j / BPF), shared out over the WPG waves.  The copies'
+  // LDS addresses are plain numbers to the compiler, which then does not tie
+  // the LDS reads that follow to them (it would wait for every copy before
+  // the first read of any LDS array); the chunk barrier waits for them.
+  const unsigned loff = lane * 16 * BPF;
+  auto lds_addr = [](TI *buf) {
+    unsigned x = (unsigned)(size_t)(__attribute__((address_space(3))) char *)buf;
+    asm volatile("" : "+s"(x));
+    return x;
+  };
+  const unsigned ldsA = lds_addr(bufA), ldsB = lds_addr(bufB);
+  auto stage = [&](unsigned lbuf, size_t cb) {
+    const char *wbase = reinterpret_cast<const char *>(a.W) + cb * C * D * sizeof(TI);
+    const char *kbase = reinterpret_cast<const char *>(a.Kt) + (cb + ktoff) * D * C * sizeof(TI);
+#pragma unroll
+    for (int jj = 0; jj < NBLK / WPG; ++jj) {
+      const int j = jj * WPG + wid, p = j / BPF, hh = j % BPF;
+      const char *src = (p < FW ? wbase + p * 1024 * BPF : kbase + (p - FW) * 1024 * BPF) + hh * 16;
+      __builtin_amdgcn_global_load_lds((const void *)(src + loff),
+                                       (__attribute__((address_space(3))) void *)(size_t)(lbuf + j * 1024),
+                                       16, 0, 0);
+    }
+  };
+  auto frag = [&](const TI *buf, int p) -> AF {
+    AF f;
+    const char *base = reinterpret_cast<const char *>(buf) + p * BPF * 1024 + lane * 16;
+    if constexpr (F32) {
+      const float4 x0 = *reinterpret_cast<const float4 *>(base);
+      const float4 x1 = *reinterpret_cast<const float4 *>(base + 1024);
+      f.v[0] = x0.x; f.v[1] = x0.y; f.v[2] = x0.z; f.v[3] = x0.w;
+      f.v[4] = x1.x; f.v[5] = x1.y; f.v[6] = x1.z; f.v[7] = x1.w;
+    } else {
+      f.hi = *reinterpret_cast<const bf16x8 *>(base);
+    }
+    return f;
+  };
+  struct UG {
+    float4 u[MVW], g[MVW];
+    float glast;
+  };
+  auto fetch_ug = [&](size_t cb, UG &x) {
+#pragma unroll
+    for (int m = 0; m < MVW; ++m) {
+      x.u[m] = *reinterpret_cast<const float4 *>(a.U + ((cb * MV + mv0 + m) * (D / 16) + slice) * 256 + lane * 4);
+      x.g[m] = *reinterpret_cast<const float4 *>(a.G + cb * C + 16 * (mv0 + m) + 4 * g);
+    }
+    x.glast = a.G[cb * C + C - 1 + vgpr_zero()];
+  };
+  auto put_state = [&]() {
+#pragma unroll
+    for (int kbl = 0; kbl < KBWW; ++kbl) {   // own k-block kbl (tiles 2kbl, 2kbl+1)
+      const float x[8] = {h[2 * kbl][0], h[2 * kbl][1], h[2 * kbl][2], h[2 * kbl][3],
+                          h[2 * kbl + 1][0], h[2 * kbl + 1][1], h[2 * kbl + 1][2], h[2 * kbl + 1][3]};
+      xh[sl][w * KBWW + kbl][lane] = make_frag<PKw::b>(x);
+    }
+  };
+  // The chunk's end: this wave's copies and loads for the next chunk done, and
+  // its LDS writes, then every wave's.  The memory counter drains in issue
+  // order and the V' stores are the last NVS operations issued, so waiting
+  // down to NVS leaves them in flight.
+  constexpr int NVS = PR::v_store == ST_BF16 ? MVW / 2 : MVW;   // 16-byte stores of V'
+  static_assert(NVS < 16, "vmcnt field");
+  auto chunk_barrier = [&]() {
+    __builtin_amdgcn_s_waitcnt(0x0070 | NVS);   // vmcnt(NVS) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+  };
+
+  UG ug[2];
+  fetch_ug(cb0, ug[0]);
+  stage(ldsA, cb0);
+  put_state();
+  __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+
+  auto step = [&](const TI *cur, unsigned nxt, UG &cu, UG &nu, int cc) {
+    const size_t cb = cb0 + cc;
+    const bool more = cc + 1 < cpj;
+    // issue order: the chunk-start state for the output stage, the next
+    // chunk's U and G (the last chunk: repeated, unused) and operand copies,
+    // then (after the W h product) this chunk's V'
+    store_result_tiles<PR::h_store>(a.Hs + ((cb * (D / 16) + slice) * MH + mh0) * Store<PR::h_store>::tile_floats, h, lane);
+    fetch_ug(more ? cb + 1 : cb, nu);
+    if (more) stage(nxt, cb + 1);
+    asm volatile("" ::: "memory");   // nothing below moves above the copies
+    const float gl2 = cu.glast * LOG2E;
+    float dcy[MVW][4];
+#pragma unroll
+    for (int m = 0; m < MVW; ++m) {
+      dcy[m][0] = exp2_fast(gl2 - cu.g[m].x * LOG2E);
+      dcy[m][1] = exp2_fast(gl2 - cu.g[m].y * LOG2E);
+      dcy[m][2] = exp2_fast(gl2 - cu.g[m].z * LOG2E);
+      dcy[m][3] = exp2_fast(gl2 - cu.g[m].w * LOG2E);
+    }
+    // V' = U - W h over all state k-blocks (the slice's, from LDS)
+    HF hb[KBW];
+#pragma unroll
+    for (int kb = 0; kb < KBW; ++kb) hb[kb] = xh[sl][kb][lane];
+    f32x4 acc[MVW];
+#pragma unroll
+    for (int m = 0; m < MVW; ++m) {
+      acc[m] = zero4();
+#pragma unroll
+      for (int kb = 0; kb < KBW; ++kb) mma(acc[m], frag(cur, (mv0 + m) * KBW + kb), hb[kb]);
+    }
+    VF vb[KBK];
+    {
+      float s[MVW][4];
+      f32x4 vps[MVW];
+#pragma unroll
+      for (int m = 0; m < MVW; ++m) {
+        const float4 uu = cu.u[m];
+        vps[m] = f32x4{uu.x - acc[m][0], uu.y - acc[m][1], uu.z - acc[m][2], uu.w - acc[m][3]};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[m][i] = vps[m][i] * dcy[m][i];
+      }
+      store_result_tiles<PR::v_store>(a.Vn + ((cb * (D / 16) + slice) * MV + mv0) * Store<PR::v_store>::tile_floats, vps, lane);
+#pragma unroll
+      for (int kbl = 0; kbl < KBKW; ++kbl) {
+        const float x[8] = {s[2 * kbl][0], s[2 * kbl][1], s[2 * kbl][2], s[2 * kbl][3],
+                            s[2 * kbl + 1][0], s[2 * kbl + 1][1], s[2 * kbl + 1][2], s[2 * kbl + 1][3]};
+        xv[sl][w * KBKW + kbl][lane] = make_frag<PKk::b>(x);
+      }
+      lds_barrier();
+#pragma unroll
+      for (int kb = 0; kb < KBK; ++kb) {
+        if constexpr (PKk::b == F_SPLIT) {
+          vb[kb].hi = xv[sl][kb][lane].hi;
+          vb[kb].lo = xv[sl][kb][lane].lo;
+        } else {
+          vb[kb] = xv[sl][kb][lane];
+        }
+      }
+    }
+    // h <- e^{G_last} h + K^T (d o V') for this wave's state rows
+    const float gl = exp2_fast(gl2);
+    f32x4 acc2[MHW];
+#pragma unroll
+    for (int t = 0; t < MHW; ++t) {
+      acc2[t] = zero4();
+#pragma unroll
+      for (int kb = 0; kb < KBK; ++kb) mma(acc2[t], frag(cur, FW + (mh0 + t) * KBK + kb), vb[kb]);
+    }
+#pragma unroll
+    for (int t = 0; t < MHW; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) h[t][i] = gl * h[t][i] + acc2[t][i];
+    put_state();
+    chunk_barrier();
+  };
+  // two chunks per trip: the LDS buffers and U/G sets alternate statically
+  for (int cc = 0; cc < cpj; cc += 2) {
+    step(bufA, ldsB, ug[0], ug[1], cc);
+    if (cc + 1 < cpj) step(bufB, ldsA, ug[1], ug[0], cc + 1);
+  }
+  store_final();
+}
+
+// ----------------------------------------------------------------------------
 // exclusive prefix of affine pairs: h_in[0] = h_init, h_in[j+1] = A_j h_in[j]
 // + B_j, h_final = A_{n-1} h_in[n-1] + B_{n-1}.  One workgroup per 16-column
 // slice of the state (the recurrence is column-separable); its NWS waves

@@ -511,6 +511,43 @@ def test_forward_throughput_form(gdn, C):
     _check("h_T", h, h_ref, 2e-2, ro)
 
 
+@pytest.mark.parametrize("dtype,C,T,B,Hqk,Hv,h0", [
+    ("bf16", 128, 2 * 128 + 1, 1, 3, 33, 0.02),   # 33 walks, 3 chunks (the last one token)
+    ("bf16", 64, 5 * 64 - 3, 3, 4, 16, 0.0),      # 48 walks, partial last chunk
+    ("f32", 64, 7 * 64, 2, 4, 20, 0.5),           # 40 walks, odd chunk count, strong h0
+    ("bf16", 128, 4 * 128, 2, 32, 32, 0.1),       # 64 walks, as the dense layer
+])
+def test_forward_paired_form(gdn, dtype, C, T, B, Hqk, Hv, h0):
+    # 33..64 walks (B * H_v): two slices of a head per workgroup sharing one
+    # LDS copy of each chunk's W and K^T
+    w = WORKLOADS["tiny"].replace(T=T, B=B, Hqk=Hqk, Hv=Hv, chunk=C, dtype=dtype, h0_std=h0)
+    x = make_inputs(w, device="cuda", seed=T + B * Hv)
+    o, h, o_ref, h_ref = _run_and_compare(gdn, w, x)
+    ro = _rms(o_ref)
+    _check("o", o, o_ref, TOL[dtype], ro)
+    _check("h_T", h, h_ref, TOL[dtype], ro)
+
+
+def test_varlen_paired_form(gdn):
+    # 3 sequences x 16 value heads = 48 walks (the paired form), one of them
+    # empty and one a single token, against the oracle per sequence
+    lens = [0, 1, 3 * 128 + 50]
+    x, h0, cu = _packed(gdn, "bf16", 128, lens, 4, 16, 0.05, seed=23)
+    o, hT = gdn.chunk_fwd_varlen(x["q"], x["k"], x["v"], x["g"], x["beta"], cu, h0, chunk=128)
+    torch.cuda.synchronize()
+    assert torch.equal(hT[0], h0[0])
+    a = 0
+    for s_, n in enumerate(lens):
+        if n == 0:
+            continue
+        sl = slice(a, a + n)
+        o_ref, h_ref = oracle.fwd(*[x[kk][:, sl].cpu() for kk in ("q", "k", "v", "g", "beta")], h0[s_:s_ + 1].cpu())
+        ro = _rms(o_ref)
+        _check(f"o[{s_}]", o[:, sl].float().cpu().numpy(), o_ref, 2e-2, ro)
+        _check(f"h_T[{s_}]", hT[s_:s_ + 1].cpu().numpy(), h_ref, 2e-2, ro)
+        a += n
+
+
 @pytest.mark.parametrize("name", ["long_256k", "million_1m"])
 def test_long_sequence_full_size_sampled(gdn, name):
     # full length, in the benchmark's launch configuration; the oracle walks
