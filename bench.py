@@ -119,6 +119,8 @@ def _stage_of(kernel_name):
         return "prefix"
     if "out_kernel" in n:
         return "out"
+    if "walk_pair_kernel" in n:   # (walk only; no KIND argument)
+        return "walk"
     if "walk_ring_kernel" in n or "walk_shared_kernel" in n:
         # walk_*_kernel<C, TI, MODE, KIND[, WPG]>: KIND 1 = fold (demangled or
         # mangled name; TI is not an integer argument in the mangled form)

@@ -132,9 +132,12 @@ gdn_status launch_walk(const FwdArgs &a, const Lx &x) {
   // or 4 waves that split its rows, so the walk spreads over the chip.
   const long units = (long)a.B * a.Hv * a.jobs;
   constexpr int NWS = C >= 128 ? 4 : 2;   // waves per slice: whole k-blocks of V' rows each
+  // (the walk always hands h and V' to the output stage; the throughput and
+  // paired forms count on those stores)
+  if (KIND == WALK && (!a.Hs || !a.Vn)) return GDN_ERR_NULL;
   if (units * (width / 128) >= 512) {
     launch(walk_shared_kernel<C, TI, MODE, KIND, 8>, dim3((unsigned)(units * (width / 128))), dim3(512), x, a);
-  } else if (KIND == WALK && a.Hs && a.Vn && units > 32 && units <= 64) {
+  } else if (KIND == WALK && units > 32 && units <= 64) {
     // two latency-form slices per compute unit would each stream the same
     // operands: one workgroup of two slices shares a copy in LDS instead
     launch(walk_pair_kernel<C, TI, MODE, NWS>, dim3((unsigned)(units * (D / 32))), dim3(128 * NWS), x, a);

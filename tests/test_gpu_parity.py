@@ -372,6 +372,47 @@ def test_groups_weak_decay_compose_matters(gdn):
     assert _err(bad, o_ref) > 10 * 2e-2 * ro
 
 
+@pytest.mark.parametrize("C", [64, 128])
+def test_sequence_shards_through_the_boundary(gdn, C):
+    # The sequence-sharded flow, each shard standing in for a device, through
+    # the exported entry points only: every shard folds its whole length into
+    # one affine pair (gdn_chunk_fold, one group); the pairs are gathered
+    # and their exclusive prefix (gdn_compose_prefix) gives each shard its
+    # incoming state; each shard's forward from that state (gdn_chunk_fwd)
+    # gives its outputs.  Together they are the whole sequence's o and h_T.
+    # Weak decay keeps each shard's map far from zero, so the incoming
+    # states carry the earlier shards.
+    S, L = 4, 4 * C
+    w = WORKLOADS["tiny"].replace(T=S * L, Hqk=2, Hv=4, chunk=C, dtype="bf16", h0_std=0.05, B=2)
+    x = make_inputs(w, device="cuda", seed=40 + C, g_const=0.0, beta_scale=0.1)
+    shard = lambda t, d: t[:, d * L:(d + 1) * L].contiguous()
+    A, Bm = [], []
+    for d in range(S):
+        a_, b_ = gdn.chunk_fold(*[shard(x[kk], d) for kk in ("k", "v", "g", "beta")], n_groups=1, chunk=C)
+        A.append(a_)
+        Bm.append(b_)
+    BH = w.B * w.Hv
+    A = torch.cat(A, dim=2).reshape(BH, S, 128, 128)
+    Bm = torch.cat(Bm, dim=2).reshape(BH, S, 128, 128)
+    h_in, h_fin = gdn.compose_prefix(A, Bm, x["h0"].reshape(BH, 128, 128), split_bf16=True)
+    outs, h_last = [], None
+    for d in range(S):
+        o_d, h_last = gdn.chunk_fwd(*[shard(x[kk], d) for kk in ("q", "k", "v", "g", "beta")],
+                                    h_in[:, d].reshape(w.B, w.Hv, 128, 128).contiguous(), chunk=C)
+        outs.append(o_d)
+    torch.cuda.synchronize()
+    o = torch.cat(outs, dim=1).float().cpu().numpy()
+    o_ref, h_ref = oracle.fwd(**{kk: _cpu(vv) for kk, vv in x.items()})
+    ro = _rms(o_ref)
+    _check("o", o, o_ref, 2e-2, ro)
+    _check("h_T (last shard)", h_last.cpu().numpy(), h_ref, 2e-2, ro)
+    _check("h_T (prefix)", h_fin.reshape(w.B, w.Hv, 128, 128).cpu().numpy(), h_ref, 2e-2, ro)
+    # negative control: shards started from zero states miss by far
+    o0 = torch.cat([gdn.chunk_fwd(*[shard(x[kk], d) for kk in ("q", "k", "v", "g", "beta")], None, chunk=C)[0]
+                    for d in range(S)], dim=1).float().cpu().numpy()
+    assert _err(o0, o_ref) > 10 * 2e-2 * ro
+
+
 def test_long_sequence_reduced(gdn):
     # the long-sequence workload's shape and group structure at 1/16 of its length
     w = WORKLOADS["long_256k"].replace(T=16384, n_groups=16)
