@@ -589,6 +589,58 @@ def test_varlen_paired_form(gdn):
         a += n
 
 
+def _graph_replays_equal(fn, outs, refs, n=3):
+    # capture fn (which writes into the tensors `outs`) in a HIP graph after
+    # one warm-up call on a side stream, then replay it n times with eager
+    # work (the outputs cleared by a fill kernel) and synchronisations in
+    # between; every replay must give `refs` bit for bit
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fn()
+    for r in range(n):
+        for t in outs:
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for t, ref in zip(outs, refs):
+            assert torch.equal(t, ref), f"replay {r}"
+
+
+@pytest.mark.parametrize("ng", [0, 4])
+def test_graph_replay_equals_eager(gdn, ng):
+    # the forward recorded in a HIP graph (no allocation, copy or memset inside
+    # the library) and replayed gives the eager call's outputs, bit for bit
+    w = WORKLOADS["qwen3next_8b_layer"].replace(T=2048)
+    x = make_inputs(w, device="cuda", seed=51)
+    args = (x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"])
+    o_ref, h_ref = gdn.chunk_fwd(*args, chunk=128, n_groups=ng)
+    shape = gdn.make_shape(w.B, w.T, w.Hqk, w.Hv, 128, 128, 128, ng, x["k"].dtype, torch.float32)
+    ws = torch.empty(gdn.workspace_size(shape), dtype=torch.uint8, device="cuda")
+    o, hT = torch.empty_like(o_ref), torch.empty_like(h_ref)
+    _graph_replays_equal(lambda: gdn.chunk_fwd(*args, chunk=128, n_groups=ng, workspace=ws, out=o, final_state=hT),
+                         (o, hT), (o_ref, h_ref))
+
+
+def test_graph_replay_equals_eager_packed(gdn):
+    # packed sequences: the chunk tables are built on the device inside the graph
+    lens = [5, 300, 0, 129, 1000]
+    x, h0, cu = _packed(gdn, "bf16", 128, lens, 2, 4, 0.05, seed=52)
+    args = (x["q"], x["k"], x["v"], x["g"], x["beta"], cu, h0)
+    o_ref, h_ref = gdn.chunk_fwd_varlen(*args, chunk=128)
+    shape = gdn.make_shape(len(lens), sum(lens), 2, 4, 128, 128, 128, 0, torch.bfloat16, torch.float32)
+    ws = torch.empty(gdn.workspace_size_varlen(shape), dtype=torch.uint8, device="cuda")
+    o, hT = torch.empty_like(o_ref), torch.empty_like(h_ref)
+    _graph_replays_equal(lambda: gdn.chunk_fwd_varlen(*args, chunk=128, workspace=ws, out=o, final_state=hT),
+                         (o, hT), (o_ref, h_ref))
+
+
 @pytest.mark.parametrize("name", ["long_256k", "million_1m"])
 def test_long_sequence_full_size_sampled(gdn, name):
     # full length, in the benchmark's launch configuration; the oracle walks
