@@ -15,10 +15,13 @@ Two halves:
   pair (A, B) and the chunk output.  These give the values each hot-path step
   must reproduce and, run end to end, an independent evaluation of the rule
   used to pin the per-token oracle.
+* ``backward.py``: the gradient of the per-token rule with respect to q, k,
+  v, g, beta and h0 (reverse-mode differentiation written out token by
+  token, numpy fp64), the reference for a backward pass.
 
 Parity status: every function here is pinned by a CPU test against closed
-forms, invariants or an independent algorithm (tests/test_oracle_*.py); none
-is "parity unpinned".
+forms, invariants, finite differences or an independent algorithm
+(tests/test_oracle_*.py); none is "parity unpinned".
 """
 from __future__ import annotations
 
