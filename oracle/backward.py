@@ -127,3 +127,15 @@ def bwd(q, k, v, g, beta, h0=None, do=None, dhT=None):
         dq[:, :, hm[hv]] += dqh[:, :, hv]
         dkk[:, :, hm[hv]] += dkh[:, :, hv]
     return dict(dq=dq, dk=dkk, dv=dvv, dg=dg, dbeta=db, dh0=dS)
+
+
+def ut_inverse_grad(T, dT):
+    """Cotangent of the strict-lower S for T = (I + S)^-1, given T and the
+    cotangent dT: dS = -(T^T dT T^T) restricted to the strict lower triangle
+    (S has no other free entries).  This is the analytic backward of the
+    triangular inverse that "Fuse the Gated Delta Net inter-chunk scan into a
+    Pallas TPU kernel" (section "Changes", triangular-inversion item) states;
+    it follows from d(X^-1) = -X^-1 dX X^-1 with X = I + S."""
+    T = np.asarray(T, np.float64)
+    dT = np.asarray(dT, np.float64)
+    return -np.tril(T.T @ dT @ T.T, -1)

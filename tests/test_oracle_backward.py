@@ -2,7 +2,8 @@
 
 oracle/backward.py differentiates the per-token rule by hand; these tests tie
 it to the forward (central finite differences), to exact identities of the
-rule, and to the closed form of a special case.
+rule, and to the closed form of a special case; and the triangular inverse's
+analytic backward to central differences of the inverse itself.
 """
 import numpy as np
 import pytest
@@ -34,7 +35,6 @@ def _loss(x, do, dhT):
 def test_forward_matches_the_c_oracle(oracle_lib):
     # the forward that the gradients differentiate is the rule of gdn_oracle.c
     x, _, _ = _inputs(B=2, T=33, Hqk=2, Hv=4, dk=8, dv=6, seed=1)
-    S, o = bw.states(**x)
     xf = {kk: vv.astype(np.float32) for kk, vv in x.items()}
     xd = {kk: vv.astype(np.float64) for kk, vv in xf.items()}   # the same rounded inputs in fp64
     S, o = bw.states(**xd)
@@ -105,3 +105,31 @@ def test_zero_cotangents_give_zero_gradients():
     x, do, dhT = _inputs(seed=5)
     gr = bw.bwd(**x)
     assert all(np.abs(vv).max() == 0 for vv in gr.values())
+
+
+@pytest.mark.parametrize("C", [8, 32])
+def test_ut_inverse_grad_matches_central_differences(C):
+    # the analytic backward of the triangular inverse against central
+    # differences of the forward-substitution inverse, entry by entry over the
+    # strict lower triangle (the only free entries of S)
+    from oracle import chunked
+
+    rs = np.random.default_rng(C)
+    k = rs.standard_normal((C, 6))
+    k /= np.linalg.norm(k, axis=1, keepdims=True)
+    beta = 1 / (1 + np.exp(-rs.standard_normal(C)))
+    G = np.cumsum(np.log(1 / (1 + np.exp(-(rs.standard_normal(C) + 3)))))
+    S = chunked.gated_strict_kkt(k, beta, G)
+    dT = rs.standard_normal((C, C))
+    T = chunked.ut_inverse(S)
+    dS = bw.ut_inverse_grad(T, dT)
+    eps = 1e-6
+    fd = np.zeros_like(S)
+    for i in range(C):
+        for j in range(i):
+            Sp, Sm = S.copy(), S.copy()
+            Sp[i, j] += eps
+            Sm[i, j] -= eps
+            fd[i, j] = np.sum((chunked.ut_inverse(Sp) - chunked.ut_inverse(Sm)) * dT) / (2 * eps)
+    assert np.abs(np.triu(dS)).max() == 0
+    assert np.abs(fd - dS).max() <= 1e-7 * max(1.0, np.abs(fd).max())
