@@ -133,3 +133,40 @@ def test_ut_inverse_grad_matches_central_differences(C):
             fd[i, j] = np.sum((chunked.ut_inverse(Sp) - chunked.ut_inverse(Sm)) * dT) / (2 * eps)
     assert np.abs(np.triu(dS)).max() == 0
     assert np.abs(fd - dS).max() <= 1e-7 * max(1.0, np.abs(fd).max())
+
+
+@pytest.mark.parametrize("C,T,Hqk,Hv,h0", [(1, 6, 1, 1, True), (4, 21, 1, 2, True), (16, 48, 2, 4, False),
+                                           (16, 37, 1, 3, True)])
+def test_chunked_backward_equals_per_token(C, T, Hqk, Hv, h0):
+    # two independent derivations of the same gradients: the per-token reverse
+    # pass and the chunked one (WY form, triangular inverse and its analytic
+    # backward, reverse walk over chunks; a shorter last chunk when C does not
+    # divide T)
+    x, do, dhT = _inputs(B=2, T=T, Hqk=Hqk, Hv=Hv, dk=6, dv=5, seed=C + T, h0=h0)
+    a = bw.bwd(**x, do=do, dhT=dhT)
+    c = bw.chunked_bwd(**x, do=do, dhT=dhT, C=C)
+    for kk in a:
+        assert np.abs(a[kk] - c[kk]).max() <= 1e-12 * max(1.0, np.abs(a[kk]).max()), kk
+
+
+def test_reverse_walk_is_the_transposed_chunk_map():
+    # the cotangent of each chunk's incoming state is A_n^T (that of its
+    # outgoing state) + a term that depends on the chunk's own outputs only,
+    # A_n the chunk's state map e^{G_last} I - K_g^T W
+    from oracle import chunked
+
+    C = 8
+    x, do, dhT = _inputs(B=1, T=5 * C, Hqk=1, Hv=1, dk=6, dv=5, seed=3)
+    _, walk, par = bw.chunked_bwd(**x, do=do, dhT=dhT, C=C, return_walk=True)
+    nxt = dhT[0, 0]
+    for n in range(4, -1, -1):
+        s = slice(n * C, (n + 1) * C)
+        G = chunked.decay_cumsum(x["g"][0, s, 0])
+        T = chunked.ut_inverse(chunked.gated_strict_kkt(x["k"][0, s, 0], x["beta"][0, s, 0], G))
+        W, U, Kg = chunked.wy(T, x["k"][0, s, 0], x["v"][0, s, 0], x["beta"][0, s, 0], G)
+        A, _ = chunked.chunk_affine(W, U, Kg, G)
+        np.testing.assert_allclose(walk[0, 0, n], A.T @ nxt + par[0, 0, n], rtol=0, atol=1e-12)
+        nxt = walk[0, 0, n]
+    # with no output cotangent the walk is the transposed maps alone
+    _, walk0, par0 = bw.chunked_bwd(**x, dhT=dhT, C=C, return_walk=True)
+    assert np.abs(par0).max() == 0
