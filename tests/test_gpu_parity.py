@@ -569,6 +569,22 @@ def test_forward_paired_form(gdn, dtype, C, T, B, Hqk, Hv, h0):
     _check("h_T", h, h_ref, TOL[dtype], ro)
 
 
+@pytest.mark.parametrize("dtype,C,T,B,Hqk,Hv", [
+    ("bf16", 128, 3 * 128 - 7, 5, 19, 19),   # 95 walks: the latency form
+    ("bf16", 128, 3 * 128 - 7, 3, 16, 32),   # 96 walks: the 4-slice throughput form
+    ("bf16", 64, 4 * 64 + 3, 4, 8, 24),      # 96 walks at C = 64, partial last chunk
+    ("f32", 64, 3 * 64, 5, 4, 20),           # 100 walks, fp32
+])
+def test_forward_walk_form_thresholds(gdn, dtype, C, T, B, Hqk, Hv):
+    # either side of the walk count at which the walk changes launch form
+    w = WORKLOADS["tiny"].replace(T=T, B=B, Hqk=Hqk, Hv=Hv, chunk=C, dtype=dtype, h0_std=0.05)
+    x = make_inputs(w, device="cuda", seed=B * Hv + C)
+    o, h, o_ref, h_ref = _run_and_compare(gdn, w, x)
+    ro = _rms(o_ref)
+    _check("o", o, o_ref, TOL[dtype], ro)
+    _check("h_T", h, h_ref, TOL[dtype], ro)
+
+
 def test_varlen_paired_form(gdn):
     # 3 sequences x 16 value heads = 48 walks (the paired form), one of them
     # empty and one a single token, against the oracle per sequence
