@@ -127,20 +127,21 @@ template <int C, typename TI, int MODE, int KIND>
 gdn_status launch_walk(const FwdArgs &a, const Lx &x) {
   const int width = KIND == FOLD ? 2 * D : D;
   // Launch form by the number of walks (units), measured:
-  //  * many (walk: 96 or more; fold: 256 or more): the throughput form, one
+  //  * many (walk: 65 or more; fold: 256 or more): the throughput form, one
   //    wave per 16-column slice, the slices of a workgroup sharing each
   //    chunk's operands through LDS -- 4 slices per workgroup for the walk
-  //    (10-19% faster than 8 between 96 and 512 walks, and at 8192), 8 for
-  //    the fold (whose 4-slice form ran 40% slower);
+  //    (10-19% faster than 8 between 96 and 512 walks, and at 8192; 0-9%
+  //    faster than the latency form from 65 to 95), 8 for the fold (whose
+  //    4-slice form ran 40% slower);
   //  * 33..64 walks: two slices per workgroup, each split over waves by rows;
-  //  * fewer, and 65..95 walks: one slice per workgroup of 2 or 4 waves that
-  //    split its rows, so that a short walk spreads over the chip.
+  //  * fewer: one slice per workgroup of 2 or 4 waves that split its rows,
+  //    so that a short walk spreads over the chip.
   const long units = (long)a.B * a.Hv * a.jobs;
   constexpr int NWS = C >= 128 ? 4 : 2;   // waves per slice: whole k-blocks of V' rows each
   // (the walk always hands h and V' to the output stage; the throughput and
   // paired forms count on those stores)
   if (KIND == WALK && (!a.Hs || !a.Vn)) return GDN_ERR_NULL;
-  if (KIND == WALK && units >= 96) {
+  if (KIND == WALK && units >= 65) {
     launch(walk_shared_kernel<C, TI, MODE, KIND, 4>, dim3((unsigned)(units * (width / 64))), dim3(256), x, a);
   } else if (KIND == FOLD && units * (width / 128) >= 512) {
     launch(walk_shared_kernel<C, TI, MODE, KIND, 8>, dim3((unsigned)(units * (width / 128))), dim3(512), x, a);
