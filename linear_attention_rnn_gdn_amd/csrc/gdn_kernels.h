@@ -17,20 +17,23 @@
 // Kernels:
 //   prep_kernel    one workgroup (8 waves) per (chunk, value head, batch):
 //                  G, S, T, W, U, and K^T for the walk
-//   walk_ring_kernel / walk_shared_kernel
-//                  the sequential chunk walk, one wave per 16-column slice of
-//                  the state, which stays in matrix-core result registers and
-//                  feeds the next product directly.  The ring form (one wave
-//                  per workgroup) streams W and K^T through registers, for
-//                  walks too few to fill the chip; the shared form (8 waves
-//                  per workgroup) copies them once per workgroup into LDS.
-//                  Modes: WALK (state = h, writes chunk-start states and V')
-//                  and FOLD (state = the augmented [A | B] of a group,
-//                  started from [I | 0]; writes the group's pair).
+//   walk_ring_kernel / walk_pair_kernel / walk_shared_kernel
+//                  the sequential chunk walk over 16-column slices of the
+//                  state, which stays in matrix-core result registers and
+//                  feeds the next product directly.  The ring form (one slice
+//                  per workgroup, its rows split over 2 or 4 waves) streams W
+//                  and K^T through registers, for walks too few to fill the
+//                  chip; the paired form (two such slices per workgroup)
+//                  shares one LDS copy of them; the shared form (4 or 8
+//                  slices per workgroup, one wave each) copies them once per
+//                  workgroup into LDS.  Modes: WALK (state = h, writes
+//                  chunk-start states and V') and FOLD (state = the augmented
+//                  [A | B] of a group, started from [I | 0]; writes the
+//                  group's pair).
 //   prefix_kernel  one workgroup per (column slice, bh): exclusive prefix of
 //                  the groups' affine pairs.
-//   out_kernel     one workgroup per (32-column slice, chunk, bh): the output,
-//                  with P^T kept in registers between its two products.
+//   out_kernel     one 4-wave workgroup per (chunk, bh): the output, with
+//                  P^T formed once per chunk into LDS between its products.
 //
 // Workspace tensors (cb = bh*N + n indexes a chunk of a value head).  The
 // tensors that pass from one kernel to the next are stored fragment-major: in
