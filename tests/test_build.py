@@ -1,6 +1,7 @@
 """Build checks that need no GPU: every kernel of the library compiles for
 gfx950 without register spills (scratch memory per lane), which would put
-per-lane memory traffic into the hot loops."""
+per-lane memory traffic into the hot loops, and within the 160 KB of LDS a
+workgroup may use (a larger one would fail only at launch)."""
 import os
 import re
 import shutil
@@ -24,3 +25,7 @@ def test_no_kernel_uses_scratch(tmp_path):
     assert names and len(names) == len(scratch)
     spilled = [(n, b) for n, b in zip(names, scratch) if b]
     assert not spilled, f"kernels using scratch: {spilled}"
+    lds = [int(x) for x in re.findall(r"LDS Size \[bytes/block\]: (\d+)", out.stderr)]
+    assert len(lds) == len(names)
+    big = [(n, b) for n, b in zip(names, lds) if b > 160 * 1024]
+    assert not big, f"kernels over 160 KB of LDS: {big}"
