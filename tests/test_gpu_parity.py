@@ -514,6 +514,29 @@ def test_varlen_many_short_sequences(gdn):
         _check(f"h_T[{s_}]", hT[s_:s_ + 1].cpu().numpy(), h_ref, 2e-2, ro)
 
 
+def test_varlen_throughput_form_with_empty_sequences(gdn):
+    # 24 sequences x 4 value heads = 96 walks (the 4-slice throughput form),
+    # a third of them empty: those return h0 as h_T untouched, the others
+    # match the oracle per sequence
+    lens = [0 if i % 3 == 1 else 1 + (37 * i) % 300 for i in range(24)]
+    x, h0, cu = _packed(gdn, "bf16", 128, lens, 2, 4, 0.05, seed=29)
+    o, hT = gdn.chunk_fwd_varlen(x["q"], x["k"], x["v"], x["g"], x["beta"], cu, h0, chunk=128)
+    torch.cuda.synchronize()
+    a = 0
+    for s_, n in enumerate(lens):
+        if n == 0:
+            assert torch.equal(hT[s_], h0[s_])
+            continue
+        sl = slice(a, a + n)
+        if s_ % 4 == 0:   # a sample against the oracle
+            o_ref, h_ref = oracle.fwd(*[x[kk][:, sl].cpu() for kk in ("q", "k", "v", "g", "beta")],
+                                      h0[s_:s_ + 1].cpu())
+            ro = _rms(o_ref)
+            _check(f"o[{s_}]", o[:, sl].float().cpu().numpy(), o_ref, 2e-2, ro)
+            _check(f"h_T[{s_}]", hT[s_:s_ + 1].cpu().numpy(), h_ref, 2e-2, ro)
+        a += n
+
+
 def test_varlen_bf16_output(gdn):
     # packed sequences with a bf16 o: the fp32-o call's values rounded once
     # (the output stage rounds its fp32 result), bit for bit
