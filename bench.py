@@ -6,12 +6,21 @@ inputs (decay cumsum, UT transform, WY pair, the sequential chunk walk or the
 chunk-group fold / prefix / replay, and the outputs), with inputs, outputs
 and workspace resident in HBM before the timed region starts.
 
-Prints ONE JSON line.  `value` is tokens/s (B*T per step).  `roofline` is for
-the kernel that takes the most time per step, timed live with HIP events on
-the stream the library launches on (torch's current stream), against the
-bytes that kernel must move at minimum; `path_roofline` relates the whole
-step to the method's own algorithmic bytes and FLOPs.  `cpu_baseline` times
-the fp64 oracle on this host's cores over a bounded sample of the workload.
+Timing: each of the K timed steps runs after a 512 MB write that evicts the
+memory-side cache (MALL, 256 MB), and is bracketed by its own HIP events on
+the stream the library launches on (torch's current stream); `ms_per_step` is
+the median.  The same K steps run back to back (cache warm) are reported as
+`warm`.
+
+Prints ONE JSON line.  `value` is tokens/s (B*T per step).  `roofline`
+relates the whole step to the method's own algorithmic HBM bytes (inputs read
+once, o and h_T written once; the long path's fold re-read, pairs and
+incoming states), with `traffic` the HBM bytes per step that the rocprofv3
+counters measured for the same kernels (when taken on the current sources);
+`dominant_kernel` gives the longest kernel against the bytes this design
+makes it move.  `cpu_baseline` times the fp64 oracle on this host's cores
+over a bounded sample of the workload (and on one thread for the small
+workloads).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -96,9 +105,10 @@ def kernel_source_sha():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload, kernel):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel sources; else None."""
+def measured_traffic(workload, kernels):
+    """HBM bytes per step of `kernels` (one launch each) from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel sources
+    and covers every kernel; else None."""
     p = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     try:
         d = json.load(open(p))
@@ -106,8 +116,11 @@ def measured_traffic(workload, kernel):
         return None
     if d.get("kernel_source_sha") != kernel_source_sha():
         return None
-    e = d.get("workloads", {}).get(workload, {}).get(kernel)
-    return None if e is None else e.get("bytes_per_launch")
+    per = d.get("workloads", {}).get(workload, {})
+    try:
+        return sum(per[k]["bytes_per_launch"] for k in kernels)
+    except (KeyError, TypeError):
+        return None
 
 
 def _stage_of(kernel_name):
@@ -192,38 +205,46 @@ def summarize_pmc(fetch_dir, write_dir, workload, copy_bytes):
     print(json.dumps(d, indent=1))
 
 
-def cpu_baseline(w, x, budget_s=15.0):
+def cpu_baseline(w, x, budget_s=15.0, one_thread=False):
     """Time the fp64 oracle (as it stands) on this host over a bounded sample:
-    the first T_s tokens of every head of the workload."""
+    the first T_s tokens of every head of the workload, on all host cores
+    (and, if `one_thread`, also on one thread over a shorter sample)."""
     import oracle
 
     nthreads = oracle.default_threads()
-    cpu = {kk: (None if vv is None else vv) for kk, vv in x.items()}
+    cpu = {kk: (None if vv is None else vv.cpu()) for kk, vv in x.items()}
 
-    def run(T_s):
-        sub = {kk: (vv[:, :T_s].cpu() if kk not in ("h0",) else (None if vv is None else vv.cpu()))
-               for kk, vv in cpu.items()}
+    def run(T_s, nt):
+        sub = {kk: (vv[:, :T_s].contiguous() if kk != "h0" else vv) for kk, vv in cpu.items()}
         t0 = time.perf_counter()
-        oracle.fwd(**sub, nthreads=nthreads)
+        oracle.fwd(**sub, nthreads=nt)
         return time.perf_counter() - t0
 
-    T_s = min(w.T, 256)
-    dt = run(T_s)
-    est_full = dt * w.T / T_s
-    if est_full <= 2 * budget_s:
-        T_s = w.T
-    else:
-        T_s = max(256, min(w.T, int(T_s * budget_s / max(dt, 1e-6)) // 256 * 256))
-    # repeat short samples until about 5 s of CPU work for a steady figure
-    reps, total = 0, 0.0
-    while reps == 0 or (total < 5.0 and reps < 50):
-        total += run(T_s)
-        reps += 1
-    dt = total / reps
-    return {"value": w.B * T_s / dt, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
-            "sample": f"first {T_s} of {w.T} tokens x batch {w.B}, all {w.Hv} value heads, "
-                      f"all {w.dv} state columns; fp64 per-token rule in C, {nthreads} threads; "
-                      f"mean of {reps} runs, {dt:.2f} s each"}
+    def measure(nt, budget):
+        T_s = min(w.T, 256)
+        dt = run(T_s, nt)
+        if dt * w.T / T_s <= 2 * budget:
+            T_s = w.T
+        else:
+            T_s = max(min(w.T, 256), min(w.T, int(T_s * budget / max(dt, 1e-6)) // 256 * 256))
+        # repeat short samples until about 5 s of CPU work for a steady figure
+        reps, total = 0, 0.0
+        while reps == 0 or (total < 5.0 and reps < 50):
+            total += run(T_s, nt)
+            reps += 1
+        return T_s, total / reps, reps
+
+    T_s, dt, reps = measure(nthreads, budget_s)
+    out = {"value": w.B * T_s / dt, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+           "sample": f"first {T_s} of {w.T} tokens x batch {w.B}, all {w.Hv} value heads, "
+                     f"all {w.dv} state columns; fp64 per-token rule in C, {nthreads} threads; "
+                     f"mean of {reps} runs, {dt:.2f} s each"}
+    if one_thread:
+        T1, dt1, reps1 = measure(1, budget_s / 3)
+        out["one_thread"] = {"value": w.B * T1 / dt1, "unit": "tokens/s", "cores": 1,
+                             "sample": f"first {T1} of {w.T} tokens x batch {w.B}, all heads and "
+                                       f"columns; mean of {reps1} runs, {dt1:.2f} s each"}
+    return out
 
 
 def ramp_clocks(fn, seconds=0.5):
@@ -239,13 +260,30 @@ def ramp_clocks(fn, seconds=0.5):
         torch.cuda.synchronize()
 
 
+FLUSH_BYTES = 512 << 20   # twice the 256 MB memory-side cache (MALL)
+
+
 def time_steps(fn, steps, warmup):
+    """K steps, each after a 512 MB write that evicts the memory-side cache
+    and timed alone with HIP events on the current stream (median: `cold`),
+    then the same K steps back to back (mean: `warm`).  Returns ms per step."""
+    import statistics
+
     import torch
 
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
     ramp_clocks(fn)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        flush.fill_(float(i))
+        ev[i][0].record()
+        fn()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    cold = statistics.median(a.elapsed_time(b) for a, b in ev)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -253,7 +291,8 @@ def time_steps(fn, steps, warmup):
         fn()
     e1.record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
+    del flush
+    return {"cold": cold, "warm": e0.elapsed_time(e1) / steps}
 
 
 def main():
@@ -265,6 +304,8 @@ def main():
     ap.add_argument("--secondary", default="long_256k",
                     help="second workload timed for context ('' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--n-groups", type=int, default=None,
+                    help="override the workload's chunk-group count (0 = one sequential walk)")
     ap.add_argument("--packed", default="packed_8b_mix",
                     help="packed variable-length workload reported beside the headline ('' = none)")
     ap.add_argument("--profile-run", action="store_true",
@@ -304,6 +345,8 @@ def main():
         return x, step
 
     w = WORKLOADS[args.workload]
+    if args.n_groups is not None:
+        w = w.replace(n_groups=args.n_groups)
     if args.profile_run:
         a = torch.empty(copy_bytes // 4, dtype=torch.float32, device="cuda")
         b = torch.empty_like(a)
@@ -313,76 +356,23 @@ def main():
         torch.cuda.synchronize()
         del a, b
     x, step = setup(w)
-    ms = time_steps(step, args.steps, args.warmup)
+    tm = time_steps(step, args.steps, args.warmup)
     if args.profile_run:
-        print(json.dumps({"profile_run": w.name, "ms_per_step": ms}), flush=True)
+        print(json.dumps({"profile_run": w.name, "ms_per_step": tm}), flush=True)
         return
-
-    # per-kernel times: the same steps again, each kernel launched with a pair
-    # of HIP events that record its own start and end on the launch stream
-    # (gdn_chunk_fwd_timed), all steps queued back to back; the first dropped
-    names = [n for n in ("prep", "fold", "prefix", "walk", "out")
-             if (w.n_groups > 1 or n not in ("fold", "prefix"))]
-    bit = {n: stage_bits[n].bit_length() - 1 for n in names}
-    nst = args.steps + 1
-    ev = [[[None] * 5, [None] * 5] for _ in range(nst)]
-    for k in range(nst):
-        for n in names:
-            for side in (0, 1):
-                e = torch.cuda.Event(enable_timing=True)
-                e.record()   # creates the event
-                ev[k][side][bit[n]] = e
-    torch.cuda.synchronize()
-    for k in range(nst):
-        step(events=(ev[k][0], ev[k][1]))
-    torch.cuda.synchronize()
-    stage_ms = {n: sum(ev[k][0][bit[n]].elapsed_time(ev[k][1][bit[n]]) for k in range(1, nst)) / args.steps
-                for n in names}
-
-    flops, nbytes = algorithmic(w)
-    sb = stage_bytes(w)
-    dom = max(stage_ms, key=stage_ms.get)
-    dom_s = stage_ms[dom] * 1e-3
-    achieved = sb[dom] / dom_s
-    traffic = measured_traffic(w.name, dom)
-    roof = {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK, "traffic": traffic, "kernel": dom,
-            "bytes_per_launch": sb[dom], "avg_launch_ms": stage_ms[dom]}
-    t = ms * 1e-3
-    path = {"flops": flops, "bytes": nbytes, "hbm_frac": nbytes / t / HBM_PEAK,
-            "mfma_frac": flops / t / BF16_PEAK}
-    line = {
-        "metric": METRIC,
-        "value": w.tokens / t,
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": w.dtype,
-        "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "T": w.T, "H_qk": w.Hqk, "H_v": w.Hv,
-                   "d_k": w.dk, "d_v": w.dv, "chunk": w.chunk, "n_groups": w.n_groups,
-                   "o_dtype": "f32", "parallelism": "single GPU"},
-        "mfma_util_pct": 100.0 * flops / t / BF16_PEAK,
-        "roofline": roof,
-        "path_roofline": path,
-        "stages_ms": stage_ms,
-    }
+    line = measure(w, step, tm, args.steps, args.warmup, stage_bits, torch)
     if args.secondary and args.secondary != w.name:
         del x, step
         torch.cuda.empty_cache()
         w2 = WORKLOADS[args.secondary]
         x2, step2 = setup(w2)
-        ms2 = time_steps(step2, max(2, args.steps // 4), 1)
-        f2, b2 = algorithmic(w2)
-        line["secondary"] = {"workload": w2.name, "value": w2.tokens / (ms2 * 1e-3),
-                             "unit": "tokens/s", "ms_per_step": ms2,
-                             "mfma_util_pct": 100.0 * f2 / (ms2 * 1e-3) / BF16_PEAK,
-                             "hbm_frac": b2 / (ms2 * 1e-3) / HBM_PEAK}
+        tm2 = time_steps(step2, max(3, args.steps // 4), 1)
+        sec = measure(w2, step2, tm2, max(3, args.steps // 4), 1, stage_bits, torch)
+        line["secondary"] = {kk: sec[kk] for kk in ("value", "unit", "ms_per_step", "warm", "roofline",
+                                                    "mfma_util_pct", "stages_ms", "dominant_kernel")}
+        line["secondary"]["workload"] = w2.name
+        if not args.no_cpu_baseline:
+            line["secondary"]["cpu_baseline"] = cpu_baseline(w2, x2)
         del x2, step2
         torch.cuda.empty_cache()
         x = make_inputs(w, device="cuda")
@@ -402,15 +392,88 @@ def main():
         def step_p(stages=None, events=None):
             gdn.chunk_fwd_varlen(xp["q"], xp["k"], xp["v"], xp["g"], xp["beta"], cu, xp["h0"],
                                  chunk=wp.chunk, workspace=wsp, out=op, final_state=hp)
-        msp = time_steps(step_p, max(5, args.steps // 4), 2)
+        tmp = time_steps(step_p, max(5, args.steps // 4), 2)
         line["packed"] = {"workload": args.packed, "sequences": len(cu) - 1, "tokens": wp.T,
-                          "value": wp.T / (msp * 1e-3), "unit": "tokens/s", "ms_per_step": msp}
+                          "value": wp.T / (tmp["cold"] * 1e-3), "unit": "tokens/s",
+                          "ms_per_step": tmp["cold"], "warm_ms_per_step": tmp["warm"]}
         del xp, op, hp, wsp
         torch.cuda.empty_cache()
         x = make_inputs(w, device="cuda")
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, x)
+        line["cpu_baseline"] = cpu_baseline(w, x, one_thread=w.name in SMALL)
     print(json.dumps(line), flush=True)
+
+
+SMALL = ("tiny", "qwen3next_8b_layer", "dense_d4096_layer")   # 1-thread oracle times too
+
+
+def stage_times(w, step, steps, stage_bits, torch):
+    """Per-kernel times: the steps again, each kernel launched with a pair of
+    HIP events that record its own start and end on the launch stream
+    (gdn_chunk_fwd_timed), all steps queued back to back, the first dropped."""
+    names = [n for n in ("prep", "fold", "prefix", "walk", "out")
+             if (w.n_groups > 1 or n not in ("fold", "prefix"))]
+    bit = {n: stage_bits[n].bit_length() - 1 for n in names}
+    nst = steps + 1
+    ev = [[[None] * 5, [None] * 5] for _ in range(nst)]
+    for k in range(nst):
+        for n in names:
+            for side in (0, 1):
+                e = torch.cuda.Event(enable_timing=True)
+                e.record()   # creates the event
+                ev[k][side][bit[n]] = e
+    torch.cuda.synchronize()
+    for k in range(nst):
+        step(events=(ev[k][0], ev[k][1]))
+    torch.cuda.synchronize()
+    return {n: sum(ev[k][0][bit[n]].elapsed_time(ev[k][1][bit[n]]) for k in range(1, nst)) / steps
+            for n in names}
+
+
+def measure(w, step, tm, steps, warmup, stage_bits, torch):
+    stage_ms = stage_times(w, step, steps, stage_bits, torch)
+    flops, nbytes = algorithmic(w)
+    t = tm["cold"] * 1e-3
+    achieved = nbytes / t
+    traffic = measured_traffic(w.name, list(stage_ms))
+    # the whole step against the method's own bytes (HBM binds at every bf16
+    # workload: its FLOP per byte is below the bf16 ridge of ~315)
+    roof = {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK, "traffic": traffic,
+            "traffic_ratio": None if traffic is None else traffic / nbytes,
+            "scope": "whole step (all kernels of one gdn_chunk_fwd call)",
+            "algorithmic_bytes": nbytes, "step_ms": tm["cold"],
+            "kernels_ms_sum": sum(stage_ms.values())}
+    sb = stage_bytes(w)
+    dom = max(stage_ms, key=stage_ms.get)
+    dom_s = stage_ms[dom] * 1e-3
+    dominant = {"kernel": dom, "avg_launch_ms": stage_ms[dom], "design_bytes_per_launch": sb[dom],
+                "design_bytes_frac": sb[dom] / dom_s / HBM_PEAK,
+                "algorithmic_bytes_frac": nbytes / dom_s / HBM_PEAK}
+    return {
+        "metric": METRIC,
+        "value": w.tokens / t,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": tm["cold"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "H_qk": w.Hqk, "H_v": w.Hv,
+                   "d_k": w.dk, "d_v": w.dv, "chunk": w.chunk, "n_groups": w.n_groups,
+                   "o_dtype": "f32", "parallelism": "single GPU"},
+        "warm": {"ms_per_step": tm["warm"], "value": w.tokens / (tm["warm"] * 1e-3),
+                 "hbm_frac": nbytes / (tm["warm"] * 1e-3) / HBM_PEAK},
+        "mfma_util_pct": 100.0 * flops / t / BF16_PEAK,
+        "roofline": roof,
+        "algorithmic": {"flops": flops, "bytes": nbytes, "mfma_frac": flops / t / BF16_PEAK},
+        "stages_ms": stage_ms,
+        "dominant_kernel": dominant,
+    }
 
 
 if __name__ == "__main__":

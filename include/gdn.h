@@ -111,9 +111,12 @@ gdn_status gdn_chunk_fwd(const gdn_shape *shape, const void *q, const void *k, c
  * checks are those of gdn_chunk_fwd.
  *   PREP    intra-chunk transform (decay cumsum, UT inverse, W, U)
  *   FOLD    per-group affine pairs            (n_groups > 1 only)
- *   PREFIX  exclusive prefix over the groups  (n_groups > 1 only; writes h_T)
- *   WALK    sequential chunk walk: the whole sequence (writes h_T), or every
- *           group from its incoming state (n_groups > 1)
+ *   PREFIX  exclusive prefix over the groups  (n_groups > 1 only; writes h_T,
+ *           the composition of every group's pair applied to h0, when WALK
+ *           is not among the stages)
+ *   WALK    sequential chunk walk: the whole sequence, or every group from
+ *           its incoming state (n_groups > 1); writes h_T, the end state of
+ *           the walk (of the last group's replay)
  *   OUT     chunk outputs o                                                  */
 #define GDN_STAGE_PREP 1
 #define GDN_STAGE_FOLD 2

@@ -208,12 +208,16 @@ gdn_status run_fwd(const gdn_shape &s, int stages, const void *q, const void *k,
     f.pairA = reinterpret_cast<float *>(ws + L.A);
     f.pairB = reinterpret_cast<float *>(ws + L.Bp);
     if (stages & GDN_STAGE_FOLD) GDN_TRY((launch_walk<C, TI, MODE, FOLD>(f, lx(1))));
+    // h_T: the end state of the last group's replay; the prefix's composition
+    // of all pairs (the same state up to rounding) when the replay is not
+    // among the stages
     float *h_in = reinterpret_cast<float *>(ws + L.Hin);
     if (stages & GDN_STAGE_PREFIX)
-      GDN_TRY(launch_prefix(s.B * s.H_v, J, f.pairA, f.pairB, h0, h_in, h_T, MODE == MODE_BF16, lx(2)));
+      GDN_TRY(launch_prefix(s.B * s.H_v, J, f.pairA, f.pairB, h0, h_in, (stages & GDN_STAGE_WALK) ? nullptr : h_T,
+                            MODE == MODE_BF16, lx(2)));
     FwdArgs r = a;
     r.jobs = J; r.cpj = a.N / J;
-    r.init = h_in; r.init_per_job = 1; r.fin = nullptr;
+    r.init = h_in; r.init_per_job = 1; r.fin = h_T;
     if (stages & GDN_STAGE_WALK) GDN_TRY((launch_walk<C, TI, MODE, WALK>(r, lx(3))));
   }
   if (!(stages & GDN_STAGE_OUT)) return GDN_OK;
@@ -497,3 +501,4 @@ gdn_status gdn_chunk_transform(const gdn_shape *s, const void *k, const void *v,
 }
 
 }  // extern "C"
+

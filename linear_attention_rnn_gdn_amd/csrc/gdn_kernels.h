@@ -160,7 +160,7 @@ struct FwdArgs {
   float *Hs, *Vn;                 // walk outputs (optional) / out inputs
   const float *init;              // walk: initial states (h0 [BH,D,D] or h_in [BH,J,D,D]) or null
   int init_per_job;               // init indexed by job (replay) instead of bh only
-  float *fin;                     // walk: final state per bh (h_T) when jobs == 1, or null
+  float *fin;                     // walk: final state per bh (h_T), written by the last job, or null
   float *pairA, *pairB;           // fold outputs [BH,J,D,D]
   int jobs, cpj;                  // walk/fold: jobs per bh, chunks per job
   int n0, nn;                     // chunk range [n0, n0 + nn) of this launch (prep, out, single walk)
@@ -859,7 +859,7 @@ __global__ __launch_bounds__(64 * WPG) void walk_shared_kernel(FwdArgs a) {
     if (KIND == FOLD) {
       if (c0 < D) dst = a.pairA + (bh * a.jobs + job) * D * D;
       else { dst = a.pairB + (bh * a.jobs + job) * D * D; dcol = c0 - D; }
-    } else if (a.fin) {
+    } else if (a.fin && job == a.jobs - 1) {   // (the last group's end state)
       dst = a.fin + bh * D * D;
     }
     if (dst) {
@@ -1117,7 +1117,7 @@ __global__ __launch_bounds__(64 * NWS) void walk_ring_kernel(FwdArgs a) {
     if (KIND == FOLD) {
       if (c0 < D) dst = a.pairA + (bh * a.jobs + job) * D * D;
       else { dst = a.pairB + (bh * a.jobs + job) * D * D; dcol = c0 - D; }
-    } else if (a.fin) {
+    } else if (a.fin && job == a.jobs - 1) {   // (the last group's end state)
       dst = a.fin + bh * D * D;
     }
     if (dst) {
@@ -1353,7 +1353,7 @@ __global__ __launch_bounds__(128 * NWS) void walk_pair_kernel(FwdArgs a) {
     }
   }
   auto store_final = [&]() {
-    if (a.fin) {
+    if (a.fin && job == a.jobs - 1) {   // (the last group's end state)
 #pragma unroll
       for (int t = 0; t < MHW; ++t)
 #pragma unroll

@@ -23,9 +23,10 @@
  *                     h -> A h + B that the group applies to the state: A is
  *                     the ordered product of the per-token maps
  *                     exp(g_t)(I - beta_t k_t k_t^T) (latest token on the
- *                     left), B is the state reached from h = 0.  Same pages:
- *                     "each device folds its local chunks into one (A, B)
- *                     pair".
+ *                     left), B is the state reached from h = 0: the per-group
+ *                     affine map of "GatedDeltaNet does not support
+ *                     ici_context_parallelism", section "The recurrence is
+ *                     affine, so it can be parallelized".
  *
  *  gdn_oracle_prefix  The exclusive prefix of a list of affine pairs applied
  *                     to an initial state: h_in[0] = h_init,

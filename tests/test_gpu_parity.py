@@ -359,6 +359,16 @@ def test_groups_weak_decay_compose_matters(gdn):
     ro = _rms(o_ref)
     _check("o", o, o_ref, 2e-2, ro)
     _check("h_T", h, h_ref, 2e-2, ro)
+    # h_T as the prefix composes it (all eight pairs applied to h0) equals the
+    # last group's replayed end state, which the full call returns
+    args = (x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"])
+    o_p = torch.empty((w.B, w.T, w.Hv, w.dv), dtype=torch.float32, device="cuda")
+    h_p = torch.empty((w.B, w.Hv, w.dk, w.dv), dtype=torch.float32, device="cuda")
+    gdn.chunk_fwd(*args, chunk=128, n_groups=8, out=o_p, final_state=h_p,
+                  stages=gdn.STAGE_PREP | gdn.STAGE_FOLD | gdn.STAGE_PREFIX)
+    torch.cuda.synchronize()
+    _check("h_T (prefix)", h_p.cpu().numpy(), h_ref, 2e-2, ro)
+    _check("h_T (prefix vs replay)", h_p.cpu().numpy(), h.astype(np.float64), 2e-2, ro)
     # negative control: groups replayed from a zero state miss by far
     L = 256
     bad = []
@@ -680,17 +690,80 @@ def test_graph_replay_equals_eager_packed(gdn):
                          (o, hT), (o_ref, h_ref))
 
 
+class _Stream:
+    """Running max-abs error and sum of squares of a reference, block by block."""
+
+    def __init__(self):
+        self.err, self.ss, self.n = 0.0, 0.0, 0
+
+    def add(self, got, ref):
+        self.err = max(self.err, _err(got, ref))
+        self.ss += float(np.sum(np.square(ref, dtype=np.float64)))
+        self.n += ref.size
+
+    @property
+    def rms(self):
+        return (self.ss / max(self.n, 1)) ** 0.5
+
+
+@pytest.mark.timeout(1500)
 @pytest.mark.parametrize("name", ["long_256k", "million_1m"])
-def test_long_sequence_full_size_sampled(gdn, name):
-    # full length, in the benchmark's launch configuration; the oracle walks
-    # the whole sequence for a sample of one value head and 16 state columns
+def test_long_sequence_full_size(gdn, name):
+    # Full length, in the benchmark's launch configuration (256 chunk-groups:
+    # fold, exclusive prefix, replay), every value head and state column
+    # against the oracle, streamed over blocks of heads.  The grouped result
+    # must also match one sequential walk over all chunks (the composition
+    # checked against a sequential single-device reference: "GatedDeltaNet
+    # does not support ici_context_parallelism", section "Status"), and the
+    # prefix's composition of all pairs must equal the last group's replayed
+    # end state.
     w = WORKLOADS[name]
     x = make_inputs(w, device="cuda")
-    hv = 5
-    o, h, o_ref, h_ref = _run_and_compare(gdn, w, x, heads=(hv, hv + 1), cols=(32, 48))
-    ro = _rms(o_ref)
-    _check("o", o, o_ref, 2e-2, ro)
-    _check("h_T", h, h_ref, 2e-2, ro)
-    # the same workload as one sequential walk agrees with the grouped result
-    del o, h
+    args = (x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"])
+    o_g, h_g = gdn.chunk_fwd(*args, chunk=w.chunk, n_groups=w.n_groups)
+    # the prefix's final state: the same call without the replay and output
+    h_p = torch.empty_like(h_g)
+    gdn.chunk_fwd(*args, chunk=w.chunk, n_groups=w.n_groups, out=o_g, final_state=h_p,
+                  stages=gdn.STAGE_PREP | gdn.STAGE_FOLD | gdn.STAGE_PREFIX)
+    torch.cuda.synchronize()
+    h_g_np, h_p_np = h_g.cpu().numpy(), h_p.cpu().numpy()
+    o_s, h_s = gdn.chunk_fwd(*args, chunk=w.chunk, n_groups=0)
+    torch.cuda.synchronize()
+    h_s_np = h_s.cpu().numpy()
+    xc = {kk: _cpu(vv) for kk, vv in x.items()}
+    del x, args
     torch.cuda.empty_cache()
+    rep = w.Hv // w.Hqk
+    blk = 4 if w.T <= 262144 else 2          # value heads per oracle block
+    st = {k_: _Stream() for k_ in ("o_g", "o_s", "o_gs", "h_g", "h_s", "h_gs", "h_p")}
+    for h0_ in range(0, w.Hv, blk):
+        h1_ = h0_ + blk
+        q0, q1 = h0_ // rep, (h1_ - 1) // rep + 1
+        sub = dict(q=xc["q"][:, :, q0:q1].contiguous(), k=xc["k"][:, :, q0:q1].contiguous(),
+                   v=xc["v"][:, :, q0 * rep:q1 * rep].contiguous(),
+                   g=xc["g"][:, :, q0 * rep:q1 * rep].contiguous(),
+                   beta=xc["beta"][:, :, q0 * rep:q1 * rep].contiguous(),
+                   h0=xc["h0"][:, q0 * rep:q1 * rep].contiguous() if xc["h0"] is not None else None)
+        o_ref, h_ref = oracle.fwd(**sub, heads=(h0_ - q0 * rep, h1_ - q0 * rep))
+        og = o_g[:, :, h0_:h1_].cpu().numpy()
+        os_ = o_s[:, :, h0_:h1_].cpu().numpy()
+        st["o_g"].add(og, o_ref)
+        st["o_s"].add(os_, o_ref)
+        st["o_gs"].add(og, os_.astype(np.float64))
+        del og, os_, o_ref
+        st["h_g"].add(h_g_np[:, h0_:h1_], h_ref)
+        st["h_s"].add(h_s_np[:, h0_:h1_], h_ref)
+        st["h_p"].add(h_p_np[:, h0_:h1_], h_ref)
+        st["h_gs"].add(h_g_np[:, h0_:h1_], h_s_np[:, h0_:h1_].astype(np.float64))
+        print(f"  heads {h0_}..{h1_ - 1}: o grouped {st['o_g'].err:.3e}, single {st['o_s'].err:.3e}",
+              flush=True)
+    ro, rh = st["o_g"].rms, st["h_g"].rms
+    tol = TOL[w.dtype]
+    for k_, r in (("o_g", ro), ("o_s", ro), ("o_gs", ro), ("h_g", min(rh, ro)), ("h_s", min(rh, ro)),
+                  ("h_p", min(rh, ro)), ("h_gs", min(rh, ro))):
+        print(f"  {k_}: max-abs {st[k_].err:.3e}  limit {tol * r:.3e}", flush=True)
+        assert st[k_].err <= tol * r, f"{k_}: {st[k_].err:.3e} > {tol * r:.3e}"
+    # the prefix's composition and the last group's replay: the same state
+    d = float(np.abs(h_p_np - h_g_np).max())
+    print(f"  prefix h_T vs replayed h_T: {d:.3e}", flush=True)
+    assert d <= tol * min(rh, ro)
