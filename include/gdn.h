@@ -207,6 +207,27 @@ gdn_status gdn_chunk_transform(const gdn_shape *shape, const void *k, const void
                                const float *g, const float *beta, float *G, float *Tm, float *W,
                                float *U, void *hip_stream);
 
+/* gdn_chunk_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Arguments, checks and results are those of gdn_chunk_fwd, without the
+ * workspace: the library's own static device array of
+ * GDN_NOALLOC_SCRATCH_BYTES bytes serves as the workspace.  Every GPU the
+ * library runs on holds that array until the process ends; its address is
+ * looked up on the first call on each device (the current device, which must
+ * be the stream's).  Nothing is allocated, freed or cleared.
+ *   Returns GDN_ERR_WORKSPACE, launching nothing, when the problem needs more
+ *   workspace than the array holds (gdn_workspace_size(shape) >
+ *   GDN_NOALLOC_SCRATCH_BYTES; e.g. 32 value heads x 4096 tokens at chunk 128
+ *   fit).
+ * All calls on one GPU share its array: two calls whose work may overlap on
+ * that GPU (different streams, or a graph replayed on one stream while
+ * another call runs on a second) race and give undefined results; calls
+ * ordered on one stream do not interact. */
+#define GDN_NOALLOC_SCRATCH_BYTES (256u << 20)
+gdn_status gdn_chunk_fwd_noalloc(const gdn_shape *shape, const void *q, const void *k,
+                                 const void *v, const float *g, const float *beta,
+                                 const float *h0, void *o, float *h_T, void *hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

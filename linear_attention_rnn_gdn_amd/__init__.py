@@ -46,7 +46,7 @@ _lib = None
 SYMBOLS = ("gdn_status_str", "gdn_validate", "gdn_workspace_size", "gdn_workspace_size_varlen",
            "gdn_chunk_fwd", "gdn_chunk_fwd_varlen",
            "gdn_chunk_fwd_stages", "gdn_chunk_fwd_timed", "gdn_chunk_fold", "gdn_compose_prefix",
-           "gdn_chunk_transform")
+           "gdn_chunk_transform", "gdn_chunk_fwd_noalloc")
 STAGE_PREP, STAGE_FOLD, STAGE_PREFIX, STAGE_WALK, STAGE_OUT, STAGE_ALL = 1, 2, 4, 8, 16, 31
 
 
@@ -82,6 +82,8 @@ def lib():
         L.gdn_compose_prefix.restype = I
         L.gdn_chunk_transform.argtypes = [SP] + [P] * 8 + [P]
         L.gdn_chunk_transform.restype = I
+        L.gdn_chunk_fwd_noalloc.argtypes = [SP] + [P] * 9
+        L.gdn_chunk_fwd_noalloc.restype = I
         _lib = L
     return _lib
 
@@ -189,6 +191,28 @@ def chunk_fwd(q, k, v, g, beta, h0=None, chunk=128, n_groups=0, o_dtype=torch.fl
         _check(lib().gdn_chunk_fwd_stages(ctypes.byref(shape), int(stages), *args),
                "gdn_chunk_fwd_stages")
     return o, hT
+
+
+NOALLOC_SCRATCH_BYTES = 256 << 20
+
+
+def chunk_fwd_noalloc(q, k, v, g, beta, h0, out, final_state=None, chunk=128, n_groups=0,
+                      stream=None):
+    """gdn_chunk_fwd_noalloc: the forward with the library's static device
+    scratch as its workspace (nothing is allocated by the library; the caller
+    passes the outputs).  out [B,T,H_v,d_v] (fp32 or bf16: the output dtype),
+    final_state [B,H_v,d_k,d_v] fp32 or None.  Returns (out, final_state)."""
+    B, T, Hqk, Hv, dk, dv, dev = _inputs(q, k, v, g, beta)
+    _need(out, "o", None, (B, T, Hv, dv), dev)
+    shape = make_shape(B, T, Hqk, Hv, dk, dv, chunk, n_groups, k.dtype, out.dtype)
+    if h0 is not None:
+        _need(h0, "h0", torch.float32, (B, Hv, dk, dv), dev)
+    if final_state is not None:
+        _need(final_state, "h_T", torch.float32, (B, Hv, dk, dv), dev)
+    _check(lib().gdn_chunk_fwd_noalloc(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                       _ptr(h0), _ptr(out), _ptr(final_state), _stream(stream)),
+           "gdn_chunk_fwd_noalloc")
+    return out, final_state
 
 
 def workspace_size_varlen(shape: GdnShape) -> int:

@@ -1,11 +1,14 @@
 // gdn_api.hip -- C ABI of the GDN chunked forward (declared in include/gdn.h).
 //
 // Host side only: argument checks, workspace carving and kernel launches on
-// the caller's stream.  No allocation, no synchronisation, no global state.
+// the caller's stream.  No allocation and no synchronisation; the only
+// global state is the per-device address of the no-allocation entry point's
+// static scratch array (looked up once per device).
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 
 #include "gdn.h"
 #include "gdn_kernels.h"
@@ -502,3 +505,50 @@ gdn_status gdn_chunk_transform(const gdn_shape *s, const void *k, const void *v,
 
 }  // extern "C"
 
+// ----------------------------------------------------------------------------
+// The forward for callers that cannot allocate device memory: its workspace
+// is `scratch`, a static device array that every GPU the library runs on
+// holds until the process ends.  Host code never passes the array's name to a
+// kernel (on the host it is only a stand-in for the symbol): the device
+// address comes from hipGetSymbolAddress, looked up once per device with that
+// device current and kept per device.
+namespace {
+
+constexpr size_t kScratchBytes = (size_t)GDN_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void *scratch_ptr[kMaxDevices] = {};
+
+// device address of the current device's copy of `scratch`
+gdn_status scratch_of_current_device(void **ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GDN_ERR_HIP;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return GDN_ERR_HIP;
+    scratch_ptr[dev] = p;
+  }
+  *ptr = scratch_ptr[dev];
+  return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" gdn_status gdn_chunk_fwd_noalloc(const gdn_shape *s, const void *q, const void *k, const void *v,
+                                            const float *g, const float *beta, const float *h0, void *o,
+                                            float *h_T, void *hip_stream) {
+  GDN_TRY(gdn_validate(s));
+  if (layout(*s).total > kScratchBytes) return GDN_ERR_WORKSPACE;
+  if (s->T > 0) {
+    if (!q || !k || !v || !g || !beta || !o) return GDN_ERR_NULL;
+    for (const void *p : {(const void *)q, (const void *)k, (const void *)v, (const void *)g,
+                          (const void *)beta, (const void *)h0, (const void *)o, (const void *)h_T})
+      if (misaligned(p)) return GDN_ERR_ALIGN;
+  }
+  void *ws = nullptr;
+  GDN_TRY(scratch_of_current_device(&ws));
+  return gdn_chunk_fwd(s, q, k, v, g, beta, h0, o, h_T, ws, kScratchBytes, hip_stream);
+}
