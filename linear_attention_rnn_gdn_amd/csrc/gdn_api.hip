@@ -33,9 +33,28 @@ int chunks_of(const gdn_shape &s) { return (int)(((int64_t)s.T + s.chunk - 1) / 
 // their chunks, at most T / C + s.B of them, are numbered across sequences.
 int varlen_nmax(const gdn_shape &s) { return (int)((int64_t)s.T / s.chunk + s.B); }
 
+// The walk that forms the outputs itself (walk_out_kernel) takes every
+// padded-batch walk (or replay of chunk-groups) of at least this many walks:
+// measured at chunk 128, bf16, 128 to 512 walks of 16 to 64 chunks and the
+// 262,144-token replay (8192 walks), it runs 7-14% faster than the walk
+// and the separate output stage; at 64 walks (two workgroups per walk cover
+// half the compute units) 25% slower.  Fewer walks keep the walk forms that
+// spread each walk over more of the chip, and the output stage.
+#ifndef GDN_FUSED_MIN_WALKS
+#define GDN_FUSED_MIN_WALKS 128
+#endif
+#ifndef GDN_FUSED_WPG
+#define GDN_FUSED_WPG 4
+#endif
+constexpr int kFusedWpg = GDN_FUSED_WPG;   // slices (waves) per workgroup of walk_out_kernel
+bool fused_walk(const gdn_shape &s) {
+  return (int64_t)s.B * s.H_v * groups_of(s) >= GDN_FUSED_MIN_WALKS;
+}
+
 // Workspace of `rows` sequence rows of N chunks each (plus, for `nseq` packed
-// sequences, their chunk tables).
-Layout layout_n(const gdn_shape &s, size_t rows, size_t N, size_t nseq) {
+// sequences, their chunk tables); `handoff`: room for the chunk-start states
+// and corrected values that the walk hands to a separate output stage.
+Layout layout_n(const gdn_shape &s, size_t rows, size_t N, size_t nseq, bool handoff = true) {
   const size_t BH = rows * s.H_v, C = s.chunk;
   const size_t J = groups_of(s);
   const size_t in_bytes = s.dtype == GDN_BF16 ? 2 : 4;
@@ -45,8 +64,10 @@ Layout layout_n(const gdn_shape &s, size_t rows, size_t N, size_t nseq) {
   L.W = off;  off += align_up(BH * N * C * D * in_bytes);
   L.Kt = off; off += align_up(rows * s.H_qk * N * C * D * in_bytes);   // per key head
   L.U = off;  off += align_up(BH * N * C * D * 4);
-  L.Hs = off; off += align_up(BH * N * D * D * 4);   // fp32, or bf16 hi + lo planes
-  L.Vn = off; off += align_up(BH * N * C * D * 4);
+  if (handoff) {
+    L.Hs = off; off += align_up(BH * N * D * D * 4);   // fp32, or bf16 hi + lo planes
+    L.Vn = off; off += align_up(BH * N * C * D * 4);
+  }
   if (J > 1) {
     L.A = off;   off += align_up(BH * J * D * D * 4);
     L.Bp = off;  off += align_up(BH * J * D * D * 4);
@@ -60,7 +81,7 @@ Layout layout_n(const gdn_shape &s, size_t rows, size_t N, size_t nseq) {
   L.total = off;
   return L;
 }
-Layout layout(const gdn_shape &s) { return layout_n(s, s.B, chunks_of(s), 0); }
+Layout layout(const gdn_shape &s) { return layout_n(s, s.B, chunks_of(s), 0, !fused_walk(s)); }
 Layout layout_varlen(const gdn_shape &s) { return layout_n(s, 1, varlen_nmax(s), s.B); }
 
 bool misaligned(const void *p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u); }
@@ -168,6 +189,17 @@ gdn_status launch_out(const FwdArgs &a, const Lx &x, bool rag = false) {
   return check_launch();
 }
 
+template <int C, typename TI, int MODE, typename TO>
+gdn_status launch_walk_out(const FwdArgs &a, const Lx &x) {
+  constexpr int NG = (D / 16) / kFusedWpg;   // workgroups per walk
+  const long units = (long)a.B * a.Hv * a.jobs;
+  if (a.T % C)
+    launch(walk_out_kernel<C, TI, MODE, TO, kFusedWpg, true>, dim3((unsigned)(units * NG)), dim3(64 * kFusedWpg), x, a);
+  else
+    launch(walk_out_kernel<C, TI, MODE, TO, kFusedWpg, false>, dim3((unsigned)(units * NG)), dim3(64 * kFusedWpg), x, a);
+  return check_launch();
+}
+
 gdn_status launch_prefix(int BH, int n, const float *A, const float *Bm, const float *h_init, float *h_in,
                          float *h_final, bool split, const Lx &x) {
   PrefixArgs p{BH, n, A, Bm, h_init, h_in, h_final};
@@ -192,19 +224,28 @@ gdn_status run_fwd(const gdn_shape &s, int stages, const void *q, const void *k,
     return x;
   };
   const Layout L = layout(s);
+  const bool fused = fused_walk(s);
   FwdArgs a = base_args(s);
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.o = o;
   a.G = reinterpret_cast<float *>(ws + L.G);
   a.W = ws + L.W;
   a.Kt = ws + L.Kt;
   a.U = reinterpret_cast<float *>(ws + L.U);
-  a.Hs = reinterpret_cast<float *>(ws + L.Hs);
-  a.Vn = reinterpret_cast<float *>(ws + L.Vn);
+  if (!fused) {
+    a.Hs = reinterpret_cast<float *>(ws + L.Hs);
+    a.Vn = reinterpret_cast<float *>(ws + L.Vn);
+  }
+  // the walk: with its outputs (fused), or handing h and V' to the output stage
+  auto walk = [&](const FwdArgs &w) -> gdn_status {
+    if (!fused) return launch_walk<C, TI, MODE, WALK>(w, lx(3));
+    if (s.o_dtype == GDN_F32) return launch_walk_out<C, TI, MODE, float>(w, lx(3));
+    return launch_walk_out<C, TI, MODE, __bf16>(w, lx(3));
+  };
   const int J = groups_of(s);
   if (stages & GDN_STAGE_PREP) GDN_TRY((launch_prep<C, TI, MODE>(a, lx(0))));
   if (J == 1) {
     a.init = h0; a.init_per_job = 0; a.fin = h_T;
-    if (stages & GDN_STAGE_WALK) GDN_TRY((launch_walk<C, TI, MODE, WALK>(a, lx(3))));
+    if (stages & GDN_STAGE_WALK) GDN_TRY(walk(a));
   } else {
     FwdArgs f = a;
     f.jobs = J; f.cpj = a.N / J;
@@ -221,9 +262,17 @@ gdn_status run_fwd(const gdn_shape &s, int stages, const void *q, const void *k,
     FwdArgs r = a;
     r.jobs = J; r.cpj = a.N / J;
     r.init = h_in; r.init_per_job = 1; r.fin = h_T;
-    if (stages & GDN_STAGE_WALK) GDN_TRY((launch_walk<C, TI, MODE, WALK>(r, lx(3))));
+    if (stages & GDN_STAGE_WALK) GDN_TRY(walk(r));
   }
   if (!(stages & GDN_STAGE_OUT)) return GDN_OK;
+  if (fused) {
+    // the walk wrote o: the output stage has no kernel (its timing events,
+    // if any, bound an empty interval)
+    const Lx x = lx(4);
+    if (x.e0 && hipEventRecord(x.e0, st) != hipSuccess) return GDN_ERR_HIP;
+    if (x.e1 && hipEventRecord(x.e1, st) != hipSuccess) return GDN_ERR_HIP;
+    return GDN_OK;
+  }
   if (s.o_dtype == GDN_F32) return launch_out<C, TI, MODE, float>(a, lx(4));
   return launch_out<C, TI, MODE, __bf16>(a, lx(4));
 }

@@ -1935,6 +1935,477 @@ __global__ __launch_bounds__(NT, 2) void out_kernel(FwdArgs a) {
 }
 
 // ----------------------------------------------------------------------------
+// walk with outputs (rows a5, a6 and a9 in one kernel): the sequential chunk
+// walk of walk_shared_kernel that also forms each chunk's outputs from the
+// chunk-start state and corrected values it holds in registers, so neither
+// goes to memory.  Per chunk, each wave (one 16-column slice c0.. of the
+// state):
+//   V' = U - W h                                   (W from LDS, h as B operand)
+//   P^T = (K Q^T) o Gamma^T o [i <= r]              (shared: the workgroup's
+//                                                    waves split its tiles)
+//   O^T[c][r] = e^{G_r} (h^T Q^T)[c][r] + (V'^T P^T)[c][r]   for c in the slice
+//   h <- e^{G_last} h + K^T (d o V')
+// The chunk-start state and V' are A operands of the output products as they
+// stand in registers: two stacked result tiles give lane group g the
+// k-values kk(g, j) of a block of 32, the k order in which the query and key
+// rows are read (and in which P^T's tiles are formed).
+//
+// LDS holds one chunk's operands in four slots -- W fragments, K^T
+// fragments, the Q tile, and the K tile, which the P^T fragments replace once
+// formed -- plus G; each slot is refilled for the next chunk (global_load_lds,
+// no registers) as soon as every wave is past its last read of it:
+//   W  after V',  K^T after the state update,  Q, K and G after the outputs.
+// Each refill thus has two of the chunk's phases to land.  The waits before
+// the barriers count the copies, U loads and o stores each wave issued after
+// the ones waited for (the memory counter completes in issue order).
+template <int C, typename TI> struct WalkOutLds {
+  using OL = OutLds<C, TI>;
+  static constexpr int BPF = 8 * (int)sizeof(TI) / 16;            // 1 KB blocks per fragment
+  static constexpr int FW = (C / 16) * (D / 32), FK = (D / 16) * (C / 32);
+  static constexpr int WB = FW * BPF * 1024, KTB = FK * BPF * 1024;  // W, K^T fragment bytes
+  static constexpr int QB = OL::KB;                                 // Q (or K) tile bytes
+  static constexpr int PB = OL::NPAIR * 2048;                       // P^T fragment bytes
+  static constexpr int PKB = PB > QB ? PB : QB;                     // the K tile, then P^T
+};
+
+// s_waitcnt immediate: vmcnt(n) lgkmcnt(0)
+__host__ __device__ constexpr int vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4); }
+// wait (s_waitcnt IMM), then the workgroup barrier; no memory access moves
+// across it
+template <int IMM>
+__device__ __forceinline__ void wait_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(IMM);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int C, typename TI, int MODE, typename TO, int WPG, bool RAG>
+__global__ __launch_bounds__(64 * WPG) void walk_out_kernel(FwdArgs a) {
+  using PR = Prec<MODE>;
+  using PKw = PolicyKinds<PR::wh>;      // W x h
+  using PKk = PolicyKinds<PR::kv>;      // K^T x (d o V')
+  using PKq = PolicyKinds<PR::exact>;   // K x Q^T
+  using PKh = PolicyKinds<PR::hq>;      // h^T x Q^T
+  using PKv = PolicyKinds<PR::pv>;      // V'^T x P^T
+  using L = WalkOutLds<C, TI>;
+  using OL = OutLds<C, TI>;
+  constexpr bool F32 = sizeof(TI) == 4;
+  static_assert(PKw::a == (F32 ? F_F32 : F_BF16) && PKk::a == PKw::a, "W and K^T fragments are used as stored");
+  static_assert(PKq::a == PKq::b && PKq::b == PKh::b, "one query fragment serves both products");
+  static_assert(PKw::b == PKh::a || (PKw::b == F_BF16 && PKh::a == F_SPLIT), "W h takes the state split for h^T Q^T");
+  constexpr int MV = C / 16, MH = D / 16, KBW = D / 32, KBK = C / 32, R = C / 16;
+  constexpr int NG = (D / 16) / WPG;   // workgroups per walk
+  constexpr int BPF = L::BPF;
+  // per wave and chunk: 1 KB copies of W, K^T, Q (and K); U loads; o stores
+  constexpr int NCW = L::WB / 1024 / WPG, NCK = L::KTB / 1024 / WPG, NCQ = L::QB / 1024 / WPG;
+  static_assert(L::WB % (1024 * WPG) == 0 && L::KTB % (1024 * WPG) == 0 && L::QB % (1024 * WPG) == 0,
+                "copies shared out evenly");
+  constexpr int GL = C / 4 / WPG;   // lanes of each wave copying 16 bytes of G
+  static_assert(GL >= 1 && GL * 4 * WPG == C, "G copies shared out evenly");
+  constexpr int NU = MV;
+  // o stores counted as issued: none in the partial-chunk instantiation,
+  // where a store may be skipped
+  constexpr int NST = RAG ? 0 : R;
+  constexpr int RU = R / (2 * WPG) > 0 ? 2 : 1;   // query tiles per wave in forming P^T
+  static_assert(WPG == 4 && R == 4 * RU, "P^T: query tiles {w, R-1-w} (R = 8) or {w} (R = 4) per wave");
+  // one array per slot (the compiler then tells the LDS reads of one slot
+  // from the copies into another, and waits for neither at the reads)
+  __shared__ __align__(16) char sW[L::WB];
+  __shared__ __align__(16) char sKt[L::KTB];
+  __shared__ __align__(16) char sQ[L::QB];
+  __shared__ __align__(16) char sPK[L::PKB];
+  __shared__ __align__(16) float sG[C];
+
+  int unit, grp;
+  xcd_unit(blockIdx.x, NG, a.B * a.Hv * a.jobs, unit, grp);
+  const int job = unit % a.jobs;
+  const size_t bh = (size_t)(unit / a.jobs);
+  const int b = (int)(bh / a.Hv), hv = (int)(bh % a.Hv), hq = hv / (a.Hv / a.Hqk);
+  const int lane = threadIdx.x & 63, lr = lane & 15, g = lane >> 4, lq = 4 * g;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int slice = grp * WPG + wv, c0 = 16 * slice;
+  const int nfirst = a.n0 + job * a.cpj;   // first chunk of this walk in its sequence row
+  const int cpj = a.cpj;
+  const size_t cb0 = uniform64(bh * a.N + nfirst);
+  const long long ktoff = (long long)uniform64((unsigned long long)kt_offset(a, bh));
+
+  // state tiles: h[m] holds rows 16m + 4g + i, column c0 + lr
+  f32x4 h[MH];
+#pragma unroll
+  for (int m = 0; m < MH; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int kr = 16 * m + 4 * g + i;
+      float x = 0.f;
+      if (a.init) {
+        const float *src = a.init_per_job ? a.init + (bh * a.jobs + job) * D * D : a.init + bh * D * D;
+        x = src[(size_t)kr * D + c0 + lr];
+      }
+      h[m][i] = x;
+    }
+  auto store_final = [&]() {
+    if (a.fin && job == a.jobs - 1) {   // (the last group's end state)
+#pragma unroll
+      for (int m = 0; m < MH; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a.fin[bh * D * D + (size_t)(16 * m + 4 * g + i) * D + c0 + lr] = h[m][i];
+    }
+  };
+  if (cpj == 0) {
+    store_final();
+    return;
+  }
+
+  // LDS destinations of the copies as plain numbers (so that the compiler
+  // does not tie the LDS reads to the copies and wait for all of them), and
+  // re-derived at each use through an empty asm statement: hoisted out of the
+  // chunk loop, the 33 copy destinations and their global bases would hold as
+  // many scalar registers for the whole walk
+  auto lds_addr = [](const void *p) {
+    unsigned x = (unsigned)(size_t)(__attribute__((address_space(3))) const char *)p;
+    asm volatile("" : "+s"(x));
+    return x;
+  };
+  // copies: a wave-uniform 64-bit base (scalar registers) plus a 32-bit
+  // per-lane offset
+  auto dma = [&](const char *ubase, unsigned voff, unsigned ldst) {
+    __builtin_amdgcn_global_load_lds((const void *)(ubase + voff), (__attribute__((address_space(3))) void *)(size_t)ldst,
+                                     16, 0, 0);
+  };
+  auto ubase = [](const void *p, size_t off) -> const char * {
+    return reinterpret_cast<const char *>(uniform64(reinterpret_cast<unsigned long long>(p) + off));
+  };
+  const unsigned fl = lane * 16 * BPF;   // this lane's bytes within a fragment
+  // fragment-major tensors: LDS block j = half j % BPF of fragment j / BPF
+  auto copy_frags = [&](const char *src, char *slot, int ncopies) {
+    const unsigned ls = lds_addr(slot);
+    for (int jj = 0; jj < ncopies; ++jj) {   // (not unrolled: one base at a time)
+      const int j = jj * WPG + wv;
+      dma(ubase(src, (size_t)(j / BPF) * 1024 * BPF + (j % BPF) * 16), fl, ls + j * 1024);
+    }
+  };
+  auto copy_w = [&](size_t cb) { copy_frags(reinterpret_cast<const char *>(a.W) + cb * C * D * sizeof(TI), sW, NCW); };
+  auto copy_kt = [&](size_t cb) {
+    copy_frags(reinterpret_cast<const char *>(a.Kt) + (cb + ktoff) * D * C * sizeof(TI), sKt, NCK);
+  };
+  // a C x D tile of q or k (query/key head hq) in the swizzled row-major
+  // layout of OutLds: piece c of row r at piece position c ^ (r mod 16).  Rows
+  // past the chunk's real tokens repeat its last one (finite values that meet
+  // zero rows of V' and write no output).  LDS block j holds pieces 64j ..
+  // 64j + 63: rows RB j .. RB j + RB - 1 (RB = 64 / RP).
+  constexpr int RB = 64 / OL::RP;
+  const size_t rowb = (size_t)a.Hqk * D * sizeof(TI);   // bytes between tokens
+  auto copy_rows = [&](const void *src, size_t tok0, int rows, char *slot) {
+    const unsigned ls = lds_addr(slot);
+    const char *base = reinterpret_cast<const char *>(src) + (tok0 * a.Hqk + hq) * D * sizeof(TI);
+    for (int jj = 0; jj < NCQ; ++jj) {
+      const int j = jj * WPG + wv, r = RB * j + lane / OL::RP, c = (lane % OL::RP) ^ (r & 15);
+      const int rr = !RAG ? r : (r < rows ? r : rows - 1);
+      dma(ubase(base, 0), (unsigned)(rr * rowb + c * 16), ls + j * 1024);
+    }
+  };
+  auto copy_g = [&](size_t cb) {
+    if (lane < GL) dma(ubase(a.G, (cb * C + wv * GL * 4) * sizeof(float)), lane * 16, lds_addr(sG) + wv * GL * 16);
+  };
+  auto chunk_tokens = [&](int cc, size_t &tok0, int &rows) {
+    const size_t n = (size_t)nfirst + cc;
+    tok0 = (size_t)b * a.T + n * C;
+    rows = !RAG ? C : (int)((size_t)a.T - n * C < (size_t)C ? (size_t)a.T - n * C : (size_t)C);
+  };
+  auto copy_qkg = [&](int cc) {
+    size_t tok0;
+    int rows;
+    chunk_tokens(cc, tok0, rows);
+    copy_rows(a.q, tok0, rows, sQ);
+    copy_rows(a.k, tok0, rows, sPK);
+    copy_g(cb0 + cc);
+  };
+  float4 u[MV];
+  auto fetch_u = [&](size_t cb) {
+#pragma unroll
+    for (int m = 0; m < MV; ++m)
+      u[m] = *reinterpret_cast<const float4 *>(a.U + ((cb * MV + m) * (D / 16) + slice) * 256 + lane * 4);
+  };
+  // operand fragment p of the W or K^T slot
+  auto frag = [&](const char *slot, int p) -> Frag<PKw::a> {
+    Frag<PKw::a> f;
+    const char *base = slot + p * BPF * 1024 + lane * 16;
+    if constexpr (F32) {
+      const float4 x0 = *reinterpret_cast<const float4 *>(base);
+      const float4 x1 = *reinterpret_cast<const float4 *>(base + 1024);
+      f.v[0] = x0.x; f.v[1] = x0.y; f.v[2] = x0.z; f.v[3] = x0.w;
+      f.v[4] = x1.x; f.v[5] = x1.y; f.v[6] = x1.z; f.v[7] = x1.w;
+    } else {
+      f.hi = *reinterpret_cast<const bf16x8 *>(base);
+    }
+    return f;
+  };
+  // this lane's byte offsets of its row fragment halves within a 16-row tile
+  // of Q or K: row lr, k-values 32kb + 16hh + 4g .. +3 (piece c at c ^ lr)
+  int koff[KBW][2];
+#pragma unroll
+  for (int kb = 0; kb < KBW; ++kb)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int k = 32 * kb + 16 * hh + 4 * g;
+      const int c = k * (int)sizeof(TI) / 16, off = (k * (int)sizeof(TI)) % 16;
+      koff[kb][hh] = lr * OL::RP * 16 + ((c ^ lr) * 16) + off;
+    }
+  using QF = Frag<PKq::b>;
+  auto row_frag = [&](const char *slot, int tile, int kb) -> QF {
+    const char *t = slot + tile * 16 * OL::RP * 16;
+    QF f;
+    if constexpr (!F32 && PKq::b == F_BF16) {
+      const uint2 w0 = *reinterpret_cast<const uint2 *>(t + koff[kb][0]);
+      const uint2 w1 = *reinterpret_cast<const uint2 *>(t + koff[kb][1]);
+      f.hi = __builtin_bit_cast(bf16x8, uint4{w0.x, w0.y, w1.x, w1.y});
+    } else {
+      static_assert(F32 && PKq::b == F_F32, "fp32 rows feed the fp32 matrix cores");
+      const float4 x0 = *reinterpret_cast<const float4 *>(t + koff[kb][0]);
+      const float4 x1 = *reinterpret_cast<const float4 *>(t + koff[kb][1]);
+      f.v[0] = x0.x; f.v[1] = x0.y; f.v[2] = x0.z; f.v[3] = x0.w;
+      f.v[4] = x1.x; f.v[5] = x1.y; f.v[6] = x1.z; f.v[7] = x1.w;
+    }
+    return f;
+  };
+  const float *Gs = sG;
+  TO *og = reinterpret_cast<TO *>(a.o);
+
+  // the first chunk's operands
+  copy_w(cb0);
+  copy_kt(cb0);
+  copy_qkg(0);
+  fetch_u(cb0);
+  wait_barrier<vm_lgkm0(0)>();
+
+  for (int cc = 0; cc < cpj; ++cc) {
+    const size_t cb = cb0 + cc;
+    const bool more = cc + 1 < cpj;
+    size_t tok0;
+    int rows;
+    chunk_tokens(cc, tok0, rows);
+
+    // ---- V' = U - W h.  W fragments are read one output tile ahead.
+    Frag<PKw::b> hb[KBW];
+#pragma unroll
+    for (int kb = 0; kb < KBW; ++kb) {
+      const float x[8] = {h[2 * kb][0], h[2 * kb][1], h[2 * kb][2], h[2 * kb][3],
+                          h[2 * kb + 1][0], h[2 * kb + 1][1], h[2 * kb + 1][2], h[2 * kb + 1][3]};
+      hb[kb] = make_frag<PKw::b>(x);
+    }
+    f32x4 vps[MV];
+    {
+      Frag<PKw::a> fa[2][KBW];
+#pragma unroll
+      for (int kb = 0; kb < KBW; ++kb) fa[0][kb] = frag(sW, kb);
+#pragma unroll
+      for (int m = 0; m < MV; ++m) {
+        if (m + 1 < MV) {
+#pragma unroll
+          for (int kb = 0; kb < KBW; ++kb) fa[(m + 1) & 1][kb] = frag(sW, (m + 1) * KBW + kb);
+        }
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kb = 0; kb < KBW; ++kb) mma(acc, fa[m & 1][kb], hb[kb]);
+        vps[m] = f32x4{u[m].x - acc[0], u[m].y - acc[1], u[m].z - acc[2], u[m].w - acc[3]};
+      }
+    }
+    // every wave past W; this chunk's Q, K and G landed (the K^T copies,
+    // issued after them, may still be in flight)
+    wait_barrier<vm_lgkm0(NCK)>();
+    if (more) copy_w(cb + 1);
+
+    // ---- P^T = (K Q^T) o Gamma^T o [i <= r]: wave w forms the pairs (query
+    //      tile rt, key tiles 2kp and 2kp + 1) of its query tiles {w, R-1-w}
+    //      (equal shares of the triangle); only the pairs on the diagonal are
+    //      masked
+    Frag<PKv::b> pt[RU][R / 2];
+#pragma unroll
+    for (int uu = 0; uu < RU; ++uu) {
+      // (opaque each chunk: the masks and decays derived from it are formed
+      // where used instead of being hoisted out of the chunk loop, where they
+      // would hold scalar registers for the whole walk)
+      int rt = uu == 0 ? wv : R - 1 - wv;
+      asm volatile("" : "+s"(rt));
+      QF qf[KBW];
+#pragma unroll
+      for (int kb = 0; kb < KBW; ++kb) qf[kb] = row_frag(sQ, rt, kb);
+      const int r = 16 * rt + lr;
+      const float Gr = Gs[r] * LOG2E;
+#pragma unroll
+      for (int kp = 0; kp < R / 2; ++kp) {
+        if (2 * kp > rt) continue;
+        QF k0[KBW], k1[KBW];
+#pragma unroll
+        for (int kb = 0; kb < KBW; ++kb) {
+          k0[kb] = row_frag(sPK, 2 * kp, kb);
+          k1[kb] = row_frag(sPK, 2 * kp + 1, kb);   // (past the diagonal: read, multiplied, masked)
+        }
+        f32x4 p0 = zero4(), p1 = zero4();
+#pragma unroll
+        for (int kb = 0; kb < KBW; ++kb) {
+          mma(p0, k0[kb], qf[kb]);
+          mma(p1, k1[kb], qf[kb]);
+        }
+        const float4 gk0 = *reinterpret_cast<const float4 *>(Gs + 32 * kp + lq);
+        const float4 gk1 = *reinterpret_cast<const float4 *>(Gs + 32 * kp + 16 + lq);
+        const float g0[4] = {gk0.x, gk0.y, gk0.z, gk0.w}, g1[4] = {gk1.x, gk1.y, gk1.z, gk1.w};
+        float b8[8];
+        if (2 * kp + 1 < rt) {   // both key tiles wholly before the query tile
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            b8[i] = p0[i] * exp2_fast(Gr - g0[i] * LOG2E);
+            b8[4 + i] = p1[i] * exp2_fast(Gr - g1[i] * LOG2E);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int k0i = 32 * kp + lq + i, k1i = k0i + 16;
+            b8[i] = k0i <= r ? p0[i] * exp2_fast(Gr - g0[i] * LOG2E) : 0.f;
+            b8[4 + i] = k1i <= r ? p1[i] * exp2_fast(Gr - g1[i] * LOG2E) : 0.f;
+          }
+        }
+        pt[uu][kp] = make_frag<PKv::b>(b8);
+      }
+    }
+    wait_barrier<vm_lgkm0(63)>();   // every wave past the K tile
+#pragma unroll
+    for (int uu = 0; uu < RU; ++uu) {
+      const int rt = uu == 0 ? wv : R - 1 - wv;
+#pragma unroll
+      for (int kp = 0; kp < R / 2; ++kp) {
+        if (2 * kp > rt) continue;
+        char *pf = sPK + (OL::pbase(rt) + kp) * 2048 + lane * 16;
+        if constexpr (PKv::b == F_SPLIT) {
+          *reinterpret_cast<bf16x8 *>(pf) = pt[uu][kp].hi;
+          *reinterpret_cast<bf16x8 *>(pf + 1024) = pt[uu][kp].lo;
+        } else {
+          *reinterpret_cast<float4 *>(pf) = float4{pt[uu][kp].v[0], pt[uu][kp].v[1], pt[uu][kp].v[2], pt[uu][kp].v[3]};
+          *reinterpret_cast<float4 *>(pf + 1024) = float4{pt[uu][kp].v[4], pt[uu][kp].v[5], pt[uu][kp].v[6], pt[uu][kp].v[7]};
+        }
+      }
+    }
+    wait_barrier<vm_lgkm0(63)>();   // P^T in place
+
+    // ---- outputs O^T = e^{G_r} h^T Q^T + V'^T P^T for this slice's columns:
+    //      first h^T Q^T for every query tile (query fragments one tile ahead),
+    //      then V'^T P^T pair by pair (P^T fragments one pair ahead)
+    f32x4 a1[R];
+    {
+      Frag<PKh::a> hT[KBW];   // the chunk-start state, split for this product
+#pragma unroll
+      for (int kb = 0; kb < KBW; ++kb) {
+        const float x[8] = {h[2 * kb][0], h[2 * kb][1], h[2 * kb][2], h[2 * kb][3],
+                            h[2 * kb + 1][0], h[2 * kb + 1][1], h[2 * kb + 1][2], h[2 * kb + 1][3]};
+        hT[kb] = make_frag<PKh::a>(x);
+      }
+      QF qf[2][KBW];
+#pragma unroll
+      for (int kb = 0; kb < KBW; ++kb) qf[0][kb] = row_frag(sQ, 0, kb);
+#pragma unroll
+      for (int rt = 0; rt < R; ++rt) {
+        if (rt + 1 < R) {
+#pragma unroll
+          for (int kb = 0; kb < KBW; ++kb) qf[(rt + 1) & 1][kb] = row_frag(sQ, rt + 1, kb);
+        }
+        a1[rt] = zero4();
+#pragma unroll
+        for (int kb = 0; kb < KBW; ++kb) mma(a1[rt], hT[kb], qf[rt & 1][kb]);
+      }
+    }
+    const float gl2 = Gs[C - 1] * LOG2E;
+    const float gl = exp2_fast(gl2);
+    Frag<PKk::b> vb[KBK];
+    {
+      Frag<PKv::a> vT[KBK];
+#pragma unroll
+      for (int kb = 0; kb < KBK; ++kb) {
+        float x[8], y[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int m = 2 * kb + j / 4, i = j % 4;
+          x[j] = vps[m][i];
+          y[j] = vps[m][i] * exp2_fast(gl2 - Gs[16 * m + lq + i] * LOG2E);
+        }
+        vT[kb] = make_frag<PKv::a>(x);
+        vb[kb] = make_frag<PKk::b>(y);
+      }
+      auto pfrag = [&](int p) -> Frag<PKv::b> {
+        const char *pf = sPK + p * 2048 + lane * 16;
+        Frag<PKv::b> bf;
+        if constexpr (PKv::b == F_SPLIT) {
+          bf.hi = *reinterpret_cast<const bf16x8 *>(pf);
+          bf.lo = *reinterpret_cast<const bf16x8 *>(pf + 1024);
+        } else {
+          const float4 x0 = *reinterpret_cast<const float4 *>(pf), x1 = *reinterpret_cast<const float4 *>(pf + 1024);
+          bf.v[0] = x0.x; bf.v[1] = x0.y; bf.v[2] = x0.z; bf.v[3] = x0.w;
+          bf.v[4] = x1.x; bf.v[5] = x1.y; bf.v[6] = x1.z; bf.v[7] = x1.w;
+        }
+        return bf;
+      };
+      // pairs in storage order: (rt, kp), kp <= rt / 2, p = pbase(rt) + kp
+      Frag<PKv::b> pf[2];
+      pf[0] = pfrag(0);
+#pragma unroll
+      for (int rt = 0; rt < R; ++rt) {
+        f32x4 a2 = zero4();
+#pragma unroll
+        for (int kp = 0; kp <= rt / 2; ++kp) {
+          const int p = OL::pbase(rt) + kp;
+          if (p + 1 < OL::NPAIR) pf[(p + 1) & 1] = pfrag(p + 1);
+          mma(a2, vT[kp], pf[p & 1]);
+        }
+        const int r = 16 * rt + lr;
+        const float er = exp2_fast(Gs[r] * LOG2E);
+        TO ov[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ov[i] = from_f32<TO>(er * a1[rt][i] + a2[i]);
+        TO *dst = og + ((tok0 + r) * a.Hv + hv) * D + c0 + lq;
+        if (!RAG || r < rows) {
+          if constexpr (sizeof(TO) == 4) st16_stream(dst, ov);
+          else st8_stream(dst, ov);
+        }
+      }
+    }
+    // every wave past Q, P^T and G; this chunk's K^T landed (the next chunk's
+    // W and this chunk's o stores, issued after it, may be in flight)
+    if (more) wait_barrier<vm_lgkm0(NCW + NST)>();
+    else wait_barrier<vm_lgkm0(NST)>();
+    if (more) {
+      copy_qkg(cc + 1);
+      fetch_u(cb + 1);
+    }
+
+    // ---- h <- e^{G_last} h + K^T (d o V'), K^T fragments one state tile ahead
+    {
+      Frag<PKw::a> fk[2][KBK];
+#pragma unroll
+      for (int kb = 0; kb < KBK; ++kb) fk[0][kb] = frag(sKt, kb);
+#pragma unroll
+      for (int m = 0; m < MH; ++m) {
+        if (m + 1 < MH) {
+#pragma unroll
+          for (int kb = 0; kb < KBK; ++kb) fk[(m + 1) & 1][kb] = frag(sKt, (m + 1) * KBK + kb);
+        }
+        f32x4 acc2 = zero4();
+#pragma unroll
+        for (int kb = 0; kb < KBK; ++kb) mma(acc2, fk[m & 1][kb], vb[kb]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) h[m][i] = gl * h[m][i] + acc2[i];
+      }
+    }
+    if (more) {
+      // every wave past K^T; the next chunk's W landed (this chunk's o
+      // stores and the next chunk's Q, K, G copies and U may be in flight)
+      wait_barrier<vm_lgkm0(NST + 2 * NCQ + 1 + NU)>();
+      copy_kt(cb + 1);
+    }
+  }
+  store_final();
+}
+
+// ----------------------------------------------------------------------------
 // packed variable-length sequences: the chunk tables.  Sequence s covers
 // tokens [cu[s], cu[s+1]) of the packed tensors (offsets clamped into
 // [0, T], a sequence ending no earlier than it starts) and is cut into

@@ -210,6 +210,25 @@ def test_bf16_output(gdn):
     _check("h_T", h, h_ref, 2e-2, ro)
 
 
+@pytest.mark.parametrize("dtype,C,B,Hqk,Hv,T", [("bf16", 128, 4, 16, 32, 1000), ("bf16", 64, 8, 8, 16, 64 * 5),
+                                                 ("f32", 64, 6, 8, 24, 64 * 4 - 9)])
+def test_walk_with_outputs_bf16_output(gdn, dtype, C, B, Hqk, Hv, T):
+    # 128 walks or more: the walk forms the outputs itself (walk_out_kernel).
+    # A bf16 o is the fp32-o call's
+    # values rounded once, bit for bit; the fp32 o within the bar
+    w = WORKLOADS["tiny"].replace(T=T, B=B, Hqk=Hqk, Hv=Hv, chunk=C, dtype=dtype, h0_std=0.05)
+    x = make_inputs(w, device="cuda", seed=B * Hv + T)
+    args = (x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"])
+    o32, h32 = gdn.chunk_fwd(*args, chunk=C)
+    o16, h16 = gdn.chunk_fwd(*args, chunk=C, o_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(o16, o32.to(torch.bfloat16)) and torch.equal(h16, h32)
+    o_ref, h_ref = oracle.fwd(**{kk: _cpu(vv) for kk, vv in x.items()})
+    ro = _rms(o_ref)
+    _check("o", o32.cpu().numpy(), o_ref, TOL[dtype], ro)
+    _check("h_T", h32.cpu().numpy(), h_ref, TOL[dtype], ro)
+
+
 def test_empty_sequence_returns_initial_state(gdn):
     w = WORKLOADS["tiny"].replace(T=0, dtype="bf16", chunk=128, h0_std=0.3)
     x = make_inputs(w, device="cuda", seed=5)
@@ -438,6 +457,8 @@ def test_long_sequence_reduced(gdn):
     ("bf16", 128, 128 * 9 + 1, 2, 4, 0.1, 0),     # a one-token last chunk
     ("bf16", 64, 63, 1, 2, 0.05, 0),              # shorter than one chunk
     ("bf16", 128, 4000, 2, 4, 0.02, 4),           # chunk-groups, the last one ragged
+    ("bf16", 128, 4000, 8, 16, 0.02, 4),          # the same replayed by the walk with outputs (128 walks)
+    ("bf16", 64, 64 * 9 + 5, 8, 16, 0.05, 5),     # C = 64, walk with outputs (160 walks), ragged
 ])
 def test_forward_ragged_tail(gdn, dtype, C, T, Hqk, Hv, h0, ng):
     # T not a multiple of the chunk: the last chunk is padded with identity
