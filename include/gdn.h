@@ -77,20 +77,34 @@ typedef struct {
   int32_t dtype, o_dtype;
 } gdn_shape;
 
-/* Human-readable name of a status code (static string). */
+/* Human-readable name of a status code (static string).  (A library
+ * convention: the pages define no error handling.) */
 const char *gdn_status_str(gdn_status s);
 
-/* Host-only check of a problem description; launches nothing. */
+/* Host-only check of a problem description; launches nothing.  The
+ * supported sizes are those above; the head dimension 128 and chunks of 64
+ * and 128 are the ones the pages' runs use ("Fuse the Gated Delta Net
+ * inter-chunk scan into a Pallas TPU kernel", section "Performance" and the
+ * discussion thread). */
 gdn_status gdn_validate(const gdn_shape *shape);
 
 /* Bytes of device workspace gdn_chunk_fwd / gdn_chunk_fold need for `shape`
+ * (a library convention; the pages define no workspace)
  * (written to *bytes).  The workspace holds per-chunk intermediates (decay
  * cumsums, W, U, chunk-start states, corrected values per value head; K^T
  * per query/key head) and, with groups, the (A, B) pairs and incoming
  * states.  It carries nothing between calls. */
 gdn_status gdn_workspace_size(const gdn_shape *shape, size_t *bytes);
 
-/* The whole chunked forward.
+/* The whole chunked forward: o and the final state h_T of the per-token rule
+ * above from the initial state h0, evaluated chunk by chunk (the scan that
+ * takes an initial state and returns the outputs and the final state: "Fuse
+ * the Gated Delta Net inter-chunk scan into a Pallas TPU kernel", sections
+ * "Changes" and "Tests"; the inter-chunk affine step: "Shard the
+ * GatedDeltaNet sequence under ici_context_parallelism", PR description;
+ * with n_groups > 1 the two-pass composition of "GatedDeltaNet does not
+ * support ici_context_parallelism", section "The recurrence is affine, so it
+ * can be parallelized").
  *   q, k  [B, T, H_qk, d_k]  dtype          v [B, T, H_v, d_v] dtype
  *   g     [B, T, H_v] fp32 per-token log decay (g <= 0 expected, not required)
  *   beta  [B, T, H_v] fp32
@@ -103,7 +117,26 @@ gdn_status gdn_chunk_fwd(const gdn_shape *shape, const void *q, const void *k, c
                          const float *g, const float *beta, const float *h0, void *o,
                          float *h_T, void *ws, size_t ws_bytes, void *hip_stream);
 
-/* The same computation issued one stage at a time, for timing each kernel.
+/* gdn_chunk_fwd that also writes the affine map of the whole sequence, in
+ * the same walk (the walk carries the augmented state [A | h] from [I | h0]):
+ *   A [B, H_v, d_k, d_k] fp32  = the product over the tokens (latest on the
+ *        left) of exp(g_t)(I - beta_t k_t k_t^T), so that h_T = A h0 + B with
+ *        B the state reached from a zero state (h_T itself when h0 = NULL).
+ * The optional third output of the scan ("Fuse the Gated Delta Net
+ * inter-chunk scan into a Pallas TPU kernel", discussion thread, on
+ * returning A beside the outputs and the final state) with which a sequence
+ * shard yields its pair for the composition of "Shard the GatedDeltaNet
+ * sequence under ici_context_parallelism" (PR description) without a
+ * separate pass.  shape->n_groups must be 0 or 1 (GDN_ERR_SHAPE otherwise);
+ * A must not be NULL.  Other arguments, checks and results as gdn_chunk_fwd
+ * (o and h_T are those of gdn_chunk_fwd, bit for bit). */
+gdn_status gdn_chunk_fwd_affine(const gdn_shape *shape, const void *q, const void *k,
+                                const void *v, const float *g, const float *beta,
+                                const float *h0, void *o, float *h_T, float *A, void *ws,
+                                size_t ws_bytes, void *hip_stream);
+
+/* The same computation issued one stage at a time, for timing each kernel
+ * (the stages are the steps of the chunked forward cited at gdn_chunk_fwd).
  * `stages` is a mask of GDN_STAGE_* bits; only the selected stages are
  * launched.  The stages communicate through `ws`, so issuing every stage in
  * increasing bit order on one stream with one workspace (one call per bit,
@@ -142,7 +175,9 @@ gdn_status gdn_chunk_fwd_timed(const gdn_shape *shape, int32_t stages, const voi
                                const float *h0, void *o, float *h_T, void *ws, size_t ws_bytes,
                                void *hip_stream, void *const *ev_start, void *const *ev_stop);
 
-/* The chunked forward over packed variable-length sequences.  shape->B
+/* The chunked forward over packed variable-length sequences: the forward of
+ * gdn_chunk_fwd (same pages) applied to each sequence with its own initial
+ * and final state; the packing itself is this library's.  shape->B
  * sequences are concatenated along one row of shape->T tokens: sequence s
  * holds tokens [cu_seqlens[s], cu_seqlens[s+1]), each with its own initial
  * and final state and no state passing between sequences.  Each sequence is
@@ -164,7 +199,11 @@ gdn_status gdn_chunk_fwd_varlen(const gdn_shape *shape, const int32_t *cu_seqlen
                                 const float *h0, void *o, float *h_T, void *ws, size_t ws_bytes,
                                 void *hip_stream);
 
-/* Per-group affine pairs of the chunk-group split (shape->n_groups >= 1
+/* Per-group affine pairs of the chunk-group split: each group's map
+ * h -> A h + Bm ("GatedDeltaNet does not support ici_context_parallelism",
+ * section "The recurrence is affine, so it can be parallelized"; "Shard the
+ * GatedDeltaNet sequence under ici_context_parallelism", PR description: one
+ * pair per device from a scan over its chunks) (shape->n_groups >= 1
  * groups of equal length; 0 is taken as 1).  For group j of value head h:
  *   A[b,h,j] = product over the group's tokens t (latest on the left) of
  *              exp(g_t)(I - beta_t k_t k_t^T)            [d_k, d_k] fp32
@@ -177,7 +216,12 @@ gdn_status gdn_chunk_fold(const gdn_shape *shape, const void *k, const void *v, 
                           void *hip_stream);
 
 /* Exclusive prefix of affine pairs applied to an initial state, per
- * (batch*head) row bh:
+ * (batch*head) row bh (the incoming-state routine of the code-review
+ * suggestion on "Shard the GatedDeltaNet sequence under
+ * ici_context_parallelism": the state entering each device and the final
+ * state; composition law (A2,B2) o (A1,B1) = (A2 A1, A2 B1 + B2) of
+ * "GatedDeltaNet does not support ici_context_parallelism", section "The
+ * recurrence is affine, so it can be parallelized"):
  *   h_in[bh,0] = h_init[bh];  h_in[bh,j+1] = A[bh,j] h_in[bh,j] + Bm[bh,j];
  *   h_final[bh] = A[bh,n-1] h_in[bh,n-1] + Bm[bh,n-1].
  *   A [batch_heads, n, d_k, d_k] fp32, Bm [batch_heads, n, d_k, d_v] fp32,
@@ -194,7 +238,11 @@ gdn_status gdn_compose_prefix(int32_t batch_heads, int32_t n, int32_t d_k, int32
 
 /* The intra-chunk transform alone (decay cumsum, gated strict-lower
  * beta K K^T, UT inversion by the doubling ladder, WY formation), for every
- * chunk of every value head.  N = ceil(T / chunk); the rows of a partial
+ * chunk of every value head ("Fuse the Gated Delta Net inter-chunk scan into
+ * a Pallas TPU kernel", section "Changes": the triangular inverse by the
+ * blockwise doubling ladder; the pages leave w, u and S undefined, and the
+ * forms below are the ones under which the affine step of the PR page equals
+ * the per-token rule).  N = ceil(T / chunk); the rows of a partial
  * last chunk past T are its identity padding (G repeats the last real
  * cumsum, T has unit rows, W and U zero rows).
  *   G  [B, H_v, N, C] fp32     G[r] = sum_{s<=r} g_s within the chunk

@@ -46,7 +46,7 @@ _lib = None
 SYMBOLS = ("gdn_status_str", "gdn_validate", "gdn_workspace_size", "gdn_workspace_size_varlen",
            "gdn_chunk_fwd", "gdn_chunk_fwd_varlen",
            "gdn_chunk_fwd_stages", "gdn_chunk_fwd_timed", "gdn_chunk_fold", "gdn_compose_prefix",
-           "gdn_chunk_transform", "gdn_chunk_fwd_noalloc")
+           "gdn_chunk_transform", "gdn_chunk_fwd_noalloc", "gdn_chunk_fwd_affine")
 STAGE_PREP, STAGE_FOLD, STAGE_PREFIX, STAGE_WALK, STAGE_OUT, STAGE_ALL = 1, 2, 4, 8, 16, 31
 
 
@@ -84,6 +84,8 @@ def lib():
         L.gdn_chunk_transform.restype = I
         L.gdn_chunk_fwd_noalloc.argtypes = [SP] + [P] * 9
         L.gdn_chunk_fwd_noalloc.restype = I
+        L.gdn_chunk_fwd_affine.argtypes = [SP] + [P] * 10 + [SZ, P]
+        L.gdn_chunk_fwd_affine.restype = I
         _lib = L
     return _lib
 
@@ -213,6 +215,31 @@ def chunk_fwd_noalloc(q, k, v, g, beta, h0, out, final_state=None, chunk=128, n_
                                        _ptr(h0), _ptr(out), _ptr(final_state), _stream(stream)),
            "gdn_chunk_fwd_noalloc")
     return out, final_state
+
+
+def chunk_fwd_affine(q, k, v, g, beta, h0=None, chunk=128, o_dtype=torch.float32, workspace=None,
+                     out=None, final_state=None, affine=None, stream=None):
+    """The forward that also returns the affine map of the whole sequence
+    (gdn_chunk_fwd_affine): (o, h_T, A) with A [B,H_v,d_k,d_k] fp32 and
+    h_T = A h0 + B (B = h_T when h0 is None)."""
+    B, T, Hqk, Hv, dk, dv, dev = _inputs(q, k, v, g, beta)
+    shape = make_shape(B, T, Hqk, Hv, dk, dv, chunk, 0, k.dtype, o_dtype)
+    if h0 is not None:
+        _need(h0, "h0", torch.float32, (B, Hv, dk, dv), dev)
+    need = workspace_size(shape)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    o = out if out is not None else torch.empty((B, T, Hv, dv), dtype=o_dtype, device=dev)
+    _need(o, "o", o_dtype, (B, T, Hv, dv), dev)
+    hT = final_state if final_state is not None else torch.empty((B, Hv, dk, dv), dtype=torch.float32, device=dev)
+    _need(hT, "h_T", torch.float32, (B, Hv, dk, dv), dev)
+    A = affine if affine is not None else torch.empty((B, Hv, dk, dk), dtype=torch.float32, device=dev)
+    _need(A, "A", torch.float32, (B, Hv, dk, dk), dev)
+    _check(lib().gdn_chunk_fwd_affine(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                      _ptr(h0), _ptr(o), _ptr(hT), _ptr(A), _ptr(workspace),
+                                      ctypes.c_size_t(workspace.numel()), _stream(stream)),
+           "gdn_chunk_fwd_affine")
+    return o, hT, A
 
 
 def workspace_size_varlen(shape: GdnShape) -> int:

@@ -102,6 +102,12 @@ __global__ void copy_state_kernel(const float *src, float *dst, size_t n) {
     dst[i] = src ? src[i] : 0.f;
 }
 
+// identity matrices [n / (D * D)][D][D] (the map of an empty sequence)
+__global__ void identity_kernel(float *dst, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    dst[i] = (i % (D * D)) / D == i % D ? 1.f : 0.f;
+}
+
 FwdArgs base_args(const gdn_shape &s) {
   FwdArgs a{};
   a.B = s.B; a.T = s.T; a.Hqk = s.H_qk; a.Hv = s.H_v; a.N = chunks_of(s);
@@ -149,7 +155,7 @@ gdn_status launch_prep(const FwdArgs &a, const Lx &x, bool rag = false) {
 
 template <int C, typename TI, int MODE, int KIND>
 gdn_status launch_walk(const FwdArgs &a, const Lx &x) {
-  const int width = KIND == FOLD ? 2 * D : D;
+  const int width = KIND == WALK ? D : 2 * D;   // state columns (the augmented state for FOLD and WALK_A)
   // Launch form by the number of walks (units), measured:
   //  * many (walk: 65 or more; fold: 256 or more): the throughput form, one
   //    wave per 16-column slice, the slices of a workgroup sharing each
@@ -164,17 +170,22 @@ gdn_status launch_walk(const FwdArgs &a, const Lx &x) {
   constexpr int NWS = C >= 128 ? 4 : 2;   // waves per slice: whole k-blocks of V' rows each
   // (the walk always hands h and V' to the output stage; the throughput and
   // paired forms count on those stores)
-  if (KIND == WALK && (!a.Hs || !a.Vn)) return GDN_ERR_NULL;
-  if (KIND == WALK && units >= 65) {
-    launch(walk_shared_kernel<C, TI, MODE, KIND, 4>, dim3((unsigned)(units * (width / 64))), dim3(256), x, a);
-  } else if (KIND == FOLD && units * (width / 128) >= 512) {
-    launch(walk_shared_kernel<C, TI, MODE, KIND, 8>, dim3((unsigned)(units * (width / 128))), dim3(512), x, a);
-  } else if (KIND == WALK && units > 32 && units <= 64) {
-    // two latency-form slices per compute unit would each stream the same
-    // operands: one workgroup of two slices shares a copy in LDS instead
-    launch(walk_pair_kernel<C, TI, MODE, NWS>, dim3((unsigned)(units * (D / 32))), dim3(128 * NWS), x, a);
-  } else {
+  if (KIND != FOLD && (!a.Hs || !a.Vn)) return GDN_ERR_NULL;
+  // (the walk that also yields A takes the latency form at any count)
+  if constexpr (KIND == WALK_A) {
     launch(walk_ring_kernel<C, TI, MODE, KIND, NWS>, dim3((unsigned)(units * (width / 16))), dim3(64 * NWS), x, a);
+  } else {
+    if (KIND == WALK && units >= 65) {
+      launch(walk_shared_kernel<C, TI, MODE, KIND, 4>, dim3((unsigned)(units * (width / 64))), dim3(256), x, a);
+    } else if (KIND == FOLD && units * (width / 128) >= 512) {
+      launch(walk_shared_kernel<C, TI, MODE, KIND, 8>, dim3((unsigned)(units * (width / 128))), dim3(512), x, a);
+    } else if (KIND == WALK && units > 32 && units <= 64) {
+      // two latency-form slices per compute unit would each stream the same
+      // operands: one workgroup of two slices shares a copy in LDS instead
+      launch(walk_pair_kernel<C, TI, MODE, NWS>, dim3((unsigned)(units * (D / 32))), dim3(128 * NWS), x, a);
+    } else {
+      launch(walk_ring_kernel<C, TI, MODE, KIND, NWS>, dim3((unsigned)(units * (width / 16))), dim3(64 * NWS), x, a);
+    }
   }
   return check_launch();
 }
@@ -189,14 +200,14 @@ gdn_status launch_out(const FwdArgs &a, const Lx &x, bool rag = false) {
   return check_launch();
 }
 
-template <int C, typename TI, int MODE, typename TO>
+template <int C, typename TI, int MODE, typename TO, int KIND = WALK>
 gdn_status launch_walk_out(const FwdArgs &a, const Lx &x) {
-  constexpr int NG = (D / 16) / kFusedWpg;   // workgroups per walk
+  constexpr int NG = (KIND == WALK_A ? 2 : 1) * (D / 16) / kFusedWpg;   // workgroups per walk
   const long units = (long)a.B * a.Hv * a.jobs;
   if (a.T % C)
-    launch(walk_out_kernel<C, TI, MODE, TO, kFusedWpg, true>, dim3((unsigned)(units * NG)), dim3(64 * kFusedWpg), x, a);
+    launch(walk_out_kernel<C, TI, MODE, TO, kFusedWpg, true, KIND>, dim3((unsigned)(units * NG)), dim3(64 * kFusedWpg), x, a);
   else
-    launch(walk_out_kernel<C, TI, MODE, TO, kFusedWpg, false>, dim3((unsigned)(units * NG)), dim3(64 * kFusedWpg), x, a);
+    launch(walk_out_kernel<C, TI, MODE, TO, kFusedWpg, false, KIND>, dim3((unsigned)(units * NG)), dim3(64 * kFusedWpg), x, a);
   return check_launch();
 }
 
@@ -212,10 +223,12 @@ gdn_status launch_prefix(int BH, int n, const float *A, const float *Bm, const f
   return check_launch();
 }
 
+// A (optional): the affine map of the whole sequence, from the walk of the
+// augmented state [A | h] (one group only)
 template <int C, typename TI, int MODE>
 gdn_status run_fwd(const gdn_shape &s, int stages, const void *q, const void *k, const void *v, const float *g,
                    const float *beta, const float *h0, void *o, float *h_T, char *ws, hipStream_t st,
-                   void *const *ev0 = nullptr, void *const *ev1 = nullptr) {
+                   void *const *ev0 = nullptr, void *const *ev1 = nullptr, float *A = nullptr) {
   // stage bit b (GDN_STAGE_* = 1 << b) launches with events ev0[b], ev1[b]
   auto lx = [&](int b) {
     Lx x{st};
@@ -237,6 +250,11 @@ gdn_status run_fwd(const gdn_shape &s, int stages, const void *q, const void *k,
   }
   // the walk: with its outputs (fused), or handing h and V' to the output stage
   auto walk = [&](const FwdArgs &w) -> gdn_status {
+    if (A) {
+      if (!fused) return launch_walk<C, TI, MODE, WALK_A>(w, lx(3));
+      if (s.o_dtype == GDN_F32) return launch_walk_out<C, TI, MODE, float, WALK_A>(w, lx(3));
+      return launch_walk_out<C, TI, MODE, __bf16, WALK_A>(w, lx(3));
+    }
     if (!fused) return launch_walk<C, TI, MODE, WALK>(w, lx(3));
     if (s.o_dtype == GDN_F32) return launch_walk_out<C, TI, MODE, float>(w, lx(3));
     return launch_walk_out<C, TI, MODE, __bf16>(w, lx(3));
@@ -244,7 +262,7 @@ gdn_status run_fwd(const gdn_shape &s, int stages, const void *q, const void *k,
   const int J = groups_of(s);
   if (stages & GDN_STAGE_PREP) GDN_TRY((launch_prep<C, TI, MODE>(a, lx(0))));
   if (J == 1) {
-    a.init = h0; a.init_per_job = 0; a.fin = h_T;
+    a.init = h0; a.init_per_job = 0; a.fin = h_T; a.pairA = A;
     if (stages & GDN_STAGE_WALK) GDN_TRY(walk(a));
   } else {
     FwdArgs f = a;
@@ -339,9 +357,9 @@ gdn_status run_transform(const gdn_shape &s, const void *k, const void *v, const
 
 struct FwdCall {
   const gdn_shape &s; int stages; const void *q, *k, *v; const float *g, *beta, *h0; void *o; float *h_T;
-  char *w; hipStream_t st; void *const *ev0 = nullptr, *const *ev1 = nullptr;
+  char *w; hipStream_t st; void *const *ev0 = nullptr, *const *ev1 = nullptr; float *A = nullptr;
   template <int C, typename TI, int MODE> gdn_status run() {
-    return run_fwd<C, TI, MODE>(s, stages, q, k, v, g, beta, h0, o, h_T, w, st, ev0, ev1);
+    return run_fwd<C, TI, MODE>(s, stages, q, k, v, g, beta, h0, o, h_T, w, st, ev0, ev1, A);
   }
 };
 struct VarlenCall {
@@ -465,6 +483,33 @@ gdn_status gdn_chunk_fwd_timed(const gdn_shape *s, int32_t stages, const void *q
   if (ws_bytes < layout(*s).total) return GDN_ERR_WORKSPACE;
   char *w = reinterpret_cast<char *>(ws);
   FwdCall f{*s, stages, q, k, v, g, beta, h0, o, h_T, w, st, ev_start, ev_stop};
+  return dispatch(*s, f);
+}
+
+gdn_status gdn_chunk_fwd_affine(const gdn_shape *s, const void *q, const void *k, const void *v, const float *g,
+                                const float *beta, const float *h0, void *o, float *h_T, float *A, void *ws,
+                                size_t ws_bytes, void *hip_stream) {
+  GDN_TRY(gdn_validate(s));
+  if (s->n_groups > 1) return GDN_ERR_SHAPE;
+  if (!A) return GDN_ERR_NULL;
+  if (misaligned(A)) return GDN_ERR_ALIGN;
+  hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+  if (s->T == 0) {   // no tokens: A = I, h_T = h0
+    if (misaligned(h0) || misaligned(h_T)) return GDN_ERR_ALIGN;
+    const size_t n = (size_t)s->B * s->H_v * D * D;
+    hipLaunchKernelGGL(identity_kernel, dim3(256), dim3(256), 0, st, A, n);
+    GDN_TRY(check_launch());
+    if (!h_T) return GDN_OK;
+    hipLaunchKernelGGL(copy_state_kernel, dim3(256), dim3(256), 0, st, h0, h_T, n);
+    return check_launch();
+  }
+  if (!q || !k || !v || !g || !beta || !o || !ws) return GDN_ERR_NULL;
+  for (const void *p : {(const void *)q, (const void *)k, (const void *)v, (const void *)g,
+                        (const void *)beta, (const void *)h0, (const void *)o, (const void *)h_T,
+                        (const void *)ws})
+    if (misaligned(p)) return GDN_ERR_ALIGN;
+  if (ws_bytes < layout(*s).total) return GDN_ERR_WORKSPACE;
+  FwdCall f{*s, GDN_STAGE_ALL, q, k, v, g, beta, h0, o, h_T, reinterpret_cast<char *>(ws), st, nullptr, nullptr, A};
   return dispatch(*s, f);
 }
 

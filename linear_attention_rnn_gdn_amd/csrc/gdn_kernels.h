@@ -69,7 +69,11 @@ namespace gdn {
 
 constexpr int D = 128;        // d_k = d_v
 constexpr int NT = 256;       // threads per workgroup
-constexpr int WALK = 0, FOLD = 1;
+// walk kinds: WALK (the state h from h0; hands h and V' to the output stage),
+// FOLD (the augmented state [A | B] of a group from [I | 0]: the group's
+// pair), WALK_A (the augmented state [A | h] from [I | h0]: a walk that also
+// yields the affine map A of the whole sequence, with h as in WALK)
+constexpr int WALK = 0, FOLD = 1, WALK_A = 2;
 
 template <typename TI> struct LdPad { static constexpr int v = 8; };
 template <> struct LdPad<float> { static constexpr int v = 4; };
@@ -1047,7 +1051,7 @@ __global__ __launch_bounds__(64 * NWS) void walk_ring_kernel(FwdArgs a) {
   using AF = Frag<PKw::a>;
   using HF = Frag<PKw::b>;   // state operand (for W h)
   using VF = Frag<PKk::b>;   // d o V' operand (for K^T (d o V'))
-  constexpr int NS = (KIND == FOLD ? 2 * D : D) / 16;   // slices
+  constexpr int NS = (KIND == WALK ? D : 2 * D) / 16;   // slices (the augmented state: A columns first)
   constexpr int MV = C / 16, MH = D / 16;                // V' and state row tiles
   constexpr int KBW = D / 32, KBK = C / 32;              // k-blocks of the two products
   constexpr int MVW = MV / NWS, MHW = MH / NWS;          // row tiles per wave
@@ -1072,6 +1076,8 @@ __global__ __launch_bounds__(64 * NWS) void walk_ring_kernel(FwdArgs a) {
   const int c0 = slice * 16;   // first column (of the augmented [A|B] in FOLD)
   const bool has_u = KIND == WALK || c0 >= D;
   const int us = KIND == WALK ? slice : slice - D / 16;   // U column tile
+  // h columns of the augmented state in WALK_A: as a WALK slice of index us
+  const bool hcols = KIND == WALK || (KIND == WALK_A && c0 >= D);
   const int mv0 = w * MVW, mh0 = w * MHW;                 // this wave's first V' / state tile
   // this walk's chunks, as in walk_shared_kernel
   size_t cb0;
@@ -1100,11 +1106,11 @@ __global__ __launch_bounds__(64 * NWS) void walk_ring_kernel(FwdArgs a) {
     for (int i = 0; i < 4; ++i) {
       const int kr = 16 * (mh0 + t) + 4 * g + i;
       float x = 0.f;
-      if (KIND == FOLD) {
-        x = (col < D && kr == col) ? 1.f : 0.f;
-      } else if (a.init) {
+      if (KIND != WALK && col < D) {
+        x = kr == col ? 1.f : 0.f;
+      } else if (KIND != FOLD && a.init) {
         const float *src = a.init_per_job ? a.init + (bh * a.jobs + job) * D * D : a.init + bh * D * D;
-        x = src[(size_t)kr * D + col];
+        x = src[(size_t)kr * D + (KIND == WALK ? col : col - D)];
       }
       h[t][i] = x;
     }
@@ -1114,11 +1120,14 @@ __global__ __launch_bounds__(64 * NWS) void walk_ring_kernel(FwdArgs a) {
   auto store_final = [&]() {
     float *dst = nullptr;
     int dcol = c0;
-    if (KIND == FOLD) {
-      if (c0 < D) dst = a.pairA + (bh * a.jobs + job) * D * D;
-      else { dst = a.pairB + (bh * a.jobs + job) * D * D; dcol = c0 - D; }
+    if (KIND != WALK && c0 < D) {
+      dst = a.pairA + (bh * a.jobs + job) * D * D;
+    } else if (KIND == FOLD) {
+      dst = a.pairB + (bh * a.jobs + job) * D * D;
+      dcol = c0 - D;
     } else if (a.fin && job == a.jobs - 1) {   // (the last group's end state)
       dst = a.fin + bh * D * D;
+      dcol = KIND == WALK ? c0 : c0 - D;
     }
     if (dst) {
 #pragma unroll
@@ -1257,10 +1266,10 @@ __global__ __launch_bounds__(64 * NWS) void walk_ring_kernel(FwdArgs a) {
     // The chunk-start state and V' go out after the chunk's last loads: the
     // memory counter drains in issue order, so a store issued ahead of a load
     // would hold up every wait for that load.
-    if (KIND == WALK && a.Hs)
-      store_result_tiles<PR::h_store>(a.Hs + ((cb * (D / 16) + slice) * MH + mh0) * Store<PR::h_store>::tile_floats, h, lane);
-    if (KIND == WALK && a.Vn)
-      store_result_tiles<PR::v_store>(a.Vn + ((cb * (D / 16) + slice) * MV + mv0) * Store<PR::v_store>::tile_floats, vps, lane);
+    if (KIND != FOLD && hcols && a.Hs)
+      store_result_tiles<PR::h_store>(a.Hs + ((cb * (D / 16) + us) * MH + mh0) * Store<PR::h_store>::tile_floats, h, lane);
+    if (KIND != FOLD && hcols && a.Vn)
+      store_result_tiles<PR::v_store>(a.Vn + ((cb * (D / 16) + us) * MV + mv0) * Store<PR::v_store>::tile_floats, vps, lane);
 #pragma unroll
     for (int t = 0; t < MHW; ++t)
 #pragma unroll
@@ -1980,7 +1989,146 @@ __device__ __forceinline__ void wait_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int C, typename TI, int MODE, typename TO, int WPG, bool RAG>
+// The A columns of the augmented state [A | h] (WALK_A): A <- e^{G_last} A -
+// K^T (d o (W A)) from A = I, written to a.pairA at the end.  Workgroups of
+// walk_out_kernel that hold A columns run this instead of the output-forming
+// loop: only W, K^T and G are needed, copied into the same LDS slots.
+template <int C, typename TI, int MODE, int WPG>
+__device__ __forceinline__ void walk_a_columns(const FwdArgs &a, size_t bh, int slice, char *sW, char *sKt, float *sG) {
+  using PR = Prec<MODE>;
+  using PKw = PolicyKinds<PR::wh>;
+  using PKk = PolicyKinds<PR::kv>;
+  using L = WalkOutLds<C, TI>;
+  constexpr bool F32 = sizeof(TI) == 4;
+  constexpr int MV = C / 16, MH = D / 16, KBW = D / 32, KBK = C / 32, BPF = L::BPF;
+  constexpr int NCW = L::WB / 1024 / WPG, NCK = L::KTB / 1024 / WPG, GL = C / 4 / WPG;
+  static_assert(KBK >= 1 && NCW >= 1 && NCK >= 1, "whole copies");
+  const int lane = threadIdx.x & 63, g = lane >> 4, lr = lane & 15, lq = 4 * g;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c0 = 16 * slice;   // column of A
+  const int cpj = a.cpj;
+  const size_t cb0 = uniform64(bh * a.N + a.n0);
+  const long long ktoff = (long long)uniform64((unsigned long long)kt_offset(a, bh));
+  f32x4 h[MH];
+#pragma unroll
+  for (int m = 0; m < MH; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) h[m][i] = 16 * m + 4 * g + i == c0 + lr ? 1.f : 0.f;
+  auto lds_addr = [](const void *p) {
+    unsigned x = (unsigned)(size_t)(__attribute__((address_space(3))) const char *)p;
+    asm volatile("" : "+s"(x));
+    return x;
+  };
+  auto dma = [&](const char *ubase, unsigned voff, unsigned ldst) {
+    __builtin_amdgcn_global_load_lds((const void *)(ubase + voff), (__attribute__((address_space(3))) void *)(size_t)ldst,
+                                     16, 0, 0);
+  };
+  auto ubase = [](const void *p, size_t off) -> const char * {
+    return reinterpret_cast<const char *>(uniform64(reinterpret_cast<unsigned long long>(p) + off));
+  };
+  const unsigned fl = lane * 16 * BPF;
+  auto copy_frags = [&](const char *src, char *slot, int ncopies) {
+    const unsigned ls = lds_addr(slot);
+    for (int jj = 0; jj < ncopies; ++jj) {
+      const int j = jj * WPG + wv;
+      dma(ubase(src, (size_t)(j / BPF) * 1024 * BPF + (j % BPF) * 16), fl, ls + j * 1024);
+    }
+  };
+  auto copy_w = [&](size_t cb) { copy_frags(reinterpret_cast<const char *>(a.W) + cb * C * D * sizeof(TI), sW, NCW); };
+  auto copy_ktg = [&](size_t cb) {
+    copy_frags(reinterpret_cast<const char *>(a.Kt) + (cb + ktoff) * D * C * sizeof(TI), sKt, NCK);
+    if (lane < GL) dma(ubase(a.G, (cb * C + wv * GL * 4) * sizeof(float)), lane * 16, lds_addr(sG) + wv * GL * 16);
+  };
+  auto frag = [&](const char *slot, int p) -> Frag<PKw::a> {
+    Frag<PKw::a> f;
+    const char *base = slot + p * BPF * 1024 + lane * 16;
+    if constexpr (F32) {
+      const float4 x0 = *reinterpret_cast<const float4 *>(base);
+      const float4 x1 = *reinterpret_cast<const float4 *>(base + 1024);
+      f.v[0] = x0.x; f.v[1] = x0.y; f.v[2] = x0.z; f.v[3] = x0.w;
+      f.v[4] = x1.x; f.v[5] = x1.y; f.v[6] = x1.z; f.v[7] = x1.w;
+    } else {
+      f.hi = *reinterpret_cast<const bf16x8 *>(base);
+    }
+    return f;
+  };
+  copy_w(cb0);
+  copy_ktg(cb0);
+  wait_barrier<vm_lgkm0(0)>();
+  for (int cc = 0; cc < cpj; ++cc) {
+    const size_t cb = cb0 + cc;
+    const bool more = cc + 1 < cpj;
+    // V'_A = -W A
+    Frag<PKw::b> hb[KBW];
+#pragma unroll
+    for (int kb = 0; kb < KBW; ++kb) {
+      const float x[8] = {h[2 * kb][0], h[2 * kb][1], h[2 * kb][2], h[2 * kb][3],
+                          h[2 * kb + 1][0], h[2 * kb + 1][1], h[2 * kb + 1][2], h[2 * kb + 1][3]};
+      hb[kb] = make_frag<PKw::b>(x);
+    }
+    f32x4 vps[MV];
+    {
+      Frag<PKw::a> fa[2][KBW];
+#pragma unroll
+      for (int kb = 0; kb < KBW; ++kb) fa[0][kb] = frag(sW, kb);
+#pragma unroll
+      for (int m = 0; m < MV; ++m) {
+        if (m + 1 < MV) {
+#pragma unroll
+          for (int kb = 0; kb < KBW; ++kb) fa[(m + 1) & 1][kb] = frag(sW, (m + 1) * KBW + kb);
+        }
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kb = 0; kb < KBW; ++kb) mma(acc, fa[m & 1][kb], hb[kb]);
+        vps[m] = f32x4{-acc[0], -acc[1], -acc[2], -acc[3]};
+      }
+    }
+    // every wave past W; this chunk's K^T and G landed
+    wait_barrier<vm_lgkm0(0)>();
+    if (more) copy_w(cb + 1);
+    // A <- e^{G_last} A + K^T (d o V'_A)
+    const float gl2 = sG[C - 1] * LOG2E;
+    const float gl = exp2_fast(gl2);
+    Frag<PKk::b> vb[KBK];
+#pragma unroll
+    for (int kb = 0; kb < KBK; ++kb) {
+      float y[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int m = 2 * kb + j / 4, i = j % 4;
+        y[j] = vps[m][i] * exp2_fast(gl2 - sG[16 * m + lq + i] * LOG2E);
+      }
+      vb[kb] = make_frag<PKk::b>(y);
+    }
+    {
+      Frag<PKw::a> fk[2][KBK];
+#pragma unroll
+      for (int kb = 0; kb < KBK; ++kb) fk[0][kb] = frag(sKt, kb);
+#pragma unroll
+      for (int m = 0; m < MH; ++m) {
+        if (m + 1 < MH) {
+#pragma unroll
+          for (int kb = 0; kb < KBK; ++kb) fk[(m + 1) & 1][kb] = frag(sKt, (m + 1) * KBK + kb);
+        }
+        f32x4 acc2 = zero4();
+#pragma unroll
+        for (int kb = 0; kb < KBK; ++kb) mma(acc2, fk[m & 1][kb], vb[kb]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) h[m][i] = gl * h[m][i] + acc2[i];
+      }
+    }
+    if (more) {
+      wait_barrier<vm_lgkm0(0)>();   // every wave past K^T and G; the next chunk's W landed
+      copy_ktg(cb + 1);
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < MH; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a.pairA[bh * D * D + (size_t)(16 * m + 4 * g + i) * D + c0 + lr] = h[m][i];
+}
+
+template <int C, typename TI, int MODE, typename TO, int WPG, bool RAG, int KIND>
 __global__ __launch_bounds__(64 * WPG) void walk_out_kernel(FwdArgs a) {
   using PR = Prec<MODE>;
   using PKw = PolicyKinds<PR::wh>;      // W x h
@@ -1995,7 +2143,9 @@ __global__ __launch_bounds__(64 * WPG) void walk_out_kernel(FwdArgs a) {
   static_assert(PKq::a == PKq::b && PKq::b == PKh::b, "one query fragment serves both products");
   static_assert(PKw::b == PKh::a || (PKw::b == F_BF16 && PKh::a == F_SPLIT), "W h takes the state split for h^T Q^T");
   constexpr int MV = C / 16, MH = D / 16, KBW = D / 32, KBK = C / 32, R = C / 16;
-  constexpr int NG = (D / 16) / WPG;   // workgroups per walk
+  static_assert(KIND == WALK || KIND == WALK_A, "walk kinds with outputs");
+  constexpr int NGH = (D / 16) / WPG;                      // workgroups of h columns per walk
+  constexpr int NG = (KIND == WALK_A ? 2 : 1) * NGH;        // workgroups per walk (A columns first)
   constexpr int BPF = L::BPF;
   // per wave and chunk: 1 KB copies of W, K^T, Q (and K); U loads; o stores
   constexpr int NCW = L::WB / 1024 / WPG, NCK = L::KTB / 1024 / WPG, NCQ = L::QB / 1024 / WPG;
@@ -2021,9 +2171,16 @@ __global__ __launch_bounds__(64 * WPG) void walk_out_kernel(FwdArgs a) {
   xcd_unit(blockIdx.x, NG, a.B * a.Hv * a.jobs, unit, grp);
   const int job = unit % a.jobs;
   const size_t bh = (size_t)(unit / a.jobs);
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (KIND == WALK_A) {
+    if (grp < NGH) {   // (uniform per workgroup) columns of A
+      walk_a_columns<C, TI, MODE, WPG>(a, bh, grp * WPG + wv, sW, sKt, sG);
+      return;
+    }
+    grp -= NGH;
+  }
   const int b = (int)(bh / a.Hv), hv = (int)(bh % a.Hv), hq = hv / (a.Hv / a.Hqk);
   const int lane = threadIdx.x & 63, lr = lane & 15, g = lane >> 4, lq = 4 * g;
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int slice = grp * WPG + wv, c0 = 16 * slice;
   const int nfirst = a.n0 + job * a.cpj;   // first chunk of this walk in its sequence row
   const int cpj = a.cpj;

@@ -137,6 +137,11 @@ def test_entry_points_reject_bad_arguments_without_launching(gdn):
     assert L.gdn_compose_prefix(0, 8, 128, 128, ok, ok, null, ok, null, 0, null) == -2
     assert L.gdn_compose_prefix(4, 8, 128, 128, odd, ok, null, ok, null, 0, null) == -4
     assert L.gdn_validate(None) == -1
+    # the forward with the affine map: one group only, A required
+    assert L.gdn_chunk_fwd_affine(ctypes.byref(s), ok, ok, ok, ok, ok, null, ok, null, null, ok, ws, null) == -1
+    assert L.gdn_chunk_fwd_affine(ctypes.byref(s), ok, ok, ok, ok, ok, null, ok, null, odd, ok, ws, null) == -4
+    grouped = _shape(gdn, n_groups=4)
+    assert L.gdn_chunk_fwd_affine(ctypes.byref(grouped), ok, ok, ok, ok, ok, null, ok, null, ok, ok, ws, null) == -2
 
 
 def test_varlen_checks_without_launching(gdn):

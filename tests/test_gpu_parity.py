@@ -401,28 +401,63 @@ def test_groups_weak_decay_compose_matters(gdn):
     assert _err(bad, o_ref) > 10 * 2e-2 * ro
 
 
+@pytest.mark.parametrize("dtype,C,B,Hqk,Hv,T,gc", [
+    ("bf16", 128, 1, 2, 4, 1000, -0.01),    # the latency form of the walk, weak decay, ragged
+    ("bf16", 128, 4, 16, 32, 640, None),    # 128 walks: the walk with outputs
+    ("bf16", 64, 8, 8, 16, 64 * 7, -0.01),  # C = 64, 128 walks, weak decay
+    ("f32", 64, 2, 1, 3, 64 * 5 - 3, -0.01),
+])
+def test_forward_affine(gdn, dtype, C, B, Hqk, Hv, T, gc):
+    # gdn_chunk_fwd_affine: the walk of [A | h] from [I | h0] also yields the
+    # map A of the whole sequence.  o and h_T are gdn_chunk_fwd's, bit for
+    # bit; A is the oracle's product of the per-token maps (its fold of the
+    # sequence as one group), and h_T = A h0 + B with B the oracle's state
+    # reached from zero.
+    w = WORKLOADS["tiny"].replace(T=T, B=B, Hqk=Hqk, Hv=Hv, chunk=C, dtype=dtype, h0_std=0.05)
+    x = make_inputs(w, device="cuda", seed=T + B * Hv, g_const=gc, beta_scale=0.3 if gc is not None else None)
+    args = (x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"])
+    o, hT, A = gdn.chunk_fwd_affine(*args, chunk=C)
+    o1, h1 = gdn.chunk_fwd(*args, chunk=C)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o1) and torch.equal(hT, h1)
+    Ar, Br = oracle.fold(_cpu(x["k"]), _cpu(x["v"]), _cpu(x["g"]), _cpu(x["beta"]), n_groups=1)
+    Ar, Br = Ar[:, :, 0], Br[:, :, 0]
+    # (A: W x state products take bf16 operands on the bf16 path)
+    tol = 1e-2 if dtype == "bf16" else 1e-4
+    ea = _err(A.cpu().numpy(), Ar)
+    print(f"  A: max-abs {ea:.3e} (max |A| {np.abs(Ar).max():.3e})", flush=True)
+    assert ea <= tol * np.abs(Ar).max()
+    hr = np.einsum("bhij,bhjc->bhic", Ar, x["h0"].cpu().double().numpy()) + Br
+    o_ref, h_ref = oracle.fwd(**{kk: _cpu(vv) for kk, vv in x.items()})
+    assert np.abs(hr - h_ref).max() <= 1e-9 * max(1.0, np.abs(h_ref).max())   # (the oracle's own identity)
+    ro = _rms(o_ref)
+    _check("o", o.cpu().numpy(), o_ref, TOL[dtype], ro)
+    _check("h_T", hT.cpu().numpy(), h_ref, TOL[dtype], ro)
+
+
 @pytest.mark.parametrize("C", [64, 128])
 def test_sequence_shards_through_the_boundary(gdn, C):
     # The sequence-sharded flow, each shard standing in for a device, through
-    # the exported entry points only: every shard folds its whole length into
-    # one affine pair (gdn_chunk_fold, one group); the pairs are gathered
-    # and their exclusive prefix (gdn_compose_prefix) gives each shard its
-    # incoming state; each shard's forward from that state (gdn_chunk_fwd)
-    # gives its outputs.  Together they are the whole sequence's o and h_T.
-    # Weak decay keeps each shard's map far from zero, so the incoming
-    # states carry the earlier shards.
+    # the exported entry points only.  First pass: every shard runs the
+    # forward from a zero state with its affine map (gdn_chunk_fwd_affine):
+    # its pair is (A, h_T).  The pairs are gathered and their exclusive prefix
+    # (gdn_compose_prefix) gives each shard its incoming state; the second
+    # pass, each shard's forward from that state (gdn_chunk_fwd), gives its
+    # outputs.  Together they are the whole sequence's o and h_T.  Weak decay
+    # keeps each shard's map far from zero, so the incoming states carry the
+    # earlier shards.
     S, L = 4, 4 * C
     w = WORKLOADS["tiny"].replace(T=S * L, Hqk=2, Hv=4, chunk=C, dtype="bf16", h0_std=0.05, B=2)
     x = make_inputs(w, device="cuda", seed=40 + C, g_const=0.0, beta_scale=0.1)
     shard = lambda t, d: t[:, d * L:(d + 1) * L].contiguous()
     A, Bm = [], []
     for d in range(S):
-        a_, b_ = gdn.chunk_fold(*[shard(x[kk], d) for kk in ("k", "v", "g", "beta")], n_groups=1, chunk=C)
+        _, b_, a_ = gdn.chunk_fwd_affine(*[shard(x[kk], d) for kk in ("q", "k", "v", "g", "beta")], None, chunk=C)
         A.append(a_)
         Bm.append(b_)
     BH = w.B * w.Hv
-    A = torch.cat(A, dim=2).reshape(BH, S, 128, 128)
-    Bm = torch.cat(Bm, dim=2).reshape(BH, S, 128, 128)
+    A = torch.stack(A, dim=2).reshape(BH, S, 128, 128)
+    Bm = torch.stack(Bm, dim=2).reshape(BH, S, 128, 128)
     h_in, h_fin = gdn.compose_prefix(A, Bm, x["h0"].reshape(BH, 128, 128), split_bf16=True)
     outs, h_last = [], None
     for d in range(S):
@@ -436,6 +471,13 @@ def test_sequence_shards_through_the_boundary(gdn, C):
     _check("o", o, o_ref, 2e-2, ro)
     _check("h_T (last shard)", h_last.cpu().numpy(), h_ref, 2e-2, ro)
     _check("h_T (prefix)", h_fin.reshape(w.B, w.Hv, 128, 128).cpu().numpy(), h_ref, 2e-2, ro)
+    # the first pass's pairs equal the exported fold's (one group per shard)
+    for d in (0, S - 1):
+        Af, Bf = gdn.chunk_fold(*[shard(x[kk], d) for kk in ("k", "v", "g", "beta")], n_groups=1, chunk=C)
+        torch.cuda.synchronize()
+        ra = float((A[:, d] - Af.reshape(BH, 128, 128)).abs().max()) / float(Af.abs().max())
+        rb = float((Bm[:, d] - Bf.reshape(BH, 128, 128)).abs().max()) / float(Bf.abs().max())
+        assert ra <= 1e-2 and rb <= 1e-2, (d, ra, rb)
     # negative control: shards started from zero states miss by far
     o0 = torch.cat([gdn.chunk_fwd(*[shard(x[kk], d) for kk in ("q", "k", "v", "g", "beta")], None, chunk=C)[0]
                     for d in range(S)], dim=1).float().cpu().numpy()
