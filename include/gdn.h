@@ -255,6 +255,31 @@ gdn_status gdn_chunk_transform(const gdn_shape *shape, const void *k, const void
                                const float *g, const float *beta, float *G, float *Tm, float *W,
                                float *U, void *hip_stream);
 
+/* The chunked backward's state cotangents: the scan's backward walks the
+ * chunks in reverse ("Fuse the Gated Delta Net inter-chunk scan into a
+ * Pallas TPU kernel", section "Changes"), the cotangent of chunk n's
+ * incoming state being
+ *     dh_n = exp(G_last) dh_{n+1} - W^T (K_g dh_{n+1}) + ddh_n,   dh_N = dh_T,
+ * with W, K_g the forward's chunk quantities (gdn_chunk_transform) and
+ * ddh_n = (diag(e^G) Q - P W)^T dO_n the part that reaches the state through
+ * the chunk's own outputs (P = (Q K^T) o Gamma o [i <= r]).  These are the
+ * first stage of the gradients of gdn_chunk_fwd; they depend on q, k, g,
+ * beta and the cotangents only (not on v or h0).
+ *   q, k   [B, T, H_qk, d_k] dtype       g, beta [B, T, H_v] fp32
+ *   dO     [B, T, H_v, d_v] fp32          cotangent of o
+ *   dh_T   [B, H_v, d_k, d_v] fp32        cotangent of h_T, NULL = zero
+ *   dh_chunks [B, H_v, N, d_k, d_v] fp32  dh_n for every chunk n, or NULL
+ *   dh0    [B, H_v, d_k, d_v] fp32        cotangent of h0 (= dh_0), or NULL
+ *   (at least one of dh_chunks and dh0 non-NULL)
+ *   ws     at least gdn_workspace_size_bwd() bytes.
+ * shape->n_groups must be 0 or 1 and shape->o_dtype is ignored; other
+ * conventions as gdn_chunk_fwd. */
+gdn_status gdn_workspace_size_bwd(const gdn_shape *shape, size_t *bytes);
+gdn_status gdn_chunk_bwd_state(const gdn_shape *shape, const void *q, const void *k, const float *g,
+                               const float *beta, const float *dO, const float *dh_T,
+                               float *dh_chunks, float *dh0, void *ws, size_t ws_bytes,
+                               void *hip_stream);
+
 /* gdn_chunk_fwd for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
  * Arguments, checks and results are those of gdn_chunk_fwd, without the

@@ -46,7 +46,8 @@ _lib = None
 SYMBOLS = ("gdn_status_str", "gdn_validate", "gdn_workspace_size", "gdn_workspace_size_varlen",
            "gdn_chunk_fwd", "gdn_chunk_fwd_varlen",
            "gdn_chunk_fwd_stages", "gdn_chunk_fwd_timed", "gdn_chunk_fold", "gdn_compose_prefix",
-           "gdn_chunk_transform", "gdn_chunk_fwd_noalloc", "gdn_chunk_fwd_affine")
+           "gdn_chunk_transform", "gdn_chunk_fwd_noalloc", "gdn_chunk_fwd_affine",
+           "gdn_workspace_size_bwd", "gdn_chunk_bwd_state")
 STAGE_PREP, STAGE_FOLD, STAGE_PREFIX, STAGE_WALK, STAGE_OUT, STAGE_ALL = 1, 2, 4, 8, 16, 31
 
 
@@ -86,6 +87,10 @@ def lib():
         L.gdn_chunk_fwd_noalloc.restype = I
         L.gdn_chunk_fwd_affine.argtypes = [SP] + [P] * 10 + [SZ, P]
         L.gdn_chunk_fwd_affine.restype = I
+        L.gdn_workspace_size_bwd.argtypes = [SP, ctypes.POINTER(SZ)]
+        L.gdn_workspace_size_bwd.restype = I
+        L.gdn_chunk_bwd_state.argtypes = [SP] + [P] * 9 + [SZ, P]
+        L.gdn_chunk_bwd_state.restype = I
         _lib = L
     return _lib
 
@@ -240,6 +245,37 @@ def chunk_fwd_affine(q, k, v, g, beta, h0=None, chunk=128, o_dtype=torch.float32
                                       ctypes.c_size_t(workspace.numel()), _stream(stream)),
            "gdn_chunk_fwd_affine")
     return o, hT, A
+
+
+def chunk_bwd_state(q, k, g, beta, dO, dh_T=None, chunk=128, want_chunks=True, workspace=None, stream=None):
+    """The chunked backward's state cotangents (gdn_chunk_bwd_state): the
+    reverse chunk walk dh_n = e^{G_last} dh_{n+1} - W^T (K_g dh_{n+1}) + ddh_n
+    from dh_T.  q, k [B,T,H_qk,d_k]; g, beta [B,T,H_v] fp32; dO [B,T,H_v,d_v]
+    fp32; dh_T [B,H_v,d_k,d_v] fp32 or None.  Returns (dh_chunks
+    [B,H_v,N,d_k,d_v] or None, dh0 [B,H_v,d_k,d_v])."""
+    B, T, Hqk, dk = k.shape
+    Hv, dv = dO.shape[2], dO.shape[3]
+    dev = k.device
+    _need(q, "q", k.dtype, (B, T, Hqk, dk), dev)
+    _need(k, "k", None, None, dev)
+    _need(g, "g", torch.float32, (B, T, Hv), dev)
+    _need(beta, "beta", torch.float32, (B, T, Hv), dev)
+    _need(dO, "dO", torch.float32, (B, T, Hv, dv), dev)
+    if dh_T is not None:
+        _need(dh_T, "dh_T", torch.float32, (B, Hv, dk, dv), dev)
+    shape = make_shape(B, T, Hqk, Hv, dk, dv, chunk, 0, k.dtype, torch.float32)
+    n = ctypes.c_size_t(0)
+    _check(lib().gdn_workspace_size_bwd(ctypes.byref(shape), ctypes.byref(n)), "gdn_workspace_size_bwd")
+    if workspace is None:
+        workspace = torch.empty(max(int(n.value), 1), dtype=torch.uint8, device=dev)
+    N = -(-T // chunk)
+    dhc = torch.empty((B, Hv, N, dk, dv), dtype=torch.float32, device=dev) if want_chunks else None
+    dh0 = torch.empty((B, Hv, dk, dv), dtype=torch.float32, device=dev)
+    _check(lib().gdn_chunk_bwd_state(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(g), _ptr(beta), _ptr(dO),
+                                     _ptr(dh_T), _ptr(dhc), _ptr(dh0), _ptr(workspace),
+                                     ctypes.c_size_t(workspace.numel()), _stream(stream)),
+           "gdn_chunk_bwd_state")
+    return dhc, dh0
 
 
 def workspace_size_varlen(shape: GdnShape) -> int:

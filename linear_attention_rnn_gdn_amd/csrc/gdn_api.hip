@@ -11,6 +11,7 @@
 #include <mutex>
 
 #include "gdn.h"
+#include "gdn_bwd.h"
 #include "gdn_kernels.h"
 
 using namespace gdn;
@@ -646,3 +647,95 @@ extern "C" gdn_status gdn_chunk_fwd_noalloc(const gdn_shape *s, const void *q, c
   GDN_TRY(scratch_of_current_device(&ws));
   return gdn_chunk_fwd(s, q, k, v, g, beta, h0, o, h_T, ws, kScratchBytes, hip_stream);
 }
+
+// ----------------------------------------------------------------------------
+// The chunked backward's state cotangents: prep in its transform form (G and
+// W in fp32), the chunk-parallel term ddh_n, then the reverse walk.
+namespace {
+
+struct BwdLayout {
+  size_t G, W, ddh, total;
+};
+BwdLayout layout_bwd(const gdn_shape &s) {
+  const size_t BH = (size_t)s.B * s.H_v, N = chunks_of(s), C = s.chunk;
+  BwdLayout L{};
+  size_t off = 0;
+  L.G = off;   off += align_up(BH * N * C * 4);
+  L.W = off;   off += align_up(BH * N * C * D * 4);
+  L.ddh = off; off += align_up(BH * N * D * D * 4);
+  L.total = off;
+  return L;
+}
+
+template <int C, typename TI, int MODE>
+gdn_status run_bwd_state(const gdn_shape &s, const void *q, const void *k, const float *g, const float *beta,
+                         const float *dO, const float *dh_T, float *dh, float *dh0, char *ws, hipStream_t st) {
+  const BwdLayout L = layout_bwd(s);
+  FwdArgs a = base_args(s);
+  a.k = k; a.g = g; a.beta = beta;
+  a.G = reinterpret_cast<float *>(ws + L.G);
+  a.W = ws + L.W;   // fp32, row-major (the transform form)
+  a.U = nullptr; a.Tm = nullptr;
+  GDN_TRY((launch_prep<C, TI, MODE, false>(a, Lx{st})));
+  BwdArgs b{};
+  b.B = s.B; b.T = s.T; b.Hqk = s.H_qk; b.Hv = s.H_v; b.N = chunks_of(s);
+  b.q = q; b.k = k; b.dO = dO;
+  b.G = a.G; b.W = reinterpret_cast<const float *>(a.W);
+  b.ddh = reinterpret_cast<float *>(ws + L.ddh);
+  b.dhT = dh_T; b.dh = dh; b.dh0 = dh0;
+  const unsigned units = (unsigned)((long)b.N * s.B * s.H_v);
+  if (s.T % C)
+    hipLaunchKernelGGL((bwd_ddh_kernel<C, TI, MODE, true>), dim3(units), dim3(256), 0, st, a, b);
+  else
+    hipLaunchKernelGGL((bwd_ddh_kernel<C, TI, MODE, false>), dim3(units), dim3(256), 0, st, a, b);
+  GDN_TRY(check_launch());
+  if (s.T % C)
+    hipLaunchKernelGGL((bwd_walk_kernel<C, TI, MODE, true>), dim3((unsigned)(s.B * s.H_v)), dim3(512), 0, st, b);
+  else
+    hipLaunchKernelGGL((bwd_walk_kernel<C, TI, MODE, false>), dim3((unsigned)(s.B * s.H_v)), dim3(512), 0, st, b);
+  return check_launch();
+}
+
+struct BwdStateCall {
+  const gdn_shape &s; const void *q, *k; const float *g, *beta, *dO, *dh_T; float *dh, *dh0; char *w; hipStream_t st;
+  template <int C, typename TI, int MODE> gdn_status run() {
+    return run_bwd_state<C, TI, MODE>(s, q, k, g, beta, dO, dh_T, dh, dh0, w, st);
+  }
+};
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_workspace_size_bwd(const gdn_shape *s, size_t *bytes) {
+  if (!bytes) return GDN_ERR_NULL;
+  GDN_TRY(gdn_validate(s));
+  if (s->n_groups > 1) return GDN_ERR_SHAPE;
+  *bytes = layout_bwd(*s).total;
+  return GDN_OK;
+}
+
+gdn_status gdn_chunk_bwd_state(const gdn_shape *s, const void *q, const void *k, const float *g,
+                               const float *beta, const float *dO, const float *dh_T, float *dh_chunks,
+                               float *dh0, void *ws, size_t ws_bytes, void *hip_stream) {
+  GDN_TRY(gdn_validate(s));
+  if (s->n_groups > 1) return GDN_ERR_SHAPE;
+  if (!dh_chunks && !dh0) return GDN_ERR_NULL;
+  hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+  for (const void *p : {(const void *)dh_T, (const void *)dh_chunks, (const void *)dh0})
+    if (misaligned(p)) return GDN_ERR_ALIGN;
+  if (s->T == 0) {   // no chunks: the cotangent of h0 is that of h_T
+    if (!dh0) return GDN_OK;
+    hipLaunchKernelGGL(copy_state_kernel, dim3(256), dim3(256), 0, st, dh_T, dh0, (size_t)s->B * s->H_v * D * D);
+    return check_launch();
+  }
+  if (!q || !k || !g || !beta || !dO || !ws) return GDN_ERR_NULL;
+  for (const void *p : {(const void *)q, (const void *)k, (const void *)g, (const void *)beta, (const void *)dO,
+                        (const void *)ws})
+    if (misaligned(p)) return GDN_ERR_ALIGN;
+  if (ws_bytes < layout_bwd(*s).total) return GDN_ERR_WORKSPACE;
+  BwdStateCall f{*s, q, k, g, beta, dO, dh_T, dh_chunks, dh0, reinterpret_cast<char *>(ws), st};
+  return dispatch(*s, f);
+}
+
+}  // extern "C"

@@ -486,8 +486,10 @@ __global__ __launch_bounds__(PNT, 4) void prep_kernel(FwdArgs a) {   // two work
   TileBlock<C, TI, PNT / 2> xt;
   if (!vhalf)
     xt.load(tix, reinterpret_cast<const TI *>(a.k) + (((size_t)b * a.T + t0) * a.Hqk + hq) * D, (size_t)a.Hqk * D, rows);
-  else
+  else if (FWD || a.U)
     xt.load(tix, reinterpret_cast<const TI *>(a.v) + (((size_t)b * a.T + t0) * a.Hv + hv) * D, (size_t)a.Hv * D, rows);
+  else
+    xt.load(tix, nullptr, 0, 0);   // (the transform hook without U reads no values: zero rows)
 
   // (1) decay cumsum over the chunk (inclusive), beta
   {
@@ -752,6 +754,7 @@ __global__ __launch_bounds__(PNT, 4) void prep_kernel(FwdArgs a) {   // two work
     }
   };
   wu_pass(std::integral_constant<int, 0>{});
+  if (!FWD && !a.U) return;   // (the transform hook without U: the backward's W and G only)
   lds_barrier();
   if (vhalf) TileBlock<C, TI, PNT / 2>::put_transposed(tix, sX, xw);
   lds_barrier();

@@ -484,6 +484,41 @@ def test_sequence_shards_through_the_boundary(gdn, C):
     assert _err(o0, o_ref) > 10 * 2e-2 * ro
 
 
+@pytest.mark.parametrize("dtype,C,B,Hqk,Hv,T", [
+    ("f32", 64, 1, 2, 2, 512),      # the tiny workload's shape
+    ("bf16", 128, 1, 2, 4, 640),    # 8B-layer heads ratio, five chunks
+    ("bf16", 64, 2, 1, 2, 64 * 4 - 21),   # partial last chunk
+])
+def test_bwd_state_matches_oracle(gdn, dtype, C, B, Hqk, Hv, T):
+    # the backward's reverse chunk walk (gdn_chunk_bwd_state): the cotangent
+    # of every chunk's incoming state and of h0, against the chunked fp64
+    # gradient of the rule (oracle/backward.py: chunked_bwd, itself pinned by
+    # finite differences and against the per-token reverse pass).  Bars as
+    # for the forward, relative to the RMS of the oracle's cotangents.
+    from oracle import backward
+
+    w = WORKLOADS["tiny"].replace(T=T, B=B, Hqk=Hqk, Hv=Hv, chunk=C, dtype=dtype, h0_std=0.05)
+    x = make_inputs(w, device="cuda", seed=T + Hv)
+    gen = torch.Generator().manual_seed(T + 7)
+    dO = torch.randn((B, T, Hv, 128), generator=gen).to("cuda")
+    dhT = (torch.randn((B, Hv, 128, 128), generator=gen) * 0.1).to("cuda")
+    dhc, dh0 = gdn.chunk_bwd_state(x["q"], x["k"], x["g"], x["beta"], dO, dhT, chunk=C)
+    torch.cuda.synchronize()
+    out, walk, _ = backward.chunked_bwd(*[_cpu(x[kk]) for kk in ("q", "k", "v", "g", "beta")], _cpu(x["h0"]),
+                                        do=_cpu(dO), dhT=_cpu(dhT), C=C, return_walk=True)
+    r = _rms(walk)
+    for name, got, ref in (("dh_n", dhc.cpu().numpy(), walk), ("dh0", dh0.cpu().numpy(), out["dh0"])):
+        e = _err(got, ref)
+        print(f"  {name}: max-abs {e:.3e}  limit {TOL[dtype] * r:.3e}", flush=True)
+        assert e <= TOL[dtype] * r
+    # dh_T = 0 and dO = 0 give zero cotangents; dO = 0 alone gives the
+    # transposed maps applied to dh_T only (ddh = 0)
+    z = torch.zeros_like(dO)
+    dhz, dh0z = gdn.chunk_bwd_state(x["q"], x["k"], x["g"], x["beta"], z, None, chunk=C)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dhz) == 0 and torch.count_nonzero(dh0z) == 0
+
+
 def test_long_sequence_reduced(gdn):
     # the long-sequence workload's shape and group structure at 1/16 of its length
     w = WORKLOADS["long_256k"].replace(T=16384, n_groups=16)
