@@ -230,8 +230,23 @@ gdn_status gdn_chunk_fold(const gdn_shape *shape, const void *k, const void *v, 
  *   fp32 or NULL (at least one of them non-NULL).
  * flags bit 0 (GDN_PREFIX_SPLIT_BF16): form the products from hi/lo bf16
  * halves on the bf16 matrix cores (about 1e-5 relative) instead of fp32
- * matrix-core products. */
+ * matrix-core products.
+ * With h_in given, n having a divisor s >= 3 near sqrt(n), and the blocked
+ * prefix expected to be faster for this (batch_heads, n) (a cost model of
+ * both forms' measured step latency and traffic: long chains over few rows),
+ * the prefix is blocked (depth 2 s + n / s sequential steps instead of n, the
+ * log-depth composition of the issue page, section "Status", and of the
+ * associative scan over gathered pairs in the code-review suggestion on the
+ * PR page, in two levels): the pairs of each block of s are composed into one
+ * pair, the sequential prefix runs over the blocks' pairs, and every block is
+ * replayed from its incoming state; h_in holds the intermediates.  The
+ * results agree with the sequential prefix to rounding.  flags bit 1
+ * (GDN_PREFIX_SEQUENTIAL) forces the one-pair-at-a-time prefix, bit 2
+ * (GDN_PREFIX_BLOCKED) the blocked one wherever such an s exists (both bits:
+ * GDN_ERR_SHAPE). */
 #define GDN_PREFIX_SPLIT_BF16 1
+#define GDN_PREFIX_SEQUENTIAL 2
+#define GDN_PREFIX_BLOCKED 4
 gdn_status gdn_compose_prefix(int32_t batch_heads, int32_t n, int32_t d_k, int32_t d_v,
                               const float *A, const float *Bm, const float *h_init,
                               float *h_in, float *h_final, int32_t flags, void *hip_stream);

@@ -24,7 +24,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdn.so")
 
 F32, BF16 = 0, 1
-PREFIX_SPLIT_BF16 = 1
+PREFIX_SPLIT_BF16, PREFIX_SEQUENTIAL, PREFIX_BLOCKED = 1, 2, 4
 STATUS = {0: "ok", -1: "null pointer", -2: "unsupported or inconsistent sizes",
           -3: "unsupported dtype", -4: "misaligned pointer", -5: "workspace too small",
           -6: "kernel launch failed"}
@@ -337,8 +337,9 @@ def chunk_fold(k, v, g, beta, n_groups, chunk=128, workspace=None, stream=None):
     return A, Bm
 
 
-def compose_prefix(A, Bm, h_init=None, split_bf16=False, want_h_in=True, stream=None):
-    """Exclusive prefix of affine pairs (gdn_compose_prefix).
+def compose_prefix(A, Bm, h_init=None, split_bf16=False, want_h_in=True, stream=None, form=None):
+    """Exclusive prefix of affine pairs (gdn_compose_prefix).  ``form``: None
+    lets the library choose, "sequential" or "blocked" force one.
     A [BH,n,d_k,d_k], Bm [BH,n,d_k,d_v] fp32; h_init [BH,d_k,d_v] or None.
     Returns (h_in [BH,n,d_k,d_v] or None, h_final [BH,d_k,d_v])."""
     BH, n, dk, _ = A.shape
@@ -351,7 +352,9 @@ def compose_prefix(A, Bm, h_init=None, split_bf16=False, want_h_in=True, stream=
     h_in = torch.empty((BH, n, dk, dv), dtype=torch.float32, device=dev) if want_h_in else None
     h_fin = torch.empty((BH, dk, dv), dtype=torch.float32, device=dev)
     st = lib().gdn_compose_prefix(BH, n, dk, dv, _ptr(A), _ptr(Bm), _ptr(h_init), _ptr(h_in),
-                                  _ptr(h_fin), PREFIX_SPLIT_BF16 if split_bf16 else 0,
+                                  _ptr(h_fin), (PREFIX_SPLIT_BF16 if split_bf16 else 0) |
+                                  {None: 0, "sequential": PREFIX_SEQUENTIAL,
+                                   "blocked": PREFIX_BLOCKED}[form],
                                   _stream(stream))
     _check(st, "gdn_compose_prefix")
     return h_in, h_fin

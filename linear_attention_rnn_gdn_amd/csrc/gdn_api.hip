@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <cstdlib>
 #include <mutex>
 
 #include "gdn.h"
@@ -212,20 +213,62 @@ gdn_status launch_walk_out(const FwdArgs &a, const Lx &x) {
   return check_launch();
 }
 
+// Pairs per block of the blocked prefix: the divisor of n nearest sqrt(n)
+// (at least 3: a block's slots hold its composed pair and incoming state), if
+// the blocked prefix is expected to be faster; 0 = the sequential prefix.
+// Both are modelled from their MI355X timings over 1..32 rows and 32..1024
+// pairs: the sequential prefix costs the larger of 2.75 us per pair (a chain
+// of dependent steps) and its traffic (A and B read, h_in written: 3 * 64 KB
+// per pair) at 2.1 TB/s; the blocked one the larger of its 2 s + n / s steps
+// (5.6 us each with split-bf16 products, 9 us with fp32 ones) and its
+// traffic (A and B read twice: 5 * 64 KB per pair) at 2.4 TB/s.
+// force: the blocked prefix whenever n has such a divisor.
+int prefix_block(int n, int BH, bool split, bool force) {
+  if (n < 9) return 0;
+  int s = 0;
+  for (int c = 3; c <= n / 3; ++c)
+    if (n % c == 0 && (s == 0 || std::abs(c * c - n) < std::abs(s * s - n))) s = c;
+  if (s == 0 || force) return s;
+  const double pair_bytes = (double)D * D * 4 * BH;
+  const double t_seq = std::max(n * 2.75e-6, 3 * pair_bytes * n / 2.1e12);
+  const double t_blk = std::max((2 * s + n / s) * (split ? 5.6e-6 : 9e-6), 5 * pair_bytes * n / 2.4e12);
+  return t_blk < t_seq ? s : 0;
+}
+
 gdn_status launch_prefix(int BH, int n, const float *A, const float *Bm, const float *h_init, float *h_in,
-                         float *h_final, bool split, const Lx &x) {
-  PrefixArgs p{BH, n, A, Bm, h_init, h_in, h_final};
-  const unsigned blocks = (unsigned)(D / 16) * BH;   // one workgroup per 16-column slice
+                         float *h_final, bool split, const Lx &x, int form = 0) {   // form: 0 chosen, 1 sequential, 2 blocked
   constexpr int NWS = 4;                              // waves per slice, 32 state rows each
-  if (split)
-    launch(prefix_kernel<P_SPLIT_AB, NWS>, dim3(blocks), dim3(64 * NWS), x, p);
-  else
-    launch(prefix_kernel<P_F32, NWS>, dim3(blocks), dim3(64 * NWS), x, p);
+  const int s = (h_in && form != 1) ? prefix_block(n, BH, split, form == 2) : 0;
+  if (s == 0) {
+    PrefixArgs p{BH, n, A, Bm, h_init, h_in, h_final};
+    const unsigned blocks = (unsigned)(D / 16) * BH;   // one workgroup per 16-column slice
+    if (split)
+      launch(prefix_kernel<P_SPLIT_AB, NWS>, dim3(blocks), dim3(64 * NWS), x, p);
+    else
+      launch(prefix_kernel<P_F32, NWS>, dim3(blocks), dim3(64 * NWS), x, p);
+    return check_launch();
+  }
+  // blocked: compose each block's pairs, the sequential prefix over the
+  // blocks' pairs (kept in the incoming-state slots), replay every block
+  // (the stage's timing events bound the three launches)
+  const int nb = n / s;
+  PairWalkArgs w{BH, n, s, A, Bm, h_in};
+  const size_t DD = (size_t)D * D;
+  PrefixArgs p{BH, nb, h_in + DD, h_in + 2 * DD, h_init, h_in, h_final, (long long)(s * DD), (long long)(n * DD)};
+  const Lx first{x.st, x.e0, nullptr}, mid{x.st}, last{x.st, nullptr, x.e1};
+  const unsigned units = (unsigned)((long)BH * nb), slices = (unsigned)(D / 16) * BH;
+  if (split) {
+    launch(pair_walk_kernel<P_SPLIT_AB, PW_COMPOSE>, dim3(2 * units), dim3(512), first, w);
+    launch(prefix_kernel<P_SPLIT_AB, NWS>, dim3(slices), dim3(64 * NWS), mid, p);
+    launch(pair_walk_kernel<P_SPLIT_AB, PW_REPLAY>, dim3(units), dim3(512), last, w);
+  } else {
+    launch(pair_walk_kernel<P_F32, PW_COMPOSE>, dim3(2 * units), dim3(512), first, w);
+    launch(prefix_kernel<P_F32, NWS>, dim3(slices), dim3(64 * NWS), mid, p);
+    launch(pair_walk_kernel<P_F32, PW_REPLAY>, dim3(units), dim3(512), last, w);
+  }
   return check_launch();
 }
 
-// A (optional): the affine map of the whole sequence, from the walk of the
-// augmented state [A | h] (one group only)
 template <int C, typename TI, int MODE>
 gdn_status run_fwd(const gdn_shape &s, int stages, const void *q, const void *k, const void *v, const float *g,
                    const float *beta, const float *h0, void *o, float *h_T, char *ws, hipStream_t st,
@@ -577,12 +620,15 @@ gdn_status gdn_compose_prefix(int32_t batch_heads, int32_t n, int32_t d_k, int32
                               const float *Bm, const float *h_init, float *h_in, float *h_final, int32_t flags,
                               void *hip_stream) {
   if (batch_heads < 1 || batch_heads > 65535 || n < 1 || d_k != D || d_v != D) return GDN_ERR_SHAPE;
+  if ((int64_t)batch_heads * n > (1 << 30)) return GDN_ERR_SHAPE;
   if (!A || !Bm || (!h_in && !h_final)) return GDN_ERR_NULL;
   for (const void *p : {(const void *)A, (const void *)Bm, (const void *)h_init, (const void *)h_in,
                         (const void *)h_final})
     if (misaligned(p)) return GDN_ERR_ALIGN;
+  if ((flags & GDN_PREFIX_SEQUENTIAL) && (flags & GDN_PREFIX_BLOCKED)) return GDN_ERR_SHAPE;
+  const int form = (flags & GDN_PREFIX_SEQUENTIAL) ? 1 : (flags & GDN_PREFIX_BLOCKED) ? 2 : 0;
   return launch_prefix(batch_heads, n, A, Bm, h_init, h_in, h_final, (flags & GDN_PREFIX_SPLIT_BF16) != 0,
-                       Lx{reinterpret_cast<hipStream_t>(hip_stream)});
+                       Lx{reinterpret_cast<hipStream_t>(hip_stream)}, form);
 }
 
 gdn_status gdn_chunk_transform(const gdn_shape *s, const void *k, const void *v, const float *g,

@@ -1550,6 +1550,9 @@ struct PrefixArgs {
   int BH, n;
   const float *A, *Bm, *h_init;
   float *h_in, *h_final;
+  // element strides (floats) between consecutive pairs / incoming states of
+  // a row and between rows; 0 = contiguous [BH, n, D, D]
+  long long js, bs;
 };
 
 template <int PREC, int NWS>
@@ -1575,6 +1578,7 @@ __global__ __launch_bounds__(64 * NWS) void prefix_kernel(PrefixArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       h[t][i] = a.h_init ? a.h_init[(bh * D + 16 * (m0 + t) + 4 * g + i) * D + c0 + lr] : 0.f;
+  const size_t js_ = a.js ? (size_t)a.js : (size_t)D * D, bs_ = a.bs ? (size_t)a.bs : (size_t)a.n * D * D;
 
   // fragment p = (own row tile t, k-block kb) of A_j: row 16(m0+t) + lr,
   // columns 32kb + 4g .. +3 and 32kb + 16 + 4g .. +3
@@ -1582,11 +1586,11 @@ __global__ __launch_bounds__(64 * NWS) void prefix_kernel(PrefixArgs a) {
     float4 x0, x1;
   };
   auto load = [&](size_t j, int p) -> Run2 {
-    const float *row = a.A + ((bh * a.n + j) * D + 16 * (m0 + p / KB) + lr) * D + 32 * (p % KB) + 4 * g;
+    const float *row = a.A + (bh * bs_ + j * js_) + (size_t)(16 * (m0 + p / KB) + lr) * D + 32 * (p % KB) + 4 * g;
     return Run2{*reinterpret_cast<const float4 *>(row), *reinterpret_cast<const float4 *>(row + 16)};
   };
   auto load_b = [&](size_t j, f32x4 (&bq)[MHW]) {
-    const float *B = a.Bm + (bh * a.n + j) * D * D + c0 + lr;
+    const float *B = a.Bm + (bh * bs_ + j * js_) + c0 + lr;
 #pragma unroll
     for (int t = 0; t < MHW; ++t)
 #pragma unroll
@@ -1608,7 +1612,7 @@ __global__ __launch_bounds__(64 * NWS) void prefix_kernel(PrefixArgs a) {
       xh[P][w][lane] = make_frag<PK::b>(x);
     }
     if (a.h_in) {
-      float *dst = a.h_in + ((bh * a.n + j) * D) * D + c0 + lr;
+      float *dst = a.h_in + (bh * bs_ + j * js_) + c0 + lr;
 #pragma unroll
       for (int t = 0; t < MHW; ++t)
 #pragma unroll
@@ -1643,6 +1647,180 @@ __global__ __launch_bounds__(64 * NWS) void prefix_kernel(PrefixArgs a) {
     for (int t = 0; t < MHW; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) a.h_final[(bh * D + 16 * (m0 + t) + 4 * g + i) * D + c0 + lr] = h[t][i];
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Blocked (two-level, log-depth in the block size) exclusive prefix of affine
+// pairs: the pairs of every block of s consecutive groups are composed into
+// one pair (COMPOSE), the sequential prefix runs over the blocks' pairs, and
+// every block replays its own pairs from its incoming state (REPLAY).  Both
+// block passes are walks of a state through the pairs' maps,
+//   state <- A_j state + B_j,
+// COMPOSE on the augmented state [X | Y] from [I | 0] (X the product of the
+// block's A, Y its composed B; the composition law (A2,B2) o (A1,B1) =
+// (A2 A1, A2 B1 + B2) of "GatedDeltaNet does not support
+// ici_context_parallelism", section "The recurrence is affine, so it can be
+// parallelized"), REPLAY on the state h from the block's incoming state,
+// writing the state entering every pair (the exclusive prefix).  One
+// workgroup of eight waves per (row bh, block) and 128 state columns (two for
+// COMPOSE: X and Y); A_j, read once per workgroup and split once into
+// matrix-core operand fragments in LDS (two buffers: the next pair's arrive
+// during this pair's products), is shared by every wave, each holding 16
+// columns of the state.
+//
+// The blocked prefix keeps its intermediates in the incoming-state array
+// itself: for block beta (pairs beta s .. beta s + s - 1 of a row, s >= 3),
+// slot beta s + 1 holds the block's composed A, slot beta s + 2 its composed
+// B, and slot beta s the block's incoming state (written by the sequential
+// prefix, read by REPLAY, which then writes every slot of the block).
+constexpr int PW_COMPOSE = 0, PW_REPLAY = 1;
+struct PairWalkArgs {
+  int BH, J, s;               // rows, pairs per row, pairs per block
+  const float *A, *Bm;        // [BH, J, D, D]
+  float *h_in;                // [BH, J, D, D]: intermediates and the result
+};
+
+template <int PREC, int KIND>
+__global__ __launch_bounds__(512) void pair_walk_kernel(PairWalkArgs a) {
+  using PK = PolicyKinds<PREC>;
+  using AF = Frag<PK::a>;
+  using SF = Frag<PK::b>;
+  static_assert(PK::a == PK::b && (PK::a == F_SPLIT || PK::a == F_F32), "fp32-accurate pair products");
+  constexpr int MH = D / 16, KB = D / 32, NF = MH * KB;   // state row tiles, k-blocks, A fragments
+  constexpr int NSL = 1;                                   // 16-column slices per wave
+  constexpr int PER = NF * 64 / 512;                       // (fragment, lane) items staged per thread
+  __shared__ __align__(16) char buf[2][NF * 2048];
+  const int nblk = a.J / a.s;
+  int unit, part;   // part: the 128 columns of the state this workgroup holds
+  xcd_unit(blockIdx.x, KIND == PW_COMPOSE ? 2 : 1, a.BH * nblk, unit, part);
+  const size_t bh = unit / nblk;
+  const int blk = unit % nblk, j0 = blk * a.s;
+  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, g = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const size_t DD = (size_t)D * D;
+  float *row = a.h_in + bh * a.J * DD;   // this row's slots
+
+  // state tiles st[sl][m]: rows 16m + 4g + i, column c(sl) + lr of the
+  // state (COMPOSE: columns 0..255 of [X | Y]; REPLAY: 0..127 of h)
+  f32x4 st[NSL][MH];
+  auto col0 = [&](int sl) { return D * part + 16 * (NSL * w + sl); };
+#pragma unroll
+  for (int sl = 0; sl < NSL; ++sl)
+#pragma unroll
+    for (int m = 0; m < MH; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * m + 4 * g + i, c = col0(sl) + lr;
+        st[sl][m][i] = KIND == PW_COMPOSE ? (c == r ? 1.f : 0.f) : row[(size_t)j0 * DD + (size_t)r * D + c];
+      }
+  // stage A_j: item (fragment f, lane ln) holds A[16m + lr'][32kb + kk(g', jj)]
+  float ax[PER][8];
+  auto load_a = [&](int j) {
+    const float *Aj = a.A + (bh * a.J + j) * DD;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int it = tid + 512 * u, f = it / 64, ln = it % 64, m = f / KB, kb = f % KB;
+      const float *p = Aj + (size_t)(16 * m + (ln & 15)) * D + 32 * kb + 4 * (ln >> 4);
+      const float4 x0 = *reinterpret_cast<const float4 *>(p), x1 = *reinterpret_cast<const float4 *>(p + 16);
+      ax[u][0] = x0.x; ax[u][1] = x0.y; ax[u][2] = x0.z; ax[u][3] = x0.w;
+      ax[u][4] = x1.x; ax[u][5] = x1.y; ax[u][6] = x1.z; ax[u][7] = x1.w;
+    }
+  };
+  auto put_a = [&](char *b) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int it = tid + 512 * u, f = it / 64, ln = it % 64;
+      char *d = b + f * 2048 + ln * 16;
+      if constexpr (PK::a == F_SPLIT) {
+        bf16x8 hi, lo;
+        to_bf16x8_split(ax[u], hi, lo);
+        *reinterpret_cast<bf16x8 *>(d) = hi;
+        *reinterpret_cast<bf16x8 *>(d + 1024) = lo;
+      } else {
+        *reinterpret_cast<float4 *>(d) = float4{ax[u][0], ax[u][1], ax[u][2], ax[u][3]};
+        *reinterpret_cast<float4 *>(d + 1024) = float4{ax[u][4], ax[u][5], ax[u][6], ax[u][7]};
+      }
+    }
+  };
+  auto afrag = [&](const char *b, int f) -> AF {
+    AF x;
+    const char *p = b + f * 2048 + lane * 16;
+    if constexpr (PK::a == F_SPLIT) {
+      x.hi = *reinterpret_cast<const bf16x8 *>(p);
+      x.lo = *reinterpret_cast<const bf16x8 *>(p + 1024);
+    } else {
+      const float4 x0 = *reinterpret_cast<const float4 *>(p), x1 = *reinterpret_cast<const float4 *>(p + 1024);
+      x.v[0] = x0.x; x.v[1] = x0.y; x.v[2] = x0.z; x.v[3] = x0.w;
+      x.v[4] = x1.x; x.v[5] = x1.y; x.v[6] = x1.z; x.v[7] = x1.w;
+    }
+    return x;
+  };
+  // B_j for this wave's columns that take it (COMPOSE: the Y half; REPLAY: all)
+  const bool takes_b = KIND == PW_REPLAY || col0(0) >= D;
+  f32x4 bq[NSL][MH];
+  auto load_b = [&](int j) {
+    const float *Bj = a.Bm + (bh * a.J + j) * DD;
+#pragma unroll
+    for (int sl = 0; sl < NSL; ++sl)
+#pragma unroll
+      for (int m = 0; m < MH; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          bq[sl][m][i] = takes_b ? Bj[(size_t)(16 * m + 4 * g + i) * D + (col0(sl) + lr) % D] : 0.f;
+  };
+
+  load_a(j0);
+  put_a(buf[0]);
+  __syncthreads();
+  for (int t = 0; t < a.s; ++t) {
+    const int j = j0 + t;
+    const bool more = t + 1 < a.s;
+    if (more) load_a(j + 1);
+    load_b(j);
+    if (KIND == PW_REPLAY) {   // the state entering pair j
+#pragma unroll
+      for (int m = 0; m < MH; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) row[(size_t)j * DD + (size_t)(16 * m + 4 * g + i) * D + col0(0) + lr] = st[0][m][i];
+    }
+    const char *cur = buf[t & 1];
+    SF sb[NSL][KB];
+#pragma unroll
+    for (int sl = 0; sl < NSL; ++sl)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const float x[8] = {st[sl][2 * kb][0], st[sl][2 * kb][1], st[sl][2 * kb][2], st[sl][2 * kb][3],
+                            st[sl][2 * kb + 1][0], st[sl][2 * kb + 1][1], st[sl][2 * kb + 1][2], st[sl][2 * kb + 1][3]};
+        sb[sl][kb] = make_frag<PK::b>(x);
+      }
+#pragma unroll
+    for (int m = 0; m < MH; ++m) {
+      f32x4 acc[NSL];
+#pragma unroll
+      for (int sl = 0; sl < NSL; ++sl) acc[sl] = bq[sl][m];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const AF af = afrag(cur, m * KB + kb);
+#pragma unroll
+        for (int sl = 0; sl < NSL; ++sl) mma(acc[sl], af, sb[sl][kb]);
+      }
+#pragma unroll
+      for (int sl = 0; sl < NSL; ++sl) st[sl][m] = acc[sl];
+    }
+    if (more) put_a(buf[(t + 1) & 1]);
+    __syncthreads();
+  }
+  if (KIND == PW_COMPOSE) {   // X -> slot j0 + 1, Y -> slot j0 + 2
+#pragma unroll
+    for (int sl = 0; sl < NSL; ++sl) {
+      const int c = col0(sl) + lr;
+      float *dst = row + (size_t)(j0 + (c < D ? 1 : 2)) * DD + c % D;
+#pragma unroll
+      for (int m = 0; m < MH; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[(size_t)(16 * m + 4 * g + i) * D] = st[sl][m][i];
+    }
   }
 }
 

@@ -56,6 +56,9 @@ int main() {
   expect(gdn_chunk_transform(&s, ok, ok, fk, fk, nullptr, nullptr, fo, fo, nullptr), GDN_ERR_NULL, "transform null G");
   expect(gdn_compose_prefix(4, 8, 128, 128, fk, fk, nullptr, nullptr, nullptr, 0, nullptr), GDN_ERR_NULL, "prefix outs");
   expect(gdn_compose_prefix(4, 8, 64, 128, fk, fk, nullptr, fo, nullptr, 0, nullptr), GDN_ERR_SHAPE, "prefix d_k");
+  expect(gdn_compose_prefix(4, 8, 128, 128, fk, fk, nullptr, fo, nullptr, GDN_PREFIX_SEQUENTIAL | GDN_PREFIX_BLOCKED,
+                            nullptr),
+         GDN_ERR_SHAPE, "prefix forms");
   expect(gdn_compose_prefix(4, 8, 128, 128, reinterpret_cast<const float *>(odd), fk, nullptr, fo, nullptr, 0, nullptr),
          GDN_ERR_ALIGN, "prefix misaligned");
   expect(gdn_chunk_fwd_affine(&s, ok, ok, ok, fk, fk, nullptr, ok, nullptr, nullptr, ok, bytes, nullptr), GDN_ERR_NULL,

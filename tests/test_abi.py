@@ -136,6 +136,8 @@ def test_entry_points_reject_bad_arguments_without_launching(gdn):
     assert L.gdn_compose_prefix(4, 8, 64, 128, ok, ok, null, ok, null, 0, null) == -2
     assert L.gdn_compose_prefix(0, 8, 128, 128, ok, ok, null, ok, null, 0, null) == -2
     assert L.gdn_compose_prefix(4, 8, 128, 128, odd, ok, null, ok, null, 0, null) == -4
+    # sequential and blocked forced together
+    assert L.gdn_compose_prefix(4, 8, 128, 128, ok, ok, null, ok, null, 6, null) == -2
     assert L.gdn_validate(None) == -1
     # the forward with the affine map: one group only, A required
     assert L.gdn_chunk_fwd_affine(ctypes.byref(s), ok, ok, ok, ok, ok, null, ok, null, null, ok, ws, null) == -1

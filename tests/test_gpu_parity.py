@@ -346,6 +346,39 @@ def test_compose_prefix_matches_oracle(gdn, split):
     assert _err(h_fin.cpu().numpy(), r_fin) <= tol * _rms(r_fin)
 
 
+@pytest.mark.parametrize("n", [35, 37, 48, 64, 256])
+@pytest.mark.parametrize("split", [False, True])
+def test_blocked_prefix_matches_oracle(gdn, n, split):
+    # Three rows of 35..256 pairs, the blocked prefix forced (each block of
+    # ~sqrt(n) pairs composed, the prefix over the blocks, every block
+    # replayed) -- blocks of 5 (n = 35), 6 (48), 8 (64) and 16 (256) pairs;
+    # 37 pairs (prime) have no blocks and take the sequential prefix.
+    # Against the oracle's one-pair-at-a-time prefix, and against the
+    # library's sequential one (GDN_PREFIX_SEQUENTIAL)
+    BH = 3
+    gen = torch.Generator().manual_seed(100 + n)
+    A = (torch.randn(BH, n, 128, 128, generator=gen) * (0.95 / 128 ** 0.5)).float()
+    Bm = torch.randn(BH, n, 128, 128, generator=gen).float()
+    h0 = torch.randn(BH, 128, 128, generator=gen).float()
+    h_in, h_fin = gdn.compose_prefix(A.cuda(), Bm.cuda(), h0.cuda(), split_bf16=split, form="blocked")
+    s_in, s_fin = gdn.compose_prefix(A.cuda(), Bm.cuda(), h0.cuda(), split_bf16=split, form="sequential")
+    c_in, c_fin = gdn.compose_prefix(A.cuda(), Bm.cuda(), h0.cuda(), split_bf16=split)
+    torch.cuda.synchronize()
+    # the chosen form is one of the two, bit for bit
+    assert torch.equal(c_in, h_in) or torch.equal(c_in, s_in)
+    r_in, r_fin = oracle.prefix(A.numpy(), Bm.numpy(), h0.numpy())
+    # fp32: as for nine pairs.  Split bf16: each step adds rounding of
+    # relative size ~2^-16 (the dropped lo*lo terms); along a chain with
+    # contraction 0.95 those add up to about sqrt(1 / (1 - 0.95^2)) ~ 3.2
+    # times one step's, and the max runs over ~30x more elements than the
+    # nine-pair case's 1e-4 -> 5e-4
+    tol = 5e-4 if split else 2e-5
+    for name, got, ref in (("h_in", h_in, r_in), ("h_final", h_fin, r_fin), ("h_in seq", s_in, r_in)):
+        e = _err(got.cpu().numpy(), ref)
+        print(f"  {name}: max-abs {e:.3e}  limit {tol * _rms(ref):.3e}", flush=True)
+        assert e <= tol * _rms(ref)
+
+
 @pytest.mark.parametrize("ng", [2, 4, 16])
 def test_group_count_invariance(gdn, ng):
     w = WORKLOADS["qwen3next_8b_layer"].replace(T=2048)
