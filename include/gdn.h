@@ -295,6 +295,38 @@ gdn_status gdn_chunk_bwd_state(const gdn_shape *shape, const void *q, const void
                                float *dh_chunks, float *dh0, void *ws, size_t ws_bytes,
                                void *hip_stream);
 
+/* The chunked backward's gradients: of L = sum_t <o_t, dO_t> + <h_T, dh_T>
+ * with respect to q, k, v, g, beta and h0, for the forward of gdn_chunk_fwd
+ * ("Fuse the Gated Delta Net inter-chunk scan into a Pallas TPU kernel",
+ * section "Changes": the scan's backward walks the chunks in reverse, the
+ * triangular inverse has the analytic backward dS = -(T^T dT T^T) on the
+ * strict lower triangle; section "Tests": every gradient, with a non-zero
+ * initial state and a final-state cotangent).  Four passes on the stream:
+ * the intra-chunk transform (G, T, W, U in fp32); the forward's incoming
+ * state of every chunk; the reverse walk's state cotangents (as
+ * gdn_chunk_bwd_state); then, per chunk and value head, the adjoint of each
+ * line of the chunk's forward in reverse order.
+ *   q, k [B, T, H_qk, d_k], v [B, T, H_v, d_v] in shape->dtype; g, beta
+ *   [B, T, H_v] fp32; h0 [B, H_v, d_k, d_v] fp32 or NULL (zero); dO
+ *   [B, T, H_v, d_v] fp32; dh_T [B, H_v, d_k, d_v] fp32 or NULL (zero).
+ *   Outputs (all fp32, caller-allocated, 16-byte aligned): dq, dk
+ *   [B, T, H_qk, d_k] (the sum over the value heads that read each key head),
+ *   dv [B, T, H_v, d_v], dg, dbeta [B, T, H_v], dh0 [B, H_v, d_k, d_v] or
+ *   NULL.
+ *   ws: gdn_workspace_size_bwd_grads(shape) bytes (about 5 d_k x d_v + 2
+ *   chunk x (chunk + d_v) floats per chunk and value head, plus a fixed
+ *   scratch of at most 512 slots of 9 chunk x d_v + 7 chunk^2 floats).
+ * shape->n_groups must be 0 or 1 (GDN_ERR_SHAPE otherwise); o_dtype is not
+ * used.  Products follow the forward's precision policy (fp32 inputs: fp32
+ * matrix-core products; bf16 inputs: hi/lo split bf16 products).  T = 0:
+ * dh0 = dh_T (or zero); nothing else is written.  Other errors as for
+ * gdn_chunk_fwd. */
+gdn_status gdn_workspace_size_bwd_grads(const gdn_shape *shape, size_t *bytes);
+gdn_status gdn_chunk_bwd(const gdn_shape *shape, const void *q, const void *k, const void *v,
+                         const float *g, const float *beta, const float *h0, const float *dO,
+                         const float *dh_T, float *dq, float *dk, float *dv, float *dg,
+                         float *dbeta, float *dh0, void *ws, size_t ws_bytes, void *hip_stream);
+
 /* gdn_chunk_fwd for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
  * Arguments, checks and results are those of gdn_chunk_fwd, without the

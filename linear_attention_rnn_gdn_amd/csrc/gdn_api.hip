@@ -7,6 +7,7 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <cstdlib>
 #include <mutex>
@@ -742,6 +743,108 @@ gdn_status run_bwd_state(const gdn_shape &s, const void *q, const void *k, const
   return check_launch();
 }
 
+// The full chunked backward: prep's transform form (G, T, W, U), the
+// forward's incoming states, the reverse walk's state cotangents, then the
+// chunk gradients on a persistent grid of kGradSlots workgroups, each with
+// its scratch slot; dq, dk per value head are summed per key head last.
+constexpr int kGradSlots = 512;
+struct GradLayout {
+  size_t G, Tm, W, U, ddh, dh, hs, dqv, dkv, scratch, total;
+};
+GradLayout layout_grads(const gdn_shape &s) {
+  const size_t BH = (size_t)s.B * s.H_v, N = chunks_of(s), C = s.chunk, DD = (size_t)D * D;
+  const size_t units = BH * N;
+  GradLayout L{};
+  size_t off = 0;
+  L.G = off;   off += align_up(BH * N * C * 4);
+  L.Tm = off;  off += align_up(BH * N * C * C * 4);
+  L.W = off;   off += align_up(BH * N * C * D * 4);
+  L.U = off;   off += align_up(BH * N * C * D * 4);
+  L.ddh = off; off += align_up(BH * N * DD * 4);
+  L.dh = off;  off += align_up(BH * N * DD * 4);
+  L.hs = off;  off += align_up(BH * N * DD * 4);
+  if (s.H_v != s.H_qk) {
+    L.dqv = off; off += align_up((size_t)s.B * s.T * s.H_v * D * 4);
+    L.dkv = off; off += align_up((size_t)s.B * s.T * s.H_v * D * 4);
+  }
+  const size_t slots = std::min(units, (size_t)kGradSlots);
+  const size_t slot = C == 128 ? grad_slot_floats<128>() : grad_slot_floats<64>();
+  L.scratch = off; off += align_up(slots * slot * 4);
+  L.total = off;
+  return L;
+}
+
+template <int C, typename TI, int MODE>
+gdn_status run_bwd_grads(const gdn_shape &s, const void *q, const void *k, const void *v, const float *g,
+                         const float *beta, const float *h0, const float *dO, const float *dh_T, float *dq, float *dk,
+                         float *dv, float *dg, float *dbeta, float *dh0, char *ws, hipStream_t st) {
+  const GradLayout L = layout_grads(s);
+  const int N = chunks_of(s);
+  const bool rag = s.T % C != 0;
+  FwdArgs a = base_args(s);
+  a.k = k; a.v = v; a.g = g; a.beta = beta;
+  a.G = reinterpret_cast<float *>(ws + L.G);
+  a.Tm = reinterpret_cast<float *>(ws + L.Tm);
+  a.W = ws + L.W;
+  a.U = reinterpret_cast<float *>(ws + L.U);
+  GDN_TRY((launch_prep<C, TI, MODE, false>(a, Lx{st})));
+  const unsigned rowsBH = (unsigned)(s.B * s.H_v);
+  StatesArgs sa{s.B, s.T, s.H_qk, s.H_v, N, k, a.G, reinterpret_cast<const float *>(a.W), a.U, h0,
+                reinterpret_cast<float *>(ws + L.hs)};
+  if (rag)
+    hipLaunchKernelGGL((fwd_states_kernel<C, TI, MODE, true>), dim3(rowsBH), dim3(512), 0, st, sa);
+  else
+    hipLaunchKernelGGL((fwd_states_kernel<C, TI, MODE, false>), dim3(rowsBH), dim3(512), 0, st, sa);
+  GDN_TRY(check_launch());
+  BwdArgs b{};
+  b.B = s.B; b.T = s.T; b.Hqk = s.H_qk; b.Hv = s.H_v; b.N = N;
+  b.q = q; b.k = k; b.dO = dO;
+  b.G = a.G; b.W = reinterpret_cast<const float *>(a.W);
+  b.ddh = reinterpret_cast<float *>(ws + L.ddh);
+  b.dhT = dh_T; b.dh = reinterpret_cast<float *>(ws + L.dh); b.dh0 = dh0;
+  const unsigned units = (unsigned)((long)N * s.B * s.H_v);
+  if (rag) {
+    hipLaunchKernelGGL((bwd_ddh_kernel<C, TI, MODE, true>), dim3(units), dim3(256), 0, st, a, b);
+    hipLaunchKernelGGL((bwd_walk_kernel<C, TI, MODE, true>), dim3(rowsBH), dim3(512), 0, st, b);
+  } else {
+    hipLaunchKernelGGL((bwd_ddh_kernel<C, TI, MODE, false>), dim3(units), dim3(256), 0, st, a, b);
+    hipLaunchKernelGGL((bwd_walk_kernel<C, TI, MODE, false>), dim3(rowsBH), dim3(512), 0, st, b);
+  }
+  GDN_TRY(check_launch());
+  const bool per_v = s.H_v != s.H_qk;
+  GradArgs ga{};
+  ga.B = s.B; ga.T = s.T; ga.Hqk = s.H_qk; ga.Hv = s.H_v; ga.N = N; ga.units = (int)units;
+  ga.q = q; ga.k = k; ga.v = v; ga.beta = beta; ga.dO = dO;
+  ga.G = a.G; ga.Tm = a.Tm; ga.W = reinterpret_cast<const float *>(a.W); ga.U = a.U;
+  ga.hs = reinterpret_cast<const float *>(ws + L.hs); ga.dh = b.dh; ga.dhT = dh_T;
+  ga.dq = per_v ? reinterpret_cast<float *>(ws + L.dqv) : dq;
+  ga.dk = per_v ? reinterpret_cast<float *>(ws + L.dkv) : dk;
+  ga.per_value_head = per_v;
+  ga.dv = dv; ga.dg = dg; ga.dbeta = dbeta;
+  ga.scratch = reinterpret_cast<float *>(ws + L.scratch);
+  const unsigned grid = std::min(units, (unsigned)kGradSlots);
+  if (rag)
+    hipLaunchKernelGGL((bwd_chunk_kernel<C, TI, MODE, true>), dim3(grid), dim3(512), 0, st, ga);
+  else
+    hipLaunchKernelGGL((bwd_chunk_kernel<C, TI, MODE, false>), dim3(grid), dim3(512), 0, st, ga);
+  GDN_TRY(check_launch());
+  if (per_v) {
+    const size_t rows = (size_t)s.B * s.T;
+    hipLaunchKernelGGL(sum_value_heads_kernel, dim3(1024), dim3(256), 0, st, ga.dq, dq, rows, s.H_qk, s.H_v / s.H_qk);
+    hipLaunchKernelGGL(sum_value_heads_kernel, dim3(1024), dim3(256), 0, st, ga.dk, dk, rows, s.H_qk, s.H_v / s.H_qk);
+    GDN_TRY(check_launch());
+  }
+  return GDN_OK;
+}
+
+struct BwdGradCall {
+  const gdn_shape &s; const void *q, *k, *v; const float *g, *beta, *h0, *dO, *dh_T;
+  float *dq, *dk, *dv, *dg, *dbeta, *dh0; char *w; hipStream_t st;
+  template <int C, typename TI, int MODE> gdn_status run() {
+    return run_bwd_grads<C, TI, MODE>(s, q, k, v, g, beta, h0, dO, dh_T, dq, dk, dv, dg, dbeta, dh0, w, st);
+  }
+};
+
 struct BwdStateCall {
   const gdn_shape &s; const void *q, *k; const float *g, *beta, *dO, *dh_T; float *dh, *dh0; char *w; hipStream_t st;
   template <int C, typename TI, int MODE> gdn_status run() {
@@ -759,6 +862,38 @@ gdn_status gdn_workspace_size_bwd(const gdn_shape *s, size_t *bytes) {
   if (s->n_groups > 1) return GDN_ERR_SHAPE;
   *bytes = layout_bwd(*s).total;
   return GDN_OK;
+}
+
+gdn_status gdn_workspace_size_bwd_grads(const gdn_shape *s, size_t *bytes) {
+  if (!bytes) return GDN_ERR_NULL;
+  GDN_TRY(gdn_validate(s));
+  if (s->n_groups > 1) return GDN_ERR_SHAPE;
+  *bytes = layout_grads(*s).total;
+  return GDN_OK;
+}
+
+gdn_status gdn_chunk_bwd(const gdn_shape *s, const void *q, const void *k, const void *v, const float *g,
+                         const float *beta, const float *h0, const float *dO, const float *dh_T, float *dq,
+                         float *dk, float *dv, float *dg, float *dbeta, float *dh0, void *ws, size_t ws_bytes,
+                         void *hip_stream) {
+  GDN_TRY(gdn_validate(s));
+  if (s->n_groups > 1) return GDN_ERR_SHAPE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+  for (const void *p : {(const void *)h0, (const void *)dh_T, (const void *)dh0})
+    if (misaligned(p)) return GDN_ERR_ALIGN;
+  if (s->T == 0) {   // no tokens: the cotangent of h0 is that of h_T
+    if (!dh0) return GDN_OK;
+    hipLaunchKernelGGL(copy_state_kernel, dim3(256), dim3(256), 0, st, dh_T, dh0, (size_t)s->B * s->H_v * D * D);
+    return check_launch();
+  }
+  if (!q || !k || !v || !g || !beta || !dO || !dq || !dk || !dv || !dg || !dbeta || !ws) return GDN_ERR_NULL;
+  for (const void *p : {(const void *)q, (const void *)k, (const void *)v, (const void *)g, (const void *)beta,
+                        (const void *)dO, (const void *)dq, (const void *)dk, (const void *)dv, (const void *)dg,
+                        (const void *)dbeta, (const void *)ws})
+    if (misaligned(p)) return GDN_ERR_ALIGN;
+  if (ws_bytes < layout_grads(*s).total) return GDN_ERR_WORKSPACE;
+  BwdGradCall f{*s, q, k, v, g, beta, h0, dO, dh_T, dq, dk, dv, dg, dbeta, dh0, reinterpret_cast<char *>(ws), st};
+  return dispatch(*s, f);
 }
 
 gdn_status gdn_chunk_bwd_state(const gdn_shape *s, const void *q, const void *k, const float *g,

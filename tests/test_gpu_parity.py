@@ -552,6 +552,44 @@ def test_bwd_state_matches_oracle(gdn, dtype, C, B, Hqk, Hv, T):
     assert torch.count_nonzero(dhz) == 0 and torch.count_nonzero(dh0z) == 0
 
 
+@pytest.mark.parametrize("dtype,C,B,Hqk,Hv,T", [
+    ("f32", 64, 1, 1, 2, 200),       # fp32, partial last chunk, two value heads per key head
+    ("bf16", 128, 1, 2, 4, 300),     # chunk 128, partial last chunk
+    ("bf16", 64, 2, 1, 1, 128),      # whole chunks, two batch rows
+    ("bf16", 64, 1, 2, 2, 50),       # shorter than one chunk
+])
+def test_bwd_grads_match_oracle(gdn, dtype, C, B, Hqk, Hv, T):
+    # the full backward (gdn_chunk_bwd): dq, dk, dv, dg, dbeta, dh0 against
+    # the oracle's per-token reverse pass of the rule (oracle/backward.py:
+    # bwd, pinned by finite differences), with a non-zero h0 and dh_T.  Bars
+    # relative to the RMS of each oracle gradient: fp32 as for the forward;
+    # bf16 inputs 1e-3 -- unlike the forward's bf16 W x h products, every
+    # product of the backward takes its fp32 operands as hi/lo bf16 halves
+    # (about 2^-16 relative each), chained through about ten products and
+    # the two walks
+    from oracle import backward
+    tol = {"f32": 1e-4, "bf16": 1e-3}[dtype]
+
+    w = WORKLOADS["tiny"].replace(T=T, B=B, Hqk=Hqk, Hv=Hv, chunk=C, dtype=dtype, h0_std=0.05)
+    x = make_inputs(w, device="cuda", seed=T + 3 * Hv + B)
+    gen = torch.Generator().manual_seed(T + 11)
+    dO = torch.randn((B, T, Hv, 128), generator=gen).to("cuda")
+    dhT = (torch.randn((B, Hv, 128, 128), generator=gen) * 0.1).to("cuda")
+    got = gdn.chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], dO, h0=x["h0"], dh_T=dhT, chunk=C)
+    torch.cuda.synchronize()
+    ref = backward.bwd(*[_cpu(x[kk]) for kk in ("q", "k", "v", "g", "beta", "h0")], do=_cpu(dO), dhT=_cpu(dhT))
+    for name in ("dq", "dk", "dv", "dg", "dbeta", "dh0"):
+        r = ref[name]
+        e = _err(got[name].cpu().numpy(), r)
+        print(f"  {name}: max-abs {e:.3e}  limit {tol * _rms(r):.3e}", flush=True)
+        assert e <= tol * _rms(r), name
+    # no cotangents: every gradient zero
+    z = gdn.chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], torch.zeros_like(dO), h0=x["h0"], chunk=C)
+    torch.cuda.synchronize()
+    for name in ("dq", "dk", "dv", "dg", "dbeta", "dh0"):
+        assert torch.count_nonzero(z[name]) == 0, name
+
+
 def test_long_sequence_reduced(gdn):
     # the long-sequence workload's shape and group structure at 1/16 of its length
     w = WORKLOADS["long_256k"].replace(T=16384, n_groups=16)
