@@ -60,6 +60,85 @@ def algorithmic(w, o_bytes=4):
     return flops, nbytes
 
 
+def bwd_algorithmic(w):
+    """FLOPs and HBM bytes of one backward call (gdn_chunk_bwd).  FLOPs: the
+    products of the chunked backward per chunk and value head -- the
+    intra-chunk transform (K K^T, the triangular inverse, W and U), the
+    forward-state walk (W h, K_g^T X), the reverse walk and its chunk term
+    (K dh, W^T X, Q K^T, P W, Qeff^T dO) and the chunk gradients (the adjoint
+    of every line of the chunk's forward: 5 products of C x d x d, 12 of
+    C x C x d, 2 of C x C x C) -- counted dense, as launched.  Bytes: the
+    inputs and cotangents read once, the gradients written once."""
+    C, d = w.chunk, w.dk
+    N = -(-w.T // C)
+    units = w.B * w.Hv * N
+    cdd, ccd, ccc = 2 * C * d * d, 2 * C * C * d, 2 * C * C * C
+    per = (ccd / 2 + ccc / 6 + 2 * ccd) + 2 * cdd + (3 * cdd + 2 * ccd) + (5 * cdd + 12 * ccd + 2 * ccc)
+    flops = units * per
+    tok = w.B * w.T
+    s = 2 if w.dtype == "bf16" else 4
+    nbytes = tok * (2 * w.Hqk * d * s + w.Hv * d * s + 8 * w.Hv + w.Hv * d * 4)      # q, k, v, g, beta, dO
+    nbytes += tok * (2 * w.Hqk * d * 4 + w.Hv * d * 4 + 8 * w.Hv)                    # dq, dk, dv, dg, dbeta
+    nbytes += w.B * w.Hv * d * d * 4 * 3                                              # h0, dh_T, dh0
+    return flops, nbytes
+
+
+def measure_backward(w, x, steps, warmup, torch, gdn, with_cpu=True):
+    """Time gdn_chunk_bwd on the workload's inputs (random dO and dh_T), as
+    the forward: median of `steps` calls after a cache-evicting write, and
+    back to back."""
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    dO = torch.randn((w.B, w.T, w.Hv, w.dv), generator=gen, device="cuda")
+    dhT = torch.randn((w.B, w.Hv, w.dk, w.dv), generator=gen, device="cuda") * 0.1
+    shape = gdn.make_shape(w.B, w.T, w.Hqk, w.Hv, w.dk, w.dv, w.chunk, 0, x["k"].dtype, torch.float32)
+    ws = torch.empty(gdn.workspace_size_bwd_grads(shape), dtype=torch.uint8, device="cuda")
+    out = gdn.chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], dO, h0=x["h0"], dh_T=dhT, chunk=w.chunk,
+                        workspace=ws)
+
+    def step():
+        gdn.chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], dO, h0=x["h0"], dh_T=dhT, chunk=w.chunk,
+                      workspace=ws, out=out)
+    tm = time_steps(step, steps, warmup)
+    flops, nbytes = bwd_algorithmic(w)
+    t = tm["cold"] * 1e-3
+    res = {"workload": w.name, "ms_per_step": tm["cold"], "warm_ms_per_step": tm["warm"],
+           "value": w.tokens / t, "unit": "tokens/s",
+           "roofline": {"bound": "mfma", "achieved": flops / t / 1e12, "peak": BF16_PEAK / 1e12,
+                        "unit": "TFLOP/s", "frac": flops / t / BF16_PEAK,
+                        "hbm_frac": nbytes / t / HBM_PEAK, "algorithmic_flops": flops,
+                        "algorithmic_bytes": nbytes,
+                        "note": "bf16 inputs: every product runs as three bf16 matrix-core passes "
+                                "(hi/lo split operands)"},
+           "workspace_bytes": ws.numel()}
+    if with_cpu:
+        res["cpu_baseline"] = cpu_baseline_bwd(w, x, dO, dhT)
+    del ws, out, dO, dhT
+    return res
+
+
+def cpu_baseline_bwd(w, x, dO, dhT, budget_s=10.0):
+    """The oracle's per-token reverse pass (numpy fp64, as it stands) over the
+    first T_s tokens of batch row 0, all value heads."""
+    from oracle import backward
+
+    cpu = {kk: (None if vv is None else vv[:1].cpu()) for kk, vv in x.items()}
+    dOc, dhc = dO[:1].cpu(), dhT[:1].cpu()
+
+    def run(T_s):
+        t0 = time.perf_counter()
+        backward.bwd(*[cpu[kk][:, :T_s] for kk in ("q", "k", "v", "g", "beta")], cpu["h0"],
+                     do=dOc[:, :T_s], dhT=dhc)
+        return time.perf_counter() - t0
+    T_s = min(w.T, 64)
+    dt = run(T_s)
+    T_s = max(T_s, min(w.T, int(T_s * budget_s / max(dt, 1e-6)) // 64 * 64))
+    dt = run(T_s)
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or None
+    return {"value": T_s / dt, "unit": "tokens/s", "cores": threads or os.cpu_count(), "kind": "oracle",
+            "sample": f"first {T_s} of {w.T} tokens of batch row 0, all {w.Hv} value heads; numpy fp64 "
+                      f"per-token reverse pass, {dt:.2f} s (threads: numpy's BLAS default)"}
+
+
 def stage_bytes(w, o_bytes=4):
     """Minimum HBM bytes each kernel must move in this design (its inputs read
     once, its outputs written once)."""
@@ -304,6 +383,8 @@ def main():
     ap.add_argument("--secondary", default="long_256k",
                     help="second workload timed for context ('' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the backward (gdn_chunk_bwd) timed at the headline workload")
     ap.add_argument("--n-groups", type=int, default=None,
                     help="override the workload's chunk-group count (0 = one sequential walk)")
     ap.add_argument("--packed", default="packed_8b_mix",
@@ -361,6 +442,10 @@ def main():
         print(json.dumps({"profile_run": w.name, "ms_per_step": tm}), flush=True)
         return
     line = measure(w, step, tm, args.steps, args.warmup, stage_bits, torch)
+    if not args.no_backward:
+        line["backward"] = measure_backward(w, x, max(5, args.steps // 5), 2, torch, gdn,
+                                            with_cpu=not args.no_cpu_baseline)
+        torch.cuda.empty_cache()
     if args.secondary and args.secondary != w.name:
         del x, step
         torch.cuda.empty_cache()

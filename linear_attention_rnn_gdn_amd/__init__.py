@@ -282,26 +282,34 @@ def chunk_bwd_state(q, k, g, beta, dO, dh_T=None, chunk=128, want_chunks=True, w
     return dhc, dh0
 
 
-def chunk_bwd(q, k, v, g, beta, dO, h0=None, dh_T=None, chunk=128, workspace=None, stream=None):
+def workspace_size_bwd_grads(shape: GdnShape) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().gdn_workspace_size_bwd_grads(ctypes.byref(shape), ctypes.byref(n)), "gdn_workspace_size_bwd_grads")
+    return int(n.value)
+
+
+def chunk_bwd(q, k, v, g, beta, dO, h0=None, dh_T=None, chunk=128, workspace=None, out=None, stream=None):
     """Gradients of sum_t <o_t, dO_t> + <h_T, dh_T> through the chunked
     forward (gdn_chunk_bwd).  q, k [B,T,H_qk,d_k]; v [B,T,H_v,d_v]; g, beta
     [B,T,H_v] fp32; dO [B,T,H_v,d_v] fp32; h0, dh_T [B,H_v,d_k,d_v] fp32 or
     None.  Returns a dict of fp32 tensors dq, dk [B,T,H_qk,d_k], dv
-    [B,T,H_v,d_v], dg, dbeta [B,T,H_v], dh0 [B,H_v,d_k,d_v]."""
+    [B,T,H_v,d_v], dg, dbeta [B,T,H_v], dh0 [B,H_v,d_k,d_v] (``out``: such a
+    dict to write into)."""
     B, T, Hqk, Hv, dk, dv, dev = _inputs(q, k, v, g, beta)
     _need(dO, "dO", torch.float32, (B, T, Hv, dv), dev)
     for name, x in (("h0", h0), ("dh_T", dh_T)):
         if x is not None:
             _need(x, name, torch.float32, (B, Hv, dk, dv), dev)
     shape = make_shape(B, T, Hqk, Hv, dk, dv, chunk, 0, q.dtype, torch.float32)
-    n = ctypes.c_size_t(0)
-    _check(lib().gdn_workspace_size_bwd_grads(ctypes.byref(shape), ctypes.byref(n)), "gdn_workspace_size_bwd_grads")
     if workspace is None:
-        workspace = torch.empty(max(int(n.value), 1), dtype=torch.uint8, device=dev)
+        workspace = torch.empty(max(workspace_size_bwd_grads(shape), 1), dtype=torch.uint8, device=dev)
     f32 = dict(dtype=torch.float32, device=dev)
-    out = dict(dq=torch.empty((B, T, Hqk, dk), **f32), dk=torch.empty((B, T, Hqk, dk), **f32),
-               dv=torch.empty((B, T, Hv, dv), **f32), dg=torch.empty((B, T, Hv), **f32),
-               dbeta=torch.empty((B, T, Hv), **f32), dh0=torch.empty((B, Hv, dk, dv), **f32))
+    want = dict(dq=(B, T, Hqk, dk), dk=(B, T, Hqk, dk), dv=(B, T, Hv, dv), dg=(B, T, Hv), dbeta=(B, T, Hv),
+                dh0=(B, Hv, dk, dv))
+    if out is None:
+        out = {kk: torch.empty(sh, **f32) for kk, sh in want.items()}
+    for kk, sh in want.items():
+        _need(out[kk], kk, torch.float32, sh, dev)
     _check(lib().gdn_chunk_bwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0),
                                _ptr(dO), _ptr(dh_T), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
                                _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out["dh0"]), _ptr(workspace),
