@@ -315,7 +315,7 @@ gdn_status gdn_chunk_bwd_state(const gdn_shape *shape, const void *q, const void
  *   NULL.
  *   ws: gdn_workspace_size_bwd_grads(shape) bytes (about 5 d_k x d_v + 2
  *   chunk x (chunk + d_v) floats per chunk and value head, plus a fixed
- *   scratch of at most 512 slots of 9 chunk x d_v + 7 chunk^2 floats).
+ *   scratch of at most 256 slots of 5 chunk x d_v + 7 chunk^2 floats).
  * shape->n_groups must be 0 or 1 (GDN_ERR_SHAPE otherwise); o_dtype is not
  * used.  Products follow the forward's precision policy (fp32 inputs: fp32
  * matrix-core products; bf16 inputs: hi/lo split bf16 products).  T = 0:

@@ -747,7 +747,7 @@ gdn_status run_bwd_state(const gdn_shape &s, const void *q, const void *k, const
 // forward's incoming states, the reverse walk's state cotangents, then the
 // chunk gradients on a persistent grid of kGradSlots workgroups, each with
 // its scratch slot; dq, dk per value head are summed per key head last.
-constexpr int kGradSlots = 512;
+constexpr int kGradSlots = 256;
 struct GradLayout {
   size_t G, Tm, W, U, ddh, dh, hs, dqv, dkv, scratch, total;
 };

@@ -347,7 +347,12 @@ __global__ __launch_bounds__(512) void fwd_states_kernel(StatesArgs a) {
     for (int kb = 0; kb < KBW; ++kb)
 #pragma unroll
       for (int j = 0; j < 8; ++j) hb[kb][j] = h[2 * kb + j / 4][j % 4];
+    // (U lands in the V' tiles themselves: no second set of registers)
     f32x4 x[MV];
+#pragma unroll
+    for (int mv = 0; mv < MV; ++mv)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[mv][i] = a.U[(cb * C + 16 * mv + 4 * g + i) * D + c0 + lr];
 #pragma unroll
     for (int mv = 0; mv < MV; ++mv) {
       f32x4 acc = zero4();
@@ -359,10 +364,7 @@ __global__ __launch_bounds__(512) void fwd_states_kernel(StatesArgs a) {
         mma_k32<PW>(acc, wa, hb[kb]);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * mv + 4 * g + i;
-        x[mv][i] = (a.U[(cb * C + r) * D + c0 + lr] - acc[i]) * exp2_fast(gl2 - sG[r] * LOG2E);
-      }
+      for (int i = 0; i < 4; ++i) x[mv][i] = (x[mv][i] - acc[i]) * exp2_fast(gl2 - sG[16 * mv + 4 * g + i] * LOG2E);
     }
     // h <- e^{G_last} h + K^T X
     float xb[KBK][8];
@@ -410,12 +412,13 @@ __global__ __launch_bounds__(512) void fwd_states_kernel(StatesArgs a) {
 //          + [r = last] (e^{G_last} <h, dh'> + sum_r s_r <(V' dh'^T)_r, k_r>)
 //   dg  = reverse cumulative sum of dG over the chunk
 // E = e^G, Gam_ri = e^{G_r - G_i} (i <= r).  One workgroup of eight waves
-// per (chunk, value head) at a time (a persistent grid); every product is a
-// set of 16 x 16 result tiles shared out over the waves, each tile formed
-// from operands read straight from memory (L2) in whichever orientation the
-// product takes them, into the workgroup's scratch slot in between.  The
-// chunk's Q, K, V and dO are first copied there as fp32 with zero rows past
-// the sequence's end (the identity padding of a partial last chunk).
+// per (chunk, value head) at a time (a persistent grid).  Every product is a
+// set of 16 x 16 result tiles shared out over the waves, formed from its two
+// operands staged whole in LDS (two buffers of up to 128 x 128 fp32, loaded
+// with coalesced 16-byte reads, the chunk's inputs converted to fp32 with
+// zero rows past the sequence's end -- the identity padding of a partial last
+// chunk); either operand may be read transposed from its buffer.  The
+// intermediates go to the workgroup's scratch slot between products.
 __device__ float g_zero_state[D * D];   // dh' of the last chunk without dh_T
 
 struct GradArgs {
@@ -433,33 +436,122 @@ struct GradArgs {
   float *scratch;             // [gridDim.x][grad_slot_floats(C)]
 };
 
-template <int C> constexpr size_t grad_slot_floats() { return (size_t)9 * C * D + (size_t)7 * C * C; }
+template <int C> constexpr size_t grad_slot_floats() { return (size_t)5 * C * D + (size_t)7 * C * C; }
 
-// A (rows i0.., k) times B (k, columns j0..) over k < K into acc: element
-// (i, k) of A at A[i * lda + k] (TA = false) or A[k * lda + i] (TA = true),
-// element (k, j) of B at B[k * ldb + j] (TB = false) or B[j * ldb + k]
-// (TB = true).  Lane (lr, g) takes k = k0 + 8g + j, j = 0..7, of each block.
-template <int P, bool TA, bool TB>
-__device__ __forceinline__ void tile_mm(f32x4 &acc, const float *A, int lda, int i0, const float *B, int ldb, int j0,
-                                        int K, int lane) {
+// A staged operand in LDS: up to 128 rows (the rows of A, or the columns of
+// B, of a product) of up to 128 k-values each, k contiguous.  With bf16
+// inputs every value is split once, when staged, into hi and lo bf16 planes
+// (the products' hi/lo policy), so that a fragment is two 16-byte reads; with
+// fp32 inputs the values stay fp32.  A source matrix is staged as is or
+// transposed, whichever puts its contraction index along the rows.
+constexpr int GLDH = 136;   // bf16 plane row stride (elements; 272 bytes)
+constexpr int GLDX = 132;   // fp32 row stride
+template <int MODE> struct GStage {
+  static constexpr bool SPLIT = MODE != MODE_F32;
+  static constexpr int KIND = SPLIT ? F_SPLIT : F_F32;
+  static constexpr int BYTES = SPLIT ? 2 * 128 * GLDH * 2 : 128 * GLDX * 4;
+  // source row r, columns c .. c+3 to (r, c..c+3), or transposed to (c..c+3, r)
+  template <bool TR>
+  __device__ static void put4(char *buf, int r, int c, float4 x) {
+    if constexpr (SPLIT) {
+      unsigned short *hi = reinterpret_cast<unsigned short *>(buf), *lo = hi + 128 * GLDH;
+      const unsigned h01 = pk_bf16(x.x, x.y), h23 = pk_bf16(x.z, x.w);
+      const unsigned l01 = pk_bf16(x.x - __builtin_bit_cast(float, h01 << 16),
+                                   x.y - __builtin_bit_cast(float, h01 & 0xffff0000u));
+      const unsigned l23 = pk_bf16(x.z - __builtin_bit_cast(float, h23 << 16),
+                                   x.w - __builtin_bit_cast(float, h23 & 0xffff0000u));
+      if constexpr (!TR) {
+        *reinterpret_cast<uint2 *>(hi + r * GLDH + c) = uint2{h01, h23};
+        *reinterpret_cast<uint2 *>(lo + r * GLDH + c) = uint2{l01, l23};
+      } else {
+        hi[(c + 0) * GLDH + r] = (unsigned short)h01;
+        hi[(c + 1) * GLDH + r] = (unsigned short)(h01 >> 16);
+        hi[(c + 2) * GLDH + r] = (unsigned short)h23;
+        hi[(c + 3) * GLDH + r] = (unsigned short)(h23 >> 16);
+        lo[(c + 0) * GLDH + r] = (unsigned short)l01;
+        lo[(c + 1) * GLDH + r] = (unsigned short)(l01 >> 16);
+        lo[(c + 2) * GLDH + r] = (unsigned short)l23;
+        lo[(c + 3) * GLDH + r] = (unsigned short)(l23 >> 16);
+      }
+    } else {
+      float *f = reinterpret_cast<float *>(buf);
+      if constexpr (!TR) {
+        *reinterpret_cast<float4 *>(f + r * GLDX + c) = x;
+      } else {
+        f[(c + 0) * GLDX + r] = x.x;
+        f[(c + 1) * GLDX + r] = x.y;
+        f[(c + 2) * GLDX + r] = x.z;
+        f[(c + 3) * GLDX + r] = x.w;
+      }
+    }
+  }
+  // row i, k-values k0 .. k0+7 (k0 a multiple of 8)
+  __device__ static Frag<KIND> frag(const char *buf, int i, int k0) {
+    Frag<KIND> f;
+    if constexpr (SPLIT) {
+      const __bf16 *hi = reinterpret_cast<const __bf16 *>(buf), *lo = hi + 128 * GLDH;
+      f.hi = *reinterpret_cast<const bf16x8 *>(hi + i * GLDH + k0);
+      f.lo = *reinterpret_cast<const bf16x8 *>(lo + i * GLDH + k0);
+    } else {
+      float x[8];
+      ld8(reinterpret_cast<const float *>(buf) + i * GLDX + k0, x);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) f.v[j] = x[j];
+    }
+    return f;
+  }
+};
+
+// NR x NC fp32 rows (row stride ld) staged, 512 threads
+template <int MODE, int NR, int NC, bool TR>
+__device__ __forceinline__ void stage(char *buf, const float *src, size_t ld, int tid) {
+  constexpr int N4 = NR * NC / 4, PER = N4 / 512;
+  static_assert(N4 % 512 == 0, "whole float4 per thread");
+  float4 v[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int e = tid + 512 * u, r = e / (NC / 4), c = (e % (NC / 4)) * 4;
+    v[u] = *reinterpret_cast<const float4 *>(src + r * ld + c);
+  }
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int e = tid + 512 * u, r = e / (NC / 4), c = (e % (NC / 4)) * 4;
+    GStage<MODE>::template put4<TR>(buf, r, c, v[u]);
+  }
+}
+// NR x D input rows of type T (row stride ld elements) staged as fp32 values,
+// rows at or past `rows` zero
+template <int MODE, int NR, bool TR, typename T>
+__device__ __forceinline__ void stage_in(char *buf, const T *src, size_t ld, int rows, int tid) {
+  constexpr int VE = 16 / (int)sizeof(T), NV = NR * D / VE, PER = NV / 512;
+  static_assert(NV % 512 == 0, "whole vectors per thread");
+  uint4 v[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int e = tid + 512 * u, r = e / (D / VE), c = (e % (D / VE)) * VE;
+    v[u] = r < rows ? *reinterpret_cast<const uint4 *>(src + r * ld + c) : uint4{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int e = tid + 512 * u, r = e / (D / VE), c = (e % (D / VE)) * VE;
+    const T *x = reinterpret_cast<const T *>(&v[u]);
+#pragma unroll
+    for (int j = 0; j < VE; j += 4)
+      GStage<MODE>::template put4<TR>(buf, r, c + j,
+                                      float4{to_f32(x[j]), to_f32(x[j + 1]), to_f32(x[j + 2]), to_f32(x[j + 3])});
+  }
+}
+
+// acc += A B for the 16 x 16 tile (rows i0.. of A, columns j0.. of B) over K
+// k-values: A staged with its rows, B with its columns, along the buffer rows.
+// Lane (lr, g) takes k = k0 + 8g .. k0 + 8g + 7 of each block of 32.
+template <int MODE, int K>
+__device__ __forceinline__ void tile_st(f32x4 &acc, const char *A, int i0, const char *B, int j0, int lane) {
   const int lr = lane & 15, g = lane >> 4;
 #pragma unroll 2
   for (int k0 = 0; k0 < K; k0 += 32) {
     const int kb = k0 + 8 * g;
-    float a8[8], b8[8];
-    if constexpr (!TA) {
-      ld8(A + (size_t)(i0 + lr) * lda + kb, a8);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) a8[j] = A[(size_t)(kb + j) * lda + i0 + lr];
-    }
-    if constexpr (TB) {
-      ld8(B + (size_t)(j0 + lr) * ldb + kb, b8);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) b8[j] = B[(size_t)(kb + j) * ldb + j0 + lr];
-    }
-    mma_k32<P>(acc, a8, b8);
+    mma(acc, GStage<MODE>::frag(A, i0 + lr, kb), GStage<MODE>::frag(B, j0 + lr, kb));
   }
 }
 
@@ -493,20 +585,43 @@ __device__ __forceinline__ void add_col_sums(float *acc, int j0, const float (&v
 
 template <int C, typename TI, int MODE, bool RAG>
 __global__ __launch_bounds__(512) void bwd_chunk_kernel(GradArgs a) {
-  constexpr int P = MODE == MODE_F32 ? P_F32 : P_SPLIT_AB;
+  using GS = GStage<MODE>;
   constexpr int CD = C * D, CC = C * C, DD = D * D, TC = C / 16, TD = D / 16;
-  constexpr int NW = 8;   // waves
-  __shared__ float sG[C], sE[C], sS[C], sB[C], sdG[C], sdB[C];
-  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, g = lane >> 4;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  constexpr int NW = 8;                                     // waves
+  constexpr int NCD = TC * TD / NW, NCC = TC * TC / NW;     // result tiles per wave: C x D, C x C
+  static_assert(NCD * NW == TC * TD && NCC * NW == TC * TC, "whole tiles per wave");
+  __shared__ __align__(16) char sA[GS::BYTES];
+  __shared__ __align__(16) char sB[GS::BYTES];
+  __shared__ float sG[C], sE[C], sS[C], sBt[C], sdG[C], sdB[C];
+  const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   float *slot = a.scratch + (size_t)blockIdx.x * grad_slot_floats<C>();
-  float *Qs = slot, *Ks = Qs + CD, *Vs = Ks + CD, *dOs = Vs + CD, *Vp = dOs + CD, *dV = Vp + CD, *dW = dV + CD,
-        *dQp = dW + CD, *dKp = dQp + CD;
+  float *Vp = slot, *dV = Vp + CD, *dW = dV + CD, *dQp = dW + CD, *dKp = dQp + CD;
   float *R = dKp + CD, *Pm = R + CC, *dR = Pm + CC, *dT = dR + CC, *X = dT + CC, *dKk = X + CC, *Kk = dKk + CC;
   const int grp = a.Hv / a.Hqk;
   const int oheads = a.per_value_head ? a.Hv : a.Hqk;
+  // each wave's result tiles of a C x D or C x C product: f(row i0, column j0)
+  auto for_cd = [&](auto f) {
+#pragma unroll 1
+    for (int u = 0; u < NCD; ++u) {
+      const int t = wv + NW * u;
+      f(16 * (t / TD), 16 * (t % TD));
+    }
+  };
+  auto for_cc = [&](auto f) {
+#pragma unroll 1
+    for (int u = 0; u < NCC; ++u) {
+      const int t = wv + NW * u;
+      f(16 * (t / TC), 16 * (t % TC));
+    }
+  };
 
   for (int unit = blockIdx.x; unit < a.units; unit += gridDim.x) {
+    // (the thread index made opaque per unit: the per-thread offsets of the
+    // staging copies and tile reads are then formed inside the loop, not
+    // hoisted out of it into more registers than there are)
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, lr = lane & 15, g = lane >> 4;
     const size_t cb = unit, bh = cb / a.N;
     const int n = (int)(cb % a.N), b = (int)(bh / a.Hv), hv = (int)(bh % a.Hv), hq = hv / grp;
     const int oh = a.per_value_head ? hv : hq;
@@ -514,126 +629,153 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(GradArgs a) {
     const int rows = !RAG ? C : (a.T - n * C < C ? a.T - n * C : C);
     const float *Tm = a.Tm + cb * CC, *Wm = a.W + cb * CD, *Um = a.U + cb * CD, *h = a.hs + cb * DD;
     const float *dhn = n + 1 < a.N ? a.dh + (cb + 1) * DD : a.dhT ? a.dhT + bh * DD : g_zero_state;
-    __syncthreads();   // the previous unit is done with the slot and the LDS sums
+    const TI *qin = reinterpret_cast<const TI *>(a.q) + (t0 * a.Hqk + hq) * D;
+    const TI *kin = reinterpret_cast<const TI *>(a.k) + (t0 * a.Hqk + hq) * D;
+    const TI *vin = reinterpret_cast<const TI *>(a.v) + (t0 * a.Hv + hv) * D;
+    const float *doin = a.dO + (t0 * a.Hv + hv) * D;
+    const size_t ldq = (size_t)a.Hqk * D, ldv = (size_t)a.Hv * D;
+    // one input element as fp32 (zero past the sequence's end)
+    auto in_at = [&](const TI *p, size_t ld, int r, int c) { return r < rows ? to_f32(p[r * ld + c]) : 0.f; };
+    auto gam = [&](int r, int c) { return exp2_fast(sG[r] - sG[c]); };   // Gam_rc, c <= r
+    // result element (row 4g + i of the tile) helpers
+    auto row = [&](int i0, int i) { return i0 + 4 * g + i; };
 
-    // inputs as fp32, zero past the sequence's end
-    constexpr int VE = 16 / (int)sizeof(TI);
-    for (int e = tid; e < CD / VE; e += 64 * NW) {
-      const int r = e / (D / VE), c = (e % (D / VE)) * VE;
-      float xq[VE], xk[VE], xv[VE];
-#pragma unroll
-      for (int j = 0; j < VE; ++j) xq[j] = xk[j] = xv[j] = 0.f;
-      if (r < rows) {
-        const TI *pq = reinterpret_cast<const TI *>(a.q) + ((t0 + r) * a.Hqk + hq) * D + c;
-        const TI *pk = reinterpret_cast<const TI *>(a.k) + ((t0 + r) * a.Hqk + hq) * D + c;
-        const TI *pv = reinterpret_cast<const TI *>(a.v) + ((t0 + r) * a.Hv + hv) * D + c;
-#pragma unroll
-        for (int j = 0; j < VE; ++j) {
-          xq[j] = to_f32(pq[j]);
-          xk[j] = to_f32(pk[j]);
-          xv[j] = to_f32(pv[j]);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < VE; j += 4) {
-        *reinterpret_cast<float4 *>(Qs + r * D + c + j) = float4{xq[j], xq[j + 1], xq[j + 2], xq[j + 3]};
-        *reinterpret_cast<float4 *>(Ks + r * D + c + j) = float4{xk[j], xk[j + 1], xk[j + 2], xk[j + 3]};
-        *reinterpret_cast<float4 *>(Vs + r * D + c + j) = float4{xv[j], xv[j + 1], xv[j + 2], xv[j + 3]};
-      }
-    }
-    for (int e = tid; e < CD / 4; e += 64 * NW) {
-      const int r = e / (D / 4), c = (e % (D / 4)) * 4;
-      float4 x{0.f, 0.f, 0.f, 0.f};
-      if (r < rows) x = *reinterpret_cast<const float4 *>(a.dO + ((t0 + r) * a.Hv + hv) * D + c);
-      *reinterpret_cast<float4 *>(dOs + r * D + c) = x;
-    }
+    __syncthreads();   // the previous unit is done with the LDS
     if (tid < C) {
       const float Gr = a.G[cb * C + tid], Gl = a.G[cb * C + C - 1];
       sG[tid] = Gr * LOG2E;
       sE[tid] = exp2_fast(Gr * LOG2E);
       sS[tid] = exp2_fast((Gl - Gr) * LOG2E);
-      sB[tid] = tid < rows ? a.beta[(t0 + tid) * a.Hv + hv] : 0.f;
+      sBt[tid] = tid < rows ? a.beta[(t0 + tid) * a.Hv + hv] : 0.f;
       sdG[tid] = 0.f;
       sdB[tid] = 0.f;
     }
+    stage_in<MODE, C, false>(sA, qin, ldq, rows, tid);
+    stage_in<MODE, C, false>(sB, kin, ldq, rows, tid);
     __syncthreads();
-    auto gam = [&](int r, int c) { return exp2_fast(sG[r] - sG[c]); };   // Gam_rc, c <= r
-
-    // (1) V' = U - W h;  dq's first term E o (dO h^T) and its dG term;
-    //     R = Q K^T, P, K K^T
-    for (int t = wv; t < TC * TD; t += NW) {
-      const int i0 = 16 * (t / TD), j0 = 16 * (t % TD), c = j0 + lr;
+    // (1) R = Q K^T, P = R o Gam o [i <= r]; K K^T
+    for_cc([&](int i0, int j0) {
       f32x4 acc = zero4();
-      tile_mm<P, false, false>(acc, Wm, D, i0, h, D, j0, D, lane);
-      f32x4 oh_ = zero4();
-      tile_mm<P, false, true>(oh_, dOs, D, i0, h, D, j0, D, lane);
+      tile_st<MODE, D>(acc, sA, i0, sB, j0, lane);
+      const int c = j0 + lr;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = row(i0, i);
+        R[r * C + c] = acc[i];
+        Pm[r * C + c] = c <= r ? acc[i] * gam(r, c) : 0.f;
+      }
+    });
+    for_cc([&](int i0, int j0) {
+      f32x4 acc = zero4();
+      tile_st<MODE, D>(acc, sB, i0, sB, j0, lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Kk[row(i0, i) * C + j0 + lr] = acc[i];
+    });
+    __syncthreads();
+    stage<MODE, C, D, false>(sA, Wm, D, tid);
+    stage<MODE, D, D, true>(sB, h, D, tid);
+    __syncthreads();
+    // (2) V' = U - W h
+    for_cd([&](int i0, int j0) {
+      f32x4 acc = zero4();
+      tile_st<MODE, D>(acc, sA, i0, sB, j0, lane);
+      const int c = j0 + lr;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = row(i0, i);
+        Vp[r * D + c] = Um[r * D + c] - acc[i];
+      }
+    });
+    __syncthreads();
+    stage_in<MODE, C, false>(sA, doin, ldv, rows, tid);
+    stage<MODE, D, D, false>(sB, h, D, tid);
+    __syncthreads();
+    // (3) dO h^T: dq's first term E o (dO h^T); dG_r += E_r <q_r, (dO h^T)_r>
+    for_cd([&](int i0, int j0) {
+      f32x4 acc = zero4();
+      tile_st<MODE, D>(acc, sA, i0, sB, j0, lane);
+      const int c = j0 + lr;
       float rs[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = i0 + 4 * g + i;
-        Vp[r * D + c] = Um[r * D + c] - acc[i];
-        dQp[r * D + c] = sE[r] * oh_[i];
-        rs[i] = sE[r] * Qs[r * D + c] * oh_[i];
+        const int r = row(i0, i);
+        dQp[r * D + c] = sE[r] * acc[i];
+        rs[i] = sE[r] * in_at(qin, ldq, r, c) * acc[i];
       }
       add_row_sums(sdG, i0, rs, 1.f, lane);
-    }
-    for (int t = wv; t < TC * TC; t += NW) {
-      const int i0 = 16 * (t / TC), j0 = 16 * (t % TC), c = j0 + lr;
-      f32x4 acc = zero4(), kk_ = zero4();
-      tile_mm<P, false, true>(acc, Qs, D, i0, Ks, D, j0, D, lane);
-      tile_mm<P, false, true>(kk_, Ks, D, i0, Ks, D, j0, D, lane);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = i0 + 4 * g + i;
-        R[r * C + c] = acc[i];
-        Pm[r * C + c] = c <= r ? acc[i] * gam(r, c) : 0.f;
-        Kk[r * C + c] = kk_[i];
-      }
-    }
+    });
     __syncthreads();
-
-    // (2) dP, dR and dP o R's dG terms;  dV = P^T dO + diag(s) K dh';
-    //     V' dh'^T: dk's first term and its dG terms;  <h, dh'>
-    for (int t = wv; t < TC * TC; t += NW) {
-      const int i0 = 16 * (t / TC), j0 = 16 * (t % TC), c = j0 + lr;
+    stage<MODE, C, D, false>(sB, Vp, D, tid);
+    __syncthreads();
+    // (4) dP = (dO V'^T) o [i <= r]: dR = dP o Gam; dG terms of dP o R o Gam
+    for_cc([&](int i0, int j0) {
       f32x4 acc = zero4();
-      tile_mm<P, false, true>(acc, dOs, D, i0, Vp, D, j0, D, lane);
+      tile_st<MODE, D>(acc, sA, i0, sB, j0, lane);
+      const int c = j0 + lr;
       float tv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = i0 + 4 * g + i;
+        const int r = row(i0, i);
         const float gm = c <= r ? gam(r, c) : 0.f;
         dR[r * C + c] = acc[i] * gm;
         tv[i] = acc[i] * R[r * C + c] * gm;
       }
       add_row_sums(sdG, i0, tv, 1.f, lane);
       add_col_sums(sdG, j0, tv, -1.f, lane);
-    }
-    for (int t = wv; t < TC * TD; t += NW) {
-      const int i0 = 16 * (t / TD), j0 = 16 * (t % TD), c = j0 + lr;
-      f32x4 pd = zero4(), kd = zero4(), vd = zero4();
-      tile_mm<P, true, false>(pd, Pm, C, i0, dOs, D, j0, C, lane);
-      tile_mm<P, false, false>(kd, Ks, D, i0, dhn, D, j0, D, lane);
-      tile_mm<P, false, true>(vd, Vp, D, i0, dhn, D, j0, D, lane);
+    });
+    __syncthreads();
+    stage<MODE, C, C, true>(sA, Pm, C, tid);
+    stage_in<MODE, C, true>(sB, doin, ldv, rows, tid);
+    __syncthreads();
+    // (5) P^T dO (into dV; (6) adds the second term)
+    for_cd([&](int i0, int j0) {
+      f32x4 acc = zero4();
+      tile_st<MODE, C>(acc, sA, i0, sB, j0, lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dV[row(i0, i) * D + j0 + lr] = acc[i];
+    });
+    __syncthreads();
+    stage_in<MODE, C, false>(sA, kin, ldq, rows, tid);
+    stage<MODE, D, D, true>(sB, dhn, D, tid);
+    __syncthreads();
+    // (6) dV = P^T dO + diag(s) K dh'
+    for_cd([&](int i0, int j0) {
+      f32x4 acc = zero4();
+      tile_st<MODE, D>(acc, sA, i0, sB, j0, lane);
+      const int c = j0 + lr;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = row(i0, i);
+        dV[r * D + c] += sS[r] * acc[i];
+      }
+    });
+    __syncthreads();
+    stage<MODE, C, D, false>(sA, Vp, D, tid);
+    stage<MODE, D, D, false>(sB, dhn, D, tid);
+    __syncthreads();
+    // (7) V' dh'^T: dk's first term diag(s) V' dh'^T and its dG terms; <h, dh'>
+    for_cd([&](int i0, int j0) {
+      f32x4 acc = zero4();
+      tile_st<MODE, D>(acc, sA, i0, sB, j0, lane);
+      const int c = j0 + lr;
       float dd[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = i0 + 4 * g + i;
-        dV[r * D + c] = pd[i] + sS[r] * kd[i];
-        const float x = sS[r] * vd[i];
+        const int r = row(i0, i);
+        const float x = sS[r] * acc[i];
         dKp[r * D + c] = x;
-        dd[i] = x * Ks[r * D + c];
+        dd[i] = x * in_at(kin, ldq, r, c);
       }
       // dG_r -= dd_r, dG_last += sum_r dd_r
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float x = sum_cols(dd[i]);
         if (lr == 0) {
-          atomicAdd(sdG + i0 + 4 * g + i, -x);
+          atomicAdd(sdG + row(i0, i), -x);
           atomicAdd(sdG + C - 1, x);
         }
       }
-    }
+    });
     {
       float hsum = 0.f;
       for (int e = tid; e < DD / 4; e += 64 * NW) {
@@ -644,113 +786,171 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(GradArgs a) {
       if (lane == 0) atomicAdd(sdG + C - 1, exp2_fast(sG[C - 1]) * hsum);
     }
     __syncthreads();
-
-    // (3) dW = -dV h^T;  dq = E o (dO h^T) + dR K;  dU~ = T^T dV: dv, dbeta
-    for (int t = wv; t < TC * TD; t += NW) {
-      const int i0 = 16 * (t / TD), j0 = 16 * (t % TD), c = j0 + lr;
-      f32x4 wd = zero4(), rq = zero4(), ut = zero4();
-      tile_mm<P, false, true>(wd, dV, D, i0, h, D, j0, D, lane);
-      tile_mm<P, false, false>(rq, dR, C, i0, Ks, D, j0, C, lane);
-      tile_mm<P, true, false>(ut, Tm, C, i0, dV, D, j0, C, lane);
+    stage<MODE, C, D, false>(sA, dV, D, tid);
+    stage<MODE, D, D, false>(sB, h, D, tid);
+    __syncthreads();
+    // (8) dW = -dV h^T
+    for_cd([&](int i0, int j0) {
+      f32x4 acc = zero4();
+      tile_st<MODE, D>(acc, sA, i0, sB, j0, lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dW[row(i0, i) * D + j0 + lr] = -acc[i];
+    });
+    __syncthreads();
+    stage<MODE, C, C, false>(sA, dR, C, tid);
+    stage_in<MODE, C, true>(sB, kin, ldq, rows, tid);
+    __syncthreads();
+    // (9) dq = E o (dO h^T) + dR K
+    for_cd([&](int i0, int j0) {
+      f32x4 acc = zero4();
+      tile_st<MODE, C>(acc, sA, i0, sB, j0, lane);
+      const int c = j0 + lr;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = row(i0, i);
+        if (r < rows) a.dq[((t0 + r) * oheads + oh) * D + c] = dQp[r * D + c] + acc[i];
+      }
+    });
+    __syncthreads();
+    stage<MODE, C, C, true>(sA, Tm, C, tid);
+    stage<MODE, C, D, true>(sB, dV, D, tid);
+    __syncthreads();
+    // (10) dU~ = T^T dV: dv = diag(beta) dU~, dbeta_r += <dU~_r, v_r>
+    for_cd([&](int i0, int j0) {
+      f32x4 acc = zero4();
+      tile_st<MODE, C>(acc, sA, i0, sB, j0, lane);
+      const int c = j0 + lr;
       float bv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = i0 + 4 * g + i;
-        dW[r * D + c] = -wd[i];
-        if (r < rows) {
-          a.dq[((t0 + r) * oheads + oh) * D + c] = dQp[r * D + c] + rq[i];
-          a.dv[((t0 + r) * a.Hv + hv) * D + c] = sB[r] * ut[i];
-        }
-        bv[i] = ut[i] * Vs[r * D + c];
+        const int r = row(i0, i);
+        if (r < rows) a.dv[((t0 + r) * a.Hv + hv) * D + c] = sBt[r] * acc[i];
+        bv[i] = acc[i] * in_at(vin, ldv, r, c);
       }
       add_row_sums(sdB, i0, bv, 1.f, lane);
-    }
+    });
     __syncthreads();
-
-    // (4) dW~ = T^T dW: dk's second term, dbeta and dG terms;
-    //     dT = (dW K^T) diag(beta E) + (dV V^T) diag(beta)
-    for (int t = wv; t < TC * TD; t += NW) {
-      const int i0 = 16 * (t / TD), j0 = 16 * (t % TD), c = j0 + lr;
+    stage<MODE, C, D, true>(sB, dW, D, tid);
+    __syncthreads();
+    // (11) dW~ = T^T dW: dk += diag(beta E) dW~; rw_r = <dW~_r, k_r>:
+    //      dbeta_r += E_r rw_r, dG_r += beta_r E_r rw_r
+    for_cd([&](int i0, int j0) {
       f32x4 acc = zero4();
-      tile_mm<P, true, false>(acc, Tm, C, i0, dW, D, j0, C, lane);
+      tile_st<MODE, C>(acc, sA, i0, sB, j0, lane);
+      const int c = j0 + lr;
       float rw[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = i0 + 4 * g + i;
-        dKp[r * D + c] += sB[r] * sE[r] * acc[i];
-        rw[i] = acc[i] * Ks[r * D + c];
+        const int r = row(i0, i);
+        dKp[r * D + c] += sBt[r] * sE[r] * acc[i];
+        rw[i] = acc[i] * in_at(kin, ldq, r, c);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float x = sum_cols(rw[i]);
-        const int r = i0 + 4 * g + i;
+        const int r = row(i0, i);
         if (lr == 0) {
           atomicAdd(sdB + r, sE[r] * x);
-          atomicAdd(sdG + r, sB[r] * sE[r] * x);
+          atomicAdd(sdG + r, sBt[r] * sE[r] * x);
         }
       }
-    }
-    for (int t = wv; t < TC * TC; t += NW) {
-      const int i0 = 16 * (t / TC), j0 = 16 * (t % TC), c = j0 + lr;
-      f32x4 wk = zero4(), vv = zero4();
-      tile_mm<P, false, true>(wk, dW, D, i0, Ks, D, j0, D, lane);
-      tile_mm<P, false, true>(vv, dV, D, i0, Vs, D, j0, D, lane);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = i0 + 4 * g + i;
-        dT[r * C + c] = (wk[i] * sE[c] + vv[i]) * sB[c];
-      }
-    }
+    });
     __syncthreads();
-
-    // (5) X = dT T^T
-    for (int t = wv; t < TC * TC; t += NW) {
-      const int i0 = 16 * (t / TC), j0 = 16 * (t % TC), c = j0 + lr;
-      f32x4 acc = zero4();
-      tile_mm<P, false, true>(acc, dT, C, i0, Tm, C, j0, C, lane);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) X[(i0 + 4 * g + i) * C + c] = acc[i];
-    }
+    stage<MODE, C, D, false>(sA, dW, D, tid);
+    stage_in<MODE, C, false>(sB, kin, ldq, rows, tid);
     __syncthreads();
-
-    // (6) dS = -strict-lower(T^T X): dbeta, dG terms, dKk
-    for (int t = wv; t < TC * TC; t += NW) {
-      const int i0 = 16 * (t / TC), j0 = 16 * (t % TC), c = j0 + lr;
+    // (12) (dW K^T) diag(beta E) (into dT; (13) adds the second term)
+    for_cc([&](int i0, int j0) {
       f32x4 acc = zero4();
-      tile_mm<P, true, false>(acc, Tm, C, i0, X, C, j0, C, lane);
+      tile_st<MODE, D>(acc, sA, i0, sB, j0, lane);
+      const int c = j0 + lr;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dT[row(i0, i) * C + c] = acc[i] * sE[c] * sBt[c];
+    });
+    __syncthreads();
+    stage<MODE, C, D, false>(sA, dV, D, tid);
+    stage_in<MODE, C, false>(sB, vin, ldv, rows, tid);
+    __syncthreads();
+    // (13) dT += (dV V^T) diag(beta)
+    for_cc([&](int i0, int j0) {
+      f32x4 acc = zero4();
+      tile_st<MODE, D>(acc, sA, i0, sB, j0, lane);
+      const int c = j0 + lr;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dT[row(i0, i) * C + c] += acc[i] * sBt[c];
+    });
+    __syncthreads();
+    stage<MODE, C, C, false>(sA, dT, C, tid);
+    stage<MODE, C, C, false>(sB, Tm, C, tid);
+    __syncthreads();
+    // (14) X = dT T^T
+    for_cc([&](int i0, int j0) {
+      f32x4 acc = zero4();
+      tile_st<MODE, C>(acc, sA, i0, sB, j0, lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) X[row(i0, i) * C + j0 + lr] = acc[i];
+    });
+    __syncthreads();
+    stage<MODE, C, C, true>(sA, Tm, C, tid);
+    stage<MODE, C, C, true>(sB, X, C, tid);
+    __syncthreads();
+    // (15) dS = -strict-lower(T^T X): dbeta, dG terms of diag(beta) dS o K K^T
+    //      o Gam, dKk = diag(beta) dS o Gam
+    for_cc([&](int i0, int j0) {
+      f32x4 acc = zero4();
+      tile_st<MODE, C>(acc, sA, i0, sB, j0, lane);
+      const int c = j0 + lr;
       float bs[4], tv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = i0 + 4 * g + i;
+        const int r = row(i0, i);
         const float ds = c < r ? -acc[i] : 0.f;
         const float gm = c < r ? gam(r, c) : 0.f;
-        const float kkv = Kk[r * C + c];
-        bs[i] = ds * gm * kkv;
-        tv[i] = sB[r] * bs[i];
-        dKk[r * C + c] = sB[r] * ds * gm;
+        bs[i] = ds * gm * Kk[r * C + c];
+        tv[i] = sBt[r] * bs[i];
+        dKk[r * C + c] = sBt[r] * ds * gm;
       }
       add_row_sums(sdB, i0, bs, 1.f, lane);
       add_row_sums(sdG, i0, tv, 1.f, lane);
       add_col_sums(sdG, j0, tv, -1.f, lane);
-    }
+    });
     __syncthreads();
-
-    // (7) dk = diag(s) V' dh'^T + diag(beta E) dW~ + dR^T Q + (dKk + dKk^T) K;
-    //     dg = reverse cumulative sum of dG, dbeta
-    for (int t = wv; t < TC * TD; t += NW) {
-      const int i0 = 16 * (t / TD), j0 = 16 * (t % TD), c = j0 + lr;
-      f32x4 acc;
+    stage<MODE, C, C, true>(sA, dR, C, tid);
+    stage_in<MODE, C, true>(sB, qin, ldq, rows, tid);
+    __syncthreads();
+    // (16) dk += dR^T Q
+    for_cd([&](int i0, int j0) {
+      f32x4 acc = zero4();
+      tile_st<MODE, C>(acc, sA, i0, sB, j0, lane);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = dKp[(i0 + 4 * g + i) * D + c];
-      tile_mm<P, true, false>(acc, dR, C, i0, Qs, D, j0, C, lane);
-      tile_mm<P, false, false>(acc, dKk, C, i0, Ks, D, j0, C, lane);
-      tile_mm<P, true, false>(acc, dKk, C, i0, Ks, D, j0, C, lane);
+      for (int i = 0; i < 4; ++i) dKp[row(i0, i) * D + j0 + lr] += acc[i];
+    });
+    __syncthreads();
+    stage<MODE, C, C, false>(sA, dKk, C, tid);
+    stage_in<MODE, C, true>(sB, kin, ldq, rows, tid);
+    __syncthreads();
+    // (17) dk += dKk K
+    for_cd([&](int i0, int j0) {
+      f32x4 acc = zero4();
+      tile_st<MODE, C>(acc, sA, i0, sB, j0, lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dKp[row(i0, i) * D + j0 + lr] += acc[i];
+    });
+    __syncthreads();
+    stage<MODE, C, C, true>(sA, dKk, C, tid);
+    __syncthreads();
+    // (18) dk = diag(s) V' dh'^T + diag(beta E) dW~ + dR^T Q + dKk K + dKk^T K;
+    //      dg = reverse cumulative sum of dG; dbeta
+    for_cd([&](int i0, int j0) {
+      f32x4 acc = zero4();
+      tile_st<MODE, C>(acc, sA, i0, sB, j0, lane);
+      const int c = j0 + lr;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = i0 + 4 * g + i;
-        if (r < rows) a.dk[((t0 + r) * oheads + oh) * D + c] = acc[i];
+        const int r = row(i0, i);
+        if (r < rows) a.dk[((t0 + r) * oheads + oh) * D + c] = dKp[r * D + c] + acc[i];
       }
-    }
+    });
     if (tid < rows) {
       float sdg = 0.f;
       for (int j = tid; j < C; ++j) sdg += sdG[j];
