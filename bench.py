@@ -139,6 +139,16 @@ def cpu_baseline_bwd(w, x, dO, dhT, budget_s=10.0):
                       f"per-token reverse pass, {dt:.2f} s (threads: numpy's BLAS default)"}
 
 
+FUSED_MIN_WALKS = 128   # the library's GDN_FUSED_MIN_WALKS
+
+
+def fused_walk(w):
+    """Whether the library runs the walk that forms the outputs itself (no
+    separate output stage) for this workload: as many walks as
+    FUSED_MIN_WALKS or more (batch rows x value heads x groups)."""
+    return w.B * w.Hv * max(w.n_groups, 1) >= FUSED_MIN_WALKS
+
+
 def stage_bytes(w, o_bytes=4):
     """Minimum HBM bytes each kernel must move in this design (its inputs read
     once, its outputs written once)."""
@@ -166,12 +176,15 @@ def stage_bytes(w, o_bytes=4):
         "prep": k_b + v_b + gb_b + G_b + W_b + Kt_b + U_b,
         "out": q_b + k_b + G_b + Hs_b + Vn_b + tok * w.Hv * dv * o_bytes,
     }
-    if J == 1:
-        out["walk"] = W_b + U_b + G_b + Kt_b + h0_b + Hs_b + Vn_b + st
-    else:
+    init = h0_b if J == 1 else hin
+    if J > 1:
         out["fold"] = W_b + U_b + G_b + Kt_b + pairs
         out["prefix"] = pairs + h0_b + hin + st
-        out["walk"] = W_b + U_b + G_b + Kt_b + hin + Hs_b + Vn_b
+    if fused_walk(w):   # the walk reads q and writes o itself; no handoff
+        del out["out"]
+        out["walk"] = W_b + U_b + G_b + Kt_b + init + q_b + tok * w.Hv * dv * o_bytes + st
+    else:
+        out["walk"] = W_b + U_b + G_b + Kt_b + init + Hs_b + Vn_b + (st if J == 1 else 0)
     return out
 
 
@@ -207,8 +220,10 @@ def _stage_of(kernel_name):
     n = kernel_name
     if "prep_kernel" in n:
         return "prep"
-    if "prefix_kernel" in n:
+    if "prefix_kernel" in n or "pair_walk_kernel" in n:   # (the blocked prefix's block passes)
         return "prefix"
+    if "walk_out_kernel" in n:   # the walk that forms the outputs itself
+        return "walk"
     if "out_kernel" in n:
         return "out"
     if "walk_pair_kernel" in n:   # (walk only; no KIND argument)
@@ -497,7 +512,7 @@ def stage_times(w, step, steps, stage_bits, torch):
     HIP events that record its own start and end on the launch stream
     (gdn_chunk_fwd_timed), all steps queued back to back, the first dropped."""
     names = [n for n in ("prep", "fold", "prefix", "walk", "out")
-             if (w.n_groups > 1 or n not in ("fold", "prefix"))]
+             if (w.n_groups > 1 or n not in ("fold", "prefix")) and not (n == "out" and fused_walk(w))]
     bit = {n: stage_bits[n].bit_length() - 1 for n in names}
     nst = steps + 1
     ev = [[[None] * 5, [None] * 5] for _ in range(nst)]
