@@ -40,7 +40,9 @@ struct BwdArgs {
 // (wave w takes query tiles {w, R-1-w}, or {w} at C = 64), P^T's tiles in
 // registers, then written to LDS transposed next to dO^T for the product.
 template <int C, typename TI> struct BwdLds {
-  static constexpr int QK = C * D * (int)sizeof(TI);       // one row-major Q or K tile
+  static constexpr int LDQ = D + 16 / (int)sizeof(TI);     // Q, K row stride: 16 bytes of padding put
+                                                           // the 16 rows a fragment read touches on distinct banks
+  static constexpr int QK = C * LDQ * (int)sizeof(TI);     // one row-major Q or K tile
   static constexpr int LDT = C + 4;                        // row stride of the [D][C] transposed tiles
   static constexpr int LDW = D + 4;                        // row stride of W [C][D]
   static constexpr int TB = D * LDT * 4;                   // a transposed fp32 tile
@@ -82,8 +84,8 @@ __global__ __launch_bounds__(256) void bwd_ddh_kernel(FwdArgs fa, BwdArgs a) {
       xq = *reinterpret_cast<const uint4 *>(reinterpret_cast<const TI *>(a.q) + ((t0 + r) * a.Hqk + hq) * D + c);
       xk = *reinterpret_cast<const uint4 *>(reinterpret_cast<const TI *>(a.k) + ((t0 + r) * a.Hqk + hq) * D + c);
     }
-    *reinterpret_cast<uint4 *>(sQ + r * D + c) = xq;
-    *reinterpret_cast<uint4 *>(sK + r * D + c) = xk;
+    *reinterpret_cast<uint4 *>(sQ + r * L::LDQ + c) = xq;
+    *reinterpret_cast<uint4 *>(sK + r * L::LDQ + c) = xk;
   }
   for (int e = tid; e < C * D / 4; e += 256) {
     const int r = e / (D / 4), c = (e % (D / 4)) * 4;
@@ -96,7 +98,7 @@ __global__ __launch_bounds__(256) void bwd_ddh_kernel(FwdArgs fa, BwdArgs a) {
   // lane (lr, g) holds P^T[16kt + 4g + i][16rt + lr]; two key tiles stacked
   // are the A operand of P W with the keys in the order kk(g, j)
   auto row8 = [&](const TI *t, int r, int k0, float (&x)[8]) {   // 8 consecutive elements of row r
-    ld8(t + r * D + k0, x);
+    ld8(t + r * L::LDQ + k0, x);
   };
   f32x4 pt[RU][R];
   float qeff[RU][TD][4];
@@ -140,7 +142,7 @@ __global__ __launch_bounds__(256) void bwd_ddh_kernel(FwdArgs fa, BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int rr = 16 * rt + 4 * g + i;
-        qeff[u][dt][i] = exp2_fast(sG[rr] * LOG2E) * to_f32(sQ[rr * D + 16 * dt + lr]) - acc[i];
+        qeff[u][dt][i] = exp2_fast(sG[rr] * LOG2E) * to_f32(sQ[rr * L::LDQ + 16 * dt + lr]) - acc[i];
       }
     }
   }
@@ -179,264 +181,25 @@ __global__ __launch_bounds__(256) void bwd_ddh_kernel(FwdArgs fa, BwdArgs a) {
   }
 }
 
-// the reverse walk: one workgroup of eight waves per (batch, value head),
-// wave s holding the 16 columns 16s.. of dh in matrix-core result registers;
-// per chunk, from the last to the first, K (row-major, the input rows), W
-// (fp32, row stride D + 4) and G go to LDS, then
-//   Y = K dh,  X = diag(e^{G_last - G}) Y,  dh <- e^{G_last} dh - W^T X + ddh_n
-template <int C, typename TI, int MODE, bool RAG>
-__global__ __launch_bounds__(512) void bwd_walk_kernel(BwdArgs a) {
-  constexpr int PKD = MODE == MODE_F32 ? P_F32 : P_SPLIT_B;    // K (data) x dh
-  constexpr int PS = MODE == MODE_F32 ? P_F32 : P_SPLIT_AB;    // W^T x X
-  constexpr int MV = C / 16, MH = D / 16, KBW = D / 32, KBK = C / 32;
-  constexpr int LDW = D + 4;
-  __shared__ __align__(16) TI sK[C * D];
-  __shared__ __align__(16) float sW[C * LDW];
-  __shared__ __align__(16) float sG[C];
-  const size_t bh = blockIdx.x;
-  const int b = (int)(bh / a.Hv), hv = (int)(bh % a.Hv), hq = hv / (a.Hv / a.Hqk);
-  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, g = lane >> 4;
-  const int s = __builtin_amdgcn_readfirstlane(tid >> 6), c0 = 16 * s;
-  // dh tiles: dh[m] holds rows 16m + 4g + i, column c0 + lr
-  f32x4 dh[MH];
-#pragma unroll
-  for (int m = 0; m < MH; ++m)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dh[m][i] = a.dhT ? a.dhT[(bh * D + 16 * m + 4 * g + i) * D + c0 + lr] : 0.f;
-  // the k order of a k-block: two stacked result tiles give lane group g the
-  // rows kk(g, j) = 4g + j (j < 4), 16 + 4g + j - 4 (j >= 4)
-  auto kk = [&](int j) { return j < 4 ? 4 * g + j : 16 + 4 * g + j - 4; };
-  for (int n = a.N - 1; n >= 0; --n) {
-    const size_t cb = bh * a.N + n, t0 = (size_t)b * a.T + (size_t)n * C;
-    const int rows = !RAG ? C : (a.T - n * C < C ? a.T - n * C : C);
-    __syncthreads();   // every wave past the previous chunk's tiles
-    constexpr int VE = 16 / (int)sizeof(TI);
-    for (int e = tid; e < C * D / VE; e += 512) {
-      const int r = e / (D / VE), c = (e % (D / VE)) * VE;
-      uint4 x{0u, 0u, 0u, 0u};
-      if (r < rows) x = *reinterpret_cast<const uint4 *>(reinterpret_cast<const TI *>(a.k) + ((t0 + r) * a.Hqk + hq) * D + c);
-      *reinterpret_cast<uint4 *>(sK + r * D + c) = x;
-    }
-    for (int e = tid; e < C * D / 4; e += 512) {
-      const int r = e / (D / 4), c = (e % (D / 4)) * 4;
-      *reinterpret_cast<float4 *>(sW + r * LDW + c) = *reinterpret_cast<const float4 *>(a.W + (cb * C + r) * D + c);
-    }
-    if (tid < C) sG[tid] = a.G[cb * C + tid];
-    // the incoming-state cotangent of chunk n + 1 (the state after chunk n)
-    if (a.dh && n + 1 < a.N) {
-#pragma unroll
-      for (int m = 0; m < MH; ++m)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) a.dh[((bh * a.N + n + 1) * D + 16 * m + 4 * g + i) * D + c0 + lr] = dh[m][i];
-    }
-    __syncthreads();
-    const float gl2 = sG[C - 1] * LOG2E;
-    // Y = K dh: rows of the chunk (tiles mv), dh as the B operand
-    float db[KBW][8];
-#pragma unroll
-    for (int kb = 0; kb < KBW; ++kb)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) db[kb][j] = dh[2 * kb + j / 4][j % 4];
-    f32x4 y[MV];
-#pragma unroll
-    for (int mv = 0; mv < MV; ++mv) {
-      y[mv] = zero4();
-#pragma unroll
-      for (int kb = 0; kb < KBW; ++kb) {
-        float ka[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) ka[j] = to_f32(sK[(16 * mv + lr) * D + 32 * kb + kk(j)]);
-        mma_k32<PKD>(y[mv], ka, db[kb]);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) y[mv][i] *= exp2_fast(gl2 - sG[16 * mv + 4 * g + i] * LOG2E);
-    }
-    // dh <- e^{G_last} dh - W^T X + ddh_n
-    float xb[KBK][8];
-#pragma unroll
-    for (int kb = 0; kb < KBK; ++kb)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) xb[kb][j] = y[2 * kb + j / 4][j % 4];
-    const float gl = exp2_fast(gl2);
-#pragma unroll
-    for (int m = 0; m < MH; ++m) {
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int kb = 0; kb < KBK; ++kb) {
-        float wa[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) wa[j] = sW[(32 * kb + kk(j)) * LDW + 16 * m + lr];
-        mma_k32<PS>(acc, wa, xb[kb]);
-      }
-      const float4 dd = *reinterpret_cast<const float4 *>(a.ddh + ((cb * MH + s) * MH + m) * 256 + lane * 4);
-      const float ddv[4] = {dd.x, dd.y, dd.z, dd.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dh[m][i] = gl * dh[m][i] - acc[i] + ddv[i];
-    }
-  }
-  // chunk 0's incoming-state cotangent: that of h0
-#pragma unroll
-  for (int m = 0; m < MH; ++m)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const size_t e = (size_t)(16 * m + 4 * g + i) * D + c0 + lr;
-      if (a.dh) a.dh[(bh * a.N) * D * D + e] = dh[m][i];
-      if (a.dh0) a.dh0[bh * D * D + e] = dh[m][i];
-    }
-}
+__device__ __forceinline__ uint4 uint4_pair(uint2 a, uint2 b) { return uint4{a.x, a.y, b.x, b.y}; }
 
-// ----------------------------------------------------------------------------
-// The forward's incoming state of every chunk, fp32 row-major, for the
-// chunk gradients: h_0 = h0 and
-//   h_{n+1} = e^{G_last} h_n + K_g^T (U - W h_n),   K_g = diag(e^{G_last - G}) K,
-// with W and U of the transform form (fp32).  One workgroup of eight waves
-// per (batch, value head), wave s holding the 16 columns 16s.. of h in
-// matrix-core result registers, as in the reverse walk.
-struct StatesArgs {
-  int B, T, Hqk, Hv, N;
-  const void *k;              // [B, T, H_qk, D] input dtype
-  const float *G, *W, *U;     // transform form: [cb][C], [cb][C][D], [cb][C][D]
-  const float *h0;            // [B, H_v, D, D] or null (zero)
-  float *hs;                  // [B, H_v, N, D, D]
-};
-
-template <int C, typename TI, int MODE, bool RAG>
-__global__ __launch_bounds__(512) void fwd_states_kernel(StatesArgs a) {
-  constexpr int PW = MODE == MODE_F32 ? P_F32 : P_SPLIT_AB;   // W (fp32) x h
-  constexpr int PK = MODE == MODE_F32 ? P_F32 : P_SPLIT_B;    // K^T (data) x X
-  constexpr int MV = C / 16, MH = D / 16, KBW = D / 32, KBK = C / 32;
-  constexpr int LDW = D + 4;
-  __shared__ __align__(16) TI sK[C * D];
-  __shared__ __align__(16) float sW[C * LDW];
-  __shared__ __align__(16) float sG[C];
-  const size_t bh = blockIdx.x;
-  const int b = (int)(bh / a.Hv), hv = (int)(bh % a.Hv), hq = hv / (a.Hv / a.Hqk);
-  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, g = lane >> 4;
-  const int s = __builtin_amdgcn_readfirstlane(tid >> 6), c0 = 16 * s;
-  f32x4 h[MH];   // rows 16m + 4g + i, column c0 + lr
-#pragma unroll
-  for (int m = 0; m < MH; ++m)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) h[m][i] = a.h0 ? a.h0[(bh * D + 16 * m + 4 * g + i) * D + c0 + lr] : 0.f;
-  auto kk = [&](int j) { return j < 4 ? 4 * g + j : 16 + 4 * g + j - 4; };
-  for (int n = 0; n < a.N; ++n) {
-    const size_t cb = bh * a.N + n, t0 = (size_t)b * a.T + (size_t)n * C;
-    const int rows = !RAG ? C : (a.T - n * C < C ? a.T - n * C : C);
-    __syncthreads();
-    constexpr int VE = 16 / (int)sizeof(TI);
-    for (int e = tid; e < C * D / VE; e += 512) {
-      const int r = e / (D / VE), c = (e % (D / VE)) * VE;
-      uint4 x{0u, 0u, 0u, 0u};
-      if (r < rows) x = *reinterpret_cast<const uint4 *>(reinterpret_cast<const TI *>(a.k) + ((t0 + r) * a.Hqk + hq) * D + c);
-      *reinterpret_cast<uint4 *>(sK + r * D + c) = x;
-    }
-    for (int e = tid; e < C * D / 4; e += 512) {
-      const int r = e / (D / 4), c = (e % (D / 4)) * 4;
-      *reinterpret_cast<float4 *>(sW + r * LDW + c) = *reinterpret_cast<const float4 *>(a.W + (cb * C + r) * D + c);
-    }
-    if (tid < C) sG[tid] = a.G[cb * C + tid];
-#pragma unroll
-    for (int m = 0; m < MH; ++m)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a.hs[(cb * D + 16 * m + 4 * g + i) * D + c0 + lr] = h[m][i];
-    __syncthreads();
-    const float gl2 = sG[C - 1] * LOG2E;
-    // X = diag(e^{G_last - G}) (U - W h)
-    float hb[KBW][8];
-#pragma unroll
-    for (int kb = 0; kb < KBW; ++kb)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) hb[kb][j] = h[2 * kb + j / 4][j % 4];
-    // (U lands in the V' tiles themselves: no second set of registers)
-    f32x4 x[MV];
-#pragma unroll
-    for (int mv = 0; mv < MV; ++mv)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) x[mv][i] = a.U[(cb * C + 16 * mv + 4 * g + i) * D + c0 + lr];
-#pragma unroll
-    for (int mv = 0; mv < MV; ++mv) {
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int kb = 0; kb < KBW; ++kb) {
-        float wa[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) wa[j] = sW[(16 * mv + lr) * LDW + 32 * kb + kk(j)];
-        mma_k32<PW>(acc, wa, hb[kb]);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) x[mv][i] = (x[mv][i] - acc[i]) * exp2_fast(gl2 - sG[16 * mv + 4 * g + i] * LOG2E);
-    }
-    // h <- e^{G_last} h + K^T X
-    float xb[KBK][8];
-#pragma unroll
-    for (int kb = 0; kb < KBK; ++kb)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) xb[kb][j] = x[2 * kb + j / 4][j % 4];
-    const float gl = exp2_fast(gl2);
-#pragma unroll
-    for (int m = 0; m < MH; ++m) {
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int kb = 0; kb < KBK; ++kb) {
-        float ka[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) ka[j] = to_f32(sK[(32 * kb + kk(j)) * D + 16 * m + lr]);
-        mma_k32<PK>(acc, ka, xb[kb]);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) h[m][i] = gl * h[m][i] + acc[i];
-    }
+// 8 k-values of an input-dtype row in the order kk(g, j) (p points at the
+// block's first k-value): bf16 data as one exact bf16 fragment, fp32 as fp32
+template <typename TI>
+__device__ __forceinline__ Frag<sizeof(TI) == 2 ? F_BF16 : F_F32> kk_frag(const TI *p, int g) {
+  if constexpr (sizeof(TI) == 2) {
+    Frag<F_BF16> f;
+    f.hi = __builtin_bit_cast(bf16x8, uint4_pair(*reinterpret_cast<const uint2 *>(p + 4 * g),
+                                                 *reinterpret_cast<const uint2 *>(p + 16 + 4 * g)));
+    return f;
+  } else {
+    Frag<F_F32> f;
+    const float4 u = *reinterpret_cast<const float4 *>(p + 4 * g), w = *reinterpret_cast<const float4 *>(p + 16 + 4 * g);
+    f.v[0] = u.x; f.v[1] = u.y; f.v[2] = u.z; f.v[3] = u.w;
+    f.v[4] = w.x; f.v[5] = w.y; f.v[6] = w.z; f.v[7] = w.w;
+    return f;
   }
 }
-
-// ----------------------------------------------------------------------------
-// The gradients of one chunk (the adjoint of each line of the chunk's forward,
-// in reverse order; the chunk backward that the scan kernel of "Fuse the Gated
-// Delta Net inter-chunk scan into a Pallas TPU kernel", section "Changes",
-// walks, with the triangular inverse's analytic backward
-// dS = -(T^T dT T^T) on the strict lower triangle).  Given the chunk's
-// inputs, its incoming state h (fwd_states_kernel) and the cotangent dh' of
-// its outgoing state (the reverse walk's dh of the next chunk, or dh_T):
-//   V'  = U - W h                          P  = (Q K^T) o Gam o [i <= r]
-//   dP  = (dO V'^T) o [i <= r]             dR = dP o Gam
-//   dq  = diag(E) dO h^T + dR K
-//   dV  = P^T dO + diag(s) K dh'           (dV' over both paths; s = e^{G_last - G})
-//   dW  = -dV h^T                          dU~ = T^T dV,  dW~ = T^T dW
-//   dv  = diag(beta) dU~
-//   dT  = (dW K^T) diag(beta E) + (dV V^T) diag(beta)
-//   dS  = -strict-lower(T^T dT T^T)        dKk = diag(beta) dS o Gam
-//   dk  = diag(s) V' dh'^T + diag(beta E) dW~ + dR^T Q + (dKk + dKk^T) K
-//   dbeta_r = <dU~_r, v_r> + E_r <dW~_r, k_r> + sum_i dS_ri Gam_ri (K K^T)_ri
-//   dG_r = E_r <q_r, (dO h^T)_r> + beta_r E_r <dW~_r, k_r> - s_r <(V' dh'^T)_r, k_r>
-//          + (row r - column r sums of (dP o R + diag(beta) dS o K K^T) o Gam)
-//          + [r = last] (e^{G_last} <h, dh'> + sum_r s_r <(V' dh'^T)_r, k_r>)
-//   dg  = reverse cumulative sum of dG over the chunk
-// E = e^G, Gam_ri = e^{G_r - G_i} (i <= r).  One workgroup of eight waves
-// per (chunk, value head) at a time (a persistent grid).  Every product is a
-// set of 16 x 16 result tiles shared out over the waves, formed from its two
-// operands staged whole in LDS (two buffers of up to 128 x 128 fp32, loaded
-// with coalesced 16-byte reads, the chunk's inputs converted to fp32 with
-// zero rows past the sequence's end -- the identity padding of a partial last
-// chunk); either operand may be read transposed from its buffer.  The
-// intermediates go to the workgroup's scratch slot between products.
-__device__ float g_zero_state[D * D];   // dh' of the last chunk without dh_T
-
-struct GradArgs {
-  int B, T, Hqk, Hv, N, units;
-  const void *q, *k, *v;      // [B, T, H, D] input dtype
-  const float *beta;          // [B, T, H_v]
-  const float *dO;            // [B, T, H_v, D]
-  const float *G, *Tm, *W, *U;   // transform form: [cb][C], [cb][C][C], [cb][C][D], [cb][C][D]
-  const float *hs, *dh;       // [B, H_v, N, D, D]: incoming states, their cotangents
-  const float *dhT;           // [B, H_v, D, D] or null (zero)
-  float *dq, *dk;             // [B, T, qk_heads, D]
-  int per_value_head;         // dq, dk per value head (H_v heads) instead of per key head
-  float *dv;                  // [B, T, H_v, D]
-  float *dg, *dbeta;          // [B, T, H_v]
-  float *scratch;             // [gridDim.x][grad_slot_floats(C)]
-};
-
-template <int C> constexpr size_t grad_slot_floats() { return (size_t)5 * C * D + (size_t)7 * C * C; }
 
 // A staged operand in LDS: up to 128 rows (the rows of A, or the columns of
 // B, of a product) of up to 128 k-values each, k contiguous.  With bf16
@@ -484,6 +247,26 @@ template <int MODE> struct GStage {
         f[(c + 3) * GLDX + r] = x.w;
       }
     }
+  }
+  // row i, the k-values k0 + kk(g, j) of a block of 32 (k0 a multiple of
+  // 32): 4g .. 4g+3 and 16+4g .. 16+4g+3, the rows two stacked result tiles
+  // give lane group g
+  __device__ static Frag<KIND> frag_kk(const char *buf, int i, int k0, int g) {
+    Frag<KIND> f;
+    if constexpr (SPLIT) {
+      const __bf16 *hi = reinterpret_cast<const __bf16 *>(buf), *lo = hi + 128 * GLDH;
+      const int o = i * GLDH + k0 + 4 * g;
+      f.hi = __builtin_bit_cast(bf16x8, uint4_pair(*reinterpret_cast<const uint2 *>(hi + o),
+                                                   *reinterpret_cast<const uint2 *>(hi + o + 16)));
+      f.lo = __builtin_bit_cast(bf16x8, uint4_pair(*reinterpret_cast<const uint2 *>(lo + o),
+                                                   *reinterpret_cast<const uint2 *>(lo + o + 16)));
+    } else {
+      const float *x = reinterpret_cast<const float *>(buf) + i * GLDX + k0 + 4 * g;
+      const float4 u = *reinterpret_cast<const float4 *>(x), w = *reinterpret_cast<const float4 *>(x + 16);
+      f.v[0] = u.x; f.v[1] = u.y; f.v[2] = u.z; f.v[3] = u.w;
+      f.v[4] = w.x; f.v[5] = w.y; f.v[6] = w.z; f.v[7] = w.w;
+    }
+    return f;
   }
   // row i, k-values k0 .. k0+7 (k0 a multiple of 8)
   __device__ static Frag<KIND> frag(const char *buf, int i, int k0) {
@@ -541,6 +324,263 @@ __device__ __forceinline__ void stage_in(char *buf, const T *src, size_t ld, int
                                       float4{to_f32(x[j]), to_f32(x[j + 1]), to_f32(x[j + 2]), to_f32(x[j + 3])});
   }
 }
+
+// the reverse walk: one workgroup of eight waves per (batch, value head),
+// wave s holding the 16 columns 16s.. of dh in matrix-core result registers;
+// per chunk, from the last to the first, K (row-major, the input rows), W
+// (fp32, row stride D + 4) and G go to LDS, then
+//   Y = K dh,  X = diag(e^{G_last - G}) Y,  dh <- e^{G_last} dh - W^T X + ddh_n
+template <int C, typename TI, int MODE, bool RAG>
+__global__ __launch_bounds__(512) void bwd_walk_kernel(BwdArgs a) {
+  constexpr int PKD = MODE == MODE_F32 ? P_F32 : P_SPLIT_B;    // K (data) x dh
+  constexpr int PS = MODE == MODE_F32 ? P_F32 : P_SPLIT_AB;    // W^T x X
+  constexpr int MV = C / 16, MH = D / 16, KBW = D / 32, KBK = C / 32;
+  constexpr int LDW = D + 4;
+  constexpr int LDK = D + 16 / (int)sizeof(TI);   // K row stride: 16 bytes of padding put the
+                                                  // 16 rows a fragment read touches on distinct banks
+  __shared__ __align__(16) TI sK[C * LDK];      // K rows
+  __shared__ __align__(16) float sW[C * LDW];   // W rows (fp32; read by columns as W^T)
+  __shared__ __align__(16) float sG[C];
+  const size_t bh = blockIdx.x;
+  const int b = (int)(bh / a.Hv), hv = (int)(bh % a.Hv), hq = hv / (a.Hv / a.Hqk);
+  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, g = lane >> 4;
+  const int s = __builtin_amdgcn_readfirstlane(tid >> 6), c0 = 16 * s;
+  // dh tiles: dh[m] holds rows 16m + 4g + i, column c0 + lr
+  f32x4 dh[MH];
+#pragma unroll
+  for (int m = 0; m < MH; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dh[m][i] = a.dhT ? a.dhT[(bh * D + 16 * m + 4 * g + i) * D + c0 + lr] : 0.f;
+  for (int n = a.N - 1; n >= 0; --n) {
+    const size_t cb = bh * a.N + n, t0 = (size_t)b * a.T + (size_t)n * C;
+    const int rows = !RAG ? C : (a.T - n * C < C ? a.T - n * C : C);
+    __syncthreads();   // every wave past the previous chunk's tiles
+    constexpr int VE = 16 / (int)sizeof(TI);
+    for (int e = tid; e < C * D / VE; e += 512) {
+      const int r = e / (D / VE), c = (e % (D / VE)) * VE;
+      uint4 x{0u, 0u, 0u, 0u};
+      if (r < rows) x = *reinterpret_cast<const uint4 *>(reinterpret_cast<const TI *>(a.k) + ((t0 + r) * a.Hqk + hq) * D + c);
+      *reinterpret_cast<uint4 *>(sK + r * LDK + c) = x;
+    }
+    for (int e = tid; e < C * D / 4; e += 512) {
+      const int r = e / (D / 4), c = (e % (D / 4)) * 4;
+      *reinterpret_cast<float4 *>(sW + r * LDW + c) = *reinterpret_cast<const float4 *>(a.W + (cb * C + r) * D + c);
+    }
+    if (tid < C) sG[tid] = a.G[cb * C + tid];
+    // the incoming-state cotangent of chunk n + 1 (the state after chunk n)
+    if (a.dh && n + 1 < a.N) {
+#pragma unroll
+      for (int m = 0; m < MH; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a.dh[((bh * a.N + n + 1) * D + 16 * m + 4 * g + i) * D + c0 + lr] = dh[m][i];
+    }
+    __syncthreads();
+    const float gl2 = sG[C - 1] * LOG2E;
+    // Y = K dh, dh as the B operand split once for all row tiles (two
+    // stacked result tiles give lane group g the k-values kk(g, j))
+    Frag<PolicyKinds<PKD>::b> db[KBW];
+#pragma unroll
+    for (int kb = 0; kb < KBW; ++kb) {
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = dh[2 * kb + j / 4][j % 4];
+      db[kb] = make_frag<PolicyKinds<PKD>::b>(x);
+    }
+    f32x4 y[MV];
+#pragma unroll
+    for (int mv = 0; mv < MV; ++mv) {
+      y[mv] = zero4();
+#pragma unroll
+      for (int kb = 0; kb < KBW; ++kb) mma(y[mv], kk_frag<TI>(sK + (16 * mv + lr) * LDK + 32 * kb, g), db[kb]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) y[mv][i] *= exp2_fast(gl2 - sG[16 * mv + 4 * g + i] * LOG2E);
+    }
+    // dh <- e^{G_last} dh - W^T X + ddh_n, X split once
+    Frag<PolicyKinds<PS>::b> xb[KBK];
+#pragma unroll
+    for (int kb = 0; kb < KBK; ++kb) {
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = y[2 * kb + j / 4][j % 4];
+      xb[kb] = make_frag<PolicyKinds<PS>::b>(x);
+    }
+    const float gl = exp2_fast(gl2);
+#pragma unroll
+    for (int m = 0; m < MH; ++m) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int kb = 0; kb < KBK; ++kb) {
+        // W^T's row 16m + lr, k-values kk(g, j): column 16m + lr of W
+        float wa[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) wa[jj] = sW[(32 * kb + (jj < 4 ? 4 * g + jj : 16 + 4 * g + jj - 4)) * LDW + 16 * m + lr];
+        mma(acc, make_frag<PolicyKinds<PS>::a>(wa), xb[kb]);
+      }
+      const float4 dd = *reinterpret_cast<const float4 *>(a.ddh + ((cb * MH + s) * MH + m) * 256 + lane * 4);
+      const float ddv[4] = {dd.x, dd.y, dd.z, dd.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dh[m][i] = gl * dh[m][i] - acc[i] + ddv[i];
+    }
+  }
+  // chunk 0's incoming-state cotangent: that of h0
+#pragma unroll
+  for (int m = 0; m < MH; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const size_t e = (size_t)(16 * m + 4 * g + i) * D + c0 + lr;
+      if (a.dh) a.dh[(bh * a.N) * D * D + e] = dh[m][i];
+      if (a.dh0) a.dh0[bh * D * D + e] = dh[m][i];
+    }
+}
+
+// ----------------------------------------------------------------------------
+// The forward's incoming state of every chunk, fp32 row-major, for the
+// chunk gradients: h_0 = h0 and
+//   h_{n+1} = e^{G_last} h_n + K_g^T (U - W h_n),   K_g = diag(e^{G_last - G}) K,
+// with W and U of the transform form (fp32).  One workgroup of eight waves
+// per (batch, value head), wave s holding the 16 columns 16s.. of h in
+// matrix-core result registers, as in the reverse walk.
+struct StatesArgs {
+  int B, T, Hqk, Hv, N;
+  const void *k;              // [B, T, H_qk, D] input dtype
+  const float *G, *W, *U;     // transform form: [cb][C], [cb][C][D], [cb][C][D]
+  const float *h0;            // [B, H_v, D, D] or null (zero)
+  float *hs;                  // [B, H_v, N, D, D]
+};
+
+template <int C, typename TI, int MODE, bool RAG>
+__global__ __launch_bounds__(512) void fwd_states_kernel(StatesArgs a) {
+  constexpr int PW = MODE == MODE_F32 ? P_F32 : P_SPLIT_AB;   // W (fp32) x h
+  constexpr int PK = MODE == MODE_F32 ? P_F32 : P_SPLIT_B;    // K^T (data) x X
+  using GS = GStage<MODE>;
+  static_assert(PolicyKinds<PW>::a == GS::KIND, "W staged as the product's A operand");
+  constexpr int MV = C / 16, MH = D / 16, KBW = D / 32, KBK = C / 32;
+  constexpr int LDKT = C + 8;                     // K^T row stride (elements)
+  __shared__ __align__(16) TI sKt[D * LDKT];      // K^T: row d, the chunk's tokens along k
+  __shared__ __align__(16) char sW[GS::BYTES];    // W rows, split once
+  __shared__ __align__(16) float sG[C];
+  const size_t bh = blockIdx.x;
+  const int b = (int)(bh / a.Hv), hv = (int)(bh % a.Hv), hq = hv / (a.Hv / a.Hqk);
+  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, g = lane >> 4;
+  const int s = __builtin_amdgcn_readfirstlane(tid >> 6), c0 = 16 * s;
+  f32x4 h[MH];   // rows 16m + 4g + i, column c0 + lr
+#pragma unroll
+  for (int m = 0; m < MH; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) h[m][i] = a.h0 ? a.h0[(bh * D + 16 * m + 4 * g + i) * D + c0 + lr] : 0.f;
+  for (int n = 0; n < a.N; ++n) {
+    const size_t cb = bh * a.N + n, t0 = (size_t)b * a.T + (size_t)n * C;
+    const int rows = !RAG ? C : (a.T - n * C < C ? a.T - n * C : C);
+    __syncthreads();
+    constexpr int VE = 16 / (int)sizeof(TI);
+    for (int e = tid; e < C * D / VE; e += 512) {
+      const int r = e / (D / VE), c = (e % (D / VE)) * VE;
+      uint4 v{0u, 0u, 0u, 0u};
+      if (r < rows) v = *reinterpret_cast<const uint4 *>(reinterpret_cast<const TI *>(a.k) + ((t0 + r) * a.Hqk + hq) * D + c);
+      const TI *x = reinterpret_cast<const TI *>(&v);
+#pragma unroll
+      for (int j = 0; j < VE; ++j) sKt[(c + j) * LDKT + r] = x[j];
+    }
+    stage<MODE, C, D, false>(sW, a.W + cb * C * D, D, tid);
+    if (tid < C) sG[tid] = a.G[cb * C + tid];
+#pragma unroll
+    for (int m = 0; m < MH; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a.hs[(cb * D + 16 * m + 4 * g + i) * D + c0 + lr] = h[m][i];
+    __syncthreads();
+    const float gl2 = sG[C - 1] * LOG2E;
+    // X = diag(e^{G_last - G}) (U - W h), h as the B operand split once (U
+    // lands in the V' tiles themselves)
+    Frag<PolicyKinds<PW>::b> hb[KBW];
+#pragma unroll
+    for (int kb = 0; kb < KBW; ++kb) {
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = h[2 * kb + j / 4][j % 4];
+      hb[kb] = make_frag<PolicyKinds<PW>::b>(x);
+    }
+    f32x4 x[MV];
+#pragma unroll
+    for (int mv = 0; mv < MV; ++mv) {
+      // (one row tile's U at a time: hoisted all at once they outgrow the registers)
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[mv][i] = a.U[(cb * C + 16 * mv + 4 * g + i) * D + c0 + lr];
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int kb = 0; kb < KBW; ++kb) mma(acc, GS::frag_kk(sW, 16 * mv + lr, 32 * kb, g), hb[kb]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[mv][i] = (x[mv][i] - acc[i]) * exp2_fast(gl2 - sG[16 * mv + 4 * g + i] * LOG2E);
+    }
+    // h <- e^{G_last} h + K^T X, X split once
+    Frag<PolicyKinds<PK>::b> xb[KBK];
+#pragma unroll
+    for (int kb = 0; kb < KBK; ++kb) {
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = x[2 * kb + j / 4][j % 4];
+      xb[kb] = make_frag<PolicyKinds<PK>::b>(v);
+    }
+    const float gl = exp2_fast(gl2);
+#pragma unroll
+    for (int m = 0; m < MH; ++m) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int kb = 0; kb < KBK; ++kb) mma(acc, kk_frag<TI>(sKt + (16 * m + lr) * LDKT + 32 * kb, g), xb[kb]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) h[m][i] = gl * h[m][i] + acc[i];
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// The gradients of one chunk (the adjoint of each line of the chunk's forward,
+// in reverse order; the chunk backward that the scan kernel of "Fuse the Gated
+// Delta Net inter-chunk scan into a Pallas TPU kernel", section "Changes",
+// walks, with the triangular inverse's analytic backward
+// dS = -(T^T dT T^T) on the strict lower triangle).  Given the chunk's
+// inputs, its incoming state h (fwd_states_kernel) and the cotangent dh' of
+// its outgoing state (the reverse walk's dh of the next chunk, or dh_T):
+//   V'  = U - W h                          P  = (Q K^T) o Gam o [i <= r]
+//   dP  = (dO V'^T) o [i <= r]             dR = dP o Gam
+//   dq  = diag(E) dO h^T + dR K
+//   dV  = P^T dO + diag(s) K dh'           (dV' over both paths; s = e^{G_last - G})
+//   dW  = -dV h^T                          dU~ = T^T dV,  dW~ = T^T dW
+//   dv  = diag(beta) dU~
+//   dT  = (dW K^T) diag(beta E) + (dV V^T) diag(beta)
+//   dS  = -strict-lower(T^T dT T^T)        dKk = diag(beta) dS o Gam
+//   dk  = diag(s) V' dh'^T + diag(beta E) dW~ + dR^T Q + (dKk + dKk^T) K
+//   dbeta_r = <dU~_r, v_r> + E_r <dW~_r, k_r> + sum_i dS_ri Gam_ri (K K^T)_ri
+//   dG_r = E_r <q_r, (dO h^T)_r> + beta_r E_r <dW~_r, k_r> - s_r <(V' dh'^T)_r, k_r>
+//          + (row r - column r sums of (dP o R + diag(beta) dS o K K^T) o Gam)
+//          + [r = last] (e^{G_last} <h, dh'> + sum_r s_r <(V' dh'^T)_r, k_r>)
+//   dg  = reverse cumulative sum of dG over the chunk
+// E = e^G, Gam_ri = e^{G_r - G_i} (i <= r).  One workgroup of eight waves
+// per (chunk, value head) at a time (a persistent grid).  Every product is a
+// set of 16 x 16 result tiles shared out over the waves, formed from its two
+// operands staged whole in LDS (two buffers of up to 128 x 128 fp32, loaded
+// with coalesced 16-byte reads, the chunk's inputs converted to fp32 with
+// zero rows past the sequence's end -- the identity padding of a partial last
+// chunk); either operand may be read transposed from its buffer.  The
+// intermediates go to the workgroup's scratch slot between products.
+__device__ float g_zero_state[D * D];   // dh' of the last chunk without dh_T
+
+struct GradArgs {
+  int B, T, Hqk, Hv, N, units;
+  const void *q, *k, *v;      // [B, T, H, D] input dtype
+  const float *beta;          // [B, T, H_v]
+  const float *dO;            // [B, T, H_v, D]
+  const float *G, *Tm, *W, *U;   // transform form: [cb][C], [cb][C][C], [cb][C][D], [cb][C][D]
+  const float *hs, *dh;       // [B, H_v, N, D, D]: incoming states, their cotangents
+  const float *dhT;           // [B, H_v, D, D] or null (zero)
+  float *dq, *dk;             // [B, T, qk_heads, D]
+  int per_value_head;         // dq, dk per value head (H_v heads) instead of per key head
+  float *dv;                  // [B, T, H_v, D]
+  float *dg, *dbeta;          // [B, T, H_v]
+  float *scratch;             // [gridDim.x][grad_slot_floats(C)]
+};
+
+template <int C> constexpr size_t grad_slot_floats() { return (size_t)5 * C * D + (size_t)7 * C * C; }
 
 // acc += A B for the 16 x 16 tile (rows i0.. of A, columns j0.. of B) over K
 // k-values: A staged with its rows, B with its columns, along the buffer rows.

@@ -590,6 +590,31 @@ def test_bwd_grads_match_oracle(gdn, dtype, C, B, Hqk, Hv, T):
         assert torch.count_nonzero(z[name]) == 0, name
 
 
+@pytest.mark.timeout(900)
+def test_bwd_grads_full_size(gdn):
+    # the backward at the 4096-token layer's full size and in the launch
+    # configuration the bench times (chunk 128, 16 key / 32 value heads, h0
+    # drawn), every gradient element against the oracle's per-token reverse
+    # pass of the rule (about ten seconds of host work); bar as for the small
+    # cases
+    from oracle import backward
+
+    w = WORKLOADS["qwen3next_8b_layer"]
+    x = make_inputs(w, device="cuda")
+    gen = torch.Generator().manual_seed(77)
+    dO = torch.randn((w.B, w.T, w.Hv, 128), generator=gen).to("cuda")
+    dhT = (torch.randn((w.B, w.Hv, 128, 128), generator=gen) * 0.1).to("cuda")
+    got = gdn.chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], dO, h0=x["h0"], dh_T=dhT, chunk=w.chunk)
+    torch.cuda.synchronize()
+    got = {kk: vv.cpu().numpy() for kk, vv in got.items()}
+    ref = backward.bwd(*[_cpu(x[kk]) for kk in ("q", "k", "v", "g", "beta", "h0")], do=_cpu(dO), dhT=_cpu(dhT))
+    for name in ("dq", "dk", "dv", "dg", "dbeta", "dh0"):
+        r = ref[name]
+        e = _err(got[name], r)
+        print(f"  {name}: max-abs {e:.3e}  limit {1e-3 * _rms(r):.3e}", flush=True)
+        assert e <= 1e-3 * _rms(r), name
+
+
 def test_long_sequence_reduced(gdn):
     # the long-sequence workload's shape and group structure at 1/16 of its length
     w = WORKLOADS["long_256k"].replace(T=16384, n_groups=16)
