@@ -248,6 +248,27 @@ template <int MODE> struct GStage {
       }
     }
   }
+  // a 4 x 4 block of the source, rows r0 .. r0+3 and columns c0 .. c0+3
+  // (v[row][column]), transposed: column c0 + e becomes row c0 + e with the
+  // four values at r0 .. r0+3 (one 8-byte write per plane and row)
+  __device__ static void put4x4t(char *buf, int r0, int c0, const float (&v)[4][4]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (SPLIT) {
+        unsigned short *hi = reinterpret_cast<unsigned short *>(buf), *lo = hi + 128 * GLDH;
+        const unsigned h01 = pk_bf16(v[0][e], v[1][e]), h23 = pk_bf16(v[2][e], v[3][e]);
+        const unsigned l01 = pk_bf16(v[0][e] - __builtin_bit_cast(float, h01 << 16),
+                                     v[1][e] - __builtin_bit_cast(float, h01 & 0xffff0000u));
+        const unsigned l23 = pk_bf16(v[2][e] - __builtin_bit_cast(float, h23 << 16),
+                                     v[3][e] - __builtin_bit_cast(float, h23 & 0xffff0000u));
+        *reinterpret_cast<uint2 *>(hi + (c0 + e) * GLDH + r0) = uint2{h01, h23};
+        *reinterpret_cast<uint2 *>(lo + (c0 + e) * GLDH + r0) = uint2{l01, l23};
+      } else {
+        *reinterpret_cast<float4 *>(reinterpret_cast<float *>(buf) + (c0 + e) * GLDX + r0) =
+            float4{v[0][e], v[1][e], v[2][e], v[3][e]};
+      }
+    }
+  }
   // row i, the k-values k0 + kk(g, j) of a block of 32 (k0 a multiple of
   // 32): 4g .. 4g+3 and 16+4g .. 16+4g+3, the rows two stacked result tiles
   // give lane group g
@@ -285,43 +306,90 @@ template <int MODE> struct GStage {
   }
 };
 
-// NR x NC fp32 rows (row stride ld) staged, 512 threads
+// NR x NC fp32 rows (row stride ld) staged, 512 threads.  Transposed, each
+// thread takes 4 x 4 blocks, the lanes of a wave consecutive row blocks of
+// one column block, so that the transposed rows are written contiguously
 template <int MODE, int NR, int NC, bool TR>
 __device__ __forceinline__ void stage(char *buf, const float *src, size_t ld, int tid) {
-  constexpr int N4 = NR * NC / 4, PER = N4 / 512;
-  static_assert(N4 % 512 == 0, "whole float4 per thread");
-  float4 v[PER];
+  if constexpr (!TR) {
+    constexpr int N4 = NR * NC / 4, PER = N4 / 512;
+    static_assert(N4 % 512 == 0, "whole float4 per thread");
+    float4 v[PER];
 #pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    const int e = tid + 512 * u, r = e / (NC / 4), c = (e % (NC / 4)) * 4;
-    v[u] = *reinterpret_cast<const float4 *>(src + r * ld + c);
-  }
+    for (int u = 0; u < PER; ++u) {
+      const int e = tid + 512 * u, r = e / (NC / 4), c = (e % (NC / 4)) * 4;
+      v[u] = *reinterpret_cast<const float4 *>(src + r * ld + c);
+    }
 #pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    const int e = tid + 512 * u, r = e / (NC / 4), c = (e % (NC / 4)) * 4;
-    GStage<MODE>::template put4<TR>(buf, r, c, v[u]);
+    for (int u = 0; u < PER; ++u) {
+      const int e = tid + 512 * u, r = e / (NC / 4), c = (e % (NC / 4)) * 4;
+      GStage<MODE>::template put4<false>(buf, r, c, v[u]);
+    }
+  } else {
+    constexpr int RB = NR / 4, NB = RB * (NC / 4), PER = (NB + 511) / 512;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int b = tid + 512 * u;
+      if (NB % 512 != 0 && b >= NB) break;
+      const int r0 = 4 * (b % RB), c0 = 4 * (b / RB);
+      float v[4][4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 x = *reinterpret_cast<const float4 *>(src + (r0 + i) * ld + c0);
+        v[i][0] = x.x; v[i][1] = x.y; v[i][2] = x.z; v[i][3] = x.w;
+      }
+      GStage<MODE>::put4x4t(buf, r0, c0, v);
+    }
   }
 }
 // NR x D input rows of type T (row stride ld elements) staged as fp32 values,
 // rows at or past `rows` zero
 template <int MODE, int NR, bool TR, typename T>
 __device__ __forceinline__ void stage_in(char *buf, const T *src, size_t ld, int rows, int tid) {
-  constexpr int VE = 16 / (int)sizeof(T), NV = NR * D / VE, PER = NV / 512;
-  static_assert(NV % 512 == 0, "whole vectors per thread");
-  uint4 v[PER];
+  constexpr int VE = 16 / (int)sizeof(T);
+  if constexpr (!TR) {
+    constexpr int NV = NR * D / VE, PER = NV / 512;
+    static_assert(NV % 512 == 0, "whole vectors per thread");
+    uint4 v[PER];
 #pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    const int e = tid + 512 * u, r = e / (D / VE), c = (e % (D / VE)) * VE;
-    v[u] = r < rows ? *reinterpret_cast<const uint4 *>(src + r * ld + c) : uint4{0u, 0u, 0u, 0u};
-  }
+    for (int u = 0; u < PER; ++u) {
+      const int e = tid + 512 * u, r = e / (D / VE), c = (e % (D / VE)) * VE;
+      v[u] = r < rows ? *reinterpret_cast<const uint4 *>(src + r * ld + c) : uint4{0u, 0u, 0u, 0u};
+    }
 #pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    const int e = tid + 512 * u, r = e / (D / VE), c = (e % (D / VE)) * VE;
-    const T *x = reinterpret_cast<const T *>(&v[u]);
+    for (int u = 0; u < PER; ++u) {
+      const int e = tid + 512 * u, r = e / (D / VE), c = (e % (D / VE)) * VE;
+      const T *x = reinterpret_cast<const T *>(&v[u]);
 #pragma unroll
-    for (int j = 0; j < VE; j += 4)
-      GStage<MODE>::template put4<TR>(buf, r, c + j,
-                                      float4{to_f32(x[j]), to_f32(x[j + 1]), to_f32(x[j + 2]), to_f32(x[j + 3])});
+      for (int j = 0; j < VE; j += 4)
+        GStage<MODE>::template put4<false>(buf, r, c + j,
+                                           float4{to_f32(x[j]), to_f32(x[j + 1]), to_f32(x[j + 2]), to_f32(x[j + 3])});
+    }
+  } else {
+    // blocks of 4 rows x one 16-byte vector, the lanes of a wave consecutive
+    // row blocks of one column block (as in stage)
+    constexpr int RB = NR / 4, NB = RB * (D / VE), PER = (NB + 511) / 512;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int b = tid + 512 * u;
+      if (NB % 512 != 0 && b >= NB) break;
+      const int r0 = 4 * (b % RB), c0 = VE * (b / RB);
+      uint4 w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        w[i] = r0 + i < rows ? *reinterpret_cast<const uint4 *>(src + (r0 + i) * ld + c0) : uint4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int h = 0; h < VE; h += 4) {
+        float v[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const T *x = reinterpret_cast<const T *>(&w[i]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[i][e] = to_f32(x[h + e]);
+        }
+        GStage<MODE>::put4x4t(buf, r0, c0 + h, v);
+      }
+    }
   }
 }
 
