@@ -540,14 +540,29 @@ __global__ __launch_bounds__(512) void fwd_states_kernel(StatesArgs a) {
     const size_t cb = bh * a.N + n, t0 = (size_t)b * a.T + (size_t)n * C;
     const int rows = !RAG ? C : (a.T - n * C < C ? a.T - n * C : C);
     __syncthreads();
-    constexpr int VE = 16 / (int)sizeof(TI);
-    for (int e = tid; e < C * D / VE; e += 512) {
-      const int r = e / (D / VE), c = (e % (D / VE)) * VE;
-      uint4 v{0u, 0u, 0u, 0u};
-      if (r < rows) v = *reinterpret_cast<const uint4 *>(reinterpret_cast<const TI *>(a.k) + ((t0 + r) * a.Hqk + hq) * D + c);
-      const TI *x = reinterpret_cast<const TI *>(&v);
+    // K^T: blocks of 4 rows x one 16-byte vector transposed in registers, the
+    // lanes of a wave consecutive row blocks, so that each transposed row is
+    // written 4 values per lane, contiguous across lanes
+    constexpr int VE = 16 / (int)sizeof(TI), RB = C / 4, NB = RB * (D / VE);
+    struct Four {
+      TI v[4];
+    };
+    using W4 = typename std::conditional<sizeof(TI) == 2, uint2, uint4>::type;
+    for (int bk = tid; bk < NB; bk += 512) {
+      const int r0 = 4 * (bk % RB), c = VE * (bk / RB);
+      uint4 w[4];
 #pragma unroll
-      for (int j = 0; j < VE; ++j) sKt[(c + j) * LDKT + r] = x[j];
+      for (int i = 0; i < 4; ++i)
+        w[i] = r0 + i < rows ? *reinterpret_cast<const uint4 *>(reinterpret_cast<const TI *>(a.k) +
+                                                                ((t0 + r0 + i) * a.Hqk + hq) * D + c)
+                             : uint4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int j = 0; j < VE; ++j) {
+        Four f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f.v[i] = reinterpret_cast<const TI *>(&w[i])[j];
+        *reinterpret_cast<W4 *>(sKt + (c + j) * LDKT + r0) = __builtin_bit_cast(W4, f);
+      }
     }
     stage<MODE, C, D, false>(sW, a.W + cb * C * D, D, tid);
     if (tid < C) sG[tid] = a.G[cb * C + tid];
