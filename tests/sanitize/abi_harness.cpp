@@ -77,6 +77,20 @@ int main() {
   expect(gdn_workspace_size_varlen(&vl, &bytes), GDN_OK, "varlen workspace");
   expect(gdn_chunk_fwd_varlen(&vl, nullptr, ok, ok, ok, fk, fk, nullptr, ok, nullptr, ok, bytes, nullptr),
          GDN_ERR_NULL, "varlen null offsets");
+  // the backward: one walk per sequence, required pointers, alignment, workspace
+  expect(gdn_workspace_size_bwd_grads(&s, &bytes), GDN_OK, "backward workspace");
+  expect(gdn_chunk_bwd(&s, ok, ok, ok, fk, fk, nullptr, fk, nullptr, nullptr, fo, fo, fo, fo, nullptr, ok, bytes,
+                       nullptr),
+         GDN_ERR_NULL, "backward null dq");
+  expect(gdn_chunk_bwd(&s, ok, ok, ok, fk, fk, nullptr, fk, nullptr, fo, fo, fo, fo, fo, nullptr, ok, bytes - 1,
+                       nullptr),
+         GDN_ERR_WORKSPACE, "backward workspace too small");
+  expect(gdn_chunk_bwd(&grouped, ok, ok, ok, fk, fk, nullptr, fk, nullptr, fo, fo, fo, fo, fo, nullptr, ok, bytes,
+                       nullptr),
+         GDN_ERR_SHAPE, "backward grouped");
+  expect(gdn_chunk_bwd(&s, reinterpret_cast<const void *>(odd), ok, ok, fk, fk, nullptr, fk, nullptr, fo, fo, fo, fo,
+                       fo, nullptr, ok, bytes, nullptr),
+         GDN_ERR_ALIGN, "backward misaligned q");
   for (int c = -7; c <= 1; ++c)
     if (!gdn_status_str((gdn_status)c)) { std::fprintf(stderr, "FAILED: status string %d\n", c); ++fails; }
   if (fails) return 1;

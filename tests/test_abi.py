@@ -146,6 +146,38 @@ def test_entry_points_reject_bad_arguments_without_launching(gdn):
     assert L.gdn_chunk_fwd_affine(ctypes.byref(grouped), ok, ok, ok, ok, ok, null, ok, null, ok, ok, ws, null) == -2
 
 
+def test_backward_checks_without_launching(gdn):
+    # gdn_chunk_bwd and gdn_chunk_bwd_state: one walk per sequence (no
+    # chunk-groups), every input and gradient required (dh0 optional), 16-byte
+    # alignment, workspace size; all rejected before anything is launched
+    L = gdn.lib()
+    s = _shape(gdn)
+    ws = gdn.workspace_size_bwd_grads(s)
+    assert ws > gdn.workspace_size(s)
+    assert gdn.workspace_size_bwd_grads(_shape(gdn, T=8192)) > ws
+    with pytest.raises(gdn.GdnError):
+        gdn.workspace_size_bwd_grads(_shape(gdn, n_groups=4))
+    ok = _fake(1 << 20)
+    odd = _fake((1 << 20) + 4)
+    null = None
+    good = [ok] * 8 + [ok] * 5 + [null]   # q k v g beta h0 dO dh_T | dq dk dv dg dbeta | dh0
+    def call(args, shape=s, nbytes=ws):
+        return L.gdn_chunk_bwd(ctypes.byref(shape), *args, ok, nbytes, null)
+    for i in (0, 1, 2, 3, 4, 6, 8, 9, 10, 11, 12):   # required pointers
+        args = list(good)
+        args[i] = null
+        assert call(args) == -1, i
+    for i in range(14):
+        args = list(good)
+        args[i] = odd
+        assert call(args) == -4, i
+    assert call(good, nbytes=ws - 1) == -5
+    assert call(good, shape=_shape(gdn, n_groups=4)) == -2
+    assert call(good, shape=_shape(gdn, chunk=96)) == -2
+    # the state cotangents alone: at least one output
+    assert L.gdn_chunk_bwd_state(ctypes.byref(s), ok, ok, ok, ok, ok, null, null, null, ok, ws, null) == -1
+
+
 def test_varlen_checks_without_launching(gdn):
     # packed sequences: one walk per sequence (no chunk-groups); NULL offsets
     # are rejected before anything is launched
