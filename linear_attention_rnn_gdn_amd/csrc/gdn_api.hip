@@ -218,9 +218,10 @@ gdn_status launch_walk_out(const FwdArgs &a, const Lx &x) {
 // (at least 3: a block's slots hold its composed pair and incoming state), if
 // the blocked prefix is expected to be faster; 0 = the sequential prefix.
 // Both are modelled from their MI355X timings over 1..32 rows and 32..1024
-// pairs: the sequential prefix costs the larger of 2.75 us per pair (a chain
-// of dependent steps) and its traffic (A and B read, h_in written: 3 * 64 KB
-// per pair) at 2.1 TB/s; the blocked one the larger of its 2 s + n / s steps
+// pairs: the sequential prefix costs the larger of 2.1 us per pair with
+// split-bf16 products, 2.55 us with fp32 ones (a chain of dependent steps),
+// and its traffic (A and B read, h_in written: 3 * 64 KB per pair) at 2.5
+// (2.15) TB/s; the blocked one the larger of its 2 s + n / s steps
 // (5.6 us each with split-bf16 products, 9 us with fp32 ones) and its
 // traffic (A and B read twice: 5 * 64 KB per pair) at 2.4 TB/s.
 // force: the blocked prefix whenever n has such a divisor.
@@ -231,9 +232,17 @@ int prefix_block(int n, int BH, bool split, bool force) {
     if (n % c == 0 && (s == 0 || std::abs(c * c - n) < std::abs(s * s - n))) s = c;
   if (s == 0 || force) return s;
   const double pair_bytes = (double)D * D * 4 * BH;
-  const double t_seq = std::max(n * 2.75e-6, 3 * pair_bytes * n / 2.1e12);
+  const double t_seq = std::max(n * (split ? 2.1e-6 : 2.55e-6), 3 * pair_bytes * n / (split ? 2.5e12 : 2.15e12));
   const double t_blk = std::max((2 * s + n / s) * (split ? 5.6e-6 : 9e-6), 5 * pair_bytes * n / 2.4e12);
   return t_blk < t_seq ? s : 0;
+}
+
+// the sequential prefix kernel for the precision and whether h_in is written
+void launch_prefix_seq(bool split, bool hin, dim3 grid, dim3 block, const Lx &x, const PrefixArgs &p) {
+  if (split && hin) launch(prefix_kernel<P_SPLIT_AB, 4, true>, grid, block, x, p);
+  else if (split) launch(prefix_kernel<P_SPLIT_AB, 4, false>, grid, block, x, p);
+  else if (hin) launch(prefix_kernel<P_F32, 4, true>, grid, block, x, p);
+  else launch(prefix_kernel<P_F32, 4, false>, grid, block, x, p);
 }
 
 gdn_status launch_prefix(int BH, int n, const float *A, const float *Bm, const float *h_init, float *h_in,
@@ -243,10 +252,7 @@ gdn_status launch_prefix(int BH, int n, const float *A, const float *Bm, const f
   if (s == 0) {
     PrefixArgs p{BH, n, A, Bm, h_init, h_in, h_final};
     const unsigned blocks = (unsigned)(D / 16) * BH;   // one workgroup per 16-column slice
-    if (split)
-      launch(prefix_kernel<P_SPLIT_AB, NWS>, dim3(blocks), dim3(64 * NWS), x, p);
-    else
-      launch(prefix_kernel<P_F32, NWS>, dim3(blocks), dim3(64 * NWS), x, p);
+    launch_prefix_seq(split, h_in != nullptr, dim3(blocks), dim3(64 * NWS), x, p);
     return check_launch();
   }
   // blocked: compose each block's pairs, the sequential prefix over the
@@ -260,11 +266,11 @@ gdn_status launch_prefix(int BH, int n, const float *A, const float *Bm, const f
   const unsigned units = (unsigned)((long)BH * nb), slices = (unsigned)(D / 16) * BH;
   if (split) {
     launch(pair_walk_kernel<P_SPLIT_AB, PW_COMPOSE>, dim3(2 * units), dim3(512), first, w);
-    launch(prefix_kernel<P_SPLIT_AB, NWS>, dim3(slices), dim3(64 * NWS), mid, p);
+    launch_prefix_seq(true, true, dim3(slices), dim3(64 * NWS), mid, p);
     launch(pair_walk_kernel<P_SPLIT_AB, PW_REPLAY>, dim3(units), dim3(512), last, w);
   } else {
     launch(pair_walk_kernel<P_F32, PW_COMPOSE>, dim3(2 * units), dim3(512), first, w);
-    launch(prefix_kernel<P_F32, NWS>, dim3(slices), dim3(64 * NWS), mid, p);
+    launch_prefix_seq(false, true, dim3(slices), dim3(64 * NWS), mid, p);
     launch(pair_walk_kernel<P_F32, PW_REPLAY>, dim3(units), dim3(512), last, w);
   }
   return check_launch();

@@ -1544,8 +1544,7 @@ __global__ __launch_bounds__(128 * NWS) void walk_pair_kernel(FwdArgs a) {
 // operand: per lane two 16-byte runs of a row, in the k order of two stacked
 // result tiles, so a wave's two state tiles are one k-block of the B operand
 // as they stand; the waves pass their k-blocks through LDS (double-buffered:
-// one barrier per step).  Each wave streams only its rows of A_j, one step
-// ahead; B_j also arrives one step ahead.
+// one barrier per step).
 struct PrefixArgs {
   int BH, n;
   const float *A, *Bm, *h_init;
@@ -1555,16 +1554,40 @@ struct PrefixArgs {
   long long js, bs;
 };
 
-template <int PREC, int NWS>
+// s_waitcnt immediate: vmcnt(n) lgkmcnt(0)
+__host__ __device__ constexpr int vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4); }
+
+// A_j and B_j are copied straight into LDS (global_load_lds, no registers),
+// two steps ahead, into two stages declared as separate LDS arrays, the
+// waits for the copies placed by hand.  Each
+// wave copies and reads only its own 32 rows (A_j: 16 copies of 1 KB, copy q
+// = (row tile t, k-block kb, half) giving lane (lr, g) the 16 bytes at row
+// 16(m0+t) + lr, columns 32kb + 16 half + 4g ..; B_j: 2 copies, lane l the 16
+// bytes at row 16t + l/4, columns c0 + 4(l%4) ..), so a copy needs no
+// barrier, only the wave's own memory counter.  Per step and wave, in order:
+// the h_in row stores (8), the exchange barrier, the wait for this step's
+// copies (issued two steps before; 26 operations per step follow them, so
+// 34 may stay in flight -- 18 without h_in stores, and 26 (18) at the first
+// step, after the start's copies), the reads of A_j and B_j, the copies of
+// step j+2 into the stage just read, then the products.  (B_j loaded into
+// registers, one memory operation per element, would put the two steps in
+// flight over the counter's 63.)
+template <int PREC, int NWS, bool HIN>   // HIN: h_in is written
 __global__ __launch_bounds__(64 * NWS) void prefix_kernel(PrefixArgs a) {
   using PK = PolicyKinds<PREC>;
   using HF = Frag<PK::b>;
   constexpr int MH = D / 16, KB = D / 32;
-  constexpr int MHW = MH / NWS;   // state row tiles per wave
+  constexpr int MHW = MH / NWS;
   static_assert(MHW == 2, "each wave holds one k-block of the state");
-  constexpr int F = MHW * KB;     // A fragments per wave and step
-  constexpr int RING = 2 * F;     // two steps in flight: slot P F + p, P the step parity
+  constexpr int F = MHW * KB;                  // A fragments per wave and step
+  constexpr int WA = 2 * F * 1024;             // a wave's rows of A_j (16 copies of 1 KB)
+  constexpr int WB = MHW * 1024;               // a wave's rows of B_j (2 copies of 1 KB)
+  constexpr int NOPS = 2 * F + MHW + (HIN ? 4 * MHW : 0);   // memory operations per step and wave
   __shared__ __align__(16) HF xh[2][KB][64];
+  __shared__ __align__(16) char sA0[NWS * WA];
+  __shared__ __align__(16) char sA1[NWS * WA];
+  __shared__ __align__(16) char sB0[NWS * WB];
+  __shared__ __align__(16) char sB1[NWS * WB];
   int unit, slice;
   xcd_unit(blockIdx.x, D / 16, a.BH, unit, slice);
   const size_t bh = (size_t)unit;
@@ -1580,38 +1603,49 @@ __global__ __launch_bounds__(64 * NWS) void prefix_kernel(PrefixArgs a) {
       h[t][i] = a.h_init ? a.h_init[(bh * D + 16 * (m0 + t) + 4 * g + i) * D + c0 + lr] : 0.f;
   const size_t js_ = a.js ? (size_t)a.js : (size_t)D * D, bs_ = a.bs ? (size_t)a.bs : (size_t)a.n * D * D;
 
-  // fragment p = (own row tile t, k-block kb) of A_j: row 16(m0+t) + lr,
-  // columns 32kb + 4g .. +3 and 32kb + 16 + 4g .. +3
-  struct Run2 {
-    float4 x0, x1;
+  // the stages' LDS addresses as plain numbers (the compiler then does not
+  // tie the LDS reads to the copies; the waits below are explicit)
+  auto lds_addr = [](const void *p) {
+    unsigned x = (unsigned)(size_t)(__attribute__((address_space(3))) const char *)p;
+    asm volatile("" : "+s"(x));
+    return x;
   };
-  auto load = [&](size_t j, int p) -> Run2 {
-    const float *row = a.A + (bh * bs_ + j * js_) + (size_t)(16 * (m0 + p / KB) + lr) * D + 32 * (p % KB) + 4 * g;
-    return Run2{*reinterpret_cast<const float4 *>(row), *reinterpret_cast<const float4 *>(row + 16)};
+  const unsigned sa0 = lds_addr(sA0) + w * WA, sa1 = lds_addr(sA1) + w * WA;
+  const unsigned sb0 = lds_addr(sB0) + w * WB, sb1 = lds_addr(sB1) + w * WB;
+  const unsigned voff_a = lr * D * 4 + 16 * g;                    // this lane's 16 bytes of an A copy
+  const unsigned voff_b = (lane >> 2) * D * 4 + 16 * (lane & 3);  // and of a B copy
+  auto dma = [](const char *base, unsigned voff, unsigned dst) {
+    __builtin_amdgcn_global_load_lds((const void *)(base + voff), (__attribute__((address_space(3))) void *)(size_t)dst,
+                                     16, 0, 0);
   };
-  auto load_b = [&](size_t j, f32x4 (&bq)[MHW]) {
-    const float *B = a.Bm + (bh * bs_ + j * js_) + c0 + lr;
-#pragma unroll
-    for (int t = 0; t < MHW; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) bq[t][i] = B[(size_t)(16 * (m0 + t) + 4 * g + i) * D];
+  auto ubase = [](const float *p, size_t off) {
+    return reinterpret_cast<const char *>(uniform64(reinterpret_cast<unsigned long long>(p + off)));
   };
-  Run2 ring[RING];
+  // step j's copies: B_j first, then A_j
+  auto copy = [&](size_t j, unsigned sa, unsigned sb) {
+    const size_t pj = bh * bs_ + j * js_ + (size_t)(16 * m0) * D;
 #pragma unroll
-  for (int p = 0; p < RING; ++p) ring[p] = load(p < F || a.n < 2 ? 0 : 1, p % F);
-  f32x4 bq[2][MHW];
-  load_b(0, bq[0]);
+    for (int t = 0; t < MHW; ++t) dma(ubase(a.Bm, pj + (size_t)(16 * t) * D + c0), voff_b, sb + t * 1024);
+#pragma unroll
+    for (int q = 0; q < 2 * F; ++q) {
+      const int p = q >> 1, t = p / KB, kb = p % KB, half = q & 1;
+      dma(ubase(a.A, pj + (size_t)(16 * t) * D + 32 * kb + 16 * half), voff_a, sa + q * 1024);
+    }
+  };
+  copy(0, sa0, sb0);
+  copy(a.n > 1 ? 1 : 0, sa1, sb1);
 
-  auto step = [&](f32x4 (&bc)[MHW], f32x4 (&bn)[MHW], int j, auto Pc) {
-    constexpr int P = decltype(Pc)::value;   // step parity: LDS buffer
-    const size_t jn = j + 1 < a.n ? j + 1 : j;   // last step: loads repeat (unused)
-    const size_t jr = j + 2 < a.n ? j + 2 : jn;   // ring refill: two steps ahead
-    load_b(jn, bn);
+  auto step = [&](int j, auto Pc, auto Wc) {
+    constexpr int P = decltype(Pc)::value;      // step parity: exchange buffer and stage
+    constexpr int WAIT = decltype(Wc)::value;   // operations that may stay in flight
+    const size_t jr = j + 2 < a.n ? j + 2 : (j + 1 < a.n ? j + 1 : j);   // last steps: copies repeat (unused)
+    const char *sa = (P == 0 ? sA0 : sA1) + w * WA + lane * 16;
+    const char *sb = (P == 0 ? sB0 : sB1) + w * WB;
     {
       const float x[8] = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
       xh[P][w][lane] = make_frag<PK::b>(x);
     }
-    if (a.h_in) {
+    if constexpr (HIN) {
       float *dst = a.h_in + (bh * bs_ + j * js_) + c0 + lr;
 #pragma unroll
       for (int t = 0; t < MHW; ++t)
@@ -1622,26 +1656,52 @@ __global__ __launch_bounds__(64 * NWS) void prefix_kernel(PrefixArgs a) {
     HF hb[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) hb[kb] = xh[P][kb][lane];
+    // this step's copies landed
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(vm_lgkm0(WAIT));
+    asm volatile("" ::: "memory");
+    float4 fr[2 * F];
+#pragma unroll
+    for (int q = 0; q < 2 * F; ++q) fr[q] = *reinterpret_cast<const float4 *>(sa + q * 1024);
+    float bc[MHW][4];
+#pragma unroll
+    for (int t = 0; t < MHW; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bc[t][i] = *reinterpret_cast<const float *>(sb + t * 1024 + (4 * g + i) * 64 + lr * 4);
+    // every read of this stage done before the next copies into it
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(vm_lgkm0(63));   // lgkmcnt(0); the memory counter left as it is
+    asm volatile("" ::: "memory");
+    copy(jr, P == 0 ? sa0 : sa1, P == 0 ? sb0 : sb1);
 #pragma unroll
     for (int t = 0; t < MHW; ++t) {
       f32x4 acc = zero4();
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         const int p = t * KB + kb;
-        const Run2 r = ring[P * F + p];
-        const float x[8] = {r.x0.x, r.x0.y, r.x0.z, r.x0.w, r.x1.x, r.x1.y, r.x1.z, r.x1.w};
-        ring[P * F + p] = load(jr, p);
+        const float x[8] = {fr[2 * p].x, fr[2 * p].y, fr[2 * p].z, fr[2 * p].w,
+                            fr[2 * p + 1].x, fr[2 * p + 1].y, fr[2 * p + 1].z, fr[2 * p + 1].w};
         mma(acc, make_frag<PK::a>(x), hb[kb]);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) h[t][i] = acc[i] + bc[t][i];
     }
   };
-  // two steps per trip: the B sets and the LDS buffers alternate
-  for (int j = 0; j < a.n; j += 2) {
-    step(bq[0], bq[1], j, std::integral_constant<int, 0>{});
-    if (j + 1 < a.n) step(bq[1], bq[0], j + 1, std::integral_constant<int, 1>{});
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  constexpr int W_FIRST = NOPS;                          // the start's second copies + step 0's stores
+  constexpr int W_STEADY = NOPS + (HIN ? 4 * MHW : 0);   // step j-1's operations + step j's stores
+  step(0, I0{}, std::integral_constant<int, W_FIRST>{});
+  // then pairs of steps with no branch inside (so that the counter's state at
+  // the loop head is the same on every path), and an odd last step
+  int j = 1;
+  for (; j + 1 < a.n; j += 2) {
+    step(j, I1{}, std::integral_constant<int, W_STEADY>{});
+    step(j + 1, I0{}, std::integral_constant<int, W_STEADY>{});
   }
+  if (j < a.n) step(j, I1{}, std::integral_constant<int, W_STEADY>{});
+  // (every copy done before the workgroup ends)
+  __builtin_amdgcn_s_waitcnt(vm_lgkm0(0));
   if (a.h_final) {
 #pragma unroll
     for (int t = 0; t < MHW; ++t)
@@ -2158,8 +2218,6 @@ template <int C, typename TI> struct WalkOutLds {
   static constexpr int PKB = PB > QB ? PB : QB;                     // the K tile, then P^T
 };
 
-// s_waitcnt immediate: vmcnt(n) lgkmcnt(0)
-__host__ __device__ constexpr int vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4); }
 // wait (s_waitcnt IMM), then the workgroup barrier; no memory access moves
 // across it
 template <int IMM>
