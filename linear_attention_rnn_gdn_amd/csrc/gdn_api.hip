@@ -797,11 +797,6 @@ gdn_status run_bwd_grads(const gdn_shape &s, const void *q, const void *k, const
   const unsigned rowsBH = (unsigned)(s.B * s.H_v);
   StatesArgs sa{s.B, s.T, s.H_qk, s.H_v, N, k, a.G, reinterpret_cast<const float *>(a.W), a.U, h0,
                 reinterpret_cast<float *>(ws + L.hs)};
-  if (rag)
-    hipLaunchKernelGGL((fwd_states_kernel<C, TI, MODE, true>), dim3(rowsBH), dim3(512), 0, st, sa);
-  else
-    hipLaunchKernelGGL((fwd_states_kernel<C, TI, MODE, false>), dim3(rowsBH), dim3(512), 0, st, sa);
-  GDN_TRY(check_launch());
   BwdArgs b{};
   b.B = s.B; b.T = s.T; b.Hqk = s.H_qk; b.Hv = s.H_v; b.N = N;
   b.q = q; b.k = k; b.dO = dO;
@@ -809,12 +804,13 @@ gdn_status run_bwd_grads(const gdn_shape &s, const void *q, const void *k, const
   b.ddh = reinterpret_cast<float *>(ws + L.ddh);
   b.dhT = dh_T; b.dh = reinterpret_cast<float *>(ws + L.dh); b.dh0 = dh0;
   const unsigned units = (unsigned)((long)N * s.B * s.H_v);
+  // the reverse walk's chunk term, then both walks in one launch
   if (rag) {
     hipLaunchKernelGGL((bwd_ddh_kernel<C, TI, MODE, true>), dim3(units), dim3(256), 0, st, a, b);
-    hipLaunchKernelGGL((bwd_walk_kernel<C, TI, MODE, true>), dim3(rowsBH), dim3(512), 0, st, b);
+    hipLaunchKernelGGL((bwd_walks_kernel<C, TI, MODE, true>), dim3(2 * rowsBH), dim3(512), 0, st, sa, b);
   } else {
     hipLaunchKernelGGL((bwd_ddh_kernel<C, TI, MODE, false>), dim3(units), dim3(256), 0, st, a, b);
-    hipLaunchKernelGGL((bwd_walk_kernel<C, TI, MODE, false>), dim3(rowsBH), dim3(512), 0, st, b);
+    hipLaunchKernelGGL((bwd_walks_kernel<C, TI, MODE, false>), dim3(2 * rowsBH), dim3(512), 0, st, sa, b);
   }
   GDN_TRY(check_launch());
   const bool per_v = s.H_v != s.H_qk;

@@ -398,18 +398,26 @@ __device__ __forceinline__ void stage_in(char *buf, const T *src, size_t ld, int
 // per chunk, from the last to the first, K (row-major, the input rows), W
 // (fp32, row stride D + 4) and G go to LDS, then
 //   Y = K dh,  X = diag(e^{G_last - G}) Y,  dh <- e^{G_last} dh - W^T X + ddh_n
+template <int C, typename TI> struct BwdWalkLds {
+  static constexpr int LDW = D + 4;
+  static constexpr int LDK = D + 16 / (int)sizeof(TI);   // K row stride: 16 bytes of padding put the
+                                                         // 16 rows a fragment read touches on distinct banks
+  static constexpr int K_OFF = 0;                                    // K rows
+  static constexpr int W_OFF = K_OFF + C * LDK * (int)sizeof(TI);    // W rows (fp32; read by columns as W^T)
+  static constexpr int G_OFF = W_OFF + C * LDW * 4;
+  static constexpr int BYTES = G_OFF + C * 4;
+};
+
 template <int C, typename TI, int MODE, bool RAG>
-__global__ __launch_bounds__(512) void bwd_walk_kernel(BwdArgs a) {
+__device__ __forceinline__ void bwd_walk_body(const BwdArgs &a, size_t bh, char *lds) {
   constexpr int PKD = MODE == MODE_F32 ? P_F32 : P_SPLIT_B;    // K (data) x dh
   constexpr int PS = MODE == MODE_F32 ? P_F32 : P_SPLIT_AB;    // W^T x X
   constexpr int MV = C / 16, MH = D / 16, KBW = D / 32, KBK = C / 32;
-  constexpr int LDW = D + 4;
-  constexpr int LDK = D + 16 / (int)sizeof(TI);   // K row stride: 16 bytes of padding put the
-                                                  // 16 rows a fragment read touches on distinct banks
-  __shared__ __align__(16) TI sK[C * LDK];      // K rows
-  __shared__ __align__(16) float sW[C * LDW];   // W rows (fp32; read by columns as W^T)
-  __shared__ __align__(16) float sG[C];
-  const size_t bh = blockIdx.x;
+  using L = BwdWalkLds<C, TI>;
+  constexpr int LDW = L::LDW, LDK = L::LDK;
+  TI *sK = reinterpret_cast<TI *>(lds + L::K_OFF);
+  float *sW = reinterpret_cast<float *>(lds + L::W_OFF);
+  float *sG = reinterpret_cast<float *>(lds + L::G_OFF);
   const int b = (int)(bh / a.Hv), hv = (int)(bh % a.Hv), hq = hv / (a.Hv / a.Hqk);
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, g = lane >> 4;
   const int s = __builtin_amdgcn_readfirstlane(tid >> 6), c0 = 16 * s;
@@ -422,6 +430,12 @@ __global__ __launch_bounds__(512) void bwd_walk_kernel(BwdArgs a) {
   for (int n = a.N - 1; n >= 0; --n) {
     const size_t cb = bh * a.N + n, t0 = (size_t)b * a.T + (size_t)n * C;
     const int rows = !RAG ? C : (a.T - n * C < C ? a.T - n * C : C);
+    // the lane's indices, opaque each chunk: the LDS addresses derived from
+    // them are formed where used instead of being hoisted out of the loop
+    // (more than the registers hold)
+    int tl = tid;
+    asm volatile("" : "+v"(tl));
+    const int lane = tl & 63, lr = lane & 15, g = lane >> 4;
     __syncthreads();   // every wave past the previous chunk's tiles
     constexpr int VE = 16 / (int)sizeof(TI);
     for (int e = tid; e < C * D / VE; e += 512) {
@@ -501,6 +515,12 @@ __global__ __launch_bounds__(512) void bwd_walk_kernel(BwdArgs a) {
     }
 }
 
+template <int C, typename TI, int MODE, bool RAG>
+__global__ __launch_bounds__(512) void bwd_walk_kernel(BwdArgs a) {
+  __shared__ __align__(16) char lds[BwdWalkLds<C, TI>::BYTES];
+  bwd_walk_body<C, TI, MODE, RAG>(a, blockIdx.x, lds);
+}
+
 // ----------------------------------------------------------------------------
 // The forward's incoming state of every chunk, fp32 row-major, for the
 // chunk gradients: h_0 = h0 and
@@ -516,18 +536,26 @@ struct StatesArgs {
   float *hs;                  // [B, H_v, N, D, D]
 };
 
+template <int C, typename TI, int MODE> struct StatesLds {
+  static constexpr int LDKT = C + 8;                                  // K^T row stride (elements)
+  static constexpr int KT_OFF = 0;                                    // K^T: row d, the chunk's tokens along k
+  static constexpr int W_OFF = KT_OFF + D * LDKT * (int)sizeof(TI);   // W rows, split once
+  static constexpr int G_OFF = W_OFF + GStage<MODE>::BYTES;
+  static constexpr int BYTES = G_OFF + C * 4;
+};
+
 template <int C, typename TI, int MODE, bool RAG>
-__global__ __launch_bounds__(512) void fwd_states_kernel(StatesArgs a) {
+__device__ __forceinline__ void fwd_states_body(const StatesArgs &a, size_t bh, char *lds) {
   constexpr int PW = MODE == MODE_F32 ? P_F32 : P_SPLIT_AB;   // W (fp32) x h
   constexpr int PK = MODE == MODE_F32 ? P_F32 : P_SPLIT_B;    // K^T (data) x X
   using GS = GStage<MODE>;
   static_assert(PolicyKinds<PW>::a == GS::KIND, "W staged as the product's A operand");
   constexpr int MV = C / 16, MH = D / 16, KBW = D / 32, KBK = C / 32;
-  constexpr int LDKT = C + 8;                     // K^T row stride (elements)
-  __shared__ __align__(16) TI sKt[D * LDKT];      // K^T: row d, the chunk's tokens along k
-  __shared__ __align__(16) char sW[GS::BYTES];    // W rows, split once
-  __shared__ __align__(16) float sG[C];
-  const size_t bh = blockIdx.x;
+  using L = StatesLds<C, TI, MODE>;
+  constexpr int LDKT = L::LDKT;
+  TI *sKt = reinterpret_cast<TI *>(lds + L::KT_OFF);
+  char *sW = lds + L::W_OFF;
+  float *sG = reinterpret_cast<float *>(lds + L::G_OFF);
   const int b = (int)(bh / a.Hv), hv = (int)(bh % a.Hv), hq = hv / (a.Hv / a.Hqk);
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, g = lane >> 4;
   const int s = __builtin_amdgcn_readfirstlane(tid >> 6), c0 = 16 * s;
@@ -614,6 +642,20 @@ __global__ __launch_bounds__(512) void fwd_states_kernel(StatesArgs a) {
       for (int i = 0; i < 4; ++i) h[m][i] = gl * h[m][i] + acc[i];
     }
   }
+}
+
+// The forward-state walk and the reverse walk in one launch: they depend on
+// the transform (and the reverse walk on its chunk term) but not on each
+// other, and each fills only one workgroup per (batch, value head), so they
+// run side by side.  Workgroups [0, B H_v) walk the forward states, the
+// next B H_v the cotangents; the two share one LDS buffer.
+template <int C, typename TI, int MODE, bool RAG>
+__global__ __launch_bounds__(512) void bwd_walks_kernel(StatesArgs sa, BwdArgs ba) {
+  constexpr int SB = StatesLds<C, TI, MODE>::BYTES, WB = BwdWalkLds<C, TI>::BYTES;
+  __shared__ __align__(16) char lds[SB > WB ? SB : WB];
+  const unsigned nbh = (unsigned)(sa.B * sa.Hv);
+  if (blockIdx.x < nbh) fwd_states_body<C, TI, MODE, RAG>(sa, blockIdx.x, lds);
+  else bwd_walk_body<C, TI, MODE, RAG>(ba, blockIdx.x - nbh, lds);
 }
 
 // ----------------------------------------------------------------------------

@@ -1183,14 +1183,17 @@ __global__ __launch_bounds__(64 * NWS) void walk_ring_kernel(FwdArgs a) {
     return make_frag<PKw::b>(x);
   };
 
+  // U and G of the first chunk before the ring's fragments: the loop's
+  // memory waits are merged over its entry and its back edge, and on entry
+  // the first chunk's operands should not be the newest loads
+  UG ug[2];
+  fetch_ug(cb0, ug[0]);
   AF ring[RING];
 #pragma unroll
   for (int q = 0; q < RING; ++q) {
     const size_t c = cb0 + q / FPW;
     ring[q] = load(c < cb0 + cpj - 1 ? c : cb0 + cpj - 1, q % FPW);
   }
-  UG ug[2];
-  fetch_ug(cb0, ug[0]);
   // the state operand of the first chunk
 #pragma unroll
   for (int kbl = 0; kbl < KBWW; ++kbl) xh[w][kbl][lane] = state_frag(kbl);
@@ -1269,9 +1272,11 @@ __global__ __launch_bounds__(64 * NWS) void walk_ring_kernel(FwdArgs a) {
     // The chunk-start state and V' go out after the chunk's last loads: the
     // memory counter drains in issue order, so a store issued ahead of a load
     // would hold up every wait for that load.
-    if (KIND != FOLD && hcols && a.Hs)
+    // (the plain walk always has both: no branch in the loop, whose memory
+    // waits the compiler would otherwise merge conservatively)
+    if (KIND == WALK || (KIND == WALK_A && hcols && a.Hs))
       store_result_tiles<PR::h_store>(a.Hs + ((cb * (D / 16) + us) * MH + mh0) * Store<PR::h_store>::tile_floats, h, lane);
-    if (KIND != FOLD && hcols && a.Vn)
+    if (KIND == WALK || (KIND == WALK_A && hcols && a.Vn))
       store_result_tiles<PR::v_store>(a.Vn + ((cb * (D / 16) + us) * MV + mv0) * Store<PR::v_store>::tile_floats, vps, lane);
 #pragma unroll
     for (int t = 0; t < MHW; ++t)
@@ -1281,11 +1286,14 @@ __global__ __launch_bounds__(64 * NWS) void walk_ring_kernel(FwdArgs a) {
     for (int kbl = 0; kbl < KBWW; ++kbl) xh[w][kbl][lane] = state_frag(kbl);
     lds_barrier();
   };
-  // two chunks per trip so the U/G sets alternate without copies
-  for (int cc = 0; cc < cpj; cc += 2) {
+  // two chunks per trip so the U/G sets alternate without copies, and no
+  // branch inside a trip; an odd last chunk after the loop
+  int cc = 0;
+  for (; cc + 1 < cpj; cc += 2) {
     step(ug[0], ug[1], cc, std::integral_constant<int, 0>{});
-    if (cc + 1 < cpj) step(ug[1], ug[0], cc + 1, std::integral_constant<int, 1>{});
+    step(ug[1], ug[0], cc + 1, std::integral_constant<int, 1>{});
   }
+  if (cc < cpj) step(ug[0], ug[1], cc, std::integral_constant<int, 0>{});
 
   store_final();
 }
@@ -2575,9 +2583,14 @@ __global__ __launch_bounds__(64 * WPG) void walk_out_kernel(FwdArgs a) {
   fetch_u(cb0);
   wait_barrier<vm_lgkm0(0)>();
 
-  for (int cc = 0; cc < cpj; ++cc) {
+  // one chunk; more: a next chunk follows, whose operands are copied during
+  // this one (the last chunk is a separate copy of the body, so that the
+  // loop holds no branch around a memory operation: the compiler merges its
+  // memory waits over every path through the loop)
+  auto chunk = [&](int cc, auto MoreC) {
+    constexpr bool more = decltype(MoreC)::value;
     const size_t cb = cb0 + cc;
-    const bool more = cc + 1 < cpj;
+
     size_t tok0;
     int rows;
     chunk_tokens(cc, tok0, rows);
@@ -2610,7 +2623,7 @@ __global__ __launch_bounds__(64 * WPG) void walk_out_kernel(FwdArgs a) {
     // every wave past W; this chunk's Q, K and G landed (the K^T copies,
     // issued after them, may still be in flight)
     wait_barrier<vm_lgkm0(NCK)>();
-    if (more) copy_w(cb + 1);
+    if constexpr (more) copy_w(cb + 1);
 
     // ---- P^T = (K Q^T) o Gamma^T o [i <= r]: wave w forms the pairs (query
     //      tile rt, key tiles 2kp and 2kp + 1) of its query tiles {w, R-1-w}
@@ -2766,9 +2779,9 @@ __global__ __launch_bounds__(64 * WPG) void walk_out_kernel(FwdArgs a) {
     }
     // every wave past Q, P^T and G; this chunk's K^T landed (the next chunk's
     // W and this chunk's o stores, issued after it, may be in flight)
-    if (more) wait_barrier<vm_lgkm0(NCW + NST)>();
+    if constexpr (more) wait_barrier<vm_lgkm0(NCW + NST)>();
     else wait_barrier<vm_lgkm0(NST)>();
-    if (more) {
+    if constexpr (more) {
       copy_qkg(cc + 1);
       fetch_u(cb + 1);
     }
@@ -2791,13 +2804,15 @@ __global__ __launch_bounds__(64 * WPG) void walk_out_kernel(FwdArgs a) {
         for (int i = 0; i < 4; ++i) h[m][i] = gl * h[m][i] + acc2[i];
       }
     }
-    if (more) {
+    if constexpr (more) {
       // every wave past K^T; the next chunk's W landed (this chunk's o
       // stores and the next chunk's Q, K, G copies and U may be in flight)
       wait_barrier<vm_lgkm0(NST + 2 * NCQ + 1 + NU)>();
       copy_kt(cb + 1);
     }
-  }
+  };
+  for (int cc = 0; cc + 1 < cpj; ++cc) chunk(cc, std::true_type{});
+  chunk(cpj - 1, std::false_type{});
   store_final();
 }
 
