@@ -395,16 +395,15 @@ __device__ __forceinline__ void stage_in(char *buf, const T *src, size_t ld, int
 
 // the reverse walk: one workgroup of eight waves per (batch, value head),
 // wave s holding the 16 columns 16s.. of dh in matrix-core result registers;
-// per chunk, from the last to the first, K (row-major, the input rows), W
-// (fp32, row stride D + 4) and G go to LDS, then
+// per chunk, from the last to the first, K (row-major, the input rows), W^T
+// (staged transposed, split once) and G go to LDS, then
 //   Y = K dh,  X = diag(e^{G_last - G}) Y,  dh <- e^{G_last} dh - W^T X + ddh_n
-template <int C, typename TI> struct BwdWalkLds {
-  static constexpr int LDW = D + 4;
+template <int C, typename TI, int MODE> struct BwdWalkLds {
   static constexpr int LDK = D + 16 / (int)sizeof(TI);   // K row stride: 16 bytes of padding put the
                                                          // 16 rows a fragment read touches on distinct banks
   static constexpr int K_OFF = 0;                                    // K rows
-  static constexpr int W_OFF = K_OFF + C * LDK * (int)sizeof(TI);    // W rows (fp32; read by columns as W^T)
-  static constexpr int G_OFF = W_OFF + C * LDW * 4;
+  static constexpr int W_OFF = K_OFF + C * LDK * (int)sizeof(TI);    // W^T, staged (split once)
+  static constexpr int G_OFF = W_OFF + GStage<MODE>::BYTES;
   static constexpr int BYTES = G_OFF + C * 4;
 };
 
@@ -413,10 +412,12 @@ __device__ __forceinline__ void bwd_walk_body(const BwdArgs &a, size_t bh, char 
   constexpr int PKD = MODE == MODE_F32 ? P_F32 : P_SPLIT_B;    // K (data) x dh
   constexpr int PS = MODE == MODE_F32 ? P_F32 : P_SPLIT_AB;    // W^T x X
   constexpr int MV = C / 16, MH = D / 16, KBW = D / 32, KBK = C / 32;
-  using L = BwdWalkLds<C, TI>;
-  constexpr int LDW = L::LDW, LDK = L::LDK;
+  using L = BwdWalkLds<C, TI, MODE>;
+  using GS = GStage<MODE>;
+  static_assert(PolicyKinds<PS>::a == GS::KIND, "W^T staged as the product's A operand");
+  constexpr int LDK = L::LDK;
   TI *sK = reinterpret_cast<TI *>(lds + L::K_OFF);
-  float *sW = reinterpret_cast<float *>(lds + L::W_OFF);
+  char *sW = lds + L::W_OFF;
   float *sG = reinterpret_cast<float *>(lds + L::G_OFF);
   const int b = (int)(bh / a.Hv), hv = (int)(bh % a.Hv), hq = hv / (a.Hv / a.Hqk);
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, g = lane >> 4;
@@ -444,10 +445,7 @@ __device__ __forceinline__ void bwd_walk_body(const BwdArgs &a, size_t bh, char 
       if (r < rows) x = *reinterpret_cast<const uint4 *>(reinterpret_cast<const TI *>(a.k) + ((t0 + r) * a.Hqk + hq) * D + c);
       *reinterpret_cast<uint4 *>(sK + r * LDK + c) = x;
     }
-    for (int e = tid; e < C * D / 4; e += 512) {
-      const int r = e / (D / 4), c = (e % (D / 4)) * 4;
-      *reinterpret_cast<float4 *>(sW + r * LDW + c) = *reinterpret_cast<const float4 *>(a.W + (cb * C + r) * D + c);
-    }
+    stage<MODE, C, D, true>(sW, a.W + cb * C * D, D, tl);
     if (tid < C) sG[tid] = a.G[cb * C + tid];
     // the incoming-state cotangent of chunk n + 1 (the state after chunk n)
     if (a.dh && n + 1 < a.N) {
@@ -491,13 +489,7 @@ __device__ __forceinline__ void bwd_walk_body(const BwdArgs &a, size_t bh, char 
     for (int m = 0; m < MH; ++m) {
       f32x4 acc = zero4();
 #pragma unroll
-      for (int kb = 0; kb < KBK; ++kb) {
-        // W^T's row 16m + lr, k-values kk(g, j): column 16m + lr of W
-        float wa[8];
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) wa[jj] = sW[(32 * kb + (jj < 4 ? 4 * g + jj : 16 + 4 * g + jj - 4)) * LDW + 16 * m + lr];
-        mma(acc, make_frag<PolicyKinds<PS>::a>(wa), xb[kb]);
-      }
+      for (int kb = 0; kb < KBK; ++kb) mma(acc, GS::frag_kk(sW, 16 * m + lr, 32 * kb, g), xb[kb]);
       const float4 dd = *reinterpret_cast<const float4 *>(a.ddh + ((cb * MH + s) * MH + m) * 256 + lane * 4);
       const float ddv[4] = {dd.x, dd.y, dd.z, dd.w};
 #pragma unroll
@@ -517,7 +509,7 @@ __device__ __forceinline__ void bwd_walk_body(const BwdArgs &a, size_t bh, char 
 
 template <int C, typename TI, int MODE, bool RAG>
 __global__ __launch_bounds__(512) void bwd_walk_kernel(BwdArgs a) {
-  __shared__ __align__(16) char lds[BwdWalkLds<C, TI>::BYTES];
+  __shared__ __align__(16) char lds[BwdWalkLds<C, TI, MODE>::BYTES];
   bwd_walk_body<C, TI, MODE, RAG>(a, blockIdx.x, lds);
 }
 
@@ -651,7 +643,7 @@ __device__ __forceinline__ void fwd_states_body(const StatesArgs &a, size_t bh, 
 // next B H_v the cotangents; the two share one LDS buffer.
 template <int C, typename TI, int MODE, bool RAG>
 __global__ __launch_bounds__(512) void bwd_walks_kernel(StatesArgs sa, BwdArgs ba) {
-  constexpr int SB = StatesLds<C, TI, MODE>::BYTES, WB = BwdWalkLds<C, TI>::BYTES;
+  constexpr int SB = StatesLds<C, TI, MODE>::BYTES, WB = BwdWalkLds<C, TI, MODE>::BYTES;
   __shared__ __align__(16) char lds[SB > WB ? SB : WB];
   const unsigned nbh = (unsigned)(sa.B * sa.Hv);
   if (blockIdx.x < nbh) fwd_states_body<C, TI, MODE, RAG>(sa, blockIdx.x, lds);
