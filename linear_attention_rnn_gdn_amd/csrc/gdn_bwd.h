@@ -771,6 +771,33 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(GradArgs a) {
       f(16 * (t / TC), 16 * (t % TC));
     }
   };
+  // the same, with the memory reads a tile's epilogue needs issued one tile
+  // ahead: ld(i0, j0) returns them (registers), f(i0, j0, x) forms the tile.
+  // (Read after the tile's products, each read had cost a whole memory
+  // latency per tile.)  Past the last tile, ld reads that tile again, unused.
+  auto for_tiles_ld = [&](auto n_per_wave, auto tiles_per_row, auto ld, auto f) {
+    constexpr int NT = decltype(n_per_wave)::value, TR = decltype(tiles_per_row)::value;
+    auto x = ld(16 * (wv / TR), 16 * (wv % TR));
+#pragma unroll 1
+    for (int u = 0; u < NT; ++u) {
+      const int t = wv + NW * u, tn = wv + NW * (u + 1 < NT ? u + 1 : u);
+      const auto xn = ld(16 * (tn / TR), 16 * (tn % TR));
+      f(16 * (t / TR), 16 * (t % TR), x);
+      x = xn;
+    }
+  };
+  auto for_cd_ld = [&](auto ld, auto f) {
+    for_tiles_ld(std::integral_constant<int, NCD>{}, std::integral_constant<int, TD>{}, ld, f);
+  };
+  auto for_cc_ld = [&](auto ld, auto f) {
+    for_tiles_ld(std::integral_constant<int, NCC>{}, std::integral_constant<int, TC>{}, ld, f);
+  };
+  struct E4 {
+    float v[4];
+  };
+  struct E8 {
+    float v[4], w[4];
+  };
 
   for (int unit = blockIdx.x; unit < a.units; unit += gridDim.x) {
     // (the thread index made opaque per unit: the per-thread offsets of the
@@ -779,8 +806,12 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(GradArgs a) {
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
     const int lane = tid & 63, lr = lane & 15, g = lane >> 4;
-    const size_t cb = unit, bh = cb / a.N;
-    const int n = (int)(cb % a.N), b = (int)(bh / a.Hv), hv = (int)(bh % a.Hv), hq = hv / grp;
+    // (the divisors too, and in 32 bits: their reciprocals, hoisted out of
+    // the loop, had outgrown the registers)
+    int Nn = a.N, Hvn = a.Hv, grpn = grp;
+    asm volatile("" : "+s"(Nn), "+s"(Hvn), "+s"(grpn));
+    const int bhi = unit / Nn, n = unit % Nn, b = bhi / Hvn, hv = bhi % Hvn, hq = hv / grpn;
+    const size_t cb = unit, bh = bhi;
     const int oh = a.per_value_head ? hv : hq;
     const size_t t0 = (size_t)b * a.T + (size_t)n * C;
     const int rows = !RAG ? C : (a.T - n * C < C ? a.T - n * C : C);
@@ -833,22 +864,29 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(GradArgs a) {
     stage<MODE, D, D, true>(sB, h, D, tid);
     __syncthreads();
     // (2) V' = U - W h
-    for_cd([&](int i0, int j0) {
+    for_cd_ld([&](int i0, int j0) {
+      E4 e;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) e.v[i] = Um[row(i0, i) * D + j0 + lr];
+      return e;
+    }, [&](int i0, int j0, const E4 &e) {
       f32x4 acc = zero4();
       tile_st<MODE, D>(acc, sA, i0, sB, j0, lane);
       const int c = j0 + lr;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = row(i0, i);
-        Vp[r * D + c] = Um[r * D + c] - acc[i];
-      }
+      for (int i = 0; i < 4; ++i) Vp[row(i0, i) * D + c] = e.v[i] - acc[i];
     });
     __syncthreads();
     stage_in<MODE, C, false>(sA, doin, ldv, rows, tid);
     stage<MODE, D, D, false>(sB, h, D, tid);
     __syncthreads();
     // (3) dO h^T: dq's first term E o (dO h^T); dG_r += E_r <q_r, (dO h^T)_r>
-    for_cd([&](int i0, int j0) {
+    for_cd_ld([&](int i0, int j0) {
+      E4 e;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) e.v[i] = in_at(qin, ldq, row(i0, i), j0 + lr);
+      return e;
+    }, [&](int i0, int j0, const E4 &e) {
       f32x4 acc = zero4();
       tile_st<MODE, D>(acc, sA, i0, sB, j0, lane);
       const int c = j0 + lr;
@@ -857,7 +895,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(GradArgs a) {
       for (int i = 0; i < 4; ++i) {
         const int r = row(i0, i);
         dQp[r * D + c] = sE[r] * acc[i];
-        rs[i] = sE[r] * in_at(qin, ldq, r, c) * acc[i];
+        rs[i] = sE[r] * e.v[i] * acc[i];
       }
       add_row_sums(sdG, i0, rs, 1.f, lane);
     });
@@ -865,7 +903,12 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(GradArgs a) {
     stage<MODE, C, D, false>(sB, Vp, D, tid);
     __syncthreads();
     // (4) dP = (dO V'^T) o [i <= r]: dR = dP o Gam; dG terms of dP o R o Gam
-    for_cc([&](int i0, int j0) {
+    for_cc_ld([&](int i0, int j0) {
+      E4 e;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) e.v[i] = R[row(i0, i) * C + j0 + lr];
+      return e;
+    }, [&](int i0, int j0, const E4 &e) {
       f32x4 acc = zero4();
       tile_st<MODE, D>(acc, sA, i0, sB, j0, lane);
       const int c = j0 + lr;
@@ -875,7 +918,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(GradArgs a) {
         const int r = row(i0, i);
         const float gm = c <= r ? gam(r, c) : 0.f;
         dR[r * C + c] = acc[i] * gm;
-        tv[i] = acc[i] * R[r * C + c] * gm;
+        tv[i] = acc[i] * e.v[i] * gm;
       }
       add_row_sums(sdG, i0, tv, 1.f, lane);
       add_col_sums(sdG, j0, tv, -1.f, lane);
@@ -896,14 +939,19 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(GradArgs a) {
     stage<MODE, D, D, true>(sB, dhn, D, tid);
     __syncthreads();
     // (6) dV = P^T dO + diag(s) K dh'
-    for_cd([&](int i0, int j0) {
+    for_cd_ld([&](int i0, int j0) {
+      E4 e;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) e.v[i] = dV[row(i0, i) * D + j0 + lr];
+      return e;
+    }, [&](int i0, int j0, const E4 &e) {
       f32x4 acc = zero4();
       tile_st<MODE, D>(acc, sA, i0, sB, j0, lane);
       const int c = j0 + lr;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = row(i0, i);
-        dV[r * D + c] += sS[r] * acc[i];
+        dV[r * D + c] = e.v[i] + sS[r] * acc[i];
       }
     });
     __syncthreads();
@@ -911,7 +959,12 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(GradArgs a) {
     stage<MODE, D, D, false>(sB, dhn, D, tid);
     __syncthreads();
     // (7) V' dh'^T: dk's first term diag(s) V' dh'^T and its dG terms; <h, dh'>
-    for_cd([&](int i0, int j0) {
+    for_cd_ld([&](int i0, int j0) {
+      E4 e;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) e.v[i] = in_at(kin, ldq, row(i0, i), j0 + lr);
+      return e;
+    }, [&](int i0, int j0, const E4 &e) {
       f32x4 acc = zero4();
       tile_st<MODE, D>(acc, sA, i0, sB, j0, lane);
       const int c = j0 + lr;
@@ -921,7 +974,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(GradArgs a) {
         const int r = row(i0, i);
         const float x = sS[r] * acc[i];
         dKp[r * D + c] = x;
-        dd[i] = x * in_at(kin, ldq, r, c);
+        dd[i] = x * e.v[i];
       }
       // dG_r -= dd_r, dG_last += sum_r dd_r
 #pragma unroll
@@ -958,14 +1011,19 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(GradArgs a) {
     stage_in<MODE, C, true>(sB, kin, ldq, rows, tid);
     __syncthreads();
     // (9) dq = E o (dO h^T) + dR K
-    for_cd([&](int i0, int j0) {
+    for_cd_ld([&](int i0, int j0) {
+      E4 e;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) e.v[i] = dQp[row(i0, i) * D + j0 + lr];
+      return e;
+    }, [&](int i0, int j0, const E4 &e) {
       f32x4 acc = zero4();
       tile_st<MODE, C>(acc, sA, i0, sB, j0, lane);
       const int c = j0 + lr;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = row(i0, i);
-        if (r < rows) a.dq[((t0 + r) * oheads + oh) * D + c] = dQp[r * D + c] + acc[i];
+        if (r < rows) a.dq[((t0 + r) * oheads + oh) * D + c] = e.v[i] + acc[i];
       }
     });
     __syncthreads();
@@ -973,7 +1031,12 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(GradArgs a) {
     stage<MODE, C, D, true>(sB, dV, D, tid);
     __syncthreads();
     // (10) dU~ = T^T dV: dv = diag(beta) dU~, dbeta_r += <dU~_r, v_r>
-    for_cd([&](int i0, int j0) {
+    for_cd_ld([&](int i0, int j0) {
+      E4 e;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) e.v[i] = in_at(vin, ldv, row(i0, i), j0 + lr);
+      return e;
+    }, [&](int i0, int j0, const E4 &e) {
       f32x4 acc = zero4();
       tile_st<MODE, C>(acc, sA, i0, sB, j0, lane);
       const int c = j0 + lr;
@@ -982,7 +1045,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(GradArgs a) {
       for (int i = 0; i < 4; ++i) {
         const int r = row(i0, i);
         if (r < rows) a.dv[((t0 + r) * a.Hv + hv) * D + c] = sBt[r] * acc[i];
-        bv[i] = acc[i] * in_at(vin, ldv, r, c);
+        bv[i] = acc[i] * e.v[i];
       }
       add_row_sums(sdB, i0, bv, 1.f, lane);
     });
@@ -991,7 +1054,15 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(GradArgs a) {
     __syncthreads();
     // (11) dW~ = T^T dW: dk += diag(beta E) dW~; rw_r = <dW~_r, k_r>:
     //      dbeta_r += E_r rw_r, dG_r += beta_r E_r rw_r
-    for_cd([&](int i0, int j0) {
+    for_cd_ld([&](int i0, int j0) {
+      E8 e;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        e.v[i] = dKp[row(i0, i) * D + j0 + lr];
+        e.w[i] = in_at(kin, ldq, row(i0, i), j0 + lr);
+      }
+      return e;
+    }, [&](int i0, int j0, const E8 &e) {
       f32x4 acc = zero4();
       tile_st<MODE, C>(acc, sA, i0, sB, j0, lane);
       const int c = j0 + lr;
@@ -999,8 +1070,8 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(GradArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = row(i0, i);
-        dKp[r * D + c] += sBt[r] * sE[r] * acc[i];
-        rw[i] = acc[i] * in_at(kin, ldq, r, c);
+        dKp[r * D + c] = e.v[i] + sBt[r] * sE[r] * acc[i];
+        rw[i] = acc[i] * e.w[i];
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -1029,12 +1100,17 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(GradArgs a) {
     stage_in<MODE, C, false>(sB, vin, ldv, rows, tid);
     __syncthreads();
     // (13) dT += (dV V^T) diag(beta)
-    for_cc([&](int i0, int j0) {
+    for_cc_ld([&](int i0, int j0) {
+      E4 e;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) e.v[i] = dT[row(i0, i) * C + j0 + lr];
+      return e;
+    }, [&](int i0, int j0, const E4 &e) {
       f32x4 acc = zero4();
       tile_st<MODE, D>(acc, sA, i0, sB, j0, lane);
       const int c = j0 + lr;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dT[row(i0, i) * C + c] += acc[i] * sBt[c];
+      for (int i = 0; i < 4; ++i) dT[row(i0, i) * C + c] = e.v[i] + acc[i] * sBt[c];
     });
     __syncthreads();
     stage<MODE, C, C, false>(sA, dT, C, tid);
@@ -1053,7 +1129,12 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(GradArgs a) {
     __syncthreads();
     // (15) dS = -strict-lower(T^T X): dbeta, dG terms of diag(beta) dS o K K^T
     //      o Gam, dKk = diag(beta) dS o Gam
-    for_cc([&](int i0, int j0) {
+    for_cc_ld([&](int i0, int j0) {
+      E4 e;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) e.v[i] = Kk[row(i0, i) * C + j0 + lr];
+      return e;
+    }, [&](int i0, int j0, const E4 &e) {
       f32x4 acc = zero4();
       tile_st<MODE, C>(acc, sA, i0, sB, j0, lane);
       const int c = j0 + lr;
@@ -1063,7 +1144,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(GradArgs a) {
         const int r = row(i0, i);
         const float ds = c < r ? -acc[i] : 0.f;
         const float gm = c < r ? gam(r, c) : 0.f;
-        bs[i] = ds * gm * Kk[r * C + c];
+        bs[i] = ds * gm * e.v[i];
         tv[i] = sBt[r] * bs[i];
         dKk[r * C + c] = sBt[r] * ds * gm;
       }
@@ -1076,36 +1157,51 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(GradArgs a) {
     stage_in<MODE, C, true>(sB, qin, ldq, rows, tid);
     __syncthreads();
     // (16) dk += dR^T Q
-    for_cd([&](int i0, int j0) {
+    for_cd_ld([&](int i0, int j0) {
+      E4 e;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) e.v[i] = dKp[row(i0, i) * D + j0 + lr];
+      return e;
+    }, [&](int i0, int j0, const E4 &e) {
       f32x4 acc = zero4();
       tile_st<MODE, C>(acc, sA, i0, sB, j0, lane);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dKp[row(i0, i) * D + j0 + lr] += acc[i];
+      for (int i = 0; i < 4; ++i) dKp[row(i0, i) * D + j0 + lr] = e.v[i] + acc[i];
     });
     __syncthreads();
     stage<MODE, C, C, false>(sA, dKk, C, tid);
     stage_in<MODE, C, true>(sB, kin, ldq, rows, tid);
     __syncthreads();
     // (17) dk += dKk K
-    for_cd([&](int i0, int j0) {
+    for_cd_ld([&](int i0, int j0) {
+      E4 e;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) e.v[i] = dKp[row(i0, i) * D + j0 + lr];
+      return e;
+    }, [&](int i0, int j0, const E4 &e) {
       f32x4 acc = zero4();
       tile_st<MODE, C>(acc, sA, i0, sB, j0, lane);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dKp[row(i0, i) * D + j0 + lr] += acc[i];
+      for (int i = 0; i < 4; ++i) dKp[row(i0, i) * D + j0 + lr] = e.v[i] + acc[i];
     });
     __syncthreads();
     stage<MODE, C, C, true>(sA, dKk, C, tid);
     __syncthreads();
     // (18) dk = diag(s) V' dh'^T + diag(beta E) dW~ + dR^T Q + dKk K + dKk^T K;
     //      dg = reverse cumulative sum of dG; dbeta
-    for_cd([&](int i0, int j0) {
+    for_cd_ld([&](int i0, int j0) {
+      E4 e;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) e.v[i] = dKp[row(i0, i) * D + j0 + lr];
+      return e;
+    }, [&](int i0, int j0, const E4 &e) {
       f32x4 acc = zero4();
       tile_st<MODE, C>(acc, sA, i0, sB, j0, lane);
       const int c = j0 + lr;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = row(i0, i);
-        if (r < rows) a.dk[((t0 + r) * oheads + oh) * D + c] = dKp[r * D + c] + acc[i];
+        if (r < rows) a.dk[((t0 + r) * oheads + oh) * D + c] = e.v[i] + acc[i];
       }
     });
     if (tid < rows) {
