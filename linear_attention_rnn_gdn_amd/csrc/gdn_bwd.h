@@ -713,12 +713,19 @@ __device__ __forceinline__ void tile_st(f32x4 &acc, const char *A, int i0, const
 }
 
 // sums over the 16 lanes of a lane group (the columns of a result tile), and
-// over the four lane groups
+// over the four lane groups.  Within a group by DPP lane permutations (pairs,
+// quads, then the mirrors of half-rows and rows; every lane ends with the
+// same sum): as shuffles they went through LDS, a dependent chain of
+// permutes per row of every tile.
+template <int CTRL>
+__device__ __forceinline__ float dpp_from(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
 __device__ __forceinline__ float sum_cols(float x) {
-  x += __shfl_xor(x, 1, 64);
-  x += __shfl_xor(x, 2, 64);
-  x += __shfl_xor(x, 4, 64);
-  x += __shfl_xor(x, 8, 64);
+  x += dpp_from<0xB1>(x);    // quad_perm [1, 0, 3, 2]
+  x += dpp_from<0x4E>(x);    // quad_perm [2, 3, 0, 1]
+  x += dpp_from<0x141>(x);   // row_half_mirror
+  x += dpp_from<0x140>(x);   // row_mirror
   return x;
 }
 __device__ __forceinline__ float sum_groups(float x) {
