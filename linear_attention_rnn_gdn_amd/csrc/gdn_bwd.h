@@ -343,7 +343,13 @@ __device__ __forceinline__ void stage(char *buf, const float *src, size_t ld, in
   }
 }
 // NR x D input rows of type T (row stride ld elements) staged as fp32 values,
-// rows at or past `rows` zero
+// rows at or past `rows` (>= 1) zero.  Every load is issued (from the row
+// clamped into [0, rows)) and its value then selected: a load behind a
+// branch is waited for where the branches join.
+__device__ __forceinline__ uint4 row_or_zero(const void *base, size_t off_bytes, bool real) {
+  const uint4 x = *reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(base) + off_bytes);
+  return real ? x : uint4{0u, 0u, 0u, 0u};
+}
 template <int MODE, int NR, bool TR, typename T>
 __device__ __forceinline__ void stage_in(char *buf, const T *src, size_t ld, int rows, int tid) {
   constexpr int VE = 16 / (int)sizeof(T);
@@ -354,7 +360,7 @@ __device__ __forceinline__ void stage_in(char *buf, const T *src, size_t ld, int
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int e = tid + 512 * u, r = e / (D / VE), c = (e % (D / VE)) * VE;
-      v[u] = r < rows ? *reinterpret_cast<const uint4 *>(src + r * ld + c) : uint4{0u, 0u, 0u, 0u};
+      v[u] = row_or_zero(src, ((r < rows ? r : rows - 1) * ld + c) * sizeof(T), r < rows);
     }
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
@@ -377,7 +383,7 @@ __device__ __forceinline__ void stage_in(char *buf, const T *src, size_t ld, int
       uint4 w[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        w[i] = r0 + i < rows ? *reinterpret_cast<const uint4 *>(src + (r0 + i) * ld + c0) : uint4{0u, 0u, 0u, 0u};
+        w[i] = row_or_zero(src, ((r0 + i < rows ? r0 + i : rows - 1) * ld + c0) * sizeof(T), r0 + i < rows);
 #pragma unroll
       for (int h = 0; h < VE; h += 4) {
         float v[4][4];
@@ -810,9 +816,16 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(GradArgs a) {
     // (the thread index made opaque per unit: the per-thread offsets of the
     // staging copies and tile reads are then formed inside the loop, not
     // hoisted out of it into more registers than there are)
-    int tid = threadIdx.x;
-    asm volatile("" : "+v"(tid));
-    const int lane = tid & 63, lr = lane & 15, g = lane >> 4;
+    // (from the lane id, counted again each unit, and the wave index: the
+    // hardware's thread index would stay live across the whole loop)
+    int lid;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lid));
+    int tid = 64 * wv + lid;
+    int lane = tid & 63, lr = lane & 15, g = lane >> 4;
+    // the lane indices made opaque again after each barrier: offsets derived
+    // from them are then formed in the phase that uses them, not carried
+    // (in registers there are not) from one phase to a later one
+    auto lane_fence = [&]() { asm volatile("" : "+v"(tid), "+v"(lane), "+v"(lr), "+v"(g)); };
     // (the divisors too, and in 32 bits: their reciprocals, hoisted out of
     // the loop, had outgrown the registers)
     int Nn = a.N, Hvn = a.Hv, grpn = grp;
@@ -830,7 +843,12 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(GradArgs a) {
     const float *doin = a.dO + (t0 * a.Hv + hv) * D;
     const size_t ldq = (size_t)a.Hqk * D, ldv = (size_t)a.Hv * D;
     // one input element as fp32 (zero past the sequence's end)
-    auto in_at = [&](const TI *p, size_t ld, int r, int c) { return r < rows ? to_f32(p[r * ld + c]) : 0.f; };
+    // (read branch-free from the row clamped into the chunk, then selected:
+    // behind a branch, each read was waited for where the branches joined)
+    auto in_at = [&](const TI *p, size_t ld, int r, int c) {
+      const float x = to_f32(p[(size_t)(r < rows ? r : rows - 1) * ld + c]);
+      return r < rows ? x : 0.f;
+    };
     auto gam = [&](int r, int c) { return exp2_fast(sG[r] - sG[c]); };   // Gam_rc, c <= r
     // result element (row 4g + i of the tile) helpers
     auto row = [&](int i0, int i) { return i0 + 4 * g + i; };
@@ -848,6 +866,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(GradArgs a) {
     stage_in<MODE, C, false>(sA, qin, ldq, rows, tid);
     stage_in<MODE, C, false>(sB, kin, ldq, rows, tid);
     __syncthreads();
+    lane_fence();
     // (1) R = Q K^T, P = R o Gam o [i <= r]; K K^T
     for_cc([&](int i0, int j0) {
       f32x4 acc = zero4();
@@ -867,9 +886,11 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(GradArgs a) {
       for (int i = 0; i < 4; ++i) Kk[row(i0, i) * C + j0 + lr] = acc[i];
     });
     __syncthreads();
+    lane_fence();
     stage<MODE, C, D, false>(sA, Wm, D, tid);
     stage<MODE, D, D, true>(sB, h, D, tid);
     __syncthreads();
+    lane_fence();
     // (2) V' = U - W h
     for_cd_ld([&](int i0, int j0) {
       E4 e;
@@ -884,9 +905,11 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(GradArgs a) {
       for (int i = 0; i < 4; ++i) Vp[row(i0, i) * D + c] = e.v[i] - acc[i];
     });
     __syncthreads();
+    lane_fence();
     stage_in<MODE, C, false>(sA, doin, ldv, rows, tid);
     stage<MODE, D, D, false>(sB, h, D, tid);
     __syncthreads();
+    lane_fence();
     // (3) dO h^T: dq's first term E o (dO h^T); dG_r += E_r <q_r, (dO h^T)_r>
     for_cd_ld([&](int i0, int j0) {
       E4 e;
@@ -907,8 +930,10 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(GradArgs a) {
       add_row_sums(sdG, i0, rs, 1.f, lane);
     });
     __syncthreads();
+    lane_fence();
     stage<MODE, C, D, false>(sB, Vp, D, tid);
     __syncthreads();
+    lane_fence();
     // (4) dP = (dO V'^T) o [i <= r]: dR = dP o Gam; dG terms of dP o R o Gam
     for_cc_ld([&](int i0, int j0) {
       E4 e;
@@ -931,9 +956,11 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(GradArgs a) {
       add_col_sums(sdG, j0, tv, -1.f, lane);
     });
     __syncthreads();
+    lane_fence();
     stage<MODE, C, C, true>(sA, Pm, C, tid);
     stage_in<MODE, C, true>(sB, doin, ldv, rows, tid);
     __syncthreads();
+    lane_fence();
     // (5) P^T dO (into dV; (6) adds the second term)
     for_cd([&](int i0, int j0) {
       f32x4 acc = zero4();
@@ -942,9 +969,11 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(GradArgs a) {
       for (int i = 0; i < 4; ++i) dV[row(i0, i) * D + j0 + lr] = acc[i];
     });
     __syncthreads();
+    lane_fence();
     stage_in<MODE, C, false>(sA, kin, ldq, rows, tid);
     stage<MODE, D, D, true>(sB, dhn, D, tid);
     __syncthreads();
+    lane_fence();
     // (6) dV = P^T dO + diag(s) K dh'
     for_cd_ld([&](int i0, int j0) {
       E4 e;
@@ -962,9 +991,11 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(GradArgs a) {
       }
     });
     __syncthreads();
+    lane_fence();
     stage<MODE, C, D, false>(sA, Vp, D, tid);
     stage<MODE, D, D, false>(sB, dhn, D, tid);
     __syncthreads();
+    lane_fence();
     // (7) V' dh'^T: dk's first term diag(s) V' dh'^T and its dG terms; <h, dh'>
     for_cd_ld([&](int i0, int j0) {
       E4 e;
@@ -1003,9 +1034,11 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(GradArgs a) {
       if (lane == 0) atomicAdd(sdG + C - 1, exp2_fast(sG[C - 1]) * hsum);
     }
     __syncthreads();
+    lane_fence();
     stage<MODE, C, D, false>(sA, dV, D, tid);
     stage<MODE, D, D, false>(sB, h, D, tid);
     __syncthreads();
+    lane_fence();
     // (8) dW = -dV h^T
     for_cd([&](int i0, int j0) {
       f32x4 acc = zero4();
@@ -1014,9 +1047,11 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(GradArgs a) {
       for (int i = 0; i < 4; ++i) dW[row(i0, i) * D + j0 + lr] = -acc[i];
     });
     __syncthreads();
+    lane_fence();
     stage<MODE, C, C, false>(sA, dR, C, tid);
     stage_in<MODE, C, true>(sB, kin, ldq, rows, tid);
     __syncthreads();
+    lane_fence();
     // (9) dq = E o (dO h^T) + dR K
     for_cd_ld([&](int i0, int j0) {
       E4 e;
@@ -1034,9 +1069,11 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(GradArgs a) {
       }
     });
     __syncthreads();
+    lane_fence();
     stage<MODE, C, C, true>(sA, Tm, C, tid);
     stage<MODE, C, D, true>(sB, dV, D, tid);
     __syncthreads();
+    lane_fence();
     // (10) dU~ = T^T dV: dv = diag(beta) dU~, dbeta_r += <dU~_r, v_r>
     for_cd_ld([&](int i0, int j0) {
       E4 e;
@@ -1057,8 +1094,10 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(GradArgs a) {
       add_row_sums(sdB, i0, bv, 1.f, lane);
     });
     __syncthreads();
+    lane_fence();
     stage<MODE, C, D, true>(sB, dW, D, tid);
     __syncthreads();
+    lane_fence();
     // (11) dW~ = T^T dW: dk += diag(beta E) dW~; rw_r = <dW~_r, k_r>:
     //      dbeta_r += E_r rw_r, dG_r += beta_r E_r rw_r
     for_cd_ld([&](int i0, int j0) {
@@ -1091,9 +1130,11 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(GradArgs a) {
       }
     });
     __syncthreads();
+    lane_fence();
     stage<MODE, C, D, false>(sA, dW, D, tid);
     stage_in<MODE, C, false>(sB, kin, ldq, rows, tid);
     __syncthreads();
+    lane_fence();
     // (12) (dW K^T) diag(beta E) (into dT; (13) adds the second term)
     for_cc([&](int i0, int j0) {
       f32x4 acc = zero4();
@@ -1103,9 +1144,11 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(GradArgs a) {
       for (int i = 0; i < 4; ++i) dT[row(i0, i) * C + c] = acc[i] * sE[c] * sBt[c];
     });
     __syncthreads();
+    lane_fence();
     stage<MODE, C, D, false>(sA, dV, D, tid);
     stage_in<MODE, C, false>(sB, vin, ldv, rows, tid);
     __syncthreads();
+    lane_fence();
     // (13) dT += (dV V^T) diag(beta)
     for_cc_ld([&](int i0, int j0) {
       E4 e;
@@ -1120,9 +1163,11 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(GradArgs a) {
       for (int i = 0; i < 4; ++i) dT[row(i0, i) * C + c] = e.v[i] + acc[i] * sBt[c];
     });
     __syncthreads();
+    lane_fence();
     stage<MODE, C, C, false>(sA, dT, C, tid);
     stage<MODE, C, C, false>(sB, Tm, C, tid);
     __syncthreads();
+    lane_fence();
     // (14) X = dT T^T
     for_cc([&](int i0, int j0) {
       f32x4 acc = zero4();
@@ -1131,9 +1176,11 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(GradArgs a) {
       for (int i = 0; i < 4; ++i) X[row(i0, i) * C + j0 + lr] = acc[i];
     });
     __syncthreads();
+    lane_fence();
     stage<MODE, C, C, true>(sA, Tm, C, tid);
     stage<MODE, C, C, true>(sB, X, C, tid);
     __syncthreads();
+    lane_fence();
     // (15) dS = -strict-lower(T^T X): dbeta, dG terms of diag(beta) dS o K K^T
     //      o Gam, dKk = diag(beta) dS o Gam
     for_cc_ld([&](int i0, int j0) {
@@ -1160,9 +1207,11 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(GradArgs a) {
       add_col_sums(sdG, j0, tv, -1.f, lane);
     });
     __syncthreads();
+    lane_fence();
     stage<MODE, C, C, true>(sA, dR, C, tid);
     stage_in<MODE, C, true>(sB, qin, ldq, rows, tid);
     __syncthreads();
+    lane_fence();
     // (16) dk += dR^T Q
     for_cd_ld([&](int i0, int j0) {
       E4 e;
@@ -1176,9 +1225,11 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(GradArgs a) {
       for (int i = 0; i < 4; ++i) dKp[row(i0, i) * D + j0 + lr] = e.v[i] + acc[i];
     });
     __syncthreads();
+    lane_fence();
     stage<MODE, C, C, false>(sA, dKk, C, tid);
     stage_in<MODE, C, true>(sB, kin, ldq, rows, tid);
     __syncthreads();
+    lane_fence();
     // (17) dk += dKk K
     for_cd_ld([&](int i0, int j0) {
       E4 e;
@@ -1192,8 +1243,10 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(GradArgs a) {
       for (int i = 0; i < 4; ++i) dKp[row(i0, i) * D + j0 + lr] = e.v[i] + acc[i];
     });
     __syncthreads();
+    lane_fence();
     stage<MODE, C, C, true>(sA, dKk, C, tid);
     __syncthreads();
+    lane_fence();
     // (18) dk = diag(s) V' dh'^T + diag(beta E) dW~ + dR^T Q + dKk K + dKk^T K;
     //      dg = reverse cumulative sum of dG; dbeta
     for_cd_ld([&](int i0, int j0) {
