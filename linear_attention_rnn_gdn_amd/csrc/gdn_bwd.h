@@ -50,6 +50,15 @@ template <int C, typename TI> struct BwdLds {
   static constexpr int RB = C * LDW * 4 > TB ? C * LDW * 4 : TB;   // region B: W; then Qeff^T
 };
 
+// 16 bytes at base + off_bytes, or zero where the row is not one of the
+// chunk's tokens (real = false; the offset then names the chunk's last row,
+// so the read stays in bounds).  The read is issued either way and the value
+// selected: a read behind a branch is waited for where the branches join.
+__device__ __forceinline__ uint4 row_or_zero(const void *base, size_t off_bytes, bool real) {
+  const uint4 x = *reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(base) + off_bytes);
+  return real ? x : uint4{0u, 0u, 0u, 0u};
+}
+
 template <int C, typename TI, int MODE, bool RAG>
 __global__ __launch_bounds__(256) void bwd_ddh_kernel(FwdArgs fa, BwdArgs a) {
   using L = BwdLds<C, TI>;
@@ -77,13 +86,14 @@ __global__ __launch_bounds__(256) void bwd_ddh_kernel(FwdArgs fa, BwdArgs a) {
 
   // Q, K rows (zero past the chunk's tokens), W (row stride D + 4) and G
   constexpr int VE = 16 / (int)sizeof(TI);
-  for (int e = tid; e < C * D / VE; e += 256) {
-    const int r = e / (D / VE), c = (e % (D / VE)) * VE;
-    uint4 xq{0u, 0u, 0u, 0u}, xk{0u, 0u, 0u, 0u};
-    if (r < rows) {
-      xq = *reinterpret_cast<const uint4 *>(reinterpret_cast<const TI *>(a.q) + ((t0 + r) * a.Hqk + hq) * D + c);
-      xk = *reinterpret_cast<const uint4 *>(reinterpret_cast<const TI *>(a.k) + ((t0 + r) * a.Hqk + hq) * D + c);
-    }
+  // (rows past the chunk's tokens read from its last row, then zeroed: a
+  // read behind a branch is waited for at once)
+  static_assert((C * D / VE) % 256 == 0, "whole vectors per thread");
+#pragma unroll 4
+  for (int u = 0; u < C * D / VE / 256; ++u) {
+    const int e = tid + 256 * u, r = e / (D / VE), c = (e % (D / VE)) * VE;
+    const size_t row = ((t0 + (r < rows ? r : rows - 1)) * a.Hqk + hq) * D + c;
+    const uint4 xq = row_or_zero(a.q, row * sizeof(TI), r < rows), xk = row_or_zero(a.k, row * sizeof(TI), r < rows);
     *reinterpret_cast<uint4 *>(sQ + r * L::LDQ + c) = xq;
     *reinterpret_cast<uint4 *>(sK + r * L::LDQ + c) = xk;
   }
@@ -156,10 +166,12 @@ __global__ __launch_bounds__(256) void bwd_ddh_kernel(FwdArgs fa, BwdArgs a) {
       *reinterpret_cast<float4 *>(sQt + (16 * dt + lr) * L::LDT + 16 * rt + 4 * g) =
           float4{qeff[u][dt][0], qeff[u][dt][1], qeff[u][dt][2], qeff[u][dt][3]};
   }
-  for (int e = tid; e < C * D / 4; e += 256) {
-    const int r = e / (D / 4), c = (e % (D / 4)) * 4;
-    float4 x{0.f, 0.f, 0.f, 0.f};
-    if (r < rows) x = *reinterpret_cast<const float4 *>(a.dO + ((t0 + r) * a.Hv + hv) * D + c);
+  static_assert((C * D / 4) % 256 == 0, "whole vectors per thread");
+#pragma unroll 4
+  for (int u = 0; u < C * D / 4 / 256; ++u) {
+    const int e = tid + 256 * u, r = e / (D / 4), c = (e % (D / 4)) * 4;
+    const float4 x = __builtin_bit_cast(
+        float4, row_or_zero(a.dO, (((t0 + (r < rows ? r : rows - 1)) * a.Hv + hv) * D + c) * sizeof(float), r < rows));
     sOt[(c + 0) * L::LDT + r] = x.x;
     sOt[(c + 1) * L::LDT + r] = x.y;
     sOt[(c + 2) * L::LDT + r] = x.z;
@@ -343,13 +355,7 @@ __device__ __forceinline__ void stage(char *buf, const float *src, size_t ld, in
   }
 }
 // NR x D input rows of type T (row stride ld elements) staged as fp32 values,
-// rows at or past `rows` (>= 1) zero.  Every load is issued (from the row
-// clamped into [0, rows)) and its value then selected: a load behind a
-// branch is waited for where the branches join.
-__device__ __forceinline__ uint4 row_or_zero(const void *base, size_t off_bytes, bool real) {
-  const uint4 x = *reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(base) + off_bytes);
-  return real ? x : uint4{0u, 0u, 0u, 0u};
-}
+// rows at or past `rows` (>= 1) zero (row_or_zero).
 template <int MODE, int NR, bool TR, typename T>
 __device__ __forceinline__ void stage_in(char *buf, const T *src, size_t ld, int rows, int tid) {
   constexpr int VE = 16 / (int)sizeof(T);
@@ -445,11 +451,21 @@ __device__ __forceinline__ void bwd_walk_body(const BwdArgs &a, size_t bh, char 
     const int lane = tl & 63, lr = lane & 15, g = lane >> 4;
     __syncthreads();   // every wave past the previous chunk's tiles
     constexpr int VE = 16 / (int)sizeof(TI);
-    for (int e = tid; e < C * D / VE; e += 512) {
-      const int r = e / (D / VE), c = (e % (D / VE)) * VE;
-      uint4 x{0u, 0u, 0u, 0u};
-      if (r < rows) x = *reinterpret_cast<const uint4 *>(reinterpret_cast<const TI *>(a.k) + ((t0 + r) * a.Hqk + hq) * D + c);
-      *reinterpret_cast<uint4 *>(sK + r * LDK + c) = x;
+    // (rows past the chunk's tokens read from its last row, then zeroed: a
+    // read behind a branch is waited for at once)
+    static_assert((C * D / VE) % 512 == 0, "whole vectors per thread");
+    {
+      uint4 xk[C * D / VE / 512];
+#pragma unroll
+      for (int u = 0; u < C * D / VE / 512; ++u) {
+        const int e = tl + 512 * u, r = e / (D / VE), c = (e % (D / VE)) * VE;
+        xk[u] = row_or_zero(a.k, (((t0 + (r < rows ? r : rows - 1)) * a.Hqk + hq) * D + c) * sizeof(TI), r < rows);
+      }
+#pragma unroll
+      for (int u = 0; u < C * D / VE / 512; ++u) {
+        const int e = tl + 512 * u, r = e / (D / VE), c = (e % (D / VE)) * VE;
+        *reinterpret_cast<uint4 *>(sK + r * LDK + c) = xk[u];
+      }
     }
     stage<MODE, C, D, true>(sW, a.W + cb * C * D, D, tl);
     if (tid < C) sG[tid] = a.G[cb * C + tid];
@@ -579,9 +595,8 @@ __device__ __forceinline__ void fwd_states_body(const StatesArgs &a, size_t bh, 
       uint4 w[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        w[i] = r0 + i < rows ? *reinterpret_cast<const uint4 *>(reinterpret_cast<const TI *>(a.k) +
-                                                                ((t0 + r0 + i) * a.Hqk + hq) * D + c)
-                             : uint4{0u, 0u, 0u, 0u};
+        w[i] = row_or_zero(a.k, (((t0 + (r0 + i < rows ? r0 + i : rows - 1)) * a.Hqk + hq) * D + c) * sizeof(TI),
+                           r0 + i < rows);
 #pragma unroll
       for (int j = 0; j < VE; ++j) {
         Four f;
@@ -859,7 +874,8 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(GradArgs a) {
       sG[tid] = Gr * LOG2E;
       sE[tid] = exp2_fast(Gr * LOG2E);
       sS[tid] = exp2_fast((Gl - Gr) * LOG2E);
-      sBt[tid] = tid < rows ? a.beta[(t0 + tid) * a.Hv + hv] : 0.f;
+      const float bt = a.beta[(t0 + (tid < rows ? tid : rows - 1)) * a.Hv + hv];
+      sBt[tid] = tid < rows ? bt : 0.f;
       sdG[tid] = 0.f;
       sdB[tid] = 0.f;
     }
