@@ -1042,7 +1042,10 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(GradArgs a) {
     });
     {
       float hsum = 0.f;
-      for (int e = tid; e < DD / 4; e += 64 * NW) {
+      static_assert((DD / 4) % (64 * NW) == 0, "whole vectors per thread");
+#pragma unroll
+      for (int u = 0; u < DD / 4 / (64 * NW); ++u) {
+        const int e = tid + 64 * NW * u;
         const float4 x = reinterpret_cast<const float4 *>(h)[e], y = reinterpret_cast<const float4 *>(dhn)[e];
         hsum += x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w;
       }
@@ -1280,11 +1283,26 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(GradArgs a) {
         if (r < rows) a.dk[((t0 + r) * oheads + oh) * D + c] = e.v[i] + acc[i];
       }
     });
-    if (tid < rows) {
-      float sdg = 0.f;
-      for (int j = tid; j < C; ++j) sdg += sdG[j];
-      a.dg[(t0 + tid) * a.Hv + hv] = sdg;
-      a.dbeta[(t0 + tid) * a.Hv + hv] = sdB[tid];
+    // dg = the reverse cumulative sum of dG: a suffix scan over each wave's
+    // 64 entries, the first wave adding the second's total (C = 128)
+    if (tid < C) {
+      const int ln = tid & 63;
+      float x = sdG[tid];
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_down(x, off, 64);
+        x += ln + off < 64 ? y : 0.f;
+      }
+      if (C > 64 && tid < 64) {
+        float t = sdG[64 + ln];
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) t += __shfl_xor(t, off, 64);
+        x += t;
+      }
+      if (tid < rows) {
+        a.dg[(t0 + tid) * a.Hv + hv] = x;
+        a.dbeta[(t0 + tid) * a.Hv + hv] = sdB[tid];
+      }
     }
   }
 }
