@@ -478,6 +478,18 @@ __global__ __launch_bounds__(PNT, 4) void prep_kernel(FwdArgs a) {   // two work
   // are those of the unpadded sequence
   const int rows = !RAG ? C : packed ? a.ctab[n].y : (int)(a.T - t0 < (size_t)C ? a.T - t0 : (size_t)C);
 
+  // g and beta first, from the row clamped into the chunk and then selected:
+  // read before the tiles, they can be waited for while the tiles are still
+  // in flight (behind a branch, or after the tiles, the cumsum waited for
+  // everything)
+  float g_in, b_in;
+  {
+    const size_t si = ((size_t)b * a.T + t0 + (tid < rows ? tid : rows - 1)) * a.Hv + hv;
+    const float gx = a.g[si], bx = a.beta[si];
+    g_in = tid < rows ? gx : 0.f;
+    b_in = tid < rows ? bx : 0.f;
+  }
+
   // The first half of the workgroup holds the K tile in registers, the second
   // half the V tile, one 8-row block per thread (kept for the transposed
   // copies, so K and V are read from memory once).
@@ -493,12 +505,8 @@ __global__ __launch_bounds__(PNT, 4) void prep_kernel(FwdArgs a) {   // two work
 
   // (1) decay cumsum over the chunk (inclusive), beta
   {
-    float x = 0.f, bx = 0.f;
-    if (tid < rows) {
-      const size_t si = ((size_t)b * a.T + t0 + tid) * a.Hv + hv;
-      x = a.g[si];
-      bx = a.beta[si];
-    }
+    float x = g_in;
+    const float bx = b_in;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const float y = __shfl_up(x, off, 64);
