@@ -2635,73 +2635,87 @@ __global__ __launch_bounds__(64 * WPG) void walk_out_kernel(FwdArgs a) {
 
     // ---- P^T = (K Q^T) o Gamma^T o [i <= r]: wave w forms the pairs (query
     //      tile rt, key tiles 2kp and 2kp + 1) of its query tiles {w, R-1-w}
-    //      (equal shares of the triangle); only the pairs on the diagonal are
-    //      masked
-    Frag<PKv::b> pt[RU][R / 2];
+    //      (equal shares of the triangle).  Every pair is masked (outside the
+    //      diagonal the mask keeps all), so that no branch stands between the
+    //      pairs and the LDS reads of one overlap the products of the last.
+    auto form_pair = [&](const QF *qf, int rt, int kp) -> Frag<PKv::b> {
+      QF k0[KBW], k1[KBW];
 #pragma unroll
-    for (int uu = 0; uu < RU; ++uu) {
-      // (opaque each chunk: the masks and decays derived from it are formed
-      // where used instead of being hoisted out of the chunk loop, where they
-      // would hold scalar registers for the whole walk)
-      int rt = uu == 0 ? wv : R - 1 - wv;
+      for (int kb = 0; kb < KBW; ++kb) {
+        k0[kb] = row_frag(sPK, 2 * kp, kb);
+        k1[kb] = row_frag(sPK, 2 * kp + 1, kb);   // (past the diagonal: read, multiplied, masked)
+      }
+      f32x4 p0 = zero4(), p1 = zero4();
+#pragma unroll
+      for (int kb = 0; kb < KBW; ++kb) {
+        mma(p0, k0[kb], qf[kb]);
+        mma(p1, k1[kb], qf[kb]);
+      }
+      const int r = 16 * rt + lr;
+      const float Gr = Gs[r] * LOG2E;
+      const float4 gk0 = *reinterpret_cast<const float4 *>(Gs + 32 * kp + lq);
+      const float4 gk1 = *reinterpret_cast<const float4 *>(Gs + 32 * kp + 16 + lq);
+      const float g0[4] = {gk0.x, gk0.y, gk0.z, gk0.w}, g1[4] = {gk1.x, gk1.y, gk1.z, gk1.w};
+      float b8[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int k0i = 32 * kp + lq + i, k1i = k0i + 16;
+        b8[i] = k0i <= r ? p0[i] * exp2_fast(Gr - g0[i] * LOG2E) : 0.f;
+        b8[4 + i] = k1i <= r ? p1[i] * exp2_fast(Gr - g1[i] * LOG2E) : 0.f;
+      }
+      return make_frag<PKv::b>(b8);
+    };
+    auto store_pair = [&](int rt, int kp, const Frag<PKv::b> &f) {
+      char *pf = sPK + (OL::pbase(rt) + kp) * 2048 + lane * 16;
+      if constexpr (PKv::b == F_SPLIT) {
+        *reinterpret_cast<bf16x8 *>(pf) = f.hi;
+        *reinterpret_cast<bf16x8 *>(pf + 1024) = f.lo;
+      } else {
+        *reinterpret_cast<float4 *>(pf) = float4{f.v[0], f.v[1], f.v[2], f.v[3]};
+        *reinterpret_cast<float4 *>(pf + 1024) = float4{f.v[4], f.v[5], f.v[6], f.v[7]};
+      }
+    };
+    if constexpr (RU == 2) {
+      // R = 8: the pairs (w, 0) and (7-w, 0..2) of every wave, and a fifth,
+      // (w, 1) for w >= 2 and (7-w, 3) below.  (Query tiles opaque each chunk:
+      // the masks and decays derived from them are formed where used instead
+      // of being hoisted out of the chunk loop, where they would hold scalar
+      // registers for the whole walk.)
+      int rt0 = wv, rt1 = R - 1 - wv, rtx = wv >= 2 ? wv : R - 1 - wv, kpx = wv >= 2 ? 1 : 3;
+      asm volatile("" : "+s"(rt0), "+s"(rt1), "+s"(rtx), "+s"(kpx));
+      QF q0[KBW], qx[KBW], q1[KBW];
+#pragma unroll
+      for (int kb = 0; kb < KBW; ++kb) {
+        q0[kb] = row_frag(sQ, rt0, kb);
+        qx[kb] = row_frag(sQ, rtx, kb);
+      }
+      Frag<PKv::b> pt[5];
+      pt[0] = form_pair(q0, rt0, 0);
+      pt[1] = form_pair(qx, rtx, kpx);
+#pragma unroll
+      for (int kb = 0; kb < KBW; ++kb) q1[kb] = row_frag(sQ, rt1, kb);
+#pragma unroll
+      for (int kp = 0; kp < 3; ++kp) pt[2 + kp] = form_pair(q1, rt1, kp);
+      wait_barrier<vm_lgkm0(63)>();   // every wave past the K tile
+      store_pair(rt0, 0, pt[0]);
+      store_pair(rtx, kpx, pt[1]);
+#pragma unroll
+      for (int kp = 0; kp < 3; ++kp) store_pair(rt1, kp, pt[2 + kp]);
+    } else {
+      // R = 4: query tile w; its pairs (w, 0) and, for w >= 2, (w, 1)
+      int rt = wv;
       asm volatile("" : "+s"(rt));
       QF qf[KBW];
 #pragma unroll
       for (int kb = 0; kb < KBW; ++kb) qf[kb] = row_frag(sQ, rt, kb);
-      const int r = 16 * rt + lr;
-      const float Gr = Gs[r] * LOG2E;
+      Frag<PKv::b> pt[2];
 #pragma unroll
-      for (int kp = 0; kp < R / 2; ++kp) {
-        if (2 * kp > rt) continue;
-        QF k0[KBW], k1[KBW];
+      for (int kp = 0; kp < 2; ++kp)
+        if (2 * kp <= rt) pt[kp] = form_pair(qf, rt, kp);
+      wait_barrier<vm_lgkm0(63)>();   // every wave past the K tile
 #pragma unroll
-        for (int kb = 0; kb < KBW; ++kb) {
-          k0[kb] = row_frag(sPK, 2 * kp, kb);
-          k1[kb] = row_frag(sPK, 2 * kp + 1, kb);   // (past the diagonal: read, multiplied, masked)
-        }
-        f32x4 p0 = zero4(), p1 = zero4();
-#pragma unroll
-        for (int kb = 0; kb < KBW; ++kb) {
-          mma(p0, k0[kb], qf[kb]);
-          mma(p1, k1[kb], qf[kb]);
-        }
-        const float4 gk0 = *reinterpret_cast<const float4 *>(Gs + 32 * kp + lq);
-        const float4 gk1 = *reinterpret_cast<const float4 *>(Gs + 32 * kp + 16 + lq);
-        const float g0[4] = {gk0.x, gk0.y, gk0.z, gk0.w}, g1[4] = {gk1.x, gk1.y, gk1.z, gk1.w};
-        float b8[8];
-        if (2 * kp + 1 < rt) {   // both key tiles wholly before the query tile
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            b8[i] = p0[i] * exp2_fast(Gr - g0[i] * LOG2E);
-            b8[4 + i] = p1[i] * exp2_fast(Gr - g1[i] * LOG2E);
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int k0i = 32 * kp + lq + i, k1i = k0i + 16;
-            b8[i] = k0i <= r ? p0[i] * exp2_fast(Gr - g0[i] * LOG2E) : 0.f;
-            b8[4 + i] = k1i <= r ? p1[i] * exp2_fast(Gr - g1[i] * LOG2E) : 0.f;
-          }
-        }
-        pt[uu][kp] = make_frag<PKv::b>(b8);
-      }
-    }
-    wait_barrier<vm_lgkm0(63)>();   // every wave past the K tile
-#pragma unroll
-    for (int uu = 0; uu < RU; ++uu) {
-      const int rt = uu == 0 ? wv : R - 1 - wv;
-#pragma unroll
-      for (int kp = 0; kp < R / 2; ++kp) {
-        if (2 * kp > rt) continue;
-        char *pf = sPK + (OL::pbase(rt) + kp) * 2048 + lane * 16;
-        if constexpr (PKv::b == F_SPLIT) {
-          *reinterpret_cast<bf16x8 *>(pf) = pt[uu][kp].hi;
-          *reinterpret_cast<bf16x8 *>(pf + 1024) = pt[uu][kp].lo;
-        } else {
-          *reinterpret_cast<float4 *>(pf) = float4{pt[uu][kp].v[0], pt[uu][kp].v[1], pt[uu][kp].v[2], pt[uu][kp].v[3]};
-          *reinterpret_cast<float4 *>(pf + 1024) = float4{pt[uu][kp].v[4], pt[uu][kp].v[5], pt[uu][kp].v[6], pt[uu][kp].v[7]};
-        }
-      }
+      for (int kp = 0; kp < 2; ++kp)
+        if (2 * kp <= rt) store_pair(rt, kp, pt[kp]);
     }
     wait_barrier<vm_lgkm0(63)>();   // P^T in place
 
