@@ -49,6 +49,16 @@ int varlen_nmax(const gdn_shape &s) { return (int)((int64_t)s.T / s.chunk + s.B)
 #ifndef GDN_FUSED_WPG
 #define GDN_FUSED_WPG 4
 #endif
+// From this many walks on, each wave of the walk with outputs holds two state
+// slices (one workgroup per walk, which forms the chunk's P^T and copies its
+// operands once for all 128 columns) instead of one (two workgroups per walk,
+// each forming P^T and copying the chunk).  Measured at chunk 128, bf16: 22-25%
+// faster from 256 to 8192 walks (the 262,144-token replay 5.18 -> 3.86 ms),
+// 30% slower at 128 walks (one workgroup per walk leaves half the compute
+// units idle).
+#ifndef GDN_FUSED_WIDE_MIN_WALKS
+#define GDN_FUSED_WIDE_MIN_WALKS 256
+#endif
 constexpr int kFusedWpg = GDN_FUSED_WPG;   // slices (waves) per workgroup of walk_out_kernel
 bool fused_walk(const gdn_shape &s) {
   return (int64_t)s.B * s.H_v * groups_of(s) >= GDN_FUSED_MIN_WALKS;
@@ -205,12 +215,19 @@ gdn_status launch_out(const FwdArgs &a, const Lx &x, bool rag = false) {
 
 template <int C, typename TI, int MODE, typename TO, int KIND = WALK>
 gdn_status launch_walk_out(const FwdArgs &a, const Lx &x) {
-  constexpr int NG = (KIND == WALK_A ? 2 : 1) * (D / 16) / kFusedWpg;   // workgroups per walk
   const long units = (long)a.B * a.Hv * a.jobs;
-  if (a.T % C)
-    launch(walk_out_kernel<C, TI, MODE, TO, kFusedWpg, true, KIND>, dim3((unsigned)(units * NG)), dim3(64 * kFusedWpg), x, a);
+  auto go = [&](auto spw) {
+    constexpr int SPW = decltype(spw)::value;   // state slices per wave
+    constexpr int NG = (KIND == WALK_A ? 2 : 1) * (D / 16) / (kFusedWpg * SPW);   // workgroups per walk
+    if (a.T % C)
+      launch(walk_out_kernel<C, TI, MODE, TO, kFusedWpg, true, KIND, SPW>, dim3((unsigned)(units * NG)), dim3(64 * kFusedWpg), x, a);
+    else
+      launch(walk_out_kernel<C, TI, MODE, TO, kFusedWpg, false, KIND, SPW>, dim3((unsigned)(units * NG)), dim3(64 * kFusedWpg), x, a);
+  };
+  if (KIND == WALK && units >= GDN_FUSED_WIDE_MIN_WALKS)
+    go(std::integral_constant<int, KIND == WALK ? 2 : 1>{});
   else
-    launch(walk_out_kernel<C, TI, MODE, TO, kFusedWpg, false, KIND>, dim3((unsigned)(units * NG)), dim3(64 * kFusedWpg), x, a);
+    go(std::integral_constant<int, 1>{});
   return check_launch();
 }
 

@@ -34,6 +34,8 @@
 //                  the groups' affine pairs.
 //   out_kernel     one 4-wave workgroup per (chunk, bh): the output, with
 //                  P^T formed once per chunk into LDS between its products.
+//   walk_out_kernel  the walk that also forms the outputs (many walks): four
+//                  waves per workgroup, one or two 16-column slices per wave.
 //
 // Workspace tensors (cb = bh*N + n indexes a chunk of a value head).  The
 // tensors that pass from one kernel to the next are stored fragment-major: in
@@ -2204,13 +2206,15 @@ __global__ __launch_bounds__(NT, 2) void out_kernel(FwdArgs a) {
 // walk with outputs (rows a5, a6 and a9 in one kernel): the sequential chunk
 // walk of walk_shared_kernel that also forms each chunk's outputs from the
 // chunk-start state and corrected values it holds in registers, so neither
-// goes to memory.  Per chunk, each wave (one 16-column slice c0.. of the
-// state):
-//   V' = U - W h                                   (W from LDS, h as B operand)
+// goes to memory.  Per chunk, each wave (SPW 16-column slices c0.. of the
+// state; SPW = 2: one workgroup of four waves holds all 128 columns of a
+// walk, so that P^T and the chunk's copies serve every column once):
 //   P^T = (K Q^T) o Gamma^T o [i <= r]              (shared: the workgroup's
 //                                                    waves split its tiles)
-//   O^T[c][r] = e^{G_r} (h^T Q^T)[c][r] + (V'^T P^T)[c][r]   for c in the slice
+//   V' = U - W h                                   (W from LDS, h as B operand)
+//   O^T[c][r] = e^{G_r} (h^T Q^T)[c][r] + (V'^T P^T)[c][r]   for c in a slice
 //   h <- e^{G_last} h + K^T (d o V')
+// U is loaded at the chunk's start and lands while P^T is formed.
 // The chunk-start state and V' are A operands of the output products as they
 // stand in registers: two stacked result tiles give lane group g the
 // k-values kk(g, j) of a block of 32, the k order in which the query and key
@@ -2221,7 +2225,7 @@ __global__ __launch_bounds__(NT, 2) void out_kernel(FwdArgs a) {
 // formed -- plus G; each slot is refilled for the next chunk (global_load_lds,
 // no registers) as soon as every wave is past its last read of it:
 //   W  after V',  K^T after the state update,  Q, K and G after the outputs.
-// Each refill thus has two of the chunk's phases to land.  The waits before
+// Each refill thus has at least two of the chunk's phases to land.  The waits before
 // the barriers count the copies, U loads and o stores each wave issued after
 // the ones waited for (the memory counter completes in issue order).
 template <int C, typename TI> struct WalkOutLds {
@@ -2383,7 +2387,7 @@ __device__ __forceinline__ void walk_a_columns(const FwdArgs &a, size_t bh, int 
     for (int i = 0; i < 4; ++i) a.pairA[bh * D * D + (size_t)(16 * m + 4 * g + i) * D + c0 + lr] = h[m][i];
 }
 
-template <int C, typename TI, int MODE, typename TO, int WPG, bool RAG, int KIND>
+template <int C, typename TI, int MODE, typename TO, int WPG, bool RAG, int KIND, int SPW>
 __global__ __launch_bounds__(64 * WPG) void walk_out_kernel(FwdArgs a) {
   using PR = Prec<MODE>;
   using PKw = PolicyKinds<PR::wh>;      // W x h
@@ -2399,7 +2403,8 @@ __global__ __launch_bounds__(64 * WPG) void walk_out_kernel(FwdArgs a) {
   static_assert(PKw::b == PKh::a || (PKw::b == F_BF16 && PKh::a == F_SPLIT), "W h takes the state split for h^T Q^T");
   constexpr int MV = C / 16, MH = D / 16, KBW = D / 32, KBK = C / 32, R = C / 16;
   static_assert(KIND == WALK || KIND == WALK_A, "walk kinds with outputs");
-  constexpr int NGH = (D / 16) / WPG;                      // workgroups of h columns per walk
+  static_assert(SPW == 1 || (SPW == 2 && KIND == WALK), "two slices per wave: walks without A columns");
+  constexpr int NGH = (D / 16) / (WPG * SPW);              // workgroups of h columns per walk
   constexpr int NG = (KIND == WALK_A ? 2 : 1) * NGH;        // workgroups per walk (A columns first)
   constexpr int BPF = L::BPF;
   // per wave and chunk: 1 KB copies of W, K^T, Q (and K); U loads; o stores
@@ -2408,10 +2413,10 @@ __global__ __launch_bounds__(64 * WPG) void walk_out_kernel(FwdArgs a) {
                 "copies shared out evenly");
   constexpr int GL = C / 4 / WPG;   // lanes of each wave copying 16 bytes of G
   static_assert(GL >= 1 && GL * 4 * WPG == C, "G copies shared out evenly");
-  constexpr int NU = MV;
+  constexpr int NU = MV * SPW;
   // o stores counted as issued: none in the partial-chunk instantiation,
   // where a store may be skipped
-  constexpr int NST = RAG ? 0 : R;
+  constexpr int NST = RAG ? 0 : R * SPW;
   constexpr int RU = R / (2 * WPG) > 0 ? 2 : 1;   // query tiles per wave in forming P^T
   static_assert(WPG == 4 && R == 4 * RU, "P^T: query tiles {w, R-1-w} (R = 8) or {w} (R = 4) per wave");
   // one array per slot (the compiler then tells the LDS reads of one slot
@@ -2436,32 +2441,37 @@ __global__ __launch_bounds__(64 * WPG) void walk_out_kernel(FwdArgs a) {
   }
   const int b = (int)(bh / a.Hv), hv = (int)(bh % a.Hv), hq = hv / (a.Hv / a.Hqk);
   const int lane = threadIdx.x & 63, lr = lane & 15, g = lane >> 4, lq = 4 * g;
-  const int slice = grp * WPG + wv, c0 = 16 * slice;
+  // this wave's state slices: slice0 .. slice0 + SPW - 1, columns c0 + 16 s ..
+  const int slice0 = (grp * WPG + wv) * SPW, c0 = 16 * slice0;
   const int nfirst = a.n0 + job * a.cpj;   // first chunk of this walk in its sequence row
   const int cpj = a.cpj;
   const size_t cb0 = uniform64(bh * a.N + nfirst);
   const long long ktoff = (long long)uniform64((unsigned long long)kt_offset(a, bh));
 
-  // state tiles: h[m] holds rows 16m + 4g + i, column c0 + lr
-  f32x4 h[MH];
+  // state tiles: h[s][m] holds rows 16m + 4g + i, column c0 + 16s + lr
+  f32x4 h[SPW][MH];
 #pragma unroll
-  for (int m = 0; m < MH; ++m)
+  for (int s = 0; s < SPW; ++s)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int kr = 16 * m + 4 * g + i;
-      float x = 0.f;
-      if (a.init) {
-        const float *src = a.init_per_job ? a.init + (bh * a.jobs + job) * D * D : a.init + bh * D * D;
-        x = src[(size_t)kr * D + c0 + lr];
+    for (int m = 0; m < MH; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int kr = 16 * m + 4 * g + i;
+        float x = 0.f;
+        if (a.init) {
+          const float *src = a.init_per_job ? a.init + (bh * a.jobs + job) * D * D : a.init + bh * D * D;
+          x = src[(size_t)kr * D + c0 + 16 * s + lr];
+        }
+        h[s][m][i] = x;
       }
-      h[m][i] = x;
-    }
   auto store_final = [&]() {
     if (a.fin && job == a.jobs - 1) {   // (the last group's end state)
 #pragma unroll
-      for (int m = 0; m < MH; ++m)
+      for (int s = 0; s < SPW; ++s)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a.fin[bh * D * D + (size_t)(16 * m + 4 * g + i) * D + c0 + lr] = h[m][i];
+        for (int m = 0; m < MH; ++m)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) a.fin[bh * D * D + (size_t)(16 * m + 4 * g + i) * D + c0 + 16 * s + lr] = h[s][m][i];
     }
   };
   if (cpj == 0) {
@@ -2533,11 +2543,13 @@ __global__ __launch_bounds__(64 * WPG) void walk_out_kernel(FwdArgs a) {
     copy_rows(a.k, tok0, rows, sPK);
     copy_g(cb0 + cc);
   };
-  float4 u[MV];
+  float4 u[SPW][MV];
   auto fetch_u = [&](size_t cb) {
 #pragma unroll
-    for (int m = 0; m < MV; ++m)
-      u[m] = *reinterpret_cast<const float4 *>(a.U + ((cb * MV + m) * (D / 16) + slice) * 256 + lane * 4);
+    for (int s = 0; s < SPW; ++s)
+#pragma unroll
+      for (int m = 0; m < MV; ++m)
+        u[s][m] = *reinterpret_cast<const float4 *>(a.U + ((cb * MV + m) * (D / 16) + slice0 + s) * 256 + lane * 4);
   };
   // operand fragment p of the W or K^T slot
   auto frag = [&](const char *slot, int p) -> Frag<PKw::a> {
@@ -2584,12 +2596,11 @@ __global__ __launch_bounds__(64 * WPG) void walk_out_kernel(FwdArgs a) {
   const float *Gs = sG;
   TO *og = reinterpret_cast<TO *>(a.o);
 
-  // the first chunk's operands
+  // the first chunk's copies, in the order of the chunk loop's (W, then Q,
+  // K and G, then K^T)
   copy_w(cb0);
-  copy_kt(cb0);
   copy_qkg(0);
-  fetch_u(cb0);
-  wait_barrier<vm_lgkm0(0)>();
+  copy_kt(cb0);
 
   // one chunk; more: a next chunk follows, whose operands are copied during
   // this one (the last chunk is a separate copy of the body, so that the
@@ -2603,35 +2614,11 @@ __global__ __launch_bounds__(64 * WPG) void walk_out_kernel(FwdArgs a) {
     int rows;
     chunk_tokens(cc, tok0, rows);
 
-    // ---- V' = U - W h.  W fragments are read one output tile ahead.
-    Frag<PKw::b> hb[KBW];
-#pragma unroll
-    for (int kb = 0; kb < KBW; ++kb) {
-      const float x[8] = {h[2 * kb][0], h[2 * kb][1], h[2 * kb][2], h[2 * kb][3],
-                          h[2 * kb + 1][0], h[2 * kb + 1][1], h[2 * kb + 1][2], h[2 * kb + 1][3]};
-      hb[kb] = make_frag<PKw::b>(x);
-    }
-    f32x4 vps[MV];
-    {
-      Frag<PKw::a> fa[2][KBW];
-#pragma unroll
-      for (int kb = 0; kb < KBW; ++kb) fa[0][kb] = frag(sW, kb);
-#pragma unroll
-      for (int m = 0; m < MV; ++m) {
-        if (m + 1 < MV) {
-#pragma unroll
-          for (int kb = 0; kb < KBW; ++kb) fa[(m + 1) & 1][kb] = frag(sW, (m + 1) * KBW + kb);
-        }
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int kb = 0; kb < KBW; ++kb) mma(acc, fa[m & 1][kb], hb[kb]);
-        vps[m] = f32x4{u[m].x - acc[0], u[m].y - acc[1], u[m].z - acc[2], u[m].w - acc[3]};
-      }
-    }
-    // every wave past W; this chunk's Q, K and G landed (the K^T copies,
-    // issued after them, may still be in flight)
-    wait_barrier<vm_lgkm0(NCK)>();
-    if constexpr (more) copy_w(cb + 1);
+    // U of this chunk, issued first: it lands while P^T is formed
+    fetch_u(cb);
+    // this chunk's W, Q, K and G landed (its K^T copies and U, issued after
+    // them, may be in flight)
+    wait_barrier<vm_lgkm0(NCK + NU)>();
 
     // ---- P^T = (K Q^T) o Gamma^T o [i <= r]: wave w forms the pairs (query
     //      tile rt, key tiles 2kp and 2kp + 1) of its query tiles {w, R-1-w}
@@ -2719,36 +2706,94 @@ __global__ __launch_bounds__(64 * WPG) void walk_out_kernel(FwdArgs a) {
     }
     wait_barrier<vm_lgkm0(63)>();   // P^T in place
 
-    // ---- outputs O^T = e^{G_r} h^T Q^T + V'^T P^T for this slice's columns:
-    //      first h^T Q^T for every query tile (query fragments one tile ahead),
-    //      then V'^T P^T pair by pair (P^T fragments one pair ahead)
-    f32x4 a1[R];
-    {
-      Frag<PKh::a> hT[KBW];   // the chunk-start state, split for this product
+    // ---- V' = U - W h.  W fragments are read one output tile ahead (and
+    //      serve every slice of the wave).
+    Frag<PKw::b> hb[SPW][KBW];
+#pragma unroll
+    for (int s = 0; s < SPW; ++s)
 #pragma unroll
       for (int kb = 0; kb < KBW; ++kb) {
-        const float x[8] = {h[2 * kb][0], h[2 * kb][1], h[2 * kb][2], h[2 * kb][3],
-                            h[2 * kb + 1][0], h[2 * kb + 1][1], h[2 * kb + 1][2], h[2 * kb + 1][3]};
-        hT[kb] = make_frag<PKh::a>(x);
+        const float x[8] = {h[s][2 * kb][0], h[s][2 * kb][1], h[s][2 * kb][2], h[s][2 * kb][3],
+                            h[s][2 * kb + 1][0], h[s][2 * kb + 1][1], h[s][2 * kb + 1][2], h[s][2 * kb + 1][3]};
+        hb[s][kb] = make_frag<PKw::b>(x);
       }
-      QF qf[2][KBW];
+    f32x4 vps[SPW][MV];
+    {
+      Frag<PKw::a> fa[2][KBW];
 #pragma unroll
-      for (int kb = 0; kb < KBW; ++kb) qf[0][kb] = row_frag(sQ, 0, kb);
+      for (int kb = 0; kb < KBW; ++kb) fa[0][kb] = frag(sW, kb);
 #pragma unroll
-      for (int rt = 0; rt < R; ++rt) {
-        if (rt + 1 < R) {
+      for (int m = 0; m < MV; ++m) {
+        if (m + 1 < MV) {
 #pragma unroll
-          for (int kb = 0; kb < KBW; ++kb) qf[(rt + 1) & 1][kb] = row_frag(sQ, rt + 1, kb);
+          for (int kb = 0; kb < KBW; ++kb) fa[(m + 1) & 1][kb] = frag(sW, (m + 1) * KBW + kb);
         }
-        a1[rt] = zero4();
 #pragma unroll
-        for (int kb = 0; kb < KBW; ++kb) mma(a1[rt], hT[kb], qf[rt & 1][kb]);
+        for (int s = 0; s < SPW; ++s) {
+          f32x4 acc = zero4();
+#pragma unroll
+          for (int kb = 0; kb < KBW; ++kb) mma(acc, fa[m & 1][kb], hb[s][kb]);
+          vps[s][m] = f32x4{u[s][m].x - acc[0], u[s][m].y - acc[1], u[s][m].z - acc[2], u[s][m].w - acc[3]};
+        }
       }
     }
+    // (V' complete here: sunk below the next chunk's W copies, its
+    // subtractions would wait for those copies as well as for U)
+#pragma unroll
+    for (int s = 0; s < SPW; ++s)
+#pragma unroll
+      for (int m = 0; m < MV; ++m) asm volatile("" : "+v"(vps[s][m]));
+    wait_barrier<vm_lgkm0(63)>();   // every wave past W
+    if constexpr (more) copy_w(cb + 1);
+
+    // ---- outputs O^T = e^{G_r} h^T Q^T + V'^T P^T for each slice's columns,
+    //      one slice after the other: first h^T Q^T for every query tile
+    //      (query fragments one tile ahead), then V'^T P^T pair by pair (P^T
+    //      fragments one pair ahead)
     const float gl2 = Gs[C - 1] * LOG2E;
     const float gl = exp2_fast(gl2);
-    Frag<PKk::b> vb[KBK];
-    {
+    Frag<PKk::b> vb[SPW][KBK];   // d o V' for the state update (G is recopied before it)
+    auto pfrag = [&](int p) -> Frag<PKv::b> {
+      const char *pf = sPK + p * 2048 + lane * 16;
+      Frag<PKv::b> bf;
+      if constexpr (PKv::b == F_SPLIT) {
+        bf.hi = *reinterpret_cast<const bf16x8 *>(pf);
+        bf.lo = *reinterpret_cast<const bf16x8 *>(pf + 1024);
+      } else {
+        const float4 x0 = *reinterpret_cast<const float4 *>(pf), x1 = *reinterpret_cast<const float4 *>(pf + 1024);
+        bf.v[0] = x0.x; bf.v[1] = x0.y; bf.v[2] = x0.z; bf.v[3] = x0.w;
+        bf.v[4] = x1.x; bf.v[5] = x1.y; bf.v[6] = x1.z; bf.v[7] = x1.w;
+      }
+      return bf;
+    };
+#pragma unroll
+    for (int s = 0; s < SPW; ++s) {
+      // (one slice after the other: the scheduler would otherwise interleave
+      // both slices' products and hold both sets of operands)
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4 a1[R];
+      {
+        Frag<PKh::a> hT[KBW];   // the chunk-start state, split for this product
+#pragma unroll
+        for (int kb = 0; kb < KBW; ++kb) {
+          const float x[8] = {h[s][2 * kb][0], h[s][2 * kb][1], h[s][2 * kb][2], h[s][2 * kb][3],
+                              h[s][2 * kb + 1][0], h[s][2 * kb + 1][1], h[s][2 * kb + 1][2], h[s][2 * kb + 1][3]};
+          hT[kb] = make_frag<PKh::a>(x);
+        }
+        QF qf[2][KBW];
+#pragma unroll
+        for (int kb = 0; kb < KBW; ++kb) qf[0][kb] = row_frag(sQ, 0, kb);
+#pragma unroll
+        for (int rt = 0; rt < R; ++rt) {
+          if (rt + 1 < R) {
+#pragma unroll
+            for (int kb = 0; kb < KBW; ++kb) qf[(rt + 1) & 1][kb] = row_frag(sQ, rt + 1, kb);
+          }
+          a1[rt] = zero4();
+#pragma unroll
+          for (int kb = 0; kb < KBW; ++kb) mma(a1[rt], hT[kb], qf[rt & 1][kb]);
+        }
+      }
       Frag<PKv::a> vT[KBK];
 #pragma unroll
       for (int kb = 0; kb < KBK; ++kb) {
@@ -2756,25 +2801,12 @@ __global__ __launch_bounds__(64 * WPG) void walk_out_kernel(FwdArgs a) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int m = 2 * kb + j / 4, i = j % 4;
-          x[j] = vps[m][i];
-          y[j] = vps[m][i] * exp2_fast(gl2 - Gs[16 * m + lq + i] * LOG2E);
+          x[j] = vps[s][m][i];
+          y[j] = vps[s][m][i] * exp2_fast(gl2 - Gs[16 * m + lq + i] * LOG2E);
         }
         vT[kb] = make_frag<PKv::a>(x);
-        vb[kb] = make_frag<PKk::b>(y);
+        vb[s][kb] = make_frag<PKk::b>(y);
       }
-      auto pfrag = [&](int p) -> Frag<PKv::b> {
-        const char *pf = sPK + p * 2048 + lane * 16;
-        Frag<PKv::b> bf;
-        if constexpr (PKv::b == F_SPLIT) {
-          bf.hi = *reinterpret_cast<const bf16x8 *>(pf);
-          bf.lo = *reinterpret_cast<const bf16x8 *>(pf + 1024);
-        } else {
-          const float4 x0 = *reinterpret_cast<const float4 *>(pf), x1 = *reinterpret_cast<const float4 *>(pf + 1024);
-          bf.v[0] = x0.x; bf.v[1] = x0.y; bf.v[2] = x0.z; bf.v[3] = x0.w;
-          bf.v[4] = x1.x; bf.v[5] = x1.y; bf.v[6] = x1.z; bf.v[7] = x1.w;
-        }
-        return bf;
-      };
       // pairs in storage order: (rt, kp), kp <= rt / 2, p = pbase(rt) + kp
       Frag<PKv::b> pf[2];
       pf[0] = pfrag(0);
@@ -2792,7 +2824,7 @@ __global__ __launch_bounds__(64 * WPG) void walk_out_kernel(FwdArgs a) {
         TO ov[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) ov[i] = from_f32<TO>(er * a1[rt][i] + a2[i]);
-        TO *dst = og + ((tok0 + r) * a.Hv + hv) * D + c0 + lq;
+        TO *dst = og + ((tok0 + r) * a.Hv + hv) * D + c0 + 16 * s + lq;
         if (!RAG || r < rows) {
           if constexpr (sizeof(TO) == 4) st16_stream(dst, ov);
           else st8_stream(dst, ov);
@@ -2803,12 +2835,10 @@ __global__ __launch_bounds__(64 * WPG) void walk_out_kernel(FwdArgs a) {
     // W and this chunk's o stores, issued after it, may be in flight)
     if constexpr (more) wait_barrier<vm_lgkm0(NCW + NST)>();
     else wait_barrier<vm_lgkm0(NST)>();
-    if constexpr (more) {
-      copy_qkg(cc + 1);
-      fetch_u(cb + 1);
-    }
+    if constexpr (more) copy_qkg(cc + 1);
 
-    // ---- h <- e^{G_last} h + K^T (d o V'), K^T fragments one state tile ahead
+    // ---- h <- e^{G_last} h + K^T (d o V'), K^T fragments one state tile
+    //      ahead (and serving every slice of the wave)
     {
       Frag<PKw::a> fk[2][KBK];
 #pragma unroll
@@ -2819,17 +2849,20 @@ __global__ __launch_bounds__(64 * WPG) void walk_out_kernel(FwdArgs a) {
 #pragma unroll
           for (int kb = 0; kb < KBK; ++kb) fk[(m + 1) & 1][kb] = frag(sKt, (m + 1) * KBK + kb);
         }
-        f32x4 acc2 = zero4();
 #pragma unroll
-        for (int kb = 0; kb < KBK; ++kb) mma(acc2, fk[m & 1][kb], vb[kb]);
+        for (int s = 0; s < SPW; ++s) {
+          f32x4 acc2 = zero4();
 #pragma unroll
-        for (int i = 0; i < 4; ++i) h[m][i] = gl * h[m][i] + acc2[i];
+          for (int kb = 0; kb < KBK; ++kb) mma(acc2, fk[m & 1][kb], vb[s][kb]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) h[s][m][i] = gl * h[s][m][i] + acc2[i];
+        }
       }
     }
     if constexpr (more) {
       // every wave past K^T; the next chunk's W landed (this chunk's o
-      // stores and the next chunk's Q, K, G copies and U may be in flight)
-      wait_barrier<vm_lgkm0(NST + 2 * NCQ + 1 + NU)>();
+      // stores and the next chunk's Q, K and G copies may be in flight)
+      wait_barrier<vm_lgkm0(NST + 2 * NCQ + 1)>();
       copy_kt(cb + 1);
     }
   };

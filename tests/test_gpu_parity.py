@@ -210,12 +210,19 @@ def test_bf16_output(gdn):
     _check("h_T", h, h_ref, 2e-2, ro)
 
 
-@pytest.mark.parametrize("dtype,C,B,Hqk,Hv,T", [("bf16", 128, 4, 16, 32, 1000), ("bf16", 64, 8, 8, 16, 64 * 5),
-                                                 ("f32", 64, 6, 8, 24, 64 * 4 - 9)])
+@pytest.mark.parametrize("dtype,C,B,Hqk,Hv,T", [
+    ("bf16", 128, 4, 16, 32, 1000),     # 128 walks: one state slice per wave
+    ("bf16", 64, 8, 8, 16, 64 * 5),
+    ("f32", 64, 6, 8, 24, 64 * 4 - 9),
+    ("bf16", 128, 5, 17, 51, 300),      # 255 walks, partial last chunk
+    ("bf16", 128, 8, 16, 32, 1000),     # 256 walks: two state slices per wave
+    ("bf16", 64, 16, 8, 16, 64 * 3),    # 256 walks at C = 64
+    ("f32", 64, 8, 8, 32, 64 * 3 - 5),  # 256 walks, fp32, partial last chunk
+])
 def test_walk_with_outputs_bf16_output(gdn, dtype, C, B, Hqk, Hv, T):
-    # 128 walks or more: the walk forms the outputs itself (walk_out_kernel).
-    # A bf16 o is the fp32-o call's
-    # values rounded once, bit for bit; the fp32 o within the bar
+    # 128 walks or more: the walk forms the outputs itself (walk_out_kernel),
+    # from 256 walks on with two state slices per wave.  A bf16 o is the
+    # fp32-o call's values rounded once, bit for bit; the fp32 o within the bar
     w = WORKLOADS["tiny"].replace(T=T, B=B, Hqk=Hqk, Hv=Hv, chunk=C, dtype=dtype, h0_std=0.05)
     x = make_inputs(w, device="cuda", seed=B * Hv + T)
     args = (x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"])
