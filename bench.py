@@ -6,10 +6,12 @@ inputs (decay cumsum, UT transform, WY pair, the sequential chunk walk or the
 chunk-group fold / prefix / replay, and the outputs), with inputs, outputs
 and workspace resident in HBM before the timed region starts.
 
-Timing: each of the K timed steps runs after a 512 MB write that evicts the
+Timing: each of the K timed steps runs after a 512 MB read that evicts the
 memory-side cache (MALL, 256 MB), and is bracketed by its own HIP events on
 the stream the library launches on (torch's current stream); `ms_per_step` is
-the median.  The same K steps run back to back (cache warm) are reported as
+the median.  The same K steps each after a 512 MB write instead are reported
+as `after_write_flush` (the cache then holds ~256 MB of that buffer's dirty
+lines, whose write-back lands in the step), and back to back (cache warm) as
 `warm`.
 
 Prints ONE JSON line.  `value` is tokens/s (B*T per step).  `roofline`
@@ -102,6 +104,7 @@ def measure_backward(w, x, steps, warmup, torch, gdn, with_cpu=True):
     flops, nbytes = bwd_algorithmic(w)
     t = tm["cold"] * 1e-3
     res = {"workload": w.name, "ms_per_step": tm["cold"], "warm_ms_per_step": tm["warm"],
+           "after_write_flush_ms_per_step": tm["dirty"],
            "value": w.tokens / t, "unit": "tokens/s",
            "roofline": {"bound": "mfma", "achieved": flops / t / 1e12, "peak": BF16_PEAK / 1e12,
                         "unit": "TFLOP/s", "frac": flops / t / BF16_PEAK,
@@ -358,26 +361,37 @@ FLUSH_BYTES = 512 << 20   # twice the 256 MB memory-side cache (MALL)
 
 
 def time_steps(fn, steps, warmup):
-    """K steps, each after a 512 MB write that evicts the memory-side cache
-    and timed alone with HIP events on the current stream (median: `cold`),
-    then the same K steps back to back (mean: `warm`).  Returns ms per step."""
+    """K steps, each after reading a 512 MB buffer, which evicts the
+    memory-side cache and leaves it holding clean lines only, timed alone with
+    HIP events on the current stream (median: `cold`); the same K steps each
+    after a 512 MB write instead (median: `dirty`: the step then also writes
+    back the cache's dirty lines of that buffer, about 256 MB, which is not its
+    own work); then the K steps back to back (mean: `warm`).  Returns ms per
+    step."""
     import statistics
 
     import torch
 
     flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    flush.fill_(1.0)
+    sink = torch.empty(1, dtype=torch.float32, device="cuda")
     ramp_clocks(fn)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for i in range(steps):
-        flush.fill_(float(i))
-        ev[i][0].record()
-        fn()
-        ev[i][1].record()
-    torch.cuda.synchronize()
-    cold = statistics.median(a.elapsed_time(b) for a, b in ev)
+
+    def timed(evict):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for i in range(steps):
+            evict(i)
+            ev[i][0].record()
+            fn()
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        return statistics.median(a.elapsed_time(b) for a, b in ev)
+
+    cold = timed(lambda i: sink.copy_(flush.sum().view(1)))
+    dirty = timed(lambda i: flush.fill_(float(i)))
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -386,7 +400,7 @@ def time_steps(fn, steps, warmup):
     e1.record()
     torch.cuda.synchronize()
     del flush
-    return {"cold": cold, "warm": e0.elapsed_time(e1) / steps}
+    return {"cold": cold, "dirty": dirty, "warm": e0.elapsed_time(e1) / steps}
 
 
 def main():
@@ -468,7 +482,7 @@ def main():
         x2, step2 = setup(w2)
         tm2 = time_steps(step2, max(3, args.steps // 4), 1)
         sec = measure(w2, step2, tm2, max(3, args.steps // 4), 1, stage_bits, torch)
-        line["secondary"] = {kk: sec[kk] for kk in ("value", "unit", "ms_per_step", "warm", "roofline",
+        line["secondary"] = {kk: sec[kk] for kk in ("value", "unit", "ms_per_step", "warm", "after_write_flush", "roofline",
                                                     "mfma_util_pct", "stages_ms", "dominant_kernel")}
         line["secondary"]["workload"] = w2.name
         if not args.no_cpu_baseline:
@@ -568,6 +582,8 @@ def measure(w, step, tm, steps, warmup, stage_bits, torch):
                    "o_dtype": "f32", "parallelism": "single GPU"},
         "warm": {"ms_per_step": tm["warm"], "value": w.tokens / (tm["warm"] * 1e-3),
                  "hbm_frac": nbytes / (tm["warm"] * 1e-3) / HBM_PEAK},
+        "after_write_flush": {"ms_per_step": tm["dirty"], "value": w.tokens / (tm["dirty"] * 1e-3),
+                              "hbm_frac": nbytes / (tm["dirty"] * 1e-3) / HBM_PEAK},
         "mfma_util_pct": 100.0 * flops / t / BF16_PEAK,
         "roofline": roof,
         "algorithmic": {"flops": flops, "bytes": nbytes, "mfma_frac": flops / t / BF16_PEAK},
