@@ -755,9 +755,9 @@ gdn_status run_bwd_state(const gdn_shape &s, const void *q, const void *k, const
   b.dhT = dh_T; b.dh = dh; b.dh0 = dh0;
   const unsigned units = (unsigned)((long)b.N * s.B * s.H_v);
   if (s.T % C)
-    hipLaunchKernelGGL((bwd_ddh_kernel<C, TI, MODE, true>), dim3(units), dim3(256), 0, st, a, b);
+    hipLaunchKernelGGL((bwd_ddh_kernel<C, TI, MODE, true>), dim3(units), dim3(ddh_threads<C>()), 0, st, a, b);
   else
-    hipLaunchKernelGGL((bwd_ddh_kernel<C, TI, MODE, false>), dim3(units), dim3(256), 0, st, a, b);
+    hipLaunchKernelGGL((bwd_ddh_kernel<C, TI, MODE, false>), dim3(units), dim3(ddh_threads<C>()), 0, st, a, b);
   GDN_TRY(check_launch());
   if (s.T % C)
     hipLaunchKernelGGL((bwd_walk_kernel<C, TI, MODE, true>), dim3((unsigned)(s.B * s.H_v)), dim3(512), 0, st, b);
@@ -823,10 +823,10 @@ gdn_status run_bwd_grads(const gdn_shape &s, const void *q, const void *k, const
   const unsigned units = (unsigned)((long)N * s.B * s.H_v);
   // the reverse walk's chunk term, then both walks in one launch
   if (rag) {
-    hipLaunchKernelGGL((bwd_ddh_kernel<C, TI, MODE, true>), dim3(units), dim3(256), 0, st, a, b);
+    hipLaunchKernelGGL((bwd_ddh_kernel<C, TI, MODE, true>), dim3(units), dim3(ddh_threads<C>()), 0, st, a, b);
     hipLaunchKernelGGL((bwd_walks_kernel<C, TI, MODE, true>), dim3(2 * rowsBH), dim3(512), 0, st, sa, b);
   } else {
-    hipLaunchKernelGGL((bwd_ddh_kernel<C, TI, MODE, false>), dim3(units), dim3(256), 0, st, a, b);
+    hipLaunchKernelGGL((bwd_ddh_kernel<C, TI, MODE, false>), dim3(units), dim3(ddh_threads<C>()), 0, st, a, b);
     hipLaunchKernelGGL((bwd_walks_kernel<C, TI, MODE, false>), dim3(2 * rowsBH), dim3(512), 0, st, sa, b);
   }
   GDN_TRY(check_launch());

@@ -35,10 +35,13 @@ struct BwdArgs {
   float *dh0;                 // [B, H_v, D, D], or null
 };
 
-// the chunk-parallel term ddh_n = Qeff^T dO, one workgroup of four waves per
-// (chunk, value head); Qeff = diag(e^G) Q - P W is formed per query tile
-// (wave w takes query tiles {w, R-1-w}, or {w} at C = 64), P^T's tiles in
-// registers, then written to LDS transposed next to dO^T for the product.
+// the chunk-parallel term ddh_n = Qeff^T dO, one workgroup per (chunk, value
+// head) of eight waves at C = 128 (four at C = 64); Qeff = diag(e^G) Q - P W
+// is formed per query tile: wave w takes query tiles {w', R-1-w'} (w' = w mod
+// 4; {w'} at C = 64), forms their P^T tiles in registers and, with the other
+// wave of the same w' at C = 128, half of the Qeff columns each; Qeff is then
+// written to LDS transposed next to dO^T for the product.
+template <int C> constexpr int ddh_threads() { return C >= 128 ? 512 : 256; }
 template <int C, typename TI> struct BwdLds {
   static constexpr int LDQ = D + 16 / (int)sizeof(TI);     // Q, K row stride: 16 bytes of padding put
                                                            // the 16 rows a fragment read touches on distinct banks
@@ -60,11 +63,13 @@ __device__ __forceinline__ uint4 row_or_zero(const void *base, size_t off_bytes,
 }
 
 template <int C, typename TI, int MODE, bool RAG>
-__global__ __launch_bounds__(256) void bwd_ddh_kernel(FwdArgs fa, BwdArgs a) {
+__global__ __launch_bounds__(ddh_threads<C>()) void bwd_ddh_kernel(FwdArgs fa, BwdArgs a) {
   using L = BwdLds<C, TI>;
   constexpr int PX = MODE == MODE_F32 ? P_F32 : P_BF16;       // K Q^T
   constexpr int PS = MODE == MODE_F32 ? P_F32 : P_SPLIT_AB;   // fp32 x fp32
   constexpr int R = C / 16, RU = R >= 8 ? 2 : 1, KBD = D / 32, TD = D / 16;
+  constexpr int NTH = ddh_threads<C>(), NW = NTH / 64;        // threads, waves
+  constexpr int DS = NW / 4, TDW = TD / DS;                   // waves per query-tile pair, Qeff column tiles each
   static_assert(R == 4 * RU, "query tiles {w, R-1-w} per wave");
   __shared__ __align__(16) char rA[L::RA];
   __shared__ __align__(16) char rB[L::RB];
@@ -83,21 +88,22 @@ __global__ __launch_bounds__(256) void bwd_ddh_kernel(FwdArgs fa, BwdArgs a) {
   const int rows = !RAG ? C : (a.T - n * C < C ? a.T - n * C : C);
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, g = lane >> 4;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wq = wv % 4, dt0 = (wv / 4) * TDW;   // query-tile pair, first Qeff column tile
 
   // Q, K rows (zero past the chunk's tokens), W (row stride D + 4) and G
   constexpr int VE = 16 / (int)sizeof(TI);
   // (rows past the chunk's tokens read from its last row, then zeroed: a
   // read behind a branch is waited for at once)
-  static_assert((C * D / VE) % 256 == 0, "whole vectors per thread");
+  static_assert((C * D / VE) % NTH == 0, "whole vectors per thread");
 #pragma unroll 4
-  for (int u = 0; u < C * D / VE / 256; ++u) {
-    const int e = tid + 256 * u, r = e / (D / VE), c = (e % (D / VE)) * VE;
+  for (int u = 0; u < C * D / VE / NTH; ++u) {
+    const int e = tid + NTH * u, r = e / (D / VE), c = (e % (D / VE)) * VE;
     const size_t row = ((t0 + (r < rows ? r : rows - 1)) * a.Hqk + hq) * D + c;
     const uint4 xq = row_or_zero(a.q, row * sizeof(TI), r < rows), xk = row_or_zero(a.k, row * sizeof(TI), r < rows);
     *reinterpret_cast<uint4 *>(sQ + r * L::LDQ + c) = xq;
     *reinterpret_cast<uint4 *>(sK + r * L::LDQ + c) = xk;
   }
-  for (int e = tid; e < C * D / 4; e += 256) {
+  for (int e = tid; e < C * D / 4; e += NTH) {
     const int r = e / (D / 4), c = (e % (D / 4)) * 4;
     *reinterpret_cast<float4 *>(sW + r * L::LDW + c) = *reinterpret_cast<const float4 *>(a.W + (cb * C + r) * D + c);
   }
@@ -111,10 +117,10 @@ __global__ __launch_bounds__(256) void bwd_ddh_kernel(FwdArgs fa, BwdArgs a) {
     ld8(t + r * L::LDQ + k0, x);
   };
   f32x4 pt[RU][R];
-  float qeff[RU][TD][4];
+  float qeff[RU][TDW][4];
 #pragma unroll
   for (int u = 0; u < RU; ++u) {
-    const int rt = u == 0 ? wv : R - 1 - wv;
+    const int rt = u == 0 ? wq : R - 1 - wq;
     const int r = 16 * rt + lr;
     const float Gr = sG[r] * LOG2E;
 #pragma unroll
@@ -137,7 +143,8 @@ __global__ __launch_bounds__(256) void bwd_ddh_kernel(FwdArgs fa, BwdArgs a) {
     // Qeff rows of query tile rt: e^{G_r} Q[r][d] - (P W)[r][d]; result lane
     // (lr, g) holds rows 16rt + 4g + i, column 16dt + lr
 #pragma unroll
-    for (int dt = 0; dt < TD; ++dt) {
+    for (int jt = 0; jt < TDW; ++jt) {
+      const int dt = dt0 + jt;
       f32x4 acc = zero4();
 #pragma unroll
       for (int kb = 0; kb < C / 32; ++kb) {
@@ -152,7 +159,7 @@ __global__ __launch_bounds__(256) void bwd_ddh_kernel(FwdArgs fa, BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int rr = 16 * rt + 4 * g + i;
-        qeff[u][dt][i] = exp2_fast(sG[rr] * LOG2E) * to_f32(sQ[rr * L::LDQ + 16 * dt + lr]) - acc[i];
+        qeff[u][jt][i] = exp2_fast(sG[rr] * LOG2E) * to_f32(sQ[rr * L::LDQ + 16 * dt + lr]) - acc[i];
       }
     }
   }
@@ -160,16 +167,16 @@ __global__ __launch_bounds__(256) void bwd_ddh_kernel(FwdArgs fa, BwdArgs a) {
   // Qeff^T [d][r] and dO^T [c][r] (zero past the chunk's tokens)
 #pragma unroll
   for (int u = 0; u < RU; ++u) {
-    const int rt = u == 0 ? wv : R - 1 - wv;
+    const int rt = u == 0 ? wq : R - 1 - wq;
 #pragma unroll
-    for (int dt = 0; dt < TD; ++dt)
-      *reinterpret_cast<float4 *>(sQt + (16 * dt + lr) * L::LDT + 16 * rt + 4 * g) =
-          float4{qeff[u][dt][0], qeff[u][dt][1], qeff[u][dt][2], qeff[u][dt][3]};
+    for (int jt = 0; jt < TDW; ++jt)
+      *reinterpret_cast<float4 *>(sQt + (16 * (dt0 + jt) + lr) * L::LDT + 16 * rt + 4 * g) =
+          float4{qeff[u][jt][0], qeff[u][jt][1], qeff[u][jt][2], qeff[u][jt][3]};
   }
-  static_assert((C * D / 4) % 256 == 0, "whole vectors per thread");
+  static_assert((C * D / 4) % NTH == 0, "whole vectors per thread");
 #pragma unroll 4
-  for (int u = 0; u < C * D / 4 / 256; ++u) {
-    const int e = tid + 256 * u, r = e / (D / 4), c = (e % (D / 4)) * 4;
+  for (int u = 0; u < C * D / 4 / NTH; ++u) {
+    const int e = tid + NTH * u, r = e / (D / 4), c = (e % (D / 4)) * 4;
     const float4 x = __builtin_bit_cast(
         float4, row_or_zero(a.dO, (((t0 + (r < rows ? r : rows - 1)) * a.Hv + hv) * D + c) * sizeof(float), r < rows));
     sOt[(c + 0) * L::LDT + r] = x.x;
@@ -178,8 +185,8 @@ __global__ __launch_bounds__(256) void bwd_ddh_kernel(FwdArgs fa, BwdArgs a) {
     sOt[(c + 3) * L::LDT + r] = x.w;
   }
   __syncthreads();
-  // ddh tiles (d tile dt, column tile ct): wave w takes tiles w, w + 4, ...
-  for (int t = wv; t < TD * TD; t += 4) {
+  // ddh tiles (d tile dt, column tile ct): wave w takes tiles w, w + NW, ...
+  for (int t = wv; t < TD * TD; t += NW) {
     const int dt = t % TD, ct = t / TD;
     f32x4 acc = zero4();
 #pragma unroll
