@@ -525,15 +525,17 @@ __device__ __forceinline__ void bwd_walk_body(const BwdArgs &a, size_t bh, char 
       for (int i = 0; i < 4; ++i) dh[m][i] = gl * dh[m][i] - acc[i] + ddv[i];
     }
   }
-  // chunk 0's incoming-state cotangent: that of h0
+  // chunk 0's incoming-state cotangent: that of h0 (one branch per
+  // destination: a branch per element made the compiler wait for each store
+  // before issuing the next)
+  auto put = [&](float *dst) {
 #pragma unroll
-  for (int m = 0; m < MH; ++m)
+    for (int m = 0; m < MH; ++m)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const size_t e = (size_t)(16 * m + 4 * g + i) * D + c0 + lr;
-      if (a.dh) a.dh[(bh * a.N) * D * D + e] = dh[m][i];
-      if (a.dh0) a.dh0[bh * D * D + e] = dh[m][i];
-    }
+      for (int i = 0; i < 4; ++i) dst[(size_t)(16 * m + 4 * g + i) * D + c0 + lr] = dh[m][i];
+  };
+  if (a.dh) put(a.dh + (bh * a.N) * D * D);
+  if (a.dh0) put(a.dh0 + bh * D * D);
 }
 
 template <int C, typename TI, int MODE, bool RAG>

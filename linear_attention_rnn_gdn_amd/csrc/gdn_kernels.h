@@ -624,6 +624,11 @@ __global__ __launch_bounds__(PNT, 4) void prep_kernel(FwdArgs a) {   // two work
   if constexpr (C > 64) ladder_level<C, 64, PR::ladder, PW>(sT, sM, wave, lane);
   static_assert(C == 64 || C == 128, "ladder levels for C = 64 and 128");
 
+  // K^T -> LDS from the registers
+  if (!vhalf) TileBlock<C, TI, PNT / 2>::put_transposed(tix, sX, xw);
+  // G (and T in the transform form) stored after the transposition: stored
+  // before it, they were waited for together with the K tile's loads, which
+  // the compiler counts with them where the two halves' paths join
   if (a.Tm) {
     float *Tg = a.Tm + cb * C * C;
     for (int idx = tid; idx < C * C; idx += PNT) {
@@ -632,9 +637,6 @@ __global__ __launch_bounds__(PNT, 4) void prep_kernel(FwdArgs a) {   // two work
     }
   }
   if (tid < C) a.G[cb * C + tid] = sG[tid];
-
-  // K^T -> LDS from the registers
-  if (!vhalf) TileBlock<C, TI, PNT / 2>::put_transposed(tix, sX, xw);
   lds_barrier();
   // (written by the first value head of each key head only)
   if (FWD && hv % (a.Hv / a.Hqk) == 0) {
