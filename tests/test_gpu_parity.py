@@ -622,6 +622,32 @@ def test_bwd_grads_full_size(gdn):
         assert e <= 1e-3 * _rms(r), name
 
 
+@pytest.mark.parametrize("B,Hqk,Hv", [(1, 16, 32), (4, 8, 16)])
+def test_bwd_workspace_reuse(gdn, B, Hqk, Hv):
+    # one workspace (filled with 0xFF bytes first) for several backward calls
+    # in a row on different inputs: no call may depend on what an earlier one
+    # left in it.  Each call equals a call on a fresh workspace (to 1e-5 of
+    # each gradient's RMS: the row sums gather through LDS atomics, whose
+    # order is not fixed).
+    w = WORKLOADS["qwen3next_8b_layer"].replace(T=1024 + 77, B=B, Hqk=Hqk, Hv=Hv)
+    shape = gdn.make_shape(w.B, w.T, w.Hqk, w.Hv, 128, 128, 128, 0, torch.bfloat16, torch.float32)
+    ws = torch.empty(gdn.workspace_size_bwd_grads(shape), dtype=torch.uint8, device="cuda")
+    ws.fill_(0xFF)
+    for seed in (11, 12, 13):
+        x = make_inputs(w, device="cuda", seed=seed)
+        gen = torch.Generator().manual_seed(seed)
+        dO = torch.randn((w.B, w.T, w.Hv, 128), generator=gen).to("cuda")
+        dhT = (torch.randn((w.B, w.Hv, 128, 128), generator=gen) * 0.1).to("cuda")
+        args = (x["q"], x["k"], x["v"], x["g"], x["beta"], dO)
+        got = gdn.chunk_bwd(*args, h0=x["h0"], dh_T=dhT, chunk=128, workspace=ws)
+        ref = gdn.chunk_bwd(*args, h0=x["h0"], dh_T=dhT, chunk=128)
+        torch.cuda.synchronize()
+        for name in ("dq", "dk", "dv", "dg", "dbeta", "dh0"):
+            r = ref[name].double()
+            e = float((got[name].double() - r).abs().max())
+            assert e <= 1e-5 * float(r.pow(2).mean().sqrt()), (seed, name, e)
+
+
 def test_long_sequence_reduced(gdn):
     # the long-sequence workload's shape and group structure at 1/16 of its length
     w = WORKLOADS["long_256k"].replace(T=16384, n_groups=16)
