@@ -187,12 +187,21 @@ gdn_status launch_walk(const FwdArgs &a, const Lx &x) {
   // (the walk that also yields A takes the latency form at any count)
   if constexpr (KIND == WALK_A) {
     launch(walk_ring_kernel<C, TI, MODE, KIND, NWS>, dim3((unsigned)(units * (width / 16))), dim3(64 * NWS), x, a);
+  } else if constexpr (KIND == FOLD) {
+    if (units * (width / 128) >= 512) {
+      // persistent (one workgroup per compute unit, each taking every
+      // num_cus-th item and copying its next item's first chunk during the
+      // last chunk of the one before) when every item's chunk count is even
+      const long items = units * (width / 128);
+      const long grid = a.cpj % 2 == 0 ? std::min(items, (long)num_cus()) : items;
+      launch(walk_shared_kernel<C, TI, MODE, KIND, 8>, dim3((unsigned)grid), dim3(512), x, a);
+    } else {
+      launch(walk_ring_kernel<C, TI, MODE, KIND, NWS>, dim3((unsigned)(units * (width / 16))), dim3(64 * NWS), x, a);
+    }
   } else {
-    if (KIND == WALK && units >= 65) {
+    if (units >= 65) {
       launch(walk_shared_kernel<C, TI, MODE, KIND, 4>, dim3((unsigned)(units * (width / 64))), dim3(256), x, a);
-    } else if (KIND == FOLD && units * (width / 128) >= 512) {
-      launch(walk_shared_kernel<C, TI, MODE, KIND, 8>, dim3((unsigned)(units * (width / 128))), dim3(512), x, a);
-    } else if (KIND == WALK && units > 32 && units <= 64) {
+    } else if (units > 32) {
       // two latency-form slices per compute unit would each stream the same
       // operands: one workgroup of two slices shares a copy in LDS instead
       launch(walk_pair_kernel<C, TI, MODE, NWS>, dim3((unsigned)(units * (D / 32))), dim3(128 * NWS), x, a);

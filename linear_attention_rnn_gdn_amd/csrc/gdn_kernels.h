@@ -823,53 +823,83 @@ __global__ __launch_bounds__(64 * WPG) void walk_shared_kernel(FwdArgs a) {
   __shared__ __align__(16) TI bufA[OPS::ELEMS];
   __shared__ __align__(16) TI bufB[OPS::ELEMS];
 
-  int unit, grp;
-  xcd_unit(blockIdx.x, NG, a.B * a.Hv * a.jobs, unit, grp);
-  const int job = unit % a.jobs;
-  const size_t bh = (size_t)(unit / a.jobs);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lr = lane & 15, g = lane >> 4;
-  const int slice = grp * WPG + wave;
-  const int c0 = slice * 16;   // first column (of the augmented [A|B] in FOLD)
-  const bool has_u = KIND == WALK || c0 >= D;
-  const int us = KIND == WALK ? slice : slice - D / 16;   // U column tile
-  // this walk's chunks: the job's share of the head's, or (packed sequences)
-  // the sequence's, in the workspace row of its value head
-  size_t cb0;
-  int cpj;
-  long long ktoff;
-  if (KIND != FOLD && a.jtab) {   // (packed sequences walk, never fold)
-    const int2 jt = a.jtab[bh / a.Hv];
-    // (wave-uniform: scalar loop bounds)
-    cb0 = (bh % a.Hv) * a.N + __builtin_amdgcn_readfirstlane(jt.x);
-    cpj = __builtin_amdgcn_readfirstlane(jt.y);
-    ktoff = kt_offset(a, bh % a.Hv);
-  } else {
-    cb0 = bh * a.N + a.n0 + (size_t)job * a.cpj;
-    cpj = a.cpj;
-    ktoff = kt_offset(a, bh);
-  }
-  cb0 = uniform64(cb0);
-  ktoff = (long long)uniform64((unsigned long long)ktoff);
+  const int tid = threadIdx.x, wave = tid >> 6;
+  int lane = tid & 63, lr = lane & 15, g = lane >> 4;
+  // A workgroup item: one workgroup's share (grp) of one walk (unit).  A
+  // persistent grid (the fold, fewer workgroups than items) takes items
+  // blockIdx.x, blockIdx.x + gridDim.x, ... and copies each next item's first
+  // chunk during the last chunk of the one before.
+  const int items = a.B * a.Hv * a.jobs * NG;
+  struct Item {
+    size_t bh, cb0;      // walk; its first chunk in the workspace row of its value head
+    long long ktoff;     // K^T chunk offset
+    int job, cpj, c0, us;
+    bool has_u;
+  };
+  auto item = [&](int L) {
+    Item it;
+    int unit, grp;
+    xcd_unit(L, NG, a.B * a.Hv * a.jobs, unit, grp);
+    it.job = unit % a.jobs;
+    it.bh = (size_t)(unit / a.jobs);
+    const int slice = grp * WPG + wave;
+    it.c0 = slice * 16;   // first column (of the augmented [A|B] in FOLD)
+    it.has_u = KIND == WALK || it.c0 >= D;
+    it.us = KIND == WALK ? slice : slice - D / 16;   // U column tile
+    // this walk's chunks: the job's share of the head's, or (packed
+    // sequences) the sequence's, in the workspace row of its value head
+    if (KIND != FOLD && a.jtab) {   // (packed sequences walk, never fold)
+      const int2 jt = a.jtab[it.bh / a.Hv];
+      // (wave-uniform: scalar loop bounds)
+      it.cb0 = (it.bh % a.Hv) * a.N + __builtin_amdgcn_readfirstlane(jt.x);
+      it.cpj = __builtin_amdgcn_readfirstlane(jt.y);
+      it.ktoff = kt_offset(a, it.bh % a.Hv);
+    } else {
+      it.cb0 = it.bh * a.N + a.n0 + (size_t)it.job * a.cpj;
+      it.cpj = a.cpj;
+      it.ktoff = kt_offset(a, it.bh);
+    }
+    it.cb0 = uniform64(it.cb0);
+    it.ktoff = (long long)uniform64((unsigned long long)it.ktoff);
+    return it;
+  };
+  int L = blockIdx.x, k = 0;
+  // A persistent workgroup's slots L = blockIdx.x + k gridDim.x take item L,
+  // or in odd slots item L ^ 8 (the unit's other workgroup share): the
+  // shares differ in cost (only the B half reads U), and a workgroup that kept
+  // one of them would finish half again as late as one that mixes them.
+  // (L ^ 8 stays in the same block of gridDim.x slots when that is a multiple
+  // of 16 and the items fill whole blocks.)
+  const bool mix = KIND == FOLD && gridDim.x % 16 == 0 && items % gridDim.x == 0;
+  auto slot_item = [&](int Ls, int ks) { return item(mix && (ks & 1) ? Ls ^ 8 : Ls); };
+  Item cur_item = slot_item(L, 0);
+  size_t bh = cur_item.bh, cb0 = cur_item.cb0;
+  long long ktoff = cur_item.ktoff;
+  int job = cur_item.job, cpj = cur_item.cpj, c0 = cur_item.c0, us = cur_item.us;
+  bool has_u = cur_item.has_u;
+  int slice = c0 / 16;
 
   // state tiles: h[m] holds rows 16m + 4g + i, column c0 + lr
   f32x4 h[MH];
+  auto init_state = [&]() {
 #pragma unroll
-  for (int m = 0; m < MH; ++m) {
-    const int col = c0 + lr;
+    for (int m = 0; m < MH; ++m) {
+      const int col = c0 + lr;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int kr = 16 * m + 4 * g + i;
-      float x = 0.f;
-      if (KIND == FOLD) {
-        x = (col < D && kr == col) ? 1.f : 0.f;
-      } else if (a.init) {
-        const float *src = a.init_per_job ? a.init + (bh * a.jobs + job) * D * D : a.init + bh * D * D;
-        x = src[(size_t)kr * D + col];
+      for (int i = 0; i < 4; ++i) {
+        const int kr = 16 * m + 4 * g + i;
+        float x = 0.f;
+        if (KIND == FOLD) {
+          x = (col < D && kr == col) ? 1.f : 0.f;
+        } else if (a.init) {
+          const float *src = a.init_per_job ? a.init + (bh * a.jobs + job) * D * D : a.init + bh * D * D;
+          x = src[(size_t)kr * D + col];
+        }
+        h[m][i] = x;
       }
-      h[m][i] = x;
     }
-  }
+  };
+  init_state();
 
   // final state slice (the pair of a group in FOLD)
   auto store_final = [&]() {
@@ -900,9 +930,9 @@ __global__ __launch_bounds__(64 * WPG) void walk_shared_kernel(FwdArgs a) {
   // (addresses: a wave-uniform base plus a 32-bit lane offset)
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const unsigned loff = lane * 16 * BPF;
-  auto stage = [&](TI *buf, size_t cb) {
+  auto stage = [&](TI *buf, size_t cb, long long kto) {
     const char *wbase = reinterpret_cast<const char *>(a.W) + cb * C * D * sizeof(TI);
-    const char *kbase = reinterpret_cast<const char *>(a.Kt) + (cb + ktoff) * D * C * sizeof(TI);
+    const char *kbase = reinterpret_cast<const char *>(a.Kt) + (cb + kto) * D * C * sizeof(TI);
 #pragma unroll
     for (int jj = 0; jj < NBLK / WPG; ++jj) {
       const int j = jj * WPG + wv, p = j / BPF, hh = j % BPF;
@@ -940,24 +970,29 @@ __global__ __launch_bounds__(64 * WPG) void walk_shared_kernel(FwdArgs a) {
   struct UG {
     float4 u[MV];
   };
-  auto fetch_u = [&](size_t cb, UG &x) {
+  auto fetch_u = [&](size_t cb, UG &x, bool hu, int ust) {
 #pragma unroll
     for (int m = 0; m < MV; ++m)
-      x.u[m] = has_u ? *reinterpret_cast<const float4 *>(a.U + ((cb * MV + m) * (D / 16) + us) * 256 + lane * 4)
-                     : float4{0.f, 0.f, 0.f, 0.f};
+      x.u[m] = hu ? *reinterpret_cast<const float4 *>(a.U + ((cb * MV + m) * (D / 16) + ust) * 256 + lane * 4)
+                  : float4{0.f, 0.f, 0.f, 0.f};
   };
 
   UG ug[2];
-  stage(bufA, cb0);
-  fetch_u(cb0, ug[0]);
+  stage(bufA, cb0, ktoff);
+  fetch_u(cb0, ug[0], has_u, us);
   chunk_barrier();
+  // the item after this one in the workgroup, if any (persistent grids)
+  bool has_next = false;
+  Item nxt_item = cur_item;
 
   auto step = [&](const TI *cur, TI *nxt, UG &cu, UG &nu, int cc) {
     const size_t cb = cb0 + cc;
     const bool more = cc + 1 < cpj;
-    // everything for the next chunk; waited for at the chunk's end only
-    fetch_u(more ? cb + 1 : cb, nu);
-    if (more) stage(nxt, cb + 1);
+    // everything for the next chunk (of this item, or the next item's first);
+    // waited for at the chunk's end only
+    const size_t pcb = more ? cb + 1 : has_next ? nxt_item.cb0 : cb;
+    fetch_u(pcb, nu, more || !has_next ? has_u : nxt_item.has_u, more ? us : nxt_item.us);
+    if (more || has_next) stage(nxt, pcb, more ? ktoff : nxt_item.ktoff);
     const float *Gs = reinterpret_cast<const float *>(reinterpret_cast<const char *>(cur) + OPS::GOFF);
     const float gl2 = Gs[C - 1] * LOG2E;
     float dcy[MV][4];
@@ -1036,13 +1071,29 @@ __global__ __launch_bounds__(64 * WPG) void walk_shared_kernel(FwdArgs a) {
     }
     chunk_barrier();
   };
-  // two chunks per trip: the LDS buffers and U/G sets alternate statically
-  for (int cc = 0; cc < cpj; cc += 2) {
-    step(bufA, bufB, ug[0], ug[1], cc);
-    if (cc + 1 < cpj) step(bufB, bufA, ug[1], ug[0], cc + 1);
+  for (;;) {
+    // (a persistent grid runs only where every item has an even chunk count,
+    // so that each item starts in bufA)
+    const int Ln = L + (int)gridDim.x;
+    has_next = KIND == FOLD && Ln < items;   // (the walk's grid is never persistent)
+    if (has_next) nxt_item = slot_item(Ln, k + 1);
+    // two chunks per trip: the LDS buffers and U/G sets alternate statically
+    for (int cc = 0; cc < cpj; cc += 2) {
+      step(bufA, bufB, ug[0], ug[1], cc);
+      if (cc + 1 < cpj) step(bufB, bufA, ug[1], ug[0], cc + 1);
+    }
+    store_final();
+    if (!has_next) break;
+    L = Ln;
+    ++k;
+    // (the lane indices opaque again for each item: the addresses derived
+    // from them are then formed per item, not held across all of them)
+    asm volatile("" : "+v"(lane), "+v"(lr), "+v"(g));
+    cur_item = nxt_item;
+    bh = cur_item.bh; cb0 = cur_item.cb0; ktoff = cur_item.ktoff; job = cur_item.job; cpj = cur_item.cpj;
+    c0 = cur_item.c0; us = cur_item.us; has_u = cur_item.has_u; slice = c0 / 16;
+    init_state();
   }
-
-  store_final();
 }
 
 // ----------------------------------------------------------------------------
