@@ -335,6 +335,27 @@ def test_fold_matches_oracle(gdn, dtype, C):
     assert _err(Bm.cpu().numpy(), Br) <= tol * np.abs(Br).max()
 
 
+@pytest.mark.parametrize("dtype,C,Hqk,Hv,ng,cpj", [
+    ("bf16", 128, 4, 8, 32, 2),    # 256 group-walks, 512 workgroup items: the persistent fold, halves alternating
+    ("bf16", 128, 5, 10, 30, 2),   # 600 items (not whole blocks of the grid): persistent, halves not alternated
+    ("bf16", 128, 4, 8, 32, 3),    # an odd chunk count per group: one workgroup per item
+    ("bf16", 64, 4, 8, 32, 2),
+    ("f32", 64, 4, 8, 32, 2),
+])
+def test_fold_throughput_forms(gdn, dtype, C, Hqk, Hv, ng, cpj):
+    # the fold of 256 or more group-walks (8 slices per workgroup, two
+    # workgroups per group), against the oracle's fold of every group
+    w = WORKLOADS["tiny"].replace(T=C * cpj * ng, Hqk=Hqk, Hv=Hv, chunk=C, dtype=dtype)
+    x = make_inputs(w, device="cuda", seed=ng + cpj, g_const=-0.01)   # weak decay: A far from 0
+    A, Bm = gdn.chunk_fold(x["k"], x["v"], x["g"], x["beta"], n_groups=ng, chunk=C)
+    torch.cuda.synchronize()
+    Ar, Br = oracle.fold(_cpu(x["k"]), _cpu(x["v"]), _cpu(x["g"]), _cpu(x["beta"]), n_groups=ng)
+    # bars as in test_fold_matches_oracle (errors scaled by the largest entry)
+    tol = 1e-2 if dtype == "bf16" else 1e-4
+    assert _err(A.cpu().numpy(), Ar) <= tol * np.abs(Ar).max()
+    assert _err(Bm.cpu().numpy(), Br) <= tol * np.abs(Br).max()
+
+
 @pytest.mark.parametrize("split", [False, True])
 def test_compose_prefix_matches_oracle(gdn, split):
     BH, n = 3, 9
