@@ -2588,13 +2588,22 @@ __global__ __launch_bounds__(64 * WPG) void walk_out_kernel(FwdArgs a) {
     tok0 = (size_t)b * a.T + n * C;
     rows = !RAG ? C : (int)((size_t)a.T - n * C < (size_t)C ? (size_t)a.T - n * C : (size_t)C);
   };
-  auto copy_qkg = [&](int cc) {
+  auto copy_q = [&](int cc) {
     size_t tok0;
     int rows;
     chunk_tokens(cc, tok0, rows);
     copy_rows(a.q, tok0, rows, sQ);
+  };
+  auto copy_kg = [&](int cc) {
+    size_t tok0;
+    int rows;
+    chunk_tokens(cc, tok0, rows);
     copy_rows(a.k, tok0, rows, sPK);
     copy_g(cb0 + cc);
+  };
+  auto copy_qkg = [&](int cc) {
+    copy_q(cc);
+    copy_kg(cc);
   };
   float4 u[SPW][MV];
   auto fetch_u = [&](size_t cb) {
@@ -2819,34 +2828,42 @@ __global__ __launch_bounds__(64 * WPG) void walk_out_kernel(FwdArgs a) {
       }
       return bf;
     };
+    // h^T Q^T for each slice first, so that the next chunk's Q can be copied
+    // while V'^T P^T runs (one slice after the other in each part: the
+    // scheduler would otherwise interleave both slices' products and hold
+    // both sets of operands)
+    f32x4 a1[SPW][R];
 #pragma unroll
     for (int s = 0; s < SPW; ++s) {
-      // (one slice after the other: the scheduler would otherwise interleave
-      // both slices' products and hold both sets of operands)
       __builtin_amdgcn_sched_barrier(0);
-      f32x4 a1[R];
-      {
-        Frag<PKh::a> hT[KBW];   // the chunk-start state, split for this product
+      Frag<PKh::a> hT[KBW];   // the chunk-start state, split for this product
 #pragma unroll
-        for (int kb = 0; kb < KBW; ++kb) {
-          const float x[8] = {h[s][2 * kb][0], h[s][2 * kb][1], h[s][2 * kb][2], h[s][2 * kb][3],
-                              h[s][2 * kb + 1][0], h[s][2 * kb + 1][1], h[s][2 * kb + 1][2], h[s][2 * kb + 1][3]};
-          hT[kb] = make_frag<PKh::a>(x);
-        }
-        QF qf[2][KBW];
-#pragma unroll
-        for (int kb = 0; kb < KBW; ++kb) qf[0][kb] = row_frag(sQ, 0, kb);
-#pragma unroll
-        for (int rt = 0; rt < R; ++rt) {
-          if (rt + 1 < R) {
-#pragma unroll
-            for (int kb = 0; kb < KBW; ++kb) qf[(rt + 1) & 1][kb] = row_frag(sQ, rt + 1, kb);
-          }
-          a1[rt] = zero4();
-#pragma unroll
-          for (int kb = 0; kb < KBW; ++kb) mma(a1[rt], hT[kb], qf[rt & 1][kb]);
-        }
+      for (int kb = 0; kb < KBW; ++kb) {
+        const float x[8] = {h[s][2 * kb][0], h[s][2 * kb][1], h[s][2 * kb][2], h[s][2 * kb][3],
+                            h[s][2 * kb + 1][0], h[s][2 * kb + 1][1], h[s][2 * kb + 1][2], h[s][2 * kb + 1][3]};
+        hT[kb] = make_frag<PKh::a>(x);
       }
+      QF qf[2][KBW];
+#pragma unroll
+      for (int kb = 0; kb < KBW; ++kb) qf[0][kb] = row_frag(sQ, 0, kb);
+#pragma unroll
+      for (int rt = 0; rt < R; ++rt) {
+        if (rt + 1 < R) {
+#pragma unroll
+          for (int kb = 0; kb < KBW; ++kb) qf[(rt + 1) & 1][kb] = row_frag(sQ, rt + 1, kb);
+        }
+        a1[s][rt] = zero4();
+#pragma unroll
+        for (int kb = 0; kb < KBW; ++kb) mma(a1[s][rt], hT[kb], qf[rt & 1][kb]);
+      }
+    }
+    if constexpr (more) {
+      wait_barrier<vm_lgkm0(63)>();   // every wave past Q
+      copy_q(cc + 1);
+    }
+#pragma unroll
+    for (int s = 0; s < SPW; ++s) {
+      __builtin_amdgcn_sched_barrier(0);
       Frag<PKv::a> vT[KBK];
 #pragma unroll
       for (int kb = 0; kb < KBK; ++kb) {
@@ -2876,7 +2893,7 @@ __global__ __launch_bounds__(64 * WPG) void walk_out_kernel(FwdArgs a) {
         const float er = exp2_fast(Gs[r] * LOG2E);
         TO ov[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ov[i] = from_f32<TO>(er * a1[rt][i] + a2[i]);
+        for (int i = 0; i < 4; ++i) ov[i] = from_f32<TO>(er * a1[s][rt][i] + a2[i]);
         TO *dst = og + ((tok0 + r) * a.Hv + hv) * D + c0 + 16 * s + lq;
         if (!RAG || r < rows) {
           if constexpr (sizeof(TO) == 4) st16_stream(dst, ov);
@@ -2884,11 +2901,12 @@ __global__ __launch_bounds__(64 * WPG) void walk_out_kernel(FwdArgs a) {
         }
       }
     }
-    // every wave past Q, P^T and G; this chunk's K^T landed (the next chunk's
-    // W and this chunk's o stores, issued after it, may be in flight)
-    if constexpr (more) wait_barrier<vm_lgkm0(NCW + NST)>();
+    // every wave past P^T and G; this chunk's K^T landed (the next chunk's
+    // W and Q copies and this chunk's o stores, issued after it, may be in
+    // flight)
+    if constexpr (more) wait_barrier<vm_lgkm0(NCW + NCQ + NST)>();
     else wait_barrier<vm_lgkm0(NST)>();
-    if constexpr (more) copy_qkg(cc + 1);
+    if constexpr (more) copy_kg(cc + 1);
 
     // ---- h <- e^{G_last} h + K^T (d o V'), K^T fragments one state tile
     //      ahead (and serving every slice of the wave)
