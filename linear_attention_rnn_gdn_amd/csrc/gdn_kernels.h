@@ -2273,14 +2273,17 @@ __global__ __launch_bounds__(NT, 2) void out_kernel(FwdArgs a) {
 // k-values kk(g, j) of a block of 32, the k order in which the query and key
 // rows are read (and in which P^T's tiles are formed).
 //
-// LDS holds one chunk's operands in four slots -- W fragments, K^T
-// fragments, the Q tile, and the K tile, which the P^T fragments replace once
-// formed -- plus G; each slot is refilled for the next chunk (global_load_lds,
-// no registers) as soon as every wave is past its last read of it:
-//   W  after V',  K^T after the state update,  Q, K and G after the outputs.
-// Each refill thus has at least two of the chunk's phases to land.  The waits before
-// the barriers count the copies, U loads and o stores each wave issued after
-// the ones waited for (the memory counter completes in issue order).
+// LDS holds one chunk's operands in four slots -- W fragments (then the P^T
+// fragments: they wait in registers while V' reads W), K^T fragments, the Q
+// tile and the K tile -- plus G; each slot is refilled for the next chunk
+// (global_load_lds, no registers) as soon as every wave is past its last
+// read of it:
+//   K after V' (P^T was formed before it),  Q after h^T Q^T,
+//   G and W after V'^T P^T,  K^T after the state update.
+// The next chunk's P^T, which needs K and Q first, thus finds them copied
+// most of a chunk earlier.  The waits before the barriers count the copies,
+// U loads and o stores each wave issued after the ones waited for (the
+// memory counter completes in issue order).
 template <int C, typename TI> struct WalkOutLds {
   using OL = OutLds<C, TI>;
   static constexpr int BPF = 8 * (int)sizeof(TI) / 16;            // 1 KB blocks per fragment
@@ -2288,7 +2291,7 @@ template <int C, typename TI> struct WalkOutLds {
   static constexpr int WB = FW * BPF * 1024, KTB = FK * BPF * 1024;  // W, K^T fragment bytes
   static constexpr int QB = OL::KB;                                 // Q (or K) tile bytes
   static constexpr int PB = OL::NPAIR * 2048;                       // P^T fragment bytes
-  static constexpr int PKB = PB > QB ? PB : QB;                     // the K tile, then P^T
+  static constexpr int WPB = PB > WB ? PB : WB;                     // W, then P^T
 };
 
 // wait (s_waitcnt IMM), then the workgroup barrier; no memory access moves
@@ -2474,10 +2477,10 @@ __global__ __launch_bounds__(64 * WPG) void walk_out_kernel(FwdArgs a) {
   static_assert(WPG == 4 && R == 4 * RU, "P^T: query tiles {w, R-1-w} (R = 8) or {w} (R = 4) per wave");
   // one array per slot (the compiler then tells the LDS reads of one slot
   // from the copies into another, and waits for neither at the reads)
-  __shared__ __align__(16) char sW[L::WB];
+  __shared__ __align__(16) char sW[L::WPB];   // W, then P^T
   __shared__ __align__(16) char sKt[L::KTB];
   __shared__ __align__(16) char sQ[L::QB];
-  __shared__ __align__(16) char sPK[L::PKB];
+  __shared__ __align__(16) char sPK[L::QB];   // K
   __shared__ __align__(16) float sG[C];
 
   int unit, grp;
@@ -2594,16 +2597,11 @@ __global__ __launch_bounds__(64 * WPG) void walk_out_kernel(FwdArgs a) {
     chunk_tokens(cc, tok0, rows);
     copy_rows(a.q, tok0, rows, sQ);
   };
-  auto copy_kg = [&](int cc) {
+  auto copy_k = [&](int cc) {
     size_t tok0;
     int rows;
     chunk_tokens(cc, tok0, rows);
     copy_rows(a.k, tok0, rows, sPK);
-    copy_g(cb0 + cc);
-  };
-  auto copy_qkg = [&](int cc) {
-    copy_q(cc);
-    copy_kg(cc);
   };
   float4 u[SPW][MV];
   auto fetch_u = [&](size_t cb) {
@@ -2658,10 +2656,12 @@ __global__ __launch_bounds__(64 * WPG) void walk_out_kernel(FwdArgs a) {
   const float *Gs = sG;
   TO *og = reinterpret_cast<TO *>(a.o);
 
-  // the first chunk's copies, in the order of the chunk loop's (W, then Q,
-  // K and G, then K^T)
+  // the first chunk's copies, in the order of the chunk loop's (K, Q, G, W,
+  // then K^T)
+  copy_k(0);
+  copy_q(0);
+  copy_g(cb0);
   copy_w(cb0);
-  copy_qkg(0);
   copy_kt(cb0);
 
   // one chunk; more: a next chunk follows, whose operands are copied during
@@ -2678,9 +2678,49 @@ __global__ __launch_bounds__(64 * WPG) void walk_out_kernel(FwdArgs a) {
 
     // U of this chunk, issued first: it lands while P^T is formed
     fetch_u(cb);
-    // this chunk's W, Q, K and G landed (its K^T copies and U, issued after
-    // them, may be in flight)
-    wait_barrier<vm_lgkm0(NCK + NU)>();
+    // this chunk's K, Q and G landed (its W and K^T copies and U, issued
+    // after them, may be in flight)
+    wait_barrier<vm_lgkm0(NCW + NCK + NU)>();
+
+    // ---- V' = U - W h, formed while the P^T fragments wait in registers
+    //      (their LDS slot is W's)
+    f32x4 vps[SPW][MV];
+    auto form_vprime = [&]() {
+      Frag<PKw::b> hb[SPW][KBW];
+#pragma unroll
+      for (int s = 0; s < SPW; ++s)
+#pragma unroll
+        for (int kb = 0; kb < KBW; ++kb) {
+          const float x[8] = {h[s][2 * kb][0], h[s][2 * kb][1], h[s][2 * kb][2], h[s][2 * kb][3],
+                              h[s][2 * kb + 1][0], h[s][2 * kb + 1][1], h[s][2 * kb + 1][2], h[s][2 * kb + 1][3]};
+          hb[s][kb] = make_frag<PKw::b>(x);
+        }
+      {
+        Frag<PKw::a> fa[2][KBW];
+#pragma unroll
+        for (int kb = 0; kb < KBW; ++kb) fa[0][kb] = frag(sW, kb);
+#pragma unroll
+        for (int m = 0; m < MV; ++m) {
+          if (m + 1 < MV) {
+#pragma unroll
+            for (int kb = 0; kb < KBW; ++kb) fa[(m + 1) & 1][kb] = frag(sW, (m + 1) * KBW + kb);
+          }
+#pragma unroll
+          for (int s = 0; s < SPW; ++s) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int kb = 0; kb < KBW; ++kb) mma(acc, fa[m & 1][kb], hb[s][kb]);
+            vps[s][m] = f32x4{u[s][m].x - acc[0], u[s][m].y - acc[1], u[s][m].z - acc[2], u[s][m].w - acc[3]};
+          }
+        }
+      }
+      // (V' complete here: sunk below the next chunk's K copies, its
+      // subtractions would wait for those copies as well as for U)
+#pragma unroll
+      for (int s = 0; s < SPW; ++s)
+#pragma unroll
+        for (int m = 0; m < MV; ++m) asm volatile("" : "+v"(vps[s][m]));
+    };
 
     // ---- P^T = (K Q^T) o Gamma^T o [i <= r]: wave w forms the pairs (query
     //      tile rt, key tiles 2kp and 2kp + 1) of its query tiles {w, R-1-w}
@@ -2715,7 +2755,7 @@ __global__ __launch_bounds__(64 * WPG) void walk_out_kernel(FwdArgs a) {
       return make_frag<PKv::b>(b8);
     };
     auto store_pair = [&](int rt, int kp, const Frag<PKv::b> &f) {
-      char *pf = sPK + (OL::pbase(rt) + kp) * 2048 + lane * 16;
+      char *pf = sW + (OL::pbase(rt) + kp) * 2048 + lane * 16;
       if constexpr (PKv::b == F_SPLIT) {
         *reinterpret_cast<bf16x8 *>(pf) = f.hi;
         *reinterpret_cast<bf16x8 *>(pf + 1024) = f.lo;
@@ -2745,7 +2785,9 @@ __global__ __launch_bounds__(64 * WPG) void walk_out_kernel(FwdArgs a) {
       for (int kb = 0; kb < KBW; ++kb) q1[kb] = row_frag(sQ, rt1, kb);
 #pragma unroll
       for (int kp = 0; kp < 3; ++kp) pt[2 + kp] = form_pair(q1, rt1, kp);
-      wait_barrier<vm_lgkm0(63)>();   // every wave past the K tile
+      form_vprime();
+      wait_barrier<vm_lgkm0(63)>();   // every wave past the K tile and W
+      if constexpr (more) copy_k(cc + 1);
       store_pair(rt0, 0, pt[0]);
       store_pair(rtx, kpx, pt[1]);
 #pragma unroll
@@ -2761,52 +2803,15 @@ __global__ __launch_bounds__(64 * WPG) void walk_out_kernel(FwdArgs a) {
 #pragma unroll
       for (int kp = 0; kp < 2; ++kp)
         if (2 * kp <= rt) pt[kp] = form_pair(qf, rt, kp);
-      wait_barrier<vm_lgkm0(63)>();   // every wave past the K tile
+      form_vprime();
+      wait_barrier<vm_lgkm0(63)>();   // every wave past the K tile and W
+      if constexpr (more) copy_k(cc + 1);
 #pragma unroll
       for (int kp = 0; kp < 2; ++kp)
         if (2 * kp <= rt) store_pair(rt, kp, pt[kp]);
     }
     wait_barrier<vm_lgkm0(63)>();   // P^T in place
 
-    // ---- V' = U - W h.  W fragments are read one output tile ahead (and
-    //      serve every slice of the wave).
-    Frag<PKw::b> hb[SPW][KBW];
-#pragma unroll
-    for (int s = 0; s < SPW; ++s)
-#pragma unroll
-      for (int kb = 0; kb < KBW; ++kb) {
-        const float x[8] = {h[s][2 * kb][0], h[s][2 * kb][1], h[s][2 * kb][2], h[s][2 * kb][3],
-                            h[s][2 * kb + 1][0], h[s][2 * kb + 1][1], h[s][2 * kb + 1][2], h[s][2 * kb + 1][3]};
-        hb[s][kb] = make_frag<PKw::b>(x);
-      }
-    f32x4 vps[SPW][MV];
-    {
-      Frag<PKw::a> fa[2][KBW];
-#pragma unroll
-      for (int kb = 0; kb < KBW; ++kb) fa[0][kb] = frag(sW, kb);
-#pragma unroll
-      for (int m = 0; m < MV; ++m) {
-        if (m + 1 < MV) {
-#pragma unroll
-          for (int kb = 0; kb < KBW; ++kb) fa[(m + 1) & 1][kb] = frag(sW, (m + 1) * KBW + kb);
-        }
-#pragma unroll
-        for (int s = 0; s < SPW; ++s) {
-          f32x4 acc = zero4();
-#pragma unroll
-          for (int kb = 0; kb < KBW; ++kb) mma(acc, fa[m & 1][kb], hb[s][kb]);
-          vps[s][m] = f32x4{u[s][m].x - acc[0], u[s][m].y - acc[1], u[s][m].z - acc[2], u[s][m].w - acc[3]};
-        }
-      }
-    }
-    // (V' complete here: sunk below the next chunk's W copies, its
-    // subtractions would wait for those copies as well as for U)
-#pragma unroll
-    for (int s = 0; s < SPW; ++s)
-#pragma unroll
-      for (int m = 0; m < MV; ++m) asm volatile("" : "+v"(vps[s][m]));
-    wait_barrier<vm_lgkm0(63)>();   // every wave past W
-    if constexpr (more) copy_w(cb + 1);
 
     // ---- outputs O^T = e^{G_r} h^T Q^T + V'^T P^T for each slice's columns,
     //      one slice after the other: first h^T Q^T for every query tile
@@ -2816,7 +2821,7 @@ __global__ __launch_bounds__(64 * WPG) void walk_out_kernel(FwdArgs a) {
     const float gl = exp2_fast(gl2);
     Frag<PKk::b> vb[SPW][KBK];   // d o V' for the state update (G is recopied before it)
     auto pfrag = [&](int p) -> Frag<PKv::b> {
-      const char *pf = sPK + p * 2048 + lane * 16;
+      const char *pf = sW + p * 2048 + lane * 16;
       Frag<PKv::b> bf;
       if constexpr (PKv::b == F_SPLIT) {
         bf.hi = *reinterpret_cast<const bf16x8 *>(pf);
@@ -2901,12 +2906,15 @@ __global__ __launch_bounds__(64 * WPG) void walk_out_kernel(FwdArgs a) {
         }
       }
     }
-    // every wave past P^T and G; this chunk's K^T landed (the next chunk's
-    // W and Q copies and this chunk's o stores, issued after it, may be in
-    // flight)
-    if constexpr (more) wait_barrier<vm_lgkm0(NCW + NCQ + NST)>();
+    // every wave past P^T (W's slot) and G; this chunk's K^T landed (U, the
+    // next chunk's K and Q copies and this chunk's o stores, issued after it,
+    // may be in flight)
+    if constexpr (more) wait_barrier<vm_lgkm0(NU + 2 * NCQ + NST)>();
     else wait_barrier<vm_lgkm0(NST)>();
-    if constexpr (more) copy_kg(cc + 1);
+    if constexpr (more) {
+      copy_g(cb + 1);
+      copy_w(cb + 1);
+    }
 
     // ---- h <- e^{G_last} h + K^T (d o V'), K^T fragments one state tile
     //      ahead (and serving every slice of the wave)
@@ -2931,9 +2939,7 @@ __global__ __launch_bounds__(64 * WPG) void walk_out_kernel(FwdArgs a) {
       }
     }
     if constexpr (more) {
-      // every wave past K^T; the next chunk's W landed (this chunk's o
-      // stores and the next chunk's Q, K and G copies may be in flight)
-      wait_barrier<vm_lgkm0(NST + 2 * NCQ + 1)>();
+      wait_barrier<vm_lgkm0(63)>();   // every wave past K^T
       copy_kt(cb + 1);
     }
   };
