@@ -685,6 +685,7 @@ def test_long_sequence_reduced(gdn):
     ("bf16", 64, 63, 1, 2, 0.05, 0),              # shorter than one chunk
     ("bf16", 128, 4000, 2, 4, 0.02, 4),           # chunk-groups, the last one ragged
     ("bf16", 128, 4000, 8, 16, 0.02, 4),          # the same replayed by the walk with outputs (128 walks)
+    ("bf16", 128, 4000, 8, 32, 0.02, 4),          # 256 replay walks: two state slices per wave, ragged
     ("bf16", 64, 64 * 9 + 5, 8, 16, 0.05, 5),     # C = 64, walk with outputs (160 walks), ragged
 ])
 def test_forward_ragged_tail(gdn, dtype, C, T, Hqk, Hv, h0, ng):
