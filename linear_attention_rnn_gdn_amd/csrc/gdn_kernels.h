@@ -208,6 +208,21 @@ __device__ __forceinline__ void chunk_head_unit(int L, const FwdArgs &a, int &n,
   hv = hq * grp + part;
 }
 
+// 1-D workgroup index of the walks -> (walk bh, its job, the workgroup's
+// share grp of it, of NG), with the shares of the value heads that share a qk
+// head on one XCD next to each other (as the per-chunk kernels place them):
+// chunk by chunk they read the same K^T (and, in the walk with outputs, the
+// same q and k rows) and share them in that XCD's L2.
+__device__ __forceinline__ void walk_unit(int L, int NG, const FwdArgs &a, size_t &bh, int &job, int &grp) {
+  const int R = a.Hv / a.Hqk;
+  int unit, part;
+  xcd_unit(L, NG * R, a.B * a.Hqk * a.jobs, unit, part);
+  grp = part % NG;
+  job = unit % a.jobs;
+  const int bq = unit / a.jobs;   // b * Hqk + hq
+  bh = (size_t)(bq / a.Hqk) * a.Hv + (size_t)(bq % a.Hqk) * R + part / NG;
+}
+
 // ----------------------------------------------------------------------------
 // prep: decay cumsum, S, T (ladder), W, U for one chunk of one value head.
 // FWD: the forward path's layouts (W in the input dtype, fragment-major W,
@@ -838,10 +853,8 @@ __global__ __launch_bounds__(64 * WPG) void walk_shared_kernel(FwdArgs a) {
   };
   auto item = [&](int L) {
     Item it;
-    int unit, grp;
-    xcd_unit(L, NG, a.B * a.Hv * a.jobs, unit, grp);
-    it.job = unit % a.jobs;
-    it.bh = (size_t)(unit / a.jobs);
+    int grp;
+    walk_unit(L, NG, a, it.bh, it.job, grp);
     const int slice = grp * WPG + wave;
     it.c0 = slice * 16;   // first column (of the augmented [A|B] in FOLD)
     it.has_u = KIND == WALK || it.c0 >= D;
@@ -2483,10 +2496,9 @@ __global__ __launch_bounds__(64 * WPG) void walk_out_kernel(FwdArgs a) {
   __shared__ __align__(16) char sPK[L::QB];   // K
   __shared__ __align__(16) float sG[C];
 
-  int unit, grp;
-  xcd_unit(blockIdx.x, NG, a.B * a.Hv * a.jobs, unit, grp);
-  const int job = unit % a.jobs;
-  const size_t bh = (size_t)(unit / a.jobs);
+  size_t bh;
+  int job, grp;
+  walk_unit(blockIdx.x, NG, a, bh, job, grp);
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (KIND == WALK_A) {
     if (grp < NGH) {   // (uniform per workgroup) columns of A
