@@ -183,9 +183,9 @@ def stage_bytes(w, o_bytes=4):
     if J > 1:
         out["fold"] = W_b + U_b + G_b + Kt_b + pairs
         out["prefix"] = pairs + h0_b + hin + st
-    if fused_walk(w):   # the walk reads q and writes o itself; no handoff
+    if fused_walk(w):   # the walk reads q and k and writes o itself; no handoff
         del out["out"]
-        out["walk"] = W_b + U_b + G_b + Kt_b + init + q_b + tok * w.Hv * dv * o_bytes + st
+        out["walk"] = W_b + U_b + G_b + Kt_b + init + q_b + k_b + tok * w.Hv * dv * o_bytes + st
     else:
         out["walk"] = W_b + U_b + G_b + Kt_b + init + Hs_b + Vn_b + (st if J == 1 else 0)
     return out
