@@ -339,6 +339,7 @@ def test_fold_matches_oracle(gdn, dtype, C):
     ("bf16", 128, 4, 8, 32, 2),    # 256 group-walks, 512 workgroup items: the persistent fold, halves alternating
     ("bf16", 128, 5, 10, 30, 2),   # 600 items (not whole blocks of the grid): persistent, halves not alternated
     ("bf16", 128, 4, 8, 32, 3),    # an odd chunk count per group: one workgroup per item
+    ("bf16", 128, 2, 8, 32, 2),    # four value heads per qk head, placed side by side
     ("bf16", 64, 4, 8, 32, 2),
     ("f32", 64, 4, 8, 32, 2),
 ])
